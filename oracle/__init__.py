@@ -1,0 +1,8 @@
+"""CPU oracle of the Wukong interaction stack -- TEST INFRASTRUCTURE ONLY.
+
+Imported only by the tests, the package's smoke check and the benchmark's
+CPU-baseline leg.  It shares no code with the HIP library.
+"""
+from .wukong_oracle import (LN_EPS, STORAGE_NAMES, brute_force_layer, decode_bf16,  # noqa: F401
+                            fm_interaction, fmb_mlp, layer_norm, lcb, round_bf16, to_f64,
+                            wukong_layer, wukong_stack)

@@ -1,0 +1,238 @@
+"""Seeded synthetic inputs and weights for the Wukong interaction stack.
+
+Both the CPU oracle's tests and the GPU path's tests and benchmark draw their
+host arrays from here, so the two sides see bit-identical inputs.  Nothing in
+this module computes any part of the layer: it only draws random numbers,
+scales them and rounds them to the storage type.
+
+Random streams
+--------------
+Every tensor has a tag such as ``"stack8_n256/L3/mlp_w1"``.  The tag and the
+seed are hashed (BLAKE2b) to a 128-bit Philox-4x64 key; the tensor is filled
+in fixed-size chunks, each with its own key (tag + chunk index), so the values
+do not depend on how many threads fill them.  Philox is a counter-based
+generator (Salmon et al., "Parallel random numbers: as easy as 1, 2, 3",
+SC 2011) and numpy's implementation of its raw stream is platform-stable.
+
+Distributions
+-------------
+* inputs X: N(0, 1); for the small-d workload each 32-wide feature row is four
+  8-wide units side by side, all scaled by one per-feature factor
+  s_i = 10**U(-1, 1) (log-uniform on [0.1, 10]) shared by every example;
+* weights: Xavier-uniform, bound sqrt(6 / (fan_in + fan_out)) with PyTorch's
+  fan convention for an [out, in] matrix (fan_in = in, fan_out = out);
+* LayerNorm gamma = 1, beta = 0 and biases = 0 for the measured runs, or
+  gamma = 1 + U(-0.5, 0.5), beta and biases U(-0.5, 0.5) for parity runs.
+
+Storage
+-------
+fp32 configurations return float32 arrays.  bf16 configurations return the
+bf16 bit patterns as uint16 arrays, rounded once from float32 with
+round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import hashlib
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+from .configs import LayerShape, WukongConfig
+
+CHUNK = 1 << 22  # elements per independently keyed chunk
+
+
+def stream_key(seed: int, tag: str) -> int:
+    h = hashlib.blake2b(f"{seed}|{tag}".encode(), digest_size=16).digest()
+    return int.from_bytes(h, "little")
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _fill(seed: int, tag: str, size: int, kind: str) -> np.ndarray:
+    """float32 array of `size` draws: kind 'uniform' -> U[0,1), 'normal' -> N(0,1)."""
+    out = np.empty(size, dtype=np.float32)
+    nchunks = (size + CHUNK - 1) // CHUNK
+
+    def work(i):
+        lo, hi = i * CHUNK, min(size, (i + 1) * CHUNK)
+        g = np.random.Generator(np.random.Philox(key=stream_key(seed, f"{tag}#{i}")))
+        if kind == "uniform":
+            g.random(dtype=np.float32, out=out[lo:hi])
+        elif kind == "normal":
+            g.standard_normal(dtype=np.float32, out=out[lo:hi])
+        else:  # pragma: no cover
+            raise ValueError(kind)
+
+    if nchunks <= 1:
+        for i in range(nchunks):
+            work(i)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round-to-nearest-even); returns uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    flat_in = x.reshape(-1).view(np.uint32)
+    flat_out = out.reshape(-1)
+    n = flat_in.size
+
+    def work(i):
+        lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
+        b = flat_in[lo:hi]
+        bias = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+        flat_out[lo:hi] = ((b + bias) >> np.uint32(16)).astype(np.uint16)
+
+    nchunks = (n + CHUNK - 1) // CHUNK
+    if nchunks <= 1:
+        for i in range(nchunks):
+            work(i)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    raise ValueError(dtype)
+
+
+def xavier_uniform(seed: int, tag: str, out_features: int, in_features: int, dtype: str) -> np.ndarray:
+    a = math.sqrt(6.0 / (in_features + out_features))
+    u = _fill(seed, tag, out_features * in_features, "uniform")
+    w = (u * np.float32(2.0) - np.float32(1.0)) * np.float32(a)
+    return _store(w.reshape(out_features, in_features), dtype)
+
+
+def _uniform_pm(seed: int, tag: str, size: int, half_width: float, center: float = 0.0) -> np.ndarray:
+    u = _fill(seed, tag, size, "uniform")
+    return (u * np.float32(2.0) - np.float32(1.0)) * np.float32(half_width) + np.float32(center)
+
+
+@dataclass
+class HostLayerWeights:
+    """Host copies of one layer's parameters (float32, or uint16 bf16 bits)."""
+
+    phi: np.ndarray            # [k, n]
+    w_l: np.ndarray            # [n_L, n]
+    fm_gamma: np.ndarray       # [n*k]
+    fm_beta: np.ndarray        # [n*k]
+    mlp_w: List[np.ndarray]    # W_t: [m_t, m_{t-1}]
+    mlp_b: List[np.ndarray]    # b_t: [m_t]
+    out_gamma: np.ndarray      # [d]
+    out_beta: np.ndarray       # [d]
+    dtype: str = "f32"
+
+    def nbytes(self) -> int:
+        arrs = [self.phi, self.w_l, self.fm_gamma, self.fm_beta, self.out_gamma, self.out_beta]
+        arrs += self.mlp_w + self.mlp_b
+        return int(sum(a.nbytes for a in arrs))
+
+
+def make_layer_weights(cfg_name: str, layer: int, shape: LayerShape, dtype: str, seed: int,
+                       affine: str = "identity") -> HostLayerWeights:
+    """Xavier-uniform weights of one layer.  affine: 'identity' or 'random'."""
+    t = f"{cfg_name}/L{layer}"
+    n, d, k = shape.n, shape.d, shape.k
+    phi = xavier_uniform(seed, f"{t}/phi", k, n, dtype)
+    w_l = xavier_uniform(seed, f"{t}/w_l", shape.n_l, n, dtype)
+    mlp_w, mlp_b = [], []
+    for i, (a, b) in enumerate(zip(shape.mlp[:-1], shape.mlp[1:])):
+        mlp_w.append(xavier_uniform(seed, f"{t}/mlp_w{i}", b, a, dtype))
+        if affine == "random":
+            mlp_b.append(_store(_uniform_pm(seed, f"{t}/mlp_b{i}", b, 0.5), dtype))
+        else:
+            mlp_b.append(_store(np.zeros(b, np.float32), dtype))
+    if affine == "random":
+        fm_g = _uniform_pm(seed, f"{t}/fm_gamma", n * k, 0.5, 1.0)
+        fm_b = _uniform_pm(seed, f"{t}/fm_beta", n * k, 0.5)
+        o_g = _uniform_pm(seed, f"{t}/out_gamma", d, 0.5, 1.0)
+        o_b = _uniform_pm(seed, f"{t}/out_beta", d, 0.5)
+    elif affine == "identity":
+        fm_g, fm_b = np.ones(n * k, np.float32), np.zeros(n * k, np.float32)
+        o_g, o_b = np.ones(d, np.float32), np.zeros(d, np.float32)
+    else:
+        raise ValueError(affine)
+    return HostLayerWeights(phi, w_l, _store(fm_g, dtype), _store(fm_b, dtype), mlp_w, mlp_b,
+                            _store(o_g, dtype), _store(o_b, dtype), dtype)
+
+
+def make_stack_weights(cfg: WukongConfig, seed: int, affine: str = "identity",
+                       num_layers: Optional[int] = None) -> List[HostLayerWeights]:
+    l = cfg.num_layers if num_layers is None else num_layers
+    return [make_layer_weights(cfg.name, i, cfg.layers[i], cfg.dtype, seed, affine) for i in range(l)]
+
+
+def feature_scales(cfg: WukongConfig, seed: int) -> np.ndarray:
+    """Per-feature scale s_i = 10**U(-1,1), shared by all examples (float32 [n])."""
+    n = cfg.layers[0].n
+    u = _fill(seed, f"{cfg.name}/x_feature_scale", n, "uniform")
+    return np.power(np.float32(10.0), u * np.float32(2.0) - np.float32(1.0)).astype(np.float32)
+
+
+def make_input(cfg: WukongConfig, seed: int, batch: Optional[int] = None,
+               first_example: int = 0) -> np.ndarray:
+    """X of shape [batch, n, d] in the config's storage type.
+
+    Examples are drawn independently per index, so make_input(..., batch=b,
+    first_example=s) equals rows s..s+b of the full batch: a subset can be
+    regenerated without drawing the whole batch.
+    """
+    s0 = cfg.layers[0]
+    n, d = s0.n, s0.d
+    b = cfg.batch if batch is None else batch
+    per = n * d
+    x = np.empty((b, n, d), dtype=np.float32)
+    # examples are keyed in blocks of EX_BLOCK so any sub-range can be regenerated
+    ex_block = max(1, CHUNK // per)
+    blk0 = first_example // ex_block
+    blk1 = (first_example + b + ex_block - 1) // ex_block
+
+    def work(blk):
+        lo_ex = blk * ex_block
+        vals = np.empty(ex_block * per, dtype=np.float32)
+        g = np.random.Generator(np.random.Philox(key=stream_key(seed, f"{cfg.name}/x#{blk}")))
+        g.standard_normal(dtype=np.float32, out=vals)
+        vals = vals.reshape(ex_block, n, d)
+        a = max(lo_ex, first_example)
+        z = min(lo_ex + ex_block, first_example + b)
+        if a < z:
+            x[a - first_example:z - first_example] = vals[a - lo_ex:z - lo_ex]
+
+    blocks = list(range(blk0, blk1))
+    if len(blocks) <= 1:
+        for blk in blocks:
+            work(blk)
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(work, blocks))
+    if cfg.x_dist == "feature_scaled_units":
+        # each row is unit_width-wide units side by side; one scale per feature row
+        assert cfg.unit_width > 0 and d % cfg.unit_width == 0
+        x *= feature_scales(cfg, seed)[None, :, None]
+    elif cfg.x_dist != "normal":
+        raise ValueError(cfg.x_dist)
+    return _store(x, cfg.dtype)
