@@ -1,0 +1,183 @@
+/*
+ * wukong.h -- C ABI of libwukong: forward pass of the stacked Wukong
+ * interaction layer on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation (Wukong paper, section 2.2 "Wukong", as summarised on the
+ * xdnf.cn repost of the Zhihu article; the page's equations were lost in
+ * extraction, so this follows its prose):  a Wukong layer runs a
+ * Factorization Machine Block (FMB) and a Linear Compress Block (LCB) side by
+ * side on one example's feature matrix X (n embeddings of width d), then
+ * concatenates their outputs, adds the residual X and applies a LayerNorm.
+ * The FMB "first compresses the number of features to k, then computes the
+ * interaction" and ends in an MLP whose output is an n_F x d matrix; the LCB
+ * is a weight matrix W_L mapping the n input embeddings to n_L outputs.
+ * Section 2.3 of the same page lists the scaling knobs: the number of layers
+ * l, n_F, n_L, k and the MLP's depth and widths.  WHALE's non-sequential
+ * branch (WHALE summary, section 2.1 "Wukong module") applies the same
+ * stacked FMB + LCB layer by layer, which is why a single layer is exposed
+ * as well as the stack.
+ *
+ * Per example and layer, with row-major tensors:
+ *   Z  = Phi X                (k x d)      Phi is a learned [k, n] weight
+ *   F  = X Z^T                (n x k)      = (X X^T) Phi^T, the compressed FM
+ *   Fn = LN(vec(F); gamma_fm, beta_fm)     over all n*k values, row-major
+ *   h_t = ReLU(W_t h_{t-1} + b_t), t < T;  h_T = W_T h_{T-1} + b_T;  h_0 = Fn
+ *   M  = reshape(h_T, n_F x d)             row-major
+ *   Lc = W_L X                (n_L x d)
+ *   Y[r] = LN([M; Lc][r] + X[r]; gamma_out, beta_out)   each row over d
+ * LayerNorm uses the biased variance and the caller's epsilon.  n_F + n_L
+ * must equal n (the residual adds X row by row).
+ *
+ * Conventions for every entry point
+ *   - Tensors are dense, row-major, last dimension contiguous, in device
+ *     memory, owned by the caller.  The library never allocates device
+ *     memory, frees it or keeps a pointer past the call.
+ *   - Every tensor of a layer has the layer's dtype (WK_F32 or WK_BF16).
+ *     WK_BF16 layers compute with fp32 accumulation and fp32 LayerNorm
+ *     statistics; the tensors they store in bf16 are Z (as a product
+ *     operand), Fn, every h_t, M and Y.  Lc is not rounded: the LCB rows of
+ *     Y are finished from fp32 values.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without waiting.  Nothing synchronises with the
+ *     host.  A fault inside a kernel surfaces at the caller's next sync.
+ *   - All arguments are checked before anything is launched: a call that
+ *     returns an error has launched nothing.
+ *   - Device pointers must be 16-byte aligned.  x and y must not overlap
+ *     each other or the workspace.
+ *   - Calls are thread-safe; concurrent calls need distinct workspaces and
+ *     outputs.
+ */
+#ifndef WUKONG_H_
+#define WUKONG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define WUKONG_ABI_VERSION 1
+
+typedef enum {
+  WK_OK = 0,
+  WK_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad dimension, aliasing */
+  WK_ERR_UNSUPPORTED = 2, /* valid request outside the compiled kernel set   */
+  WK_ERR_WORKSPACE = 3,   /* workspace smaller than the *_workspace_size     */
+  WK_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed      */
+} wk_status;
+
+typedef enum { WK_F32 = 0, WK_BF16 = 1 } wk_dtype;
+
+/* Shape of one layer.  mlp_dims is a HOST array of num_linear + 1 widths
+ * [n*k, m_1, ..., n_f*d]; the FMB MLP has num_linear Linear layers.
+ * WK_BF16 additionally needs d % 16 == 0, n % 8 == 0, k % 4 == 0 and every
+ * MLP width % 8 == 0 (else WK_ERR_UNSUPPORTED).  ln_eps >= 0 is the
+ * LayerNorm epsilon of both LayerNorms (1e-5 is the usual value). */
+typedef struct {
+  int32_t n, d, k, n_f, n_l;
+  int32_t num_linear;
+  const int32_t* mlp_dims;
+  float ln_eps;
+  int32_t dtype; /* wk_dtype */
+} wk_layer_desc;
+
+/* Device pointers to one layer's parameters (layer dtype, row-major).
+ * mlp_w and mlp_b are HOST arrays of num_linear device pointers;
+ * W_t is [m_t, m_{t-1}] (output-major, as torch.nn.Linear stores it) and
+ * b_t is [m_t].  mlp_b itself, any of its entries, and any gamma/beta may
+ * be NULL, meaning a zero bias, gamma = 1 or beta = 0. */
+typedef struct {
+  const void* phi;          /* [k, n]   */
+  const void* w_l;          /* [n_l, n] */
+  const void* fm_ln_gamma;  /* [n*k]    */
+  const void* fm_ln_beta;   /* [n*k]    */
+  const void* const* mlp_w; /* host array [num_linear] of device [m_t, m_{t-1}] */
+  const void* const* mlp_b; /* host array [num_linear] of device [m_t], or NULL */
+  const void* out_ln_gamma; /* [d]      */
+  const void* out_ln_beta;  /* [d]      */
+} wk_layer_weights;
+
+/* Version of this header the library was built from (WUKONG_ABI_VERSION). */
+int32_t wukong_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char* wukong_status_string(int32_t status);
+
+/* Bytes of device workspace wukong_layer_forward needs for `batch`
+ * examples, or 0 if desc is invalid or unsupported. */
+size_t wukong_layer_workspace_size(const wk_layer_desc* desc, int64_t batch);
+
+/* One Wukong layer: y[b] = layer(x[b]) for b < batch.
+ *   x [batch, n, d] and y [batch, n, d] in the layer dtype.
+ *   workspace: device scratch of at least wukong_layer_workspace_size bytes;
+ *   its contents on return are the layer's intermediates laid out as
+ *   wukong_layer_workspace_layout describes.  batch == 0 is a no-op. */
+int32_t wukong_layer_forward(const wk_layer_desc* desc, const wk_layer_weights* weights,
+                             int64_t batch, const void* x, void* y, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Byte offsets, within a layer's workspace, of the intermediates a
+ * wukong_layer_forward call leaves there (for per-kernel checks):
+ *   fn      [batch, n*k]       the normalised interaction Fn
+ *   hidden  [batch, m_t] for t = 1..num_linear-1: hidden[t-1]; the hidden
+ *           activations alternate between two buffers, so only the last two
+ *           survive (offset -1 marks an overwritten one)
+ *   m       [batch, n_f*d]     the last MLP output M
+ * Returns WK_OK, or an error as wukong_layer_forward would for desc/batch. */
+typedef struct {
+  int64_t fn;
+  int64_t m;
+  int32_t num_hidden;
+  int64_t hidden[8]; /* first min(num_hidden, 8) entries are meaningful */
+} wk_workspace_layout;
+int32_t wukong_layer_workspace_layout(const wk_layer_desc* desc, int64_t batch,
+                                      wk_workspace_layout* out);
+
+/* Bytes of workspace wukong_stack_forward needs (0 if invalid). */
+size_t wukong_stack_workspace_size(int32_t num_layers, const wk_layer_desc* descs,
+                                   int64_t batch);
+
+/* l stacked Wukong layers: layer i reads layer i-1's output (Wukong paper,
+ * section 2.3: l is the depth of the interaction stack).  descs and weights
+ * are HOST arrays of num_layers entries; every layer must keep n and d
+ * (n_F + n_L = n) and share one dtype.  x [batch, n, d] in, y [batch, n, d]
+ * out; intermediate layer outputs live in the workspace. */
+int32_t wukong_stack_forward(int32_t num_layers, const wk_layer_desc* descs,
+                             const wk_layer_weights* weights, int64_t batch, const void* x,
+                             void* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------- tracing
+ * Per-kernel timing for benchmarks: a trace owns a pool of HIP events.
+ * wukong_stack_forward_traced behaves exactly like wukong_stack_forward and
+ * additionally records an event before and after each kernel it launches
+ * (on `stream`).  Records are appended until the pool is full; later
+ * launches go unrecorded.  Kernel kinds: */
+enum {
+  WK_KERNEL_FMB_LCB = 1,    /* compress + interaction + LN(F) + LCB rows of Y */
+  WK_KERNEL_MLP_LINEAR = 2, /* one FMB-MLP Linear (+bias, +ReLU)             */
+  WK_KERNEL_RESIDUAL_LN = 3 /* FMB rows of Y: LN(M + X)                      */
+};
+typedef struct wk_trace wk_trace;
+/* Creates a trace able to hold `capacity` launch records (creates HIP events
+ * on the current device). */
+int32_t wukong_trace_create(int32_t capacity, wk_trace** out);
+int32_t wukong_trace_destroy(wk_trace* trace);
+/* Forgets all records (events are reused). */
+int32_t wukong_trace_reset(wk_trace* trace);
+int32_t wukong_trace_count(const wk_trace* trace);
+/* Record i: kernel kind, layer index, index within the layer (the Linear
+ * number for WK_KERNEL_MLP_LINEAR, else 0), launch geometry (workgroups)
+ * and elapsed milliseconds.  Waits for record i's stop event. */
+int32_t wukong_trace_get(wk_trace* trace, int32_t i, int32_t* kind, int32_t* layer,
+                         int32_t* index, int64_t* workgroups, float* ms);
+int32_t wukong_stack_forward_traced(int32_t num_layers, const wk_layer_desc* descs,
+                                    const wk_layer_weights* weights, int64_t batch,
+                                    const void* x, void* y, void* workspace,
+                                    size_t workspace_bytes, void* stream, wk_trace* trace);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WUKONG_H_ */

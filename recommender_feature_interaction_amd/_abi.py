@@ -1,0 +1,326 @@
+"""ctypes binding of libwukong's C ABI (include/wukong.h).
+
+Argument marshalling only: torch supplies device memory and the stream, every
+step of the layer runs in the HIP kernels behind the C ABI.  There is no CPU
+fallback: if libwukong.so is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwukong.so")
+_lib = None
+
+F32, BF16 = 0, 1
+WK_OK, WK_ERR_INVALID_ARG, WK_ERR_UNSUPPORTED, WK_ERR_WORKSPACE, WK_ERR_HIP = 0, 1, 2, 3, 4
+KERNEL_FMB_LCB, KERNEL_MLP_LINEAR, KERNEL_RESIDUAL_LN = 1, 2, 3
+KERNEL_NAMES = {KERNEL_FMB_LCB: "fmb_lcb", KERNEL_MLP_LINEAR: "mlp_linear", KERNEL_RESIDUAL_LN: "residual_ln"}
+ABI_VERSION = 1
+
+
+class wk_layer_desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("d", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("n_f", ctypes.c_int32), ("n_l", ctypes.c_int32), ("num_linear", ctypes.c_int32),
+                ("mlp_dims", ctypes.POINTER(ctypes.c_int32)), ("ln_eps", ctypes.c_float),
+                ("dtype", ctypes.c_int32)]
+
+
+class wk_layer_weights(ctypes.Structure):
+    _fields_ = [("phi", ctypes.c_void_p), ("w_l", ctypes.c_void_p),
+                ("fm_ln_gamma", ctypes.c_void_p), ("fm_ln_beta", ctypes.c_void_p),
+                ("mlp_w", ctypes.POINTER(ctypes.c_void_p)), ("mlp_b", ctypes.POINTER(ctypes.c_void_p)),
+                ("out_ln_gamma", ctypes.c_void_p), ("out_ln_beta", ctypes.c_void_p)]
+
+
+class wk_workspace_layout(ctypes.Structure):
+    _fields_ = [("fn", ctypes.c_int64), ("m", ctypes.c_int64), ("num_hidden", ctypes.c_int32),
+                ("hidden", ctypes.c_int64 * 8)]
+
+
+# (name, restype, argtypes) of every exported symbol
+_SIGNATURES = [
+    ("wukong_abi_version", ctypes.c_int32, []),
+    ("wukong_status_string", ctypes.c_char_p, [ctypes.c_int32]),
+    ("wukong_layer_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_layer_desc), ctypes.c_int64]),
+    ("wukong_layer_workspace_layout", ctypes.c_int32,
+     [ctypes.POINTER(wk_layer_desc), ctypes.c_int64, ctypes.POINTER(wk_workspace_layout)]),
+    ("wukong_layer_forward", ctypes.c_int32,
+     [ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_stack_workspace_size", ctypes.c_size_t,
+     [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.c_int64]),
+    ("wukong_stack_forward", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_trace_create", ctypes.c_int32, [ctypes.c_int32, ctypes.POINTER(ctypes.c_void_p)]),
+    ("wukong_trace_destroy", ctypes.c_int32, [ctypes.c_void_p]),
+    ("wukong_trace_reset", ctypes.c_int32, [ctypes.c_void_p]),
+    ("wukong_trace_count", ctypes.c_int32, [ctypes.c_void_p]),
+    ("wukong_trace_get", ctypes.c_int32,
+     [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32),
+      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_float)]),
+    ("wukong_stack_forward_traced", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+]
+EXPORTED_SYMBOLS = tuple(s[0] for s in _SIGNATURES)
+
+
+class WukongError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libwukong.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m recommender_feature_interaction_amd.build` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(_LIB_PATH)
+    for name, res, args in _SIGNATURES:
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if lib.wukong_abi_version() != ABI_VERSION:
+        raise RuntimeError("libwukong.so ABI version mismatch; rebuild it")
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().wukong_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != WK_OK:
+        raise WukongError(status, where)
+
+
+# ------------------------------------------------------------------ layers
+@dataclass(frozen=True)
+class LayerSpec:
+    n: int
+    d: int
+    k: int
+    n_f: int
+    n_l: int
+    mlp: Tuple[int, ...]
+    eps: float = 1e-5
+    dtype: str = "bf16"  # "bf16" or "f32"
+
+    @property
+    def wk_dtype(self) -> int:
+        return BF16 if self.dtype == "bf16" else F32
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def make_desc(self) -> Tuple[wk_layer_desc, object]:
+        dims = (ctypes.c_int32 * len(self.mlp))(*self.mlp)
+        desc = wk_layer_desc(self.n, self.d, self.k, self.n_f, self.n_l, len(self.mlp) - 1,
+                             ctypes.cast(dims, ctypes.POINTER(ctypes.c_int32)), self.eps, self.wk_dtype)
+        return desc, dims
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def to_device(a, dtype: str, device) -> torch.Tensor:
+    """Host array (float32, or uint16 bf16 bit patterns) or tensor -> contiguous device tensor."""
+    if isinstance(a, torch.Tensor):
+        want = torch.bfloat16 if dtype == "bf16" else torch.float32
+        if a.dtype != want:
+            raise TypeError(f"expected {want}, got {a.dtype}")
+        return a.to(device).contiguous()
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        if a.dtype != np.uint16:
+            raise TypeError("bf16 host data must be uint16 bit patterns")
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    if a.dtype != np.float32:
+        raise TypeError("f32 host data must be float32")
+    return torch.from_numpy(a).to(device)
+
+
+class DeviceLayer:
+    """One layer's parameters resident in device memory, plus its C descriptors."""
+
+    def __init__(self, spec: LayerSpec, phi, w_l, mlp_w: Sequence, mlp_b: Optional[Sequence] = None,
+                 fm_gamma=None, fm_beta=None, out_gamma=None, out_beta=None, device="cuda"):
+        dt = spec.dtype
+        T = len(spec.mlp) - 1
+        if len(mlp_w) != T or (mlp_b is not None and len(mlp_b) != T):
+            raise ValueError("mlp_w / mlp_b must have one entry per Linear")
+        cv = lambda a: None if a is None else to_device(a, dt, device)  # noqa: E731
+        self.spec = spec
+        self.phi, self.w_l = cv(phi), cv(w_l)
+        self.fm_gamma, self.fm_beta = cv(fm_gamma), cv(fm_beta)
+        self.out_gamma, self.out_beta = cv(out_gamma), cv(out_beta)
+        self.mlp_w = [cv(w) for w in mlp_w]
+        self.mlp_b = None if mlp_b is None else [cv(b) for b in mlp_b]
+        n, d, k = spec.n, spec.d, spec.k
+        expect = [("phi", self.phi, (k, n)), ("w_l", self.w_l, (spec.n_l, n)),
+                  ("fm_gamma", self.fm_gamma, (n * k,)), ("fm_beta", self.fm_beta, (n * k,)),
+                  ("out_gamma", self.out_gamma, (d,)), ("out_beta", self.out_beta, (d,))]
+        for t in range(T):
+            expect.append((f"mlp_w[{t}]", self.mlp_w[t], (spec.mlp[t + 1], spec.mlp[t])))
+            if self.mlp_b is not None:
+                expect.append((f"mlp_b[{t}]", self.mlp_b[t], (spec.mlp[t + 1],)))
+        for name, t, shape in expect:
+            if t is not None and tuple(t.shape) != shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        self.desc, self._dims = spec.make_desc()
+        self._w_ptrs = (ctypes.c_void_p * T)(*[w.data_ptr() for w in self.mlp_w])
+        self._b_ptrs = None if self.mlp_b is None else (ctypes.c_void_p * T)(*[_ptr(b) for b in self.mlp_b])
+        self.weights = wk_layer_weights(
+            _ptr(self.phi), _ptr(self.w_l), _ptr(self.fm_gamma), _ptr(self.fm_beta),
+            ctypes.cast(self._w_ptrs, ctypes.POINTER(ctypes.c_void_p)),
+            None if self._b_ptrs is None else ctypes.cast(self._b_ptrs, ctypes.POINTER(ctypes.c_void_p)),
+            _ptr(self.out_gamma), _ptr(self.out_beta))
+
+    @classmethod
+    def from_host(cls, spec: LayerSpec, hw, device="cuda") -> "DeviceLayer":
+        """From an object with phi, w_l, fm_gamma, fm_beta, mlp_w, mlp_b, out_gamma, out_beta."""
+        return cls(spec, hw.phi, hw.w_l, hw.mlp_w, hw.mlp_b, hw.fm_gamma, hw.fm_beta,
+                   hw.out_gamma, hw.out_beta, device=device)
+
+    def nbytes(self) -> int:
+        ts = [self.phi, self.w_l, self.fm_gamma, self.fm_beta, self.out_gamma, self.out_beta, *self.mlp_w]
+        ts += self.mlp_b or []
+        return int(sum(t.numel() * t.element_size() for t in ts if t is not None))
+
+
+def _stream_handle(stream) -> Optional[int]:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _descs(layers: Sequence[DeviceLayer]):
+    descs = (wk_layer_desc * len(layers))(*[l.desc for l in layers])
+    ws = (wk_layer_weights * len(layers))(*[l.weights for l in layers])
+    return descs, ws
+
+
+def layer_workspace_size(spec: LayerSpec, batch: int) -> int:
+    desc, _dims = spec.make_desc()
+    return int(load_library().wukong_layer_workspace_size(ctypes.byref(desc), batch))
+
+
+def stack_workspace_size(specs: Sequence[LayerSpec], batch: int) -> int:
+    pairs = [s.make_desc() for s in specs]
+    descs = (wk_layer_desc * len(specs))(*[p[0] for p in pairs])
+    return int(load_library().wukong_stack_workspace_size(len(specs), descs, batch))
+
+
+def workspace_layout(spec: LayerSpec, batch: int) -> dict:
+    desc, _dims = spec.make_desc()
+    out = wk_workspace_layout()
+    _check(load_library().wukong_layer_workspace_layout(ctypes.byref(desc), batch, ctypes.byref(out)),
+           "wukong_layer_workspace_layout")
+    return {"fn": out.fn, "m": out.m,
+            "hidden": [out.hidden[i] for i in range(min(out.num_hidden, 8))]}
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _check_x(x: torch.Tensor, spec: LayerSpec) -> int:
+    if not x.is_cuda or x.dtype != spec.torch_dtype or not x.is_contiguous():
+        raise ValueError(f"x must be a contiguous {spec.torch_dtype} CUDA tensor")
+    if x.dim() != 3 or x.shape[1] != spec.n or x.shape[2] != spec.d:
+        raise ValueError(f"x must be [batch, {spec.n}, {spec.d}], got {tuple(x.shape)}")
+    return x.shape[0]
+
+
+def layer_forward(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One Wukong layer on x [batch, n, d]; returns y [batch, n, d]."""
+    lib = load_library()
+    B = _check_x(x, layer.spec)
+    y = torch.empty_like(x) if y is None else y
+    need = layer_workspace_size(layer.spec, B)
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    st = lib.wukong_layer_forward(ctypes.byref(layer.desc), ctypes.byref(layer.weights), B, x.data_ptr(),
+                                  y.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream_handle(stream))
+    _check(st, "wukong_layer_forward")
+    return y
+
+
+class Trace:
+    """Per-kernel HIP-event timing of stack_forward calls (see wukong_trace_*)."""
+
+    def __init__(self, capacity: int = 4096):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check(self._lib.wukong_trace_create(capacity, ctypes.byref(h)), "wukong_trace_create")
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def reset(self):
+        _check(self._lib.wukong_trace_reset(self._h), "wukong_trace_reset")
+
+    def records(self) -> List[dict]:
+        out = []
+        kind, layer, index = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        wgs, ms = ctypes.c_int64(), ctypes.c_float()
+        for i in range(self._lib.wukong_trace_count(self._h)):
+            _check(self._lib.wukong_trace_get(self._h, i, ctypes.byref(kind), ctypes.byref(layer),
+                                              ctypes.byref(index), ctypes.byref(wgs), ctypes.byref(ms)),
+                   "wukong_trace_get")
+            out.append({"kernel": KERNEL_NAMES.get(kind.value, str(kind.value)), "layer": layer.value,
+                        "index": index.value, "workgroups": wgs.value, "ms": ms.value})
+        return out
+
+    def close(self):
+        if self._h is not None:
+            self._lib.wukong_trace_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def stack_forward(x: torch.Tensor, layers: Sequence[DeviceLayer], y: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None,
+                  trace: Optional[Trace] = None) -> torch.Tensor:
+    """l stacked Wukong layers on x [batch, n, d]; returns y [batch, n, d]."""
+    lib = load_library()
+    B = _check_x(x, layers[0].spec)
+    y = torch.empty_like(x) if y is None else y
+    descs, ws = _descs(layers)
+    need = int(lib.wukong_stack_workspace_size(len(layers), descs, B))
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    args = (len(layers), descs, ws, B, x.data_ptr(), y.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if trace is None:
+        st = lib.wukong_stack_forward(*args)
+    else:
+        st = lib.wukong_stack_forward_traced(*args, trace.handle)
+    _check(st, "wukong_stack_forward")
+    return y

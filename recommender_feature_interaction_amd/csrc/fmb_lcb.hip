@@ -1,0 +1,390 @@
+// FMB + LCB kernel of the Wukong layer (bf16 storage, fp32 accumulation).
+//
+// One workgroup per example b.  Wukong paper, section 2.2 (xdnf.cn repost):
+// the FMB compresses the n embeddings to k before interacting them, and the
+// LCB multiplies X by W_L; both act on the same X, so one pass over X_b
+// serves both:
+//
+//   phase 1   [Z; Lc] = [Phi; W_L] X_b           ((k + n_L) x d, MFMA)
+//             X_b is streamed through LDS in chunks of MC rows, transposed
+//             on the way in so that the contraction index m is contiguous
+//             for the MFMA operand; the weight rows [Phi; W_L] are read
+//             straight from global memory (they are shared by every example
+//             and stay resident in L2).  Wave w owns the 16-row tiles
+//             w, w + NW, ... of [Phi; W_L] across the whole width d.
+//   LCB rows  Y_b[n_F + i] = LN_d(Lc[i] + X_b[n_F + i]) finished in
+//             registers: a row's d values sit in the 4 lanes l, l^16, l^32,
+//             l^48 of one wave, so its statistics are two xor-shuffles.
+//   phase 2   F_b = X_b Z_b^T (n x k, MFMA): Z_b (bf16) goes through LDS,
+//             X_b rows are re-read from global memory (an L2 hit) in the
+//             natural layout, which is the operand layout this product needs.
+//   LN(F)     mean and variance over all n*k values (wave shuffles + LDS),
+//             then Fn_b = bf16(LN(vec(F_b))) written row-major.
+//
+// MFMA used: v_mfma_f32_16x16x32_bf16 (16-row tiles keep the padding of the
+// irregular k, n_L and n small).
+#include "wk_device.h"
+#include "wk_kernels.h"
+
+namespace wk {
+
+namespace {
+
+template <int ET, int NW, int ZW, int MW, int KW, int MC>
+__global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
+  constexpr int D = 16 * ET;
+  constexpr int XT_LD = MC + 8;          // LDS row pitch of X^T (u16), padded against bank conflicts
+  constexpr int DZ = (D + 31) / 32 * 32; // d rounded up to the 32-wide K step of phase 2
+  constexpr int Z_LD = DZ + 8;
+  constexpr int NT = NW * 64;
+  constexpr int MB = MC / 8;
+  constexpr int EB = D / 8;
+  constexpr int NBLK = MB * EB;          // 8x8 transpose blocks per chunk
+  constexpr int BPT = (NBLK + NT - 1) / NT;
+  constexpr int KS = MC / 32;
+  constexpr bool EB_FAST = (EB < 8);     // narrow rows: let consecutive lanes walk along a row
+
+  extern __shared__ __align__(16) uint16_t smem[];
+  __shared__ float red[2 * NW];
+  uint16_t* XT = smem;
+  uint16_t* Zs = smem;  // reused once phase 1 is done
+
+  const int n = p.n, k = p.k, n_l = p.n_l, n_f = p.n_f;
+  const int64_t b = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const uint16_t* xb = p.x + b * (int64_t)n * D;
+  const int ZT = (k + n_l + 15) >> 4;
+
+  // ------------------------------------------------------------- phase 1
+  const uint16_t* wrow[ZW];
+#pragma unroll
+  for (int zi = 0; zi < ZW; ++zi) {
+    const int zt = wave + zi * NW;
+    const int z = zt * 16 + li;
+    const uint16_t* r = nullptr;
+    if (zt < ZT) {
+      if (z < k)
+        r = p.phi + (int64_t)z * n;
+      else if (z < k + n_l)
+        r = p.w_l + (int64_t)(z - k) * n;
+    }
+    wrow[zi] = r;
+  }
+  f32x4 acc[ZW][ET];
+#pragma unroll
+  for (int zi = 0; zi < ZW; ++zi)
+#pragma unroll
+    for (int et = 0; et < ET; ++et) acc[zi][et] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 xr[BPT][8];
+  auto load_chunk = [&](int m0) {
+#pragma unroll
+    for (int bi = 0; bi < BPT; ++bi) {
+      const int blk = tid + bi * NT;
+      const int mb = EB_FAST ? blk / EB : blk % MB;
+      const int eb = EB_FAST ? blk % EB : blk / MB;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int m = m0 + mb * 8 + r;
+        if (blk < NBLK && m < n)
+          xr[bi][r] = *reinterpret_cast<const u32x4*>(xb + (int64_t)m * D + eb * 8);
+        else
+          xr[bi][r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int bi = 0; bi < BPT; ++bi) {
+      const int blk = tid + bi * NT;
+      if (blk < NBLK) {
+        const int mb = EB_FAST ? blk / EB : blk % MB;
+        const int eb = EB_FAST ? blk % EB : blk / MB;
+        // 8x8 transpose: output row e = 8eb + c holds the 8 values of column c.
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = xr[bi][2 * q][c >> 1];
+            const uint32_t hi = xr[bi][2 * q + 1][c >> 1];
+            o[q] = (c & 1) ? pack_hi(lo, hi) : pack_lo(lo, hi);
+          }
+          *reinterpret_cast<u32x4*>(XT + (eb * 8 + c) * XT_LD + mb * 8) = o;
+        }
+      }
+    }
+  };
+
+  const int nchunks = (n + MC - 1) / MC;
+  load_chunk(0);
+  for (int c = 0; c < nchunks; ++c) {
+    const int m0 = c * MC;
+    u32x4 wf[ZW][KS];
+#pragma unroll
+    for (int zi = 0; zi < ZW; ++zi)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int mk = m0 + ks * 32 + lg * 8;
+        if (wrow[zi] != nullptr && mk < n)
+          wf[zi][ks] = *reinterpret_cast<const u32x4*>(wrow[zi] + mk);
+        else
+          wf[zi][ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+    __syncthreads();  // everyone is done reading the previous chunk
+    store_chunk();
+    if (c + 1 < nchunks) load_chunk(m0 + MC);
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (m0 + ks * 32 < n) {
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          const u32x4 a = *reinterpret_cast<const u32x4*>(XT + (et * 16 + li) * XT_LD + ks * 32 + lg * 8);
+#pragma unroll
+          for (int zi = 0; zi < ZW; ++zi)
+            if (wave + zi * NW < ZT) acc[zi][et] = mfma16x16x32(a, wf[zi][ks], acc[zi][et]);
+        }
+      }
+    }
+  }
+  __syncthreads();  // X^T no longer needed: its LDS becomes Z
+
+  // Z rows -> LDS as bf16 (the phase-2 operand); padding rows/columns are zero.
+  for (int i = tid; i < 16 * KW * Z_LD / 8; i += NT)
+    reinterpret_cast<u32x4*>(Zs)[i] = u32x4{0u, 0u, 0u, 0u};
+  __syncthreads();
+
+  const uint16_t* og = p.out_gamma;
+  const uint16_t* ob = p.out_beta;
+  const float inv_d = 1.0f / static_cast<float>(D);
+#pragma unroll
+  for (int zi = 0; zi < ZW; ++zi) {
+    const int zt = wave + zi * NW;
+    if (zt >= ZT) continue;  // wave-uniform
+    const int z = zt * 16 + li;
+    if (z < k) {
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        u32x2 v;
+        v[0] = pack_bf16x2(acc[zi][et][0], acc[zi][et][1]);
+        v[1] = pack_bf16x2(acc[zi][et][2], acc[zi][et][3]);
+        *reinterpret_cast<u32x2*>(Zs + z * Z_LD + et * 16 + lg * 4) = v;
+      }
+    }
+    // LCB rows of this tile: Y[n_F + i] = LN_d(Lc[i] + X[n_F + i])
+    if (zt * 16 + 15 >= k && zt * 16 < k + n_l) {  // wave-uniform
+      const bool is_l = (z >= k) && (z < k + n_l);
+      const int row = n_f + (z - k);
+      float v[ET][4];
+      float s = 0.f;
+#pragma unroll
+      for (int et = 0; et < ET; ++et) {
+        u32x2 xv = u32x2{0u, 0u};
+        if (is_l) xv = *reinterpret_cast<const u32x2*>(xb + (int64_t)row * D + et * 16 + lg * 4);
+        v[et][0] = acc[zi][et][0] + bf16lo(xv[0]);
+        v[et][1] = acc[zi][et][1] + bf16hi(xv[0]);
+        v[et][2] = acc[zi][et][2] + bf16lo(xv[1]);
+        v[et][3] = acc[zi][et][3] + bf16hi(xv[1]);
+        s += (v[et][0] + v[et][1]) + (v[et][2] + v[et][3]);
+      }
+      s = xor_sum<16>(s);
+      const float mean = s * inv_d;
+      float q = 0.f;
+#pragma unroll
+      for (int et = 0; et < ET; ++et)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float dv = v[et][t] - mean;
+          q += dv * dv;
+        }
+      q = xor_sum<16>(q);
+      const float rstd = rsqrtf(q * inv_d + p.eps);
+      if (is_l) {
+        uint16_t* yrow = p.y + (b * n + row) * (int64_t)D;
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          const int e = et * 16 + lg * 4;
+          float gm[4] = {1.f, 1.f, 1.f, 1.f}, bt[4] = {0.f, 0.f, 0.f, 0.f};
+          if (og) {
+            const u32x2 g2 = *reinterpret_cast<const u32x2*>(og + e);
+            gm[0] = bf16lo(g2[0]); gm[1] = bf16hi(g2[0]); gm[2] = bf16lo(g2[1]); gm[3] = bf16hi(g2[1]);
+          }
+          if (ob) {
+            const u32x2 b2 = *reinterpret_cast<const u32x2*>(ob + e);
+            bt[0] = bf16lo(b2[0]); bt[1] = bf16hi(b2[0]); bt[2] = bf16lo(b2[1]); bt[3] = bf16hi(b2[1]);
+          }
+          u32x2 o;
+          o[0] = pack_bf16x2((v[et][0] - mean) * rstd * gm[0] + bt[0], (v[et][1] - mean) * rstd * gm[1] + bt[1]);
+          o[1] = pack_bf16x2((v[et][2] - mean) * rstd * gm[2] + bt[2], (v[et][3] - mean) * rstd * gm[3] + bt[3]);
+          *reinterpret_cast<u32x2*>(yrow + e) = o;
+        }
+      }
+    }
+  }
+  __syncthreads();  // Z complete in LDS
+
+  // ------------------------------------------------------------- phase 2
+  const int MT = (n + 15) >> 4;
+  const int KT = (k + 15) >> 4;
+  f32x4 facc[MW][KW];
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+    for (int jt = 0; jt < KW; ++jt) facc[mi][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi) {
+    const int mt = wave + mi * NW;
+    if (mt < MT) {  // wave-uniform
+      const int m = mt * 16 + li;
+#pragma unroll
+      for (int ks = 0; ks < DZ / 32; ++ks) {
+        const int e0 = ks * 32 + lg * 8;
+        u32x4 xf = u32x4{0u, 0u, 0u, 0u};
+        if (m < n && e0 < D) xf = *reinterpret_cast<const u32x4*>(xb + (int64_t)m * D + e0);
+#pragma unroll
+        for (int jt = 0; jt < KW; ++jt) {
+          if (jt < KT) {
+            const u32x4 zf = *reinterpret_cast<const u32x4*>(Zs + (jt * 16 + li) * Z_LD + e0);
+            facc[mi][jt] = mfma16x16x32(zf, xf, facc[mi][jt]);
+          }
+        }
+      }
+    }
+  }
+
+  // LN over the n*k values of F (facc[mi][jt][t] = F[16mt + li][16jt + 4lg + t])
+  float s = 0.f;
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+    for (int jt = 0; jt < KW; ++jt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = (wave + mi * NW) * 16 + li;
+        const int j = jt * 16 + lg * 4 + t;
+        if (m < n && j < k) s += facc[mi][jt][t];
+      }
+  s = xor_sum<1>(s);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) tot += red[w];
+  const float inv_nk = 1.0f / static_cast<float>(n * k);
+  const float mean = tot * inv_nk;
+  float q = 0.f;
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+    for (int jt = 0; jt < KW; ++jt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int m = (wave + mi * NW) * 16 + li;
+        const int j = jt * 16 + lg * 4 + t;
+        if (m < n && j < k) {
+          const float dv = facc[mi][jt][t] - mean;
+          q += dv * dv;
+        }
+      }
+  q = xor_sum<1>(q);
+  if (lane == 0) red[NW + wave] = q;
+  __syncthreads();
+  float qt = 0.f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) qt += red[NW + w];
+  const float rstd = rsqrtf(qt * inv_nk + p.eps);
+
+  uint16_t* fnb = p.fn + b * (int64_t)n * k;
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi)
+#pragma unroll
+    for (int jt = 0; jt < KW; ++jt) {
+      const int m = (wave + mi * NW) * 16 + li;
+      const int j0 = jt * 16 + lg * 4;
+      if (m < n && j0 < k) {  // k % 4 == 0: the 4 values j0..j0+3 are all valid
+        const int idx = m * k + j0;
+        float gm[4] = {1.f, 1.f, 1.f, 1.f}, bt[4] = {0.f, 0.f, 0.f, 0.f};
+        if (p.fm_gamma) {
+          const u32x2 g2 = *reinterpret_cast<const u32x2*>(p.fm_gamma + idx);
+          gm[0] = bf16lo(g2[0]); gm[1] = bf16hi(g2[0]); gm[2] = bf16lo(g2[1]); gm[3] = bf16hi(g2[1]);
+        }
+        if (p.fm_beta) {
+          const u32x2 b2 = *reinterpret_cast<const u32x2*>(p.fm_beta + idx);
+          bt[0] = bf16lo(b2[0]); bt[1] = bf16hi(b2[0]); bt[2] = bf16lo(b2[1]); bt[3] = bf16hi(b2[1]);
+        }
+        const f32x4 f = facc[mi][jt];
+        u32x2 o;
+        o[0] = pack_bf16x2((f[0] - mean) * rstd * gm[0] + bt[0], (f[1] - mean) * rstd * gm[1] + bt[1]);
+        o[1] = pack_bf16x2((f[2] - mean) * rstd * gm[2] + bt[2], (f[3] - mean) * rstd * gm[3] + bt[3]);
+        *reinterpret_cast<u32x2*>(fnb + idx) = o;
+      }
+    }
+}
+
+template <int ET, int NW, int ZW, int MW, int KW, int MC>
+size_t lds_bytes() {
+  constexpr int D = 16 * ET;
+  constexpr int DZ = (D + 31) / 32 * 32;
+  const size_t xt = (size_t)D * (MC + 8) * 2;
+  const size_t zs = (size_t)16 * KW * (DZ + 8) * 2;
+  return xt > zs ? xt : zs;
+}
+
+struct FmbLcbVariant {
+  int et, nw, zw, mw, kw, mc;
+  void (*kernel)(FmbLcbArgs);
+  size_t lds;
+};
+
+#define WK_FMB_VARIANT(ET, NW, ZW, MW, KW, MC)                                   \
+  FmbLcbVariant {                                                                \
+    ET, NW, ZW, MW, KW, MC, fmb_lcb_bf16_kernel<ET, NW, ZW, MW, KW, MC>,         \
+        lds_bytes<ET, NW, ZW, MW, KW, MC>()                                      \
+  }
+
+// Tight variants for the measured shapes first, then general fallbacks.
+const FmbLcbVariant kVariants[] = {
+    WK_FMB_VARIANT(10, 4, 2, 2, 2, 64),   // n=128, d=160, k=32, n_L=64
+    WK_FMB_VARIANT(10, 4, 3, 4, 3, 64),   // n=256, d=160, k=48, n_L=128
+    WK_FMB_VARIANT(10, 8, 3, 4, 6, 64),   // n=512, d=160, k=96, n_L=256
+    WK_FMB_VARIANT(2, 8, 3, 6, 2, 256),   // n=720, d=32,  k=24, n_L=360
+    WK_FMB_VARIANT(1, 4, 4, 8, 4, 256),   // general fallbacks: d = 16
+    WK_FMB_VARIANT(2, 4, 4, 8, 4, 256),   // d = 32
+    WK_FMB_VARIANT(3, 4, 4, 8, 4, 128),   // d = 48
+    WK_FMB_VARIANT(4, 4, 4, 8, 4, 128),   // d = 64
+    WK_FMB_VARIANT(8, 4, 3, 8, 4, 64),    // d = 128
+    WK_FMB_VARIANT(10, 4, 3, 8, 4, 64),   // d = 160
+    WK_FMB_VARIANT(10, 8, 3, 4, 8, 64),   // d = 160, larger n / k
+};
+
+const FmbLcbVariant* pick(int n, int d, int k, int n_l) {
+  if (d % 16 != 0) return nullptr;
+  const int et = d / 16;
+  const int zt = (k + n_l + 15) / 16, mt = (n + 15) / 16, kt = (k + 15) / 16;
+  for (const auto& v : kVariants) {
+    if (v.et != et) continue;
+    if ((zt + v.nw - 1) / v.nw > v.zw) continue;
+    if ((mt + v.nw - 1) / v.nw > v.mw) continue;
+    if (kt > v.kw) continue;
+    return &v;
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l) { return pick(n, d, k, n_l) != nullptr; }
+
+hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
+                               int64_t* workgroups) {
+  const FmbLcbVariant* v = pick(a.n, a.d, a.k, a.n_l);
+  if (!v) return hipErrorInvalidValue;
+  if (workgroups) *workgroups = batch;
+  if (batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(v->kernel, dim3((unsigned)batch), dim3(v->nw * 64), v->lds, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace wk

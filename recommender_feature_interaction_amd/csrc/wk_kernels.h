@@ -1,0 +1,74 @@
+// Internal launcher interface between the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wk {
+
+// FMB + LCB (see fmb_lcb.hip / fmb_lcb_f32.hip).  Element type: uint16_t
+// bf16 bits for the bf16 kernel, float for the fp32 kernel (void* here).
+struct FmbLcbArgs {
+  const uint16_t* x;         // [B, n, d]
+  const uint16_t* phi;       // [k, n]
+  const uint16_t* w_l;       // [n_l, n]
+  const uint16_t* fm_gamma;  // [n*k] or null
+  const uint16_t* fm_beta;   // [n*k] or null
+  const uint16_t* out_gamma; // [d] or null
+  const uint16_t* out_beta;  // [d] or null
+  uint16_t* fn;              // [B, n*k]
+  uint16_t* y;               // [B, n, d]: rows n_f..n-1 are written
+  int n, d, k, n_f, n_l;
+  float eps;
+};
+bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l);
+hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
+                               int64_t* workgroups);
+
+struct FmbLcbF32Args {
+  const float* x;
+  const float* phi;
+  const float* w_l;
+  const float* fm_gamma;
+  const float* fm_beta;
+  const float* out_gamma;
+  const float* out_beta;
+  float* fn;
+  float* y;
+  int n, d, k, n_f, n_l;
+  float eps;
+};
+bool fmb_lcb_f32_supported(int n, int d, int k, int n_l);
+hipError_t launch_fmb_lcb_f32(const FmbLcbF32Args& a, int64_t batch, hipStream_t stream,
+                              int64_t* workgroups);
+
+// One FMB-MLP Linear: C[M, N] = act(A[M, K] W[N, K]^T + bias[N]).
+struct LinearArgs {
+  const void* a;
+  const void* w;
+  const void* bias;  // or null
+  void* c;
+  int64_t M;
+  int N, K;
+  int relu;
+};
+bool linear_bf16_supported(int64_t M, int N, int K);
+hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);
+hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);
+
+// FMB rows of the layer output: Y[b, r] = LN_d(M[b, r] + X[b, r]) for r < n_f.
+struct ResidLnArgs {
+  const void* m;  // [B, n_f, d]
+  const void* x;  // [B, n, d]
+  const void* gamma;
+  const void* beta;
+  void* y;        // [B, n, d]
+  int64_t batch;
+  int n, d, n_f;
+  float eps;
+};
+bool resid_ln_bf16_supported(int d);
+hipError_t launch_resid_ln_bf16(const ResidLnArgs& a, hipStream_t stream, int64_t* workgroups);
+hipError_t launch_resid_ln_f32(const ResidLnArgs& a, hipStream_t stream, int64_t* workgroups);
+
+}  // namespace wk

@@ -1,0 +1,391 @@
+// C ABI of libwukong (declared in include/wukong.h): argument checks,
+// workspace planning and the launch sequence of a Wukong layer and stack.
+//
+// Per layer (Wukong paper, section 2.2, xdnf.cn repost), on one stream:
+//   1. FMB+LCB kernel: X -> Fn (workspace) and the LCB rows of Y
+//   2. one MLP Linear per FMB-MLP layer: Fn -> h_1 -> ... -> M (workspace),
+//      bias + ReLU fused, no ReLU after the last
+//   3. residual LayerNorm of the FMB rows: (M, X) -> rows 0..n_F-1 of Y
+// A stack (section 2.3: l layers) chains layers through two ping-pong
+// buffers in the workspace; the last layer writes y.  No host sync anywhere.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "wk_kernels.h"
+#include "wukong.h"
+
+struct wk_trace {
+  int device = 0;
+  int capacity = 0;
+  int count = 0;
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int32_t> kind, layer, index;
+  std::vector<int64_t> wgs;
+};
+
+namespace {
+
+constexpr int kMaxLinear = 64;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+size_t esize(int32_t dtype) { return dtype == WK_BF16 ? 2 : 4; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool overlap(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return an > 0 && bn > 0 && x < y + bn && y < x + an;
+}
+
+int32_t check_desc(const wk_layer_desc* d) {
+  if (!d) return WK_ERR_INVALID_ARG;
+  if (d->n <= 0 || d->d <= 0 || d->k <= 0 || d->n_f <= 0 || d->n_l <= 0) return WK_ERR_INVALID_ARG;
+  if (d->num_linear < 1 || d->num_linear > kMaxLinear || !d->mlp_dims) return WK_ERR_INVALID_ARG;
+  if (!(d->ln_eps >= 0.0f) || !std::isfinite(d->ln_eps)) return WK_ERR_INVALID_ARG;
+  if (d->dtype != WK_F32 && d->dtype != WK_BF16) return WK_ERR_INVALID_ARG;
+  for (int t = 0; t <= d->num_linear; ++t)
+    if (d->mlp_dims[t] <= 0) return WK_ERR_INVALID_ARG;
+  const int64_t nk = (int64_t)d->n * d->k, nfd = (int64_t)d->n_f * d->d;
+  if (nk > INT32_MAX || nfd > INT32_MAX) return WK_ERR_INVALID_ARG;
+  if (d->mlp_dims[0] != nk || d->mlp_dims[d->num_linear] != nfd) return WK_ERR_INVALID_ARG;
+  // The residual adds X row by row, so the concatenation must have n rows.
+  if (d->n_f + d->n_l != d->n) return WK_ERR_UNSUPPORTED;
+  if (d->dtype == WK_BF16) {
+    if (d->d % 16 || d->n % 8 || d->k % 4) return WK_ERR_UNSUPPORTED;
+    for (int t = 0; t <= d->num_linear; ++t)
+      if (d->mlp_dims[t] % 8) return WK_ERR_UNSUPPORTED;
+    if (!wk::fmb_lcb_bf16_supported(d->n, d->d, d->k, d->n_l)) return WK_ERR_UNSUPPORTED;
+    if (!wk::resid_ln_bf16_supported(d->d)) return WK_ERR_UNSUPPORTED;
+  } else {
+    if (!wk::fmb_lcb_f32_supported(d->n, d->d, d->k, d->n_l)) return WK_ERR_UNSUPPORTED;
+  }
+  return WK_OK;
+}
+
+struct LayerPlan {
+  size_t fn = 0, h[2] = {0, 0}, m = 0, bytes = 0;
+  int num_hidden_bufs = 0;
+};
+
+// Largest batch the launch geometry handles (one workgroup per example in the
+// FMB+LCB kernel; grid dimensions are 32-bit).
+constexpr int64_t kMaxBatch = (int64_t)1 << 30;
+
+LayerPlan plan_layer(const wk_layer_desc& d, int64_t batch) {
+  LayerPlan p;
+  const size_t es = esize(d.dtype);
+  const size_t B = (size_t)batch;
+  size_t off = 0;
+  p.fn = off;
+  off += align_up(B * d.n * d.k * es);
+  int64_t maxhid = 0;
+  for (int t = 1; t < d.num_linear; ++t) maxhid = d.mlp_dims[t] > maxhid ? d.mlp_dims[t] : maxhid;
+  p.num_hidden_bufs = d.num_linear >= 3 ? 2 : (d.num_linear == 2 ? 1 : 0);
+  for (int i = 0; i < p.num_hidden_bufs; ++i) {
+    p.h[i] = off;
+    off += align_up(B * (size_t)maxhid * es);
+  }
+  p.m = off;
+  off += align_up(B * (size_t)d.n_f * d.d * es);
+  p.bytes = off;
+  return p;
+}
+
+int32_t check_weights(const wk_layer_desc& d, const wk_layer_weights* w) {
+  if (!w || !w->phi || !w->w_l || !w->mlp_w) return WK_ERR_INVALID_ARG;
+  const void* opt[] = {w->fm_ln_gamma, w->fm_ln_beta, w->out_ln_gamma, w->out_ln_beta};
+  if (!aligned16(w->phi) || !aligned16(w->w_l)) return WK_ERR_INVALID_ARG;
+  for (const void* p : opt)
+    if (p && !aligned16(p)) return WK_ERR_INVALID_ARG;
+  for (int t = 0; t < d.num_linear; ++t) {
+    if (!w->mlp_w[t] || !aligned16(w->mlp_w[t])) return WK_ERR_INVALID_ARG;
+    if (w->mlp_b && w->mlp_b[t] && !aligned16(w->mlp_b[t])) return WK_ERR_INVALID_ARG;
+  }
+  return WK_OK;
+}
+
+int32_t hip_status(hipError_t e) { return e == hipSuccess ? WK_OK : WK_ERR_HIP; }
+
+struct Launch {
+  wk_trace* trace;
+  hipStream_t stream;
+  template <class F>
+  int32_t operator()(int kind, int layer, int index, F&& fn) {
+    int64_t wgs = 0;
+    if (trace && trace->count < trace->capacity) {
+      const int i = trace->count;
+      if (hipEventRecord(trace->start[i], stream) != hipSuccess) return WK_ERR_HIP;
+      const hipError_t e = fn(&wgs);
+      if (e != hipSuccess) return WK_ERR_HIP;
+      if (hipEventRecord(trace->stop[i], stream) != hipSuccess) return WK_ERR_HIP;
+      trace->kind[i] = kind;
+      trace->layer[i] = layer;
+      trace->index[i] = index;
+      trace->wgs[i] = wgs;
+      trace->count = i + 1;
+      return WK_OK;
+    }
+    return hip_status(fn(&wgs));
+  }
+};
+
+// Launches one layer; all arguments already checked.
+int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t batch, const void* x,
+                  void* y, char* scratch, const LayerPlan& plan, Launch& launch, int layer_idx) {
+  const bool bf = d.dtype == WK_BF16;
+  char* fn = scratch + plan.fn;
+  char* mbuf = scratch + plan.m;
+  int32_t st;
+  if (bf) {
+    wk::FmbLcbArgs a;
+    a.x = static_cast<const uint16_t*>(x);
+    a.phi = static_cast<const uint16_t*>(w.phi);
+    a.w_l = static_cast<const uint16_t*>(w.w_l);
+    a.fm_gamma = static_cast<const uint16_t*>(w.fm_ln_gamma);
+    a.fm_beta = static_cast<const uint16_t*>(w.fm_ln_beta);
+    a.out_gamma = static_cast<const uint16_t*>(w.out_ln_gamma);
+    a.out_beta = static_cast<const uint16_t*>(w.out_ln_beta);
+    a.fn = reinterpret_cast<uint16_t*>(fn);
+    a.y = static_cast<uint16_t*>(y);
+    a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = d.n_f; a.n_l = d.n_l; a.eps = d.ln_eps;
+    st = launch(WK_KERNEL_FMB_LCB, layer_idx, 0,
+                [&](int64_t* g) { return wk::launch_fmb_lcb_bf16(a, batch, launch.stream, g); });
+  } else {
+    wk::FmbLcbF32Args a;
+    a.x = static_cast<const float*>(x);
+    a.phi = static_cast<const float*>(w.phi);
+    a.w_l = static_cast<const float*>(w.w_l);
+    a.fm_gamma = static_cast<const float*>(w.fm_ln_gamma);
+    a.fm_beta = static_cast<const float*>(w.fm_ln_beta);
+    a.out_gamma = static_cast<const float*>(w.out_ln_gamma);
+    a.out_beta = static_cast<const float*>(w.out_ln_beta);
+    a.fn = reinterpret_cast<float*>(fn);
+    a.y = static_cast<float*>(y);
+    a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = d.n_f; a.n_l = d.n_l; a.eps = d.ln_eps;
+    st = launch(WK_KERNEL_FMB_LCB, layer_idx, 0,
+                [&](int64_t* g) { return wk::launch_fmb_lcb_f32(a, batch, launch.stream, g); });
+  }
+  if (st != WK_OK) return st;
+
+  const void* in = fn;
+  for (int t = 0; t < d.num_linear; ++t) {
+    const bool last = t == d.num_linear - 1;
+    void* out = last ? static_cast<void*>(mbuf) : static_cast<void*>(scratch + plan.h[t % 2]);
+    wk::LinearArgs a;
+    a.a = in;
+    a.w = w.mlp_w[t];
+    a.bias = w.mlp_b ? w.mlp_b[t] : nullptr;
+    a.c = out;
+    a.M = batch;
+    a.N = d.mlp_dims[t + 1];
+    a.K = d.mlp_dims[t];
+    a.relu = last ? 0 : 1;
+    st = launch(WK_KERNEL_MLP_LINEAR, layer_idx, t, [&](int64_t* g) {
+      return bf ? wk::launch_linear_bf16(a, launch.stream, g) : wk::launch_linear_f32(a, launch.stream, g);
+    });
+    if (st != WK_OK) return st;
+    in = out;
+  }
+
+  wk::ResidLnArgs r;
+  r.m = mbuf;
+  r.x = x;
+  r.gamma = w.out_ln_gamma;
+  r.beta = w.out_ln_beta;
+  r.y = y;
+  r.batch = batch;
+  r.n = d.n;
+  r.d = d.d;
+  r.n_f = d.n_f;
+  r.eps = d.ln_eps;
+  return launch(WK_KERNEL_RESIDUAL_LN, layer_idx, 0, [&](int64_t* g) {
+    return bf ? wk::launch_resid_ln_bf16(r, launch.stream, g) : wk::launch_resid_ln_f32(r, launch.stream, g);
+  });
+}
+
+struct StackPlan {
+  size_t scratch_bytes = 0, ping[2] = {0, 0}, bytes = 0;
+};
+
+int32_t check_stack(int32_t l, const wk_layer_desc* descs, int64_t batch, StackPlan* sp) {
+  if (l < 1 || !descs) return WK_ERR_INVALID_ARG;
+  if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
+  for (int i = 0; i < l; ++i) {
+    const int32_t st = check_desc(&descs[i]);
+    if (st != WK_OK) return st;
+    if (descs[i].n != descs[0].n || descs[i].d != descs[0].d || descs[i].dtype != descs[0].dtype)
+      return WK_ERR_INVALID_ARG;
+  }
+  StackPlan p;
+  for (int i = 0; i < l; ++i) {
+    const size_t b = plan_layer(descs[i], batch).bytes;
+    p.scratch_bytes = b > p.scratch_bytes ? b : p.scratch_bytes;
+  }
+  const size_t act = align_up((size_t)batch * descs[0].n * descs[0].d * esize(descs[0].dtype));
+  size_t off = p.scratch_bytes;
+  const int nping = l >= 3 ? 2 : (l == 2 ? 1 : 0);
+  for (int i = 0; i < nping; ++i) {
+    p.ping[i] = off;
+    off += act;
+  }
+  p.bytes = off;
+  if (sp) *sp = p;
+  return WK_OK;
+}
+
+int32_t stack_forward(int32_t l, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                      int64_t batch, const void* x, void* y, void* ws, size_t ws_bytes, void* stream,
+                      wk_trace* trace) {
+  StackPlan sp;
+  int32_t st = check_stack(l, descs, batch, &sp);
+  if (st != WK_OK) return st;
+  if (!weights) return WK_ERR_INVALID_ARG;
+  for (int i = 0; i < l; ++i) {
+    st = check_weights(descs[i], &weights[i]);
+    if (st != WK_OK) return st;
+  }
+  if (batch == 0) return WK_OK;
+  const size_t act = (size_t)batch * descs[0].n * descs[0].d * esize(descs[0].dtype);
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return WK_ERR_INVALID_ARG;
+  if (overlap(x, act, y, act)) return WK_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return WK_ERR_INVALID_ARG;
+  if (ws_bytes < sp.bytes) return WK_ERR_WORKSPACE;
+  if (overlap(ws, sp.bytes, x, act) || overlap(ws, sp.bytes, y, act)) return WK_ERR_INVALID_ARG;
+
+  char* base = static_cast<char*>(ws);
+  Launch launch{trace, static_cast<hipStream_t>(stream)};
+  for (int i = 0; i < l; ++i) {
+    const void* in = i == 0 ? x : static_cast<const void*>(base + sp.ping[(i - 1) % 2]);
+    void* out = i == l - 1 ? y : static_cast<void*>(base + sp.ping[i % 2]);
+    const LayerPlan lp = plan_layer(descs[i], batch);
+    st = run_layer(descs[i], weights[i], batch, in, out, base, lp, launch, i);
+    if (st != WK_OK) return st;
+  }
+  return WK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t wukong_abi_version(void) { return WUKONG_ABI_VERSION; }
+
+const char* wukong_status_string(int32_t s) {
+  switch (s) {
+    case WK_OK: return "WK_OK: success";
+    case WK_ERR_INVALID_ARG: return "WK_ERR_INVALID_ARG: null, misaligned or overlapping pointer, or inconsistent dimensions";
+    case WK_ERR_UNSUPPORTED: return "WK_ERR_UNSUPPORTED: shape or dtype outside the compiled kernel set (or n_F + n_L != n)";
+    case WK_ERR_WORKSPACE: return "WK_ERR_WORKSPACE: workspace smaller than the required size";
+    case WK_ERR_HIP: return "WK_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown wukong status";
+  }
+}
+
+size_t wukong_layer_workspace_size(const wk_layer_desc* desc, int64_t batch) {
+  StackPlan sp;
+  if (check_stack(1, desc, batch, &sp) != WK_OK) return 0;
+  return sp.bytes;
+}
+
+int32_t wukong_layer_workspace_layout(const wk_layer_desc* desc, int64_t batch, wk_workspace_layout* out) {
+  if (!out) return WK_ERR_INVALID_ARG;
+  const int32_t st = check_stack(1, desc, batch, nullptr);
+  if (st != WK_OK) return st;
+  const LayerPlan p = plan_layer(*desc, batch);
+  out->fn = (int64_t)p.fn;
+  out->m = (int64_t)p.m;
+  out->num_hidden = desc->num_linear - 1;
+  for (int i = 0; i < 8; ++i) out->hidden[i] = -1;
+  for (int t = 1; t < desc->num_linear && t <= 8; ++t) {
+    const bool survives = t >= desc->num_linear - 2;  // only the last two hidden outputs survive
+    out->hidden[t - 1] = survives ? (int64_t)p.h[(t - 1) % 2] : -1;
+  }
+  return WK_OK;
+}
+
+int32_t wukong_layer_forward(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                             const void* x, void* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return stack_forward(1, desc, weights, batch, x, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t wukong_stack_workspace_size(int32_t num_layers, const wk_layer_desc* descs, int64_t batch) {
+  StackPlan sp;
+  if (check_stack(num_layers, descs, batch, &sp) != WK_OK) return 0;
+  return sp.bytes;
+}
+
+int32_t wukong_stack_forward(int32_t num_layers, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                             int64_t batch, const void* x, void* y, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  return stack_forward(num_layers, descs, weights, batch, x, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t wukong_stack_forward_traced(int32_t num_layers, const wk_layer_desc* descs,
+                                    const wk_layer_weights* weights, int64_t batch, const void* x, void* y,
+                                    void* workspace, size_t workspace_bytes, void* stream, wk_trace* trace) {
+  if (!trace) return WK_ERR_INVALID_ARG;
+  return stack_forward(num_layers, descs, weights, batch, x, y, workspace, workspace_bytes, stream, trace);
+}
+
+int32_t wukong_trace_create(int32_t capacity, wk_trace** out) {
+  if (!out || capacity <= 0 || capacity > (1 << 20)) return WK_ERR_INVALID_ARG;
+  wk_trace* t = new (std::nothrow) wk_trace;
+  if (!t) return WK_ERR_INVALID_ARG;
+  if (hipGetDevice(&t->device) != hipSuccess) {
+    delete t;
+    return WK_ERR_HIP;
+  }
+  t->capacity = capacity;
+  t->start.assign(capacity, nullptr);
+  t->stop.assign(capacity, nullptr);
+  t->kind.assign(capacity, 0);
+  t->layer.assign(capacity, 0);
+  t->index.assign(capacity, 0);
+  t->wgs.assign(capacity, 0);
+  for (int i = 0; i < capacity; ++i) {
+    if (hipEventCreate(&t->start[i]) != hipSuccess || hipEventCreate(&t->stop[i]) != hipSuccess) {
+      wukong_trace_destroy(t);
+      return WK_ERR_HIP;
+    }
+  }
+  *out = t;
+  return WK_OK;
+}
+
+int32_t wukong_trace_destroy(wk_trace* t) {
+  if (!t) return WK_ERR_INVALID_ARG;
+  for (hipEvent_t e : t->start)
+    if (e) (void)hipEventDestroy(e);
+  for (hipEvent_t e : t->stop)
+    if (e) (void)hipEventDestroy(e);
+  delete t;
+  return WK_OK;
+}
+
+int32_t wukong_trace_reset(wk_trace* t) {
+  if (!t) return WK_ERR_INVALID_ARG;
+  t->count = 0;
+  return WK_OK;
+}
+
+int32_t wukong_trace_count(const wk_trace* t) { return t ? t->count : -1; }
+
+int32_t wukong_trace_get(wk_trace* t, int32_t i, int32_t* kind, int32_t* layer, int32_t* index,
+                         int64_t* workgroups, float* ms) {
+  if (!t || i < 0 || i >= t->count) return WK_ERR_INVALID_ARG;
+  if (kind) *kind = t->kind[i];
+  if (layer) *layer = t->layer[i];
+  if (index) *index = t->index[i];
+  if (workgroups) *workgroups = t->wgs[i];
+  if (ms) {
+    if (hipEventSynchronize(t->stop[i]) != hipSuccess) return WK_ERR_HIP;
+    if (hipEventElapsedTime(ms, t->start[i], t->stop[i]) != hipSuccess) return WK_ERR_HIP;
+  }
+  return WK_OK;
+}
+
+}  // extern "C"

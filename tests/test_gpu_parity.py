@@ -1,0 +1,147 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+fp32 layers are compared with the pure fp64 oracle (max relative error
+1e-4); bf16 layers with the oracle run at the bf16 storage points the library
+documents (Z, Fn, h_t, M, Y), gate 2e-2.  The error metric is
+max_i |g_i - o_i| / max(|o_i|, rms(o)).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import recommender_feature_interaction_amd as wk
+import wukong_synth as ws
+from _gpu_helpers import (BF16_STORAGE, Run, check, host_f64, log, sample_indices, spec_of, to_host,
+                          tol_for)
+from _metrics import TOL_BF16, TOL_F32, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    wk.load_library()  # no fallback: a missing library fails here
+
+
+def _ws_tensor(ws_t, off, count, dtype):
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    es = 2 if dtype == "bf16" else 4
+    return to_host(ws_t[off:off + count * es].view(tdt))
+
+
+def test_tiny_f32_full_batch():
+    for affine in ("identity", "random"):
+        r = Run(ws.TINY_F32, seed=0, affine=affine)
+        log(f"tiny_f32 affine={affine}")
+        y = host_f64(to_host(r.forward()))
+        check("Y", y, r.oracle(), TOL_F32)
+
+
+@pytest.mark.parametrize("cfg", [ws.TINY_F32, ws.LAYER_D160, ws.SMALLD_N720], ids=lambda c: c.name)
+def test_single_layer_intermediates(cfg):
+    B = 64 if cfg.dtype == "f32" else 48
+    r = Run(cfg, seed=11, affine="random", batch=B)
+    spec = spec_of(cfg.layers[0], cfg.dtype)
+    wst = wk.alloc_workspace(wk.layer_workspace_size(spec, B))
+    y = wk.layer_forward(r.xd, r.layers[0], workspace=wst)
+    torch.cuda.synchronize()
+    lay = wk.workspace_layout(spec, B)
+    st = BF16_STORAGE if cfg.dtype == "bf16" else ()
+    Y, it = oracle.wukong_layer(r.x, r.host_w[0], storage=st, intermediates=True)
+    tol = tol_for(cfg)
+    s = cfg.layers[0]
+    fn = host_f64(_ws_tensor(wst, lay["fn"], B * s.n * s.k, cfg.dtype)).reshape(B, -1)
+    check("Fn", fn, it["Fn"], tol)
+    for t, off in enumerate(lay["hidden"]):
+        if off >= 0:
+            h = host_f64(_ws_tensor(wst, off, B * s.mlp[t + 1], cfg.dtype)).reshape(B, -1)
+            check(f"h{t + 1}", h, it["h"][t], tol)
+    m = host_f64(_ws_tensor(wst, lay["m"], B * s.n_f * s.d, cfg.dtype)).reshape(B, s.n_f, s.d)
+    check("M", m, it["M"], tol)
+    yh = host_f64(to_host(y))
+    check("Y rows of FMB", yh[:, :s.n_f], Y[:, :s.n_f], tol)
+    check("Y rows of LCB", yh[:, s.n_f:], Y[:, s.n_f:], tol)
+
+
+@pytest.mark.parametrize("cfg,batch", [(ws.STACK8_N256, 6), (ws.STACK8_N512, 4)], ids=["stack8_n256", "stack8_n512"])
+def test_stack_two_layers(cfg, batch):
+    r = Run(cfg, seed=5, affine="random", num_layers=2, batch=batch)
+    y = host_f64(to_host(r.forward()))
+    check("Y (bf16-storage oracle)", y, r.oracle(), TOL_BF16)
+    log(f"  vs pure fp64 oracle: {rel_err(y, r.oracle(storage=())):.3e} (reported)")
+
+
+def _custom(name, dtype, n, d, k, n_f, mlp, batch, layers=1):
+    shape = ws.LayerShape(n, d, k, n_f, n - n_f, tuple(mlp))
+    return ws.WukongConfig(name, dtype, batch, tuple([shape] * layers))
+
+
+RAGGED = [
+    _custom("ragged_n40_d32", "bf16", 40, 32, 12, 16, (480, 72, 512), 37),
+    _custom("ragged_three_linear", "bf16", 24, 16, 8, 8, (192, 136, 64, 128), 5),
+    _custom("ragged_d48", "bf16", 96, 48, 20, 40, (1920, 264, 1920), 3),
+    _custom("ragged_one_linear", "bf16", 16, 64, 4, 8, (64, 512), 300),
+    _custom("ragged_stack3", "bf16", 40, 32, 12, 16, (480, 72, 512), 9, layers=3),
+    _custom("ragged_f32", "f32", 12, 24, 3, 5, (36, 20, 120), 9),
+    _custom("ragged_f32_stack", "f32", 12, 24, 3, 5, (36, 20, 120), 4, layers=2),
+]
+
+
+@pytest.mark.parametrize("cfg", RAGGED, ids=lambda c: c.name)
+def test_ragged_shapes(cfg):
+    r = Run(cfg, seed=21, affine="random")
+    y = host_f64(to_host(r.forward()))
+    check("Y", y, r.oracle(), tol_for(cfg))
+
+
+def test_determinism_and_batch_invariance():
+    r = Run(ws.LAYER_D160, seed=3, affine="random", batch=64)
+    y1 = to_host(r.forward())
+    y2 = to_host(r.forward())
+    assert np.array_equal(y1, y2), "two runs differ"
+    sub = wk.stack_forward(r.xd[5:21].contiguous(), r.layers)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(sub), y1[5:21]), "a subset's rows differ from the full batch's"
+
+
+def test_empty_and_single_example():
+    r = Run(ws.LAYER_D160, seed=4, affine="random", batch=1)
+    y = host_f64(to_host(r.forward()))
+    check("Y (batch 1)", y, r.oracle(), TOL_BF16)
+    x0 = r.xd[:0]
+    y0 = wk.stack_forward(x0, r.layers)
+    torch.cuda.synchronize()
+    assert y0.shape == (0, 128, 160)
+
+
+def test_large_magnitudes():
+    """Per-feature scales up to 10 and an extra x100 on X: F grows by 1e4 and is still normalised."""
+    r = Run(ws.SMALLD_N720, seed=8, affine="random", batch=16)
+    x = ws.bf16_bits_to_f32(r.x) * np.float32(100.0)
+    r.x = ws.to_bf16_bits(x)
+    r.xd = wk.to_device(r.x, "bf16", "cuda")
+    y = host_f64(to_host(r.forward()))
+    check("Y (x100)", y, r.oracle(), TOL_BF16)
+
+
+FULL = [(ws.LAYER_D160, 8), (ws.SMALLD_N720, 8), (ws.STACK8_N256, 4), (ws.STACK8_N512, 4)]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,count", FULL, ids=[c.name for c, _ in FULL])
+def test_full_size_sampled(cfg, count):
+    """Full batch and depth on the GPU (the benchmark's launch configuration);
+    the oracle recomputes a sample of examples one by one."""
+    r = Run(cfg, seed=cfg.batch % 97, affine="identity")
+    y = r.forward()
+    idx = sample_indices(cfg.batch, count, seed=1)
+    got = host_f64(to_host(y[torch.as_tensor(idx, device=y.device)]))
+    assert torch.isfinite(y.float()).all().item(), "non-finite values in the full output"
+    del y
+    ref = r.oracle(idx)
+    check(f"Y at examples {idx.tolist()}", got, ref, TOL_BF16)
+    log(f"  vs pure fp64 oracle: {rel_err(got, r.oracle(idx, storage=())):.3e} (reported)")

@@ -59,27 +59,65 @@ def _workers() -> int:
     return max(1, min(16, n))
 
 
-def _fill(seed: int, tag: str, size: int, kind: str) -> np.ndarray:
-    """float32 array of `size` draws: kind 'uniform' -> U[0,1), 'normal' -> N(0,1)."""
-    out = np.empty(size, dtype=np.float32)
-    nchunks = (size + CHUNK - 1) // CHUNK
-
-    def work(i):
-        lo, hi = i * CHUNK, min(size, (i + 1) * CHUNK)
-        g = np.random.Generator(np.random.Philox(key=stream_key(seed, f"{tag}#{i}")))
-        if kind == "uniform":
-            g.random(dtype=np.float32, out=out[lo:hi])
-        elif kind == "normal":
-            g.standard_normal(dtype=np.float32, out=out[lo:hi])
-        else:  # pragma: no cover
-            raise ValueError(kind)
-
+def _run_chunks(nchunks: int, work) -> None:
     if nchunks <= 1:
         for i in range(nchunks):
             work(i)
     else:
         with ThreadPoolExecutor(_workers()) as ex:
             list(ex.map(work, range(nchunks)))
+
+
+def _bf16_round_bits(x32: np.ndarray) -> np.ndarray:
+    b = x32.view(np.uint32)
+    bias = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    return ((b + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def _draw(seed: int, tag: str, size: int, kind: str, scale: float = 1.0, offset: float = 0.0,
+          dtype: str = "f32") -> np.ndarray:
+    """`size` draws, each chunk keyed independently, transformed to scale*v + offset.
+
+    kind 'uniform_pm' draws v = 2u - 1 with u ~ U[0,1) (so v ~ U[-1,1)); kind
+    'normal' draws v ~ N(0,1).  The result is stored as float32 or bf16 bits.
+    """
+    out = np.empty(size, dtype=np.float32 if dtype == "f32" else np.uint16)
+    nchunks = (size + CHUNK - 1) // CHUNK
+    sc, of = np.float32(scale), np.float32(offset)
+
+    def work(i):
+        lo, hi = i * CHUNK, min(size, (i + 1) * CHUNK)
+        g = np.random.Generator(np.random.Philox(key=stream_key(seed, f"{tag}#{i}")))
+        v = np.empty(hi - lo, dtype=np.float32)
+        if kind == "uniform_pm":
+            g.random(dtype=np.float32, out=v)
+            v *= np.float32(2.0)
+            v -= np.float32(1.0)
+        elif kind == "normal":
+            g.standard_normal(dtype=np.float32, out=v)
+        else:  # pragma: no cover
+            raise ValueError(kind)
+        if scale != 1.0:
+            v *= sc
+        if offset != 0.0:
+            v += of
+        out[lo:hi] = v if dtype == "f32" else _bf16_round_bits(v)
+
+    _run_chunks(nchunks, work)
+    return out
+
+
+def _fill(seed: int, tag: str, size: int, kind: str) -> np.ndarray:
+    """float32 U[0,1) draws (kind 'uniform'), keyed per chunk like _draw."""
+    assert kind == "uniform"
+    out = np.empty(size, dtype=np.float32)
+
+    def work(i):
+        lo, hi = i * CHUNK, min(size, (i + 1) * CHUNK)
+        g = np.random.Generator(np.random.Philox(key=stream_key(seed, f"{tag}#{i}")))
+        g.random(dtype=np.float32, out=out[lo:hi])
+
+    _run_chunks((size + CHUNK - 1) // CHUNK, work)
     return out
 
 
@@ -87,23 +125,15 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bf16 (round-to-nearest-even); returns uint16 bits."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     out = np.empty(x.shape, dtype=np.uint16)
-    flat_in = x.reshape(-1).view(np.uint32)
+    flat_in = x.reshape(-1)
     flat_out = out.reshape(-1)
     n = flat_in.size
 
     def work(i):
         lo, hi = i * CHUNK, min(n, (i + 1) * CHUNK)
-        b = flat_in[lo:hi]
-        bias = ((b >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-        flat_out[lo:hi] = ((b + bias) >> np.uint32(16)).astype(np.uint16)
+        flat_out[lo:hi] = _bf16_round_bits(flat_in[lo:hi])
 
-    nchunks = (n + CHUNK - 1) // CHUNK
-    if nchunks <= 1:
-        for i in range(nchunks):
-            work(i)
-    else:
-        with ThreadPoolExecutor(_workers()) as ex:
-            list(ex.map(work, range(nchunks)))
+    _run_chunks((n + CHUNK - 1) // CHUNK, work)
     return out
 
 
@@ -122,14 +152,12 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
 
 def xavier_uniform(seed: int, tag: str, out_features: int, in_features: int, dtype: str) -> np.ndarray:
     a = math.sqrt(6.0 / (in_features + out_features))
-    u = _fill(seed, tag, out_features * in_features, "uniform")
-    w = (u * np.float32(2.0) - np.float32(1.0)) * np.float32(a)
-    return _store(w.reshape(out_features, in_features), dtype)
+    w = _draw(seed, tag, out_features * in_features, "uniform_pm", scale=a, dtype=dtype)
+    return w.reshape(out_features, in_features)
 
 
 def _uniform_pm(seed: int, tag: str, size: int, half_width: float, center: float = 0.0) -> np.ndarray:
-    u = _fill(seed, tag, size, "uniform")
-    return (u * np.float32(2.0) - np.float32(1.0)) * np.float32(half_width) + np.float32(center)
+    return _draw(seed, tag, size, "uniform_pm", scale=half_width, offset=center)
 
 
 @dataclass
