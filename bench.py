@@ -1,0 +1,260 @@
+"""Throughput of the Wukong layer-stack forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config layer_d160]
+
+A step is one forward pass of the whole stack (FMB+LCB kernel, every MLP
+Linear, residual LayerNorm, for every layer) over one batch of seeded
+synthetic input that is already resident in HBM.  W untimed warm-up steps,
+then K timed steps bracketed by device synchronisation.  HIP events recorded
+by the library around each kernel launch (on the launch stream) give the
+per-kernel durations; the kernel with the largest share of the step is
+reported against its roofline.  The CPU oracle is timed on a bounded sample
+of the same workload on this host as a reference baseline.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD specification)
+PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+METRIC = "Wukong stack fwd examples/sec; achieved TFLOP/s as % of bf16 MFMA peak"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "fmb_lcb": "fmb_lcb.hip",
+    "mlp_linear": "linear_bf16.hip",
+    "residual_ln": "resid_ln.hip",
+}
+
+
+def kernel_accounting(cfg):
+    """Algorithmic FLOPs and HBM bytes per launch of each kernel of each layer."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    B = cfg.batch
+    out = {}
+    for li, s in enumerate(cfg.layers):
+        n, d, k, n_f, n_l = s.n, s.d, s.k, s.n_f, s.n_l
+        out[("fmb_lcb", li, 0)] = {
+            "flops": B * (2 * (k + n_l) * n * d + 2 * n * d * k),
+            # X in; Fn and the LCB rows of Y out; [Phi; W_L] once
+            "bytes": B * (n * d + n * k + n_l * d) * es + (k + n_l) * n * es,
+        }
+        for t, (a, b) in enumerate(zip(s.mlp[:-1], s.mlp[1:])):
+            out[("mlp_linear", li, t)] = {
+                "flops": 2 * B * a * b,
+                "bytes": (B * a + a * b + B * b + b) * es,
+                "shape": [B, b, a],
+            }
+        out[("residual_ln", li, 0)] = {
+            "flops": 0,
+            # M and the FMB rows of X in, FMB rows of Y out
+            "bytes": 3 * B * n_f * d * es,
+        }
+    return out
+
+
+def source_digest(name):
+    path = os.path.join(ROOT, "recommender_feature_interaction_amd", "csrc", KERNEL_SOURCES[name])
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters (profiles/), or None
+    when absent or when the kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256") != source_digest(kernel):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(cfg, host_w, x, budget_s):
+    """The oracle (pure fp64, as it stands) on the first examples of the batch,
+    in chunks, until about budget_s seconds of host time are spent."""
+    import oracle
+
+    chunk = 64 if cfg.num_layers == 1 else 4
+    done, t0 = 0, time.perf_counter()
+    while done < cfg.batch:
+        m = min(chunk, cfg.batch - done)
+        oracle.wukong_stack(x[done:done + m], host_w, storage=())
+        done += m
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(done / el, 3), "unit": "examples/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"first {done} of {cfg.batch} examples of {cfg.name}, fp64 numpy oracle, "
+                      f"{el:.1f} s on {os.cpu_count()} host CPUs"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="layer_d160")
+    ap.add_argument("--seed", type=int, default=1)
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the Wukong forward needs no "
+                                   "collectives and every example is independent, so N GPUs would each run "
+                                   "this same one-GPU workload on their share of the batch; run with --gpus 1"}))
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    import recommender_feature_interaction_amd as wk
+    import wukong_synth as ws
+
+    cfg = ws.get(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_gen = time.time()
+    host_w = ws.make_stack_weights(cfg, args.seed, "identity")
+    x_host = ws.make_input(cfg, args.seed)
+    layers = [wk.DeviceLayer.from_host(wk.LayerSpec(s.n, s.d, s.k, s.n_f, s.n_l, tuple(s.mlp), 1e-5, cfg.dtype),
+                                       h, device=dev) for s, h in zip(cfg.layers, host_w)]
+    x = wk.to_device(x_host, cfg.dtype, dev)
+    y = torch.empty_like(x)
+    specs = [l.spec for l in layers]
+    ws_t = wk.alloc_workspace(wk.stack_workspace_size(specs, cfg.batch), dev)
+    torch.cuda.synchronize()
+    print(f"# {cfg.name}: inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
+    torch.cuda.synchronize()
+
+    kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step
+    trace = None if args.no_trace else wk.Trace(capacity=kpl * args.steps + 16)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream, trace=trace)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = cfg.batch * args.steps / elapsed
+    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    acct = kernel_accounting(cfg)
+    kernels = []
+    dominant = None
+    if trace is not None:
+        recs = trace.records()
+        agg = {}
+        for r in recs:
+            key = (r["kernel"], r["layer"], r["index"])
+            a = agg.setdefault(key, {"ms": 0.0, "count": 0, "workgroups": r["workgroups"]})
+            a["ms"] += r["ms"]
+            a["count"] += 1
+        for key, a in agg.items():
+            avg = a["ms"] / a["count"]
+            ac = acct[key]
+            kr = {"kernel": key[0], "layer": key[1], "index": key[2], "avg_ms": round(avg, 5),
+                  "launches": a["count"], "workgroups": a["workgroups"],
+                  "share_of_step": round(a["ms"] / args.steps / ms_per_step, 4),
+                  "tflops": round(ac["flops"] / (avg * 1e-3) / 1e12, 2),
+                  "gbps": round(ac["bytes"] / (avg * 1e-3) / 1e9, 1)}
+            kernels.append(kr)
+        # dominant: largest total time over the kernels of the same kind and index
+        by_kind = {}
+        for kr in kernels:
+            kk = (kr["kernel"], kr["index"])
+            by_kind.setdefault(kk, []).append(kr)
+        best = max(by_kind.items(), key=lambda it: sum(k["avg_ms"] for k in it[1]))
+        dominant = best[1][0]
+        trace.close()
+
+    roofline = None
+    if dominant is not None:
+        key = (dominant["kernel"], dominant["layer"], dominant["index"])
+        ac = acct[key]
+        avg_s = dominant["avg_ms"] * 1e-3
+        traffic = read_traffic(dominant["kernel"], cfg.name)
+        if ac["flops"] > 0 and ac["flops"] / ac["bytes"] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+            peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+            ach = ac["flops"] / avg_s / 1e12
+            roofline = {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": round(ach, 2),
+                        "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+                        "kernel": f"{dominant['kernel']}[layer {dominant['layer']}, index {dominant['index']}]",
+                        "algorithmic_flops_per_launch": ac["flops"], "avg_ms": dominant["avg_ms"]}
+        else:
+            ach = ac["bytes"] / avg_s / 1e9
+            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
+                        "kernel": f"{dominant['kernel']}[layer {dominant['layer']}, index {dominant['index']}]",
+                        "algorithmic_bytes_per_launch": ac["bytes"], "avg_ms": dominant["avg_ms"]}
+
+    step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
+    s0 = cfg.layers[0]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "examples/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1) inputs, Xavier-uniform weights)",
+        "config": {"workload": cfg.name, "global_batch": cfg.batch, "layers": cfg.num_layers, "n": s0.n,
+                   "d": s0.d, "k": s0.k, "n_f": s0.n_f, "n_l": s0.n_l, "mlp": list(s0.mlp),
+                   "parallelism": "single GPU"},
+        "step_tflops": round(step_tflops, 2),
+        "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
+    }
+    if not args.no_cpu_baseline:
+        del x, y, ws_t, layers
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline(cfg, host_w, x_host, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

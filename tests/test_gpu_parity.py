@@ -1,9 +1,10 @@
 """Parity of the HIP path (through the C ABI) with the CPU oracle.
 
-fp32 layers are compared with the pure fp64 oracle (max relative error
-1e-4); bf16 layers with the oracle run at the bf16 storage points the library
-documents (Z, Fn, h_t, M, Y), gate 2e-2.  The error metric is
-max_i |g_i - o_i| / max(|o_i|, rms(o)).
+fp32 layers are compared with the pure fp64 oracle, bf16 layers with the
+oracle run at the bf16 storage points the library documents (Z, Fn, h_t, M,
+Y).  The gate (tests/_metrics.py): fp32 elementwise max relative error
+<= 1e-4; bf16 normwise max relative error <= 2e-2 and rms <= 1e-2 at any
+depth, plus elementwise <= 2e-2 for single layers and their intermediates.
 """
 import numpy as np
 import pytest
@@ -12,9 +13,8 @@ import torch
 import oracle
 import recommender_feature_interaction_amd as wk
 import wukong_synth as ws
-from _gpu_helpers import (BF16_STORAGE, Run, check, host_f64, log, sample_indices, spec_of, to_host,
-                          tol_for)
-from _metrics import TOL_BF16, TOL_F32, rel_err
+from _gpu_helpers import BF16_STORAGE, Run, check, host_f64, log, sample_indices, spec_of, to_host
+from _metrics import rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,7 @@ def test_tiny_f32_full_batch():
         r = Run(ws.TINY_F32, seed=0, affine=affine)
         log(f"tiny_f32 affine={affine}")
         y = host_f64(to_host(r.forward()))
-        check("Y", y, r.oracle(), TOL_F32)
+        check("Y", y, r.oracle(), "f32")
 
 
 @pytest.mark.parametrize("cfg", [ws.TINY_F32, ws.LAYER_D160, ws.SMALLD_N720], ids=lambda c: c.name)
@@ -51,7 +51,7 @@ def test_single_layer_intermediates(cfg):
     lay = wk.workspace_layout(spec, B)
     st = BF16_STORAGE if cfg.dtype == "bf16" else ()
     Y, it = oracle.wukong_layer(r.x, r.host_w[0], storage=st, intermediates=True)
-    tol = tol_for(cfg)
+    tol = cfg.dtype
     s = cfg.layers[0]
     fn = host_f64(_ws_tensor(wst, lay["fn"], B * s.n * s.k, cfg.dtype)).reshape(B, -1)
     check("Fn", fn, it["Fn"], tol)
@@ -70,8 +70,8 @@ def test_single_layer_intermediates(cfg):
 def test_stack_two_layers(cfg, batch):
     r = Run(cfg, seed=5, affine="random", num_layers=2, batch=batch)
     y = host_f64(to_host(r.forward()))
-    check("Y (bf16-storage oracle)", y, r.oracle(), TOL_BF16)
-    log(f"  vs pure fp64 oracle: {rel_err(y, r.oracle(storage=())):.3e} (reported)")
+    check("Y (bf16-storage oracle)", y, r.oracle(), "bf16", elementwise=False)
+    log(f"  vs pure fp64 oracle: elementwise {rel_err(y, r.oracle(storage=())):.3e} (reported)")
 
 
 def _custom(name, dtype, n, d, k, n_f, mlp, batch, layers=1):
@@ -94,7 +94,7 @@ RAGGED = [
 def test_ragged_shapes(cfg):
     r = Run(cfg, seed=21, affine="random")
     y = host_f64(to_host(r.forward()))
-    check("Y", y, r.oracle(), tol_for(cfg))
+    check("Y", y, r.oracle(), cfg.dtype, elementwise=cfg.num_layers == 1)
 
 
 def test_determinism_and_batch_invariance():
@@ -110,7 +110,7 @@ def test_determinism_and_batch_invariance():
 def test_empty_and_single_example():
     r = Run(ws.LAYER_D160, seed=4, affine="random", batch=1)
     y = host_f64(to_host(r.forward()))
-    check("Y (batch 1)", y, r.oracle(), TOL_BF16)
+    check("Y (batch 1)", y, r.oracle(), "bf16")
     x0 = r.xd[:0]
     y0 = wk.stack_forward(x0, r.layers)
     torch.cuda.synchronize()
@@ -124,7 +124,7 @@ def test_large_magnitudes():
     r.x = ws.to_bf16_bits(x)
     r.xd = wk.to_device(r.x, "bf16", "cuda")
     y = host_f64(to_host(r.forward()))
-    check("Y (x100)", y, r.oracle(), TOL_BF16)
+    check("Y (x100)", y, r.oracle(), "bf16")
 
 
 FULL = [(ws.LAYER_D160, 8), (ws.SMALLD_N720, 8), (ws.STACK8_N256, 4), (ws.STACK8_N512, 4)]
@@ -143,5 +143,5 @@ def test_full_size_sampled(cfg, count):
     assert torch.isfinite(y.float()).all().item(), "non-finite values in the full output"
     del y
     ref = r.oracle(idx)
-    check(f"Y at examples {idx.tolist()}", got, ref, TOL_BF16)
-    log(f"  vs pure fp64 oracle: {rel_err(got, r.oracle(idx, storage=())):.3e} (reported)")
+    check(f"Y at examples {idx.tolist()}", got, ref, "bf16", elementwise=cfg.num_layers == 1)
+    log(f"  vs pure fp64 oracle: elementwise {rel_err(got, r.oracle(idx, storage=())):.3e} (reported)")
