@@ -21,6 +21,16 @@
 // index is remapped so each XCD gets a contiguous run of tiles, walked in
 // groups of 8 tile-rows so that neighbouring tiles share A and W panels in
 // that XCD's L2.
+//
+// Two kernels share this structure:
+//  * linear_dma_kernel (K % 64 == 0, the fast path): v_mfma_f32_16x16x32_bf16,
+//    operands moved global -> LDS by buffer_load ... lds (no staging
+//    registers), two static LDS stages so the next K tile streams in while the
+//    current one is consumed.  Each workgroup's buffer resources start at its
+//    tile's first row and end at the last valid row, so rows past M or N read
+//    as zero.  Barriers are LDS-scoped (they do not wait for global loads).
+//  * linear_bf16_kernel (any K % 8 == 0): 32x32x16 MFMA, register-staged
+//    loads with per-element bounds checks.
 #include <mutex>
 
 #include "wk_device.h"
@@ -44,6 +54,137 @@ struct LinearKArgs {
 constexpr int kBK = 64;
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * kBK + ((ch ^ ((row >> 1) & 7)) << 3); }
+
+__device__ __forceinline__ void tile_origin(const LinearKArgs& p, int BM, int BN, int64_t& m0, int& n0) {
+  const int nblk = gridDim.x, bid = blockIdx.x, full = nblk & ~7;
+  int logical = bid;
+  if (bid < full) logical = (bid & 7) * (full >> 3) + (bid >> 3);
+  constexpr int GM = 8;
+  const int per_group = GM * p.tiles_n;
+  const int group = logical / per_group;
+  const int first_m = group * GM;
+  const int gsz = min(p.tiles_m - first_m, GM);
+  const int in_g = logical - group * per_group;
+  m0 = (int64_t)(first_m + in_g % gsz) * BM;
+  n0 = (in_g / gsz) * BN;
+}
+
+// Workgroup barrier ordering LDS only: it waits for this wave's LDS traffic,
+// not for outstanding global loads.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+#define WK_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs p) {
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  constexpr int A_INS = BM / 8 / NW, W_INS = BN / 8 / NW;  // 1 KB (8 rows) DMA instructions per wave
+  static_assert(A_INS * NW * 8 == BM && W_INS * NW * 8 == BN, "tile / wave mismatch");
+  __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  int64_t m0;
+  int n0;
+  tile_origin(p, BM, BN, m0, n0);
+  const int64_t M = p.M;
+  const int N = p.N, K = p.K;
+  const int rows_a = (int)min<int64_t>(BM, M - m0), rows_w = min(BN, N - n0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.a + m0 * K), (short)0, rows_a * K * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.w + (int64_t)n0 * K), (short)0, rows_w * K * 2, 0x00020000);
+  // A DMA instruction writes 64 lanes x 16 B = 8 LDS rows; lane -> row lane/8,
+  // LDS chunk lane%8, which holds global chunk (lane%8) ^ swizzle(row).  The
+  // swizzle of row 8b + r is (4(b & 1) + r/2) & 7: two lane offsets suffice.
+  const int lrow = lane >> 3, lpos = lane & 7;
+  const uint32_t voff0 = (uint32_t)(lrow * K + ((lpos ^ (lrow >> 1)) << 3)) * 2u;
+  const uint32_t voff1 = (uint32_t)(lrow * K + ((lpos ^ (4 + (lrow >> 1))) << 3)) * 2u;
+  const uint32_t blk_bytes = (uint32_t)(16 * K);
+  auto dma = [&](uint16_t* sa, uint16_t* sw, int k0) {
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int blk = wave * A_INS + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, WK_LDS(sa + blk * 512), 16,
+                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, k0 * 2, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < W_INS; ++i) {
+      const int blk = wave * W_INS + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, WK_LDS(sw + blk * 512), 16,
+                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, k0 * 2, 0, 0);
+    }
+  };
+  f32x4 acc[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+#pragma unroll
+    for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int l16 = lane & 15, lg = lane >> 4;
+  // W_tile x A_tile^T: lane (l16, lg) ends with C[m0 + .. + l16][n .. n + 3]
+  auto compute = [&](const uint16_t* a, const uint16_t* w) {
+#pragma unroll
+    for (int ks = 0; ks < kBK / 32; ++ks) {
+      const int ch = ks * 4 + lg;
+      u32x4 wf[NB], af[MB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) wf[i] = *reinterpret_cast<const u32x4*>(w + swz(wn * WTN + i * 16 + l16, ch));
+#pragma unroll
+      for (int j = 0; j < MB; ++j) af[j] = *reinterpret_cast<const u32x4*>(a + swz(wm * WTM + j * 16 + l16, ch));
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j) acc[i][j] = mfma16x16x32(wf[i], af[j], acc[i][j]);
+    }
+  };
+  const int KT = K / kBK;
+  dma(sA0, sW0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
+  lds_barrier();
+  for (int kt = 0; kt < KT; kt += 2) {
+    if (kt + 1 < KT) dma(sA1, sW1, (kt + 1) * kBK);
+    compute(sA0, sW0);
+    __builtin_amdgcn_s_waitcnt(0x0070);
+    lds_barrier();
+    if (kt + 1 < KT) {
+      if (kt + 2 < KT) dma(sA0, sW0, (kt + 2) * kBK);
+      compute(sA1, sW1);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      lds_barrier();
+    }
+  }
+  const uint16_t* bias = p.bias;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int n = n0 + wn * WTN + i * 16 + lg * 4;
+    float bb[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias != nullptr && n < N) {
+      const u32x2 b2 = *reinterpret_cast<const u32x2*>(bias + n);
+      bb[0] = bf16lo(b2[0]); bb[1] = bf16hi(b2[0]); bb[2] = bf16lo(b2[1]); bb[3] = bf16hi(b2[1]);
+    }
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int64_t m = m0 + wm * WTM + j * 16 + l16;
+      if (m < M && n < N) {
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          v[t] = acc[i][j][t] + bb[t];
+          if (p.relu) v[t] = fmaxf(v[t], 0.f);
+        }
+        u32x2 o;
+        o[0] = pack_bf16x2(v[0], v[1]);
+        o[1] = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<u32x2*>(p.c + m * N + n) = o;
+      }
+    }
+  }
+}
 
 template <int BM, int BN, int WGM, int WGN>
 __global__ __launch_bounds__(WGM * WGN * 64) void linear_bf16_kernel(LinearKArgs p) {
@@ -185,30 +326,39 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_bf16_kernel(LinearKArgs
 
 struct LinearVariant {
   int bm, bn, occupancy;
-  float eff;  // relative per-FLOP speed, used only to rank the variants
+  float eff;  // relative per-FLOP speed measured on the MLP shapes, used only to rank variants
   void (*kernel)(LinearKArgs);
-  size_t lds;
+  size_t dyn_lds;  // dynamic LDS bytes (the DMA kernels use static LDS)
   int threads;
+  bool needs_k64;
 };
 
-#define WK_LIN_VARIANT(BM, BN, WGM, WGN, OCC, EFF)                                       \
-  LinearVariant {                                                                        \
-    BM, BN, OCC, EFF, linear_bf16_kernel<BM, BN, WGM, WGN>, (size_t)2 * (BM + BN) * kBK * 2, \
-        WGM * WGN * 64                                                                   \
+#define WK_DMA_VARIANT(BM, BN, WGM, WGN, OCC, EFF) \
+  LinearVariant { BM, BN, OCC, EFF, linear_dma_kernel<BM, BN, WGM, WGN>, 0, WGM * WGN * 64, true }
+#define WK_LIN_VARIANT(BM, BN, WGM, WGN, OCC, EFF)                                                   \
+  LinearVariant {                                                                                    \
+    BM, BN, OCC, EFF, linear_bf16_kernel<BM, BN, WGM, WGN>, (size_t)2 * (BM + BN) * kBK * 2, WGM * WGN * 64, \
+        false                                                                                        \
   }
 
 const LinearVariant kLinVariants[] = {
-    WK_LIN_VARIANT(256, 256, 2, 2, 1, 1.00f),
-    WK_LIN_VARIANT(256, 128, 2, 2, 1, 0.92f),
-    WK_LIN_VARIANT(128, 128, 2, 2, 2, 0.80f),
+    WK_DMA_VARIANT(256, 256, 2, 4, 1, 1.00f),
+    WK_DMA_VARIANT(256, 128, 2, 4, 1, 0.78f),
+    WK_DMA_VARIANT(128, 128, 2, 2, 2, 0.80f),
+    WK_LIN_VARIANT(256, 256, 2, 2, 1, 0.55f),
+    WK_LIN_VARIANT(256, 128, 2, 2, 1, 0.50f),
+    WK_LIN_VARIANT(128, 128, 2, 2, 2, 0.45f),
 };
+constexpr int kNumLinVariants = sizeof(kLinVariants) / sizeof(kLinVariants[0]);
 
 constexpr int kNumCU = 256;
 
-const LinearVariant* pick_linear(int64_t M, int N) {
+const LinearVariant* pick_linear(int64_t M, int N, int K) {
+  const bool k64 = (K % kBK) == 0;
   const LinearVariant* best = nullptr;
   double best_cost = 0;
   for (const auto& v : kLinVariants) {
+    if (v.needs_k64 != k64) continue;
     const double tiles = (double)((M + v.bm - 1) / v.bm) * (double)((N + v.bn - 1) / v.bn);
     const double slots = (double)kNumCU * v.occupancy;
     const double rounds = (tiles + slots - 1) / slots;
@@ -228,7 +378,7 @@ bool linear_bf16_supported(int64_t M, int N, int K) {
 }
 
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups) {
-  const LinearVariant* v = pick_linear(a.M, a.N);
+  const LinearVariant* v = pick_linear(a.M, a.N, a.K);
   LinearKArgs k;
   k.a = static_cast<const uint16_t*>(a.a);
   k.w = static_cast<const uint16_t*>(a.w);
@@ -243,15 +393,16 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* 
   const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;
   if (workgroups) *workgroups = blocks;
   if (blocks == 0) return hipSuccess;
-  static std::once_flag attr_once[sizeof(kLinVariants) / sizeof(kLinVariants[0])];
-  static hipError_t attr_err[sizeof(kLinVariants) / sizeof(kLinVariants[0])];
+  static std::once_flag attr_once[kNumLinVariants];
+  static hipError_t attr_err[kNumLinVariants];
   const size_t vi = (size_t)(v - kLinVariants);
   std::call_once(attr_once[vi], [&] {
-    attr_err[vi] = hipFuncSetAttribute(reinterpret_cast<const void*>(v->kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)v->lds);
+    attr_err[vi] = v->dyn_lds == 0 ? hipSuccess
+                                   : hipFuncSetAttribute(reinterpret_cast<const void*>(v->kernel),
+                                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)v->dyn_lds);
   });
   if (attr_err[vi] != hipSuccess) return attr_err[vi];
-  hipLaunchKernelGGL(v->kernel, dim3((unsigned)blocks), dim3(v->threads), v->lds, stream, k);
+  hipLaunchKernelGGL(v->kernel, dim3((unsigned)blocks), dim3(v->threads), v->dyn_lds, stream, k);
   return hipGetLastError();
 }
 
