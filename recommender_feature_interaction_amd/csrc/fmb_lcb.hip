@@ -135,10 +135,10 @@ __global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
         else
           wf[zi][ks] = u32x4{0u, 0u, 0u, 0u};
       }
-    __syncthreads();  // everyone is done reading the previous chunk
+    lds_barrier();  // everyone is done reading the previous chunk
     store_chunk();
     if (c + 1 < nchunks) load_chunk(m0 + MC);
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       if (m0 + ks * 32 < n) {
@@ -152,12 +152,12 @@ __global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
       }
     }
   }
-  __syncthreads();  // X^T no longer needed: its LDS becomes Z
+  lds_barrier();  // X^T no longer needed: its LDS becomes Z
 
   // Z rows -> LDS as bf16 (the phase-2 operand); padding rows/columns are zero.
   for (int i = tid; i < 16 * KW * Z_LD / 8; i += NT)
     reinterpret_cast<u32x4*>(Zs)[i] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
+  lds_barrier();
 
   const uint16_t* og = p.out_gamma;
   const uint16_t* ob = p.out_beta;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
       }
     }
   }
-  __syncthreads();  // Z complete in LDS
+  lds_barrier();  // Z complete in LDS
 
   // ------------------------------------------------------------- phase 2
   const int MT = (n + 15) >> 4;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
       }
   s = xor_sum<1>(s);
   if (lane == 0) red[wave] = s;
-  __syncthreads();
+  lds_barrier();
   float tot = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) tot += red[w];
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
       }
   q = xor_sum<1>(q);
   if (lane == 0) red[NW + wave] = q;
-  __syncthreads();
+  lds_barrier();
   float qt = 0.f;
 #pragma unroll
   for (int w = 0; w < NW; ++w) qt += red[NW + w];
@@ -365,7 +365,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
   __shared__ float red[2 * NW];
   uint16_t* Xs = smem;                   // [NROWS][P]
   uint16_t* Zs = smem + NROWS * P;       // [16 KW][Z_LD]
-  uint16_t* Ws = Zs + 16 * KW * Z_LD;    // [16 ZT][WP] when WL
+  uint16_t* Gs = Zs + 16 * KW * Z_LD;    // out LayerNorm gamma [D] then beta [D] (bf16)
+  uint16_t* Ws = Gs + 2 * D;             // [16 ZT][WP] when WL
 
   const int n = p.n, k = p.k, n_l = p.n_l, n_f = p.n_f;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -391,6 +392,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
         r = p.w_l + (int64_t)(z - k) * n;
     }
     wrow[zi] = r;
+  }
+  // the output LayerNorm's gamma / beta are the same for every example: stage them once
+  // (a global load inside the example loop would wait for the in-flight X prefetch)
+  for (int i = tid; i < 2 * D; i += NT) {
+    const uint16_t* src = i < D ? p.out_gamma : p.out_beta;
+    Gs[i] = src ? src[i < D ? i : i - D] : (uint16_t)(i < D ? 0x3f80u : 0u);
   }
   if constexpr (WL) {
     // [Phi; W_L] is the same for every example: stage it once, zero-padded to 16-row tiles and NROWS columns
@@ -428,16 +435,39 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
     }
   };
 
+  // the FMB LayerNorm's gamma / beta at this lane's F positions, packed bf16 pairs: the same for every
+  // example, so loaded once (a global load in the example loop would wait for older stores)
+  constexpr bool PRE = MW * KW <= 4;  // enough registers to keep them
+  constexpr int PMW = PRE ? MW : 1, PKW = PRE ? KW : 1;
+  uint32_t fgam[PMW][PKW][2], fbet[PMW][PKW][2];
+#pragma unroll
+  for (int mi = 0; mi < PMW; ++mi)
+#pragma unroll
+    for (int jt = 0; jt < PKW; ++jt) {
+      const int m = (wave + mi * NW) * 16 + li;
+      const int j0 = jt * 16 + lg * 4;
+      u32x2 g2 = u32x2{0x3f803f80u, 0x3f803f80u}, b2 = u32x2{0u, 0u};
+      if (m < n && j0 < k) {
+        if (p.fm_gamma) g2 = *reinterpret_cast<const u32x2*>(p.fm_gamma + m * k + j0);
+        if (p.fm_beta) b2 = *reinterpret_cast<const u32x2*>(p.fm_beta + m * k + j0);
+      }
+      fgam[mi][jt][0] = g2[0]; fgam[mi][jt][1] = g2[1];
+      fbet[mi][jt][0] = b2[0]; fbet[mi][jt][1] = b2[1];
+    }
+
   int64_t b = blockIdx.x;
   if (b >= batch) return;
   load_x(b);
   store_x();
-  __syncthreads();
+  lds_barrier();
+  // the next example's X is always loaded right after the previous one was written to LDS, so the
+  // loads are older than every store of the example in between and waiting for them never waits
+  // for those stores
+  if (b + gridDim.x < batch) load_x(b + gridDim.x);
   const float inv_d = 1.0f / static_cast<float>(D);
   const float inv_nk = 1.0f / static_cast<float>(n * k);
   for (; b < batch; b += gridDim.x) {
     const int64_t bn = b + gridDim.x;
-    if (bn < batch) load_x(bn);  // in flight while this example is computed
 
     // ---- phase 1: [Z; Lc]^T = X^T [Phi; W_L]^T, K = m in steps of 32
     f32x4 acc[ZW][ET];
@@ -491,7 +521,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
 
     // ---- Z -> LDS (bf16, zero padding), LCB rows of Y
     for (int i = tid; i < 16 * KW * Z_LD / 8; i += NT) reinterpret_cast<u32x4*>(Zs)[i] = u32x4{0u, 0u, 0u, 0u};
-    __syncthreads();
+    lds_barrier();
 #pragma unroll
     for (int zi = 0; zi < ZW; ++zi) {
       const int zt = wave + zi * NW;
@@ -538,15 +568,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
 #pragma unroll
           for (int et = 0; et < ET; ++et) {
             const int e = et * 16 + lg * 4;
-            float gm[4] = {1.f, 1.f, 1.f, 1.f}, bt[4] = {0.f, 0.f, 0.f, 0.f};
-            if (p.out_gamma) {
-              const u32x2 g2 = *reinterpret_cast<const u32x2*>(p.out_gamma + e);
-              gm[0] = bf16lo(g2[0]); gm[1] = bf16hi(g2[0]); gm[2] = bf16lo(g2[1]); gm[3] = bf16hi(g2[1]);
-            }
-            if (p.out_beta) {
-              const u32x2 b2 = *reinterpret_cast<const u32x2*>(p.out_beta + e);
-              bt[0] = bf16lo(b2[0]); bt[1] = bf16hi(b2[0]); bt[2] = bf16lo(b2[1]); bt[3] = bf16hi(b2[1]);
-            }
+            const u32x2 g2 = *reinterpret_cast<const u32x2*>(Gs + e);
+            const u32x2 b2 = *reinterpret_cast<const u32x2*>(Gs + D + e);
+            const float gm[4] = {bf16lo(g2[0]), bf16hi(g2[0]), bf16lo(g2[1]), bf16hi(g2[1])};
+            const float bt[4] = {bf16lo(b2[0]), bf16hi(b2[0]), bf16lo(b2[1]), bf16hi(b2[1])};
             u32x2 o;
             o[0] = pack_bf16x2((v[et][0] - mean) * rstd * gm[0] + bt[0], (v[et][1] - mean) * rstd * gm[1] + bt[1]);
             o[1] = pack_bf16x2((v[et][2] - mean) * rstd * gm[2] + bt[2], (v[et][3] - mean) * rstd * gm[3] + bt[3]);
@@ -555,7 +580,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
         }
       }
     }
-    __syncthreads();  // Z complete
+    lds_barrier();  // Z complete
 
     // ---- phase 2: F^T = Z X^T (rows j of Z, contraction e), X rows from LDS
     f32x4 facc[MW][KW];
@@ -596,7 +621,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
         }
     sm = xor_sum<1>(sm);
     if (lane == 0) red[wave] = sm;
-    __syncthreads();
+    lds_barrier();
     float tot = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) tot += red[w];
@@ -617,7 +642,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
         }
     q = xor_sum<1>(q);
     if (lane == 0) red[NW + wave] = q;
-    __syncthreads();  // also: every wave is done reading Xs and Zs of this example
+    lds_barrier();  // also: every wave is done reading Xs and Zs of this example
     float qt = 0.f;
 #pragma unroll
     for (int w = 0; w < NW; ++w) qt += red[NW + w];
@@ -631,15 +656,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
         const int j0 = jt * 16 + lg * 4;
         if (m < n && j0 < k) {
           const int idx = m * k + j0;
-          float gm[4] = {1.f, 1.f, 1.f, 1.f}, bt[4] = {0.f, 0.f, 0.f, 0.f};
-          if (p.fm_gamma) {
-            const u32x2 g2 = *reinterpret_cast<const u32x2*>(p.fm_gamma + idx);
-            gm[0] = bf16lo(g2[0]); gm[1] = bf16hi(g2[0]); gm[2] = bf16lo(g2[1]); gm[3] = bf16hi(g2[1]);
+          u32x2 g2, b2;
+          if constexpr (PRE) {
+            g2 = u32x2{fgam[PRE ? mi : 0][PRE ? jt : 0][0], fgam[PRE ? mi : 0][PRE ? jt : 0][1]};
+            b2 = u32x2{fbet[PRE ? mi : 0][PRE ? jt : 0][0], fbet[PRE ? mi : 0][PRE ? jt : 0][1]};
+          } else {
+            g2 = p.fm_gamma ? *reinterpret_cast<const u32x2*>(p.fm_gamma + idx) : u32x2{0x3f803f80u, 0x3f803f80u};
+            b2 = p.fm_beta ? *reinterpret_cast<const u32x2*>(p.fm_beta + idx) : u32x2{0u, 0u};
           }
-          if (p.fm_beta) {
-            const u32x2 b2 = *reinterpret_cast<const u32x2*>(p.fm_beta + idx);
-            bt[0] = bf16lo(b2[0]); bt[1] = bf16hi(b2[0]); bt[2] = bf16lo(b2[1]); bt[3] = bf16hi(b2[1]);
-          }
+          const float gm[4] = {bf16lo(g2[0]), bf16hi(g2[0]), bf16lo(g2[1]), bf16hi(g2[1])};
+          const float bt[4] = {bf16lo(b2[0]), bf16hi(b2[0]), bf16lo(b2[1]), bf16hi(b2[1])};
           const f32x4 f = facc[mi][jt];
           u32x2 o;
           o[0] = pack_bf16x2((f[0] - mean) * rstd * gm[0] + bt[0], (f[1] - mean) * rstd * gm[1] + bt[1]);
@@ -649,7 +675,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
       }
     if (bn < batch) {
       store_x();  // the barrier above guarantees nobody still reads this example's X
-      __syncthreads();
+      lds_barrier();
+      if (bn + gridDim.x < batch) load_x(bn + gridDim.x);
     }
   }
 }
@@ -662,7 +689,7 @@ size_t resident_lds_bytes(int zt_rows) {
   constexpr int NROWS = (NMAX + 31) / 32 * 32;
   constexpr int DZ = (D + 31) / 32 * 32;
   const size_t w = WL ? (size_t)zt_rows * (NROWS + 8) * 2 : 0;
-  return (size_t)NROWS * Q * 16 + (size_t)16 * KW * (DZ + 8) * 2 + w;
+  return (size_t)NROWS * Q * 16 + (size_t)16 * KW * (DZ + 8) * 2 + (size_t)4 * D + w;
 }
 
 struct ResidentVariant {

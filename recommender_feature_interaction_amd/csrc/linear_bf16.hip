@@ -69,14 +69,6 @@ __device__ __forceinline__ void tile_origin(const LinearKArgs& p, int BM, int BN
   n0 = (in_g / gsz) * BN;
 }
 
-// Workgroup barrier ordering LDS only: it waits for this wave's LDS traffic,
-// not for outstanding global loads.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 #define WK_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 template <int BM, int BN, int WGM, int WGN>

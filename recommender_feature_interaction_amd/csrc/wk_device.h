@@ -20,16 +20,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// float -> bf16 bits, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// float -> bf16, round to nearest even (NaN stays NaN): one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) { return pack_bf16x2(f, 0.f) & 0xffffu; }
 
 // D(16x16) += A(16x32) * B(32x16).  Lane l supplies A[l%16][8(l/16)..+7] and
 // B[8(l/16)..+7][l%16]; it receives D[4(l/16)+t][l%16], t = 0..3.
@@ -65,6 +63,18 @@ __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
 }
 __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
+// workgroup release/acquire fence plus s_barrier, and on gfx9 the release
+// half waits for every outstanding vector memory operation (global loads and
+// stores included); this one waits for LDS traffic (lgkmcnt) only, so global
+// prefetches and stores stay in flight across it.  Use it where waves share
+// nothing but LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 }  // namespace wk
