@@ -5,13 +5,19 @@
 A step is one forward pass of the whole stack (FMB+LCB kernel, every MLP
 Linear, residual LayerNorm, for every layer) over one batch of seeded
 synthetic input that is already resident in HBM.  W untimed warm-up steps,
-then K timed steps bracketed by device synchronisation.  HIP events recorded
-by the library around each kernel launch (on the launch stream) give the
-per-kernel durations; the kernel with the largest share of the step is
-reported against its roofline.  The CPU oracle is timed on a bounded sample
-of the same workload on this host as a reference baseline.
+then K timed steps bracketed by device synchronisation give `value`.  A
+second pass of K steps runs with HIP events recorded by the library around
+each kernel launch (on the launch stream): the per-kernel durations, and the
+kernel with the largest share of the step reported against its roofline.
+The CPU oracle is timed on a bounded sample of the same workload on this host
+as a reference baseline.
 
 Prints one JSON line.
+
+    python bench.py --copy-calibration BYTES
+
+instead runs a plain device-to-device copy of BYTES bytes a few times (the
+reference kernel for scaling the FETCH_SIZE / WRITE_SIZE counters) and exits.
 """
 from __future__ import annotations
 
@@ -69,10 +75,10 @@ def source_digest(name):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def read_traffic(kernel, workload):
+def read_traffic(kernel, index, workload):
     """HBM bytes per launch measured with rocprofv3 counters (profiles/), or None
     when absent or when the kernel source changed since the counters were taken."""
-    path = os.path.join(PROFILE_DIR, f"{kernel}_{workload}_traffic.txt")
+    path = os.path.join(PROFILE_DIR, f"{kernel}_{index}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -127,8 +133,21 @@ def main():
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-trace", action="store_true", help="time without per-kernel events")
+    ap.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+
+        src = torch.empty(args.copy_calibration, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": args.copy_calibration, "launches": 3}))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -163,17 +182,28 @@ def main():
         wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
     torch.cuda.synchronize()
 
-    kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step
-    trace = None if args.no_trace else wk.Trace(capacity=kpl * args.steps + 16)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream, trace=trace)
+        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     value = cfg.batch * args.steps / elapsed
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel pass: the library records HIP events around every launch on the launch stream
+    kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step
+    trace = None
+    traced_ms = None
+    if not args.no_trace:
+        trace = wk.Trace(capacity=kpl * args.steps + 16)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream, trace=trace)
+        torch.cuda.synchronize()
+        traced_ms = (time.perf_counter() - t1) * 1e3 / args.steps
 
     acct = kernel_accounting(cfg)
     kernels = []
@@ -191,7 +221,7 @@ def main():
             ac = acct[key]
             kr = {"kernel": key[0], "layer": key[1], "index": key[2], "avg_ms": round(avg, 5),
                   "launches": a["count"], "workgroups": a["workgroups"],
-                  "share_of_step": round(a["ms"] / args.steps / ms_per_step, 4),
+                  "share_of_step": round(a["ms"] / args.steps / traced_ms, 4),
                   "tflops": round(ac["flops"] / (avg * 1e-3) / 1e12, 2),
                   "gbps": round(ac["bytes"] / (avg * 1e-3) / 1e9, 1)}
             kernels.append(kr)
@@ -209,7 +239,7 @@ def main():
         key = (dominant["kernel"], dominant["layer"], dominant["index"])
         ac = acct[key]
         avg_s = dominant["avg_ms"] * 1e-3
-        traffic = read_traffic(dominant["kernel"], cfg.name)
+        traffic = read_traffic(dominant["kernel"], dominant["index"], cfg.name)
         if ac["flops"] > 0 and ac["flops"] / ac["bytes"] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
             peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
             ach = ac["flops"] / avg_s / 1e12
@@ -242,6 +272,7 @@ def main():
         "config": {"workload": cfg.name, "global_batch": cfg.batch, "layers": cfg.num_layers, "n": s0.n,
                    "d": s0.d, "k": s0.k, "n_f": s0.n_f, "n_l": s0.n_l, "mlp": list(s0.mlp),
                    "parallelism": "single GPU"},
+        "traced_ms_per_step": None if traced_ms is None else round(traced_ms, 4),
         "step_tflops": round(step_tflops, 2),
         "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
