@@ -3,7 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config layer_d160]
 
 A step is one forward pass of the whole stack (FMB+LCB kernel, every MLP
-Linear, residual LayerNorm, for every layer) over one batch of seeded
+Linear, the residual LayerNorm of the FMB rows, for every layer) over one batch of seeded
 synthetic input that is already resident in HBM.  W untimed warm-up steps,
 then K timed steps bracketed by device synchronisation give `value`.  A
 second pass of K steps runs with HIP events recorded by the library around
@@ -43,8 +43,11 @@ KERNEL_SOURCES = {
 }
 
 
-def kernel_accounting(cfg):
-    """Algorithmic FLOPs and HBM bytes per launch of each kernel of each layer."""
+def kernel_accounting(cfg, fused_layers=()):
+    """Algorithmic FLOPs and HBM bytes per launch of each kernel of each layer.
+    In the layers listed in `fused_layers` the last Linear applies the output
+    LayerNorm itself: it reads the FMB rows of X and writes those of Y instead
+    of writing M, and there is no residual LayerNorm kernel."""
     es = 2 if cfg.dtype == "bf16" else 4
     B = cfg.batch
     out = {}
@@ -55,12 +58,17 @@ def kernel_accounting(cfg):
             # X in; Fn and the LCB rows of Y out; [Phi; W_L] once
             "bytes": B * (n * d + n * k + n_l * d) * es + (k + n_l) * n * es,
         }
+        T = len(s.mlp) - 1
         for t, (a, b) in enumerate(zip(s.mlp[:-1], s.mlp[1:])):
+            fused = li in fused_layers and t == T - 1
             out[("mlp_linear", li, t)] = {
                 "flops": 2 * B * a * b,
-                "bytes": (B * a + a * b + B * b + b) * es,
+                # A, W, bias in; C out (fused: also the FMB rows of X in, C is those of Y)
+                "bytes": (B * a + a * b + B * b + b + (B * b if fused else 0)) * es,
                 "shape": [B, b, a],
             }
+        if li in fused_layers:
+            continue
         out[("residual_ln", li, 0)] = {
             "flops": 0,
             # M and the FMB rows of X in, FMB rows of Y out
@@ -193,7 +201,7 @@ def main():
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
 
     # per-kernel pass: the library records HIP events around every launch on the launch stream
-    kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step
+    kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step (at most)
     trace = None
     traced_ms = None
     if not args.no_trace:
@@ -205,7 +213,8 @@ def main():
         torch.cuda.synchronize()
         traced_ms = (time.perf_counter() - t1) * 1e3 / args.steps
 
-    acct = kernel_accounting(cfg)
+    fused_layers = [li for li, sp in enumerate(specs) if wk.workspace_layout(sp, cfg.batch)["m"] < 0]
+    acct = kernel_accounting(cfg, fused_layers)
     kernels = []
     dominant = None
     if trace is not None:

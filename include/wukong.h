@@ -123,7 +123,10 @@ int32_t wukong_layer_forward(const wk_layer_desc* desc, const wk_layer_weights* 
  *   hidden  [batch, m_t] for t = 1..num_linear-1: hidden[t-1]; the hidden
  *           activations alternate between two buffers, so only the last two
  *           survive (offset -1 marks an overwritten one)
- *   m       [batch, n_f*d]     the last MLP output M
+ *   m       [batch, n_f*d]     the last MLP output M, or -1 when the last
+ *           Linear applies the residual LayerNorm in its own epilogue (bf16
+ *           layers with d in {16, 32, 80, 160} and a last-Linear input width
+ *           that is a multiple of 64): then M is never stored
  * Returns WK_OK, or an error as wukong_layer_forward would for desc/batch. */
 typedef struct {
   int64_t fn;

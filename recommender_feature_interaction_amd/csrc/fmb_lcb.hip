@@ -756,6 +756,7 @@ const FmbLcbVariant kVariants[] = {
     WK_FMB_VARIANT(2, 4, 4, 8, 4, 256),   // d = 32
     WK_FMB_VARIANT(3, 4, 4, 8, 4, 128),   // d = 48
     WK_FMB_VARIANT(4, 4, 4, 8, 4, 128),   // d = 64
+    WK_FMB_VARIANT(5, 4, 4, 8, 4, 128),   // d = 80
     WK_FMB_VARIANT(8, 4, 3, 8, 4, 64),    // d = 128
     WK_FMB_VARIANT(10, 4, 3, 8, 4, 64),   // d = 160
     WK_FMB_VARIANT(10, 8, 3, 4, 8, 64),   // d = 160, larger n / k

@@ -1,34 +1,31 @@
-// FMB-MLP Linear on bf16 MFMA: C[M, N] = act(A[M, K] W[N, K]^T + bias[N]).
+// FMB-MLP Linear on bf16 MFMA: C[M, N] = act(A[M, K] W[N, K]^T + bias[N]),
+// and the last Linear fused with the layer output stage (linear_ln_kernel).
 //
 // The FMB's MLP (Wukong paper, section 2.2; its depth and widths are the
 // "MLP" scaling knob of section 2.3) is where nearly all of a Wukong layer's
-// FLOPs go, so this is a plain dense contraction on v_mfma_f32_32x32x16_bf16
-// with fp32 accumulation.  A is the activation (row-major, K contiguous) and
-// W keeps torch.nn.Linear's [out, in] layout, so both operands are
-// K-contiguous and land in LDS the same way.
-//
-// Tiling: a BM x BN output tile per workgroup of WGM x WGN waves, K in steps
-// of 64.  Global -> registers -> LDS double buffer: the next K tile's loads
-// are in flight while the current one feeds the MFMAs.  LDS rows are 128 B
-// (64 bf16); the 16-byte chunk c of row r is stored at c ^ ((r >> 1) & 7),
-// which keeps both the row-wise stores and the 32-row MFMA fragment reads
-// free of bank conflicts.  Each wave computes W_tile x A_tile^T, i.e. the
-// transposed tile, so a lane ends up holding 4 consecutive output columns of
-// one row: the epilogue adds the bias, applies ReLU, rounds to bf16 and
-// stores 8 bytes per lane.
+// FLOPs go, so this is a plain dense contraction on bf16 MFMA with fp32
+// accumulation.  A is the activation (row-major, K contiguous) and W keeps
+// torch.nn.Linear's [out, in] layout, so both operands are K-contiguous and
+// land in LDS the same way: rows of 64 bf16 (128 B) whose 16-byte chunk c of
+// row r is stored at c ^ ((r >> 1) & 7), which keeps the DMA writes and the
+// 16-row MFMA fragment reads free of bank conflicts.  Each wave computes
+// W_tile x A_tile^T, i.e. the transposed tile, so a lane ends up holding 4
+// consecutive output columns of one row and stores 8 bytes at a time.
 //
 // Tile order: the hardware deals workgroup i to XCD i % 8; the logical tile
 // index is remapped so each XCD gets a contiguous run of tiles, walked in
 // groups of 8 tile-rows so that neighbouring tiles share A and W panels in
 // that XCD's L2.
 //
-// Two kernels share this structure:
+// Kernels:
 //  * linear_dma_kernel (K % 64 == 0, the fast path): v_mfma_f32_16x16x32_bf16,
 //    operands moved global -> LDS by buffer_load ... lds (no staging
 //    registers), two static LDS stages so the next K tile streams in while the
 //    current one is consumed.  Each workgroup's buffer resources start at its
 //    tile's first row and end at the last valid row, so rows past M or N read
 //    as zero.  Barriers are LDS-scoped (they do not wait for global loads).
+//  * linear_ln_kernel: the same main loop on 256 x 320 tiles, whose epilogue
+//    is the layer's output stage for the FMB rows (bias, residual, LayerNorm).
 //  * linear_bf16_kernel (any K % 8 == 0): 32x32x16 MFMA, register-staged
 //    loads with per-element bounds checks.
 #include <mutex>
@@ -51,46 +48,61 @@ struct LinearKArgs {
   int tiles_m, tiles_n;
 };
 
+struct LinearLnKArgs {
+  const uint16_t* a;
+  const uint16_t* w;
+  const uint16_t* bias;
+  const uint16_t* x;      // residual: row m at x + m * ld
+  const uint16_t* gamma;  // [D] or null
+  const uint16_t* beta;   // [D] or null
+  uint16_t* y;            // row m at y + m * ld
+  int64_t M;
+  int N, K;
+  int64_t ld;
+  float eps;
+  int tiles_m, tiles_n;
+};
+
 constexpr int kBK = 64;
+
+#define WK_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * kBK + ((ch ^ ((row >> 1) & 7)) << 3); }
 
-__device__ __forceinline__ void tile_origin(const LinearKArgs& p, int BM, int BN, int64_t& m0, int& n0) {
+__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int BM, int BN, int64_t& m0, int& n0) {
   const int nblk = gridDim.x, bid = blockIdx.x, full = nblk & ~7;
   int logical = bid;
   if (bid < full) logical = (bid & 7) * (full >> 3) + (bid >> 3);
   constexpr int GM = 8;
-  const int per_group = GM * p.tiles_n;
+  const int per_group = GM * tiles_n;
   const int group = logical / per_group;
   const int first_m = group * GM;
-  const int gsz = min(p.tiles_m - first_m, GM);
+  const int gsz = min(tiles_m - first_m, GM);
   const int in_g = logical - group * per_group;
   m0 = (int64_t)(first_m + in_g % gsz) * BM;
   n0 = (in_g / gsz) * BN;
 }
 
-#define WK_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// The K loop of the DMA kernels: acc[i][j] (lane (l16, lg)) ends holding
+// C[m0 + wm WTM + 16 j + l16][n0 + wn WTN + 16 i + 4 lg + t], t = 0..3.
 template <int BM, int BN, int WGM, int WGN>
-__global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs p) {
+__device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint16_t* w_base, int64_t M, int N,
+                                             int K, int64_t m0, int n0, uint16_t* sA0, uint16_t* sW0,
+                                             uint16_t* sA1, uint16_t* sW1,
+                                             f32x4 (&acc)[BN / WGN / 16][BM / WGM / 16]) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MB = WTM / 16, NB = WTN / 16;
   constexpr int A_INS = BM / 8 / NW, W_INS = BN / 8 / NW;  // 1 KB (8 rows) DMA instructions per wave
   static_assert(A_INS * NW * 8 == BM && W_INS * NW * 8 == BN, "tile / wave mismatch");
-  __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
-  int64_t m0;
-  int n0;
-  tile_origin(p, BM, BN, m0, n0);
-  const int64_t M = p.M;
-  const int N = p.N, K = p.K;
   const int rows_a = (int)min<int64_t>(BM, M - m0), rows_w = min(BN, N - n0);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.a + m0 * K), (short)0, rows_a * K * 2, 0x00020000);
+      (void*)(a_base + m0 * K), (short)0, rows_a * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(p.w + (int64_t)n0 * K), (short)0, rows_w * K * 2, 0x00020000);
+      (void*)(w_base + (int64_t)n0 * K), (short)0, rows_w * K * 2, 0x00020000);
   // A DMA instruction writes 64 lanes x 16 B = 8 LDS rows; lane -> row lane/8,
   // LDS chunk lane%8, which holds global chunk (lane%8) ^ swizzle(row).  The
   // swizzle of row 8b + r is (4(b & 1) + r/2) & 7: two lane offsets suffice.
@@ -112,13 +124,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
                                                ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, k0 * 2, 0, 0);
     }
   };
-  f32x4 acc[NB][MB];
 #pragma unroll
   for (int i = 0; i < NB; ++i)
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int l16 = lane & 15, lg = lane >> 4;
-  // W_tile x A_tile^T: lane (l16, lg) ends with C[m0 + .. + l16][n .. n + 3]
+  // W_tile x A_tile^T: the transposed tile, so a lane holds 4 consecutive output columns
   auto compute = [&](const uint16_t* a, const uint16_t* w) {
 #pragma unroll
     for (int ks = 0; ks < kBK / 32; ++ks) {
@@ -150,6 +161,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
       lds_barrier();
     }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs p) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l16 = lane & 15, lg = lane >> 4;
+  int64_t m0;
+  int n0;
+  tile_origin(p.tiles_m, p.tiles_n, BM, BN, m0, n0);
+  const int64_t M = p.M;
+  const int N = p.N;
+  f32x4 acc[NB][MB];
+  dma_mainloop<BM, BN, WGM, WGN>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
   const uint16_t* bias = p.bias;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -173,6 +201,104 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
         o[0] = pack_bf16x2(v[0], v[1]);
         o[1] = pack_bf16x2(v[2], v[3]);
         *reinterpret_cast<u32x2*>(p.c + m * N + n) = o;
+      }
+    }
+  }
+}
+
+// The FMB MLP's last Linear with the layer's output stage fused into its
+// epilogue (Wukong paper, section 2.2: the FMB output reshaped to n_F x d,
+// concatenated with the LCB output, residual added, LayerNorm per embedding).
+// GEMM column c of example m is embedding row c / D, element c % D, which sits
+// at y + m ld + c because the FMB rows come first in the layer output.  A wave
+// covers WTN = 160 columns, a whole number of embedding rows, and a lane holds
+// 4 consecutive columns of one row for each 16-column block, so one embedding
+// row is D/16 blocks x 4 columns x the 4 lanes l16 + 16 lg: its LayerNorm
+// statistics are a sum over registers and two xor-shuffles.  M is rounded to
+// bf16 before the residual is added, as the unfused path stores it.
+template <int BM, int BN, int WGM, int WGN, int D>
+__global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs p) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  constexpr int GI = D / 16;    // 16-column blocks per embedding row
+  constexpr int NG = WTN / D;   // embedding rows per wave and example
+  static_assert(D % 16 == 0 && WTN % D == 0, "a wave must cover whole embedding rows");
+  __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l16 = lane & 15, lg = lane >> 4;
+  int64_t m0;
+  int n0;
+  tile_origin(p.tiles_m, p.tiles_n, BM, BN, m0, n0);
+  const int64_t M = p.M;
+  const int N = p.N;
+  f32x4 acc[NB][MB];
+  dma_mainloop<BM, BN, WGM, WGN>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
+
+  // M = bf16(acc + bias), in place
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int c = n0 + wn * WTN + i * 16 + lg * 4;
+    u32x2 b2 = u32x2{0u, 0u};
+    if (p.bias && c < N) b2 = *reinterpret_cast<const u32x2*>(p.bias + c);
+    const float bb[4] = {bf16lo(b2[0]), bf16hi(b2[0]), bf16lo(b2[1]), bf16hi(b2[1])};
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const uint32_t h0 = pack_bf16x2(acc[i][j][0] + bb[0], acc[i][j][1] + bb[1]);
+      const uint32_t h1 = pack_bf16x2(acc[i][j][2] + bb[2], acc[i][j][3] + bb[3]);
+      acc[i][j] = f32x4{bf16lo(h0), bf16hi(h0), bf16lo(h1), bf16hi(h1)};
+    }
+  }
+  const float inv_d = 1.0f / static_cast<float>(D);
+#pragma unroll
+  for (int g = 0; g < NG; ++g) {
+    const int c0 = n0 + wn * WTN + g * D;  // first column of this embedding row
+    if (c0 >= N) break;                    // wave-uniform; N is a multiple of D
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int64_t m = m0 + wm * WTM + j * 16 + l16;
+      const bool valid = m < M;
+      const uint16_t* xrow = p.x + m * p.ld + c0;
+      float sm = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < GI; ++ii) {
+        const u32x2 xv = valid ? *reinterpret_cast<const u32x2*>(xrow + ii * 16 + lg * 4) : u32x2{0u, 0u};
+        f32x4& r = acc[g * GI + ii][j];
+        r[0] += bf16lo(xv[0]);
+        r[1] += bf16hi(xv[0]);
+        r[2] += bf16lo(xv[1]);
+        r[3] += bf16hi(xv[1]);
+        sm += (r[0] + r[1]) + (r[2] + r[3]);
+      }
+      sm += __shfl_xor(sm, 16, kWave);
+      sm += __shfl_xor(sm, 32, kWave);
+      const float mean = sm * inv_d;
+      float q = 0.f;
+#pragma unroll
+      for (int ii = 0; ii < GI; ++ii)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float dv = acc[g * GI + ii][j][t] - mean;
+          q += dv * dv;
+        }
+      q += __shfl_xor(q, 16, kWave);
+      q += __shfl_xor(q, 32, kWave);
+      const float rstd = rsqrtf(q * inv_d + p.eps);
+      if (valid) {
+        uint16_t* yrow = p.y + m * p.ld + c0;
+#pragma unroll
+        for (int ii = 0; ii < GI; ++ii) {
+          const int e = ii * 16 + lg * 4;
+          const u32x2 g2 = p.gamma ? *reinterpret_cast<const u32x2*>(p.gamma + e) : u32x2{0x3f803f80u, 0x3f803f80u};
+          const u32x2 e2 = p.beta ? *reinterpret_cast<const u32x2*>(p.beta + e) : u32x2{0u, 0u};
+          const f32x4 r = acc[g * GI + ii][j];
+          u32x2 o;
+          o[0] = pack_bf16x2((r[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(e2[0]),
+                             (r[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(e2[0]));
+          o[1] = pack_bf16x2((r[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(e2[1]),
+                             (r[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(e2[1]));
+          *reinterpret_cast<u32x2*>(yrow + e) = o;
+        }
       }
     }
   }
@@ -363,7 +489,53 @@ const LinearVariant* pick_linear(int64_t M, int N, int K) {
   return best;
 }
 
+// Fused Linear + output LayerNorm: 256 x 320 tiles, 8 waves of 64 rows x 160
+// columns; 160 must be a whole number of embedding rows.
+struct LinearLnVariant {
+  int d;
+  void (*kernel)(LinearLnKArgs);
+};
+#define WK_LN_VARIANT(D) LinearLnVariant { D, linear_ln_kernel<256, 320, 4, 2, D> }
+const LinearLnVariant kLnVariants[] = {WK_LN_VARIANT(16), WK_LN_VARIANT(32), WK_LN_VARIANT(80),
+                                       WK_LN_VARIANT(160)};
+constexpr int kLnBM = 256, kLnBN = 320, kLnThreads = 512;
+
+const LinearLnVariant* pick_linear_ln(int d) {
+  for (const auto& v : kLnVariants)
+    if (v.d == d) return &v;
+  return nullptr;
+}
+
 }  // namespace
+
+bool linear_ln_bf16_supported(int64_t M, int N, int K, int d) {
+  return M > 0 && K > 0 && K % kBK == 0 && d > 0 && N % d == 0 && N > 0 && pick_linear_ln(d) != nullptr;
+}
+
+hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int64_t* workgroups) {
+  const LinearLnVariant* v = pick_linear_ln(a.d);
+  if (!v || !linear_ln_bf16_supported(a.M, a.N, a.K, a.d)) return hipErrorInvalidValue;
+  LinearLnKArgs k;
+  k.a = static_cast<const uint16_t*>(a.a);
+  k.w = static_cast<const uint16_t*>(a.w);
+  k.bias = static_cast<const uint16_t*>(a.bias);
+  k.x = static_cast<const uint16_t*>(a.x);
+  k.gamma = static_cast<const uint16_t*>(a.gamma);
+  k.beta = static_cast<const uint16_t*>(a.beta);
+  k.y = static_cast<uint16_t*>(a.y);
+  k.M = a.M;
+  k.N = a.N;
+  k.K = a.K;
+  k.ld = a.ld;
+  k.eps = a.eps;
+  k.tiles_m = (int)((a.M + kLnBM - 1) / kLnBM);
+  k.tiles_n = (a.N + kLnBN - 1) / kLnBN;
+  const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;
+  if (workgroups) *workgroups = blocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(v->kernel, dim3((unsigned)blocks), dim3(kLnThreads), 0, stream, k);
+  return hipGetLastError();
+}
 
 bool linear_bf16_supported(int64_t M, int N, int K) {
   return M > 0 && N > 0 && K > 0 && (K % 8) == 0 && (N % 8) == 0;

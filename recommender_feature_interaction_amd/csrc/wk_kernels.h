@@ -56,6 +56,25 @@ bool linear_bf16_supported(int64_t M, int N, int K);
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);
 
+// The last Linear with the FMB rows' output stage fused in (bf16):
+// Y[b, r] = LN_d(bf16(A[b] W^T + bias)[r d .. r d + d) + X[b, r]) for r < n_f,
+// with X and Y rows of example b at b * ld (ld = n * d).  N = n_f * d.
+struct LinearLnArgs {
+  const void* a;
+  const void* w;
+  const void* bias;   // or null
+  const void* x;      // [B, n, d]
+  const void* gamma;  // [d] or null
+  const void* beta;   // [d] or null
+  void* y;            // [B, n, d]: rows 0..n_f-1 are written
+  int64_t M;
+  int N, K, d;
+  int64_t ld;
+  float eps;
+};
+bool linear_ln_bf16_supported(int64_t M, int N, int K, int d);
+hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int64_t* workgroups);
+
 // FMB rows of the layer output: Y[b, r] = LN_d(M[b, r] + X[b, r]) for r < n_f.
 struct ResidLnArgs {
   const void* m;  // [B, n_f, d]

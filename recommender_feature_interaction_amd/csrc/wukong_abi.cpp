@@ -3,9 +3,12 @@
 //
 // Per layer (Wukong paper, section 2.2, xdnf.cn repost), on one stream:
 //   1. FMB+LCB kernel: X -> Fn (workspace) and the LCB rows of Y
-//   2. one MLP Linear per FMB-MLP layer: Fn -> h_1 -> ... -> M (workspace),
-//      bias + ReLU fused, no ReLU after the last
-//   3. residual LayerNorm of the FMB rows: (M, X) -> rows 0..n_F-1 of Y
+//   2. one MLP Linear per FMB-MLP layer: Fn -> h_1 -> ... -> M, bias + ReLU
+//      fused, no ReLU after the last
+//   3. rows 0..n_F-1 of Y = LayerNorm(M + X).  In bf16, when d divides 160
+//      and the last Linear's K is a multiple of 64, this stage is the last
+//      Linear's epilogue and M never leaves registers; otherwise M goes to
+//      the workspace and a residual LayerNorm kernel follows.
 // A stack (section 2.3: l layers) chains layers through two ping-pong
 // buffers in the workspace; the last layer writes y.  No host sync anywhere.
 #include <hip/hip_runtime.h>
@@ -69,7 +72,14 @@ int32_t check_desc(const wk_layer_desc* d) {
 struct LayerPlan {
   size_t fn = 0, h[2] = {0, 0}, m = 0, bytes = 0;
   int num_hidden_bufs = 0;
+  bool fused_out = false;  // last Linear writes the FMB rows of Y itself; no M buffer
 };
+
+// Whether the last Linear carries the residual LayerNorm in its epilogue.
+bool fuse_output_ln(const wk_layer_desc& d) {
+  return d.dtype == WK_BF16 &&
+         wk::linear_ln_bf16_supported(1, d.mlp_dims[d.num_linear], d.mlp_dims[d.num_linear - 1], d.d);
+}
 
 // Largest batch the launch geometry handles (one workgroup per example in the
 // FMB+LCB kernel; grid dimensions are 32-bit).
@@ -89,8 +99,11 @@ LayerPlan plan_layer(const wk_layer_desc& d, int64_t batch) {
     p.h[i] = off;
     off += align_up(B * (size_t)maxhid * es);
   }
-  p.m = off;
-  off += align_up(B * (size_t)d.n_f * d.d * es);
+  p.fused_out = fuse_output_ln(d);
+  if (!p.fused_out) {
+    p.m = off;
+    off += align_up(B * (size_t)d.n_f * d.d * es);
+  }
   p.bytes = off;
   return p;
 }
@@ -172,7 +185,8 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
   if (st != WK_OK) return st;
 
   const void* in = fn;
-  for (int t = 0; t < d.num_linear; ++t) {
+  const int unfused = plan.fused_out ? d.num_linear - 1 : d.num_linear;
+  for (int t = 0; t < unfused; ++t) {
     const bool last = t == d.num_linear - 1;
     void* out = last ? static_cast<void*>(mbuf) : static_cast<void*>(scratch + plan.h[t % 2]);
     wk::LinearArgs a;
@@ -189,6 +203,26 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     });
     if (st != WK_OK) return st;
     in = out;
+  }
+
+  if (plan.fused_out) {
+    const int t = d.num_linear - 1;
+    wk::LinearLnArgs a;
+    a.a = in;
+    a.w = w.mlp_w[t];
+    a.bias = w.mlp_b ? w.mlp_b[t] : nullptr;
+    a.x = x;
+    a.gamma = w.out_ln_gamma;
+    a.beta = w.out_ln_beta;
+    a.y = y;
+    a.M = batch;
+    a.N = d.mlp_dims[t + 1];
+    a.K = d.mlp_dims[t];
+    a.d = d.d;
+    a.ld = (int64_t)d.n * d.d;
+    a.eps = d.ln_eps;
+    return launch(WK_KERNEL_MLP_LINEAR, layer_idx, t,
+                  [&](int64_t* g) { return wk::launch_linear_ln_bf16(a, launch.stream, g); });
   }
 
   wk::ResidLnArgs r;
@@ -297,7 +331,7 @@ int32_t wukong_layer_workspace_layout(const wk_layer_desc* desc, int64_t batch, 
   if (st != WK_OK) return st;
   const LayerPlan p = plan_layer(*desc, batch);
   out->fn = (int64_t)p.fn;
-  out->m = (int64_t)p.m;
+  out->m = p.fused_out ? -1 : (int64_t)p.m;
   out->num_hidden = desc->num_linear - 1;
   for (int i = 0; i < 8; ++i) out->hidden[i] = -1;
   for (int t = 1; t < desc->num_linear && t <= 8; ++t) {

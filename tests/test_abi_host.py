@@ -50,14 +50,21 @@ def al(v):
 
 def test_workspace_sizes_follow_layout():
     B = 4096
-    # Fn + one hidden buffer + M
-    assert wk.layer_workspace_size(C1, B) == al(B * 4096 * 2) + al(B * 2048 * 2) + al(B * 10240 * 2)
+    # Fn + one hidden buffer; d = 160 and K = 2048: the last Linear writes Y itself, no M
+    assert wk.layer_workspace_size(C1, B) == al(B * 4096 * 2) + al(B * 2048 * 2)
     lay = wk.workspace_layout(C1, B)
     assert lay["fn"] == 0 and lay["hidden"] == [al(B * 4096 * 2)]
-    assert lay["m"] == al(B * 4096 * 2) + al(B * 2048 * 2)
+    assert lay["m"] == -1
+    # d = 48 does not divide the fused epilogue's 160 columns: M is stored
+    d48 = wk.LayerSpec(96, 48, 20, 40, 56, (1920, 256, 1920))
+    assert wk.layer_workspace_size(d48, B) == al(B * 1920 * 2) + al(B * 256 * 2) + al(B * 1920 * 2)
+    assert wk.workspace_layout(d48, B)["m"] == al(B * 1920 * 2) + al(B * 256 * 2)
+    # K of the last Linear not a multiple of 64: M is stored
+    k72 = wk.LayerSpec(40, 32, 12, 16, 24, (480, 72, 512))
+    assert wk.workspace_layout(k72, B)["m"] == al(B * 480 * 2) + al(B * 72 * 2)
     # two hidden ping-pong buffers
     B = 100
-    assert wk.layer_workspace_size(C2, B) == al(B * 12288 * 2) + 2 * al(B * 4096 * 2) + al(B * 20480 * 2)
+    assert wk.layer_workspace_size(C2, B) == al(B * 12288 * 2) + 2 * al(B * 4096 * 2)
     # stacks add ping-pong activation buffers
     scratch = wk.layer_workspace_size(C2, B)
     act = al(B * 256 * 160 * 2)
