@@ -779,12 +779,20 @@ const FmbLcbVariant* pick(int n, int d, int k, int n_l) {
 }  // namespace
 
 bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l) {
-  return pick_resident(n, d, k, n_l) != nullptr || pick(n, d, k, n_l) != nullptr;
+  return fmb_lcb_stream_supported(n, d, k, n_l) || pick_resident(n, d, k, n_l) != nullptr ||
+         pick(n, d, k, n_l) != nullptr;
 }
 
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups) {
-  if (const ResidentVariant* r = pick_resident(a.n, a.d, a.k, a.n_l)) {
+  // Order: the resident kernel when [Phi; W_L] fits in its LDS next to X (the
+  // weights are then read once per workgroup), else the streamed kernel (X
+  // and the weights through an LDS ring, several examples per workgroup),
+  // else the resident or chunked kernels.
+  const ResidentVariant* res = pick_resident(a.n, a.d, a.k, a.n_l);
+  if (!(res && res->wl) && fmb_lcb_stream_supported(a.n, a.d, a.k, a.n_l))
+    return launch_fmb_lcb_stream(a, batch, stream, workgroups);
+  if (const ResidentVariant* r = res) {
     const int64_t grid = batch < (int64_t)256 * r->per_cu ? batch : (int64_t)256 * r->per_cu;
     if (workgroups) *workgroups = grid;
     if (batch == 0) return hipSuccess;

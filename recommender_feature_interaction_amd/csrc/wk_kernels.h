@@ -22,6 +22,11 @@ struct FmbLcbArgs {
   float eps;
 };
 bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l);
+// Streamed variant (fmb_lcb_stream.hip): several examples per workgroup, the
+// weights and X rows DMA'd through an LDS ring.  Used first when it supports
+// the shape.
+bool fmb_lcb_stream_supported(int n, int d, int k, int n_l);
+hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups);
 
