@@ -67,6 +67,10 @@ constexpr int kBK = 64;
 
 #define WK_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) alone, and lgkmcnt(0) alone
+constexpr int vm_wait(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+constexpr int lgkm_wait0() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }
+
 __device__ __forceinline__ int swz(int row, int ch) { return row * kBK + ((ch ^ ((row >> 1) & 7)) << 3); }
 
 __device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int BM, int BN, int64_t& m0, int& n0) {
@@ -222,9 +226,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
   constexpr int MB = WTM / 16, NB = WTN / 16;
   constexpr int GI = D / 16;    // 16-column blocks per embedding row
   constexpr int NG = WTN / D;   // embedding rows per wave and example
+  constexpr int NW = WGM * WGN;
+  constexpr int RES = 16 * WTN;        // u16 of one wave's 16-row residual block
+  constexpr int RES_INS = RES * 2 / 1024;  // 1 KB DMA instructions per block
   static_assert(D % 16 == 0 && WTN % D == 0, "a wave must cover whole embedding rows");
+  static_assert(RES_INS * 1024 == RES * 2 && NW * RES <= BN * kBK, "residual blocks fit a W stage");
   __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __align__(16) uint16_t Es[BN + 2 * D];  // bias of the tile's columns, then gamma, beta
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave % WGM, wn = wave / WGM;
   const int l16 = lane & 15, lg = lane >> 4;
   int64_t m0;
@@ -232,15 +242,46 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
   tile_origin(p.tiles_m, p.tiles_n, BM, BN, m0, n0);
   const int64_t M = p.M;
   const int N = p.N;
+  // epilogue constants staged before the main loop (whose first wait covers these loads), so the
+  // epilogue issues no global loads besides its residual DMA
+  for (int i = threadIdx.x; i < BN + 2 * D; i += NW * 64) {
+    uint16_t v;
+    if (i < BN) v = (p.bias && n0 + i < N) ? p.bias[n0 + i] : (uint16_t)0;
+    else if (i < BN + D) v = p.gamma ? p.gamma[i - BN] : (uint16_t)0x3f80u;
+    else v = p.beta ? p.beta[i - BN - D] : (uint16_t)0;
+    Es[i] = v;
+  }
   f32x4 acc[NB][MB];
   dma_mainloop<BM, BN, WGM, WGN>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
 
+  // Residual rows: each wave DMAs its own 16-row x WTN-column blocks (block j: tile rows
+  // wm WTM + 16 j ..) into a private slice of the now idle W stages, two blocks ahead, so
+  // the loads overlap the LayerNorms.  Rows past M read as zero and their stores are
+  // dropped (buffer resources end at row M).
+  const int rows = (int)min<int64_t>(BM, M - m0);
+  const __amdgpu_buffer_rsrc_t rx =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.x + m0 * p.ld), (short)0, (int)(rows * p.ld * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ry =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.y + m0 * p.ld), (short)0, (int)(rows * p.ld * 2), 0x00020000);
+  const int cw = n0 + wn * WTN;  // first column of this wave
+  uint16_t* const slot[2] = {sW0 + wave * RES, sW1 + wave * RES};
+  auto dma_res = [&](int j, uint16_t* dst) {
+#pragma unroll
+    for (int q = 0; q < RES_INS; ++q) {
+      const int u = q * 64 + lane;  // 16-byte unit of the block
+      const int r = u / (WTN / 8), ch = u - r * (WTN / 8);
+      const uint32_t vo = (uint32_t)(((int64_t)(wm * WTM + j * 16 + r) * p.ld + cw + ch * 8) * 2);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, WK_LDS(dst + q * 512), 16, vo, 0, 0, 0);
+    }
+  };
+  if (cw < N) {  // wave-uniform
+    dma_res(0, slot[0]);
+    if (MB > 1) dma_res(1, slot[1]);
+  }
   // M = bf16(acc + bias), in place
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int c = n0 + wn * WTN + i * 16 + lg * 4;
-    u32x2 b2 = u32x2{0u, 0u};
-    if (p.bias && c < N) b2 = *reinterpret_cast<const u32x2*>(p.bias + c);
+    const u32x2 b2 = *reinterpret_cast<const u32x2*>(Es + wn * WTN + i * 16 + lg * 4);
     const float bb[4] = {bf16lo(b2[0]), bf16hi(b2[0]), bf16lo(b2[1]), bf16hi(b2[1])};
 #pragma unroll
     for (int j = 0; j < MB; ++j) {
@@ -249,20 +290,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
       acc[i][j] = f32x4{bf16lo(h0), bf16hi(h0), bf16lo(h1), bf16hi(h1)};
     }
   }
+  if (cw >= N) return;  // wave-uniform: this wave's columns are all past N
   const float inv_d = 1.0f / static_cast<float>(D);
+  constexpr int ST = NG * GI;  // Y stores per row block
 #pragma unroll
-  for (int g = 0; g < NG; ++g) {
-    const int c0 = n0 + wn * WTN + g * D;  // first column of this embedding row
-    if (c0 >= N) break;                    // wave-uniform; N is a multiple of D
+  for (int j = 0; j < MB; ++j) {
+    // block j must have landed; younger: block j+1's DMA (if issued before it) and the
+    // stores of block j-1 and block j+1's DMA (issued after)
+    if (j == 0) {
+      if (MB > 1) __builtin_amdgcn_s_waitcnt(vm_wait(RES_INS)); else __builtin_amdgcn_s_waitcnt(vm_wait(0));
+    } else if (j + 1 < MB) {
+      __builtin_amdgcn_s_waitcnt(vm_wait(ST + RES_INS));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_wait(ST));
+    }
+    const uint16_t* res = slot[j & 1] + l16 * WTN + lg * 4;
 #pragma unroll
-    for (int j = 0; j < MB; ++j) {
-      const int64_t m = m0 + wm * WTM + j * 16 + l16;
-      const bool valid = m < M;
-      const uint16_t* xrow = p.x + m * p.ld + c0;
+    for (int g = 0; g < NG; ++g) {
       float sm = 0.f;
 #pragma unroll
       for (int ii = 0; ii < GI; ++ii) {
-        const u32x2 xv = valid ? *reinterpret_cast<const u32x2*>(xrow + ii * 16 + lg * 4) : u32x2{0u, 0u};
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(res + g * D + ii * 16);
         f32x4& r = acc[g * GI + ii][j];
         r[0] += bf16lo(xv[0]);
         r[1] += bf16hi(xv[0]);
@@ -284,22 +332,27 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
       q += __shfl_xor(q, 16, kWave);
       q += __shfl_xor(q, 32, kWave);
       const float rstd = rsqrtf(q * inv_d + p.eps);
-      if (valid) {
-        uint16_t* yrow = p.y + m * p.ld + c0;
+      const int c0 = cw + g * D;
+      // columns past N belong to no embedding row of this layer: offset past the resource
+      const uint32_t yoff = c0 < N ? (uint32_t)(((int64_t)(wm * WTM + j * 16 + l16) * p.ld + c0) * 2) : 0x80000000u;
 #pragma unroll
-        for (int ii = 0; ii < GI; ++ii) {
-          const int e = ii * 16 + lg * 4;
-          const u32x2 g2 = p.gamma ? *reinterpret_cast<const u32x2*>(p.gamma + e) : u32x2{0x3f803f80u, 0x3f803f80u};
-          const u32x2 e2 = p.beta ? *reinterpret_cast<const u32x2*>(p.beta + e) : u32x2{0u, 0u};
-          const f32x4 r = acc[g * GI + ii][j];
-          u32x2 o;
-          o[0] = pack_bf16x2((r[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(e2[0]),
-                             (r[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(e2[0]));
-          o[1] = pack_bf16x2((r[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(e2[1]),
-                             (r[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(e2[1]));
-          *reinterpret_cast<u32x2*>(yrow + e) = o;
-        }
+      for (int ii = 0; ii < GI; ++ii) {
+        const int e = ii * 16 + lg * 4;
+        const u32x2 g2 = *reinterpret_cast<const u32x2*>(Es + BN + e);
+        const u32x2 e2 = *reinterpret_cast<const u32x2*>(Es + BN + D + e);
+        const f32x4 r = acc[g * GI + ii][j];
+        u32x2 o;
+        o[0] = pack_bf16x2((r[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(e2[0]),
+                           (r[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(e2[0]));
+        o[1] = pack_bf16x2((r[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(e2[1]),
+                           (r[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(e2[1]));
+        __builtin_amdgcn_raw_buffer_store_b64(o, ry, yoff + e * 2, 0, 0);
       }
+    }
+    if (j + 2 < MB) {
+      // this wave's reads of the slot are done before the DMA reuses it
+      __builtin_amdgcn_s_waitcnt(lgkm_wait0());
+      dma_res(j + 2, slot[j & 1]);
     }
   }
 }
