@@ -90,7 +90,21 @@ __device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int BM, in
 
 // The K loop of the DMA kernels: acc[i][j] (lane (l16, lg)) ends holding
 // C[m0 + wm WTM + 16 j + l16][n0 + wn WTN + 16 i + 4 lg + t], t = 0..3.
-template <int BM, int BN, int WGM, int WGN>
+// MFMA / VMEM interleave for the scheduler: MPER MFMAs, then one VMEM read, N times.
+template <int N, int MPER>
+__device__ __forceinline__ void interleave_mfma_vmem() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(0x008, MPER, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    interleave_mfma_vmem<N - 1, MPER>();
+  }
+}
+
+// SPREAD: the next stage's DMA is issued between the first half-step's MFMAs
+// instead of in one burst, and the stage loop has no branch (K % 128 == 0;
+// the DMA issued after the last stage reads the rows' next 64 columns or
+// zeros past the resource and lands in a stage nobody reads).
+template <int BM, int BN, int WGM, int WGN, bool SPREAD = false>
 __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint16_t* w_base, int64_t M, int N,
                                              int K, int64_t m0, int n0, uint16_t* sA0, uint16_t* sW0,
                                              uint16_t* sA1, uint16_t* sW1,
@@ -153,6 +167,42 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   dma(sA0, sW0, 0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
   lds_barrier();
+  if constexpr (SPREAD) {
+    constexpr int INS = A_INS + W_INS, MPER = NB * MB / INS;
+    static_assert(MPER * INS <= NB * MB, "at least one MFMA per DMA instruction");
+    auto stage = [&](const uint16_t* a, const uint16_t* w, uint16_t* na, uint16_t* nw, int nk0) {
+      u32x4 wf[NB], af[MB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) wf[i] = *reinterpret_cast<const u32x4*>(w + swz(wn * WTN + i * 16 + l16, lg));
+#pragma unroll
+      for (int j = 0; j < MB; ++j) af[j] = *reinterpret_cast<const u32x4*>(a + swz(wm * WTM + j * 16 + l16, lg));
+      dma(na, nw, nk0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j) acc[i][j] = mfma16x16x32(wf[i], af[j], acc[i][j]);
+      __builtin_amdgcn_sched_group_barrier(0x100, NB + MB, 0);  // the fragment reads first
+      interleave_mfma_vmem<INS, MPER>();
+      __builtin_amdgcn_sched_group_barrier(0x008, NB * MB - MPER * INS, 0);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) wf[i] = *reinterpret_cast<const u32x4*>(w + swz(wn * WTN + i * 16 + l16, 4 + lg));
+#pragma unroll
+      for (int j = 0; j < MB; ++j) af[j] = *reinterpret_cast<const u32x4*>(a + swz(wm * WTM + j * 16 + l16, 4 + lg));
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j) acc[i][j] = mfma16x16x32(wf[i], af[j], acc[i][j]);
+    };
+    for (int kt = 0; kt < KT; kt += 2) {
+      stage(sA0, sW0, sA1, sW1, (kt + 1) * kBK);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      lds_barrier();
+      stage(sA1, sW1, sA0, sW0, (kt + 2) * kBK);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      lds_barrier();
+    }
+    return;
+  }
   for (int kt = 0; kt < KT; kt += 2) {
     if (kt + 1 < KT) dma(sA1, sW1, (kt + 1) * kBK);
     compute(sA0, sW0);
@@ -167,7 +217,7 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   }
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, bool SPREAD>
 __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs p) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MB = WTM / 16, NB = WTN / 16;
@@ -181,7 +231,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
   const int64_t M = p.M;
   const int N = p.N;
   f32x4 acc[NB][MB];
-  dma_mainloop<BM, BN, WGM, WGN>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
+  dma_mainloop<BM, BN, WGM, WGN, SPREAD>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
   const uint16_t* bias = p.bias;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
@@ -501,21 +551,24 @@ struct LinearVariant {
   void (*kernel)(LinearKArgs);
   size_t dyn_lds;  // dynamic LDS bytes (the DMA kernels use static LDS)
   int threads;
-  bool needs_k64;
+  int kmod;        // K must be a multiple of this (64 or 128: DMA kernels; 8: register-staged)
 };
 
-#define WK_DMA_VARIANT(BM, BN, WGM, WGN, OCC, EFF) \
-  LinearVariant { BM, BN, OCC, EFF, linear_dma_kernel<BM, BN, WGM, WGN>, 0, WGM * WGN * 64, true }
+#define WK_DMA_VARIANT(BM, BN, WGM, WGN, OCC, EFF, SPREAD)                                              \
+  LinearVariant {                                                                                     \
+    BM, BN, OCC, EFF, linear_dma_kernel<BM, BN, WGM, WGN, SPREAD>, 0, WGM * WGN * 64, SPREAD ? 128 : 64 \
+  }
 #define WK_LIN_VARIANT(BM, BN, WGM, WGN, OCC, EFF)                                                   \
   LinearVariant {                                                                                    \
     BM, BN, OCC, EFF, linear_bf16_kernel<BM, BN, WGM, WGN>, (size_t)2 * (BM + BN) * kBK * 2, WGM * WGN * 64, \
-        false                                                                                        \
+        8                                                                                            \
   }
 
 const LinearVariant kLinVariants[] = {
-    WK_DMA_VARIANT(256, 256, 2, 4, 1, 1.00f),
-    WK_DMA_VARIANT(256, 128, 2, 4, 1, 0.78f),
-    WK_DMA_VARIANT(128, 128, 2, 2, 2, 0.80f),
+    WK_DMA_VARIANT(256, 256, 2, 4, 1, 1.00f, false),
+    WK_DMA_VARIANT(256, 128, 2, 4, 1, 0.78f, false),
+    WK_DMA_VARIANT(128, 128, 2, 2, 2, 0.84f, true),   // DMA spread over the MFMAs: ~5 % over the burst form
+    WK_DMA_VARIANT(128, 128, 2, 2, 2, 0.80f, false),
     WK_LIN_VARIANT(256, 256, 2, 2, 1, 0.55f),
     WK_LIN_VARIANT(256, 128, 2, 2, 1, 0.50f),
     WK_LIN_VARIANT(128, 128, 2, 2, 2, 0.45f),
@@ -529,7 +582,8 @@ const LinearVariant* pick_linear(int64_t M, int N, int K) {
   const LinearVariant* best = nullptr;
   double best_cost = 0;
   for (const auto& v : kLinVariants) {
-    if (v.needs_k64 != k64) continue;
+    // the DMA family when K % 64 == 0 (the spread form also needs K % 128 == 0), else the fallbacks
+    if ((v.kmod >= kBK) != k64 || K % v.kmod != 0) continue;
     const double tiles = (double)((M + v.bm - 1) / v.bm) * (double)((N + v.bn - 1) / v.bn);
     const double slots = (double)kNumCU * v.occupancy;
     const double rounds = (tiles + slots - 1) / slots;

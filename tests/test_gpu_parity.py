@@ -93,6 +93,8 @@ RAGGED = [
     _custom("fused_d80", "bf16", 24, 80, 8, 10, (192, 64, 800), 7),
     _custom("fused_d16_one_linear", "bf16", 32, 16, 4, 12, (128, 192), 3),
     _custom("fused_d160_stack2", "bf16", 16, 160, 4, 8, (64, 128, 1280), 260, layers=2),
+    # K % 128 == 0 on a ragged batch: the Linear whose DMA is spread over its MFMAs
+    _custom("spread_k256_m37", "bf16", 32, 32, 8, 16, (256, 384, 512), 37),
     _custom("ragged_f32", "f32", 12, 24, 3, 5, (36, 20, 120), 9),
     _custom("ragged_f32_stack", "f32", 12, 24, 3, 5, (36, 20, 120), 4, layers=2),
 ]
