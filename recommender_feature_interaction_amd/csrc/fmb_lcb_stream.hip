@@ -50,23 +50,8 @@ constexpr int NWAVE = 8;
 constexpr int NTHREAD = NWAVE * 64;
 constexpr uint32_t kOOB = 0x80000000u;  // a voffset past every record count: the lane reads zero
 
-// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt not waited for), n <= 63
+// s_waitcnt vmcnt(n) immediate (gfx9 encoding; expcnt and lgkmcnt not waited for), n <= 63
 constexpr int vm_enc(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
-#define WK_VM_CASE(n) \
-  case n:             \
-    __builtin_amdgcn_s_waitcnt(vm_enc(n)); \
-    break;
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-    WK_VM_CASE(1) WK_VM_CASE(2) WK_VM_CASE(3) WK_VM_CASE(4) WK_VM_CASE(5) WK_VM_CASE(6)
-    WK_VM_CASE(7) WK_VM_CASE(8) WK_VM_CASE(9) WK_VM_CASE(10) WK_VM_CASE(11) WK_VM_CASE(12)
-    WK_VM_CASE(13) WK_VM_CASE(14) WK_VM_CASE(15) WK_VM_CASE(16) WK_VM_CASE(17) WK_VM_CASE(18)
-    WK_VM_CASE(19) WK_VM_CASE(20) WK_VM_CASE(21) WK_VM_CASE(22) WK_VM_CASE(23) WK_VM_CASE(24)
-    default:  // 0, or more than the table holds: wait for everything
-      __builtin_amdgcn_s_waitcnt(vm_enc(0));
-  }
-}
-#undef WK_VM_CASE
 
 struct StreamShape {
   int zt;    // 16-row tiles of [Phi; W_L]: kz + ceil(n_l / 16)
@@ -79,7 +64,10 @@ struct StreamShape {
 // plus 8 (zero padding).
 __host__ __device__ constexpr int zs_pitch(int d) { return (d + 31) / 32 * 32 + 8; }
 
-template <int ET, int ZPW, int WZ, int WE, int EPW, int MPW, int KJ, int ZTMAX, int S>
+// GUARD: a wave skips its weight tiles past the shape's ZT (operands read first, one test per
+// tile); without it every wave computes all WZ * ZPW tiles, the ones past ZT reading zero tiles
+// of the slot (needs ZTMAX >= WZ * ZPW), branch-free with each operand consumed as it is read.
+template <int ET, int ZPW, int WZ, int WE, int EPW, int MPW, int KJ, int ZTMAX, int S, bool GUARD>
 __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p, int64_t batch, StreamShape sh) {
   constexpr int D = 16 * ET;
   constexpr int E = WE * EPW;
@@ -87,11 +75,20 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
   constexpr int DZ = (D + 31) / 32 * 32;
   constexpr int NKS = DZ / 32;                 // 32-wide K steps of phase 2
   constexpr bool GB_REG = MPW * KJ <= 12;      // FMB LayerNorm gamma / beta held in registers
-  constexpr int SW = ZTMAX * 16 * KC;     // weight part of a ring slot (u16)
+  // DMA instructions per step: ZTP = ZTMAX 16-row weight tiles (tiles past the
+  // shape's ZT read as zero) and X_INS for the X rows (1 KB each), dealt round
+  // robin: waves below R issue INS_HI per step, the others INS_LO, so every
+  // counter wait is a compile-time constant.
+  constexpr int X_INS = E * D / 16;
+  constexpr int ZTP = ZTMAX;  // >= the shape's ZT (host check); may exceed WZ * ZPW (padding tiles)
+  constexpr int NINS = ZTP + X_INS;
+  constexpr int INS_HI = (NINS + NWAVE - 1) / NWAVE, INS_LO = NINS / NWAVE, R = NINS % NWAVE;
+  constexpr int SW = ZTP * 16 * KC;       // weight part of a ring slot (u16)
   constexpr int SX = E * KC * D;          // X part of a ring slot
   static_assert(WZ * WE == NWAVE, "8 waves");
   static_assert(S == 3 || S == 4, "ring of 3 or 4 slots");
-  static_assert(ZTMAX <= WZ * ZPW, "tiles per wave");
+  static_assert(GUARD || ZTMAX >= WZ * ZPW, "unguarded tiles must lie in the slot");
+  static_assert(2 * ((ZTMAX + WE * EPW * ET + NWAVE - 1) / NWAVE) <= 63, "vmcnt range");
   // The ring slots are separate objects: the compiler then knows a DMA into
   // one slot does not alias reads of another and inserts no wait for it.
   __shared__ __align__(16) uint16_t w0[SW], w1[SW], w2[SW], w3[S > 3 ? SW : 8];
@@ -120,20 +117,19 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
     Zs[(size_t)row * ZP + D + c] = 0;
   }
 
-  // ---- DMA issue: instruction i of a step goes to wave i % 8.  Instructions
-  // 0 .. ZT-1 fill the 16-row weight tiles, the rest the X rows (1 KB each).
-  const int xblk_per_ex = KC * D / 512;  // 1 KB blocks of one example's 32 rows
-  const int n_ins = ZT + E * xblk_per_ex;
-  // this wave's instructions per step (wave-uniform; readfirstlane keeps the waits scalar)
-  const int my_ins = __builtin_amdgcn_readfirstlane((n_ins - wave + NWAVE - 1) / NWAVE);
+  // ---- DMA issue: instruction i of a step goes to wave i % 8; 0 .. ZTP-1 are
+  // weight tiles, the rest X rows.
   const __amdgpu_buffer_rsrc_t rphi =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.phi, (short)0, k * n * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rwl =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.w_l, (short)0, n_l * n * 2, 0x00020000);
   auto dma_step = [&](const __amdgpu_buffer_rsrc_t& rx, uint16_t* sw, uint16_t* sx, int step) {
     const int k0 = step * KC;
-    for (int i = wave; i < n_ins; i += NWAVE) {  // wave-uniform
-      if (i < ZT) {
+#pragma unroll
+    for (int q = 0; q < INS_HI; ++q) {
+      const int i = wave + q * NWAVE;  // wave-uniform
+      if (i >= NINS) break;
+      if (i < ZTP) {
         // weight tile i: row z = 16 i + lane / 4, columns k0 + 8 (lane % 4) .. + 7
         const int col = k0 + 8 * (lane & 3);
         const int r = 16 * i + (lane >> 2);
@@ -147,8 +143,8 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rwl, WK_LDSV(dst), 16, vo, 0, 0, 0);
         }
       } else {
-        const int j = i - ZT;
-        const int ex = j / xblk_per_ex, bb = j - ex * xblk_per_ex;
+        const int j = i - ZTP;
+        const int ex = j / (D / 16), bb = j - ex * (D / 16);
         const int o = bb * 512 + lane * 8;  // element offset within the example's KC x D rows
         const int row = o / D, col = o - row * D;
         uint16_t* dst = sx + ex * KC * D + bb * 512;
@@ -234,25 +230,51 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
     auto step = [&](const uint16_t* sw, const uint16_t* sx, uint16_t* nw, uint16_t* nx, int t) {
       // step t must have landed; the (up to S - 2) steps issued after it may still be in flight
       const int newer = (STEPS - 1 - t < S - 2) ? STEPS - 1 - t : S - 2;
-      wait_vm(newer * my_ins);
+      if (newer <= 0) {
+        __builtin_amdgcn_s_waitcnt(vm_enc(0));
+      } else if (S > 3 && newer >= 2) {
+        if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_HI));
+        else __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_LO));
+      } else {
+        if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(INS_HI));
+        else __builtin_amdgcn_s_waitcnt(vm_enc(INS_LO));
+      }
       lds_barrier();
       if (t + S - 1 < STEPS) dma_step(rx, nw, nx, t + S - 1);
-      u32x4 wf[ZPW];
+      if constexpr (GUARD) {
+        // the step's X^T operands first, then one uniform test per weight tile
+        u32x4 xo[EPW][ET];
 #pragma unroll
-      for (int zi = 0; zi < ZPW; ++zi) {
-        const int zt = wz * ZPW + zi;
-        wf[zi] = zt < ZT ? *reinterpret_cast<const u32x4*>(sw + (zt * 16 + li) * KC + lg * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-      }
+        for (int ex = 0; ex < EPW; ++ex) {
+          const uint16_t* xs = sx + (we * EPW + ex) * KC * D + xa;
 #pragma unroll
-      for (int ex = 0; ex < EPW; ++ex) {
-        const uint16_t* xs = sx + (we * EPW + ex) * KC * D + xa;
+          for (int et = 0; et < ET; ++et) xo[ex][et] = tr_pair(xs + et * 16, xs + 4 * D + et * 16);
+        }
 #pragma unroll
-        for (int et = 0; et < ET; ++et) {
-          const u32x4 a = tr_pair(xs + et * 16, xs + 4 * D + et * 16);
+        for (int zi = 0; zi < ZPW; ++zi) {
+          const int zt = wz * ZPW + zi;
+          if (zt < ZT) {  // wave-uniform
+            const u32x4 wf = *reinterpret_cast<const u32x4*>(sw + (zt * 16 + li) * KC + lg * 8);
 #pragma unroll
-          for (int zi = 0; zi < ZPW; ++zi)
-            if (wz * ZPW + zi < ZT) acc[zi][ex][et] = mfma16x16x32(a, wf[zi], acc[zi][ex][et]);
+            for (int ex = 0; ex < EPW; ++ex)
+#pragma unroll
+              for (int et = 0; et < ET; ++et) acc[zi][ex][et] = mfma16x16x32(xo[ex][et], wf, acc[zi][ex][et]);
+          }
+        }
+      } else {
+        u32x4 wf[ZPW];
+#pragma unroll
+        for (int zi = 0; zi < ZPW; ++zi)
+          wf[zi] = *reinterpret_cast<const u32x4*>(sw + ((wz * ZPW + zi) * 16 + li) * KC + lg * 8);
+#pragma unroll
+        for (int ex = 0; ex < EPW; ++ex) {
+          const uint16_t* xs = sx + (we * EPW + ex) * KC * D + xa;
+#pragma unroll
+          for (int et = 0; et < ET; ++et) {
+            const u32x4 a = tr_pair(xs + et * 16, xs + 4 * D + et * 16);
+#pragma unroll
+            for (int zi = 0; zi < ZPW; ++zi) acc[zi][ex][et] = mfma16x16x32(a, wf[zi], acc[zi][ex][et]);
+          }
         }
       }
     };
@@ -461,17 +483,17 @@ struct StreamVariant {
   void (*kernel)(FmbLcbArgs, int64_t, StreamShape);
 };
 
-#define WK_STREAM(ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S)                 \
-  StreamVariant {                                                          \
-    ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S,                               \
-        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S>     \
+#define WK_STREAM(ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD)                 \
+  StreamVariant {                                                                 \
+    ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S,                                      \
+        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD>     \
   }
 
 // LDS per variant (static): S x (ZTMAX 16 KC + E KC D) + E KJ 16 ZP + 2 D u16.
 const StreamVariant kStream[] = {
-    WK_STREAM(10, 3, 4, 2, 1, 2, 3, 12, 3),  // n<=256, d=160, k<=48, ZT<=12: 2 examples per group
-    WK_STREAM(10, 3, 8, 1, 1, 4, 6, 24, 3),  // n<=512, d=160, k<=96, ZT<=24
-    WK_STREAM(2, 4, 8, 1, 4, 6, 2, 25, 4),   // n<=768, d=32,  k<=32, ZT<=25: 4 examples per group
+    WK_STREAM(10, 3, 4, 2, 1, 2, 3, 12, 3, false),  // n<=256, d=160, k<=48, ZT<=12: 2 examples per group
+    WK_STREAM(10, 3, 8, 1, 1, 4, 6, 24, 3, false),  // n<=512, d=160, k<=96, ZT<=24
+    WK_STREAM(2, 4, 8, 1, 4, 6, 2, 25, 4, true),    // n<=768, d=32,  k<=32, ZT<=25: 4 examples per group
 };
 
 StreamShape stream_shape(const StreamVariant& v, int n, int k, int n_l) {
@@ -488,11 +510,10 @@ const StreamVariant* pick_stream(int n, int d, int k, int n_l, StreamShape* out)
   for (const auto& v : kStream) {
     if (16 * v.et != d) continue;
     const StreamShape sh = stream_shape(v, n, k, n_l);
-    if (sh.zt > v.ztmax) continue;
+    if (sh.zt > v.ztmax || sh.zt > v.wz * v.zpw) continue;  // DMA'd tiles and tiles with an owner wave
     if (sh.kz > v.kj) continue;
     if ((n + 15) / 16 > NWAVE * v.mpw) continue;
-    // the vmcnt table covers up to 24 instructions per wave in flight
-    if ((sh.zt + sh.e * (KC * d / 512) + NWAVE - 1) / NWAVE * (v.s - 2) > 24) continue;
+
     // 32-bit byte offsets within one group's X and within the weights
     if ((int64_t)sh.e * n * d * 2 >= (int64_t)1 << 31 || (int64_t)(k + n_l) * n * 2 >= (int64_t)1 << 31) continue;
     if (out) *out = sh;
