@@ -48,6 +48,7 @@ F = X bf16(Phi X)^T, because the rounded Z only exists in that order.
 """
 from __future__ import annotations
 
+import math
 from typing import Dict, Iterable, List, Sequence
 
 import numpy as np
@@ -254,3 +255,72 @@ def brute_force_layer(X1, w, eps: float = LN_EPS) -> np.ndarray:
     for r in range(n):
         Y[r] = ln([rows[r][e] + X[r, e] for e in range(d)], w.out_gamma, w.out_beta)
     return Y
+
+
+# ---------------------------------------------------------------- prediction head
+def sigmoid(z) -> np.ndarray:
+    """Logistic function 1 / (1 + e^-z), evaluated without overflow for large |z|."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def prediction_head(Y, head_w: Sequence[np.ndarray], head_b: Sequence = None,
+                    storage: Iterable[str] = (), logits: bool = False):
+    """Top MLP and prediction after the layer stack (Wukong paper, section 2.2:
+    the Wukong layers do the feature interaction and an MLP then produces the
+    prediction; the page gives no sizes for it).
+
+    Readings: the MLP input is the last layer's output flattened row-major,
+    v = vec(Y) with v[r*d + e] = Y[r, e]; every Linear but the last is followed
+    by ReLU; the prediction is the logistic function of the last Linear's
+    output.  `head_w` lists [m_t, m_{t-1}] weights (m_0 = n*d), `head_b` the
+    [m_t] biases (None entries: no bias).  `storage` may name "h": the hidden
+    activations are then rounded to bf16 where produced.  Returns the
+    probabilities [S, m_T] in float64, or (probabilities, logits).
+    """
+    storage = frozenset(storage)
+    if storage - {"h"}:
+        raise ValueError(f"unknown storage names {sorted(storage - {'h'})}")
+    Y = to_f64(Y)
+    S = Y.shape[0]
+    v = Y.reshape(S, -1)
+    T = len(head_w)
+    for t in range(T):
+        W = to_f64(head_w[t])
+        v = v @ W.T
+        if head_b is not None and head_b[t] is not None:
+            v = v + to_f64(head_b[t])
+        if t + 1 < T:
+            v = np.maximum(v, 0.0)
+            v = _maybe_round(v, "h", storage)
+    p = sigmoid(v)
+    return (p, v) if logits else p
+
+
+def brute_force_head(Y1, head_w: Sequence[np.ndarray], head_b: Sequence = None) -> List[float]:
+    """The prediction head for ONE example [n, d] with explicit loops (tiny inputs only)."""
+    Y = to_f64(Y1)
+    n, d = Y.shape
+    vec = []
+    for r in range(n):
+        for e in range(d):
+            vec.append(Y[r, e])
+    T = len(head_w)
+    for t in range(T):
+        W = to_f64(head_w[t])
+        b = None if (head_b is None or head_b[t] is None) else to_f64(head_b[t])
+        nxt = []
+        for o in range(W.shape[0]):
+            acc = 0.0
+            for i in range(W.shape[1]):
+                acc += W[o, i] * vec[i]
+            if b is not None:
+                acc += b[o]
+            nxt.append(acc if t == T - 1 else max(acc, 0.0))
+        vec = nxt
+    return [1.0 / (1.0 + math.exp(-z)) for z in vec]

@@ -20,7 +20,11 @@ What pins what:
     explicit-loop brute force on tiny inputs;
   * the stack: composition of single layers and batch independence;
   * bf16 rounding: torch's float32 -> bfloat16 conversion (round to nearest
-    even) as an independent library routine.
+    even) as an independent library routine;
+  * the prediction head: explicit loops on tiny inputs, the logistic
+    function's closed forms (sigmoid(ln 3) = 3/4, sigmoid(0) = 1/2), one-hot
+    weights reading single elements of Y (row-major flatten), ReLU placement
+    by sign-controlled hidden layers, and the symmetry sigmoid(-z) = 1 - sigmoid(z).
 """
 import json
 import os
@@ -307,6 +311,62 @@ def pin_storage_points(wo):
     assert not np.array_equal(Y, Y64)
 
 
+def _head_weights(rng, dims):
+    ws = [rng.standard_normal((dims[t + 1], dims[t])) / np.sqrt(dims[t]) for t in range(len(dims) - 1)]
+    bs = [rng.standard_normal(dims[t + 1]) * 0.3 for t in range(len(dims) - 1)]
+    return ws, bs
+
+
+def pin_head_brute_force(wo):
+    rng = np.random.default_rng(41)
+    Y = rng.standard_normal((3, 3, 4))
+    ws, bs = _head_weights(rng, [12, 7, 5, 2])
+    p = wo.prediction_head(Y, ws, bs)
+    for s_ in range(3):
+        np.testing.assert_allclose(p[s_], wo.brute_force_head(Y[s_], ws, bs), rtol=1e-12, atol=1e-14)
+
+
+def pin_head_sigmoid_closed_form(wo):
+    # zero weights: the prediction is the logistic function of the bias alone
+    Y = np.random.default_rng(42).standard_normal((2, 2, 3))
+    ws = [np.zeros((3, 6)), np.zeros((3, 3))]
+    bs = [np.zeros(3), np.array([np.log(3.0), 0.0, -np.log(3.0)])]
+    p = wo.prediction_head(Y, ws, bs)
+    np.testing.assert_allclose(p, [[0.75, 0.5, 0.25]] * 2, rtol=0, atol=1e-15)
+
+
+def pin_head_flatten_order(wo):
+    # one Linear whose rows are one-hot at r*d + e: the logits are Y[r, e]
+    Y = np.arange(24, dtype=np.float64).reshape(2, 3, 4) / 24.0 - 0.4
+    picks = [(0, 1), (2, 0), (1, 3)]
+    W = np.zeros((3, 12))
+    for o, (r, e) in enumerate(picks):
+        W[o, r * 4 + e] = 1.0
+    _, z = wo.prediction_head(Y, [W], [None], logits=True)
+    np.testing.assert_array_equal(z, np.stack([[Y[s_, r, e] for r, e in picks] for s_ in range(2)]))
+
+
+def pin_head_relu_placement(wo):
+    # a hidden layer of -I on positive inputs is all zero after ReLU: only the last bias is left;
+    # +I passes the inputs through; the last Linear gets no ReLU (a negative logit survives)
+    Y = np.abs(np.random.default_rng(43).standard_normal((2, 2, 2))) + 0.1
+    v = Y.reshape(2, 4)
+    w2 = np.array([[1.0, -2.0, 0.5, 1.5]])
+    _, z = wo.prediction_head(Y, [-np.eye(4), w2], [None, np.array([-0.7])], logits=True)
+    np.testing.assert_allclose(z, np.full((2, 1), -0.7), rtol=0, atol=1e-15)
+    _, z = wo.prediction_head(Y, [np.eye(4), -np.abs(w2)], [None, None], logits=True)
+    np.testing.assert_allclose(z[:, 0], -(v @ np.abs(w2[0])), rtol=1e-14)
+
+
+def pin_head_symmetry(wo):
+    rng = np.random.default_rng(44)
+    Y = rng.standard_normal((3, 2, 5))
+    ws, bs = _head_weights(rng, [10, 6, 3])
+    p = wo.prediction_head(Y, ws, bs)
+    q = wo.prediction_head(Y, ws[:-1] + [-ws[-1]], bs[:-1] + [-bs[-1]])
+    np.testing.assert_allclose(p + q, np.ones_like(p), rtol=0, atol=1e-14)
+
+
 PINS = {name[4:]: fn for name, fn in list(globals().items()) if name.startswith("pin_")}
 
 
@@ -339,6 +399,11 @@ MUTANTS = {
     "bf16_7_bits": ("return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)", "return np.ldexp(np.round(np.ldexp(m, 7)), e - 7)"),
     "bf16_truncate": ("return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)", "return np.ldexp(np.trunc(np.ldexp(m, 8)), e - 8)"),
     "bf16_decode_shift": ("(b.astype(np.uint32) << np.uint32(16))", "(b.astype(np.uint32) << np.uint32(15))"),
+    "head_flatten_col_major": ("v = Y.reshape(S, -1)", "v = np.swapaxes(Y, 1, 2).reshape(S, -1)"),
+    "head_relu_on_last": ("if t + 1 < T:", "if True:"),
+    "head_relu_missing": ("v = np.maximum(v, 0.0)", "v = v"),
+    "head_bias_dropped": ("v = v + to_f64(head_b[t])", "v = v"),
+    "head_sigmoid_sign": ("out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))", "out[pos] = 1.0 / (1.0 + np.exp(z[pos]))"),
 }
 
 
