@@ -12,6 +12,9 @@ kernel with the largest share of the step reported against its roofline.
 The CPU oracle is timed on a bounded sample of the same workload on this host
 as a reference baseline.
 
+The prediction head (top MLP + logistic function) is then timed on its own
+on the stack's output and reported under "head"; it is not part of `value`.
+
 Prints one JSON line.
 
     python bench.py --copy-calibration BYTES
@@ -40,6 +43,8 @@ KERNEL_SOURCES = {
     "fmb_lcb": "fmb_lcb.hip",
     "mlp_linear": "linear_bf16.hip",
     "residual_ln": "resid_ln.hip",
+    "head_linear": "linear_bf16.hip",
+    "head_out": "head.hip",
 }
 
 
@@ -75,6 +80,101 @@ def kernel_accounting(cfg, fused_layers=()):
             "bytes": 3 * B * n_f * d * es,
         }
     return out
+
+
+def head_accounting(dims, batch, es):
+    """Algorithmic FLOPs and HBM bytes per launch of the prediction head's kernels."""
+    out = {}
+    T = len(dims) - 1
+    for t, (a, b) in enumerate(zip(dims[:-1], dims[1:])):
+        if t + 1 < T:  # hidden Linear + ReLU on the GEMM: A, W, bias in, C out
+            out[("head_linear", 0, t)] = {"flops": 2 * batch * a * b,
+                                          "bytes": (batch * a + a * b + b + batch * b) * es}
+        else:  # last Linear + logistic: A, W, bias in, fp32 probabilities out
+            out[("head_out", 0, 0)] = {"flops": 2 * batch * a * b,
+                                       "bytes": (batch * a + a * b + b) * es + batch * b * 4}
+    return out
+
+
+def roofline_of(kernel, ac, avg_ms, dtype, workload, traffic_index=None):
+    """Place one kernel against its roofline: MFMA (or fp32 ALU) when its
+    arithmetic intensity is above the ridge point, HBM otherwise."""
+    avg_s = avg_ms * 1e-3
+    traffic = read_traffic(kernel["kernel"], kernel["index"], workload)
+    label = f"{kernel['kernel']}[layer {kernel['layer']}, index {kernel['index']}]"
+    if ac["flops"] > 0 and ac["flops"] / ac["bytes"] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
+        peak = PEAK_BF16_TFLOPS if dtype == "bf16" else PEAK_F32_TFLOPS
+        ach = ac["flops"] / avg_s / 1e12
+        return {"bound": "mfma" if dtype == "bf16" else "alu", "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic, "kernel": label,
+                "algorithmic_flops_per_launch": ac["flops"], "avg_ms": avg_ms}
+    ach = ac["bytes"] / avg_s / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic, "kernel": label,
+            "algorithmic_bytes_per_launch": ac["bytes"], "avg_ms": avg_ms}
+
+
+def summarize_trace(recs, acct, per_step_ms, steps):
+    """Average each (kernel, layer, index) over the trace; return the rows and
+    the dominant one (largest total time over kernels of one kind and index)."""
+    agg = {}
+    for r in recs:
+        key = (r["kernel"], r["layer"], r["index"])
+        a = agg.setdefault(key, {"ms": 0.0, "count": 0, "workgroups": r["workgroups"]})
+        a["ms"] += r["ms"]
+        a["count"] += 1
+    kernels = []
+    for key, a in agg.items():
+        avg = a["ms"] / a["count"]
+        ac = acct[key]
+        kernels.append({"kernel": key[0], "layer": key[1], "index": key[2], "avg_ms": round(avg, 5),
+                        "launches": a["count"], "workgroups": a["workgroups"],
+                        "share_of_step": round(a["ms"] / steps / per_step_ms, 4),
+                        "tflops": round(ac["flops"] / (avg * 1e-3) / 1e12, 2),
+                        "gbps": round(ac["bytes"] / (avg * 1e-3) / 1e9, 1)})
+    if not kernels:
+        return kernels, None
+    by_kind = {}
+    for kr in kernels:
+        by_kind.setdefault((kr["kernel"], kr["index"]), []).append(kr)
+    best = max(by_kind.items(), key=lambda it: sum(k["avg_ms"] for k in it[1]))
+    return kernels, best[1][0]
+
+
+def measure_head(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
+    """The prediction head (top MLP + logistic function) on the stack's output,
+    timed on its own: widths cfg.head_dims(), Xavier-uniform weights."""
+    dims = cfg.head_dims()
+    w, b = ws.make_head_weights(cfg.name, dims, cfg.dtype, seed, "identity")
+    head = wk.DeviceHead(wk.HeadSpec(dims, cfg.dtype), w, b, device=y.device)
+    prob = torch.empty((cfg.batch, dims[-1]), dtype=torch.float32, device=y.device)
+    hws = wk.alloc_workspace(wk.head_workspace_size(head.spec, cfg.batch), y.device)
+    for _ in range(warmup):
+        wk.head_forward(y, head, prob=prob, workspace=hws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wk.head_forward(y, head, prob=prob, workspace=hws, stream=stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    trace = wk.Trace(capacity=len(dims) * steps + 8)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        wk.head_forward(y, head, prob=prob, workspace=hws, stream=stream, trace=trace)
+    torch.cuda.synchronize()
+    traced_ms = (time.perf_counter() - t1) * 1e3 / steps
+    acct = head_accounting(dims, cfg.batch, 2 if cfg.dtype == "bf16" else 4)
+    kernels, dom = summarize_trace(trace.records(), acct, traced_ms, steps)
+    trace.close()
+    roof = None
+    if dom is not None:
+        roof = roofline_of(dom, acct[(dom["kernel"], dom["layer"], dom["index"])], dom["avg_ms"], cfg.dtype,
+                           cfg.name)
+    flops = sum(2 * a * o for a, o in zip(dims[:-1], dims[1:])) * cfg.batch
+    return {"dims": list(dims), "ms_per_call": round(ms, 4), "examples_per_s": round(cfg.batch / ms * 1e3, 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "roofline": roof,
+            "kernels": sorted(kernels, key=lambda k: (k["kernel"] != "head_linear", k["index"]))}
 
 
 def source_digest(name):
@@ -142,6 +242,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
+    ap.add_argument("--no-head", action="store_true", help="skip the prediction-head measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -218,50 +319,18 @@ def main():
     kernels = []
     dominant = None
     if trace is not None:
-        recs = trace.records()
-        agg = {}
-        for r in recs:
-            key = (r["kernel"], r["layer"], r["index"])
-            a = agg.setdefault(key, {"ms": 0.0, "count": 0, "workgroups": r["workgroups"]})
-            a["ms"] += r["ms"]
-            a["count"] += 1
-        for key, a in agg.items():
-            avg = a["ms"] / a["count"]
-            ac = acct[key]
-            kr = {"kernel": key[0], "layer": key[1], "index": key[2], "avg_ms": round(avg, 5),
-                  "launches": a["count"], "workgroups": a["workgroups"],
-                  "share_of_step": round(a["ms"] / args.steps / traced_ms, 4),
-                  "tflops": round(ac["flops"] / (avg * 1e-3) / 1e12, 2),
-                  "gbps": round(ac["bytes"] / (avg * 1e-3) / 1e9, 1)}
-            kernels.append(kr)
-        # dominant: largest total time over the kernels of the same kind and index
-        by_kind = {}
-        for kr in kernels:
-            kk = (kr["kernel"], kr["index"])
-            by_kind.setdefault(kk, []).append(kr)
-        best = max(by_kind.items(), key=lambda it: sum(k["avg_ms"] for k in it[1]))
-        dominant = best[1][0]
+        kernels, dominant = summarize_trace(trace.records(), acct, traced_ms, args.steps)
         trace.close()
 
     roofline = None
     if dominant is not None:
-        key = (dominant["kernel"], dominant["layer"], dominant["index"])
-        ac = acct[key]
-        avg_s = dominant["avg_ms"] * 1e-3
-        traffic = read_traffic(dominant["kernel"], dominant["index"], cfg.name)
-        if ac["flops"] > 0 and ac["flops"] / ac["bytes"] > PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBPS * 1e9):
-            peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
-            ach = ac["flops"] / avg_s / 1e12
-            roofline = {"bound": "mfma" if cfg.dtype == "bf16" else "alu", "achieved": round(ach, 2),
-                        "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
-                        "kernel": f"{dominant['kernel']}[layer {dominant['layer']}, index {dominant['index']}]",
-                        "algorithmic_flops_per_launch": ac["flops"], "avg_ms": dominant["avg_ms"]}
-        else:
-            ach = ac["bytes"] / avg_s / 1e9
-            roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                        "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": traffic,
-                        "kernel": f"{dominant['kernel']}[layer {dominant['layer']}, index {dominant['index']}]",
-                        "algorithmic_bytes_per_launch": ac["bytes"], "avg_ms": dominant["avg_ms"]}
+        roofline = roofline_of(dominant, acct[(dominant["kernel"], dominant["layer"], dominant["index"])],
+                               dominant["avg_ms"], cfg.dtype, cfg.name)
+
+    head = None
+    if not args.no_head:
+        head = measure_head(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
+        print(f"# head {head['dims']}: {head['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
 
     step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
     s0 = cfg.layers[0]
@@ -286,6 +355,7 @@ def main():
         "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
         "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
+        "head": head,
     }
     if not args.no_cpu_baseline:
         del x, y, ws_t, layers

@@ -159,7 +159,9 @@ int32_t wukong_stack_forward(int32_t num_layers, const wk_layer_desc* descs,
 enum {
   WK_KERNEL_FMB_LCB = 1,    /* compress + interaction + LN(F) + LCB rows of Y */
   WK_KERNEL_MLP_LINEAR = 2, /* one FMB-MLP Linear (+bias, +ReLU)             */
-  WK_KERNEL_RESIDUAL_LN = 3 /* FMB rows of Y: LN(M + X)                      */
+  WK_KERNEL_RESIDUAL_LN = 3, /* FMB rows of Y: LN(M + X)                     */
+  WK_KERNEL_HEAD_LINEAR = 4,  /* one hidden Linear of the prediction head     */
+  WK_KERNEL_HEAD_OUT = 5      /* the head's last Linear + logistic function   */
 };
 typedef struct wk_trace wk_trace;
 /* Creates a trace able to hold `capacity` launch records (creates HIP events
@@ -178,6 +180,44 @@ int32_t wukong_stack_forward_traced(int32_t num_layers, const wk_layer_desc* des
                                     const wk_layer_weights* weights, int64_t batch,
                                     const void* x, void* y, void* workspace,
                                     size_t workspace_bytes, void* stream, wk_trace* trace);
+
+/* ---- Prediction head (top MLP) -------------------------------------------
+ * Wukong paper, section 2.2 (xdnf.cn repost): after the Wukong layers have
+ * done the feature interaction, an MLP produces the prediction.  The page
+ * gives no sizes; this head reads a layer output Y [batch, n, d] flattened
+ * row-major (feature r*d + e), applies Linear + ReLU for every Linear but the
+ * last, and writes the logistic function of the last Linear's output:
+ *   prob[b, o] = 1 / (1 + exp(-(W_T h_{T-1}[b] + b_T)[o])).
+ * bf16 heads keep the hidden activations in bf16 (as the layer's MLP does)
+ * and accumulate in fp32; the probabilities are always fp32. */
+typedef struct {
+  int32_t num_linear;   /* T >= 1 Linear layers                                 */
+  const int32_t* dims;  /* host array, length T+1: [n*d, m_1, ..., m_T]         */
+  int32_t dtype;        /* WK_F32 or WK_BF16 (Y, weights, hidden activations)   */
+} wk_head_desc;         /* bf16: dims[0..T-1] % 8 == 0; m_T >= 1 is free         */
+
+typedef struct {
+  const void* const* w; /* host array of T device pointers, W_t is [m_t, m_{t-1}] */
+  const void* const* b; /* host array of T device pointers [m_t] (NULL entries or
+                           a NULL array: no bias)                                  */
+} wk_head_weights;
+
+/* Workspace bytes for wukong_head_forward (two ping-pong buffers of the widest
+ * hidden layer), 0 for an invalid or unsupported desc; 256 for T == 1. */
+size_t wukong_head_workspace_size(const wk_head_desc* desc, int64_t batch);
+
+/* prob [batch, m_T] fp32 (device) from y [batch, dims[0]] (device, the layer
+ * output).  Same conventions as wukong_layer_forward: device pointers 16-byte
+ * aligned (prob 4-byte), arguments checked before any launch, asynchronous on
+ * `stream`, no allocation; y, prob and the workspace must not overlap. */
+int32_t wukong_head_forward(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch,
+                            const void* y, float* prob, void* workspace, size_t workspace_bytes,
+                            void* stream);
+/* As wukong_head_forward, recording one event pair per launch into `trace`
+ * (kinds WK_KERNEL_HEAD_LINEAR with the Linear number, WK_KERNEL_HEAD_OUT). */
+int32_t wukong_head_forward_traced(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch,
+                                   const void* y, float* prob, void* workspace, size_t workspace_bytes,
+                                   void* stream, wk_trace* trace);
 
 #ifdef __cplusplus
 }

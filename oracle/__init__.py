@@ -3,6 +3,6 @@
 Imported only by the tests, the package's smoke check and the benchmark's
 CPU-baseline leg.  It shares no code with the HIP library.
 """
-from .wukong_oracle import (LN_EPS, STORAGE_NAMES, brute_force_layer, decode_bf16,  # noqa: F401
-                            fm_interaction, fmb_mlp, layer_norm, lcb, round_bf16, to_f64,
-                            wukong_layer, wukong_stack)
+from .wukong_oracle import (LN_EPS, STORAGE_NAMES, brute_force_head, brute_force_layer,  # noqa: F401
+                            decode_bf16, fm_interaction, fmb_mlp, layer_norm, lcb, prediction_head,
+                            round_bf16, sigmoid, to_f64, wukong_layer, wukong_stack)

@@ -4,10 +4,11 @@ The layer (Wukong paper, section 2.2, as summarised on the xdnf.cn repost of
 the Zhihu article): a Factorization Machine Block and a Linear Compress Block
 run side by side on each example's n x d embedding matrix, their outputs are
 concatenated, the residual is added and a LayerNorm is applied; layers are
-stacked.  The compute runs in hand-written HIP kernels for gfx950 behind the
-C ABI in include/wukong.h; this package is the Python binding.
+stacked; a prediction head (top MLP + logistic function) can follow the
+stack.  The compute runs in hand-written HIP kernels for gfx950 behind the C
+ABI in include/wukong.h; this package is the Python binding.
 """
-from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceLayer, LayerSpec, Trace,  # noqa: F401
-                   WukongError, alloc_workspace, layer_forward, layer_workspace_size, library_path,
-                   load_library, stack_forward, stack_workspace_size, status_string, to_device,
-                   workspace_layout, EXPORTED_SYMBOLS)
+from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceHead, DeviceLayer, HeadSpec,  # noqa: F401
+                   LayerSpec, Trace, WukongError, alloc_workspace, head_forward, head_workspace_size,
+                   layer_forward, layer_workspace_size, library_path, load_library, stack_forward,
+                   stack_workspace_size, status_string, to_device, workspace_layout, EXPORTED_SYMBOLS)

@@ -19,8 +19,9 @@ _lib = None
 
 F32, BF16 = 0, 1
 WK_OK, WK_ERR_INVALID_ARG, WK_ERR_UNSUPPORTED, WK_ERR_WORKSPACE, WK_ERR_HIP = 0, 1, 2, 3, 4
-KERNEL_FMB_LCB, KERNEL_MLP_LINEAR, KERNEL_RESIDUAL_LN = 1, 2, 3
-KERNEL_NAMES = {KERNEL_FMB_LCB: "fmb_lcb", KERNEL_MLP_LINEAR: "mlp_linear", KERNEL_RESIDUAL_LN: "residual_ln"}
+KERNEL_FMB_LCB, KERNEL_MLP_LINEAR, KERNEL_RESIDUAL_LN, KERNEL_HEAD_LINEAR, KERNEL_HEAD_OUT = 1, 2, 3, 4, 5
+KERNEL_NAMES = {KERNEL_FMB_LCB: "fmb_lcb", KERNEL_MLP_LINEAR: "mlp_linear", KERNEL_RESIDUAL_LN: "residual_ln",
+                KERNEL_HEAD_LINEAR: "head_linear", KERNEL_HEAD_OUT: "head_out"}
 ABI_VERSION = 1
 
 
@@ -36,6 +37,14 @@ class wk_layer_weights(ctypes.Structure):
                 ("fm_ln_gamma", ctypes.c_void_p), ("fm_ln_beta", ctypes.c_void_p),
                 ("mlp_w", ctypes.POINTER(ctypes.c_void_p)), ("mlp_b", ctypes.POINTER(ctypes.c_void_p)),
                 ("out_ln_gamma", ctypes.c_void_p), ("out_ln_beta", ctypes.c_void_p)]
+
+
+class wk_head_desc(ctypes.Structure):
+    _fields_ = [("num_linear", ctypes.c_int32), ("dims", ctypes.POINTER(ctypes.c_int32)), ("dtype", ctypes.c_int32)]
+
+
+class wk_head_weights(ctypes.Structure):
+    _fields_ = [("w", ctypes.POINTER(ctypes.c_void_p)), ("b", ctypes.POINTER(ctypes.c_void_p))]
 
 
 class wk_workspace_layout(ctypes.Structure):
@@ -68,6 +77,13 @@ _SIGNATURES = [
     ("wukong_stack_forward_traced", ctypes.c_int32,
      [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64,
       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_head_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_head_desc), ctypes.c_int64]),
+    ("wukong_head_forward", ctypes.c_int32,
+     [ctypes.POINTER(wk_head_desc), ctypes.POINTER(wk_head_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_head_forward_traced", ctypes.c_int32,
+     [ctypes.POINTER(wk_head_desc), ctypes.POINTER(wk_head_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
 ]
 EXPORTED_SYMBOLS = tuple(s[0] for s in _SIGNATURES)
 
@@ -324,3 +340,76 @@ def stack_forward(x: torch.Tensor, layers: Sequence[DeviceLayer], y: Optional[to
         st = lib.wukong_stack_forward_traced(*args, trace.handle)
     _check(st, "wukong_stack_forward")
     return y
+
+
+# ------------------------------------------------------------------ prediction head
+@dataclass(frozen=True)
+class HeadSpec:
+    """The top MLP after the stack: dims = (n*d, m_1, ..., m_T)."""
+    dims: Tuple[int, ...]
+    dtype: str = "bf16"
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def make_desc(self) -> Tuple[wk_head_desc, object]:
+        dims = (ctypes.c_int32 * len(self.dims))(*self.dims)
+        desc = wk_head_desc(len(self.dims) - 1, ctypes.cast(dims, ctypes.POINTER(ctypes.c_int32)),
+                            BF16 if self.dtype == "bf16" else F32)
+        return desc, dims
+
+
+class DeviceHead:
+    """The head's weights resident in device memory, plus its C descriptors."""
+
+    def __init__(self, spec: HeadSpec, w: Sequence, b: Optional[Sequence] = None, device="cuda"):
+        T = len(spec.dims) - 1
+        if len(w) != T or (b is not None and len(b) != T):
+            raise ValueError("w / b must have one entry per Linear")
+        cv = lambda a: None if a is None else to_device(a, spec.dtype, device)  # noqa: E731
+        self.spec = spec
+        self.w = [cv(x) for x in w]
+        self.b = None if b is None else [cv(x) for x in b]
+        for t in range(T):
+            if tuple(self.w[t].shape) != (spec.dims[t + 1], spec.dims[t]):
+                raise ValueError(f"w[{t}] has shape {tuple(self.w[t].shape)}, expected "
+                                 f"{(spec.dims[t + 1], spec.dims[t])}")
+            if self.b is not None and self.b[t] is not None and tuple(self.b[t].shape) != (spec.dims[t + 1],):
+                raise ValueError(f"b[{t}] has shape {tuple(self.b[t].shape)}")
+        self.desc, self._dims = spec.make_desc()
+        self._w_ptrs = (ctypes.c_void_p * T)(*[x.data_ptr() for x in self.w])
+        self._b_ptrs = None if self.b is None else (ctypes.c_void_p * T)(*[_ptr(x) for x in self.b])
+        self.weights = wk_head_weights(ctypes.cast(self._w_ptrs, ctypes.POINTER(ctypes.c_void_p)),
+                                       None if self._b_ptrs is None
+                                       else ctypes.cast(self._b_ptrs, ctypes.POINTER(ctypes.c_void_p)))
+
+
+def head_workspace_size(spec: HeadSpec, batch: int) -> int:
+    desc, _dims = spec.make_desc()
+    return int(load_library().wukong_head_workspace_size(ctypes.byref(desc), batch))
+
+
+def head_forward(y: torch.Tensor, head: DeviceHead, prob: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None, stream=None,
+                 trace: Optional[Trace] = None) -> torch.Tensor:
+    """Prediction head on a layer output y [batch, n, d] (or [batch, n*d]); returns fp32 [batch, m_T]."""
+    lib = load_library()
+    spec = head.spec
+    if not y.is_cuda or y.dtype != spec.torch_dtype or not y.is_contiguous():
+        raise ValueError(f"y must be a contiguous {spec.torch_dtype} CUDA tensor")
+    B = y.shape[0]
+    if y.numel() != B * spec.dims[0]:
+        raise ValueError(f"y must hold {spec.dims[0]} features per example")
+    prob = torch.empty((B, spec.dims[-1]), dtype=torch.float32, device=y.device) if prob is None else prob
+    need = head_workspace_size(spec, B)
+    if workspace is None:
+        workspace = alloc_workspace(need, y.device)
+    args = (ctypes.byref(head.desc), ctypes.byref(head.weights), B, y.data_ptr(), prob.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    if trace is None:
+        st = lib.wukong_head_forward(*args)
+    else:
+        st = lib.wukong_head_forward_traced(*args, trace.handle)
+    _check(st, "wukong_head_forward")
+    return prob

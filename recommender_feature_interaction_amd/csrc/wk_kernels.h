@@ -95,4 +95,16 @@ bool resid_ln_bf16_supported(int d);
 hipError_t launch_resid_ln_bf16(const ResidLnArgs& a, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_resid_ln_f32(const ResidLnArgs& a, hipStream_t stream, int64_t* workgroups);
 
+// The prediction head's last Linear + logistic function (head.hip):
+// prob[m, o] = 1 / (1 + exp(-(A[m] . W[o] + bias[o]))), fp32 out.
+struct HeadOutArgs {
+  const void* a;     // [M, K] bf16 or fp32
+  const void* w;     // [N, K]
+  const void* bias;  // [N] or null
+  float* prob;       // [M, N]
+  int64_t M;
+  int N, K;          // bf16: K % 8 == 0
+};
+hipError_t launch_head_out(const HeadOutArgs& a, bool bf16, hipStream_t stream, int64_t* workgroups);
+
 }  // namespace wk

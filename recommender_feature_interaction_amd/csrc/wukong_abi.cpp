@@ -302,6 +302,90 @@ int32_t stack_forward(int32_t l, const wk_layer_desc* descs, const wk_layer_weig
   return WK_OK;
 }
 
+// ---- prediction head (top MLP): hidden Linears on the MLP GEMMs (+ReLU), the
+// last Linear + logistic function on the dot-product kernel.
+int32_t check_head_desc(const wk_head_desc* d) {
+  if (!d || d->num_linear < 1 || d->num_linear > kMaxLinear || !d->dims) return WK_ERR_INVALID_ARG;
+  if (d->dtype != WK_F32 && d->dtype != WK_BF16) return WK_ERR_INVALID_ARG;
+  for (int t = 0; t <= d->num_linear; ++t)
+    if (d->dims[t] <= 0) return WK_ERR_INVALID_ARG;
+  if (d->dtype == WK_BF16) {
+    for (int t = 0; t < d->num_linear; ++t)
+      if (d->dims[t] % 8) return WK_ERR_UNSUPPORTED;  // GEMM widths and the last Linear's 16-byte loads
+  }
+  return WK_OK;
+}
+
+struct HeadPlan {
+  size_t h[2] = {0, 0}, bytes = 0;
+};
+
+HeadPlan plan_head(const wk_head_desc& d, int64_t batch) {
+  HeadPlan p;
+  int64_t maxhid = 0;
+  for (int t = 1; t < d.num_linear; ++t) maxhid = d.dims[t] > maxhid ? d.dims[t] : maxhid;
+  const size_t buf = align_up((size_t)batch * (size_t)maxhid * esize(d.dtype));
+  p.h[0] = 0;
+  p.h[1] = buf;
+  p.bytes = d.num_linear > 1 ? 2 * buf : kAlign;
+  if (p.bytes == 0) p.bytes = kAlign;
+  return p;
+}
+
+int32_t head_forward(const wk_head_desc* d, const wk_head_weights* w, int64_t batch, const void* y, float* prob,
+                     void* ws, size_t ws_bytes, void* stream, wk_trace* trace) {
+  int32_t st = check_head_desc(d);
+  if (st != WK_OK) return st;
+  if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
+  if (!w || !w->w) return WK_ERR_INVALID_ARG;
+  const int T = d->num_linear;
+  for (int t = 0; t < T; ++t) {
+    if (!w->w[t] || !aligned16(w->w[t])) return WK_ERR_INVALID_ARG;
+    if (w->b && w->b[t] && !aligned16(w->b[t])) return WK_ERR_INVALID_ARG;
+  }
+  if (batch == 0) return WK_OK;
+  const HeadPlan hp = plan_head(*d, batch);
+  const size_t es = esize(d->dtype);
+  const size_t in_bytes = (size_t)batch * d->dims[0] * es;
+  const size_t out_bytes = (size_t)batch * d->dims[T] * sizeof(float);
+  if (!y || !prob || !aligned16(y) || (reinterpret_cast<uintptr_t>(prob) & 3u)) return WK_ERR_INVALID_ARG;
+  if (overlap(y, in_bytes, prob, out_bytes)) return WK_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return WK_ERR_INVALID_ARG;
+  if (ws_bytes < hp.bytes) return WK_ERR_WORKSPACE;
+  if (overlap(ws, hp.bytes, y, in_bytes) || overlap(ws, hp.bytes, prob, out_bytes)) return WK_ERR_INVALID_ARG;
+
+  const bool bf = d->dtype == WK_BF16;
+  char* base = static_cast<char*>(ws);
+  Launch launch{trace, static_cast<hipStream_t>(stream)};
+  const void* in = y;
+  for (int t = 0; t + 1 < T; ++t) {
+    void* out = base + hp.h[t % 2];
+    wk::LinearArgs a;
+    a.a = in;
+    a.w = w->w[t];
+    a.bias = w->b ? w->b[t] : nullptr;
+    a.c = out;
+    a.M = batch;
+    a.N = d->dims[t + 1];
+    a.K = d->dims[t];
+    a.relu = 1;
+    st = launch(WK_KERNEL_HEAD_LINEAR, 0, t, [&](int64_t* g) {
+      return bf ? wk::launch_linear_bf16(a, launch.stream, g) : wk::launch_linear_f32(a, launch.stream, g);
+    });
+    if (st != WK_OK) return st;
+    in = out;
+  }
+  wk::HeadOutArgs o;
+  o.a = in;
+  o.w = w->w[T - 1];
+  o.bias = w->b ? w->b[T - 1] : nullptr;
+  o.prob = prob;
+  o.M = batch;
+  o.N = d->dims[T];
+  o.K = d->dims[T - 1];
+  return launch(WK_KERNEL_HEAD_OUT, 0, 0, [&](int64_t* g) { return wk::launch_head_out(o, bf, launch.stream, g); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,6 +504,27 @@ int32_t wukong_trace_get(wk_trace* t, int32_t i, int32_t* kind, int32_t* layer, 
     if (hipEventElapsedTime(ms, t->start[i], t->stop[i]) != hipSuccess) return WK_ERR_HIP;
   }
   return WK_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t wukong_head_workspace_size(const wk_head_desc* desc, int64_t batch) {
+  if (check_head_desc(desc) != WK_OK || batch < 0 || batch > kMaxBatch) return 0;
+  return plan_head(*desc, batch).bytes;
+}
+
+int32_t wukong_head_forward(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch, const void* y,
+                            float* prob, void* workspace, size_t workspace_bytes, void* stream) {
+  return head_forward(desc, weights, batch, y, prob, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t wukong_head_forward_traced(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch,
+                                   const void* y, float* prob, void* workspace, size_t workspace_bytes, void* stream,
+                                   wk_trace* trace) {
+  if (!trace) return WK_ERR_INVALID_ARG;
+  return head_forward(desc, weights, batch, y, prob, workspace, workspace_bytes, stream, trace);
 }
 
 }  // extern "C"

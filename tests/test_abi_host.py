@@ -134,3 +134,54 @@ def test_stack_requires_matching_layers():
     descs = (_abi.wk_layer_desc * 2)(pa[0], pb[0])
     assert lib.wukong_stack_workspace_size(2, descs, 4) == 0
     assert lib.wukong_stack_workspace_size(0, descs, 4) == 0
+
+
+def _head_call(dims, batch, y, prob, ws, ws_bytes, dtype="bf16", w=None, b=None, desc=None):
+    lib = wk.load_library()
+    spec = wk.HeadSpec(tuple(dims), dtype)
+    d, _dims = spec.make_desc()
+    if desc is not None:
+        d = desc
+    T = len(dims) - 1
+    wp = (ctypes.c_void_p * T)(*([0x10000 * (t + 1) for t in range(T)] if w is None else w))
+    bp = None if b is None else (ctypes.c_void_p * T)(*b)
+    hw = _abi.wk_head_weights(ctypes.cast(wp, ctypes.POINTER(ctypes.c_void_p)),
+                              None if bp is None else ctypes.cast(bp, ctypes.POINTER(ctypes.c_void_p)))
+    return lib.wukong_head_forward(ctypes.byref(d), ctypes.byref(hw), batch, y, prob, ws, ws_bytes, None)
+
+
+def test_head_workspace_sizes():
+    # two ping-pong buffers of the widest hidden layer; 256 bytes with no hidden layer
+    assert wk.head_workspace_size(wk.HeadSpec((20480, 1024, 256, 1)), 4096) == 2 * al(4096 * 1024 * 2)
+    assert wk.head_workspace_size(wk.HeadSpec((64, 24, 40, 3), "f32"), 10) == 2 * al(10 * 40 * 4)
+    assert wk.head_workspace_size(wk.HeadSpec((64, 1)), 10) == 256
+    assert wk.head_workspace_size(wk.HeadSpec((64, 12, 1)), 10) == 0          # bf16 hidden width % 8
+    assert wk.head_workspace_size(wk.HeadSpec((60, 16, 1)), 10) == 0          # bf16 input width % 8
+    assert wk.head_workspace_size(wk.HeadSpec((60, 12, 1), "f32"), 10) > 0    # f32 takes any width
+    assert wk.head_workspace_size(wk.HeadSpec((64, 1)), -1) == 0
+
+
+def test_head_argument_errors_launch_nothing():
+    dims = (64, 32, 1)
+    need = wk.head_workspace_size(wk.HeadSpec(dims), 4)
+    Y, P, WS = 0x100000, 0x200000, 0x300000
+    assert _head_call(dims, 4, Y, P, WS, need - 1) == _abi.WK_ERR_WORKSPACE
+    assert _head_call(dims, 4, None, P, WS, need) == _abi.WK_ERR_INVALID_ARG
+    assert _head_call(dims, 4, Y, None, WS, need) == _abi.WK_ERR_INVALID_ARG
+    assert _head_call(dims, 4, Y + 8, P, WS, need) == _abi.WK_ERR_INVALID_ARG      # misaligned y
+    assert _head_call(dims, 4, Y, P + 2, WS, need) == _abi.WK_ERR_INVALID_ARG      # misaligned prob
+    assert _head_call(dims, 4, Y, Y + 64, WS, need) == _abi.WK_ERR_INVALID_ARG     # prob inside y
+    assert _head_call(dims, 4, Y, P, Y, need) == _abi.WK_ERR_INVALID_ARG           # workspace overlaps y
+    assert _head_call(dims, -1, Y, P, WS, need) == _abi.WK_ERR_INVALID_ARG
+    assert _head_call(dims, 0, None, None, None, 0) == _abi.WK_OK                  # empty batch: no-op
+    assert _head_call(dims, 4, Y, P, WS, need, w=[0x10000, None]) == _abi.WK_ERR_INVALID_ARG
+    assert _head_call(dims, 4, Y, P, WS, need, b=[0x20008, None]) == _abi.WK_ERR_INVALID_ARG  # misaligned bias
+    assert _head_call((64, 12, 1), 4, Y, P, WS, need) == _abi.WK_ERR_UNSUPPORTED
+    d, _dims = wk.HeadSpec(dims).make_desc()
+    d.dtype = 9
+    assert _head_call(dims, 4, Y, P, WS, need, desc=d) == _abi.WK_ERR_INVALID_ARG
+    d, _dims = wk.HeadSpec(dims).make_desc()
+    d.num_linear = 0
+    assert _head_call(dims, 4, Y, P, WS, need, desc=d) == _abi.WK_ERR_INVALID_ARG
+    d, _dims = wk.HeadSpec((64, 0, 1)).make_desc()
+    assert _head_call(dims, 4, Y, P, WS, need, desc=d) == _abi.WK_ERR_INVALID_ARG

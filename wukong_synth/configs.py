@@ -78,6 +78,13 @@ class WukongConfig:
     def flops_per_example(self) -> int:
         return sum(s.flops_per_example() for s in self.layers)
 
+    def head_dims(self, hidden: Tuple[int, ...] = (1024, 256), outputs: int = 1) -> Tuple[int, ...]:
+        """Widths of the prediction head on this stack's output: the page names
+        an MLP after the Wukong layers but gives no sizes, so the hidden widths
+        default to 1024 and 256 and one output (a click probability)."""
+        s = self.layers[-1]
+        return (s.n * s.d,) + tuple(hidden) + (outputs,)
+
     def with_batch(self, batch: int) -> "WukongConfig":
         return WukongConfig(self.name, self.dtype, batch, self.layers, self.x_dist,
                             self.unit_width, self.description)

@@ -214,6 +214,22 @@ def make_stack_weights(cfg: WukongConfig, seed: int, affine: str = "identity",
     return [make_layer_weights(cfg.name, i, cfg.layers[i], cfg.dtype, seed, affine) for i in range(l)]
 
 
+def make_head_weights(cfg_name: str, dims, dtype: str, seed: int, affine: str = "identity"):
+    """Xavier-uniform weights [m_t, m_{t-1}] and biases [m_t] of the prediction
+    head's Linears (biases 0 for 'identity', U(-0.5, 0.5) for 'random')."""
+    dims = tuple(dims)
+    w, b = [], []
+    for i, (a, o) in enumerate(zip(dims[:-1], dims[1:])):
+        w.append(xavier_uniform(seed, f"{cfg_name}/head/w{i}", o, a, dtype))
+        if affine == "random":
+            b.append(_store(_uniform_pm(seed, f"{cfg_name}/head/b{i}", o, 0.5), dtype))
+        elif affine == "identity":
+            b.append(_store(np.zeros(o, np.float32), dtype))
+        else:
+            raise ValueError(affine)
+    return w, b
+
+
 def feature_scales(cfg: WukongConfig, seed: int) -> np.ndarray:
     """Per-feature scale s_i = 10**U(-1,1), shared by all examples (float32 [n])."""
     n = cfg.layers[0].n
