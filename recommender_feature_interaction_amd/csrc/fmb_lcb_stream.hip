@@ -101,7 +101,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
 
   const int n = p.n, k = p.k, n_l = p.n_l, n_f = p.n_f;
   const int ZT = sh.zt, KZ = sh.kz, STEPS = sh.steps;
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63, lane_id = lane;
   // wave-uniform (readfirstlane): the DMA loop, its buffer resources and the tile choices stay scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
@@ -125,6 +125,12 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
       __builtin_amdgcn_make_buffer_rsrc((void*)p.w_l, (short)0, n_l * n * 2, 0x00020000);
   auto dma_step = [&](const __amdgpu_buffer_rsrc_t& rx, uint16_t* sw, uint16_t* sx, int step) {
     const int k0 = step * KC;
+    // The lane's offsets are recomputed at every step (a few VALU operations)
+    // from an opaque copy of the lane index: hoisted out of the step loop they
+    // would stay live through it, spill, and each reload's wait for the
+    // vector-memory counter would also wait for the DMA in flight.
+    int lane = lane_id;
+    asm volatile("" : "+v"(lane));
 #pragma unroll
     for (int q = 0; q < INS_HI; ++q) {
       const int i = wave + q * NWAVE;  // wave-uniform
@@ -204,18 +210,19 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
     const __amdgpu_buffer_rsrc_t rbet =
         __builtin_amdgcn_make_buffer_rsrc((void*)p.fm_beta, (short)0, p.fm_beta ? n * k * 2 : 0, 0x00020000);
     const bool has_gamma = p.fm_gamma != nullptr;
+    auto load_gb_row = [&](int mi, u32x2 (&gam)[KJ], u32x2 (&bet)[KJ]) {  // one 16-row block
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt) {
+        const int m = (wave + mi * NWAVE) * 16 + li;
+        const int j0 = jt * 16 + lg * 4;
+        const uint32_t off = (m < n && j0 < k) ? (uint32_t)(m * k + j0) * 2u : kOOB;
+        gam[jt] = has_gamma ? __builtin_amdgcn_raw_buffer_load_b64(rgam, off, 0, 0) : u32x2{0x3f803f80u, 0x3f803f80u};
+        bet[jt] = __builtin_amdgcn_raw_buffer_load_b64(rbet, off, 0, 0);  // zero when absent
+      }
+    };
     auto load_gb = [&]() {
 #pragma unroll
-      for (int mi = 0; mi < MPW; ++mi)
-#pragma unroll
-        for (int jt = 0; jt < KJ; ++jt) {
-          const int m = (wave + mi * NWAVE) * 16 + li;
-          const int j0 = jt * 16 + lg * 4;
-          const uint32_t off = (m < n && j0 < k) ? (uint32_t)(m * k + j0) * 2u : kOOB;
-          fgam[mi][jt] = has_gamma ? __builtin_amdgcn_raw_buffer_load_b64(rgam, off, 0, 0)
-                                   : u32x2{0x3f803f80u, 0x3f803f80u};
-          fbet[mi][jt] = __builtin_amdgcn_raw_buffer_load_b64(rbet, off, 0, 0);  // zero when absent
-        }
+      for (int mi = 0; mi < MPW; ++mi) load_gb_row(mi, fgam[mi], fbet[mi]);
     };
 
     // ---- phase 1: acc[zi][ex][et] = D[e][z] blocks of [Z; Lc]^T
@@ -416,7 +423,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
         }
       }
       if (ex + 1 < E && b + 1 < batch) load_x(ex + 1);
-      if constexpr (!GB_REG) load_gb();
+      // without room for every block's gamma / beta: two blocks' worth, the
+      // next one requested while the current one is written
+      u32x2 gA[KJ], bA[KJ], gB[KJ], bB[KJ];
+      if constexpr (!GB_REG) load_gb_row(0, gA, bA);
       float sm = 0.f;
 #pragma unroll
       for (int mi = 0; mi < MPW; ++mi)
@@ -456,14 +466,13 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
 #pragma unroll
       for (int w = 0; w < NWAVE; ++w) qt += red[NWAVE + w];
       const float rstd = rsqrtf(qt * inv_nk + p.eps);
-#pragma unroll
-      for (int mi = 0; mi < MPW; ++mi)
+      auto fn_store = [&](int mi, const u32x2 (&gam)[KJ], const u32x2 (&bet)[KJ]) {
 #pragma unroll
         for (int jt = 0; jt < KJ; ++jt) {
           const int m = (wave + mi * NWAVE) * 16 + li;
           const int j0 = jt * 16 + lg * 4;
           if (m < n && j0 < k) {  // k % 4 == 0: the 4 values j0 .. j0+3 are all valid
-            const u32x2 g2 = fgam[mi][jt], b2 = fbet[mi][jt];
+            const u32x2 g2 = gam[jt], b2 = bet[jt];
             const f32x4 f = facc[mi][jt];
             u32x2 o;
             o[0] = pack_bf16x2((f[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(b2[0]),
@@ -473,6 +482,19 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
             __builtin_amdgcn_raw_buffer_store_b64(o, rfn, (uint32_t)((ex * n + m) * k + j0) * 2u, 0, 0);
           }
         }
+      };
+#pragma unroll
+      for (int mi = 0; mi < MPW; ++mi) {
+        if constexpr (GB_REG) {
+          fn_store(mi, fgam[mi], fbet[mi]);
+        } else if (mi & 1) {
+          if (mi + 1 < MPW) load_gb_row(mi + 1, gA, bA);
+          fn_store(mi, gB, bB);
+        } else {
+          if (mi + 1 < MPW) load_gb_row(mi + 1, gB, bB);
+          fn_store(mi, gA, bA);
+        }
+      }
     }
   }
 }

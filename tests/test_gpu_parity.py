@@ -95,6 +95,11 @@ RAGGED = [
     _custom("fused_d160_stack2", "bf16", 16, 160, 4, 8, (64, 128, 1280), 260, layers=2),
     # K % 128 == 0 on a ragged batch: the Linear whose DMA is spread over its MFMAs
     _custom("spread_k256_m37", "bf16", 32, 32, 8, 16, (256, 384, 512), 37),
+    # the streamed FMB+LCB kernel: phase 2 pairs j tiles when k % 8 == 0 (16-byte LN loads / Fn stores)
+    _custom("stream_d32_k20", "bf16", 64, 32, 20, 32, (1280, 64, 1024), 7),
+    _custom("stream_d32_k24", "bf16", 48, 32, 24, 16, (1152, 136, 512), 9),
+    _custom("stream_d160_k40", "bf16", 192, 160, 40, 96, (7680, 256, 15360), 5),
+    _custom("stream_d160_k36", "bf16", 192, 160, 36, 96, (6912, 256, 15360), 3),
     _custom("ragged_f32", "f32", 12, 24, 3, 5, (36, 20, 120), 9),
     _custom("ragged_f32_stack", "f32", 12, 24, 3, 5, (36, 20, 120), 4, layers=2),
 ]
