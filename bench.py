@@ -39,12 +39,13 @@ PEAK_F32_TFLOPS = 157.3     # MI355X fp32 vector
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 METRIC = "Wukong stack fwd examples/sec; achieved TFLOP/s as % of bf16 MFMA peak"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+# sources whose SHA-256 (over their concatenation) a traffic record in profiles/ must match
 KERNEL_SOURCES = {
-    "fmb_lcb": "fmb_lcb.hip",
-    "mlp_linear": "linear_bf16.hip",
-    "residual_ln": "resid_ln.hip",
-    "head_linear": "linear_bf16.hip",
-    "head_out": "head.hip",
+    "fmb_lcb": ("fmb_lcb.hip", "fmb_lcb_stream.hip"),
+    "mlp_linear": ("linear_bf16.hip",),
+    "residual_ln": ("resid_ln.hip",),
+    "head_linear": ("linear_bf16.hip",),
+    "head_out": ("head.hip",),
 }
 
 
@@ -178,9 +179,11 @@ def measure_head(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
 
 
 def source_digest(name):
-    path = os.path.join(ROOT, "recommender_feature_interaction_amd", "csrc", KERNEL_SOURCES[name])
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for src in KERNEL_SOURCES[name]:
+        with open(os.path.join(ROOT, "recommender_feature_interaction_amd", "csrc", src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def read_traffic(kernel, index, workload):

@@ -202,8 +202,11 @@ typedef struct {
                            a NULL array: no bias)                                  */
 } wk_head_weights;
 
-/* Workspace bytes for wukong_head_forward (two ping-pong buffers of the widest
- * hidden layer), 0 for an invalid or unsupported desc; 256 for T == 1. */
+/* Workspace bytes for wukong_head_forward: two ping-pong buffers of the widest
+ * hidden layer, plus (bf16) fp32 partial sums for a hidden Linear whose batch
+ * is too small to fill the GPU, which is then split along K (the splits are
+ * summed in a fixed order, so results do not depend on timing).  0 for an
+ * invalid or unsupported desc; 256 for T == 1. */
 size_t wukong_head_workspace_size(const wk_head_desc* desc, int64_t batch);
 
 /* prob [batch, m_T] fp32 (device) from y [batch, dims[0]] (device, the layer

@@ -73,8 +73,9 @@ constexpr int lgkm_wait0() { return 15 | (7 << 4) | (0 << 8) | (3 << 14); }
 
 __device__ __forceinline__ int swz(int row, int ch) { return row * kBK + ((ch ^ ((row >> 1) & 7)) << 3); }
 
-__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int BM, int BN, int64_t& m0, int& n0) {
-  const int nblk = gridDim.x, bid = blockIdx.x, full = nblk & ~7;
+__device__ __forceinline__ void tile_origin_at(int bid, int nblk, int tiles_m, int tiles_n, int BM, int BN,
+                                               int64_t& m0, int& n0) {
+  const int full = nblk & ~7;
   int logical = bid;
   if (bid < full) logical = (bid & 7) * (full >> 3) + (bid >> 3);
   constexpr int GM = 8;
@@ -85,6 +86,9 @@ __device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int BM, in
   const int in_g = logical - group * per_group;
   m0 = (int64_t)(first_m + in_g % gsz) * BM;
   n0 = (in_g / gsz) * BN;
+}
+__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int BM, int BN, int64_t& m0, int& n0) {
+  tile_origin_at(blockIdx.x, gridDim.x, tiles_m, tiles_n, BM, BN, m0, n0);
 }
 
 
@@ -108,7 +112,8 @@ template <int BM, int BN, int WGM, int WGN, bool SPREAD = false>
 __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint16_t* w_base, int64_t M, int N,
                                              int K, int64_t m0, int n0, uint16_t* sA0, uint16_t* sW0,
                                              uint16_t* sA1, uint16_t* sW1,
-                                             f32x4 (&acc)[BN / WGN / 16][BM / WGM / 16]) {
+                                             f32x4 (&acc)[BN / WGN / 16][BM / WGM / 16], int kbeg = 0,
+                                             int klen = -1) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MB = WTM / 16, NB = WTN / 16;
@@ -133,13 +138,13 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
     for (int i = 0; i < A_INS; ++i) {
       const int blk = wave * A_INS + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, WK_LDS(sa + blk * 512), 16,
-                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, k0 * 2, 0, 0);
+                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, (kbeg + k0) * 2, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < W_INS; ++i) {
       const int blk = wave * W_INS + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, WK_LDS(sw + blk * 512), 16,
-                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, k0 * 2, 0, 0);
+                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, (kbeg + k0) * 2, 0, 0);
     }
   };
 #pragma unroll
@@ -163,7 +168,9 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
         for (int j = 0; j < MB; ++j) acc[i][j] = mfma16x16x32(wf[i], af[j], acc[i][j]);
     }
   };
-  const int KT = K / kBK;
+  // columns kbeg .. kbeg + klen of K (all of them by default); the resources
+  // still span whole rows
+  const int KT = (klen < 0 ? K : klen) / kBK;
   dma(sA0, sW0, 0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
   lds_barrier();
@@ -270,6 +277,80 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
 // row is D/16 blocks x 4 columns x the 4 lanes l16 + 16 lg: its LayerNorm
 // statistics are a sum over registers and two xor-shuffles.  M is rounded to
 // bf16 before the residual is added, as the unfused path stores it.
+// Split-K: a grid of tiles x splits; split s accumulates columns
+// [s K/splits, (s + 1) K/splits) of K and writes its fp32 partial sums to
+// part[s][m][n] (no bias, no activation).  splitk_reduce_kernel then adds the
+// partials in the fixed order s = 0, 1, .. (the result does not depend on
+// timing), the bias and the ReLU, and rounds to bf16.  For Linears whose tiles
+// alone leave CUs idle (few rows, long K: the prediction head's first Linear).
+template <int BM, int BN, int WGM, int WGN, bool SPREAD>
+__global__ __launch_bounds__(WGM * WGN * 64) void linear_splitk_kernel(LinearKArgs p, float* part, int splits) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int split = (int)blockIdx.x / ntiles, tile = (int)blockIdx.x - split * ntiles;
+  int64_t m0;
+  int n0;
+  tile_origin_at(tile, ntiles, p.tiles_m, p.tiles_n, BM, BN, m0, n0);
+  const int64_t M = p.M;
+  const int N = p.N;
+  const int klen = p.K / splits;
+  f32x4 acc[NB][MB];
+  dma_mainloop<BM, BN, WGM, WGN, SPREAD>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc, split * klen, klen);
+  float* ps = part + (int64_t)split * M * N;
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int n = n0 + wn * WTN + i * 16 + lg * 4;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int64_t m = m0 + wm * WTM + j * 16 + l16;
+      if (m < M && n < N) *reinterpret_cast<f32x4*>(ps + m * N + n) = acc[i][j];
+    }
+  }
+}
+
+// C = bf16(act(sum_s part[s] + bias)), 8 consecutive columns per thread (N % 8 == 0).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int splits, int64_t M, int N,
+                                                            const uint16_t* bias, int relu, uint16_t* c) {
+  const int64_t total = M * N / 8;
+  const int64_t plane = M * N;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
+       q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e = q * 8;
+    const int n = (int)(e % N);
+    f32x4 lo = *reinterpret_cast<const f32x4*>(part + e);
+    f32x4 hi = *reinterpret_cast<const f32x4*>(part + e + 4);
+    for (int sp = 1; sp < splits; ++sp) {
+      lo += *reinterpret_cast<const f32x4*>(part + sp * plane + e);
+      hi += *reinterpret_cast<const f32x4*>(part + sp * plane + e + 4);
+    }
+    float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    if (bias != nullptr) {
+      const u32x4 b = *reinterpret_cast<const u32x4*>(bias + n);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[2 * t] += bf16lo(b[t]);
+        v[2 * t + 1] += bf16hi(b[t]);
+      }
+    }
+    u32x4 o;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x0 = v[2 * t], x1 = v[2 * t + 1];
+      if (relu) {
+        x0 = fmaxf(x0, 0.f);
+        x1 = fmaxf(x1, 0.f);
+      }
+      o[t] = pack_bf16x2(x0, x1);
+    }
+    *reinterpret_cast<u32x4*>(c + e) = o;
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int D>
 __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs p) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
@@ -641,6 +722,60 @@ hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int6
   if (workgroups) *workgroups = blocks;
   if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(v->kernel, dim3((unsigned)blocks), dim3(kLnThreads), 0, stream, k);
+  return hipGetLastError();
+}
+
+// Split-K on 128 x 128 tiles (two workgroups per CU) when the unsplit tiling
+// leaves workgroup slots empty: splits double while the tiles do not fill
+// every slot, the split length stays a multiple of 128 (the spread main loop)
+// and at least 2048 long.  1 = no split.
+constexpr int kSplitBM = 128, kSplitBN = 128, kSplitOcc = 2, kMaxSplits = 8;
+
+int linear_bf16_splits(int64_t M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || N % 8 != 0) return 1;
+  const LinearVariant* v = pick_linear(M, N, K);
+  if (!v) return 1;
+  const double tiles_v = (double)((M + v->bm - 1) / v->bm) * (double)((N + v->bn - 1) / v->bn);
+  if (tiles_v >= (double)kNumCU * v->occupancy) return 1;
+  const double tiles = (double)((M + kSplitBM - 1) / kSplitBM) * (double)((N + kSplitBN - 1) / kSplitBN);
+  int sp = 1;
+  while (sp < kMaxSplits && tiles * sp < (double)kNumCU * kSplitOcc && K % (2 * sp * 128) == 0 &&
+         K / (2 * sp) >= 2048)
+    sp *= 2;
+  return sp;
+}
+
+size_t linear_bf16_split_bytes(int64_t M, int N, int K) {
+  const int sp = linear_bf16_splits(M, N, K);
+  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStream_t stream, int64_t* workgroups) {
+  const int sp = linear_bf16_splits(a.M, a.N, a.K);
+  if (sp <= 1 || partial == nullptr) return hipErrorInvalidValue;
+  LinearKArgs k;
+  k.a = static_cast<const uint16_t*>(a.a);
+  k.w = static_cast<const uint16_t*>(a.w);
+  k.bias = static_cast<const uint16_t*>(a.bias);
+  k.c = static_cast<uint16_t*>(a.c);
+  k.M = a.M;
+  k.N = a.N;
+  k.K = a.K;
+  k.relu = a.relu;
+  k.tiles_m = (int)((a.M + kSplitBM - 1) / kSplitBM);
+  k.tiles_n = (a.N + kSplitBN - 1) / kSplitBN;
+  const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n * sp;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (workgroups) *workgroups = blocks;
+  hipLaunchKernelGGL((linear_splitk_kernel<kSplitBM, kSplitBN, 2, 2, true>), dim3((unsigned)blocks), dim3(256), 0,
+                     stream, k, partial, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t groups8 = a.M * a.N / 8;
+  int64_t grid = (groups8 + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partial, sp, a.M, a.N,
+                     static_cast<const uint16_t*>(a.bias), a.relu, static_cast<uint16_t*>(a.c));
   return hipGetLastError();
 }
 

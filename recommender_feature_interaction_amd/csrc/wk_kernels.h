@@ -60,6 +60,13 @@ struct LinearArgs {
 bool linear_bf16_supported(int64_t M, int N, int K);
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);
+// Split-K form of the bf16 Linear for shapes whose tiles leave CUs idle:
+// linear_bf16_splits() = number of K splits (1: use launch_linear_bf16),
+// linear_bf16_split_bytes() = the fp32 partial-sum buffer it needs (0 if none);
+// the launch runs the split GEMM and the reduction (bias, ReLU, bf16).
+int linear_bf16_splits(int64_t M, int N, int K);
+size_t linear_bf16_split_bytes(int64_t M, int N, int K);
+hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStream_t stream, int64_t* workgroups);
 
 // The last Linear with the FMB rows' output stage fused in (bf16):
 // Y[b, r] = LN_d(bf16(A[b] W^T + bias)[r d .. r d + d) + X[b, r]) for r < n_f,

@@ -317,17 +317,27 @@ int32_t check_head_desc(const wk_head_desc* d) {
 }
 
 struct HeadPlan {
-  size_t h[2] = {0, 0}, bytes = 0;
+  size_t h[2] = {0, 0}, part = 0, bytes = 0;
 };
 
+// Workspace: two ping-pong buffers of the widest hidden layer, then (bf16) the
+// fp32 partial sums of the largest split-K hidden Linear.
 HeadPlan plan_head(const wk_head_desc& d, int64_t batch) {
   HeadPlan p;
   int64_t maxhid = 0;
-  for (int t = 1; t < d.num_linear; ++t) maxhid = d.dims[t] > maxhid ? d.dims[t] : maxhid;
+  size_t part = 0;
+  for (int t = 1; t < d.num_linear; ++t) {
+    maxhid = d.dims[t] > maxhid ? d.dims[t] : maxhid;
+    if (d.dtype == WK_BF16) {
+      const size_t pb = wk::linear_bf16_split_bytes(batch, d.dims[t], d.dims[t - 1]);
+      part = pb > part ? pb : part;
+    }
+  }
   const size_t buf = align_up((size_t)batch * (size_t)maxhid * esize(d.dtype));
   p.h[0] = 0;
   p.h[1] = buf;
-  p.bytes = d.num_linear > 1 ? 2 * buf : kAlign;
+  p.part = d.num_linear > 1 ? 2 * buf : 0;
+  p.bytes = p.part + align_up(part);
   if (p.bytes == 0) p.bytes = kAlign;
   return p;
 }
@@ -369,7 +379,10 @@ int32_t head_forward(const wk_head_desc* d, const wk_head_weights* w, int64_t ba
     a.N = d->dims[t + 1];
     a.K = d->dims[t];
     a.relu = 1;
+    const bool split = bf && wk::linear_bf16_splits(a.M, a.N, a.K) > 1;
+    float* part = reinterpret_cast<float*>(base + hp.part);
     st = launch(WK_KERNEL_HEAD_LINEAR, 0, t, [&](int64_t* g) {
+      if (split) return wk::launch_linear_bf16_splitk(a, part, launch.stream, g);
       return bf ? wk::launch_linear_bf16(a, launch.stream, g) : wk::launch_linear_f32(a, launch.stream, g);
     });
     if (st != WK_OK) return st;

@@ -152,7 +152,14 @@ def _head_call(dims, batch, y, prob, ws, ws_bytes, dtype="bf16", w=None, b=None,
 
 def test_head_workspace_sizes():
     # two ping-pong buffers of the widest hidden layer; 256 bytes with no hidden layer
-    assert wk.head_workspace_size(wk.HeadSpec((20480, 1024, 256, 1)), 4096) == 2 * al(4096 * 1024 * 2)
+    assert wk.head_workspace_size(wk.HeadSpec((40960, 1024, 256, 1)), 16384) == 2 * al(16384 * 1024 * 2)
+    # + fp32 partial sums when a hidden Linear is split along K (few rows, long K): 2 and 4 splits
+    assert wk.head_workspace_size(wk.HeadSpec((20480, 1024, 256, 1)), 4096) == \
+        2 * al(4096 * 1024 * 2) + 2 * 4096 * 1024 * 4
+    assert wk.head_workspace_size(wk.HeadSpec((81920, 1024, 256, 1)), 2048) == \
+        2 * al(2048 * 1024 * 2) + 4 * 2048 * 1024 * 4
+    assert wk.head_workspace_size(wk.HeadSpec((4096, 72, 1)), 37) == 2 * al(37 * 72 * 2) + al(2 * 37 * 72 * 4)
+    assert wk.head_workspace_size(wk.HeadSpec((4096, 72, 1), "f32"), 37) == 2 * al(37 * 72 * 4)  # no split
     assert wk.head_workspace_size(wk.HeadSpec((64, 24, 40, 3), "f32"), 10) == 2 * al(10 * 40 * 4)
     assert wk.head_workspace_size(wk.HeadSpec((64, 1)), 10) == 256
     assert wk.head_workspace_size(wk.HeadSpec((64, 12, 1)), 10) == 0          # bf16 hidden width % 8

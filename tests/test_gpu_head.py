@@ -73,6 +73,8 @@ HEADS_BF16 = [
     ((256, 136, 40, 3), 37),           # ragged widths: K % 64 != 0 on the second Linear
     ((128, 2), 5),                     # no hidden layer
     ((512, 64, 1), 1),
+    ((4096, 72, 1), 37),               # the hidden Linear split in two along K (ragged rows and columns)
+    ((81920, 1024, 256, 1), 40),       # the n = 512 stack's head: 8 K splits
 ]
 
 
