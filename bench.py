@@ -12,6 +12,12 @@ kernel with the largest share of the step reported against its roofline.
 The CPU oracle is timed on a bounded sample of the same workload on this host
 as a reference baseline.
 
+The same steps are timed once more with 512 MB written between them (no
+input or weight left in L2 or the last-level cache: "cold_cache_ms_per_step"),
+a 256 MiB device copy gives the on-box HBM bandwidth ("copy_gbps_measured"),
+and "step_roofline_frac" is the sum over kernels of max(FLOPs / peak, bytes /
+HBM bandwidth) divided by the measured step.
+
 The prediction head (top MLP + logistic function) is then timed on its own
 on the stack's output and reported under "head"; it is not part of `value`.
 
@@ -246,6 +252,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
     ap.add_argument("--no-head", action="store_true", help="skip the prediction-head measurement")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache (512 MB flush) step timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -330,6 +337,45 @@ def main():
         roofline = roofline_of(dominant, acct[(dominant["kernel"], dominant["layer"], dominant["index"])],
                                dominant["avg_ms"], cfg.dtype, cfg.name)
 
+    # the same steps with 512 MB written between them (untimed), so no input or
+    # weight is still in L2 or the 256 MB last-level cache when a step starts;
+    # each step timed with HIP events on the launch stream
+    cold_ms = None
+    if not args.no_cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for e0, e1 in ev:
+            flush.fill_(1)
+            e0.record(stream)
+            wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
+        del flush
+
+    # on-box copy bandwidth: a 256 MiB device-to-device copy (reads + writes)
+    csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (256 << 20) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del csrc, cdst
+    if roofline is not None and roofline["unit"] == "GB/s":
+        roofline["frac_of_measured_copy"] = round(roofline["achieved"] / copy_gbps, 4)
+
+    # layer roofline fraction: sum over kernels of max(F/P, B/BW) against the measured step
+    ideal_ms = 0.0
+    for key, ac in acct.items():
+        ideal_ms += 1e3 * max(ac["flops"] / (PEAK_BF16_TFLOPS * 1e12 if cfg.dtype == "bf16" else PEAK_F32_TFLOPS * 1e12),
+                              ac["bytes"] / (PEAK_HBM_GBPS * 1e9))
+
     head = None
     if not args.no_head:
         head = measure_head(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
@@ -357,6 +403,9 @@ def main():
         "step_tflops": round(step_tflops, 2),
         "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
         "roofline": roofline,
+        "step_roofline_frac": round(ideal_ms / ms_per_step, 4),
+        "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 4),
+        "copy_gbps_measured": round(copy_gbps, 1),
         "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
         "head": head,
     }

@@ -1,0 +1,307 @@
+// FMB + LCB for embedding units of width d = 8 (bf16, fp32 accumulation).
+//
+// Wukong paper, section 2.1: a feature's embedding is cut into 8-wide units
+// and each unit takes part in the interaction as a feature of its own, so a
+// layer sees n units of width d = 8 per example.  Section 2.2 defines the
+// layer: [Z_b; Lc_b] = [Phi; W_L] X_b, F_b = X_b Z_b^T, Fn_b = LN(vec F_b),
+// and the LCB rows of the output Y_b[n_F + i] = LN_d(Lc_b[i] + X_b[n_F + i]).
+//
+// With d = 8 an example's X_b is n x 16 bytes, too narrow for the per-example
+// MFMA tiles of the other FMB+LCB kernels, and [Phi; W_L] (k + n_L rows of n)
+// is far too large to stream per example.  So the left multiply becomes one
+// GEMM over the whole batch:
+//   1. units_transpose_kernel: Xt[b][e][j] = X[b][j][e] (the GEMM's A operand,
+//      K = n contiguous);
+//   2. the bf16 DMA GEMM with fp32 output: C[(b, e)][r] = sum_j Xt[(b, e)][j]
+//      [Phi; W_L][r][j], i.e. C[b][e][r] = [Z_b; Lc_b][r][e];
+//   3. units_epilogue_kernel, a group of examples per workgroup: the LCB rows
+//      (Lc in fp32 + residual, LayerNorm over the 8 values, bf16 out); Z_b
+//      rounded to bf16 (the MFMA operand precision of the other kernels) as a
+//      register operand; F_b^T = Z_b X_b^T on the MFMA 32 rows at a time, the
+//      statistics merged by Chan's parallel-variance formula (count, mean, sum
+//      of squared deviations) and reduced over the workgroup, then a second
+//      pass that recomputes each block and writes Fn with the FMB LayerNorm's
+//      gamma / beta.
+#include "wk_device.h"
+#include "wk_kernels.h"
+
+namespace wk {
+
+namespace {
+
+constexpr int UD = 8;        // unit width
+constexpr int UE = 4;        // examples per workgroup in the epilogue
+constexpr int UT = 256;      // threads per epilogue workgroup
+constexpr int UKMAX = 32;    // largest k (Z rows fill one 32-row MFMA operand)
+
+// Xt[b][e][j] = X[b][j][e]; two rows j, j + 1 per thread so each store is 4 bytes.
+__global__ __launch_bounds__(256) void units_transpose_kernel(const uint16_t* x, uint16_t* xt, int64_t batch, int n) {
+  const int half = n / 2;
+  const int64_t total = batch * half;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t b = q / half;
+    const int j = 2 * (int)(q - b * half);
+    const u32x4 r0 = *reinterpret_cast<const u32x4*>(x + (b * n + j) * UD);
+    const u32x4 r1 = *reinterpret_cast<const u32x4*>(x + (b * n + j + 1) * UD);
+    uint32_t* out = reinterpret_cast<uint32_t*>(xt + b * n * UD + j);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      out[(2 * t) * (n / 2)] = pack_lo(r0[t], r1[t]);      // e = 2t
+      out[(2 * t + 1) * (n / 2)] = pack_hi(r0[t], r1[t]);  // e = 2t + 1
+    }
+  }
+}
+
+struct UnitsArgs {
+  const uint16_t* x;
+  const float* c;            // [B][8][k + n_l]
+  const uint16_t* fm_gamma;  // [n k] or null
+  const uint16_t* fm_beta;
+  const uint16_t* out_gamma; // [8] or null
+  const uint16_t* out_beta;
+  uint16_t* fn;              // [B][n k]
+  uint16_t* y;               // [B][n][8]: rows n_f .. n-1 written here
+  int n, k, n_f, n_l;
+  float eps;
+};
+
+// Merge (count, mean, M2) of two disjoint sets (Chan, Golub, LeVeque).
+__device__ __forceinline__ void chan_merge(float& cnt, float& mean, float& m2, float cb, float mb, float m2b) {
+  const float tot = cnt + cb;
+  if (cb == 0.f) return;
+  if (cnt == 0.f) {
+    cnt = cb;
+    mean = mb;
+    m2 = m2b;
+    return;
+  }
+  const float delta = mb - mean;
+  mean += delta * (cb / tot);
+  m2 += m2b + delta * delta * (cnt * cb / tot);
+  cnt = tot;
+}
+
+// F^T blocks on the MFMA: D = Z X^T over 32 rows m at a time with
+// v_mfma_f32_32x32x16_bf16, the 8-wide contraction padded to 16 with zeros
+// (lanes 32..63 supply zero operands).  Lane l then holds rows m = l % 32 and
+// j = 8 (r / 4) + 4 (l / 32) + r % 4 of F, r = 0..15: chunks of 4 consecutive
+// j, so the LayerNorm's gamma / beta and Fn move in 8-byte pieces.
+__global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t batch) {
+  __shared__ float wred[UE][UT / 64][3];
+  __shared__ float stat[UE][2];  // mean, rstd of F per example
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+  const int n = p.n, k = p.k, n_f = p.n_f, n_l = p.n_l;
+  const int N = k + n_l;
+  const float inv_nk = 1.0f / (float)(n * k);
+  float og[UD], ob[UD];
+#pragma unroll
+  for (int e = 0; e < UD; ++e) {
+    og[e] = p.out_gamma ? bf16_to_f32(p.out_gamma[e]) : 1.f;
+    ob[e] = p.out_beta ? bf16_to_f32(p.out_beta[e]) : 0.f;
+  }
+  const int64_t groups = (batch + UE - 1) / UE;
+  for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+    const int64_t b0 = g * UE;
+    const int ne = (int)(batch - b0 < UE ? batch - b0 : UE);
+    // LCB rows of Y: Lc (fp32) + residual, LayerNorm over the 8 values
+    for (int q = tid; q < ne * n_l; q += UT) {
+      const int ex = q / n_l, i = q - ex * n_l;
+      const int64_t b = b0 + ex;
+      const u32x4 xr = *reinterpret_cast<const u32x4*>(p.x + (b * n + n_f + i) * UD);
+      float v[UD];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        v[2 * t] = bf16lo(xr[t]);
+        v[2 * t + 1] = bf16hi(xr[t]);
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < UD; ++e) {
+        v[e] += p.c[(b * UD + e) * (int64_t)N + k + i];
+        s += v[e];
+      }
+      const float mean = s * (1.0f / UD);
+      float m2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < UD; ++e) m2 += (v[e] - mean) * (v[e] - mean);
+      const float rstd = rsqrtf(m2 * (1.0f / UD) + p.eps);
+      u32x4 o;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        o[t] = pack_bf16x2((v[2 * t] - mean) * rstd * og[2 * t] + ob[2 * t],
+                           (v[2 * t + 1] - mean) * rstd * og[2 * t + 1] + ob[2 * t + 1]);
+      *reinterpret_cast<u32x4*>(p.y + (b * n + n_f + i) * UD) = o;
+    }
+
+    // Z operands: lane l < 32 holds Z[l][0..7] rounded to bf16 (zero for l >= k)
+    u32x4 zop[UE];
+#pragma unroll
+    for (int ex = 0; ex < UE; ++ex) {
+      zop[ex] = u32x4{0u, 0u, 0u, 0u};
+      if (ex < ne && h == 0 && l32 < k) {
+        const float* cz = p.c + (b0 + ex) * UD * (int64_t)N + l32;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) zop[ex][t] = pack_bf16x2(cz[(2 * t) * N], cz[(2 * t + 1) * N]);
+      }
+    }
+    auto f_block = [&](int ex, int m) {  // this lane's 16 values of rows m .. m + 31 of F^T
+      u32x4 xop = u32x4{0u, 0u, 0u, 0u};
+      if (h == 0 && m < n) xop = *reinterpret_cast<const u32x4*>(p.x + ((b0 + ex) * n + m) * UD);
+      f32x16 zero;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+      return mfma32x32x16(zop[ex], xop, zero);
+    };
+    // pass 1: statistics (count, mean, M2) per example
+    float cnt[UE], mu[UE], m2[UE];
+#pragma unroll
+    for (int ex = 0; ex < UE; ++ex) cnt[ex] = mu[ex] = m2[ex] = 0.f;
+#pragma unroll 2
+    for (int m0 = wave * 32; m0 < n; m0 += UT / 2) {
+      const int m = m0 + l32;
+#pragma unroll
+      for (int ex = 0; ex < UE; ++ex) {
+        if (ex >= ne) break;
+        const f32x16 d = f_block(ex, m);
+        float s = 0.f, c = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = m < n && 8 * (r >> 2) + 4 * h + (r & 3) < k;
+          s += ok ? d[r] : 0.f;
+          c += ok ? 1.f : 0.f;
+        }
+        const float lm = c > 0.f ? s / c : 0.f;
+        float q = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool ok = m < n && 8 * (r >> 2) + 4 * h + (r & 3) < k;
+          q += ok ? (d[r] - lm) * (d[r] - lm) : 0.f;
+        }
+        chan_merge(cnt[ex], mu[ex], m2[ex], c, lm, q);
+      }
+    }
+#pragma unroll
+    for (int ex = 0; ex < UE; ++ex) {
+      for (int off = 1; off < 64; off <<= 1) {
+        const float cb = __shfl_xor(cnt[ex], off, 64), mb = __shfl_xor(mu[ex], off, 64),
+                    m2b = __shfl_xor(m2[ex], off, 64);
+        chan_merge(cnt[ex], mu[ex], m2[ex], cb, mb, m2b);
+      }
+      if (lane == 0) {
+        wred[ex][wave][0] = cnt[ex];
+        wred[ex][wave][1] = mu[ex];
+        wred[ex][wave][2] = m2[ex];
+      }
+    }
+    __syncthreads();
+    if (tid < UE) {
+      float c0 = 0.f, mm = 0.f, s0 = 0.f;
+      for (int w = 0; w < UT / 64; ++w) chan_merge(c0, mm, s0, wred[tid][w][0], wred[tid][w][1], wred[tid][w][2]);
+      stat[tid][0] = mm;
+      stat[tid][1] = rsqrtf(s0 * inv_nk + p.eps);
+    }
+    __syncthreads();
+    // pass 2: recompute each block, FMB LayerNorm with gamma / beta, Fn in bf16
+#pragma unroll 2
+    for (int m0 = wave * 32; m0 < n; m0 += UT / 2) {
+      const int m = m0 + l32;
+      u32x2 gv[4], bv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j0 = 8 * c + 4 * h;
+        const bool ok = m < n && j0 < k;  // k % 4 == 0: all of j0 .. j0 + 3 valid
+        const int64_t off = (int64_t)m * k + j0;
+        gv[c] = ok && p.fm_gamma ? *reinterpret_cast<const u32x2*>(p.fm_gamma + off) : u32x2{0x3f803f80u, 0x3f803f80u};
+        bv[c] = ok && p.fm_beta ? *reinterpret_cast<const u32x2*>(p.fm_beta + off) : u32x2{0u, 0u};
+      }
+#pragma unroll
+      for (int ex = 0; ex < UE; ++ex) {
+        if (ex >= ne) break;
+        const f32x16 d = f_block(ex, m);
+        const float mean = stat[ex][0], rstd = stat[ex][1];
+        uint16_t* out = p.fn + (b0 + ex) * (int64_t)n * k + (int64_t)m * k;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j0 = 8 * c + 4 * h;
+          if (m < n && j0 < k) {
+            u32x2 o;
+            o[0] = pack_bf16x2((d[4 * c] - mean) * rstd * bf16lo(gv[c][0]) + bf16lo(bv[c][0]),
+                               (d[4 * c + 1] - mean) * rstd * bf16hi(gv[c][0]) + bf16hi(bv[c][0]));
+            o[1] = pack_bf16x2((d[4 * c + 2] - mean) * rstd * bf16lo(gv[c][1]) + bf16lo(bv[c][1]),
+                               (d[4 * c + 3] - mean) * rstd * bf16hi(gv[c][1]) + bf16hi(bv[c][1]));
+            *reinterpret_cast<u32x2*>(out + j0) = o;
+          }
+        }
+      }
+    }
+    __syncthreads();  // wred and stat are reused by the next group
+  }
+}
+
+}  // namespace
+
+bool fmb_lcb_units_supported(int n, int d, int k, int n_l) {
+  return d == UD && n > 0 && n % 64 == 0 && k > 0 && k % 4 == 0 && k <= UKMAX && n_l > 0 && (k + n_l) % 8 == 0;
+}
+
+size_t fmb_lcb_units_workspace(int64_t batch, int n, int k, int n_l) {
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  return al((size_t)batch * n * UD * 2) + al((size_t)(k + n_l) * n * 2) + al((size_t)batch * UD * (k + n_l) * 4);
+}
+
+hipError_t launch_fmb_lcb_units(const FmbLcbArgs& a, int64_t batch, void* scratch, hipStream_t stream,
+                                int64_t* workgroups) {
+  if (!fmb_lcb_units_supported(a.n, a.d, a.k, a.n_l)) return hipErrorInvalidValue;
+  if (workgroups) *workgroups = 0;
+  if (batch == 0) return hipSuccess;
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  char* base = static_cast<char*>(scratch);
+  uint16_t* xt = reinterpret_cast<uint16_t*>(base);
+  uint16_t* wcat = reinterpret_cast<uint16_t*>(base + al((size_t)batch * a.n * UD * 2));
+  float* c = reinterpret_cast<float*>(base + al((size_t)batch * a.n * UD * 2) + al((size_t)(a.k + a.n_l) * a.n * 2));
+  const int N = a.k + a.n_l;
+  // [Phi; W_L] as one [k + n_l, n] operand
+  hipError_t e = hipMemcpyAsync(wcat, a.phi, (size_t)a.k * a.n * 2, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return e;
+  e = hipMemcpyAsync(wcat + (size_t)a.k * a.n, a.w_l, (size_t)a.n_l * a.n * 2, hipMemcpyDeviceToDevice, stream);
+  if (e != hipSuccess) return e;
+  int64_t tgrid = (batch * (a.n / 2) + 255) / 256;
+  if (tgrid > 8192) tgrid = 8192;
+  hipLaunchKernelGGL(units_transpose_kernel, dim3((unsigned)tgrid), dim3(256), 0, stream, a.x, xt, batch, a.n);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  LinearArgs g;
+  g.a = xt;
+  g.w = wcat;
+  g.bias = nullptr;
+  g.c = c;
+  g.M = batch * UD;
+  g.N = N;
+  g.K = a.n;
+  g.relu = 0;
+  int64_t gw = 0;
+  e = launch_linear_bf16_f32out(g, c, stream, &gw);
+  if (e != hipSuccess) return e;
+  UnitsArgs u;
+  u.x = a.x;
+  u.c = c;
+  u.fm_gamma = a.fm_gamma;
+  u.fm_beta = a.fm_beta;
+  u.out_gamma = a.out_gamma;
+  u.out_beta = a.out_beta;
+  u.fn = a.fn;
+  u.y = a.y;
+  u.n = a.n;
+  u.k = a.k;
+  u.n_f = a.n_f;
+  u.n_l = a.n_l;
+  u.eps = a.eps;
+  const int64_t groups = (batch + UE - 1) / UE;
+  const int64_t egrid = groups < 2048 ? groups : 2048;
+  hipLaunchKernelGGL(units_epilogue_kernel, dim3((unsigned)egrid), dim3(UT), 0, stream, u, batch);
+  if (workgroups) *workgroups = tgrid + gw + egrid;
+  return hipGetLastError();
+}
+
+}  // namespace wk

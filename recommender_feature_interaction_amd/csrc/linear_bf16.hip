@@ -779,6 +779,33 @@ hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStr
   return hipGetLastError();
 }
 
+// C (fp32, row-major [M, N]) = A W^T on 256 x 256 tiles with no bias or
+// activation: the split kernel with one split writes its sums straight to C.
+bool linear_bf16_f32out_supported(int64_t M, int N, int K) {
+  return M > 0 && N > 0 && K > 0 && K % kBK == 0 && N % 8 == 0;
+}
+
+hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t stream, int64_t* workgroups) {
+  if (!linear_bf16_f32out_supported(a.M, a.N, a.K) || c == nullptr) return hipErrorInvalidValue;
+  LinearKArgs k;
+  k.a = static_cast<const uint16_t*>(a.a);
+  k.w = static_cast<const uint16_t*>(a.w);
+  k.bias = nullptr;
+  k.c = nullptr;
+  k.M = a.M;
+  k.N = a.N;
+  k.K = a.K;
+  k.relu = 0;
+  k.tiles_m = (int)((a.M + 255) / 256);
+  k.tiles_n = (a.N + 255) / 256;
+  const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (workgroups) *workgroups = blocks;
+  hipLaunchKernelGGL((linear_splitk_kernel<256, 256, 2, 4, false>), dim3((unsigned)blocks), dim3(512), 0, stream, k, c,
+                     1);
+  return hipGetLastError();
+}
+
 bool linear_bf16_supported(int64_t M, int N, int K) {
   return M > 0 && N > 0 && K > 0 && (K % 8) == 0 && (N % 8) == 0;
 }

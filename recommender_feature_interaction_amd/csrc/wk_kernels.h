@@ -29,6 +29,14 @@ bool fmb_lcb_stream_supported(int n, int d, int k, int n_l);
 hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups);
+// Units of width d = 8 (fmb_lcb_units.hip): transpose, one batched GEMM with
+// fp32 output, and an epilogue kernel; needs fmb_lcb_units_workspace() bytes
+// of scratch (16-byte aligned), n % 64 == 0, k % 4 == 0, k <= 32,
+// (k + n_l) % 8 == 0.
+bool fmb_lcb_units_supported(int n, int d, int k, int n_l);
+size_t fmb_lcb_units_workspace(int64_t batch, int n, int k, int n_l);
+hipError_t launch_fmb_lcb_units(const FmbLcbArgs& a, int64_t batch, void* scratch, hipStream_t stream,
+                                int64_t* workgroups);
 
 struct FmbLcbF32Args {
   const float* x;
@@ -67,6 +75,9 @@ hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream, int64_t* w
 int linear_bf16_splits(int64_t M, int N, int K);
 size_t linear_bf16_split_bytes(int64_t M, int N, int K);
 hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStream_t stream, int64_t* workgroups);
+// C = A W^T in fp32 (no bias, no activation), K % 64 == 0, N % 8 == 0.
+bool linear_bf16_f32out_supported(int64_t M, int N, int K);
+hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t stream, int64_t* workgroups);
 
 // The last Linear with the FMB rows' output stage fused in (bf16):
 // Y[b, r] = LN_d(bf16(A[b] W^T + bias)[r d .. r d + d) + X[b, r]) for r < n_f,

@@ -58,10 +58,11 @@ int32_t check_desc(const wk_layer_desc* d) {
   // The residual adds X row by row, so the concatenation must have n rows.
   if (d->n_f + d->n_l != d->n) return WK_ERR_UNSUPPORTED;
   if (d->dtype == WK_BF16) {
-    if (d->d % 16 || d->n % 8 || d->k % 4) return WK_ERR_UNSUPPORTED;
+    const bool units = wk::fmb_lcb_units_supported(d->n, d->d, d->k, d->n_l);
+    if ((d->d % 16 && !units) || d->n % 8 || d->k % 4) return WK_ERR_UNSUPPORTED;
     for (int t = 0; t <= d->num_linear; ++t)
       if (d->mlp_dims[t] % 8) return WK_ERR_UNSUPPORTED;
-    if (!wk::fmb_lcb_bf16_supported(d->n, d->d, d->k, d->n_l)) return WK_ERR_UNSUPPORTED;
+    if (!units && !wk::fmb_lcb_bf16_supported(d->n, d->d, d->k, d->n_l)) return WK_ERR_UNSUPPORTED;
     if (!wk::resid_ln_bf16_supported(d->d)) return WK_ERR_UNSUPPORTED;
   } else {
     if (!wk::fmb_lcb_f32_supported(d->n, d->d, d->k, d->n_l)) return WK_ERR_UNSUPPORTED;
@@ -70,10 +71,16 @@ int32_t check_desc(const wk_layer_desc* d) {
 }
 
 struct LayerPlan {
-  size_t fn = 0, h[2] = {0, 0}, m = 0, bytes = 0;
+  size_t fn = 0, h[2] = {0, 0}, m = 0, units = 0, bytes = 0;
   int num_hidden_bufs = 0;
   bool fused_out = false;  // last Linear writes the FMB rows of Y itself; no M buffer
+  bool use_units = false;  // d = 8: the FMB+LCB step runs as transpose + batched GEMM + epilogue
 };
+
+// Units of width 8 (bf16) take the batched-GEMM form of the FMB+LCB step.
+bool units_path(const wk_layer_desc& d) {
+  return d.dtype == WK_BF16 && d.d % 16 != 0 && wk::fmb_lcb_units_supported(d.n, d.d, d.k, d.n_l);
+}
 
 // Whether the last Linear carries the residual LayerNorm in its epilogue.
 bool fuse_output_ln(const wk_layer_desc& d) {
@@ -103,6 +110,11 @@ LayerPlan plan_layer(const wk_layer_desc& d, int64_t batch) {
   if (!p.fused_out) {
     p.m = off;
     off += align_up(B * (size_t)d.n_f * d.d * es);
+  }
+  p.use_units = units_path(d);
+  if (p.use_units) {  // transposed X, [Phi; W_L], fp32 [Z; Lc] (dead once Fn and the LCB rows are written)
+    p.units = off;
+    off += align_up(wk::fmb_lcb_units_workspace(batch, d.n, d.k, d.n_l));
   }
   p.bytes = off;
   return p;
@@ -165,8 +177,14 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.fn = reinterpret_cast<uint16_t*>(fn);
     a.y = static_cast<uint16_t*>(y);
     a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = d.n_f; a.n_l = d.n_l; a.eps = d.ln_eps;
-    st = launch(WK_KERNEL_FMB_LCB, layer_idx, 0,
-                [&](int64_t* g) { return wk::launch_fmb_lcb_bf16(a, batch, launch.stream, g); });
+    if (plan.use_units) {
+      void* us = scratch + plan.units;
+      st = launch(WK_KERNEL_FMB_LCB, layer_idx, 0,
+                  [&](int64_t* g) { return wk::launch_fmb_lcb_units(a, batch, us, launch.stream, g); });
+    } else {
+      st = launch(WK_KERNEL_FMB_LCB, layer_idx, 0,
+                  [&](int64_t* g) { return wk::launch_fmb_lcb_bf16(a, batch, launch.stream, g); });
+    }
   } else {
     wk::FmbLcbF32Args a;
     a.x = static_cast<const float*>(x);

@@ -71,6 +71,11 @@ def test_workspace_sizes_follow_layout():
     assert wk.stack_workspace_size([C2], B) == scratch
     assert wk.stack_workspace_size([C2] * 2, B) == scratch + act
     assert wk.stack_workspace_size([C2] * 8, B) == scratch + 2 * act
+    # units of width 8: + transposed X, [Phi; W_L] and the fp32 [Z; Lc] after the M buffer
+    u = wk.LayerSpec(64, 8, 8, 32, 32, (512, 64, 256))
+    B = 9
+    assert wk.layer_workspace_size(u, B) == (al(B * 512 * 2) + al(B * 64 * 2) + al(B * 256 * 2)
+                                             + al(al(B * 64 * 8 * 2) + al(40 * 64 * 2) + al(B * 8 * 40 * 4)))
     f32 = wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128), dtype="f32")
     assert wk.layer_workspace_size(f32, 64) == al(64 * 64 * 4) + al(64 * 64 * 4) + al(64 * 128 * 4)
 
@@ -87,6 +92,12 @@ def test_invalid_and_unsupported_descs():
     assert _size(wk.LayerSpec(128, 150, 32, 64, 64, (4096, 2048, 9600))) == 0       # bf16 needs d % 16
     assert _size(wk.LayerSpec(128, 150, 32, 64, 64, (4096, 2048, 9600), dtype="f32")) == 0  # f32 LDS limit
     assert _size(wk.LayerSpec(16, 24, 4, 8, 8, (64, 30, 192), dtype="f32")) > 0     # f32 takes any width
+    # bf16 units of width 8 (the batched-GEMM form): n % 64, k % 4, k <= 32, (k + n_l) % 8
+    assert _size(wk.LayerSpec(64, 8, 8, 32, 32, (512, 64, 256))) > 0
+    assert _size(wk.LayerSpec(2880, 8, 24, 1440, 1440, (69120, 1024, 11520))) > 0
+    assert _size(wk.LayerSpec(72, 8, 8, 36, 36, (576, 64, 288))) == 0              # n % 64
+    assert _size(wk.LayerSpec(64, 8, 40, 32, 32, (2560, 64, 256))) == 0            # k > 32
+    assert _size(wk.LayerSpec(64, 8, 12, 32, 32, (768, 64, 256))) == 0             # (k + n_l) % 8
 
 
 def _call_forward(spec, batch, x, y, ws, ws_bytes, weights=None, desc=None):

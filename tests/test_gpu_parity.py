@@ -40,7 +40,7 @@ def test_tiny_f32_full_batch():
         check("Y", y, r.oracle(), "f32")
 
 
-@pytest.mark.parametrize("cfg", [ws.TINY_F32, ws.LAYER_D160, ws.SMALLD_N720], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [ws.TINY_F32, ws.LAYER_D160, ws.SMALLD_N720, ws.UNITS_N2880], ids=lambda c: c.name)
 def test_single_layer_intermediates(cfg):
     B = 64 if cfg.dtype == "f32" else 48
     r = Run(cfg, seed=11, affine="random", batch=B)
@@ -100,6 +100,10 @@ RAGGED = [
     _custom("stream_d32_k24", "bf16", 48, 32, 24, 16, (1152, 136, 512), 9),
     _custom("stream_d160_k40", "bf16", 192, 160, 40, 96, (7680, 256, 15360), 5),
     _custom("stream_d160_k36", "bf16", 192, 160, 36, 96, (6912, 256, 15360), 3),
+    # units of width 8: transpose + batched GEMM (fp32 out) + epilogue
+    _custom("units_d8_n64", "bf16", 64, 8, 8, 32, (512, 64, 256), 9),
+    _custom("units_d8_k24", "bf16", 128, 8, 24, 64, (3072, 128, 512), 37),
+    _custom("units_d8_k32_stack2", "bf16", 192, 8, 32, 96, (6144, 136, 768), 6, layers=2),
     _custom("ragged_f32", "f32", 12, 24, 3, 5, (36, 20, 120), 9),
     _custom("ragged_f32_stack", "f32", 12, 24, 3, 5, (36, 20, 120), 4, layers=2),
 ]
@@ -142,7 +146,7 @@ def test_large_magnitudes():
     check("Y (x100)", y, r.oracle(), "bf16")
 
 
-FULL = [(ws.LAYER_D160, 8), (ws.SMALLD_N720, 8), (ws.STACK8_N256, 4), (ws.STACK8_N512, 4)]
+FULL = [(ws.LAYER_D160, 8), (ws.SMALLD_N720, 8), (ws.STACK8_N256, 4), (ws.STACK8_N512, 4), (ws.UNITS_N2880, 8)]
 
 
 @pytest.mark.slow

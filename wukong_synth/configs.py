@@ -15,7 +15,7 @@ This module holds shapes only.  It performs none of the layer's arithmetic.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 from typing import Tuple
 
 
@@ -70,6 +70,7 @@ class WukongConfig:
     x_dist: str = "normal"  # "normal" or "feature_scaled_units"
     unit_width: int = 0  # width of the embedding units a feature row is built from
     description: str = ""
+    units_per_feature: int = 1  # rows of X that belong to one feature (unit-level layers)
 
     @property
     def num_layers(self) -> int:
@@ -86,12 +87,10 @@ class WukongConfig:
         return (s.n * s.d,) + tuple(hidden) + (outputs,)
 
     def with_batch(self, batch: int) -> "WukongConfig":
-        return WukongConfig(self.name, self.dtype, batch, self.layers, self.x_dist,
-                            self.unit_width, self.description)
+        return replace(self, batch=batch)
 
     def with_layers(self, num_layers: int) -> "WukongConfig":
-        return WukongConfig(self.name, self.dtype, self.batch, self.layers[:num_layers],
-                            self.x_dist, self.unit_width, self.description)
+        return replace(self, layers=self.layers[:num_layers])
 
 
 def _stack(shape: LayerShape, l: int) -> Tuple[LayerShape, ...]:
@@ -134,8 +133,20 @@ SMALLD_N720 = WukongConfig(
     description="single layer, bf16, B=8192, n=720, d=32 (4 units of 8), k=24, n_F=n_L=360, MLP 17280-1024-11520",
 )
 
+# Unit-level interaction (section 2.1 of the same page: each 8-wide unit takes
+# part in the interaction as a feature of its own): the n = 720 workload's
+# features split into their 4 units, so n = 2880 rows of width 8.  k, n_F,
+# n_L and the MLP keep the n = 720 layer's proportions (the page gives none).
+UNITS_N2880 = WukongConfig(
+    "units_n2880", "bf16", 8192,
+    _stack(LayerShape(2880, 8, 24, 1440, 1440, (69120, 1024, 11520)), 1),
+    x_dist="feature_scaled_unit_rows", unit_width=8, units_per_feature=4,
+    description="unit-level single layer, bf16, B=8192, n=2880 units of d=8 (4 per feature), k=24, "
+                "n_F=n_L=1440, MLP 69120-1024-11520",
+)
+
 CONFIGS = (TINY_F32, LAYER_D160, STACK8_N256, STACK8_N512, SMALLD_N720)
-BY_NAME = {c.name: c for c in CONFIGS}
+BY_NAME = {c.name: c for c in CONFIGS + (UNITS_N2880,)}
 
 
 def get(name_or_index) -> WukongConfig:

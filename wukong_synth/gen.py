@@ -230,9 +230,9 @@ def make_head_weights(cfg_name: str, dims, dtype: str, seed: int, affine: str = 
     return w, b
 
 
-def feature_scales(cfg: WukongConfig, seed: int) -> np.ndarray:
-    """Per-feature scale s_i = 10**U(-1,1), shared by all examples (float32 [n])."""
-    n = cfg.layers[0].n
+def feature_scales(cfg: WukongConfig, seed: int, count: Optional[int] = None) -> np.ndarray:
+    """Per-feature scale s_i = 10**U(-1,1), shared by all examples (float32 [count], default n)."""
+    n = cfg.layers[0].n if count is None else count
     u = _fill(seed, f"{cfg.name}/x_feature_scale", n, "uniform")
     return np.power(np.float32(10.0), u * np.float32(2.0) - np.float32(1.0)).astype(np.float32)
 
@@ -277,6 +277,12 @@ def make_input(cfg: WukongConfig, seed: int, batch: Optional[int] = None,
         # each row is unit_width-wide units side by side; one scale per feature row
         assert cfg.unit_width > 0 and d % cfg.unit_width == 0
         x *= feature_scales(cfg, seed)[None, :, None]
+    elif cfg.x_dist == "feature_scaled_unit_rows":
+        # each row is one unit; units_per_feature consecutive rows share their feature's scale
+        upf = cfg.units_per_feature
+        assert d == cfg.unit_width and n % upf == 0
+        s = feature_scales(cfg, seed, n // upf)
+        x *= np.repeat(s, upf)[None, :, None]
     elif cfg.x_dist != "normal":
         raise ValueError(cfg.x_dist)
     return _store(x, cfg.dtype)
