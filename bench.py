@@ -47,7 +47,7 @@ METRIC = "Wukong stack fwd examples/sec; achieved TFLOP/s as % of bf16 MFMA peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 # sources whose SHA-256 (over their concatenation) a traffic record in profiles/ must match
 KERNEL_SOURCES = {
-    "fmb_lcb": ("fmb_lcb.hip", "fmb_lcb_stream.hip"),
+    "fmb_lcb": ("fmb_lcb.hip", "fmb_lcb_stream.hip", "fmb_lcb_units.hip", "linear_bf16.hip"),
     "mlp_linear": ("linear_bf16.hip",),
     "residual_ln": ("resid_ln.hip",),
     "head_linear": ("linear_bf16.hip",),
@@ -253,6 +253,7 @@ def main():
     ap.add_argument("--no-trace", action="store_true", help="skip the per-kernel event pass")
     ap.add_argument("--no-head", action="store_true", help="skip the prediction-head measurement")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache (512 MB flush) step timing")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -310,6 +311,30 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = cfg.batch * args.steps / elapsed
     print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # the same step captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed:
+    # identical kernels and buffers, without per-call host work and launch gaps
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                wk.stack_forward(x, layers, y=y, workspace=ws_t)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            wk.stack_forward(x, layers, y=y, workspace=ws_t)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
+        del graph
+        print(f"# graph replay: {graph_ms:.3f} ms/step", file=sys.stderr, flush=True)
 
     # per-kernel pass: the library records HIP events around every launch on the launch stream
     kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step (at most)
@@ -405,6 +430,7 @@ def main():
         "roofline": roofline,
         "step_roofline_frac": round(ideal_ms / ms_per_step, 4),
         "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 4),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
         "copy_gbps_measured": round(copy_gbps, 1),
         "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
         "head": head,

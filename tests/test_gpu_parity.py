@@ -126,6 +126,37 @@ def test_determinism_and_batch_invariance():
     assert np.array_equal(to_host(sub), y1[5:21]), "a subset's rows differ from the full batch's"
 
 
+@pytest.mark.parametrize("cfg,batch", [(ws.LAYER_D160, 64), (ws.STACK8_N256.with_layers(2), 6),
+                                       (_custom("units_graph", "bf16", 128, 8, 24, 64, (3072, 128, 512), 11), 11)],
+                         ids=["layer_d160", "stack2_n256", "units_d8"])
+def test_graph_replay_matches_eager(cfg, batch):
+    """A stack captured into a HIP graph and replayed several times, with other
+    eager work between the replays, gives the eager result bit for bit."""
+    r = Run(cfg, seed=12, affine="random", batch=batch)
+    specs = [l.spec for l in r.layers]
+    wst = wk.alloc_workspace(wk.stack_workspace_size(specs, batch))
+    y_eager = to_host(wk.stack_forward(r.xd, r.layers, workspace=wst))
+    torch.cuda.synchronize()
+    yg = torch.empty_like(r.xd)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        wk.stack_forward(r.xd, r.layers, y=yg, workspace=wst)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wk.stack_forward(r.xd, r.layers, y=yg, workspace=wst)
+    other = torch.empty_like(r.xd)
+    for i in range(3):
+        yg.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(yg), y_eager), f"replay {i} differs from the eager result"
+        wk.stack_forward(r.xd, r.layers, y=other, workspace=wst)  # eager work between replays
+        torch.cuda.synchronize()
+    log(f"  {cfg.name}: 3 graph replays equal the eager output")
+
+
 def test_empty_and_single_example():
     r = Run(ws.LAYER_D160, seed=4, affine="random", batch=1)
     y = host_f64(to_host(r.forward()))
