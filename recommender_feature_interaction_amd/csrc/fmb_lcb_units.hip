@@ -14,14 +14,14 @@
 //      K = n contiguous);
 //   2. the bf16 DMA GEMM with fp32 output: C[(b, e)][r] = sum_j Xt[(b, e)][j]
 //      [Phi; W_L][r][j], i.e. C[b][e][r] = [Z_b; Lc_b][r][e];
-//   3. units_epilogue_kernel, a group of examples per workgroup: the LCB rows
-//      (Lc in fp32 + residual, LayerNorm over the 8 values, bf16 out); Z_b
-//      rounded to bf16 (the MFMA operand precision of the other kernels) as a
-//      register operand; F_b^T = Z_b X_b^T on the MFMA 32 rows at a time, the
+//   3. units_epilogue_kernel, a group of examples per workgroup: Z_b rounded
+//      to bf16 (the MFMA operand precision of the other kernels) as a register
+//      operand; F_b^T = Z_b X_b^T on the MFMA 32 rows at a time, the
 //      statistics merged by Chan's parallel-variance formula (count, mean, sum
-//      of squared deviations) and reduced over the workgroup, then a second
-//      pass that recomputes each block and writes Fn with the FMB LayerNorm's
-//      gamma / beta.
+//      of squared deviations) and reduced over the workgroup, with the LCB
+//      rows of Y finished from the same X rows (Lc in fp32 + residual,
+//      LayerNorm over the 8 values); then a second pass that recomputes each
+//      block and writes Fn with the FMB LayerNorm's gamma / beta.
 #include "wk_device.h"
 #include "wk_kernels.h"
 
@@ -104,11 +104,33 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
   for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
     const int64_t b0 = g * UE;
     const int ne = (int)(batch - b0 < UE ? batch - b0 : UE);
-    // LCB rows of Y: Lc (fp32) + residual, LayerNorm over the 8 values
-    for (int q = tid; q < ne * n_l; q += UT) {
-      const int ex = q / n_l, i = q - ex * n_l;
+    // Z operands: lane l < 32 holds Z[l][0..7] rounded to bf16 (zero for l >= k)
+    u32x4 zop[UE];
+#pragma unroll
+    for (int ex = 0; ex < UE; ++ex) {
+      zop[ex] = u32x4{0u, 0u, 0u, 0u};
+      if (ex < ne && h == 0 && l32 < k) {
+        const float* cz = p.c + (b0 + ex) * UD * (int64_t)N + l32;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) zop[ex][t] = pack_bf16x2(cz[(2 * t) * N], cz[(2 * t + 1) * N]);
+      }
+    }
+    auto x_row = [&](int ex, int m) {  // lanes 0..31: X row m; lanes 32..63: zero (the padding)
+      u32x4 xop = u32x4{0u, 0u, 0u, 0u};
+      if (h == 0 && m < n) xop = *reinterpret_cast<const u32x4*>(p.x + ((b0 + ex) * n + m) * UD);
+      return xop;
+    };
+    auto f_block = [&](int ex, const u32x4& xop) {  // this lane's 16 values of rows m .. m + 31 of F^T
+      f32x16 zero;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+      return mfma32x32x16(zop[ex], xop, zero);
+    };
+    // an LCB row of Y from the X row already in registers: Lc (fp32) + residual,
+    // LayerNorm over the 8 values
+    auto lcb_row = [&](int ex, int m, const u32x4& xr) {
       const int64_t b = b0 + ex;
-      const u32x4 xr = *reinterpret_cast<const u32x4*>(p.x + (b * n + n_f + i) * UD);
+      const int i = m - n_f;
       float v[UD];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -131,39 +153,30 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
       for (int t = 0; t < 4; ++t)
         o[t] = pack_bf16x2((v[2 * t] - mean) * rstd * og[2 * t] + ob[2 * t],
                            (v[2 * t + 1] - mean) * rstd * og[2 * t + 1] + ob[2 * t + 1]);
-      *reinterpret_cast<u32x4*>(p.y + (b * n + n_f + i) * UD) = o;
-    }
-
-    // Z operands: lane l < 32 holds Z[l][0..7] rounded to bf16 (zero for l >= k)
-    u32x4 zop[UE];
-#pragma unroll
-    for (int ex = 0; ex < UE; ++ex) {
-      zop[ex] = u32x4{0u, 0u, 0u, 0u};
-      if (ex < ne && h == 0 && l32 < k) {
-        const float* cz = p.c + (b0 + ex) * UD * (int64_t)N + l32;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) zop[ex][t] = pack_bf16x2(cz[(2 * t) * N], cz[(2 * t + 1) * N]);
-      }
-    }
-    auto f_block = [&](int ex, int m) {  // this lane's 16 values of rows m .. m + 31 of F^T
-      u32x4 xop = u32x4{0u, 0u, 0u, 0u};
-      if (h == 0 && m < n) xop = *reinterpret_cast<const u32x4*>(p.x + ((b0 + ex) * n + m) * UD);
-      f32x16 zero;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) zero[r] = 0.f;
-      return mfma32x32x16(zop[ex], xop, zero);
+      *reinterpret_cast<u32x4*>(p.y + (b * n + m) * UD) = o;
     };
     // pass 1: statistics (count, mean, M2) per example
     float cnt[UE], mu[UE], m2[UE];
 #pragma unroll
     for (int ex = 0; ex < UE; ++ex) cnt[ex] = mu[ex] = m2[ex] = 0.f;
-#pragma unroll 2
+    // The next block's loads are issued before this block's stores: the
+    // vector-memory counter retires in order, so a load issued after a store
+    // would also wait for the store to complete.
+    u32x4 xc[UE], xn[UE];
+    auto load_x = [&](int m, u32x4 (&xs)[UE]) {
+#pragma unroll
+      for (int ex = 0; ex < UE; ++ex) xs[ex] = ex < ne ? x_row(ex, m) : u32x4{0u, 0u, 0u, 0u};
+    };
+    if (wave * 32 < n) load_x(wave * 32 + l32, xc);
     for (int m0 = wave * 32; m0 < n; m0 += UT / 2) {
       const int m = m0 + l32;
+      if (m0 + UT / 2 < n) load_x(m0 + UT / 2 + l32, xn);
 #pragma unroll
       for (int ex = 0; ex < UE; ++ex) {
         if (ex >= ne) break;
-        const f32x16 d = f_block(ex, m);
+        const u32x4 xop = xc[ex];
+        const f32x16 d = f_block(ex, xop);
+        if (h == 0 && m >= n_f && m < n) lcb_row(ex, m, xop);
         float s = 0.f, c = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -180,6 +193,8 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
         }
         chan_merge(cnt[ex], mu[ex], m2[ex], c, lm, q);
       }
+#pragma unroll
+      for (int ex = 0; ex < UE; ++ex) xc[ex] = xn[ex];
     }
 #pragma unroll
     for (int ex = 0; ex < UE; ++ex) {
@@ -203,10 +218,9 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
     }
     __syncthreads();
     // pass 2: recompute each block, FMB LayerNorm with gamma / beta, Fn in bf16
-#pragma unroll 2
-    for (int m0 = wave * 32; m0 < n; m0 += UT / 2) {
-      const int m = m0 + l32;
-      u32x2 gv[4], bv[4];
+    // (the next block's X rows and gamma / beta requested before this block's stores)
+    u32x2 gc[4], bc[4], gn[4], bn[4];
+    auto load_gb = [&](int m, u32x2 (&gv)[4], u32x2 (&bv)[4]) {
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int j0 = 8 * c + 4 * h;
@@ -215,10 +229,21 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
         gv[c] = ok && p.fm_gamma ? *reinterpret_cast<const u32x2*>(p.fm_gamma + off) : u32x2{0x3f803f80u, 0x3f803f80u};
         bv[c] = ok && p.fm_beta ? *reinterpret_cast<const u32x2*>(p.fm_beta + off) : u32x2{0u, 0u};
       }
+    };
+    if (wave * 32 < n) {
+      load_x(wave * 32 + l32, xc);
+      load_gb(wave * 32 + l32, gc, bc);
+    }
+    for (int m0 = wave * 32; m0 < n; m0 += UT / 2) {
+      const int m = m0 + l32;
+      if (m0 + UT / 2 < n) {
+        load_x(m0 + UT / 2 + l32, xn);
+        load_gb(m0 + UT / 2 + l32, gn, bn);
+      }
 #pragma unroll
       for (int ex = 0; ex < UE; ++ex) {
         if (ex >= ne) break;
-        const f32x16 d = f_block(ex, m);
+        const f32x16 d = f_block(ex, xc[ex]);
         const float mean = stat[ex][0], rstd = stat[ex][1];
         uint16_t* out = p.fn + (b0 + ex) * (int64_t)n * k + (int64_t)m * k;
 #pragma unroll
@@ -226,13 +251,20 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
           const int j0 = 8 * c + 4 * h;
           if (m < n && j0 < k) {
             u32x2 o;
-            o[0] = pack_bf16x2((d[4 * c] - mean) * rstd * bf16lo(gv[c][0]) + bf16lo(bv[c][0]),
-                               (d[4 * c + 1] - mean) * rstd * bf16hi(gv[c][0]) + bf16hi(bv[c][0]));
-            o[1] = pack_bf16x2((d[4 * c + 2] - mean) * rstd * bf16lo(gv[c][1]) + bf16lo(bv[c][1]),
-                               (d[4 * c + 3] - mean) * rstd * bf16hi(gv[c][1]) + bf16hi(bv[c][1]));
+            o[0] = pack_bf16x2((d[4 * c] - mean) * rstd * bf16lo(gc[c][0]) + bf16lo(bc[c][0]),
+                               (d[4 * c + 1] - mean) * rstd * bf16hi(gc[c][0]) + bf16hi(bc[c][0]));
+            o[1] = pack_bf16x2((d[4 * c + 2] - mean) * rstd * bf16lo(gc[c][1]) + bf16lo(bc[c][1]),
+                               (d[4 * c + 3] - mean) * rstd * bf16hi(gc[c][1]) + bf16hi(bc[c][1]));
             *reinterpret_cast<u32x2*>(out + j0) = o;
           }
         }
+      }
+#pragma unroll
+      for (int ex = 0; ex < UE; ++ex) xc[ex] = xn[ex];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        gc[c] = gn[c];
+        bc[c] = bn[c];
       }
     }
     __syncthreads();  // wred and stat are reused by the next group
