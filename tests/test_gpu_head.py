@@ -88,6 +88,15 @@ def test_bf16_head(dims, batch):
     log(f"  logits span [{z.min():.2f}, {z.max():.2f}] (probabilities not saturated)")
 
 
+def test_head_without_biases():
+    """NULL biases mean zero bias (both the GEMM and the output kernel)."""
+    r = HeadRun((4096, 72, 1), 37, "bf16", seed=5)
+    head = wk.DeviceHead(wk.HeadSpec(r.dims, "bf16"), r.w)
+    p = host_f64(to_host(wk.head_forward(r.yd, head)))
+    torch.cuda.synchronize()
+    check("prob (no biases)", p, oracle.prediction_head(r.y, r.w, None, storage=("h",)), "bf16")
+
+
 def test_head_after_layer_end_to_end():
     """X -> Wukong layer -> head on the GPU against the oracle's layer and head."""
     cfg = ws.LAYER_D160

@@ -13,7 +13,7 @@ import torch
 import oracle
 import recommender_feature_interaction_amd as wk
 import wukong_synth as ws
-from _gpu_helpers import BF16_STORAGE, Run, check, host_f64, log, sample_indices, spec_of, to_host
+from _gpu_helpers import BF16_STORAGE, Run, check, host_f64, log, sample_indices, spec_of, storage_for, to_host
 from _metrics import rel_err
 
 pytestmark = pytest.mark.gpu
@@ -155,6 +155,29 @@ def test_graph_replay_matches_eager(cfg, batch):
         wk.stack_forward(r.xd, r.layers, y=other, workspace=wst)  # eager work between replays
         torch.cuda.synchronize()
     log(f"  {cfg.name}: 3 graph replays equal the eager output")
+
+
+NULL_AFFINE = [ws.TINY_F32, ws.LAYER_D160, ws.SMALLD_N720,
+               _custom("null_stream_d160", "bf16", 192, 160, 40, 96, (7680, 256, 15360), 3),
+               _custom("null_units_d8", "bf16", 128, 8, 24, 64, (3072, 128, 512), 5),
+               _custom("null_chunked_d48", "bf16", 96, 48, 20, 40, (1920, 264, 1920), 3)]
+
+
+@pytest.mark.parametrize("cfg", NULL_AFFINE, ids=lambda c: c.name)
+def test_null_optional_parameters(cfg):
+    """NULL LayerNorm gamma / beta and MLP biases mean identity / zero (include/wukong.h)."""
+    import dataclasses
+    B = min(cfg.batch, 8)
+    c = cfg.with_batch(B)
+    host = ws.make_stack_weights(c, 31, "random")
+    bare = [dataclasses.replace(h, fm_gamma=None, fm_beta=None, out_gamma=None, out_beta=None,
+                                mlp_b=[None] * len(h.mlp_w)) for h in host]
+    layers = [wk.DeviceLayer(spec_of(c.layers[i], c.dtype), h.phi, h.w_l, h.mlp_w) for i, h in enumerate(host)]
+    x = ws.make_input(c, 31)
+    y = wk.stack_forward(wk.to_device(x, c.dtype, "cuda"), layers)
+    torch.cuda.synchronize()
+    ref = oracle.wukong_stack(x, bare, storage=storage_for(c))
+    check("Y (no gamma / beta / biases)", host_f64(to_host(y)), ref, c.dtype)
 
 
 def test_empty_and_single_example():
