@@ -1,4 +1,5 @@
-"""CPU oracle of the Wukong interaction stack -- TEST INFRASTRUCTURE ONLY.
+"""CPU oracle of the Wukong interaction stack and of WHALE's fusion step --
+TEST INFRASTRUCTURE ONLY.
 
 Imported only by the tests, the package's smoke check and the benchmark's
 CPU-baseline leg.  It shares no code with the HIP library.
@@ -6,3 +7,5 @@ CPU-baseline leg.  It shares no code with the HIP library.
 from .wukong_oracle import (LN_EPS, STORAGE_NAMES, brute_force_head, brute_force_layer,  # noqa: F401
                             decode_bf16, fm_interaction, fmb_mlp, layer_norm, lcb, prediction_head,
                             round_bf16, sigmoid, to_f64, wukong_layer, wukong_stack)
+from .whale_oracle import (FUSION_STORAGE, brute_force_attention, cross_attention, silu,  # noqa: F401
+                           whale_fusion)
