@@ -161,7 +161,10 @@ enum {
   WK_KERNEL_MLP_LINEAR = 2, /* one FMB-MLP Linear (+bias, +ReLU)             */
   WK_KERNEL_RESIDUAL_LN = 3, /* FMB rows of Y: LN(M + X)                     */
   WK_KERNEL_HEAD_LINEAR = 4,  /* one hidden Linear of the prediction head     */
-  WK_KERNEL_HEAD_OUT = 5      /* the head's last Linear + logistic function   */
+  WK_KERNEL_HEAD_OUT = 5,     /* the head's last Linear + logistic function   */
+  WK_KERNEL_FUSION_ATTN = 6,  /* WHALE fusion: shared K = V cross-attention    */
+  WK_KERNEL_FUSION_LINEAR = 7, /* fusion Linear (index 0), SwiGLU up (1), down (2) */
+  WK_KERNEL_FUSION_LN = 8     /* fusion: the pre-norm LayerNorm               */
 };
 typedef struct wk_trace wk_trace;
 /* Creates a trace able to hold `capacity` launch records (creates HIP events
@@ -221,6 +224,57 @@ int32_t wukong_head_forward(const wk_head_desc* desc, const wk_head_weights* wei
 int32_t wukong_head_forward_traced(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch,
                                    const void* y, float* prob, void* workspace, size_t workspace_bytes,
                                    void* stream, wk_trace* trace);
+
+/* ---- WHALE fusion step ----------------------------------------------------
+ * WHALE technical summaries, section 2.1 (attention-based fusion module) and
+ * section 2.2 (shared key-value, shared-gate SwiGLU): the Wukong output H_w
+ * is the query, the sequence branch's output H_s is both the keys and the
+ * values (K = V), the attention output is concatenated with H_w, projected by
+ * the Fusion MLP, and passed through a pre-norm SwiGLU FFN whose gate and up
+ * projections are one matrix.  Per example (rows of H_w are query tokens):
+ *   A   = softmax(H_w H_s^T / sqrt(d)) H_s               [n, d]
+ *   Q   = [H_w, A] W_f^T + b_f                            [n, d]
+ *   U   = LN_d(Q; gamma, beta) W_up^T + b_up              [n, d_ff]
+ *   H_f = Q + (silu(U) * U) W_down^T + b_down             [n, d]
+ * Readings: no separate Q/K/V projections, one head; the Fusion MLP is one
+ * Linear 2d -> d.  bf16 only: A, Q, LN(Q), silu(U)*U and H_f are stored in bf16,
+ * the softmax weights enter P V as bf16 (their sum stays fp32), fp32
+ * accumulation throughout. */
+typedef struct {
+  int32_t n;            /* query tokens per example (rows of H_w), n % 16 == 0  */
+  int32_t d;            /* width of H_w, H_s, H_f: 32, 64, 96, 128 or 160      */
+  int32_t L;            /* positions of H_s per example, L >= 1                 */
+  int32_t d_ff;         /* SwiGLU hidden width, d_ff % 8 == 0                   */
+  float ln_eps;         /* pre-norm LayerNorm epsilon (biased variance)         */
+  int32_t dtype;        /* WK_BF16                                              */
+} wk_fusion_desc;
+
+typedef struct {        /* device pointers, row-major, [out, in] weights          */
+  const void* w_f;      /* [d, 2d]                                              */
+  const void* b_f;      /* [d] or NULL                                          */
+  const void* ln_gamma; /* [d] or NULL (= 1)                                    */
+  const void* ln_beta;  /* [d] or NULL (= 0)                                    */
+  const void* w_up;     /* [d_ff, d]: gate and up projection                    */
+  const void* b_up;     /* [d_ff] or NULL                                       */
+  const void* w_down;   /* [d, d_ff]                                            */
+  const void* b_down;   /* [d] or NULL                                          */
+} wk_fusion_weights;
+
+/* Workspace bytes for wukong_fusion_forward ([H_w, A], Q, LN(Q), silu(U) * U),
+ * 0 for an invalid or unsupported desc. */
+size_t wukong_fusion_workspace_size(const wk_fusion_desc* desc, int64_t batch);
+
+/* hf [batch, n, d] (device) from hw [batch, n, d] and hs [batch, L, d]
+ * (device).  Same conventions as wukong_layer_forward: 16-byte aligned device
+ * pointers, arguments checked before any launch, asynchronous on `stream`, no
+ * allocation; hw, hs, hf and the workspace must not overlap. */
+int32_t wukong_fusion_forward(const wk_fusion_desc* desc, const wk_fusion_weights* weights, int64_t batch,
+                              const void* hw, const void* hs, void* hf, void* workspace, size_t workspace_bytes,
+                              void* stream);
+/* As wukong_fusion_forward, recording one event pair per launch into `trace`. */
+int32_t wukong_fusion_forward_traced(const wk_fusion_desc* desc, const wk_fusion_weights* weights, int64_t batch,
+                                     const void* hw, const void* hs, void* hf, void* workspace,
+                                     size_t workspace_bytes, void* stream, wk_trace* trace);
 
 #ifdef __cplusplus
 }

@@ -5,10 +5,12 @@ the Zhihu article): a Factorization Machine Block and a Linear Compress Block
 run side by side on each example's n x d embedding matrix, their outputs are
 concatenated, the residual is added and a LayerNorm is applied; layers are
 stacked; a prediction head (top MLP + logistic function) can follow the
-stack.  The compute runs in hand-written HIP kernels for gfx950 behind the C
+stack, and WHALE's fusion step (shared K = V cross-attention, Fusion MLP,
+pre-norm shared-gate SwiGLU) combines a layer's output with a sequence.  The compute runs in hand-written HIP kernels for gfx950 behind the C
 ABI in include/wukong.h; this package is the Python binding.
 """
-from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceHead, DeviceLayer, HeadSpec,  # noqa: F401
-                   LayerSpec, Trace, WukongError, alloc_workspace, head_forward, head_workspace_size,
+from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceFusion, DeviceHead, DeviceLayer,  # noqa: F401
+                   FusionSpec, HeadSpec, LayerSpec, Trace, WukongError, alloc_workspace, fusion_forward,
+                   fusion_workspace_size, head_forward, head_workspace_size,
                    layer_forward, layer_workspace_size, library_path, load_library, stack_forward,
                    stack_workspace_size, status_string, to_device, workspace_layout, EXPORTED_SYMBOLS)

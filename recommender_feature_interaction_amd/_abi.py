@@ -20,8 +20,11 @@ _lib = None
 F32, BF16 = 0, 1
 WK_OK, WK_ERR_INVALID_ARG, WK_ERR_UNSUPPORTED, WK_ERR_WORKSPACE, WK_ERR_HIP = 0, 1, 2, 3, 4
 KERNEL_FMB_LCB, KERNEL_MLP_LINEAR, KERNEL_RESIDUAL_LN, KERNEL_HEAD_LINEAR, KERNEL_HEAD_OUT = 1, 2, 3, 4, 5
+KERNEL_FUSION_ATTN, KERNEL_FUSION_LINEAR, KERNEL_FUSION_LN = 6, 7, 8
 KERNEL_NAMES = {KERNEL_FMB_LCB: "fmb_lcb", KERNEL_MLP_LINEAR: "mlp_linear", KERNEL_RESIDUAL_LN: "residual_ln",
-                KERNEL_HEAD_LINEAR: "head_linear", KERNEL_HEAD_OUT: "head_out"}
+                KERNEL_HEAD_LINEAR: "head_linear", KERNEL_HEAD_OUT: "head_out",
+                KERNEL_FUSION_ATTN: "fusion_attention", KERNEL_FUSION_LINEAR: "fusion_linear",
+                KERNEL_FUSION_LN: "fusion_ln"}
 ABI_VERSION = 1
 
 
@@ -45,6 +48,16 @@ class wk_head_desc(ctypes.Structure):
 
 class wk_head_weights(ctypes.Structure):
     _fields_ = [("w", ctypes.POINTER(ctypes.c_void_p)), ("b", ctypes.POINTER(ctypes.c_void_p))]
+
+
+class wk_fusion_desc(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("d", ctypes.c_int32), ("L", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("ln_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class wk_fusion_weights(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("w_f", "b_f", "ln_gamma", "ln_beta", "w_up", "b_up", "w_down", "b_down")]
 
 
 class wk_workspace_layout(ctypes.Structure):
@@ -76,6 +89,13 @@ _SIGNATURES = [
       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_float)]),
     ("wukong_stack_forward_traced", ctypes.c_int32,
      [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_fusion_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_fusion_desc), ctypes.c_int64]),
+    ("wukong_fusion_forward", ctypes.c_int32,
+     [ctypes.POINTER(wk_fusion_desc), ctypes.POINTER(wk_fusion_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_fusion_forward_traced", ctypes.c_int32,
+     [ctypes.POINTER(wk_fusion_desc), ctypes.POINTER(wk_fusion_weights), ctypes.c_int64, ctypes.c_void_p,
       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     ("wukong_head_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_head_desc), ctypes.c_int64]),
     ("wukong_head_forward", ctypes.c_int32,
@@ -413,3 +433,73 @@ def head_forward(y: torch.Tensor, head: DeviceHead, prob: Optional[torch.Tensor]
         st = lib.wukong_head_forward_traced(*args, trace.handle)
     _check(st, "wukong_head_forward")
     return prob
+
+
+# ------------------------------------------------------------------ WHALE fusion step
+@dataclass(frozen=True)
+class FusionSpec:
+    """WHALE's fusion step: n query tokens (rows of H_w) of width d, L sequence positions, SwiGLU width d_ff."""
+    n: int
+    d: int
+    L: int
+    d_ff: int
+    ln_eps: float = 1e-5
+    dtype: str = "bf16"
+
+    def make_desc(self) -> wk_fusion_desc:
+        return wk_fusion_desc(self.n, self.d, self.L, self.d_ff, self.ln_eps, BF16 if self.dtype == "bf16" else F32)
+
+
+class DeviceFusion:
+    """The fusion step's weights resident in device memory (None = absent bias / identity LN affine)."""
+
+    def __init__(self, spec: FusionSpec, w_f, w_up, w_down, b_f=None, ln_gamma=None, ln_beta=None, b_up=None,
+                 b_down=None, device="cuda"):
+        cv = lambda a: None if a is None else to_device(a, spec.dtype, device)  # noqa: E731
+        self.spec = spec
+        self.w_f, self.w_up, self.w_down = cv(w_f), cv(w_up), cv(w_down)
+        self.b_f, self.ln_gamma, self.ln_beta, self.b_up, self.b_down = (cv(b_f), cv(ln_gamma), cv(ln_beta),
+                                                                          cv(b_up), cv(b_down))
+        d, dff = spec.d, spec.d_ff
+        for name, t, shape in (("w_f", self.w_f, (d, 2 * d)), ("w_up", self.w_up, (dff, d)),
+                               ("w_down", self.w_down, (d, dff)), ("b_f", self.b_f, (d,)),
+                               ("ln_gamma", self.ln_gamma, (d,)), ("ln_beta", self.ln_beta, (d,)),
+                               ("b_up", self.b_up, (dff,)), ("b_down", self.b_down, (d,))):
+            if t is not None and tuple(t.shape) != shape:
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
+        self.desc = spec.make_desc()
+        self.weights = wk_fusion_weights(*[_ptr(t) for t in (self.w_f, self.b_f, self.ln_gamma, self.ln_beta,
+                                                              self.w_up, self.b_up, self.w_down, self.b_down)])
+
+
+def fusion_workspace_size(spec: FusionSpec, batch: int) -> int:
+    desc = spec.make_desc()
+    return int(load_library().wukong_fusion_workspace_size(ctypes.byref(desc), batch))
+
+
+def fusion_forward(hw: torch.Tensor, hs: torch.Tensor, fusion: DeviceFusion, hf: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None,
+                   trace: Optional[Trace] = None) -> torch.Tensor:
+    """H_f [batch, n, d] from the Wukong output hw [batch, n, d] and the sequence output hs [batch, L, d]."""
+    lib = load_library()
+    spec = fusion.spec
+    for name, t, per in (("hw", hw, spec.n * spec.d), ("hs", hs, spec.L * spec.d)):
+        if not t.is_cuda or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be a bf16 CUDA tensor")
+        if not t.is_contiguous() or t.numel() != t.shape[0] * per:
+            raise ValueError(f"{name} must be contiguous with {per} elements per example")
+    B = hw.shape[0]
+    if hs.shape[0] != B:
+        raise ValueError("hw and hs need the same batch")
+    hf = torch.empty((B, spec.n, spec.d), dtype=torch.bfloat16, device=hw.device) if hf is None else hf
+    if workspace is None:
+        workspace = alloc_workspace(fusion_workspace_size(spec, B), hw.device)
+    args = (ctypes.byref(fusion.desc), ctypes.byref(fusion.weights), B, hw.data_ptr(), hs.data_ptr(),
+            hf.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(stream))
+    if trace is None:
+        st = lib.wukong_fusion_forward(*args)
+    else:
+        st = lib.wukong_fusion_forward_traced(*args, trace.handle)
+    _check(st, "wukong_fusion_forward")
+    return hf

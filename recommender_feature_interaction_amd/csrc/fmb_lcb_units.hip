@@ -311,7 +311,7 @@ hipError_t launch_fmb_lcb_units(const FmbLcbArgs& a, int64_t batch, void* scratc
   g.M = batch * UD;
   g.N = N;
   g.K = a.n;
-  g.relu = 0;
+  g.act = kActNone;
   int64_t gw = 0;
   e = launch_linear_bf16_f32out(g, c, stream, &gw);
   if (e != hipSuccess) return e;

@@ -160,7 +160,7 @@ hipError_t launch_linear_f32(const LinearArgs& a, hipStream_t stream, int64_t* w
   if (gy == 0 || gx == 0) return hipSuccess;
   hipLaunchKernelGGL(linear_f32_kernel, dim3(gx, (unsigned)gy), dim3(256), 0, stream,
                      static_cast<const float*>(a.a), static_cast<const float*>(a.w),
-                     static_cast<const float*>(a.bias), static_cast<float*>(a.c), a.M, a.N, a.K, a.relu);
+                     static_cast<const float*>(a.bias), static_cast<float*>(a.c), a.M, a.N, a.K, a.act == kActRelu ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -44,9 +44,20 @@ struct LinearKArgs {
   uint16_t* c;
   int64_t M;
   int N, K;
-  int relu;
+  int act;                // LinearAct
+  const uint16_t* res;    // [M, N] added after the activation, or null
   int tiles_m, tiles_n;
 };
+
+__device__ __forceinline__ float apply_act(float v, int act) {
+  if (act == kActRelu) return fmaxf(v, 0.f);
+  if (act == kActSiluGate) {  // v * silu(v) = v^2 * logistic(v), overflow-free
+    const float e = expf(-fabsf(v));
+    const float sig = v >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
+    return v * v * sig;
+  }
+  return v;
+}
 
 struct LinearLnKArgs {
   const uint16_t* a;
@@ -254,9 +265,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
       if (m < M && n < N) {
         float v[4];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          v[t] = acc[i][j][t] + bb[t];
-          if (p.relu) v[t] = fmaxf(v[t], 0.f);
+        for (int t = 0; t < 4; ++t) v[t] = apply_act(acc[i][j][t] + bb[t], p.act);
+        if (p.res != nullptr) {
+          const u32x2 r2 = *reinterpret_cast<const u32x2*>(p.res + m * N + n);
+          v[0] += bf16lo(r2[0]); v[1] += bf16hi(r2[0]); v[2] += bf16lo(r2[1]); v[3] += bf16hi(r2[1]);
         }
         u32x2 o;
         o[0] = pack_bf16x2(v[0], v[1]);
@@ -313,9 +325,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_splitk_kernel(LinearKAr
   }
 }
 
-// C = bf16(act(sum_s part[s] + bias)), 8 consecutive columns per thread (N % 8 == 0).
+// C = bf16(act(sum_s part[s] + bias) + res), 8 consecutive columns per thread (N % 8 == 0).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int splits, int64_t M, int N,
-                                                            const uint16_t* bias, int relu, uint16_t* c) {
+                                                            const uint16_t* bias, int act, const uint16_t* res,
+                                                            uint16_t* c) {
   const int64_t total = M * N / 8;
   const int64_t plane = M * N;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total;
@@ -337,13 +350,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
         v[2 * t + 1] += bf16hi(b[t]);
       }
     }
+    u32x4 rr = u32x4{0u, 0u, 0u, 0u};
+    if (res != nullptr) rr = *reinterpret_cast<const u32x4*>(res + e);
     u32x4 o;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      float x0 = v[2 * t], x1 = v[2 * t + 1];
-      if (relu) {
-        x0 = fmaxf(x0, 0.f);
-        x1 = fmaxf(x1, 0.f);
+      float x0 = apply_act(v[2 * t], act), x1 = apply_act(v[2 * t + 1], act);
+      if (res != nullptr) {
+        x0 += bf16lo(rr[t]);
+        x1 += bf16hi(rr[t]);
       }
       o[t] = pack_bf16x2(x0, x1);
     }
@@ -612,9 +627,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_bf16_kernel(LinearKArgs
         if (m < M && n < N) {
           float v[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            v[t] = acc[i][j][q * 4 + t] + bb[t];
-            if (p.relu) v[t] = fmaxf(v[t], 0.f);
+          for (int t = 0; t < 4; ++t) v[t] = apply_act(acc[i][j][q * 4 + t] + bb[t], p.act);
+          if (p.res != nullptr) {
+            const u32x2 r2 = *reinterpret_cast<const u32x2*>(p.res + m * N + n);
+            v[0] += bf16lo(r2[0]); v[1] += bf16hi(r2[0]); v[2] += bf16lo(r2[1]); v[3] += bf16hi(r2[1]);
           }
           u32x2 o;
           o[0] = pack_bf16x2(v[0], v[1]);
@@ -761,7 +777,8 @@ hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStr
   k.M = a.M;
   k.N = a.N;
   k.K = a.K;
-  k.relu = a.relu;
+  k.act = a.act;
+  k.res = static_cast<const uint16_t*>(a.res);
   k.tiles_m = (int)((a.M + kSplitBM - 1) / kSplitBM);
   k.tiles_n = (a.N + kSplitBN - 1) / kSplitBN;
   const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n * sp;
@@ -775,7 +792,8 @@ hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStr
   int64_t grid = (groups8 + 255) / 256;
   if (grid > 4096) grid = 4096;
   hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, partial, sp, a.M, a.N,
-                     static_cast<const uint16_t*>(a.bias), a.relu, static_cast<uint16_t*>(a.c));
+                     static_cast<const uint16_t*>(a.bias), a.act, static_cast<const uint16_t*>(a.res),
+                     static_cast<uint16_t*>(a.c));
   return hipGetLastError();
 }
 
@@ -795,7 +813,8 @@ hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t 
   k.M = a.M;
   k.N = a.N;
   k.K = a.K;
-  k.relu = 0;
+  k.act = kActNone;
+  k.res = nullptr;
   k.tiles_m = (int)((a.M + 255) / 256);
   k.tiles_n = (a.N + 255) / 256;
   const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;
@@ -820,7 +839,8 @@ hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* 
   k.M = a.M;
   k.N = a.N;
   k.K = a.K;
-  k.relu = a.relu;
+  k.act = a.act;
+  k.res = static_cast<const uint16_t*>(a.res);
   k.tiles_m = (int)((a.M + v->bm - 1) / v->bm);
   k.tiles_n = (a.N + v->bn - 1) / v->bn;
   const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;

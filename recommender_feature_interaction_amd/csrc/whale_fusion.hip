@@ -1,0 +1,304 @@
+// WHALE's attention-based fusion step: the cross-branch attention and a row
+// LayerNorm (bf16, fp32 accumulation).  The Linear layers of the step run on
+// the MLP GEMM kernels.
+//
+// WHALE technical summaries, section 2.1: the Wukong module's interaction
+// representation H_w is the query and the HSTU module's behaviour
+// representation H_s (the whole sequence of L positions) gives the keys and
+// the values; section 2.2: keys and values are one shared tensor (K = V),
+// which halves the attention's memory traffic.  Per example:
+//   A = softmax(H_w H_s^T / sqrt(d)) H_s,   C = [H_w, A]   (n x 2d)
+//
+// whale_attention_kernel: one workgroup of 4 waves per (example, 128
+// queries), 32 queries per wave.  Key tiles of 32 positions x d are DMA'd
+// (buffer_load ... lds) into a ring of 4 LDS slots, 3 tiles ahead; each tile
+// is read twice from LDS, as K (rows, for S = Q K^T) and as V (transposed
+// reads, for O += P V): the shared K = V is loaded once.  S and O use
+// v_mfma_f32_16x16x32_bf16; the softmax is the online form (running row
+// maximum and sum, O rescaled when the maximum grows), in base 2 with the
+// 1/sqrt(d) scale folded into the exponent.  P goes through a per-wave LDS
+// tile in bf16 to become the A operand of P V.  Positions past L read as
+// zero through the buffer resource and are masked to -inf.
+#include <math.h>
+
+#include "wk_device.h"
+#include "wk_kernels.h"
+
+namespace wk {
+
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define WF_LDS_I16X4(p) ((__attribute__((address_space(3))) i16x4*)(p))
+#define WF_LDSV(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int AW = 4;    // waves per workgroup
+constexpr int AQ = 32;   // queries per wave (two 16-row tiles)
+constexpr int AKT = 32;  // sequence positions per step
+
+constexpr int vm_enc(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
+
+// Eight consecutive rows r0 .. r0 + 7 of a row-major [*, D] LDS tile at one
+// column, as one MFMA operand: in each 16-lane group, ds_read_b64_tr_b16 hands
+// lane i value i % 4 of the 8-byte rows addressed by lanes 4k + i / 4, so lanes
+// pointing at row 8 g + s / 4, column c0 + 4 (s % 4) receive rows 8 g .. 8 g + 3
+// of column c0 + s; the second read covers rows 8 g + 4 .. 8 g + 7.
+__device__ __forceinline__ u32x4 tr_rows8(const uint16_t* p0, const uint16_t* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WF_LDS_I16X4(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WF_LDS_I16X4(p1));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+struct AttnArgs {
+  const uint16_t* hw;  // [B, n, D]
+  const uint16_t* hs;  // [B, L, D]
+  uint16_t* c;         // [B, n, 2D]: H_w copied to columns 0..D-1, A to D..2D-1
+  int64_t batch;
+  int n, L;
+  float scale_log2;    // log2(e) / sqrt(D)
+};
+
+template <int D>
+__global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p) {
+  constexpr int DC = D / 32;                // 32-wide chunks of the Q K^T contraction
+  constexpr int DT = D / 16;                // 16-wide output column tiles
+  constexpr int TILE = AKT * D;             // u16 per key tile
+  constexpr int INS = TILE * 2 / 1024;      // 1 KB DMA instructions per tile
+  constexpr int INS_HI = (INS + AW - 1) / AW, INS_LO = INS / AW, R = INS % AW;
+  static_assert(D % 32 == 0 && INS * 1024 == TILE * 2, "D must be a multiple of 32");
+  __shared__ __align__(16) uint16_t s0[TILE], s1[TILE], s2[TILE], s3[TILE];
+  __shared__ __align__(16) uint16_t ps[AW][AQ * AKT];
+  uint16_t* const slot[4] = {s0, s1, s2, s3};  // indexed with compile-time numbers only
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int n = p.n, L = p.L;
+  const int qchunks = (n + AW * AQ - 1) / (AW * AQ);
+  const int64_t b = blockIdx.x / qchunks;
+  const int q0 = (int)(blockIdx.x - b * qchunks) * (AW * AQ) + wave * AQ;
+  const int T = (L + AKT - 1) / AKT;
+
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.hs + b * (int64_t)L * D), (short)0, L * D * 2, 0x00020000);
+  auto dma = [&](uint16_t* dst, int step) {
+#pragma unroll
+    for (int q = 0; q < INS_HI; ++q) {
+      const int i = wave + q * AW;  // wave-uniform
+      if (i < INS) {
+        const uint32_t vo = (uint32_t)step * (TILE * 2) + (uint32_t)(i * 1024 + lane * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, WF_LDSV(dst + i * 512), 16, vo, 0, 0, 0);
+      }
+    }
+  };
+
+  // queries of this wave as MFMA A operands: rows q0 + 16 qt + li, columns 32 c + 8 lg ..
+  u32x4 qf[2][DC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int q = q0 + qt * 16 + li;
+#pragma unroll
+    for (int c = 0; c < DC; ++c)
+      qf[qt][c] = q < n ? *reinterpret_cast<const u32x4*>(p.hw + (b * n + q) * D + c * 32 + lg * 8)
+                        : u32x4{0u, 0u, 0u, 0u};
+  }
+
+#pragma unroll
+  for (int u = 0; u < 3; ++u)
+    if (u < T) dma(slot[u], u);
+
+  f32x4 o[2][DT];
+  float mrow[2][4], lrow[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      mrow[qt][t] = -INFINITY;
+      lrow[qt][t] = 0.f;
+    }
+  }
+  const int xa = (8 * lg + (li >> 2)) * D + 4 * (li & 3);  // transposed-read lane offset
+  uint16_t* pw = ps[wave];
+
+  auto step = [&](const uint16_t* kt, uint16_t* next, int t) {
+    const int newer = (T - 1 - t < 2) ? T - 1 - t : 2;  // DMA steps issued after step t
+    if (newer <= 0) {
+      __builtin_amdgcn_s_waitcnt(vm_enc(0));
+    } else if (newer == 1) {
+      if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(INS_HI));
+      else __builtin_amdgcn_s_waitcnt(vm_enc(INS_LO));
+    } else {
+      if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_HI));
+      else __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_LO));
+    }
+    lds_barrier();
+    if (t + 3 < T) dma(next, t + 3);
+    // S = Q K^T: rows 4 lg + r of query tile qt, key 16 kk + li
+    f32x4 s[2][2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) s[qt][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + (kk * 16 + li) * D + c * 32 + lg * 8);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) s[qt][kk] = mfma16x16x32(qf[qt][c], kf, s[qt][kk]);
+      }
+    }
+    // online softmax (base 2), P to this wave's LDS tile as bf16 [32 queries][32 keys]
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float v0 = s[qt][0][r] * p.scale_log2, v1 = s[qt][1][r] * p.scale_log2;
+        if (t * AKT + li >= L) v0 = -INFINITY;
+        if (t * AKT + 16 + li >= L) v1 = -INFINITY;
+        float mx = fmaxf(v0, v1);
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        const float mnew = fmaxf(mrow[qt][r], mx);
+        const float alpha = exp2f(mrow[qt][r] - mnew);
+        const float e0 = exp2f(v0 - mnew), e1 = exp2f(v1 - mnew);
+        float sum = e0 + e1;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off, 64);
+        lrow[qt][r] = lrow[qt][r] * alpha + sum;
+        mrow[qt][r] = mnew;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qt][dt][r] *= alpha;
+        const int row = qt * 16 + 4 * lg + r;
+        pw[row * AKT + li] = (uint16_t)f32_to_bf16(e0);
+        pw[row * AKT + 16 + li] = (uint16_t)f32_to_bf16(e1);
+      }
+    }
+    // O += P V, V = the same key tile read transposed
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const u32x4 pf = *reinterpret_cast<const u32x4*>(pw + (qt * 16 + li) * AKT + lg * 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const u32x4 vf = tr_rows8(kt + xa + dt * 16, kt + xa + 4 * D + dt * 16);
+        o[qt][dt] = mfma16x16x32(pf, vf, o[qt][dt]);
+      }
+    }
+  };
+  for (int t0 = 0; t0 < T; t0 += 4) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {  // unrolled: every slot is a known object at each step
+      if (t0 + u >= T) break;
+      step(slot[u], slot[(u + 3) & 3], t0 + u);
+    }
+  }
+
+  // A = O / l into columns D .. 2D-1 of C; H_w rows into columns 0 .. D-1
+  uint16_t* cb = p.c + b * (int64_t)n * (2 * D);
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int q = q0 + qt * 16 + 4 * lg + r;
+      if (q < n) {
+        const float inv = 1.0f / lrow[qt][r];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) cb[(int64_t)q * (2 * D) + D + dt * 16 + li] = (uint16_t)f32_to_bf16(o[qt][dt][r] * inv);
+      }
+    }
+  }
+  for (int i = lane; i < AQ * (D / 8); i += 64) {
+    const int r = i / (D / 8), cc = i - r * (D / 8);
+    const int q = q0 + r;
+    if (q < n)
+      *reinterpret_cast<u32x4*>(cb + (int64_t)q * (2 * D) + cc * 8) =
+          *reinterpret_cast<const u32x4*>(p.hw + (b * n + q) * D + cc * 8);
+  }
+}
+
+// y[r] = LN(x[r]) * gamma + beta over rows of d (d % 8 == 0, d <= 512): one wave per row.
+__global__ __launch_bounds__(256) void row_ln_bf16_kernel(const uint16_t* x, uint16_t* y, int64_t rows, int d,
+                                                           const uint16_t* gamma, const uint16_t* beta, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;  // wave-uniform
+  const bool on = lane * 8 < d;
+  float v[8];
+  u32x4 xv = on ? *reinterpret_cast<const u32x4*>(x + r * d + lane * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    v[2 * t] = bf16lo(xv[t]);
+    v[2 * t + 1] = bf16hi(xv[t]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s += v[e];
+  s = xor_sum<1>(s);
+  const float mean = s / (float)d;
+  float q = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) q += on ? (v[e] - mean) * (v[e] - mean) : 0.f;
+  q = xor_sum<1>(q);
+  const float rstd = rsqrtf(q / (float)d + eps);
+  if (!on) return;
+  u32x4 g = gamma ? *reinterpret_cast<const u32x4*>(gamma + lane * 8) : u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  u32x4 bt = beta ? *reinterpret_cast<const u32x4*>(beta + lane * 8) : u32x4{0u, 0u, 0u, 0u};
+  u32x4 o;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    o[t] = pack_bf16x2((v[2 * t] - mean) * rstd * bf16lo(g[t]) + bf16lo(bt[t]),
+                       (v[2 * t + 1] - mean) * rstd * bf16hi(g[t]) + bf16hi(bt[t]));
+  *reinterpret_cast<u32x4*>(y + r * d + lane * 8) = o;
+}
+
+}  // namespace
+
+bool whale_attention_supported(int n, int d, int L) {
+  return n > 0 && n % 16 == 0 && L > 0 && (d == 32 || d == 64 || d == 96 || d == 128 || d == 160) &&
+         (int64_t)L * d * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_whale_attention(const void* hw, const void* hs, void* c, int64_t batch, int n, int d, int L,
+                                  hipStream_t stream, int64_t* workgroups) {
+  if (!whale_attention_supported(n, d, L)) return hipErrorInvalidValue;
+  AttnArgs a;
+  a.hw = static_cast<const uint16_t*>(hw);
+  a.hs = static_cast<const uint16_t*>(hs);
+  a.c = static_cast<uint16_t*>(c);
+  a.batch = batch;
+  a.n = n;
+  a.L = L;
+  a.scale_log2 = (float)(1.4426950408889634 / sqrt((double)d));
+  const int64_t qchunks = (n + AW * AQ - 1) / (AW * AQ);
+  const int64_t blocks = batch * qchunks;
+  if (workgroups) *workgroups = blocks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(AW * 64);
+  switch (d) {
+    case 32: hipLaunchKernelGGL(whale_attention_kernel<32>, grid, block, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL(whale_attention_kernel<64>, grid, block, 0, stream, a); break;
+    case 96: hipLaunchKernelGGL(whale_attention_kernel<96>, grid, block, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL(whale_attention_kernel<128>, grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL(whale_attention_kernel<160>, grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_ln_bf16(const void* x, void* y, int64_t rows, int d, const void* gamma, const void* beta,
+                              float eps, hipStream_t stream, int64_t* workgroups) {
+  if (d <= 0 || d % 8 != 0 || d > 512) return hipErrorInvalidValue;
+  const int64_t blocks = (rows + 3) / 4;
+  if (workgroups) *workgroups = blocks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(row_ln_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), rows, d,
+                     static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta), eps);
+  return hipGetLastError();
+}
+
+}  // namespace wk

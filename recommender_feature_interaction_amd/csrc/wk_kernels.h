@@ -29,6 +29,14 @@ bool fmb_lcb_stream_supported(int n, int d, int k, int n_l);
 hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups);
+// WHALE fusion step (whale_fusion.hip): shared K = V cross-attention writing
+// C = [H_w, A] ([B, n, 2d] bf16), n % 16 == 0, d in {32, 64, 96, 128, 160};
+// and a row LayerNorm (d % 8 == 0, d <= 512).
+bool whale_attention_supported(int n, int d, int L);
+hipError_t launch_whale_attention(const void* hw, const void* hs, void* c, int64_t batch, int n, int d, int L,
+                                  hipStream_t stream, int64_t* workgroups);
+hipError_t launch_row_ln_bf16(const void* x, void* y, int64_t rows, int d, const void* gamma, const void* beta,
+                              float eps, hipStream_t stream, int64_t* workgroups);
 // Units of width d = 8 (fmb_lcb_units.hip): transpose, one batched GEMM with
 // fp32 output, and an epilogue kernel; needs fmb_lcb_units_workspace() bytes
 // of scratch (16-byte aligned), n % 64 == 0, k % 4 == 0, k <= 32,
@@ -56,6 +64,10 @@ hipError_t launch_fmb_lcb_f32(const FmbLcbF32Args& a, int64_t batch, hipStream_t
                               int64_t* workgroups);
 
 // One FMB-MLP Linear: C[M, N] = act(A[M, K] W[N, K]^T + bias[N]).
+// Activation applied after the bias: none, ReLU, or the shared-gate SwiGLU
+// u * silu(u) (gate and up projection are one matrix).  bf16 kernels take
+// all three; the fp32 kernel takes none and ReLU.
+enum LinearAct { kActNone = 0, kActRelu = 1, kActSiluGate = 2 };
 struct LinearArgs {
   const void* a;
   const void* w;
@@ -63,7 +75,8 @@ struct LinearArgs {
   void* c;
   int64_t M;
   int N, K;
-  int relu;
+  int act;
+  const void* res = nullptr;  // bf16 only: [M, N] added after the activation, or null
 };
 bool linear_bf16_supported(int64_t M, int N, int K);
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);

@@ -215,7 +215,7 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.M = batch;
     a.N = d.mlp_dims[t + 1];
     a.K = d.mlp_dims[t];
-    a.relu = last ? 0 : 1;
+    a.act = last ? wk::kActNone : wk::kActRelu;
     st = launch(WK_KERNEL_MLP_LINEAR, layer_idx, t, [&](int64_t* g) {
       return bf ? wk::launch_linear_bf16(a, launch.stream, g) : wk::launch_linear_f32(a, launch.stream, g);
     });
@@ -396,7 +396,7 @@ int32_t head_forward(const wk_head_desc* d, const wk_head_weights* w, int64_t ba
     a.M = batch;
     a.N = d->dims[t + 1];
     a.K = d->dims[t];
-    a.relu = 1;
+    a.act = wk::kActRelu;
     const bool split = bf && wk::linear_bf16_splits(a.M, a.N, a.K) > 1;
     float* part = reinterpret_cast<float*>(base + hp.part);
     st = launch(WK_KERNEL_HEAD_LINEAR, 0, t, [&](int64_t* g) {
@@ -415,6 +415,88 @@ int32_t head_forward(const wk_head_desc* d, const wk_head_weights* w, int64_t ba
   o.N = d->dims[T];
   o.K = d->dims[T - 1];
   return launch(WK_KERNEL_HEAD_OUT, 0, 0, [&](int64_t* g) { return wk::launch_head_out(o, bf, launch.stream, g); });
+}
+
+// ---- WHALE fusion step: attention, three Linears on the MLP GEMMs, one row LayerNorm.
+int32_t check_fusion_desc(const wk_fusion_desc* d) {
+  if (!d || d->n <= 0 || d->d <= 0 || d->L <= 0 || d->d_ff <= 0) return WK_ERR_INVALID_ARG;
+  if (!(d->ln_eps >= 0.0f) || !std::isfinite(d->ln_eps)) return WK_ERR_INVALID_ARG;
+  if (d->dtype != WK_F32 && d->dtype != WK_BF16) return WK_ERR_INVALID_ARG;
+  if (d->dtype != WK_BF16) return WK_ERR_UNSUPPORTED;
+  if (!wk::whale_attention_supported(d->n, d->d, d->L) || d->d_ff % 8) return WK_ERR_UNSUPPORTED;
+  return WK_OK;
+}
+
+struct FusionPlan {
+  size_t c = 0, q = 0, qn = 0, g = 0, bytes = 0;
+};
+
+FusionPlan plan_fusion(const wk_fusion_desc& d, int64_t batch) {
+  FusionPlan p;
+  const size_t rows = (size_t)batch * d.n;
+  p.c = 0;
+  p.q = p.c + align_up(rows * 2 * d.d * 2);
+  p.qn = p.q + align_up(rows * d.d * 2);
+  p.g = p.qn + align_up(rows * d.d * 2);
+  p.bytes = p.g + align_up(rows * d.d_ff * 2);
+  if (p.bytes == 0) p.bytes = kAlign;
+  return p;
+}
+
+int32_t fusion_forward(const wk_fusion_desc* d, const wk_fusion_weights* w, int64_t batch, const void* hw,
+                       const void* hs, void* hf, void* ws, size_t ws_bytes, void* stream, wk_trace* trace) {
+  int32_t st = check_fusion_desc(d);
+  if (st != WK_OK) return st;
+  if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
+  if (!w || !w->w_f || !w->w_up || !w->w_down) return WK_ERR_INVALID_ARG;
+  const void* ptrs[] = {w->w_f, w->b_f, w->ln_gamma, w->ln_beta, w->w_up, w->b_up, w->w_down, w->b_down};
+  for (const void* q : ptrs)
+    if (q && !aligned16(q)) return WK_ERR_INVALID_ARG;
+  if (batch == 0) return WK_OK;
+  const size_t act = (size_t)batch * d->n * d->d * 2, seq = (size_t)batch * d->L * d->d * 2;
+  if (!hw || !hs || !hf || !aligned16(hw) || !aligned16(hs) || !aligned16(hf)) return WK_ERR_INVALID_ARG;
+  if (overlap(hw, act, hf, act) || overlap(hs, seq, hf, act)) return WK_ERR_INVALID_ARG;
+  const FusionPlan fp = plan_fusion(*d, batch);
+  if (!ws || !aligned16(ws)) return WK_ERR_INVALID_ARG;
+  if (ws_bytes < fp.bytes) return WK_ERR_WORKSPACE;
+  if (overlap(ws, fp.bytes, hw, act) || overlap(ws, fp.bytes, hs, seq) || overlap(ws, fp.bytes, hf, act))
+    return WK_ERR_INVALID_ARG;
+
+  char* base = static_cast<char*>(ws);
+  void* c = base + fp.c;
+  void* q = base + fp.q;
+  void* qn = base + fp.qn;
+  void* g = base + fp.g;
+  const int64_t rows = batch * d->n;
+  Launch launch{trace, static_cast<hipStream_t>(stream)};
+  st = launch(WK_KERNEL_FUSION_ATTN, 0, 0, [&](int64_t* wg) {
+    return wk::launch_whale_attention(hw, hs, c, batch, d->n, d->d, d->L, launch.stream, wg);
+  });
+  if (st != WK_OK) return st;
+  auto linear = [&](int index, const void* a, const void* wt, const void* bias, void* out, int N, int K, int act_kind,
+                    const void* res) {
+    wk::LinearArgs la;
+    la.a = a;
+    la.w = wt;
+    la.bias = bias;
+    la.c = out;
+    la.M = rows;
+    la.N = N;
+    la.K = K;
+    la.act = act_kind;
+    la.res = res;
+    return launch(WK_KERNEL_FUSION_LINEAR, 0, index,
+                  [&](int64_t* wg) { return wk::launch_linear_bf16(la, launch.stream, wg); });
+  };
+  st = linear(0, c, w->w_f, w->b_f, q, d->d, 2 * d->d, wk::kActNone, nullptr);
+  if (st != WK_OK) return st;
+  st = launch(WK_KERNEL_FUSION_LN, 0, 0, [&](int64_t* wg) {
+    return wk::launch_row_ln_bf16(q, qn, rows, d->d, w->ln_gamma, w->ln_beta, d->ln_eps, launch.stream, wg);
+  });
+  if (st != WK_OK) return st;
+  st = linear(1, qn, w->w_up, w->b_up, g, d->d_ff, d->d, wk::kActSiluGate, nullptr);
+  if (st != WK_OK) return st;
+  return linear(2, g, w->w_down, w->b_down, hf, d->d, d->d_ff, wk::kActNone, q);
 }
 
 }  // namespace
@@ -549,6 +631,24 @@ size_t wukong_head_workspace_size(const wk_head_desc* desc, int64_t batch) {
 int32_t wukong_head_forward(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch, const void* y,
                             float* prob, void* workspace, size_t workspace_bytes, void* stream) {
   return head_forward(desc, weights, batch, y, prob, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t wukong_fusion_workspace_size(const wk_fusion_desc* desc, int64_t batch) {
+  if (check_fusion_desc(desc) != WK_OK || batch < 0 || batch > kMaxBatch) return 0;
+  return plan_fusion(*desc, batch).bytes;
+}
+
+int32_t wukong_fusion_forward(const wk_fusion_desc* desc, const wk_fusion_weights* weights, int64_t batch,
+                              const void* hw, const void* hs, void* hf, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return fusion_forward(desc, weights, batch, hw, hs, hf, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t wukong_fusion_forward_traced(const wk_fusion_desc* desc, const wk_fusion_weights* weights, int64_t batch,
+                                     const void* hw, const void* hs, void* hf, void* workspace,
+                                     size_t workspace_bytes, void* stream, wk_trace* trace) {
+  if (!trace) return WK_ERR_INVALID_ARG;
+  return fusion_forward(desc, weights, batch, hw, hs, hf, workspace, workspace_bytes, stream, trace);
 }
 
 int32_t wukong_head_forward_traced(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch,

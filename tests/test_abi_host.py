@@ -203,3 +203,35 @@ def test_head_argument_errors_launch_nothing():
     assert _head_call(dims, 4, Y, P, WS, need, desc=d) == _abi.WK_ERR_INVALID_ARG
     d, _dims = wk.HeadSpec((64, 0, 1)).make_desc()
     assert _head_call(dims, 4, Y, P, WS, need, desc=d) == _abi.WK_ERR_INVALID_ARG
+
+
+def test_fusion_workspace_and_argument_errors():
+    lib = wk.load_library()
+    spec = wk.FusionSpec(128, 160, 1024, 640)
+    B = 7
+    rows = B * 128
+    assert wk.fusion_workspace_size(spec, B) == al(rows * 320 * 2) + 2 * al(rows * 160 * 2) + al(rows * 640 * 2)
+    assert wk.fusion_workspace_size(wk.FusionSpec(120, 160, 1024, 640), B) == 0   # n % 16
+    assert wk.fusion_workspace_size(wk.FusionSpec(128, 48, 1024, 640), B) == 0    # d not a compiled width
+    assert wk.fusion_workspace_size(wk.FusionSpec(128, 160, 0, 640), B) == 0      # L >= 1
+    assert wk.fusion_workspace_size(wk.FusionSpec(128, 160, 64, 644), B) == 0     # d_ff % 8
+    assert wk.fusion_workspace_size(wk.FusionSpec(128, 160, 64, 640, dtype="f32"), B) == 0
+    need = wk.fusion_workspace_size(spec, B)
+    desc = spec.make_desc()
+    good = _abi.wk_fusion_weights(0x10000, None, None, None, 0x20000, None, 0x30000, None)
+    HW, HS, HF, WS = 0x1000000, 0x2000000, 0x9000000, 0x10000000
+
+    def call(hw=HW, hs=HS, hf=HF, ws=WS, nbytes=need, weights=good, batch=B):
+        return lib.wukong_fusion_forward(ctypes.byref(desc), ctypes.byref(weights), batch, hw, hs, hf, ws, nbytes,
+                                         None)
+    assert call(nbytes=need - 1) == _abi.WK_ERR_WORKSPACE
+    assert call(hw=None) == _abi.WK_ERR_INVALID_ARG
+    assert call(hs=HS + 8) == _abi.WK_ERR_INVALID_ARG                 # misaligned
+    assert call(hf=HW + 256) == _abi.WK_ERR_INVALID_ARG               # output overlaps the queries
+    assert call(ws=HS) == _abi.WK_ERR_INVALID_ARG                     # workspace overlaps the sequence
+    assert call(batch=-1) == _abi.WK_ERR_INVALID_ARG
+    assert call(hw=None, hs=None, hf=None, ws=None, nbytes=0, batch=0) == _abi.WK_OK
+    assert call(weights=_abi.wk_fusion_weights(0x10000, None, None, None, None, None, 0x30000, None)) == \
+        _abi.WK_ERR_INVALID_ARG
+    assert call(weights=_abi.wk_fusion_weights(0x10000, 0x20008, None, None, 0x20000, None, 0x30000, None)) == \
+        _abi.WK_ERR_INVALID_ARG                                       # misaligned bias

@@ -230,6 +230,41 @@ def make_head_weights(cfg_name: str, dims, dtype: str, seed: int, affine: str = 
     return w, b
 
 
+@dataclass
+class HostFusionWeights:
+    """Host copies of WHALE fusion-step parameters (float32, or uint16 bf16 bits)."""
+
+    w_f: np.ndarray               # [d, 2d]
+    b_f: Optional[np.ndarray]     # [d]
+    gamma: Optional[np.ndarray]   # [d]
+    beta: Optional[np.ndarray]    # [d]
+    w_up: np.ndarray              # [d_ff, d]
+    b_up: Optional[np.ndarray]    # [d_ff]
+    w_down: np.ndarray            # [d, d_ff]
+    b_down: Optional[np.ndarray]  # [d]
+
+
+def make_fusion_weights(tag: str, d: int, d_ff: int, dtype: str, seed: int,
+                        affine: str = "identity") -> HostFusionWeights:
+    """Xavier-uniform Linear weights; biases 0 / LN gamma 1, beta 0 ('identity') or U(+-0.5) ('random')."""
+    w_f = xavier_uniform(seed, f"{tag}/fusion/w_f", d, 2 * d, dtype)
+    w_up = xavier_uniform(seed, f"{tag}/fusion/w_up", d_ff, d, dtype)
+    w_down = xavier_uniform(seed, f"{tag}/fusion/w_down", d, d_ff, dtype)
+    if affine == "random":
+        vec = lambda name, k, c=0.0: _store(_uniform_pm(seed, f"{tag}/fusion/{name}", k, 0.5, c), dtype)  # noqa: E731
+        return HostFusionWeights(w_f, vec("b_f", d), vec("gamma", d, 1.0), vec("beta", d), w_up, vec("b_up", d_ff),
+                                 w_down, vec("b_down", d))
+    if affine != "identity":
+        raise ValueError(affine)
+    z = lambda k: _store(np.zeros(k, np.float32), dtype)  # noqa: E731
+    return HostFusionWeights(w_f, z(d), _store(np.ones(d, np.float32), dtype), z(d), w_up, z(d_ff), w_down, z(d))
+
+
+def make_sequence(tag: str, batch: int, L: int, d: int, dtype: str, seed: int) -> np.ndarray:
+    """A stand-in for the sequence branch's output H_s [batch, L, d]: N(0, 1) entries."""
+    return _draw(seed, f"{tag}/h_s", batch * L * d, "normal", dtype=dtype).reshape(batch, L, d)
+
+
 def feature_scales(cfg: WukongConfig, seed: int, count: Optional[int] = None) -> np.ndarray:
     """Per-feature scale s_i = 10**U(-1,1), shared by all examples (float32 [count], default n)."""
     n = cfg.layers[0].n if count is None else count
