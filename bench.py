@@ -18,8 +18,10 @@ a 256 MiB device copy gives the on-box HBM bandwidth ("copy_gbps_measured"),
 and "step_roofline_frac" is the sum over kernels of max(FLOPs / peak, bytes /
 HBM bandwidth) divided by the measured step.
 
-The prediction head (top MLP + logistic function) is then timed on its own
-on the stack's output and reported under "head"; it is not part of `value`.
+The prediction head (top MLP + logistic function) and WHALE's fusion step
+(the stack's output as the query H_w, a seeded sequence H_s of 1024
+positions) are then timed on their own and reported under "head" and
+"fusion"; neither is part of `value`.
 
 Prints one JSON line.
 
@@ -52,6 +54,9 @@ KERNEL_SOURCES = {
     "residual_ln": ("resid_ln.hip",),
     "head_linear": ("linear_bf16.hip",),
     "head_out": ("head.hip",),
+    "fusion_attention": ("whale_fusion.hip",),
+    "fusion_linear": ("linear_bf16.hip",),
+    "fusion_ln": ("whale_fusion.hip",),
 }
 
 
@@ -184,6 +189,63 @@ def measure_head(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
             "kernels": sorted(kernels, key=lambda k: (k["kernel"] != "head_linear", k["index"]))}
 
 
+FUSION_L = 1024  # sequence positions of H_s in the measured fusion step
+
+
+def fusion_accounting(B, n, d, L, dff):
+    """Algorithmic FLOPs and HBM bytes per launch of the fusion step's kernels (bf16)."""
+    rows = B * n
+    return {
+        # S = Q K^T and O = P V; H_s (K = V) read once, H_w read, C = [H_w, A] written
+        ("fusion_attention", 0, 0): {"flops": 4 * B * n * L * d, "bytes": (B * L * d + B * n * d + rows * 2 * d) * 2},
+        ("fusion_linear", 0, 0): {"flops": 2 * rows * 2 * d * d, "bytes": (rows * 2 * d + d * 2 * d + d + rows * d) * 2},
+        ("fusion_ln", 0, 0): {"flops": 0, "bytes": 2 * rows * d * 2},
+        ("fusion_linear", 0, 1): {"flops": 2 * rows * d * dff, "bytes": (rows * d + dff * d + dff + rows * dff) * 2},
+        ("fusion_linear", 0, 2): {"flops": 2 * rows * dff * d,
+                                  "bytes": (rows * dff + d * dff + d + 2 * rows * d) * 2},
+    }
+
+
+def measure_fusion(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
+    """WHALE's fusion step on the stack's output as H_w, with a seeded H_s of
+    FUSION_L positions and d_ff = 4d, timed on its own."""
+    s = cfg.layers[-1]
+    n, d, L, dff = s.n, s.d, FUSION_L, 4 * s.d
+    spec = wk.FusionSpec(n, d, L, dff)
+    if wk.fusion_workspace_size(spec, cfg.batch) == 0:
+        return None
+    w = ws.make_fusion_weights(cfg.name, d, dff, cfg.dtype, seed, "identity")
+    fusion = wk.DeviceFusion(spec, w.w_f, w.w_up, w.w_down, w.b_f, w.gamma, w.beta, w.b_up, w.b_down, device=y.device)
+    hs = wk.to_device(ws.make_sequence(cfg.name, cfg.batch, L, d, cfg.dtype, seed), cfg.dtype, y.device)
+    hf = torch.empty_like(y)
+    fws = wk.alloc_workspace(wk.fusion_workspace_size(spec, cfg.batch), y.device)
+    for _ in range(warmup):
+        wk.fusion_forward(y, hs, fusion, hf=hf, workspace=fws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wk.fusion_forward(y, hs, fusion, hf=hf, workspace=fws, stream=stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    trace = wk.Trace(capacity=5 * steps + 8)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        wk.fusion_forward(y, hs, fusion, hf=hf, workspace=fws, stream=stream, trace=trace)
+    torch.cuda.synchronize()
+    traced_ms = (time.perf_counter() - t1) * 1e3 / steps
+    acct = fusion_accounting(cfg.batch, n, d, L, dff)
+    kernels, dom = summarize_trace(trace.records(), acct, traced_ms, steps)
+    trace.close()
+    roof = None
+    if dom is not None:
+        roof = roofline_of(dom, acct[(dom["kernel"], dom["layer"], dom["index"])], dom["avg_ms"], cfg.dtype, cfg.name)
+    flops = sum(a["flops"] for a in acct.values())
+    return {"n": n, "d": d, "L": L, "d_ff": dff, "ms_per_call": round(ms, 4),
+            "examples_per_s": round(cfg.batch / ms * 1e3, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "roofline": roof, "kernels": sorted(kernels, key=lambda k: (k["kernel"], k["index"]))}
+
+
 def source_digest(name):
     h = hashlib.sha256()
     for src in KERNEL_SOURCES[name]:
@@ -254,6 +316,7 @@ def main():
     ap.add_argument("--no-head", action="store_true", help="skip the prediction-head measurement")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache (512 MB flush) step timing")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
+    ap.add_argument("--no-fusion", action="store_true", help="skip the WHALE fusion-step measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -406,6 +469,13 @@ def main():
         head = measure_head(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
         print(f"# head {head['dims']}: {head['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
 
+    fusion = None
+    if not args.no_fusion and cfg.dtype == "bf16":
+        fusion = measure_fusion(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
+        if fusion is not None:
+            print(f"# fusion n={fusion['n']} d={fusion['d']} L={fusion['L']}: {fusion['ms_per_call']:.3f} ms/call",
+                  file=sys.stderr, flush=True)
+
     step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
     s0 = cfg.layers[0]
     out = {
@@ -434,6 +504,7 @@ def main():
         "copy_gbps_measured": round(copy_gbps, 1),
         "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
         "head": head,
+        "fusion": fusion,
     }
     if not args.no_cpu_baseline:
         del x, y, ws_t, layers

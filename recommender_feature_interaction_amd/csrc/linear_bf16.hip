@@ -144,18 +144,26 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   const uint32_t voff0 = (uint32_t)(lrow * K + ((lpos ^ (lrow >> 1)) << 3)) * 2u;
   const uint32_t voff1 = (uint32_t)(lrow * K + ((lpos ^ (4 + (lrow >> 1))) << 3)) * 2u;
   const uint32_t blk_bytes = (uint32_t)(16 * K);
+  // A K range that ends in half a step (K % 64 == 32): in the last step the
+  // lanes of columns 32..63 read zero (an offset past every record count)
+  // instead of the next row's first columns.
+  const int kspan = klen < 0 ? K : klen;
+  const uint32_t voff0t = ((lpos ^ (lrow >> 1)) >= 4) ? 0x80000000u : voff0;
+  const uint32_t voff1t = ((lpos ^ (4 + (lrow >> 1))) >= 4) ? 0x80000000u : voff1;
   auto dma = [&](uint16_t* sa, uint16_t* sw, int k0) {
+    const bool half = k0 + kBK > kspan;  // uniform
+    const uint32_t v0 = half ? voff0t : voff0, v1 = half ? voff1t : voff1;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int blk = wave * A_INS + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, WK_LDS(sa + blk * 512), 16,
-                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, (kbeg + k0) * 2, 0, 0);
+                                               ((blk & 1) ? v1 : v0) + blk * blk_bytes, (kbeg + k0) * 2, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < W_INS; ++i) {
       const int blk = wave * W_INS + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, WK_LDS(sw + blk * 512), 16,
-                                               ((blk & 1) ? voff1 : voff0) + blk * blk_bytes, (kbeg + k0) * 2, 0, 0);
+                                               ((blk & 1) ? v1 : v0) + blk * blk_bytes, (kbeg + k0) * 2, 0, 0);
     }
   };
 #pragma unroll
@@ -180,8 +188,8 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
     }
   };
   // columns kbeg .. kbeg + klen of K (all of them by default); the resources
-  // still span whole rows
-  const int KT = (klen < 0 ? K : klen) / kBK;
+  // still span whole rows.  A last half step (K % 64 == 32) is zero-padded.
+  const int KT = (kspan + kBK - 1) / kBK;
   dma(sA0, sW0, 0);
   __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0), lgkmcnt(0)
   lds_barrier();
@@ -648,12 +656,12 @@ struct LinearVariant {
   void (*kernel)(LinearKArgs);
   size_t dyn_lds;  // dynamic LDS bytes (the DMA kernels use static LDS)
   int threads;
-  int kmod;        // K must be a multiple of this (64 or 128: DMA kernels; 8: register-staged)
+  int kmod;        // K must be a multiple of this (32 or 128: DMA kernels; 8: register-staged)
 };
 
 #define WK_DMA_VARIANT(BM, BN, WGM, WGN, OCC, EFF, SPREAD)                                              \
   LinearVariant {                                                                                     \
-    BM, BN, OCC, EFF, linear_dma_kernel<BM, BN, WGM, WGN, SPREAD>, 0, WGM * WGN * 64, SPREAD ? 128 : 64 \
+    BM, BN, OCC, EFF, linear_dma_kernel<BM, BN, WGM, WGN, SPREAD>, 0, WGM * WGN * 64, SPREAD ? 128 : 32 \
   }
 #define WK_LIN_VARIANT(BM, BN, WGM, WGN, OCC, EFF)                                                   \
   LinearVariant {                                                                                    \
@@ -675,12 +683,12 @@ constexpr int kNumLinVariants = sizeof(kLinVariants) / sizeof(kLinVariants[0]);
 constexpr int kNumCU = 256;
 
 const LinearVariant* pick_linear(int64_t M, int N, int K) {
-  const bool k64 = (K % kBK) == 0;
+  const bool k32 = (K % 32) == 0;
   const LinearVariant* best = nullptr;
   double best_cost = 0;
   for (const auto& v : kLinVariants) {
-    // the DMA family when K % 64 == 0 (the spread form also needs K % 128 == 0), else the fallbacks
-    if ((v.kmod >= kBK) != k64 || K % v.kmod != 0) continue;
+    // the DMA family when K % 32 == 0 (the spread form needs K % 128 == 0), else the fallbacks
+    if ((v.kmod >= 32) != k32 || K % v.kmod != 0) continue;
     const double tiles = (double)((M + v.bm - 1) / v.bm) * (double)((N + v.bn - 1) / v.bn);
     const double slots = (double)kNumCU * v.occupancy;
     const double rounds = (tiles + slots - 1) / slots;

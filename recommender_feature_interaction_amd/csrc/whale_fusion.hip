@@ -219,15 +219,17 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
   }
 }
 
-// y[r] = LN(x[r]) * gamma + beta over rows of d (d % 8 == 0, d <= 512): one wave per row.
+// y[r] = LN(x[r]) * gamma + beta over rows of d (d % 8 == 0, d <= 512): G lanes
+// per row (the power of two >= d / 8), 64 / G rows per wave, 8 values per lane.
+template <int G>
 __global__ __launch_bounds__(256) void row_ln_bf16_kernel(const uint16_t* x, uint16_t* y, int64_t rows, int d,
                                                            const uint16_t* gamma, const uint16_t* beta, float eps) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;  // wave-uniform
-  const bool on = lane * 8 < d;
+  constexpr int RPW = 64 / G;  // rows per wave
+  const int lane = threadIdx.x & 63, sub = lane % G;
+  const int64_t r = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * RPW + lane / G;
+  const bool on = r < rows && sub * 8 < d;
   float v[8];
-  u32x4 xv = on ? *reinterpret_cast<const u32x4*>(x + r * d + lane * 8) : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 xv = on ? *reinterpret_cast<const u32x4*>(x + r * d + sub * 8) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     v[2 * t] = bf16lo(xv[t]);
@@ -236,22 +238,23 @@ __global__ __launch_bounds__(256) void row_ln_bf16_kernel(const uint16_t* x, uin
   float s = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) s += v[e];
-  s = xor_sum<1>(s);
+  s = group_sum<G>(s);
   const float mean = s / (float)d;
   float q = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) q += on ? (v[e] - mean) * (v[e] - mean) : 0.f;
-  q = xor_sum<1>(q);
+  q = group_sum<G>(q);
   const float rstd = rsqrtf(q / (float)d + eps);
   if (!on) return;
-  u32x4 g = gamma ? *reinterpret_cast<const u32x4*>(gamma + lane * 8) : u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
-  u32x4 bt = beta ? *reinterpret_cast<const u32x4*>(beta + lane * 8) : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 g = gamma ? *reinterpret_cast<const u32x4*>(gamma + sub * 8)
+                        : u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+  const u32x4 bt = beta ? *reinterpret_cast<const u32x4*>(beta + sub * 8) : u32x4{0u, 0u, 0u, 0u};
   u32x4 o;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
     o[t] = pack_bf16x2((v[2 * t] - mean) * rstd * bf16lo(g[t]) + bf16lo(bt[t]),
                        (v[2 * t + 1] - mean) * rstd * bf16hi(g[t]) + bf16hi(bt[t]));
-  *reinterpret_cast<u32x4*>(y + r * d + lane * 8) = o;
+  *reinterpret_cast<u32x4*>(y + r * d + sub * 8) = o;
 }
 
 }  // namespace
@@ -291,13 +294,27 @@ hipError_t launch_whale_attention(const void* hw, const void* hs, void* c, int64
 hipError_t launch_row_ln_bf16(const void* x, void* y, int64_t rows, int d, const void* gamma, const void* beta,
                               float eps, hipStream_t stream, int64_t* workgroups) {
   if (d <= 0 || d % 8 != 0 || d > 512) return hipErrorInvalidValue;
-  const int64_t blocks = (rows + 3) / 4;
+  int g = 1;
+  while (g * 8 < d) g *= 2;
+  const int64_t rows_per_block = 4 * (64 / g);
+  const int64_t blocks = (rows + rows_per_block - 1) / rows_per_block;
   if (workgroups) *workgroups = blocks;
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(row_ln_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(x), static_cast<uint16_t*>(y), rows, d,
-                     static_cast<const uint16_t*>(gamma), static_cast<const uint16_t*>(beta), eps);
+  const auto* xs = static_cast<const uint16_t*>(x);
+  auto* ys = static_cast<uint16_t*>(y);
+  const auto* gs = static_cast<const uint16_t*>(gamma);
+  const auto* bs = static_cast<const uint16_t*>(beta);
+  const dim3 grid((unsigned)blocks), block(256);
+  switch (g) {
+    case 1: hipLaunchKernelGGL(row_ln_bf16_kernel<1>, grid, block, 0, stream, xs, ys, rows, d, gs, bs, eps); break;
+    case 2: hipLaunchKernelGGL(row_ln_bf16_kernel<2>, grid, block, 0, stream, xs, ys, rows, d, gs, bs, eps); break;
+    case 4: hipLaunchKernelGGL(row_ln_bf16_kernel<4>, grid, block, 0, stream, xs, ys, rows, d, gs, bs, eps); break;
+    case 8: hipLaunchKernelGGL(row_ln_bf16_kernel<8>, grid, block, 0, stream, xs, ys, rows, d, gs, bs, eps); break;
+    case 16: hipLaunchKernelGGL(row_ln_bf16_kernel<16>, grid, block, 0, stream, xs, ys, rows, d, gs, bs, eps); break;
+    case 32: hipLaunchKernelGGL(row_ln_bf16_kernel<32>, grid, block, 0, stream, xs, ys, rows, d, gs, bs, eps); break;
+    default: hipLaunchKernelGGL(row_ln_bf16_kernel<64>, grid, block, 0, stream, xs, ys, rows, d, gs, bs, eps); break;
+  }
   return hipGetLastError();
 }
 

@@ -95,6 +95,8 @@ RAGGED = [
     _custom("fused_d160_stack2", "bf16", 16, 160, 4, 8, (64, 128, 1280), 260, layers=2),
     # K % 128 == 0 on a ragged batch: the Linear whose DMA is spread over its MFMAs
     _custom("spread_k256_m37", "bf16", 32, 32, 8, 16, (256, 384, 512), 37),
+    # K % 64 == 32: the DMA GEMM's last K step is half zero-padded (K = 160, 96)
+    _custom("kstep_half_k160", "bf16", 40, 32, 4, 16, (160, 96, 512), 37),
     # the streamed FMB+LCB kernel: phase 2 pairs j tiles when k % 8 == 0 (16-byte LN loads / Fn stores)
     _custom("stream_d32_k20", "bf16", 64, 32, 20, 32, (1280, 64, 1024), 7),
     _custom("stream_d32_k24", "bf16", 48, 32, 24, 16, (1152, 136, 512), 9),
