@@ -1,4 +1,5 @@
-"""CPU oracle of the Wukong interaction stack and of WHALE's fusion step --
+"""CPU oracle of the Wukong interaction stack (forward and one layer's backward)
+and of WHALE's fusion step --
 TEST INFRASTRUCTURE ONLY.
 
 Imported only by the tests, the package's smoke check and the benchmark's
@@ -9,3 +10,4 @@ from .wukong_oracle import (LN_EPS, STORAGE_NAMES, brute_force_head, brute_force
                             round_bf16, sigmoid, to_f64, wukong_layer, wukong_stack)
 from .whale_oracle import (FUSION_STORAGE, brute_force_attention, cross_attention, silu,  # noqa: F401
                            whale_fusion)
+from .wukong_backward import BACKWARD_STORAGE, layer_backward, layer_loss, layer_norm_backward  # noqa: F401
