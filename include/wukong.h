@@ -164,7 +164,13 @@ enum {
   WK_KERNEL_HEAD_OUT = 5,     /* the head's last Linear + logistic function   */
   WK_KERNEL_FUSION_ATTN = 6,  /* WHALE fusion: shared K = V cross-attention    */
   WK_KERNEL_FUSION_LINEAR = 7, /* fusion Linear (index 0), SwiGLU up (1), down (2) */
-  WK_KERNEL_FUSION_LN = 8     /* fusion: the pre-norm LayerNorm               */
+  WK_KERNEL_FUSION_LN = 8,    /* fusion: the pre-norm LayerNorm               */
+  WK_KERNEL_BWD_OUT = 9,      /* backward: output LayerNorm + LCB rows (dR)   */
+  WK_KERNEL_BWD_TRANSPOSE = 10, /* backward: bf16 transpose (index = Linear)  */
+  WK_KERNEL_BWD_WGRAD = 11,   /* backward: dW_t (index t)                     */
+  WK_KERNEL_BWD_DGRAD = 12,   /* backward: gradient of the Linear's input (t) */
+  WK_KERNEL_BWD_FMB = 13,     /* backward: FM LayerNorm, interaction, dX      */
+  WK_KERNEL_BWD_REDUCE = 14   /* backward: per-workgroup weight-gradient sums */
 };
 typedef struct wk_trace wk_trace;
 /* Creates a trace able to hold `capacity` launch records (creates HIP events
@@ -224,6 +230,71 @@ int32_t wukong_head_forward(const wk_head_desc* desc, const wk_head_weights* wei
 int32_t wukong_head_forward_traced(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch,
                                    const void* y, float* prob, void* workspace, size_t workspace_bytes,
                                    void* stream, wk_trace* trace);
+
+/* ---- Backward pass of one layer ------------------------------------------
+ * The pages train the stack end to end (Wukong paper, xdnf.cn repost,
+ * section 3.2.1: the dense layers are trained with Adam; WHALE technical
+ * summaries, section 2.2: bf16 dense backbone).  Given dY = dLoss/dY for a
+ * layer's output, wukong_layer_backward returns dLoss/dX and every weight's
+ * gradient by the chain rule through the forward above:
+ *   dR     = LN_d backward of dY (R = [M; Lc] + X, per row)
+ *   dM, dLc = the FMB and LCB rows of dR;   dX  = dR + W_L^T dLc + ...
+ *   d_W_L  = sum_b dLc X^T
+ *   g_T = vec(dM);  d_W_t = sum_b g_{t+1} a_t^T,  d_b_t = sum_b g_{t+1},
+ *   g_t = (W_t^T g_{t+1}) * [h_t > 0]  (a_0 = Fn, a_t = h_t),  d_Fn = W_0^T g_1
+ *   dF     = LN backward of d_Fn over the n*k values of F
+ *   dZ = dF^T X;  dX += dF Z + Phi^T dZ;  d_Phi = sum_b dZ X^T
+ *   d_gamma / d_beta of both LayerNorms: sums of d(out) * normalised(in) / d(out)
+ * bf16 only.  The forward's Fn, h_t and M come from wukong_layer_forward_train;
+ * Lc, Z and F are recomputed from x.  Stored in bf16: dR (as dM and dLc),
+ * every g_t, d_Fn, dF and dZ (as product operands) and dX; fp32 accumulation
+ * and LayerNorm statistics; weight gradients are fp32.  Shapes: those of the
+ * bf16 forward with d % 16 == 0, whose per-example working set fits one
+ * workgroup's LDS (X, [Phi; W_L] and the operand panels; a c1-sized layer,
+ * n = 128, d = 160, k = 32, n_l = 64, does), else WK_ERR_UNSUPPORTED. */
+typedef struct {       /* device pointers, fp32, overwritten (not accumulated)  */
+  float* phi;          /* [k, n]                                               */
+  float* w_l;          /* [n_l, n]                                             */
+  float* fm_ln_gamma;  /* [n*k] or NULL (not computed)                         */
+  float* fm_ln_beta;   /* [n*k] or NULL                                        */
+  float* const* mlp_w; /* host array [num_linear] of device [m_t, m_{t-1}]     */
+  float* const* mlp_b; /* host array [num_linear] of device [m_t] (NULL array or entries: not computed) */
+  float* out_ln_gamma; /* [d] or NULL                                          */
+  float* out_ln_beta;  /* [d] or NULL                                          */
+} wk_layer_grads;
+
+/* Bytes of the activations wukong_layer_forward_train saves for the backward:
+ * Fn [batch, n*k], h_t [batch, m_t] for t = 1..num_linear-1 and M
+ * [batch, n_f*d], in that order, each at a 256-byte-aligned offset.  0 if desc
+ * is invalid or the backward does not support it. */
+size_t wukong_layer_saved_size(const wk_layer_desc* desc, int64_t batch);
+
+/* The forward of wukong_layer_forward that also keeps Fn, every h_t and M in
+ * `saved` (device, saved_bytes >= wukong_layer_saved_size).  y equals the
+ * plain forward's within bf16 rounding (M is rounded to bf16 before the
+ * residual LayerNorm here).  x, y and saved must not overlap. */
+int32_t wukong_layer_forward_train(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                                   const void* x, void* y, void* saved, size_t saved_bytes, void* stream);
+
+/* Workspace bytes for wukong_layer_backward (0 if unsupported). */
+size_t wukong_layer_backward_workspace_size(const wk_layer_desc* desc, int64_t batch);
+
+/* dx [batch, n, d] and the weight gradients from x (the layer input), saved
+ * (written by wukong_layer_forward_train on the same x and weights) and dy
+ * [batch, n, d].  grads->phi, grads->w_l and every grads->mlp_w[t] are
+ * required.  Same conventions as wukong_layer_forward; dx must not overlap
+ * x, dy, saved or the workspace.  batch == 0 launches nothing and leaves the
+ * gradients untouched.  Every sum over the batch is taken in a fixed order,
+ * so results do not depend on timing. */
+int32_t wukong_layer_backward(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                              const void* x, const void* saved, const void* dy, void* dx,
+                              const wk_layer_grads* grads, void* workspace, size_t workspace_bytes, void* stream);
+/* As wukong_layer_backward, recording one event pair per launch into `trace`
+ * (kinds WK_KERNEL_BWD_*). */
+int32_t wukong_layer_backward_traced(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                                     const void* x, const void* saved, const void* dy, void* dx,
+                                     const wk_layer_grads* grads, void* workspace, size_t workspace_bytes,
+                                     void* stream, wk_trace* trace);
 
 /* ---- WHALE fusion step ----------------------------------------------------
  * WHALE technical summaries, section 2.1 (attention-based fusion module) and

@@ -30,9 +30,9 @@ forward's steps taken in reverse:
         d_Phi = sum_b dZ X^T
 
 Storage rounding: besides the forward's names (see `wukong_oracle`), the
-backward may round to bf16 where it produces them: "dM" (the FMB rows of dR,
-the MLP's upstream gradient), "dh" (each g_t, t > 0), "dFn" (d_f_hat), "dL"
-(dLc as a product operand; the residual uses the unrounded dR), "dF", "dZ"
+backward may round to bf16 where it produces them: "dR" (the output
+LayerNorm's input gradient, which then serves as dM, as dLc and as the
+residual term of dX), "dh" (each g_t, t > 0), "dFn" (d_f_hat), "dF", "dZ"
 and "dX" (the final input gradient).  A rounded Z is treated as Z itself by
 the chain rule (the rounding has no derivative of its own).
 """
@@ -44,7 +44,7 @@ import numpy as np
 
 from .wukong_oracle import LN_EPS, STORAGE_NAMES, round_bf16, to_f64, wukong_layer
 
-BACKWARD_STORAGE = frozenset({"dM", "dh", "dFn", "dL", "dF", "dZ", "dX"})
+BACKWARD_STORAGE = frozenset({"dR", "dh", "dFn", "dF", "dZ", "dX"})
 
 
 def _r(x: np.ndarray, name: str, storage) -> np.ndarray:
@@ -98,11 +98,11 @@ def layer_backward(X, w, dY, eps: float = LN_EPS, storage: Iterable[str] = (),
     g_out = 1.0 if w.out_gamma is None else to_f64(w.out_gamma)
     d_out_gamma = (dY * R_hat).sum(axis=(0, 1))
     d_out_beta = dY.sum(axis=(0, 1))
-    dR = layer_norm_backward(dY * g_out, R_hat, rstd)
+    dR = _r(layer_norm_backward(dY * g_out, R_hat, rstd), "dR", storage)
 
     # 8'. concatenation and residual
-    dM = _r(dR[:, :n_f, :], "dM", storage)
-    dLc = _r(dR[:, n_f:, :], "dL", storage)
+    dM = dR[:, :n_f, :]
+    dLc = dR[:, n_f:, :]
     dX = dR.copy()
 
     # 7'. LCB

@@ -21,10 +21,14 @@ F32, BF16 = 0, 1
 WK_OK, WK_ERR_INVALID_ARG, WK_ERR_UNSUPPORTED, WK_ERR_WORKSPACE, WK_ERR_HIP = 0, 1, 2, 3, 4
 KERNEL_FMB_LCB, KERNEL_MLP_LINEAR, KERNEL_RESIDUAL_LN, KERNEL_HEAD_LINEAR, KERNEL_HEAD_OUT = 1, 2, 3, 4, 5
 KERNEL_FUSION_ATTN, KERNEL_FUSION_LINEAR, KERNEL_FUSION_LN = 6, 7, 8
+KERNEL_BWD_OUT, KERNEL_BWD_TRANSPOSE, KERNEL_BWD_WGRAD, KERNEL_BWD_DGRAD, KERNEL_BWD_FMB, KERNEL_BWD_REDUCE = \
+    9, 10, 11, 12, 13, 14
 KERNEL_NAMES = {KERNEL_FMB_LCB: "fmb_lcb", KERNEL_MLP_LINEAR: "mlp_linear", KERNEL_RESIDUAL_LN: "residual_ln",
                 KERNEL_HEAD_LINEAR: "head_linear", KERNEL_HEAD_OUT: "head_out",
                 KERNEL_FUSION_ATTN: "fusion_attention", KERNEL_FUSION_LINEAR: "fusion_linear",
-                KERNEL_FUSION_LN: "fusion_ln"}
+                KERNEL_FUSION_LN: "fusion_ln", KERNEL_BWD_OUT: "bwd_out", KERNEL_BWD_TRANSPOSE: "bwd_transpose",
+                KERNEL_BWD_WGRAD: "bwd_wgrad", KERNEL_BWD_DGRAD: "bwd_dgrad", KERNEL_BWD_FMB: "bwd_fmb",
+                KERNEL_BWD_REDUCE: "bwd_reduce"}
 ABI_VERSION = 1
 
 
@@ -58,6 +62,13 @@ class wk_fusion_desc(ctypes.Structure):
 class wk_fusion_weights(ctypes.Structure):
     _fields_ = [(name, ctypes.c_void_p) for name in
                 ("w_f", "b_f", "ln_gamma", "ln_beta", "w_up", "b_up", "w_down", "b_down")]
+
+
+class wk_layer_grads(ctypes.Structure):
+    _fields_ = [("phi", ctypes.c_void_p), ("w_l", ctypes.c_void_p),
+                ("fm_ln_gamma", ctypes.c_void_p), ("fm_ln_beta", ctypes.c_void_p),
+                ("mlp_w", ctypes.POINTER(ctypes.c_void_p)), ("mlp_b", ctypes.POINTER(ctypes.c_void_p)),
+                ("out_ln_gamma", ctypes.c_void_p), ("out_ln_beta", ctypes.c_void_p)]
 
 
 class wk_workspace_layout(ctypes.Structure):
@@ -97,6 +108,19 @@ _SIGNATURES = [
     ("wukong_fusion_forward_traced", ctypes.c_int32,
      [ctypes.POINTER(wk_fusion_desc), ctypes.POINTER(wk_fusion_weights), ctypes.c_int64, ctypes.c_void_p,
       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_layer_saved_size", ctypes.c_size_t, [ctypes.POINTER(wk_layer_desc), ctypes.c_int64]),
+    ("wukong_layer_forward_train", ctypes.c_int32,
+     [ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_layer_backward_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_layer_desc), ctypes.c_int64]),
+    ("wukong_layer_backward", ctypes.c_int32,
+     [ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(wk_layer_grads), ctypes.c_void_p,
+      ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_layer_backward_traced", ctypes.c_int32,
+     [ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(wk_layer_grads), ctypes.c_void_p,
+      ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     ("wukong_head_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_head_desc), ctypes.c_int64]),
     ("wukong_head_forward", ctypes.c_int32,
      [ctypes.POINTER(wk_head_desc), ctypes.POINTER(wk_head_weights), ctypes.c_int64, ctypes.c_void_p,
@@ -299,6 +323,103 @@ def layer_forward(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.Tensor]
                                   _stream_handle(stream))
     _check(st, "wukong_layer_forward")
     return y
+
+
+# ------------------------------------------------------------------ training: one layer's backward
+def layer_saved_size(spec: LayerSpec, batch: int) -> int:
+    desc, _dims = spec.make_desc()
+    return int(load_library().wukong_layer_saved_size(ctypes.byref(desc), batch))
+
+
+def layer_backward_workspace_size(spec: LayerSpec, batch: int) -> int:
+    desc, _dims = spec.make_desc()
+    return int(load_library().wukong_layer_backward_workspace_size(ctypes.byref(desc), batch))
+
+
+def saved_layout(spec: LayerSpec, batch: int) -> dict:
+    """Byte offsets of Fn, h_1 .. h_{T-1} and M in a training forward's saved buffer."""
+    al = lambda v: (v + 255) // 256 * 256  # noqa: E731
+    off = 0
+    out = {"fn": 0}
+    off += al(batch * spec.n * spec.k * 2)
+    out["hidden"] = []
+    for t in range(1, len(spec.mlp) - 1):
+        out["hidden"].append(off)
+        off += al(batch * spec.mlp[t] * 2)
+    out["m"] = off
+    return out
+
+
+def layer_forward_train(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.Tensor] = None,
+                        saved: Optional[torch.Tensor] = None, stream=None):
+    """Training forward of one bf16 layer: returns (y, saved), saved holding Fn, h_t and M."""
+    lib = load_library()
+    B = _check_x(x, layer.spec)
+    y = torch.empty_like(x) if y is None else y
+    need = layer_saved_size(layer.spec, B)
+    if need == 0:
+        raise WukongError(WK_ERR_UNSUPPORTED, "wukong_layer_saved_size")
+    if saved is None:
+        saved = alloc_workspace(need, x.device)
+    st = lib.wukong_layer_forward_train(ctypes.byref(layer.desc), ctypes.byref(layer.weights), B, x.data_ptr(),
+                                        y.data_ptr(), saved.data_ptr(), saved.numel() * saved.element_size(),
+                                        _stream_handle(stream))
+    _check(st, "wukong_layer_forward_train")
+    return y, saved
+
+
+class LayerGrads:
+    """fp32 device gradients of one layer's weights (the C ABI overwrites them)."""
+
+    def __init__(self, layer: DeviceLayer, affine: bool = True, bias: bool = True):
+        spec = layer.spec
+        dev = layer.phi.device
+        z = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)  # noqa: E731
+        n, d, k = spec.n, spec.d, spec.k
+        T = len(spec.mlp) - 1
+        self.phi, self.w_l = z(k, n), z(spec.n_l, n)
+        self.fm_gamma = z(n * k) if affine else None
+        self.fm_beta = z(n * k) if affine else None
+        self.out_gamma = z(d) if affine else None
+        self.out_beta = z(d) if affine else None
+        self.mlp_w = [z(spec.mlp[t + 1], spec.mlp[t]) for t in range(T)]
+        self.mlp_b = [z(spec.mlp[t + 1]) for t in range(T)] if bias else None
+        self._w = (ctypes.c_void_p * T)(*[w.data_ptr() for w in self.mlp_w])
+        self._b = None if self.mlp_b is None else (ctypes.c_void_p * T)(*[b.data_ptr() for b in self.mlp_b])
+        self.c = wk_layer_grads(
+            _ptr(self.phi), _ptr(self.w_l), _ptr(self.fm_gamma), _ptr(self.fm_beta),
+            ctypes.cast(self._w, ctypes.POINTER(ctypes.c_void_p)),
+            None if self._b is None else ctypes.cast(self._b, ctypes.POINTER(ctypes.c_void_p)),
+            _ptr(self.out_gamma), _ptr(self.out_beta))
+
+    def as_dict(self) -> dict:
+        return {"phi": self.phi, "w_l": self.w_l, "fm_gamma": self.fm_gamma, "fm_beta": self.fm_beta,
+                "mlp_w": self.mlp_w, "mlp_b": self.mlp_b, "out_gamma": self.out_gamma, "out_beta": self.out_beta}
+
+
+def layer_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layer: DeviceLayer,
+                   grads: Optional[LayerGrads] = None, dx: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None, trace: "Trace" = None):
+    """Backward of one bf16 layer: returns (dx, grads) from x, the training forward's saved buffer and dy."""
+    lib = load_library()
+    B = _check_x(x, layer.spec)
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
+        raise ValueError("dy must be contiguous and shaped like x")
+    grads = LayerGrads(layer) if grads is None else grads
+    dx = torch.empty_like(x) if dx is None else dx
+    need = layer_backward_workspace_size(layer.spec, B)
+    if need == 0:
+        raise WukongError(WK_ERR_UNSUPPORTED, "wukong_layer_backward_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    args = [ctypes.byref(layer.desc), ctypes.byref(layer.weights), B, x.data_ptr(), saved.data_ptr(),
+            dy.data_ptr(), dx.data_ptr(), ctypes.byref(grads.c), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream)]
+    if trace is None:
+        _check(lib.wukong_layer_backward(*args), "wukong_layer_backward")
+    else:
+        _check(lib.wukong_layer_backward_traced(*args, trace.handle), "wukong_layer_backward_traced")
+    return dx, grads
 
 
 class Trace:

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libwukong.so")
 
 SOURCES = ["wukong_abi.cpp", "fmb_lcb.hip", "fmb_lcb_stream.hip", "linear_bf16.hip", "resid_ln.hip",
            "fp32_path.hip", "head.hip",
-           "fmb_lcb_units.hip", "whale_fusion.hip"]
+           "fmb_lcb_units.hip", "whale_fusion.hip", "wukong_backward.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror",

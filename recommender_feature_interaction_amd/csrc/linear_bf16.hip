@@ -45,9 +45,16 @@ struct LinearKArgs {
   int64_t M;
   int N, K;
   int act;                // LinearAct
-  const uint16_t* res;    // [M, N] added after the activation, or null
+  const uint16_t* res;    // [M, N] added after the activation (kActReluMask: the mask), or null
   int tiles_m, tiles_n;
 };
+
+// The residual input: added after the activation, or, for kActReluMask, the
+// mask source (outputs where it is not positive become 0).
+__device__ __forceinline__ float apply_res(float v, float r, int act) {
+  if (act == kActReluMask) return r > 0.f ? v : 0.f;
+  return v + r;
+}
 
 __device__ __forceinline__ float apply_act(float v, int act) {
   if (act == kActRelu) return fmaxf(v, 0.f);
@@ -276,7 +283,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
         for (int t = 0; t < 4; ++t) v[t] = apply_act(acc[i][j][t] + bb[t], p.act);
         if (p.res != nullptr) {
           const u32x2 r2 = *reinterpret_cast<const u32x2*>(p.res + m * N + n);
-          v[0] += bf16lo(r2[0]); v[1] += bf16hi(r2[0]); v[2] += bf16lo(r2[1]); v[3] += bf16hi(r2[1]);
+          v[0] = apply_res(v[0], bf16lo(r2[0]), p.act);
+          v[1] = apply_res(v[1], bf16hi(r2[0]), p.act);
+          v[2] = apply_res(v[2], bf16lo(r2[1]), p.act);
+          v[3] = apply_res(v[3], bf16hi(r2[1]), p.act);
         }
         u32x2 o;
         o[0] = pack_bf16x2(v[0], v[1]);
@@ -365,8 +375,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
     for (int t = 0; t < 4; ++t) {
       float x0 = apply_act(v[2 * t], act), x1 = apply_act(v[2 * t + 1], act);
       if (res != nullptr) {
-        x0 += bf16lo(rr[t]);
-        x1 += bf16hi(rr[t]);
+        x0 = apply_res(x0, bf16lo(rr[t]), act);
+        x1 = apply_res(x1, bf16hi(rr[t]), act);
       }
       o[t] = pack_bf16x2(x0, x1);
     }
@@ -638,7 +648,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_bf16_kernel(LinearKArgs
           for (int t = 0; t < 4; ++t) v[t] = apply_act(acc[i][j][q * 4 + t] + bb[t], p.act);
           if (p.res != nullptr) {
             const u32x2 r2 = *reinterpret_cast<const u32x2*>(p.res + m * N + n);
-            v[0] += bf16lo(r2[0]); v[1] += bf16hi(r2[0]); v[2] += bf16lo(r2[1]); v[3] += bf16hi(r2[1]);
+            v[0] = apply_res(v[0], bf16lo(r2[0]), p.act);
+            v[1] = apply_res(v[1], bf16hi(r2[0]), p.act);
+            v[2] = apply_res(v[2], bf16lo(r2[1]), p.act);
+            v[3] = apply_res(v[3], bf16hi(r2[1]), p.act);
           }
           u32x2 o;
           o[0] = pack_bf16x2(v[0], v[1]);
@@ -831,6 +844,49 @@ hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t 
   hipLaunchKernelGGL((linear_splitk_kernel<256, 256, 2, 4, false>), dim3((unsigned)blocks), dim3(512), 0, stream, k, c,
                      1);
   return hipGetLastError();
+}
+
+// Split-K form of the fp32-output product for shapes whose 256 x 256 tiles
+// leave CUs idle: splits double while tiles x splits < CUs, each split keeps
+// a multiple of 64 of K and at least 1024 of it.
+int linear_bf16_f32out_splits(int64_t M, int N, int K) {
+  if (!linear_bf16_f32out_supported(M, N, K)) return 1;
+  const double tiles = (double)((M + 255) / 256) * (double)((N + 255) / 256);
+  int sp = 1;
+  while (sp < kMaxSplits && tiles * sp < (double)kNumCU && K % (2 * sp * kBK) == 0 && K / (2 * sp) >= 1024) sp *= 2;
+  return sp;
+}
+
+size_t linear_bf16_f32out_split_bytes(int64_t M, int N, int K) {
+  const int sp = linear_bf16_f32out_splits(M, N, K);
+  return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+hipError_t launch_linear_bf16_f32out_split(const LinearArgs& a, float* c, float* partial, hipStream_t stream,
+                                           int64_t* workgroups) {
+  const int sp = linear_bf16_f32out_splits(a.M, a.N, a.K);
+  if (sp <= 1) return launch_linear_bf16_f32out(a, c, stream, workgroups);
+  if (c == nullptr || partial == nullptr) return hipErrorInvalidValue;
+  LinearKArgs k;
+  k.a = static_cast<const uint16_t*>(a.a);
+  k.w = static_cast<const uint16_t*>(a.w);
+  k.bias = nullptr;
+  k.c = nullptr;
+  k.M = a.M;
+  k.N = a.N;
+  k.K = a.K;
+  k.act = kActNone;
+  k.res = nullptr;
+  k.tiles_m = (int)((a.M + 255) / 256);
+  k.tiles_n = (a.N + 255) / 256;
+  const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n * sp;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (workgroups) *workgroups = blocks;
+  hipLaunchKernelGGL((linear_splitk_kernel<256, 256, 2, 4, false>), dim3((unsigned)blocks), dim3(512), 0, stream, k,
+                     partial, sp);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_sum_planes(partial, sp, a.M * (int64_t)a.N, c, stream);
 }
 
 bool linear_bf16_supported(int64_t M, int N, int K) {

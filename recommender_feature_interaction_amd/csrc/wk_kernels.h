@@ -67,7 +67,9 @@ hipError_t launch_fmb_lcb_f32(const FmbLcbF32Args& a, int64_t batch, hipStream_t
 // Activation applied after the bias: none, ReLU, or the shared-gate SwiGLU
 // u * silu(u) (gate and up projection are one matrix).  bf16 kernels take
 // all three; the fp32 kernel takes none and ReLU.
-enum LinearAct { kActNone = 0, kActRelu = 1, kActSiluGate = 2 };
+// kActReluMask is the ReLU's backward: no activation, and `res` is the
+// forward activation whose non-positive entries zero the output.
+enum LinearAct { kActNone = 0, kActRelu = 1, kActSiluGate = 2, kActReluMask = 3 };
 struct LinearArgs {
   const void* a;
   const void* w;
@@ -76,7 +78,7 @@ struct LinearArgs {
   int64_t M;
   int N, K;
   int act;
-  const void* res = nullptr;  // bf16 only: [M, N] added after the activation, or null
+  const void* res = nullptr;  // bf16 only: [M, N] added after the activation (the mask for kActReluMask), or null
 };
 bool linear_bf16_supported(int64_t M, int N, int K);
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);
@@ -91,6 +93,17 @@ hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStr
 // C = A W^T in fp32 (no bias, no activation), K % 64 == 0, N % 8 == 0.
 bool linear_bf16_f32out_supported(int64_t M, int N, int K);
 hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t stream, int64_t* workgroups);
+// The same with K split when the tiles leave CUs idle: the fp32 partials
+// (linear_bf16_f32out_split_bytes(), 0 when unsplit) are summed in split order.
+int linear_bf16_f32out_splits(int64_t M, int N, int K);
+size_t linear_bf16_f32out_split_bytes(int64_t M, int N, int K);
+hipError_t launch_linear_bf16_f32out_split(const LinearArgs& a, float* c, float* partial, hipStream_t stream,
+                                           int64_t* workgroups);
+// out[j] = sum over p = 0, 1, .. planes-1 of part[p * len + j], in that order (fp32).
+hipError_t launch_sum_planes(const float* part, int planes, int64_t len, float* out, hipStream_t stream);
+// out[j] = sum over p of part[p * stride + j], j < len <= stride.
+hipError_t launch_sum_planes_strided(const float* part, int planes, int64_t stride, int64_t len, float* out,
+                                     hipStream_t stream);
 
 // The last Linear with the FMB rows' output stage fused in (bf16):
 // Y[b, r] = LN_d(bf16(A[b] W^T + bias)[r d .. r d + d) + X[b, r]) for r < n_f,
@@ -125,6 +138,49 @@ struct ResidLnArgs {
 bool resid_ln_bf16_supported(int d);
 hipError_t launch_resid_ln_bf16(const ResidLnArgs& a, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_resid_ln_f32(const ResidLnArgs& a, hipStream_t stream, int64_t* workgroups);
+
+// Backward pass of one bf16 layer (wukong_backward.hip).  The per-example
+// kernels need wukong_bwd_supported(n, d, k, n_l); each launches
+// wukong_bwd_workgroups(batch) workgroups and writes one fp32 plane of weight
+// gradient sums per workgroup into `part` (launch_sum_planes adds them).
+bool wukong_bwd_supported(int n, int d, int k, int n_l);
+int wukong_bwd_workgroups(int64_t batch);
+size_t wukong_bwd_out_part_floats(int d);                   // [2 d]: sum dY R_hat, sum dY
+size_t wukong_bwd_fmb_part_floats(int n, int k, int n_l);   // [k n + n_l n + 2 n k]
+struct BwdOutArgs {
+  const void* x;      // [B, n, d]
+  const void* m;      // [B, n_f, d] the forward's M
+  const void* dy;     // [B, n, d]
+  const void* w_l;    // [n_l, n]
+  const void* gamma;  // [d] output LayerNorm scale, or null
+  void* dm;           // [B, n_f, d] out: dR rows < n_f
+  void* dlc;          // [B, n_l, d] out: dR rows >= n_f
+  float* part;        // [workgroups, 2 d]
+  int64_t batch;
+  int n, d, n_l;
+  float eps;
+};
+hipError_t launch_bwd_out(const BwdOutArgs& a, hipStream_t stream, int64_t* workgroups);
+struct BwdFmbArgs {
+  const void* x;         // [B, n, d]
+  const void* dfn;       // [B, n k] gradient of the normalised interaction
+  const void* dm;        // [B, n_f, d]
+  const void* dlc;       // [B, n_l, d]
+  const void* phi;       // [k, n]
+  const void* w_l;       // [n_l, n]
+  const void* fm_gamma;  // [n k] or null
+  void* dx;              // [B, n, d] out
+  float* part;           // [workgroups, k n + n_l n + 2 n k]
+  int64_t batch;
+  int n, d, k, n_l;
+  float eps;
+};
+hipError_t launch_bwd_fmb(const BwdFmbArgs& a, hipStream_t stream, int64_t* workgroups);
+// at[c][r] = a[r][c] (a: [R, C] bf16, C % 8 == 0), zero for R <= r < Rp
+// (Rp % 8 == 0); colpart (or null) gets ceil(Rp / 64) planes of per-64-row
+// column sums, [plane][C] fp32.
+hipError_t launch_transpose_bf16(const void* a, int64_t R, int C, int64_t Rp, void* at, float* colpart,
+                                 hipStream_t stream, int64_t* workgroups);
 
 // The prediction head's last Linear + logistic function (head.hip):
 // prob[m, o] = 1 / (1 + exp(-(A[m] . W[o] + bias[o]))), fp32 out.

@@ -73,6 +73,8 @@ int32_t check_desc(const wk_layer_desc* d) {
 struct LayerPlan {
   size_t fn = 0, h[2] = {0, 0}, m = 0, units = 0, bytes = 0;
   int num_hidden_bufs = 0;
+  bool keep_hidden = false;  // h_{t+1} goes to hid[t] (the training forward keeps them all)
+  size_t hid[kMaxLinear] = {};
   bool fused_out = false;  // last Linear writes the FMB rows of Y itself; no M buffer
   bool use_units = false;  // d = 8: the FMB+LCB step runs as transpose + batched GEMM + epilogue
 };
@@ -206,7 +208,8 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
   const int unfused = plan.fused_out ? d.num_linear - 1 : d.num_linear;
   for (int t = 0; t < unfused; ++t) {
     const bool last = t == d.num_linear - 1;
-    void* out = last ? static_cast<void*>(mbuf) : static_cast<void*>(scratch + plan.h[t % 2]);
+    void* out = last ? static_cast<void*>(mbuf)
+                     : static_cast<void*>(scratch + (plan.keep_hidden ? plan.hid[t] : plan.h[t % 2]));
     wk::LinearArgs a;
     a.a = in;
     a.w = w.mlp_w[t];
@@ -499,6 +502,258 @@ int32_t fusion_forward(const wk_fusion_desc* d, const wk_fusion_weights* w, int6
   return linear(2, g, w->w_down, w->b_down, hf, d->d, d->d_ff, wk::kActNone, q);
 }
 
+// ---- backward of one bf16 layer.
+int32_t check_backward_desc(const wk_layer_desc* d) {
+  const int32_t st = check_desc(d);
+  if (st != WK_OK) return st;
+  if (d->dtype != WK_BF16 || !wk::wukong_bwd_supported(d->n, d->d, d->k, d->n_l)) return WK_ERR_UNSUPPORTED;
+  return WK_OK;
+}
+
+// Saved activations of the training forward: Fn, h_1 .. h_{T-1}, M.
+LayerPlan plan_saved(const wk_layer_desc& d, int64_t batch) {
+  LayerPlan p;
+  const size_t B = (size_t)batch;
+  size_t off = 0;
+  p.fn = off;
+  off += align_up(B * d.n * d.k * 2);
+  p.keep_hidden = true;
+  for (int t = 0; t + 1 < d.num_linear; ++t) {
+    p.hid[t] = off;
+    off += align_up(B * (size_t)d.mlp_dims[t + 1] * 2);
+  }
+  p.m = off;
+  off += align_up(B * (size_t)d.n_f * d.d * 2);
+  p.bytes = off;
+  return p;
+}
+
+int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
+
+struct BackwardPlan {
+  size_t dm = 0, dlc = 0, g[2] = {0, 0}, dfn = 0, gt = 0, at = 0, wt = 0, colpart = 0, split = 0, part_out = 0,
+         part_fmb = 0, bytes = 0;
+};
+
+BackwardPlan plan_backward(const wk_layer_desc& d, int64_t batch) {
+  BackwardPlan p;
+  const size_t B = (size_t)batch, Bp = (size_t)pad64(batch);
+  const int T = d.num_linear;
+  size_t maxhid = 0, maxw = 0, maxsplit = 0, maxdim = 0;
+  for (int t = 0; t < T; ++t) {
+    const size_t mi = (size_t)d.mlp_dims[t], mo = (size_t)d.mlp_dims[t + 1];
+    if (t > 0) maxhid = mi > maxhid ? mi : maxhid;
+    maxw = mi * mo > maxw ? mi * mo : maxw;
+    maxdim = mi > maxdim ? mi : maxdim;
+    maxdim = mo > maxdim ? mo : maxdim;
+    const size_t sb = wk::linear_bf16_f32out_split_bytes((int64_t)mo, (int)mi, (int64_t)Bp);
+    maxsplit = sb > maxsplit ? sb : maxsplit;
+  }
+  const size_t wg = (size_t)wk::wukong_bwd_workgroups(batch);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  p.dm = take(B * d.n_f * d.d * 2);
+  p.dlc = take(B * d.n_l * d.d * 2);
+  p.g[0] = take(B * maxhid * 2);
+  p.g[1] = take(B * maxhid * 2);
+  p.dfn = take(B * d.n * d.k * 2);
+  p.gt = take(maxdim * Bp * 2);
+  p.at = take(maxdim * Bp * 2);
+  p.wt = take(maxw * 2);
+  p.colpart = take((Bp / 64) * maxdim * 4);
+  p.split = take(maxsplit);
+  p.part_out = take(wg * wk::wukong_bwd_out_part_floats(d.d) * 4);
+  p.part_fmb = take(wg * wk::wukong_bwd_fmb_part_floats(d.n, d.k, d.n_l) * 4);
+  p.bytes = off;
+  return p;
+}
+
+int32_t layer_forward_train(const wk_layer_desc* d, const wk_layer_weights* w, int64_t batch, const void* x, void* y,
+                            void* saved, size_t saved_bytes, void* stream) {
+  int32_t st = check_backward_desc(d);
+  if (st != WK_OK) return st;
+  if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
+  st = check_weights(*d, w);
+  if (st != WK_OK) return st;
+  if (batch == 0) return WK_OK;
+  const size_t act = (size_t)batch * d->n * d->d * 2;
+  const LayerPlan sp = plan_saved(*d, batch);
+  if (!x || !y || !saved || !aligned16(x) || !aligned16(y) || !aligned16(saved)) return WK_ERR_INVALID_ARG;
+  if (saved_bytes < sp.bytes) return WK_ERR_WORKSPACE;
+  if (overlap(x, act, y, act) || overlap(saved, sp.bytes, x, act) || overlap(saved, sp.bytes, y, act))
+    return WK_ERR_INVALID_ARG;
+  Launch launch{nullptr, static_cast<hipStream_t>(stream)};
+  return run_layer(*d, *w, batch, x, y, static_cast<char*>(saved), sp, launch, 0);
+}
+
+int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_t batch, const void* x,
+                       const void* saved, const void* dy, void* dx, const wk_layer_grads* gr, void* ws,
+                       size_t ws_bytes, void* stream, wk_trace* trace) {
+  int32_t st = check_backward_desc(d);
+  if (st != WK_OK) return st;
+  if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
+  st = check_weights(*d, w);
+  if (st != WK_OK) return st;
+  const int T = d->num_linear;
+  if (!gr || !gr->phi || !gr->w_l || !gr->mlp_w) return WK_ERR_INVALID_ARG;
+  for (int t = 0; t < T; ++t)
+    if (!gr->mlp_w[t]) return WK_ERR_INVALID_ARG;
+  if (batch == 0) return WK_OK;
+  const size_t act = (size_t)batch * d->n * d->d * 2;
+  const LayerPlan sv = plan_saved(*d, batch);
+  const BackwardPlan bp = plan_backward(*d, batch);
+  if (!x || !saved || !dy || !dx) return WK_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(saved) || !aligned16(dy) || !aligned16(dx)) return WK_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return WK_ERR_INVALID_ARG;
+  if (ws_bytes < bp.bytes) return WK_ERR_WORKSPACE;
+  if (overlap(dx, act, x, act) || overlap(dx, act, dy, act) || overlap(dx, act, saved, sv.bytes) ||
+      overlap(dx, act, ws, bp.bytes) || overlap(ws, bp.bytes, x, act) || overlap(ws, bp.bytes, dy, act) ||
+      overlap(ws, bp.bytes, saved, sv.bytes))
+    return WK_ERR_INVALID_ARG;
+
+  char* base = static_cast<char*>(ws);
+  const char* sbase = static_cast<const char*>(saved);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Launch launch{trace, s};
+  const int64_t Bp = pad64(batch);
+  const int wg = wk::wukong_bwd_workgroups(batch);
+  void* dm = base + bp.dm;
+  void* dlc = base + bp.dlc;
+  float* part_out = reinterpret_cast<float*>(base + bp.part_out);
+  float* part_fmb = reinterpret_cast<float*>(base + bp.part_fmb);
+
+  // output LayerNorm + LCB rows: dR -> dM, dLc
+  wk::BwdOutArgs oa;
+  oa.x = x;
+  oa.m = sbase + sv.m;
+  oa.dy = dy;
+  oa.w_l = w->w_l;
+  oa.gamma = w->out_ln_gamma;
+  oa.dm = dm;
+  oa.dlc = dlc;
+  oa.part = part_out;
+  oa.batch = batch;
+  oa.n = d->n;
+  oa.d = d->d;
+  oa.n_l = d->n_l;
+  oa.eps = d->ln_eps;
+  st = launch(WK_KERNEL_BWD_OUT, 0, 0, [&](int64_t* g) { return wk::launch_bwd_out(oa, s, g); });
+  if (st != WK_OK) return st;
+  const int64_t po = (int64_t)wk::wukong_bwd_out_part_floats(d->d);
+  if (gr->out_ln_gamma) {
+    st = launch(WK_KERNEL_BWD_REDUCE, 0, 0, [&](int64_t* g) {
+      *g = 1;
+      return wk::launch_sum_planes_strided(part_out, wg, po, d->d, gr->out_ln_gamma, s);
+    });
+    if (st != WK_OK) return st;
+  }
+  if (gr->out_ln_beta) {
+    st = launch(WK_KERNEL_BWD_REDUCE, 0, 1, [&](int64_t* g) {
+      *g = 1;
+      return wk::launch_sum_planes_strided(part_out + d->d, wg, po, d->d, gr->out_ln_beta, s);
+    });
+    if (st != WK_OK) return st;
+  }
+
+  // MLP, last Linear first: g_{t+1} -> dW_t, db_t, g_t
+  const void* g_next = dm;
+  void* gt = base + bp.gt;
+  void* at = base + bp.at;
+  void* wt = base + bp.wt;
+  float* colpart = reinterpret_cast<float*>(base + bp.colpart);
+  float* split = reinterpret_cast<float*>(base + bp.split);
+  for (int t = T - 1; t >= 0; --t) {
+    const int mi = d->mlp_dims[t], mo = d->mlp_dims[t + 1];
+    const void* a_t = t == 0 ? static_cast<const void*>(sbase + sv.fn) : static_cast<const void*>(sbase + sv.hid[t - 1]);
+    float* db = gr->mlp_b ? gr->mlp_b[t] : nullptr;
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, t, [&](int64_t* g) {
+      return wk::launch_transpose_bf16(g_next, batch, mo, Bp, gt, db ? colpart : nullptr, s, g);
+    });
+    if (st != WK_OK) return st;
+    if (db) {
+      st = launch(WK_KERNEL_BWD_REDUCE, 0, 2 + t, [&](int64_t* g) {
+        *g = 1;
+        return wk::launch_sum_planes(colpart, (int)(Bp / 64), mo, db, s);
+      });
+      if (st != WK_OK) return st;
+    }
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, t, [&](int64_t* g) {
+      return wk::launch_transpose_bf16(a_t, batch, mi, Bp, at, nullptr, s, g);
+    });
+    if (st != WK_OK) return st;
+    wk::LinearArgs wa;
+    wa.a = gt;
+    wa.w = at;
+    wa.bias = nullptr;
+    wa.c = nullptr;
+    wa.M = mo;
+    wa.N = mi;
+    wa.K = (int)Bp;
+    wa.act = wk::kActNone;
+    st = launch(WK_KERNEL_BWD_WGRAD, 0, t, [&](int64_t* g) {
+      return wk::launch_linear_bf16_f32out_split(wa, gr->mlp_w[t], split, s, g);
+    });
+    if (st != WK_OK) return st;
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, t, [&](int64_t* g) {
+      return wk::launch_transpose_bf16(w->mlp_w[t], mo, mi, mo, wt, nullptr, s, g);
+    });
+    if (st != WK_OK) return st;
+    void* g_out = t == 0 ? static_cast<void*>(base + bp.dfn) : static_cast<void*>(base + bp.g[t % 2]);
+    wk::LinearArgs da;
+    da.a = g_next;
+    da.w = wt;
+    da.bias = nullptr;
+    da.c = g_out;
+    da.M = batch;
+    da.N = mi;
+    da.K = mo;
+    da.act = t == 0 ? wk::kActNone : wk::kActReluMask;
+    da.res = t == 0 ? nullptr : a_t;
+    st = launch(WK_KERNEL_BWD_DGRAD, 0, t, [&](int64_t* g) { return wk::launch_linear_bf16(da, s, g); });
+    if (st != WK_OK) return st;
+    g_next = g_out;
+  }
+
+  // FM LayerNorm, interaction, compression: dX and the FMB / LCB weight sums
+  wk::BwdFmbArgs fa;
+  fa.x = x;
+  fa.dfn = base + bp.dfn;
+  fa.dm = dm;
+  fa.dlc = dlc;
+  fa.phi = w->phi;
+  fa.w_l = w->w_l;
+  fa.fm_gamma = w->fm_ln_gamma;
+  fa.dx = dx;
+  fa.part = part_fmb;
+  fa.batch = batch;
+  fa.n = d->n;
+  fa.d = d->d;
+  fa.k = d->k;
+  fa.n_l = d->n_l;
+  fa.eps = d->ln_eps;
+  st = launch(WK_KERNEL_BWD_FMB, 0, 0, [&](int64_t* g) { return wk::launch_bwd_fmb(fa, s, g); });
+  if (st != WK_OK) return st;
+  const int64_t pf = (int64_t)wk::wukong_bwd_fmb_part_floats(d->n, d->k, d->n_l);
+  const int64_t kn = (int64_t)d->k * d->n, ln = (int64_t)d->n_l * d->n, nk = (int64_t)d->n * d->k;
+  struct Out {
+    float* dst;
+    int64_t off, len;
+  } outs[4] = {{gr->phi, 0, kn}, {gr->w_l, kn, ln}, {gr->fm_ln_gamma, kn + ln, nk}, {gr->fm_ln_beta, kn + ln + nk, nk}};
+  for (int i = 0; i < 4; ++i) {
+    if (!outs[i].dst) continue;
+    st = launch(WK_KERNEL_BWD_REDUCE, 0, 2 + T + i, [&](int64_t* g) {
+      *g = 1;
+      return wk::launch_sum_planes_strided(part_fmb + outs[i].off, wg, pf, outs[i].len, outs[i].dst, s);
+    });
+    if (st != WK_OK) return st;
+  }
+  return WK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -649,6 +904,37 @@ int32_t wukong_fusion_forward_traced(const wk_fusion_desc* desc, const wk_fusion
                                      size_t workspace_bytes, void* stream, wk_trace* trace) {
   if (!trace) return WK_ERR_INVALID_ARG;
   return fusion_forward(desc, weights, batch, hw, hs, hf, workspace, workspace_bytes, stream, trace);
+}
+
+size_t wukong_layer_saved_size(const wk_layer_desc* desc, int64_t batch) {
+  if (check_backward_desc(desc) != WK_OK || batch < 0 || batch > kMaxBatch) return 0;
+  const size_t b = plan_saved(*desc, batch).bytes;
+  return b ? b : kAlign;
+}
+
+int32_t wukong_layer_forward_train(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                                   const void* x, void* y, void* saved, size_t saved_bytes, void* stream) {
+  return layer_forward_train(desc, weights, batch, x, y, saved, saved_bytes, stream);
+}
+
+size_t wukong_layer_backward_workspace_size(const wk_layer_desc* desc, int64_t batch) {
+  if (check_backward_desc(desc) != WK_OK || batch < 0 || batch > kMaxBatch) return 0;
+  const size_t b = plan_backward(*desc, batch).bytes;
+  return b ? b : kAlign;
+}
+
+int32_t wukong_layer_backward(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                              const void* x, const void* saved, const void* dy, void* dx,
+                              const wk_layer_grads* grads, void* workspace, size_t workspace_bytes, void* stream) {
+  return layer_backward(desc, weights, batch, x, saved, dy, dx, grads, workspace, workspace_bytes, stream, nullptr);
+}
+
+int32_t wukong_layer_backward_traced(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                                     const void* x, const void* saved, const void* dy, void* dx,
+                                     const wk_layer_grads* grads, void* workspace, size_t workspace_bytes,
+                                     void* stream, wk_trace* trace) {
+  if (!trace) return WK_ERR_INVALID_ARG;
+  return layer_backward(desc, weights, batch, x, saved, dy, dx, grads, workspace, workspace_bytes, stream, trace);
 }
 
 int32_t wukong_head_forward_traced(const wk_head_desc* desc, const wk_head_weights* weights, int64_t batch,

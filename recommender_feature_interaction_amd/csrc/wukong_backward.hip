@@ -1,0 +1,720 @@
+// Backward pass of one Wukong layer in bf16 (fp32 accumulation): the two
+// per-example kernels around the MLP's backward, and the transpose and
+// reduction kernels the MLP's weight gradients use.
+//
+// The forward (Wukong paper, section 2.2, xdnf.cn repost): Z = Phi X,
+// F = X Z^T, Fn = LN(vec F), MLP -> M, Lc = W_L X, Y = LN_d([M; Lc] + X).
+// Its gradients, by the chain rule through those steps in reverse:
+//
+//  bwd_out_kernel (before the MLP's backward), per example: recompute Lc with
+//    MFMA (W_L and X in LDS), R = [M; Lc] + X row by row, and the output
+//    LayerNorm's input gradient
+//        dR = rstd (g - mean(g) - R_hat mean(g R_hat)),   g = dY gamma_out,
+//    stored in bf16 as dM (rows < n_F, the MLP's upstream gradient) and dLc;
+//    per-workgroup sums of dY R_hat and dY (gamma_out / beta_out gradients).
+//  bwd_fmb_kernel (after the MLP's backward has produced d_Fn), per example:
+//    recompute Z = Phi X and F = X Z^T with MFMA, the FM LayerNorm's
+//    statistics, dF = rstd (q - mean(q) - F_tilde mean(q F_tilde)) with
+//    q = d_Fn gamma_fm, dZ = dF^T X, and
+//        dX = dR + [dF | Phi^T | W_L^T] [Z; dZ; dLc]      (one MFMA product)
+//    plus per-workgroup sums of dZ X^T (d_Phi), dLc X^T (d_W_L), d_Fn F_tilde
+//    and d_Fn (gamma_fm / beta_fm gradients).
+//
+// One workgroup of 8 waves walks examples blockIdx.x, + gridDim.x, ... and
+// keeps the weight-gradient sums of its examples in registers; the host then
+// adds the per-workgroup planes in a fixed order (launch_sum_planes), so every
+// result is independent of timing.  X of one example, the LDS copies of Phi
+// and W_L and the per-example operands all live in LDS (up to 160 KB per
+// workgroup on gfx950): the shapes this covers are those whose LDS plan and
+// per-wave tile counts fit (wukong_bwd_supported).
+//
+// MFMA operands (v_mfma_f32_16x16x32_bf16, lane l = 16 lg + li): row_op reads
+// the 8 consecutive columns 8 lg .. of row li of a row-major LDS array (an
+// operand whose contraction index runs along rows of the array), tr_op uses
+// ds_read_b64_tr_b16 to read 8 consecutive rows 8 lg .. at column li (an
+// operand whose contraction index runs down the array's columns).  Padding
+// rows and columns of every LDS array are zero, so contraction lengths round
+// up to 32 freely.
+#include <math.h>
+
+#include "wk_device.h"
+#include "wk_kernels.h"
+
+namespace wk {
+
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+#define WB_LDS_I16X4(p) ((__attribute__((address_space(3))) i16x4*)(p))
+
+constexpr int BW = 8;            // waves per workgroup
+constexpr int BT = BW * kWave;   // threads per workgroup
+constexpr int kLdsMax = 160 * 1024;
+// bwd_fmb_kernel variants: at most QF F tiles, QP d_Phi tiles and QL d_W_L
+// tiles (16 x 16) per wave; the smallest that fits the shape is launched.
+constexpr int kQF[2] = {2, 4}, kQP[2] = {2, 4}, kQL[2] = {4, 8};
+
+__host__ __device__ constexpr int up16(int v) { return (v + 15) / 16 * 16; }
+__host__ __device__ constexpr int up32(int v) { return (v + 31) / 32 * 32; }
+
+__device__ __forceinline__ u32x4 row_op(const uint16_t* base, int pitch, int r0, int c0, int li, int lg) {
+  return *reinterpret_cast<const u32x4*>(base + (r0 + li) * pitch + c0 + 8 * lg);
+}
+
+// Lane (li, lg) addresses row r0 + 8 lg + li / 4, columns c0 + 4 (li % 4) ..;
+// the transposing read hands it rows r0 + 8 lg .. + 3 of column c0 + li, and
+// the second read (4 rows further) rows + 4 .. + 7.
+__device__ __forceinline__ u32x4 tr_op(const uint16_t* base, int pitch, int r0, int c0, int li, int lg) {
+  const uint16_t* p0 = base + (r0 + 8 * lg + (li >> 2)) * pitch + c0 + 4 * (li & 3);
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WB_LDS_I16X4(p0));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WB_LDS_I16X4(p0 + 4 * pitch));
+  const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+  return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float v) { return (uint16_t)f32_to_bf16(v); }
+
+// Sum of one value per thread over the workgroup; every thread gets it.
+// red holds BW floats; two barriers keep back-to-back calls from racing.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = xor_sum<1>(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < BW; ++w) s += red[w];
+  __syncthreads();
+  return s;
+}
+
+__device__ __forceinline__ void zero_lds(uint16_t* base, int bytes) {
+  for (int i = threadIdx.x * 16; i < bytes; i += BT * 16)
+    *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + i) = u32x4{0u, 0u, 0u, 0u};
+}
+
+// rows [0, rows) x cols [0, cols) of a row-major global bf16 matrix (cols % 8 == 0) into LDS at pitch
+__device__ __forceinline__ void load_rows(uint16_t* dst, int pitch, const uint16_t* src, int rows, int cols) {
+  const int c8 = cols / 8;
+  for (int q = threadIdx.x; q < rows * c8; q += BT) {
+    const int r = q / c8, c = (q - r * c8) * 8;
+    *reinterpret_cast<u32x4*>(dst + r * pitch + c) = *reinterpret_cast<const u32x4*>(src + (int64_t)r * cols + c);
+  }
+}
+
+// ---------------------------------------------------------------- LDS plans
+struct OutPlan {  // bwd_out_kernel
+  int n32, pd, pn, nlp, g;
+  int xs, wl, ls, red, bytes;  // byte offsets
+};
+
+__host__ __device__ inline int pow2_at_least(int v) {
+  int g = 1;
+  while (g < v) g <<= 1;
+  return g;
+}
+
+__host__ __device__ inline OutPlan out_plan(int n, int d, int n_l) {
+  OutPlan p;
+  p.n32 = up32(n);
+  p.pd = up32(d) + 8;
+  p.pn = p.n32 + 8;
+  p.nlp = up16(n_l);
+  p.g = pow2_at_least((d + 7) / 8);
+  p.xs = 0;
+  p.wl = p.xs + p.n32 * p.pd * 2;
+  p.ls = p.wl + p.nlp * p.pn * 2;
+  p.red = p.ls + p.nlp * d * 4;
+  p.bytes = p.red + BW * 2 * d * 4;
+  return p;
+}
+
+struct FmbPlan {  // bwd_fmb_kernel
+  int n16, n32, dp, pd, pn, kp, nlp, ka;
+  int xs, as, bs, red, bytes;
+};
+
+__host__ __device__ inline FmbPlan fmb_plan(int n, int d, int k, int n_l) {
+  FmbPlan p;
+  p.n16 = up16(n);
+  p.n32 = up32(n);
+  p.dp = up32(d);
+  p.pd = p.dp + 8;
+  p.pn = p.n32 + 8;
+  p.kp = up16(k);
+  p.nlp = up16(n_l);
+  p.ka = up32(2 * p.kp + p.nlp);
+  p.xs = 0;
+  p.as = p.xs + p.n32 * p.pd * 2;
+  p.bs = p.as + p.ka * p.pn * 2;
+  p.red = p.bs + p.ka * p.pd * 2;
+  p.bytes = p.red + 4 * BW * 4;
+  return p;
+}
+
+// ---------------------------------------------------------------- phase A
+struct BwdOutKArgs {
+  const uint16_t* x;      // [B, n, d]
+  const uint16_t* m;      // [B, n_f, d]
+  const uint16_t* dy;     // [B, n, d]
+  const uint16_t* w_l;    // [n_l, n]
+  const uint16_t* gamma;  // [d] or null
+  uint16_t* dm;           // [B, n_f, d]
+  uint16_t* dlc;          // [B, n_l, d]
+  float* part;            // [gridDim.x, 2 d]
+  int64_t batch;
+  int n, d, n_f, n_l;
+  float eps;
+};
+
+template <int G>
+__global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int n = p.n, d = p.d, n_f = p.n_f, n_l = p.n_l;
+  const OutPlan pl = out_plan(n, d, n_l);
+  uint16_t* Xs = smem + pl.xs / 2;
+  uint16_t* WLs = smem + pl.wl / 2;
+  float* Ls = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + pl.ls);
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + pl.red);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  constexpr int RPW = kWave / G;  // rows per wave and pass
+  const int grp = lane / G, c = (lane % G) * 8;
+  const bool col_ok = c < d;
+
+  zero_lds(smem, pl.ls);
+  __syncthreads();
+  load_rows(WLs, pl.pn, p.w_l, n_l, n);
+
+  float gam[8], pg[8], pb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    gam[j] = (p.gamma != nullptr && col_ok) ? bf16_to_f32(p.gamma[c + j]) : 1.f;
+    pg[j] = 0.f;
+    pb[j] = 0.f;
+  }
+  const int dt = d / 16, tiles = (pl.nlp / 16) * dt;
+  const float inv_d = 1.f / (float)d;
+
+  for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
+    load_rows(Xs, pl.pd, p.x + b * n * d, n, d);
+    __syncthreads();
+    // Lc = W_L X -> Ls (fp32)
+    for (int t = wave; t < tiles; t += BW) {
+      const int rb = t / dt, cb = t - rb * dt;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < pl.n32; k0 += 32)
+        acc = mfma16x16x32(row_op(WLs, pl.pn, rb * 16, k0, li, lg), tr_op(Xs, pl.pd, k0, cb * 16, li, lg), acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rb * 16 + 4 * lg + q;
+        if (r < n_l) Ls[r * d + cb * 16 + li] = acc[q];
+      }
+    }
+    __syncthreads();
+    // rows: R = [M; Lc] + X, LayerNorm backward
+    for (int r = wave * RPW + grp; r < n; r += BW * RPW) {
+      float R[8], dyv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) R[j] = dyv[j] = 0.f;
+      if (col_ok) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(Xs + r * pl.pd + c);
+        const u32x4 yv = *reinterpret_cast<const u32x4*>(p.dy + (b * n + r) * d + c);
+        if (r < n_f) {
+          const u32x4 mv = *reinterpret_cast<const u32x4*>(p.m + (b * n_f + r) * d + c);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            R[2 * j] = bf16lo(mv[j]) + bf16lo(xv[j]);
+            R[2 * j + 1] = bf16hi(mv[j]) + bf16hi(xv[j]);
+          }
+        } else {
+          const float* lr = Ls + (r - n_f) * d + c;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            R[2 * j] = lr[2 * j] + bf16lo(xv[j]);
+            R[2 * j + 1] = lr[2 * j + 1] + bf16hi(xv[j]);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          dyv[2 * j] = bf16lo(yv[j]);
+          dyv[2 * j + 1] = bf16hi(yv[j]);
+        }
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += R[j];
+      const float mean = group_sum<G>(s) * inv_d;
+      float v = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float t = col_ok ? R[j] - mean : 0.f;
+        v += t * t;
+      }
+      const float rstd = rsqrtf(group_sum<G>(v) * inv_d + p.eps);
+      float s1 = 0.f, s2 = 0.f, rh[8], g[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        rh[j] = (R[j] - mean) * rstd;
+        g[j] = dyv[j] * gam[j];
+        s1 += g[j];
+        s2 += g[j] * rh[j];
+      }
+      const float m1 = group_sum<G>(s1) * inv_d, m2 = group_sum<G>(s2) * inv_d;
+      if (col_ok) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          o[j] = pack_bf16x2(rstd * (g[2 * j] - m1 - rh[2 * j] * m2), rstd * (g[2 * j + 1] - m1 - rh[2 * j + 1] * m2));
+        uint16_t* dst = r < n_f ? p.dm + (b * n_f + r) * d + c : p.dlc + (b * n_l + (r - n_f)) * d + c;
+        *reinterpret_cast<u32x4*>(dst) = o;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pg[j] += dyv[j] * rh[j];
+          pb[j] += dyv[j];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // per-workgroup sums: lanes sharing columns (one per row group), then waves in order
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int mk = G; mk < kWave; mk <<= 1) {
+      pg[j] += __shfl_xor(pg[j], mk, kWave);
+      pb[j] += __shfl_xor(pb[j], mk, kWave);
+    }
+  }
+  if (lane < G && col_ok) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      red[(wave * 2) * d + c + j] = pg[j];
+      red[(wave * 2 + 1) * d + c + j] = pb[j];
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < 2 * d; j += BT) {
+    const int which = j / d, e = j - which * d;
+    float s = 0.f;
+    for (int w = 0; w < BW; ++w) s += red[(w * 2 + which) * d + e];
+    p.part[(int64_t)blockIdx.x * 2 * d + j] = s;
+  }
+}
+
+// ---------------------------------------------------------------- phase B
+struct BwdFmbKArgs {
+  const uint16_t* x;         // [B, n, d]
+  const uint16_t* dfn;       // [B, n k]
+  const uint16_t* dm;        // [B, n_f, d]
+  const uint16_t* dlc;       // [B, n_l, d]
+  const uint16_t* phi;       // [k, n]
+  const uint16_t* w_l;       // [n_l, n]
+  const uint16_t* fm_gamma;  // [n k] or null
+  uint16_t* dx;              // [B, n, d]
+  float* part;               // [gridDim.x, k n + n_l n + 2 n k]
+  int64_t batch;
+  int n, d, k, n_f, n_l;
+  float eps;
+};
+
+template <int QF, int QP, int QL>
+__global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
+  extern __shared__ __align__(16) uint16_t smem[];
+  const int n = p.n, d = p.d, k = p.k, n_f = p.n_f, n_l = p.n_l;
+  const FmbPlan pl = fmb_plan(n, d, k, n_l);
+  uint16_t* Xs = smem + pl.xs / 2;
+  uint16_t* As = smem + pl.as / 2;  // rows [0,kp) dF^T, [kp,2kp) Phi, [2kp,2kp+nlp) W_L
+  uint16_t* Bs = smem + pl.bs / 2;  // rows [0,kp) Z, [kp,2kp) dZ, [2kp,2kp+nlp) dLc
+  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + pl.red);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lg = lane >> 4;
+  const int kp = pl.kp, nk = n * k;
+  const int ib_n = pl.n16 / 16, jb_n = kp / 16, cb_n = d / 16;
+  const int tilesF = ib_n * jb_n, tilesP = jb_n * ib_n, tilesL = (pl.nlp / 16) * ib_n;
+  const float inv_nk = 1.f / (float)nk;
+
+  zero_lds(smem, pl.red);
+  __syncthreads();
+  load_rows(As + kp * pl.pn, pl.pn, p.phi, k, n);
+  load_rows(As + 2 * kp * pl.pn, pl.pn, p.w_l, n_l, n);
+
+  f32x4 accP[QP], accL[QL], pgam[QF], pbet[QF];
+#pragma unroll
+  for (int q = 0; q < QP; ++q) accP[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < QL; ++q) accL[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < QF; ++q) pgam[q] = pbet[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
+    load_rows(Xs, pl.pd, p.x + b * n * d, n, d);
+    load_rows(Bs + 2 * kp * pl.pd, pl.pd, p.dlc + b * n_l * d, n_l, d);
+    __syncthreads();
+    // Z = Phi X -> Bs rows [0, kp)
+    for (int t = wave; t < jb_n * cb_n; t += BW) {
+      const int rb = t / cb_n, cb = t - rb * cb_n;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < pl.n32; k0 += 32)
+        acc = mfma16x16x32(row_op(As, pl.pn, kp + rb * 16, k0, li, lg), tr_op(Xs, pl.pd, k0, cb * 16, li, lg), acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Bs[(rb * 16 + 4 * lg + q) * pl.pd + cb * 16 + li] = to_bf16(acc[q]);
+    }
+    __syncthreads();
+    // F = X Z^T, this wave's tiles in registers
+    f32x4 F[QF];
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < QF; ++q) {
+      F[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int t = wave + q * BW;
+      if (t < tilesF) {
+        const int ib = t / jb_n, jb = t - ib * jb_n;
+        for (int k0 = 0; k0 < pl.dp; k0 += 32)
+          F[q] = mfma16x16x32(row_op(Xs, pl.pd, ib * 16, k0, li, lg), row_op(Bs, pl.pd, jb * 16, k0, li, lg), F[q]);
+        // padded rows / columns of F are exactly 0 and add nothing
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s += F[q][r];
+      }
+    }
+    const float mean = block_sum(s, red) * inv_nk;
+    float v = 0.f;
+#pragma unroll
+    for (int q = 0; q < QF; ++q) {
+      const int t = wave + q * BW;
+      if (t < tilesF) {
+        const int ib = t / jb_n, jb = t - ib * jb_n;
+        const int j = jb * 16 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = ib * 16 + 4 * lg + r;
+          const float e = (i < n && j < k) ? F[q][r] - mean : 0.f;
+          v += e * e;
+        }
+      }
+    }
+    const float rstd = rsqrtf(block_sum(v, red) * inv_nk + p.eps);
+    // F -> F_tilde; means of q = d_Fn gamma_fm and of q F_tilde
+    const uint16_t* dfn_b = p.dfn + b * nk;
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int q = 0; q < QF; ++q) {
+      const int t = wave + q * BW;
+      if (t < tilesF) {
+        const int ib = t / jb_n, jb = t - ib * jb_n;
+        const int j = jb * 16 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = ib * 16 + 4 * lg + r;
+          if (i < n && j < k) {
+            const int idx = i * k + j;
+            const float g = bf16_to_f32(dfn_b[idx]) * (p.fm_gamma != nullptr ? bf16_to_f32(p.fm_gamma[idx]) : 1.f);
+            const float ft = (F[q][r] - mean) * rstd;
+            F[q][r] = ft;
+            s1 += g;
+            s2 += g * ft;
+          } else {
+            F[q][r] = 0.f;
+          }
+        }
+      }
+    }
+    s1 = block_sum(s1, red) * inv_nk;
+    s2 = block_sum(s2, red) * inv_nk;
+    // dF^T -> As rows [0, kp) (zeros at padding), FM LayerNorm parameter sums
+#pragma unroll
+    for (int q = 0; q < QF; ++q) {
+      const int t = wave + q * BW;
+      if (t < tilesF) {
+        const int ib = t / jb_n, jb = t - ib * jb_n;
+        const int j = jb * 16 + li;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = ib * 16 + 4 * lg + r;
+          float df = 0.f;
+          if (i < n && j < k) {
+            const int idx = i * k + j;
+            const float gn = bf16_to_f32(dfn_b[idx]);
+            const float g = gn * (p.fm_gamma != nullptr ? bf16_to_f32(p.fm_gamma[idx]) : 1.f);
+            df = rstd * (g - s1 - F[q][r] * s2);
+            pgam[q][r] += gn * F[q][r];
+            pbet[q][r] += gn;
+          }
+          As[j * pl.pn + i] = to_bf16(df);
+        }
+      }
+    }
+    __syncthreads();
+    // dZ = dF^T X -> Bs rows [kp, 2kp)
+    for (int t = wave; t < jb_n * cb_n; t += BW) {
+      const int rb = t / cb_n, cb = t - rb * cb_n;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < pl.n32; k0 += 32)
+        acc = mfma16x16x32(row_op(As, pl.pn, rb * 16, k0, li, lg), tr_op(Xs, pl.pd, k0, cb * 16, li, lg), acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Bs[(kp + rb * 16 + 4 * lg + q) * pl.pd + cb * 16 + li] = to_bf16(acc[q]);
+    }
+    __syncthreads();
+    // dX = dR + [dF | Phi^T | W_L^T] [Z; dZ; dLc]
+    for (int t = wave; t < ib_n * cb_n; t += BW) {
+      const int ib = t / cb_n, cb = t - ib * cb_n;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < pl.ka; k0 += 32)
+        acc = mfma16x16x32(tr_op(As, pl.pn, k0, ib * 16, li, lg), tr_op(Bs, pl.pd, k0, cb * 16, li, lg), acc);
+      const int e = cb * 16 + li;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = ib * 16 + 4 * lg + q;
+        if (i < n) {
+          const float res = i < n_f ? bf16_to_f32(p.dm[(b * n_f + i) * d + e])
+                                    : bf16_to_f32(Bs[(2 * kp + i - n_f) * pl.pd + e]);
+          p.dx[(b * n + i) * d + e] = to_bf16(acc[q] + res);
+        }
+      }
+    }
+    // d_Phi += dZ X^T, d_W_L += dLc X^T
+#pragma unroll
+    for (int q = 0; q < QP; ++q) {
+      const int t = wave + q * BW;
+      if (t < tilesP) {
+        const int rb = t / ib_n, ib = t - rb * ib_n;
+        for (int k0 = 0; k0 < pl.dp; k0 += 32)
+          accP[q] = mfma16x16x32(row_op(Bs, pl.pd, kp + rb * 16, k0, li, lg), row_op(Xs, pl.pd, ib * 16, k0, li, lg),
+                                 accP[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < QL; ++q) {
+      const int t = wave + q * BW;
+      if (t < tilesL) {
+        const int rb = t / ib_n, ib = t - rb * ib_n;
+        for (int k0 = 0; k0 < pl.dp; k0 += 32)
+          accL[q] = mfma16x16x32(row_op(Bs, pl.pd, 2 * kp + rb * 16, k0, li, lg),
+                                 row_op(Xs, pl.pd, ib * 16, k0, li, lg), accL[q]);
+      }
+    }
+    __syncthreads();
+  }
+  // this workgroup's plane: d_Phi [k, n], d_W_L [n_l, n], d_gamma_fm [n k], d_beta_fm [n k]
+  float* out = p.part + (int64_t)blockIdx.x * (k * n + n_l * n + 2 * nk);
+#pragma unroll
+  for (int q = 0; q < QP; ++q) {
+    const int t = wave + q * BW;
+    if (t < tilesP) {
+      const int rb = t / ib_n, ib = t - rb * ib_n;
+      const int i = ib * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = rb * 16 + 4 * lg + r;
+        if (j < k && i < n) out[j * n + i] = accP[q][r];
+      }
+    }
+  }
+  out += k * n;
+#pragma unroll
+  for (int q = 0; q < QL; ++q) {
+    const int t = wave + q * BW;
+    if (t < tilesL) {
+      const int rb = t / ib_n, ib = t - rb * ib_n;
+      const int i = ib * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = rb * 16 + 4 * lg + r;
+        if (j < n_l && i < n) out[j * n + i] = accL[q][r];
+      }
+    }
+  }
+  out += n_l * n;
+#pragma unroll
+  for (int q = 0; q < QF; ++q) {
+    const int t = wave + q * BW;
+    if (t < tilesF) {
+      const int ib = t / jb_n, jb = t - ib * jb_n;
+      const int j = jb * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ib * 16 + 4 * lg + r;
+        if (i < n && j < k) {
+          out[i * k + j] = pgam[q][r];
+          out[nk + i * k + j] = pbet[q][r];
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- transposes and sums
+// at[c][r] = a[r][c] for r < R and 0 for R <= r < Rp (Rp % 8 == 0); when
+// colpart is set, colpart[tile row][c] = sum of the tile's 64 rows of column c.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const uint16_t* a, int64_t R, int C, int64_t Rp,
+                                                             uint16_t* at, float* colpart) {
+  __shared__ __align__(16) uint16_t t[64][72];
+  const int c0 = blockIdx.x * 64;
+  const int64_t r0 = (int64_t)blockIdx.y * 64;
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if (r0 + rr < R && c0 + cc < C) v = *reinterpret_cast<const u32x4*>(a + (r0 + rr) * C + c0 + cc);
+    *reinterpret_cast<u32x4*>(&t[rr][cc]) = v;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int oc = q >> 3, rr = (q & 7) * 8;
+    uint32_t w[4];
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint16_t lo = t[rr + 2 * j][oc], hi = t[rr + 2 * j + 1][oc];
+      w[j] = (uint32_t)lo | ((uint32_t)hi << 16);
+      s += bf16_to_f32(lo) + bf16_to_f32(hi);
+    }
+    s += __shfl_xor(s, 1, kWave);
+    s += __shfl_xor(s, 2, kWave);
+    s += __shfl_xor(s, 4, kWave);
+    if (c0 + oc < C) {
+      if (r0 + rr < Rp) *reinterpret_cast<u32x4*>(at + (int64_t)(c0 + oc) * Rp + r0 + rr) = u32x4{w[0], w[1], w[2], w[3]};
+      if (colpart != nullptr && (q & 7) == 0) colpart[(int64_t)blockIdx.y * C + c0 + oc] = s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void sum_planes_kernel(const float* part, int planes, int64_t stride, int64_t len,
+                                                         float* out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < len; i += (int64_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int q = 0; q < planes; ++q) s += part[(int64_t)q * stride + i];
+    out[i] = s;
+  }
+}
+
+int workgroups_for(int64_t batch) { return (int)(batch < 256 ? batch : 256); }
+
+// Lets a kernel take the whole 160 KB of LDS as dynamic shared memory (a host-side attribute, set per launch).
+template <class K>
+hipError_t allow_lds(K* kern) {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host side
+namespace {
+int fmb_variant(const FmbPlan& f) {
+  const int ib = f.n16 / 16;
+  for (int v = 0; v < 2; ++v)
+    if (ib * (f.kp / 16) <= kQF[v] * BW && (f.kp / 16) * ib <= kQP[v] * BW && (f.nlp / 16) * ib <= kQL[v] * BW)
+      return v;
+  return -1;
+}
+}  // namespace
+
+bool wukong_bwd_supported(int n, int d, int k, int n_l) {
+  if (n <= 0 || d <= 0 || k <= 0 || n_l <= 0 || n_l >= n) return false;
+  if (d % 16 || n % 8 || d > 512) return false;
+  const OutPlan a = out_plan(n, d, n_l);
+  const FmbPlan f = fmb_plan(n, d, k, n_l);
+  if (a.bytes > kLdsMax || f.bytes > kLdsMax) return false;
+  return fmb_variant(f) >= 0;
+}
+
+int wukong_bwd_workgroups(int64_t batch) { return workgroups_for(batch); }
+
+size_t wukong_bwd_out_part_floats(int d) { return (size_t)2 * d; }
+size_t wukong_bwd_fmb_part_floats(int n, int k, int n_l) { return (size_t)k * n + (size_t)n_l * n + 2 * (size_t)n * k; }
+
+hipError_t launch_bwd_out(const BwdOutArgs& a, hipStream_t stream, int64_t* workgroups) {
+  if (!wukong_bwd_supported(a.n, a.d, 1, a.n_l)) return hipErrorInvalidValue;
+  const int grid = workgroups_for(a.batch);
+  if (workgroups) *workgroups = grid;
+  if (grid == 0) return hipSuccess;
+  BwdOutKArgs k;
+  k.x = static_cast<const uint16_t*>(a.x);
+  k.m = static_cast<const uint16_t*>(a.m);
+  k.dy = static_cast<const uint16_t*>(a.dy);
+  k.w_l = static_cast<const uint16_t*>(a.w_l);
+  k.gamma = static_cast<const uint16_t*>(a.gamma);
+  k.dm = static_cast<uint16_t*>(a.dm);
+  k.dlc = static_cast<uint16_t*>(a.dlc);
+  k.part = a.part;
+  k.batch = a.batch;
+  k.n = a.n;
+  k.d = a.d;
+  k.n_f = a.n - a.n_l;
+  k.n_l = a.n_l;
+  k.eps = a.eps;
+  const OutPlan pl = out_plan(a.n, a.d, a.n_l);
+  void (*kern)(BwdOutKArgs) = nullptr;
+  switch (pl.g) {
+    case 2: kern = bwd_out_kernel<2>; break;
+    case 4: kern = bwd_out_kernel<4>; break;
+    case 8: kern = bwd_out_kernel<8>; break;
+    case 16: kern = bwd_out_kernel<16>; break;
+    case 32: kern = bwd_out_kernel<32>; break;
+    case 64: kern = bwd_out_kernel<64>; break;
+    default: return hipErrorInvalidValue;
+  }
+  const hipError_t e = allow_lds(kern);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(BT), pl.bytes, stream, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fmb(const BwdFmbArgs& a, hipStream_t stream, int64_t* workgroups) {
+  if (!wukong_bwd_supported(a.n, a.d, a.k, a.n_l)) return hipErrorInvalidValue;
+  const int grid = workgroups_for(a.batch);
+  if (workgroups) *workgroups = grid;
+  if (grid == 0) return hipSuccess;
+  BwdFmbKArgs k;
+  k.x = static_cast<const uint16_t*>(a.x);
+  k.dfn = static_cast<const uint16_t*>(a.dfn);
+  k.dm = static_cast<const uint16_t*>(a.dm);
+  k.dlc = static_cast<const uint16_t*>(a.dlc);
+  k.phi = static_cast<const uint16_t*>(a.phi);
+  k.w_l = static_cast<const uint16_t*>(a.w_l);
+  k.fm_gamma = static_cast<const uint16_t*>(a.fm_gamma);
+  k.dx = static_cast<uint16_t*>(a.dx);
+  k.part = a.part;
+  k.batch = a.batch;
+  k.n = a.n;
+  k.d = a.d;
+  k.k = a.k;
+  k.n_f = a.n - a.n_l;
+  k.n_l = a.n_l;
+  k.eps = a.eps;
+  const FmbPlan pl = fmb_plan(a.n, a.d, a.k, a.n_l);
+  void (*kern)(BwdFmbKArgs) =
+      fmb_variant(pl) == 0 ? bwd_fmb_kernel<kQF[0], kQP[0], kQL[0]> : bwd_fmb_kernel<kQF[1], kQP[1], kQL[1]>;
+  const hipError_t e = allow_lds(kern);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(BT), pl.bytes, stream, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_bf16(const void* a, int64_t R, int C, int64_t Rp, void* at, float* colpart,
+                                 hipStream_t stream, int64_t* workgroups) {
+  if (R < 0 || C <= 0 || C % 8 || Rp < R || Rp % 8) return hipErrorInvalidValue;
+  const int64_t gy = (Rp + 63) / 64;
+  if (gy > 65535) return hipErrorInvalidValue;
+  const unsigned gx = (unsigned)((C + 63) / 64);
+  if (workgroups) *workgroups = (int64_t)gx * gy;
+  if (gy == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3(gx, (unsigned)gy), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(a), R, C, Rp, static_cast<uint16_t*>(at), colpart);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_planes_strided(const float* part, int planes, int64_t stride, int64_t len, float* out,
+                                     hipStream_t stream) {
+  if (planes < 1 || len < 0 || stride < len) return hipErrorInvalidValue;
+  if (len == 0) return hipSuccess;
+  int64_t grid = (len + 255) / 256;
+  if (grid > 2048) grid = 2048;
+  hipLaunchKernelGGL(sum_planes_kernel, dim3((unsigned)grid), dim3(256), 0, stream, part, planes, stride, len, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_planes(const float* part, int planes, int64_t len, float* out, hipStream_t stream) {
+  return launch_sum_planes_strided(part, planes, len, len, out, stream);
+}
+
+}  // namespace wk

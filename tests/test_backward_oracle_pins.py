@@ -133,7 +133,7 @@ def test_storage_names_and_rounding():
     w, X, dY = _case(hidden=(8,), seed=7)
     with pytest.raises(ValueError):
         WB.layer_backward(X, w, dY, storage=("dQ",))
-    full = ("Z", "Fn", "h", "M", "dM", "dh", "dFn", "dL", "dF", "dZ", "dX")
+    full = ("Z", "Fn", "h", "M", "dR", "dh", "dFn", "dF", "dZ", "dX")
     out = WB.layer_backward(X, w, dY, storage=full, intermediates=True)
     assert np.array_equal(out["dX"], WB.round_bf16(out["dX"]))
     assert np.array_equal(out["inter"]["dF"], WB.round_bf16(out["inter"]["dF"]))

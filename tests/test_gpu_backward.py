@@ -1,0 +1,162 @@
+"""Parity of one Wukong layer's backward pass (bf16) on the GPU with the CPU oracle.
+
+The HIP path runs the training forward (which keeps Fn, h_t and M) and the
+backward through the C ABI; the oracle (oracle/wukong_backward.py, pinned by
+finite differences in test_backward_oracle_pins.py) runs on the same seeded
+host arrays at the library's bf16 storage points: the forward's Z, Fn, h_t, M
+and the backward's dR, g_t, d_Fn, dF, dZ and dX.  Inputs: X as the layer
+workloads draw it, dY ~ N(0, 1) as a stand-in for the loss gradient, weights
+Xavier-uniform with random LayerNorm affines and biases.  Every output (dX
+and every weight gradient) passes the bf16 gate: elementwise 2e-2 with an rms
+floor, normwise 2e-2, rms 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import recommender_feature_interaction_amd as wk
+import wukong_synth as ws
+from _gpu_helpers import check, host_f64, log, spec_of, to_host
+
+pytestmark = pytest.mark.gpu
+
+FWD_STORAGE = ("Z", "Fn", "h", "M")
+BWD_STORAGE = ("dR", "dh", "dFn", "dF", "dZ", "dX")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    wk.load_library()
+
+
+def _custom(name, n, d, k, n_f, mlp, batch):
+    return ws.WukongConfig(name, "bf16", batch, (ws.LayerShape(n, d, k, n_f, n - n_f, tuple(mlp)),))
+
+
+CASES = [
+    _custom("bwd_tiny", 16, 16, 4, 8, (64, 64, 128), 37),                 # the tiny layer's shape in bf16
+    _custom("bwd_layer_d160_b40", 128, 160, 32, 64, (4096, 2048, 10240), 40),  # the d = 160 layer, ragged batch
+    _custom("bwd_padded", 40, 32, 20, 16, (800, 96, 72, 512), 70),        # k, n_l, n padded; three Linears
+    _custom("bwd_d48", 24, 48, 12, 16, (288, 64, 768), 65),               # d % 32 == 16
+]
+
+
+class BackwardRun:
+    def __init__(self, cfg, seed, affine="random", batch=None):
+        if batch is not None:
+            cfg = cfg.with_batch(batch)
+        self.cfg = cfg
+        self.host_w = ws.make_stack_weights(cfg, seed, affine)[0]
+        self.x = ws.make_input(cfg, seed)
+        self.dy = ws.make_upstream_grad(cfg, seed)
+        self.spec = spec_of(cfg.layers[0], "bf16")
+        self.layer = wk.DeviceLayer.from_host(self.spec, self.host_w)
+        self.xd = wk.to_device(self.x, "bf16", "cuda")
+        self.dyd = wk.to_device(self.dy, "bf16", "cuda")
+
+    def run(self, trace=None, grads=None):
+        y, saved = wk.layer_forward_train(self.xd, self.layer)
+        dx, grads = wk.layer_backward(self.xd, saved, self.dyd, self.layer, grads=grads, trace=trace)
+        torch.cuda.synchronize()
+        return y, saved, dx, grads
+
+    def oracle(self, x=None, dy=None):
+        x = self.x if x is None else x
+        dy = self.dy if dy is None else dy
+        return oracle.layer_backward(x, self.host_w, dy, storage=FWD_STORAGE + BWD_STORAGE)
+
+
+def _grad_host(t):
+    return t.detach().cpu().double().numpy()
+
+
+def check_grads(got: wk.LayerGrads, ref: dict, T: int):
+    check("d_phi", _grad_host(got.phi), ref["phi"], "bf16")
+    check("d_w_l", _grad_host(got.w_l), ref["w_l"], "bf16")
+    for name in ("fm_gamma", "fm_beta", "out_gamma", "out_beta"):
+        check(f"d_{name}", _grad_host(getattr(got, name)), ref[name], "bf16")
+    for t in range(T):
+        check(f"d_W{t}", _grad_host(got.mlp_w[t]), ref["mlp_w"][t], "bf16")
+        check(f"d_b{t}", _grad_host(got.mlp_b[t]), ref["mlp_b"][t], "bf16")
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+def test_backward_parity(cfg):
+    r = BackwardRun(cfg, seed=5)
+    log(f"backward {cfg.name} B={cfg.batch} shape={cfg.layers[0]}")
+    y, saved, dx, grads = r.run()
+    ref = r.oracle()
+    y_ref = oracle.wukong_layer(r.x, r.host_w, storage=FWD_STORAGE + ("Y",))
+    check("Y (training forward)", host_f64(to_host(y)), y_ref, "bf16")
+    check("dX", host_f64(to_host(dx)), ref["dX"], "bf16")
+    check_grads(grads, ref, len(cfg.layers[0].mlp) - 1)
+
+
+def test_saved_activations_match_the_forward():
+    cfg = CASES[2]
+    r = BackwardRun(cfg, seed=6)
+    _, saved, _, _ = r.run()
+    _, it = oracle.wukong_layer(r.x, r.host_w, storage=FWD_STORAGE, intermediates=True)
+    lay = wk.saved_layout(r.spec, cfg.batch)
+    B, n, k, d = cfg.batch, r.spec.n, r.spec.k, r.spec.d
+
+    def view(off, cols):
+        raw = saved[off:off + B * cols * 2].view(torch.bfloat16)
+        return host_f64(to_host(raw)).reshape(B, cols)
+
+    check("Fn (saved)", view(lay["fn"], n * k), it["Fn"], "bf16")
+    for t, off in enumerate(lay["hidden"]):
+        check(f"h_{t + 1} (saved)", view(off, r.spec.mlp[t + 1]), it["h"][t], "bf16")
+    check("M (saved)", view(lay["m"], r.spec.n_f * d), it["M"].reshape(B, -1), "bf16")
+
+
+def test_backward_identity_affine_no_bias_effects():
+    """Identity LayerNorm affines and zero biases (their gradients are still computed)."""
+    r = BackwardRun(CASES[0], seed=7, affine="identity")
+    _, _, dx, grads = r.run()
+    ref = r.oracle()
+    check("dX", host_f64(to_host(dx)), ref["dX"], "bf16")
+    check_grads(grads, ref, 2)
+
+
+def test_backward_determinism_trace_and_batch_rows():
+    cfg = CASES[1]
+    r = BackwardRun(cfg, seed=8)
+    tr = wk.Trace(capacity=64)
+    _, _, dx1, g1 = r.run(trace=tr)
+    kinds = [x["kernel"] for x in tr.records()]
+    tr.close()
+    log(f"  launches: {kinds}")
+    assert kinds[0] == "bwd_out" and "bwd_fmb" in kinds and kinds.count("bwd_wgrad") == 2
+    assert kinds.count("bwd_dgrad") == 2
+    dx1 = to_host(dx1)
+    g1 = {k: (v if not isinstance(v, list) else [t.clone() for t in v]) for k, v in g1.as_dict().items()}
+    g1 = {k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in g1.items()}
+    _, _, dx2, g2 = r.run()
+    assert np.array_equal(dx1, to_host(dx2)), "dX differs between two runs"
+    for k, v in g2.as_dict().items():
+        if isinstance(v, list):
+            for a, b in zip(g1[k], v):
+                assert torch.equal(a, b), k
+        elif v is not None:
+            assert torch.equal(g1[k], v), k
+    # dX of an example depends on that example only
+    sub = slice(3, 17)
+    y, saved = wk.layer_forward_train(r.xd[sub].contiguous(), r.layer)
+    dxs, _ = wk.layer_backward(r.xd[sub].contiguous(), saved, r.dyd[sub].contiguous(), r.layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dxs), dx1[sub]), "a subset's dX rows differ from the full batch's"
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_backward_full_batch_layer_d160():
+    """The d = 160 layer at its full batch of 4096: every gradient against the oracle over all examples."""
+    r = BackwardRun(ws.BY_NAME["layer_d160"], seed=9)
+    _, _, dx, grads = r.run()
+    ref = r.oracle()
+    check("dX", host_f64(to_host(dx)), ref["dX"], "bf16")
+    check_grads(grads, ref, 2)

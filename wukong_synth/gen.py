@@ -321,3 +321,10 @@ def make_input(cfg: WukongConfig, seed: int, batch: Optional[int] = None,
     elif cfg.x_dist != "normal":
         raise ValueError(cfg.x_dist)
     return _store(x, cfg.dtype)
+
+
+def make_upstream_grad(cfg: WukongConfig, seed: int, batch: Optional[int] = None) -> np.ndarray:
+    """A stand-in for dLoss/dY of a layer output [batch, n, d]: N(0, 1) entries."""
+    s0 = cfg.layers[0]
+    b = cfg.batch if batch is None else batch
+    return _draw(seed, f"{cfg.name}/dy", b * s0.n * s0.d, "normal", dtype=cfg.dtype).reshape(b, s0.n, s0.d)
