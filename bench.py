@@ -57,6 +57,12 @@ KERNEL_SOURCES = {
     "fusion_attention": ("whale_fusion.hip",),
     "fusion_linear": ("linear_bf16.hip",),
     "fusion_ln": ("whale_fusion.hip",),
+    "bwd_out": ("wukong_backward.hip",),
+    "bwd_fmb": ("wukong_backward.hip",),
+    "bwd_transpose": ("wukong_backward.hip",),
+    "bwd_reduce": ("wukong_backward.hip",),
+    "bwd_wgrad": ("linear_bf16.hip",),
+    "bwd_dgrad": ("linear_bf16.hip",),
 }
 
 
@@ -151,6 +157,94 @@ def summarize_trace(recs, acct, per_step_ms, steps):
         by_kind.setdefault((kr["kernel"], kr["index"]), []).append(kr)
     best = max(by_kind.items(), key=lambda it: sum(k["avg_ms"] for k in it[1]))
     return kernels, best[1][0]
+
+
+def backward_accounting(B, s):
+    """Algorithmic FLOPs and HBM bytes per launch of one bf16 layer's backward
+    kernels (recomputed products included: they are work the kernels do)."""
+    n, d, k, n_f, n_l = s.n, s.d, s.k, s.n_f, s.n_l
+    Bp = (B + 63) // 64 * 64
+    T = len(s.mlp) - 1
+    out = {
+        # X, M, dY in; dR (dM and dLc) out; W_L once.  Lc = W_L X recomputed.
+        ("bwd_out", 0, 0): {"flops": B * 2 * n_l * n * d, "bytes": B * (3 * n * d + n_f * d) * 2 + n_l * n * 2},
+        # X, d_Fn, dR in; dX out; [Phi; W_L] once.  Z, F recomputed; dZ, dX, d_Phi, d_W_L.
+        ("bwd_fmb", 0, 0): {"flops": B * (2 * k * n * d * 4 + 2 * n * d * (2 * k + n_l) + 2 * n_l * n * d),
+                            "bytes": B * (3 * n * d + n * k) * 2 + (k + n_l) * n * 2},
+        ("bwd_reduce", 0, 0): {"flops": 0, "bytes": 0}, ("bwd_reduce", 0, 1): {"flops": 0, "bytes": 0},
+    }
+    for t, (a, b) in enumerate(zip(s.mlp[:-1], s.mlp[1:])):
+        out[("bwd_transpose", 0, 3 * t)] = {"flops": 0, "bytes": (B * b + Bp * b) * 2}
+        out[("bwd_transpose", 0, 3 * t + 1)] = {"flops": 0, "bytes": (B * a + Bp * a) * 2}
+        out[("bwd_transpose", 0, 3 * t + 2)] = {"flops": 0, "bytes": 2 * a * b * 2}
+        out[("bwd_wgrad", 0, t)] = {"flops": 2 * b * a * B, "bytes": (a + b) * Bp * 2 + a * b * 4}
+        out[("bwd_dgrad", 0, t)] = {"flops": 2 * B * b * a,
+                                    "bytes": (B * b + a * b + B * a + (B * a if t > 0 else 0)) * 2}
+        out[("bwd_reduce", 0, 2 + t)] = {"flops": 0, "bytes": 0}
+    for i in range(4):
+        out[("bwd_reduce", 0, 2 + T + i)] = {"flops": 0, "bytes": 0}
+    return out
+
+
+def measure_training(wk, ws, torch, cfg, layer, x, stream, steps, warmup, seed):
+    """One training step of a single bf16 layer: the forward that keeps Fn, h_t
+    and M, then the backward (dX and every weight gradient) for a seeded dY."""
+    if cfg.num_layers != 1 or cfg.dtype != "bf16":
+        return None
+    s = cfg.layers[0]
+    B = cfg.batch
+    spec = layer.spec
+    need = wk.layer_backward_workspace_size(spec, B)
+    if need == 0:
+        return None
+    dy = wk.to_device(ws.make_upstream_grad(cfg, seed), "bf16", x.device)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    saved = wk.alloc_workspace(wk.layer_saved_size(spec, B), x.device)
+    bws = wk.alloc_workspace(need, x.device)
+    grads = wk.LayerGrads(layer)
+
+    def step(trace=None):
+        wk.layer_forward_train(x, layer, y=y, saved=saved, stream=stream)
+        wk.layer_backward(x, saved, dy, layer, grads=grads, dx=dx, workspace=bws, stream=stream, trace=trace)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wk.layer_forward_train(x, layer, y=y, saved=saved, stream=stream)
+    torch.cuda.synchronize()
+    fwd_ms = (time.perf_counter() - t0) * 1e3 / steps
+    T = len(s.mlp) - 1
+    per = 3 + 5 * T + 4 + 4
+    trace = wk.Trace(capacity=per * steps + 8)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        wk.layer_backward(x, saved, dy, layer, grads=grads, dx=dx, workspace=bws, stream=stream, trace=trace)
+    torch.cuda.synchronize()
+    bwd_ms = (time.perf_counter() - t1) * 1e3 / steps
+    acct = backward_accounting(B, s)
+    kernels, dom = summarize_trace(trace.records(), acct, bwd_ms, steps)
+    trace.close()
+    roof = None
+    if dom is not None:
+        roof = roofline_of(dom, acct[(dom["kernel"], dom["layer"], dom["index"])], dom["avg_ms"], "bf16", cfg.name)
+    fwd_flops = cfg.flops_per_example() * B
+    bwd_flops = sum(a["flops"] for a in acct.values())
+    return {"ms_per_step": round(ms, 4), "forward_train_ms": round(fwd_ms, 4), "backward_ms": round(bwd_ms, 4),
+            "examples_per_s": round(B / ms * 1e3, 1),
+            # the usual training count: backward = 2 x forward
+            "model_tflops": round(3 * fwd_flops / (ms * 1e-3) / 1e12, 2),
+            "kernel_tflops": round((fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12, 2),
+            "roofline": roof,
+            "kernels": sorted(kernels, key=lambda k: (k["kernel"], k["index"]))}
 
 
 def measure_head(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
@@ -317,6 +411,8 @@ def main():
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache (512 MB flush) step timing")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-fusion", action="store_true", help="skip the WHALE fusion-step measurement")
+    ap.add_argument("--no-training", action="store_true",
+                    help="skip the single-layer training step (forward + backward) measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -476,6 +572,14 @@ def main():
             print(f"# fusion n={fusion['n']} d={fusion['d']} L={fusion['L']}: {fusion['ms_per_call']:.3f} ms/call",
                   file=sys.stderr, flush=True)
 
+    training = None
+    if not args.no_training:
+        training = measure_training(wk, ws, torch, cfg, layers[0], x, stream, args.steps, args.warmup, args.seed)
+        if training is not None:
+            print(f"# training step (forward + backward): {training['ms_per_step']:.3f} ms "
+                  f"(forward {training['forward_train_ms']:.3f}, backward {training['backward_ms']:.3f})",
+                  file=sys.stderr, flush=True)
+
     step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
     s0 = cfg.layers[0]
     out = {
@@ -505,6 +609,7 @@ def main():
         "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
         "head": head,
         "fusion": fusion,
+        "training": training,
     }
     if not args.no_cpu_baseline:
         del x, y, ws_t, layers

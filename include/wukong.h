@@ -166,11 +166,14 @@ enum {
   WK_KERNEL_FUSION_LINEAR = 7, /* fusion Linear (index 0), SwiGLU up (1), down (2) */
   WK_KERNEL_FUSION_LN = 8,    /* fusion: the pre-norm LayerNorm               */
   WK_KERNEL_BWD_OUT = 9,      /* backward: output LayerNorm + LCB rows (dR)   */
-  WK_KERNEL_BWD_TRANSPOSE = 10, /* backward: bf16 transpose (index = Linear)  */
+  WK_KERNEL_BWD_TRANSPOSE = 10, /* backward: bf16 transpose of Linear t's output gradient
+                                 (index 3t), input (3t + 1) or weight (3t + 2) */
   WK_KERNEL_BWD_WGRAD = 11,   /* backward: dW_t (index t)                     */
   WK_KERNEL_BWD_DGRAD = 12,   /* backward: gradient of the Linear's input (t) */
   WK_KERNEL_BWD_FMB = 13,     /* backward: FM LayerNorm, interaction, dX      */
-  WK_KERNEL_BWD_REDUCE = 14   /* backward: per-workgroup weight-gradient sums */
+  WK_KERNEL_BWD_REDUCE = 14   /* backward: per-workgroup / per-split sums: index 0, 1
+                                 gamma_out, beta_out; 2 + t the bias of Linear t;
+                                 2 + T + 0..3 Phi, W_L, gamma_fm, beta_fm */
 };
 typedef struct wk_trace wk_trace;
 /* Creates a trace able to hold `capacity` launch records (creates HIP events

@@ -670,7 +670,7 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
     const int mi = d->mlp_dims[t], mo = d->mlp_dims[t + 1];
     const void* a_t = t == 0 ? static_cast<const void*>(sbase + sv.fn) : static_cast<const void*>(sbase + sv.hid[t - 1]);
     float* db = gr->mlp_b ? gr->mlp_b[t] : nullptr;
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, t, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, 3 * t, [&](int64_t* g) {
       return wk::launch_transpose_bf16(g_next, batch, mo, Bp, gt, db ? colpart : nullptr, s, g);
     });
     if (st != WK_OK) return st;
@@ -681,7 +681,7 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
       });
       if (st != WK_OK) return st;
     }
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, t, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, 3 * t + 1, [&](int64_t* g) {
       return wk::launch_transpose_bf16(a_t, batch, mi, Bp, at, nullptr, s, g);
     });
     if (st != WK_OK) return st;
@@ -698,7 +698,7 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
       return wk::launch_linear_bf16_f32out_split(wa, gr->mlp_w[t], split, s, g);
     });
     if (st != WK_OK) return st;
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, t, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, 3 * t + 2, [&](int64_t* g) {
       return wk::launch_transpose_bf16(w->mlp_w[t], mo, mi, mo, wt, nullptr, s, g);
     });
     if (st != WK_OK) return st;

@@ -50,9 +50,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int BW = 8;            // waves per workgroup
 constexpr int BT = BW * kWave;   // threads per workgroup
 constexpr int kLdsMax = 160 * 1024;
-// bwd_fmb_kernel variants: at most QF F tiles, QP d_Phi tiles and QL d_W_L
-// tiles (16 x 16) per wave; the smallest that fits the shape is launched.
-constexpr int kQF[2] = {2, 4}, kQP[2] = {2, 4}, kQL[2] = {4, 8};
+// bwd_fmb_kernel holds at most QF F tiles, QP d_Phi tiles and QL d_W_L tiles
+// (16 x 16) per wave in registers across its examples.
+constexpr int kQF = 2, kQP = 2, kQL = 4;
 
 __host__ __device__ constexpr int up16(int v) { return (v + 15) / 16 * 16; }
 __host__ __device__ constexpr int up32(int v) { return (v + 31) / 32 * 32; }
@@ -74,17 +74,19 @@ __device__ __forceinline__ u32x4 tr_op(const uint16_t* base, int pitch, int r0, 
 
 __device__ __forceinline__ uint16_t to_bf16(float v) { return (uint16_t)f32_to_bf16(v); }
 
-// Sum of one value per thread over the workgroup; every thread gets it.
-// red holds BW floats; two barriers keep back-to-back calls from racing.
-__device__ __forceinline__ float block_sum(float v, float* red) {
+// Sum of one value per thread over the workgroup; every thread gets it.  red
+// holds 2 slots of BW floats used alternately (slot = 0, 1, 0, ...), so one
+// LDS-only barrier per call is enough: a slot is rewritten two calls later,
+// after every thread has passed the barrier of the call in between.
+__device__ __forceinline__ float block_sum(float v, float* red, int slot) {
   v = xor_sum<1>(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
+  float* r = red + slot * BW;
+  if (lane == 0) r[wave] = v;
+  lds_barrier();
   float s = 0.f;
 #pragma unroll
-  for (int w = 0; w < BW; ++w) s += red[w];
-  __syncthreads();
+  for (int w = 0; w < BW; ++w) s += r[w];
   return s;
 }
 
@@ -102,7 +104,43 @@ __device__ __forceinline__ void load_rows(uint16_t* dst, int pitch, const uint16
   }
 }
 
+// Row-major global rows [rows, c8 * 8] -> LDS at word offset `off`, pitch
+// `pitch`.  Thread t moves chunk t % c8 of rows t / c8 + i * (BT / c8),
+// i < MAXC; all its 16-byte loads are issued before the first LDS write, so
+// an example's loads are in flight together.  The thread index goes through
+// an opaque copy so the offsets are recomputed per call, not hoisted out of
+// the example loop (where they would hold registers through every phase).
+__host__ __device__ constexpr bool stage_fits(int rows, int c8, int maxc) {
+  return c8 <= BT && rows <= maxc * (BT / c8);
+}
+
+template <int MAXC>
+__device__ __forceinline__ void stage_rows(uint16_t* smem_base, int off, int pitch, const uint16_t* src, int rows,
+                                           int c8) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int rpp = BT / c8, r0 = tid / c8, c = (tid - r0 * c8) * 8;
+  const bool act = r0 < rpp;
+  u32x4 reg[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int r = r0 + i * rpp;
+    if (act && r < rows) reg[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * c8 * 8 + c);
+  }
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int r = r0 + i * rpp;
+    if (act && r < rows) *reinterpret_cast<u32x4*>(smem_base + off + r * pitch + c) = reg[i];
+  }
+}
+
 // ---------------------------------------------------------------- LDS plans
+constexpr int kMaxXChunks = 6;  // 16-byte chunks of X per thread and example
+constexpr int kMaxRChunks = 3;  // ... of dLc, and of the FMB rows of dR
+constexpr int kMaxFChunks = 2;  // ... of d_Fn (as rows of 4 chunks)
+constexpr int kMaxRows = 8;     // LayerNorm rows per lane group and example (bwd_out_kernel)
+constexpr int kRowBatch = 4;    // ... whose loads are issued together
+
 struct OutPlan {  // bwd_out_kernel
   int n32, pd, pn, nlp, g;
   int xs, wl, ls, red, bytes;  // byte offsets
@@ -131,7 +169,7 @@ __host__ __device__ inline OutPlan out_plan(int n, int d, int n_l) {
 
 struct FmbPlan {  // bwd_fmb_kernel
   int n16, n32, dp, pd, pn, kp, nlp, ka;
-  int xs, as, bs, red, bytes;
+  int xs, as, bs, dms, dfs, red, bytes;
 };
 
 __host__ __device__ inline FmbPlan fmb_plan(int n, int d, int k, int n_l) {
@@ -147,8 +185,10 @@ __host__ __device__ inline FmbPlan fmb_plan(int n, int d, int k, int n_l) {
   p.xs = 0;
   p.as = p.xs + p.n32 * p.pd * 2;
   p.bs = p.as + p.ka * p.pn * 2;
-  p.red = p.bs + p.ka * p.pd * 2;
-  p.bytes = p.red + 4 * BW * 4;
+  p.dms = p.bs + p.ka * p.pd * 2;
+  p.dfs = p.dms + (n - n_l) * p.pd * 2;
+  p.red = p.dfs + (n * k * 2 + 15) / 16 * 16;
+  p.bytes = p.red + 2 * BW * 4;
   return p;
 }
 
@@ -181,6 +221,7 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
   constexpr int RPW = kWave / G;  // rows per wave and pass
   const int grp = lane / G, c = (lane % G) * 8;
   const bool col_ok = c < d;
+  const int row0 = wave * RPW + grp, rstep = BW * RPW;
 
   zero_lds(smem, pl.ls);
   __syncthreads();
@@ -197,8 +238,22 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
   const float inv_d = 1.f / (float)d;
 
   for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
-    load_rows(Xs, pl.pd, p.x + b * n * d, n, d);
-    __syncthreads();
+    // dY and M rows in batches of kRowBatch per lane group; the first batch is
+    // in flight with X and while Lc is computed
+    u32x4 yv[kRowBatch], mv[kRowBatch];
+    auto load_batch = [&](int q0) {
+#pragma unroll
+      for (int j = 0; j < kRowBatch; ++j) {
+        const int r = row0 + (q0 + j) * rstep;
+        if (r < n && col_ok) {
+          yv[j] = *reinterpret_cast<const u32x4*>(p.dy + (b * n + r) * d + c);
+          if (r < n_f) mv[j] = *reinterpret_cast<const u32x4*>(p.m + (b * n_f + r) * d + c);
+        }
+      }
+    };
+    load_batch(0);
+    stage_rows<kMaxXChunks>(smem, pl.xs / 2, pl.pd, p.x + b * n * d, n, d / 8);
+    lds_barrier();
     // Lc = W_L X -> Ls (fp32)
     for (int t = wave; t < tiles; t += BW) {
       const int rb = t / dt, cb = t - rb * dt;
@@ -211,71 +266,77 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
         if (r < n_l) Ls[r * d + cb * 16 + li] = acc[q];
       }
     }
-    __syncthreads();
+    lds_barrier();
     // rows: R = [M; Lc] + X, LayerNorm backward
-    for (int r = wave * RPW + grp; r < n; r += BW * RPW) {
-      float R[8], dyv[8];
+#pragma unroll 1
+    for (int q0 = 0; q0 < kMaxRows; q0 += kRowBatch) {
+      if (row0 + q0 * rstep >= n) break;  // uniform over the lane group
+      if (q0 > 0) load_batch(q0);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) R[j] = dyv[j] = 0.f;
-      if (col_ok) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(Xs + r * pl.pd + c);
-        const u32x4 yv = *reinterpret_cast<const u32x4*>(p.dy + (b * n + r) * d + c);
-        if (r < n_f) {
-          const u32x4 mv = *reinterpret_cast<const u32x4*>(p.m + (b * n_f + r) * d + c);
+      for (int j = 0; j < kRowBatch; ++j) {
+        const int r = row0 + (q0 + j) * rstep;
+        if (r >= n) break;
+        float R[8], dyv[8];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            R[2 * j] = bf16lo(mv[j]) + bf16lo(xv[j]);
-            R[2 * j + 1] = bf16hi(mv[j]) + bf16hi(xv[j]);
+        for (int e = 0; e < 8; ++e) R[e] = dyv[e] = 0.f;
+        if (col_ok) {
+          const u32x4 xv = *reinterpret_cast<const u32x4*>(Xs + r * pl.pd + c);
+          if (r < n_f) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              R[2 * e] = bf16lo(mv[j][e]) + bf16lo(xv[e]);
+              R[2 * e + 1] = bf16hi(mv[j][e]) + bf16hi(xv[e]);
+            }
+          } else {
+            const float* lr = Ls + (r - n_f) * d + c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              R[2 * e] = lr[2 * e] + bf16lo(xv[e]);
+              R[2 * e + 1] = lr[2 * e + 1] + bf16hi(xv[e]);
+            }
           }
-        } else {
-          const float* lr = Ls + (r - n_f) * d + c;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            R[2 * j] = lr[2 * j] + bf16lo(xv[j]);
-            R[2 * j + 1] = lr[2 * j + 1] + bf16hi(xv[j]);
+          for (int e = 0; e < 4; ++e) {
+            dyv[2 * e] = bf16lo(yv[j][e]);
+            dyv[2 * e + 1] = bf16hi(yv[j][e]);
           }
         }
+        float s = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          dyv[2 * j] = bf16lo(yv[j]);
-          dyv[2 * j + 1] = bf16hi(yv[j]);
+        for (int e = 0; e < 8; ++e) s += R[e];
+        const float mean = group_sum<G>(s) * inv_d;
+        float v = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float t = col_ok ? R[e] - mean : 0.f;
+          v += t * t;
         }
-      }
-      float s = 0.f;
+        const float rstd = rsqrtf(group_sum<G>(v) * inv_d + p.eps);
+        float s1 = 0.f, s2 = 0.f, rh[8], g[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) s += R[j];
-      const float mean = group_sum<G>(s) * inv_d;
-      float v = 0.f;
+        for (int e = 0; e < 8; ++e) {
+          rh[e] = (R[e] - mean) * rstd;
+          g[e] = dyv[e] * gam[e];
+          s1 += g[e];
+          s2 += g[e] * rh[e];
+        }
+        const float m1 = group_sum<G>(s1) * inv_d, m2 = group_sum<G>(s2) * inv_d;
+        if (col_ok) {
+          u32x4 o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float t = col_ok ? R[j] - mean : 0.f;
-        v += t * t;
-      }
-      const float rstd = rsqrtf(group_sum<G>(v) * inv_d + p.eps);
-      float s1 = 0.f, s2 = 0.f, rh[8], g[8];
+          for (int e = 0; e < 4; ++e)
+            o[e] = pack_bf16x2(rstd * (g[2 * e] - m1 - rh[2 * e] * m2), rstd * (g[2 * e + 1] - m1 - rh[2 * e + 1] * m2));
+          uint16_t* dst = r < n_f ? p.dm + (b * n_f + r) * d + c : p.dlc + (b * n_l + (r - n_f)) * d + c;
+          *reinterpret_cast<u32x4*>(dst) = o;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        rh[j] = (R[j] - mean) * rstd;
-        g[j] = dyv[j] * gam[j];
-        s1 += g[j];
-        s2 += g[j] * rh[j];
-      }
-      const float m1 = group_sum<G>(s1) * inv_d, m2 = group_sum<G>(s2) * inv_d;
-      if (col_ok) {
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          o[j] = pack_bf16x2(rstd * (g[2 * j] - m1 - rh[2 * j] * m2), rstd * (g[2 * j + 1] - m1 - rh[2 * j + 1] * m2));
-        uint16_t* dst = r < n_f ? p.dm + (b * n_f + r) * d + c : p.dlc + (b * n_l + (r - n_f)) * d + c;
-        *reinterpret_cast<u32x4*>(dst) = o;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pg[j] += dyv[j] * rh[j];
-          pb[j] += dyv[j];
+          for (int e = 0; e < 8; ++e) {
+            pg[e] += dyv[e] * rh[e];
+            pb[e] += dyv[e];
+          }
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
   }
   // per-workgroup sums: lanes sharing columns (one per row group), then waves in order
 #pragma unroll
@@ -323,13 +384,15 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
   extern __shared__ __align__(16) uint16_t smem[];
   const int n = p.n, d = p.d, k = p.k, n_f = p.n_f, n_l = p.n_l;
   const FmbPlan pl = fmb_plan(n, d, k, n_l);
-  uint16_t* Xs = smem + pl.xs / 2;
-  uint16_t* As = smem + pl.as / 2;  // rows [0,kp) dF^T, [kp,2kp) Phi, [2kp,2kp+nlp) W_L
-  uint16_t* Bs = smem + pl.bs / 2;  // rows [0,kp) Z, [kp,2kp) dZ, [2kp,2kp+nlp) dLc
+  uint16_t* Xs = smem + pl.xs / 2;    // X; after the weight sums, the dX tile staging
+  uint16_t* As = smem + pl.as / 2;    // rows [0,kp) dF^T, [kp,2kp) Phi, [2kp,2kp+nlp) W_L
+  uint16_t* Bs = smem + pl.bs / 2;    // rows [0,kp) Z, [kp,2kp) dZ, [2kp,2kp+nlp) dLc
+  uint16_t* DMs = smem + pl.dms / 2;  // dR rows < n_f
+  uint16_t* DFs = smem + pl.dfs / 2;  // d_Fn
   float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + pl.red);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
-  const int kp = pl.kp, nk = n * k;
+  const int kp = pl.kp, nk = n * k, d8 = d / 8;
   const int ib_n = pl.n16 / 16, jb_n = kp / 16, cb_n = d / 16;
   const int tilesF = ib_n * jb_n, tilesP = jb_n * ib_n, tilesL = (pl.nlp / 16) * ib_n;
   const float inv_nk = 1.f / (float)nk;
@@ -339,18 +402,35 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
   load_rows(As + kp * pl.pn, pl.pn, p.phi, k, n);
   load_rows(As + 2 * kp * pl.pn, pl.pn, p.w_l, n_l, n);
 
-  f32x4 accP[QP], accL[QL], pgam[QF], pbet[QF];
+  f32x4 accP[QP], accL[QL], pgam[QF], pbet[QF], gfm[QF];
 #pragma unroll
   for (int q = 0; q < QP; ++q) accP[q] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q = 0; q < QL; ++q) accL[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // gamma_fm at this lane's F positions (the same for every example)
 #pragma unroll
-  for (int q = 0; q < QF; ++q) pgam[q] = pbet[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < QF; ++q) {
+    pgam[q] = pbet[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    gfm[q] = f32x4{1.f, 1.f, 1.f, 1.f};
+    const int t = wave + q * BW;
+    if (t < tilesF && p.fm_gamma != nullptr) {
+      const int ib = t / jb_n, jb = t - ib * jb_n;
+      const int j = jb * 16 + li;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ib * 16 + 4 * lg + r;
+        if (i < n && j < k) gfm[q][r] = bf16_to_f32(p.fm_gamma[i * k + j]);
+      }
+    }
+  }
 
+  int slot = 0;
   for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
-    load_rows(Xs, pl.pd, p.x + b * n * d, n, d);
-    load_rows(Bs + 2 * kp * pl.pd, pl.pd, p.dlc + b * n_l * d, n_l, d);
-    __syncthreads();
+    stage_rows<kMaxXChunks>(smem, pl.xs / 2, pl.pd, p.x + b * n * d, n, d8);
+    stage_rows<kMaxRChunks>(smem, pl.bs / 2 + 2 * kp * pl.pd, pl.pd, p.dlc + b * n_l * d, n_l, d8);
+    stage_rows<kMaxRChunks>(smem, pl.dms / 2, pl.pd, p.dm + b * n_f * d, n_f, d8);
+    stage_rows<kMaxFChunks>(smem, pl.dfs / 2, 32, p.dfn + b * nk, nk / 32, 4);
+    lds_barrier();
     // Z = Phi X -> Bs rows [0, kp)
     for (int t = wave; t < jb_n * cb_n; t += BW) {
       const int rb = t / cb_n, cb = t - rb * cb_n;
@@ -360,7 +440,7 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) Bs[(rb * 16 + 4 * lg + q) * pl.pd + cb * 16 + li] = to_bf16(acc[q]);
     }
-    __syncthreads();
+    lds_barrier();
     // F = X Z^T, this wave's tiles in registers
     f32x4 F[QF];
     float s = 0.f;
@@ -377,7 +457,8 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
         for (int r = 0; r < 4; ++r) s += F[q][r];
       }
     }
-    const float mean = block_sum(s, red) * inv_nk;
+    const float mean = block_sum(s, red, slot) * inv_nk;
+    slot ^= 1;
     float v = 0.f;
 #pragma unroll
     for (int q = 0; q < QF; ++q) {
@@ -393,9 +474,9 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
         }
       }
     }
-    const float rstd = rsqrtf(block_sum(v, red) * inv_nk + p.eps);
+    const float rstd = rsqrtf(block_sum(v, red, slot) * inv_nk + p.eps);
+    slot ^= 1;
     // F -> F_tilde; means of q = d_Fn gamma_fm and of q F_tilde
-    const uint16_t* dfn_b = p.dfn + b * nk;
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
     for (int q = 0; q < QF; ++q) {
@@ -407,8 +488,7 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
         for (int r = 0; r < 4; ++r) {
           const int i = ib * 16 + 4 * lg + r;
           if (i < n && j < k) {
-            const int idx = i * k + j;
-            const float g = bf16_to_f32(dfn_b[idx]) * (p.fm_gamma != nullptr ? bf16_to_f32(p.fm_gamma[idx]) : 1.f);
+            const float g = bf16_to_f32(DFs[i * k + j]) * gfm[q][r];
             const float ft = (F[q][r] - mean) * rstd;
             F[q][r] = ft;
             s1 += g;
@@ -419,8 +499,10 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
         }
       }
     }
-    s1 = block_sum(s1, red) * inv_nk;
-    s2 = block_sum(s2, red) * inv_nk;
+    s1 = block_sum(s1, red, slot) * inv_nk;
+    slot ^= 1;
+    s2 = block_sum(s2, red, slot) * inv_nk;
+    slot ^= 1;
     // dF^T -> As rows [0, kp) (zeros at padding), FM LayerNorm parameter sums
 #pragma unroll
     for (int q = 0; q < QF; ++q) {
@@ -433,10 +515,8 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
           const int i = ib * 16 + 4 * lg + r;
           float df = 0.f;
           if (i < n && j < k) {
-            const int idx = i * k + j;
-            const float gn = bf16_to_f32(dfn_b[idx]);
-            const float g = gn * (p.fm_gamma != nullptr ? bf16_to_f32(p.fm_gamma[idx]) : 1.f);
-            df = rstd * (g - s1 - F[q][r] * s2);
+            const float gn = bf16_to_f32(DFs[i * k + j]);
+            df = rstd * (gn * gfm[q][r] - s1 - F[q][r] * s2);
             pgam[q][r] += gn * F[q][r];
             pbet[q][r] += gn;
           }
@@ -444,7 +524,7 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
     // dZ = dF^T X -> Bs rows [kp, 2kp)
     for (int t = wave; t < jb_n * cb_n; t += BW) {
       const int rb = t / cb_n, cb = t - rb * cb_n;
@@ -454,24 +534,7 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) Bs[(kp + rb * 16 + 4 * lg + q) * pl.pd + cb * 16 + li] = to_bf16(acc[q]);
     }
-    __syncthreads();
-    // dX = dR + [dF | Phi^T | W_L^T] [Z; dZ; dLc]
-    for (int t = wave; t < ib_n * cb_n; t += BW) {
-      const int ib = t / cb_n, cb = t - ib * cb_n;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < pl.ka; k0 += 32)
-        acc = mfma16x16x32(tr_op(As, pl.pn, k0, ib * 16, li, lg), tr_op(Bs, pl.pd, k0, cb * 16, li, lg), acc);
-      const int e = cb * 16 + li;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = ib * 16 + 4 * lg + q;
-        if (i < n) {
-          const float res = i < n_f ? bf16_to_f32(p.dm[(b * n_f + i) * d + e])
-                                    : bf16_to_f32(Bs[(2 * kp + i - n_f) * pl.pd + e]);
-          p.dx[(b * n + i) * d + e] = to_bf16(acc[q] + res);
-        }
-      }
-    }
+    lds_barrier();
     // d_Phi += dZ X^T, d_W_L += dLc X^T
 #pragma unroll
     for (int q = 0; q < QP; ++q) {
@@ -493,7 +556,30 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
                                  row_op(Xs, pl.pd, ib * 16, k0, li, lg), accL[q]);
       }
     }
-    __syncthreads();
+    lds_barrier();  // X no longer read: its LDS takes the dX tiles
+    // dX = dR + [dF | Phi^T | W_L^T] [Z; dZ; dLc] -> Xs (bf16)
+    for (int t = wave; t < ib_n * cb_n; t += BW) {
+      const int ib = t / cb_n, cb = t - ib * cb_n;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < pl.ka; k0 += 32)
+        acc = mfma16x16x32(tr_op(As, pl.pn, k0, ib * 16, li, lg), tr_op(Bs, pl.pd, k0, cb * 16, li, lg), acc);
+      const int e = cb * 16 + li;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = ib * 16 + 4 * lg + q;
+        if (i < n) {
+          const float res = i < n_f ? bf16_to_f32(DMs[i * pl.pd + e]) : bf16_to_f32(Bs[(2 * kp + i - n_f) * pl.pd + e]);
+          Xs[i * pl.pd + e] = to_bf16(acc[q] + res);
+        }
+      }
+    }
+    lds_barrier();
+    uint16_t* dxb = p.dx + b * n * d;
+    for (int q = tid; q < n * d8; q += BT) {
+      const int r = q / d8, c = (q - r * d8) * 8;
+      *reinterpret_cast<u32x4*>(dxb + r * d + c) = *reinterpret_cast<const u32x4*>(Xs + r * pl.pd + c);
+    }
+    lds_barrier();
   }
   // this workgroup's plane: d_Phi [k, n], d_W_L [n_l, n], d_gamma_fm [n k], d_beta_fm [n k]
   float* out = p.part + (int64_t)blockIdx.x * (k * n + n_l * n + 2 * nk);
@@ -587,6 +673,28 @@ __global__ __launch_bounds__(256) void sum_planes_kernel(const float* part, int 
   }
 }
 
+// 32 columns per workgroup; thread (column c, slice s) adds planes s, s + 8,
+// ... in order, then the 8 slices are added in order s = 0 .. 7.
+__global__ __launch_bounds__(256) void sum_many_planes_kernel(const float* part, int planes, int64_t stride,
+                                                              int64_t len, float* out) {
+  __shared__ float red[8][33];
+  const int c = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int64_t col = (int64_t)blockIdx.x * 32 + c;
+  float v = 0.f;
+  if (col < len) {
+#pragma unroll 4
+    for (int q = sl; q < planes; q += 8) v += part[(int64_t)q * stride + col];
+  }
+  red[sl][c] = v;
+  __syncthreads();
+  if (sl == 0 && col < len) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s += red[i][c];
+    out[col] = s;
+  }
+}
+
 int workgroups_for(int64_t batch) { return (int)(batch < 256 ? batch : 256); }
 
 // Lets a kernel take the whole 160 KB of LDS as dynamic shared memory (a host-side attribute, set per launch).
@@ -599,23 +707,35 @@ hipError_t allow_lds(K* kern) {
 
 // ---------------------------------------------------------------- host side
 namespace {
-int fmb_variant(const FmbPlan& f) {
+bool fmb_tiles_fit(const FmbPlan& f) {
   const int ib = f.n16 / 16;
-  for (int v = 0; v < 2; ++v)
-    if (ib * (f.kp / 16) <= kQF[v] * BW && (f.kp / 16) * ib <= kQP[v] * BW && (f.nlp / 16) * ib <= kQL[v] * BW)
-      return v;
-  return -1;
+  return ib * (f.kp / 16) <= kQF * BW && (f.kp / 16) * ib <= kQP * BW && (f.nlp / 16) * ib <= kQL * BW;
 }
 }  // namespace
 
-bool wukong_bwd_supported(int n, int d, int k, int n_l) {
-  if (n <= 0 || d <= 0 || k <= 0 || n_l <= 0 || n_l >= n) return false;
-  if (d % 16 || n % 8 || d > 512) return false;
+namespace {
+// The shapes bwd_out_kernel takes: its LDS plan, X staging and LayerNorm rows fit.
+bool out_supported(int n, int d, int n_l) {
+  if (n <= 0 || d <= 0 || n_l <= 0 || n_l >= n || d % 16 || n % 8 || d > 512) return false;
   const OutPlan a = out_plan(n, d, n_l);
-  const FmbPlan f = fmb_plan(n, d, k, n_l);
-  if (a.bytes > kLdsMax || f.bytes > kLdsMax) return false;
-  return fmb_variant(f) >= 0;
+  if (a.bytes > kLdsMax || !stage_fits(n, d / 8, kMaxXChunks)) return false;
+  const int rows_per_pass = BW * (kWave / a.g);
+  return (n + rows_per_pass - 1) / rows_per_pass <= kMaxRows;
 }
+
+// The shapes bwd_fmb_kernel takes: its LDS plan, staging and register tiles fit.
+bool fmb_supported(int n, int d, int k, int n_l) {
+  if (n <= 0 || d <= 0 || k <= 0 || n_l <= 0 || n_l >= n || d % 16 || n % 8) return false;
+  const FmbPlan f = fmb_plan(n, d, k, n_l);
+  if (f.bytes > kLdsMax) return false;
+  if (!stage_fits(n, d / 8, kMaxXChunks) || !stage_fits(n - n_l, d / 8, kMaxRChunks) ||
+      !stage_fits(n_l, d / 8, kMaxRChunks) || (n * k) % 32 || !stage_fits(n * k / 32, 4, kMaxFChunks))
+    return false;
+  return fmb_tiles_fit(f);
+}
+}  // namespace
+
+bool wukong_bwd_supported(int n, int d, int k, int n_l) { return out_supported(n, d, n_l) && fmb_supported(n, d, k, n_l); }
 
 int wukong_bwd_workgroups(int64_t batch) { return workgroups_for(batch); }
 
@@ -623,7 +743,7 @@ size_t wukong_bwd_out_part_floats(int d) { return (size_t)2 * d; }
 size_t wukong_bwd_fmb_part_floats(int n, int k, int n_l) { return (size_t)k * n + (size_t)n_l * n + 2 * (size_t)n * k; }
 
 hipError_t launch_bwd_out(const BwdOutArgs& a, hipStream_t stream, int64_t* workgroups) {
-  if (!wukong_bwd_supported(a.n, a.d, 1, a.n_l)) return hipErrorInvalidValue;
+  if (!out_supported(a.n, a.d, a.n_l)) return hipErrorInvalidValue;
   const int grid = workgroups_for(a.batch);
   if (workgroups) *workgroups = grid;
   if (grid == 0) return hipSuccess;
@@ -660,7 +780,7 @@ hipError_t launch_bwd_out(const BwdOutArgs& a, hipStream_t stream, int64_t* work
 }
 
 hipError_t launch_bwd_fmb(const BwdFmbArgs& a, hipStream_t stream, int64_t* workgroups) {
-  if (!wukong_bwd_supported(a.n, a.d, a.k, a.n_l)) return hipErrorInvalidValue;
+  if (!fmb_supported(a.n, a.d, a.k, a.n_l)) return hipErrorInvalidValue;
   const int grid = workgroups_for(a.batch);
   if (workgroups) *workgroups = grid;
   if (grid == 0) return hipSuccess;
@@ -682,8 +802,7 @@ hipError_t launch_bwd_fmb(const BwdFmbArgs& a, hipStream_t stream, int64_t* work
   k.n_l = a.n_l;
   k.eps = a.eps;
   const FmbPlan pl = fmb_plan(a.n, a.d, a.k, a.n_l);
-  void (*kern)(BwdFmbKArgs) =
-      fmb_variant(pl) == 0 ? bwd_fmb_kernel<kQF[0], kQP[0], kQL[0]> : bwd_fmb_kernel<kQF[1], kQP[1], kQL[1]>;
+  void (*kern)(BwdFmbKArgs) = bwd_fmb_kernel<kQF, kQP, kQL>;
   const hipError_t e = allow_lds(kern);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(grid), dim3(BT), pl.bytes, stream, k);
@@ -707,6 +826,13 @@ hipError_t launch_sum_planes_strided(const float* part, int planes, int64_t stri
                                      hipStream_t stream) {
   if (planes < 1 || len < 0 || stride < len) return hipErrorInvalidValue;
   if (len == 0) return hipSuccess;
+  if (planes > 8) {  // many planes: 8 threads per column, each over every 8th plane
+    const int64_t grid = (len + 31) / 32;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(sum_many_planes_kernel, dim3((unsigned)grid), dim3(256), 0, stream, part, planes, stride, len,
+                       out);
+    return hipGetLastError();
+  }
   int64_t grid = (len + 255) / 256;
   if (grid > 2048) grid = 2048;
   hipLaunchKernelGGL(sum_planes_kernel, dim3((unsigned)grid), dim3(256), 0, stream, part, planes, stride, len, out);

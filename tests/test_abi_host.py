@@ -235,3 +235,60 @@ def test_fusion_workspace_and_argument_errors():
         _abi.WK_ERR_INVALID_ARG
     assert call(weights=_abi.wk_fusion_weights(0x10000, 0x20008, None, None, 0x20000, None, 0x30000, None)) == \
         _abi.WK_ERR_INVALID_ARG                                       # misaligned bias
+
+
+def test_backward_sizes_and_support():
+    B = 4096
+    # saved activations: Fn, h_1, M
+    assert wk.layer_saved_size(C1, B) == al(B * 4096 * 2) + al(B * 2048 * 2) + al(B * 64 * 160 * 2)
+    lay = wk.saved_layout(C1, B)
+    assert lay == {"fn": 0, "hidden": [al(B * 4096 * 2)], "m": al(B * 4096 * 2) + al(B * 2048 * 2)}
+    assert wk.layer_backward_workspace_size(C1, B) > wk.layer_saved_size(C1, B)
+    # outside the per-example LDS plan (n = 256, d = 160), fp32, d % 16 != 0: unsupported
+    assert wk.layer_saved_size(C2, B) == 0 and wk.layer_backward_workspace_size(C2, B) == 0
+    f32 = wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128), dtype="f32")
+    assert wk.layer_backward_workspace_size(f32, B) == 0
+    assert wk.layer_backward_workspace_size(wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128)), 37) > 0
+
+
+def test_backward_argument_errors_launch_nothing():
+    lib = wk.load_library()
+    spec = wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128))
+    B = 37
+    desc, _dims = spec.make_desc()
+    wp = (ctypes.c_void_p * 2)(0x40000, 0x50000)
+    weights = _abi.wk_layer_weights(0x10000, 0x20000, None, None, ctypes.cast(wp, ctypes.POINTER(ctypes.c_void_p)),
+                                    None, None, None)
+    gw = (ctypes.c_void_p * 2)(0x60000, 0x70000)
+    grads = _abi.wk_layer_grads(0x80000, 0x90000, None, None, ctypes.cast(gw, ctypes.POINTER(ctypes.c_void_p)),
+                                None, None, None)
+    need = wk.layer_backward_workspace_size(spec, B)
+    saved_need = wk.layer_saved_size(spec, B)
+    X, SV, DY, DX, WS = 0x1000000, 0x2000000, 0x3000000, 0x4000000, 0x10000000
+
+    def call(x=X, saved=SV, dy=DY, dx=DX, ws=WS, nbytes=need, g=grads, batch=B):
+        return lib.wukong_layer_backward(ctypes.byref(desc), ctypes.byref(weights), batch, x, saved, dy, dx,
+                                         ctypes.byref(g) if g is not None else None, ws, nbytes, None)
+    assert call(nbytes=need - 1) == _abi.WK_ERR_WORKSPACE
+    assert call(x=None) == _abi.WK_ERR_INVALID_ARG
+    assert call(dy=DY + 8) == _abi.WK_ERR_INVALID_ARG                 # misaligned
+    assert call(dx=X + 256) == _abi.WK_ERR_INVALID_ARG                # dx overlaps x
+    assert call(ws=SV) == _abi.WK_ERR_INVALID_ARG                     # workspace overlaps saved
+    assert call(g=None) == _abi.WK_ERR_INVALID_ARG
+    nogw = (ctypes.c_void_p * 2)(0x60000, None)
+    bad = _abi.wk_layer_grads(0x80000, 0x90000, None, None, ctypes.cast(nogw, ctypes.POINTER(ctypes.c_void_p)),
+                              None, None, None)
+    assert call(g=bad) == _abi.WK_ERR_INVALID_ARG                     # every d_W_t is required
+    assert call(batch=-1) == _abi.WK_ERR_INVALID_ARG
+    assert call(x=None, saved=None, dy=None, dx=None, ws=None, nbytes=0, batch=0) == _abi.WK_OK
+    f32, _d2 = wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128), dtype="f32").make_desc()
+    assert lib.wukong_layer_backward(ctypes.byref(f32), ctypes.byref(weights), B, X, SV, DY, DX, ctypes.byref(grads),
+                                     WS, need, None) == _abi.WK_ERR_UNSUPPORTED
+    # the training forward
+    Y = 0x5000000
+    assert lib.wukong_layer_forward_train(ctypes.byref(desc), ctypes.byref(weights), B, X, Y, SV, saved_need - 1,
+                                          None) == _abi.WK_ERR_WORKSPACE
+    assert lib.wukong_layer_forward_train(ctypes.byref(desc), ctypes.byref(weights), B, X, X + 512, SV, saved_need,
+                                          None) == _abi.WK_ERR_INVALID_ARG
+    assert lib.wukong_layer_forward_train(ctypes.byref(desc), ctypes.byref(weights), 0, None, None, None, 0,
+                                          None) == _abi.WK_OK
