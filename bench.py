@@ -413,6 +413,8 @@ def main():
     ap.add_argument("--no-fusion", action="store_true", help="skip the WHALE fusion-step measurement")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the single-layer training step (forward + backward) measurement")
+    ap.add_argument("--only", choices=("fusion", "training"), default=None,
+                    help="profiling aid: run the stack forward once, then time only this section and print it")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
     args = ap.parse_args()
@@ -457,6 +459,16 @@ def main():
     print(f"# {cfg.name}: inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    if args.only:
+        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
+        torch.cuda.synchronize()
+        if args.only == "fusion":
+            res = measure_fusion(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
+        else:
+            res = measure_training(wk, ws, torch, cfg, layers[0], x, stream, args.steps, args.warmup, args.seed)
+        print(json.dumps({"only": args.only, "config": {"workload": cfg.name, "global_batch": cfg.batch},
+                          args.only: res}), flush=True)
+        return
     for _ in range(args.warmup):
         wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
     torch.cuda.synchronize()
