@@ -247,6 +247,84 @@ def measure_training(wk, ws, torch, cfg, layer, x, stream, steps, warmup, seed):
             "kernels": sorted(kernels, key=lambda k: (k["kernel"], k["index"]))}
 
 
+MOE_EXPERTS = 4  # experts of the measured mixture-of-experts layer
+
+
+def moe_expert_shapes(s, E=MOE_EXPERTS):
+    """E experts of a layer's width: each keeps the layer's k and hidden MLP
+    widths and produces 1/E of its FMB and LCB rows."""
+    if s.n_f % E or s.n_l % E:
+        return None
+    nf, nl = s.n_f // E, s.n_l // E
+    return [(s.k, nf, nl, (s.n * s.k,) + tuple(s.mlp[1:-1]) + (nf * s.d,))] * E
+
+
+def measure_moe(wk, ws, torch, cfg, x, stream, steps, warmup, seed):
+    """A Wukong mixture-of-experts layer (the experts run as grouped launches of
+    the layer kernels) on the workload's input, timed on its own."""
+    if cfg.num_layers != 1:
+        return None
+    s = cfg.layers[0]
+    shapes = moe_expert_shapes(s)
+    if shapes is None:
+        return None
+    specs = [wk.LayerSpec(s.n, s.d, k, nf, nl, mlp, 1e-5, cfg.dtype) for k, nf, nl, mlp in shapes]
+    spec = wk.MoeSpec(specs)
+    need = wk.moe_workspace_size(spec, cfg.batch)
+    if need == 0:
+        return None
+    experts = []
+    for e, (k, nf, nl, mlp) in enumerate(shapes):
+        h = ws.make_expert_weights(cfg.name + "/moe", e, s.n, s.d, k, nl, mlp, cfg.dtype, seed, "identity")
+        experts.append(wk.DeviceLayer.from_host(specs[e], h, device=x.device))
+    og, ob = ws.make_out_layernorm(cfg.name + "/moe", s.d, cfg.dtype, seed, "identity")
+    moe = wk.DeviceMoe(spec, experts, og, ob, device=x.device)
+    y = torch.empty_like(x)
+    mws = wk.alloc_workspace(need, x.device)
+    for _ in range(warmup):
+        wk.moe_forward(x, moe, y=y, workspace=mws, stream=stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wk.moe_forward(x, moe, y=y, workspace=mws, stream=stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = MOE_EXPERTS * (2 + len(s.mlp))
+    trace = wk.Trace(capacity=per * steps + 8)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(steps):
+        wk.moe_forward(x, moe, y=y, workspace=mws, stream=stream, trace=trace)
+    torch.cuda.synchronize()
+    traced_ms = (time.perf_counter() - t1) * 1e3 / steps
+    # per-expert accounting (trace layer index = expert), as kernel_accounting for a layer
+    es = 2 if cfg.dtype == "bf16" else 4
+    B = cfg.batch
+    acct = {}
+    for e, (k, nf, nl, mlp) in enumerate(shapes):
+        acct[("fmb_lcb", e, 0)] = {"flops": B * (2 * (k + nl) * s.n * s.d + 2 * s.n * s.d * k),
+                                   "bytes": B * (s.n * s.d + s.n * k + nl * s.d) * es + (k + nl) * s.n * es}
+        # whether the last Linear carries the output LayerNorm depends on d and that Linear only
+        fused = wk.workspace_layout(wk.LayerSpec(s.n, s.d, k, nf, s.n - nf, mlp, 1e-5, cfg.dtype), B)["m"] < 0
+        T = len(mlp) - 1
+        for t, (a_, b_) in enumerate(zip(mlp[:-1], mlp[1:])):
+            extra = B * b_ if (fused and t == T - 1) else 0
+            acct[("mlp_linear", e, t)] = {"flops": 2 * B * a_ * b_, "bytes": (B * a_ + a_ * b_ + B * b_ + b_ + extra) * es}
+        if not fused:
+            acct[("residual_ln", e, 0)] = {"flops": 0, "bytes": 3 * B * nf * s.d * es}
+    flops = sum(v["flops"] for v in acct.values())
+    kernels, dom = summarize_trace(trace.records(), acct, traced_ms, steps)
+    trace.close()
+    roof = None
+    if dom is not None:
+        roof = roofline_of(dom, acct[(dom["kernel"], dom["layer"], dom["index"])], dom["avg_ms"], cfg.dtype, cfg.name)
+    return {"experts": [{"k": k, "n_f": nf, "n_l": nl, "mlp": list(mlp)} for k, nf, nl, mlp in shapes],
+            "ms_per_call": round(ms, 4), "examples_per_s": round(cfg.batch / ms * 1e3, 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
+                                                                                PEAK_BF16_TFLOPS, 4),
+            "roofline": roof, "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"], k["index"]))}
+
+
 def measure_head(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
     """The prediction head (top MLP + logistic function) on the stack's output,
     timed on its own: widths cfg.head_dims(), Xavier-uniform weights."""
@@ -413,7 +491,8 @@ def main():
     ap.add_argument("--no-fusion", action="store_true", help="skip the WHALE fusion-step measurement")
     ap.add_argument("--no-training", action="store_true",
                     help="skip the single-layer training step (forward + backward) measurement")
-    ap.add_argument("--only", choices=("fusion", "training"), default=None,
+    ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts layer measurement")
+    ap.add_argument("--only", choices=("fusion", "training", "moe"), default=None,
                     help="profiling aid: run the stack forward once, then time only this section and print it")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (counter calibration)")
@@ -464,6 +543,8 @@ def main():
         torch.cuda.synchronize()
         if args.only == "fusion":
             res = measure_fusion(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
+        elif args.only == "moe":
+            res = measure_moe(wk, ws, torch, cfg, x, stream, args.steps, args.warmup, args.seed)
         else:
             res = measure_training(wk, ws, torch, cfg, layers[0], x, stream, args.steps, args.warmup, args.seed)
         print(json.dumps({"only": args.only, "config": {"workload": cfg.name, "global_batch": cfg.batch},
@@ -592,6 +673,12 @@ def main():
                   f"(forward {training['forward_train_ms']:.3f}, backward {training['backward_ms']:.3f})",
                   file=sys.stderr, flush=True)
 
+    moe = None
+    if not args.no_moe and cfg.dtype == "bf16":
+        moe = measure_moe(wk, ws, torch, cfg, x, stream, args.steps, args.warmup, args.seed)
+        if moe is not None:
+            print(f"# mixture of {MOE_EXPERTS} experts: {moe['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
+
     step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
     s0 = cfg.layers[0]
     out = {
@@ -622,6 +709,7 @@ def main():
         "head": head,
         "fusion": fusion,
         "training": training,
+        "moe": moe,
     }
     if not args.no_cpu_baseline:
         del x, y, ws_t, layers

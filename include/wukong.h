@@ -234,6 +234,43 @@ int32_t wukong_head_forward_traced(const wk_head_desc* desc, const wk_head_weigh
                                    const void* y, float* prob, void* workspace, size_t workspace_bytes,
                                    void* stream, wk_trace* trace);
 
+/* ---- Wukong mixture of experts -------------------------------------------
+ * Kunlun technical summary, section 2.3: the global interaction module runs
+ * several Wukong modules side by side within one layer, spreading the
+ * layer's computation over them.  The page gives no formula; reading taken
+ * here: expert e is a whole Wukong module on the layer input X (its own Phi_e,
+ * FM LayerNorm, MLP and W_L) producing n_f,e FMB rows and n_l,e LCB rows;
+ * the layer output is
+ *   Y = LN_d([M_1; ...; M_E; Lc_1; ...; Lc_E] + X; gamma_out, beta_out)
+ * (FMB rows of every expert first, in expert order, then the LCB rows), with
+ * sum_e (n_f,e + n_l,e) = n.  With one expert it is wukong_layer_forward.
+ * The experts run one after another on the stream (the same kernels, grouped
+ * launches), sharing one workspace. */
+typedef struct {
+  int32_t num_experts;           /* 1 .. 64                                           */
+  const wk_layer_desc* experts;  /* host array [num_experts]: equal n, d, dtype and
+                                    ln_eps; n_f / n_l are the expert's own row counts;
+                                    bf16 experts need d % 16 == 0                      */
+} wk_moe_desc;
+
+/* Workspace bytes for wukong_moe_layer_forward (the largest expert's layer
+ * workspace), 0 if desc is invalid or unsupported. */
+size_t wukong_moe_layer_workspace_size(const wk_moe_desc* desc, int64_t batch);
+
+/* y [batch, n, d] from x [batch, n, d].  experts: host array of num_experts
+ * weight sets (their out_ln_gamma / out_ln_beta are ignored); out_ln_gamma /
+ * out_ln_beta [d] (or NULL) are the layer's output LayerNorm.  Same
+ * conventions as wukong_layer_forward. */
+int32_t wukong_moe_layer_forward(const wk_moe_desc* desc, const wk_layer_weights* experts, const void* out_ln_gamma,
+                                 const void* out_ln_beta, int64_t batch, const void* x, void* y, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+/* As wukong_moe_layer_forward, recording one event pair per launch into
+ * `trace` (the layer index of a record is the expert index). */
+int32_t wukong_moe_layer_forward_traced(const wk_moe_desc* desc, const wk_layer_weights* experts,
+                                        const void* out_ln_gamma, const void* out_ln_beta, int64_t batch,
+                                        const void* x, void* y, void* workspace, size_t workspace_bytes,
+                                        void* stream, wk_trace* trace);
+
 /* ---- Backward pass of one layer ------------------------------------------
  * The pages train the stack end to end (Wukong paper, xdnf.cn repost,
  * section 3.2.1: the dense layers are trained with Adam; WHALE technical

@@ -7,14 +7,15 @@ concatenated, the residual is added and a LayerNorm is applied; layers are
 stacked; a prediction head (top MLP + logistic function) can follow the
 stack, WHALE's fusion step (shared K = V cross-attention, Fusion MLP,
 pre-norm shared-gate SwiGLU) combines a layer's output with a sequence, and
-a layer's backward pass gives the input and weight gradients for training.
+a layer's backward pass gives the input and weight gradients for training,
+and a mixture-of-experts layer runs several Wukong modules side by side.
 The compute runs in hand-written HIP kernels for gfx950 behind the C ABI in
 include/wukong.h; this package is the Python binding.
 """
 from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceFusion, DeviceHead, DeviceLayer,  # noqa: F401
                    FusionSpec, HeadSpec, LayerGrads, LayerSpec, Trace, WukongError, alloc_workspace,
                    fusion_forward, layer_backward, layer_backward_workspace_size, layer_forward_train,
-                   layer_saved_size, saved_layout,
+                   layer_saved_size, saved_layout, MoeSpec, DeviceMoe, moe_forward, moe_workspace_size,
                    fusion_workspace_size, head_forward, head_workspace_size,
                    layer_forward, layer_workspace_size, library_path, load_library, stack_forward,
                    stack_workspace_size, status_string, to_device, workspace_layout, EXPORTED_SYMBOLS)

@@ -71,6 +71,10 @@ class wk_layer_grads(ctypes.Structure):
                 ("out_ln_gamma", ctypes.c_void_p), ("out_ln_beta", ctypes.c_void_p)]
 
 
+class wk_moe_desc(ctypes.Structure):
+    _fields_ = [("num_experts", ctypes.c_int32), ("experts", ctypes.POINTER(wk_layer_desc))]
+
+
 class wk_workspace_layout(ctypes.Structure):
     _fields_ = [("fn", ctypes.c_int64), ("m", ctypes.c_int64), ("num_hidden", ctypes.c_int32),
                 ("hidden", ctypes.c_int64 * 8)]
@@ -108,6 +112,14 @@ _SIGNATURES = [
     ("wukong_fusion_forward_traced", ctypes.c_int32,
      [ctypes.POINTER(wk_fusion_desc), ctypes.POINTER(wk_fusion_weights), ctypes.c_int64, ctypes.c_void_p,
       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_moe_layer_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_moe_desc), ctypes.c_int64]),
+    ("wukong_moe_layer_forward", ctypes.c_int32,
+     [ctypes.POINTER(wk_moe_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_void_p, ctypes.c_void_p,
+      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_moe_layer_forward_traced", ctypes.c_int32,
+     [ctypes.POINTER(wk_moe_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_void_p, ctypes.c_void_p,
+      ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+      ctypes.c_void_p]),
     ("wukong_layer_saved_size", ctypes.c_size_t, [ctypes.POINTER(wk_layer_desc), ctypes.c_int64]),
     ("wukong_layer_forward_train", ctypes.c_int32,
      [ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64, ctypes.c_void_p,
@@ -322,6 +334,62 @@ def layer_forward(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.Tensor]
                                   y.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream_handle(stream))
     _check(st, "wukong_layer_forward")
+    return y
+
+
+# ------------------------------------------------------------------ mixture of experts
+class MoeSpec:
+    """A mixture-of-experts layer: one LayerSpec per expert (equal n, d, dtype, eps;
+    n_f / n_l are the expert's own FMB / LCB row counts, adding up to n over the experts)."""
+
+    def __init__(self, experts: Sequence[LayerSpec]):
+        self.experts = tuple(experts)
+
+    def make_desc(self):
+        pairs = [e.make_desc() for e in self.experts]
+        arr = (wk_layer_desc * len(pairs))(*[p[0] for p in pairs])
+        desc = wk_moe_desc(len(pairs), ctypes.cast(arr, ctypes.POINTER(wk_layer_desc)))
+        return desc, (arr, pairs)
+
+
+class DeviceMoe:
+    """Experts' parameters (DeviceLayer each) plus the layer's output LayerNorm, with the C descriptors."""
+
+    def __init__(self, spec: MoeSpec, experts: Sequence[DeviceLayer], out_gamma=None, out_beta=None,
+                 device="cuda"):
+        if len(experts) != len(spec.experts):
+            raise ValueError("one DeviceLayer per expert")
+        dt = spec.experts[0].dtype
+        self.spec = spec
+        self.experts = list(experts)
+        self.out_gamma = None if out_gamma is None else to_device(out_gamma, dt, device)
+        self.out_beta = None if out_beta is None else to_device(out_beta, dt, device)
+        self.desc, self._keep = spec.make_desc()
+        self.weights = (wk_layer_weights * len(experts))(*[e.weights for e in experts])
+
+
+def moe_workspace_size(spec: MoeSpec, batch: int) -> int:
+    desc, _keep = spec.make_desc()
+    return int(load_library().wukong_moe_layer_workspace_size(ctypes.byref(desc), batch))
+
+
+def moe_forward(x: torch.Tensor, moe: DeviceMoe, y: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None, trace: "Trace" = None) -> torch.Tensor:
+    """One mixture-of-experts layer on x [batch, n, d]; returns y [batch, n, d]."""
+    lib = load_library()
+    B = _check_x(x, moe.spec.experts[0])
+    y = torch.empty_like(x) if y is None else y
+    need = moe_workspace_size(moe.spec, B)
+    if need == 0:
+        raise WukongError(WK_ERR_UNSUPPORTED, "wukong_moe_layer_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    args = [ctypes.byref(moe.desc), moe.weights, _ptr(moe.out_gamma), _ptr(moe.out_beta), B, x.data_ptr(),
+            y.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream)]
+    if trace is None:
+        _check(lib.wukong_moe_layer_forward(*args), "wukong_moe_layer_forward")
+    else:
+        _check(lib.wukong_moe_layer_forward_traced(*args, trace.handle), "wukong_moe_layer_forward_traced")
     return y
 
 

@@ -44,7 +44,9 @@ bool overlap(const void* a, size_t an, const void* b, size_t bn) {
   return an > 0 && bn > 0 && x < y + bn && y < x + an;
 }
 
-int32_t check_desc(const wk_layer_desc* d) {
+// expert = true: one expert of a mixture-of-experts layer, whose FMB and LCB
+// rows are a share of the layer's n output rows (n_f + n_l < n allowed).
+int32_t check_desc(const wk_layer_desc* d, bool expert = false) {
   if (!d) return WK_ERR_INVALID_ARG;
   if (d->n <= 0 || d->d <= 0 || d->k <= 0 || d->n_f <= 0 || d->n_l <= 0) return WK_ERR_INVALID_ARG;
   if (d->num_linear < 1 || d->num_linear > kMaxLinear || !d->mlp_dims) return WK_ERR_INVALID_ARG;
@@ -56,7 +58,9 @@ int32_t check_desc(const wk_layer_desc* d) {
   if (nk > INT32_MAX || nfd > INT32_MAX) return WK_ERR_INVALID_ARG;
   if (d->mlp_dims[0] != nk || d->mlp_dims[d->num_linear] != nfd) return WK_ERR_INVALID_ARG;
   // The residual adds X row by row, so the concatenation must have n rows.
-  if (d->n_f + d->n_l != d->n) return WK_ERR_UNSUPPORTED;
+  if (expert ? d->n_f + d->n_l > d->n : d->n_f + d->n_l != d->n) return WK_ERR_UNSUPPORTED;
+  // the unit-width FMB+LCB step writes the LCB rows up to row n
+  if (expert && d->dtype == WK_BF16 && d->d % 16 != 0) return WK_ERR_UNSUPPORTED;
   if (d->dtype == WK_BF16) {
     const bool units = wk::fmb_lcb_units_supported(d->n, d->d, d->k, d->n_l);
     if ((d->d % 16 && !units) || d->n % 8 || d->k % 4) return WK_ERR_UNSUPPORTED;
@@ -160,12 +164,28 @@ struct Launch {
   }
 };
 
+// Where a layer's output rows go: its FMB rows start at row fmb_row0 and its
+// LCB rows at lcb_row0 of each example's n rows (the residual reads the same
+// rows of X); the output LayerNorm's gamma / beta.  A plain layer has
+// fmb_row0 = 0, lcb_row0 = n_f and its own gamma / beta; an expert of a
+// mixture-of-experts layer has its share of the rows and the layer's.
+struct RowMap {
+  int fmb_row0, lcb_row0;
+  const void* out_gamma;
+  const void* out_beta;
+};
+
 // Launches one layer; all arguments already checked.
 int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t batch, const void* x,
-                  void* y, char* scratch, const LayerPlan& plan, Launch& launch, int layer_idx) {
+                  void* y, char* scratch, const LayerPlan& plan, Launch& launch, int layer_idx,
+                  const RowMap* rows = nullptr) {
   const bool bf = d.dtype == WK_BF16;
   char* fn = scratch + plan.fn;
   char* mbuf = scratch + plan.m;
+  const RowMap rm = rows ? *rows : RowMap{0, d.n_f, w.out_ln_gamma, w.out_ln_beta};
+  const size_t fmb_off = (size_t)rm.fmb_row0 * d.d * esize(d.dtype);
+  const void* x_f = static_cast<const char*>(x) + fmb_off;
+  void* y_f = static_cast<char*>(y) + fmb_off;
   int32_t st;
   if (bf) {
     wk::FmbLcbArgs a;
@@ -174,11 +194,11 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.w_l = static_cast<const uint16_t*>(w.w_l);
     a.fm_gamma = static_cast<const uint16_t*>(w.fm_ln_gamma);
     a.fm_beta = static_cast<const uint16_t*>(w.fm_ln_beta);
-    a.out_gamma = static_cast<const uint16_t*>(w.out_ln_gamma);
-    a.out_beta = static_cast<const uint16_t*>(w.out_ln_beta);
+    a.out_gamma = static_cast<const uint16_t*>(rm.out_gamma);
+    a.out_beta = static_cast<const uint16_t*>(rm.out_beta);
     a.fn = reinterpret_cast<uint16_t*>(fn);
     a.y = static_cast<uint16_t*>(y);
-    a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = d.n_f; a.n_l = d.n_l; a.eps = d.ln_eps;
+    a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = rm.lcb_row0; a.n_l = d.n_l; a.eps = d.ln_eps;
     if (plan.use_units) {
       void* us = scratch + plan.units;
       st = launch(WK_KERNEL_FMB_LCB, layer_idx, 0,
@@ -194,11 +214,11 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.w_l = static_cast<const float*>(w.w_l);
     a.fm_gamma = static_cast<const float*>(w.fm_ln_gamma);
     a.fm_beta = static_cast<const float*>(w.fm_ln_beta);
-    a.out_gamma = static_cast<const float*>(w.out_ln_gamma);
-    a.out_beta = static_cast<const float*>(w.out_ln_beta);
+    a.out_gamma = static_cast<const float*>(rm.out_gamma);
+    a.out_beta = static_cast<const float*>(rm.out_beta);
     a.fn = reinterpret_cast<float*>(fn);
     a.y = static_cast<float*>(y);
-    a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = d.n_f; a.n_l = d.n_l; a.eps = d.ln_eps;
+    a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = rm.lcb_row0; a.n_l = d.n_l; a.eps = d.ln_eps;
     st = launch(WK_KERNEL_FMB_LCB, layer_idx, 0,
                 [&](int64_t* g) { return wk::launch_fmb_lcb_f32(a, batch, launch.stream, g); });
   }
@@ -232,10 +252,10 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.a = in;
     a.w = w.mlp_w[t];
     a.bias = w.mlp_b ? w.mlp_b[t] : nullptr;
-    a.x = x;
-    a.gamma = w.out_ln_gamma;
-    a.beta = w.out_ln_beta;
-    a.y = y;
+    a.x = x_f;
+    a.gamma = rm.out_gamma;
+    a.beta = rm.out_beta;
+    a.y = y_f;
     a.M = batch;
     a.N = d.mlp_dims[t + 1];
     a.K = d.mlp_dims[t];
@@ -248,10 +268,10 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
 
   wk::ResidLnArgs r;
   r.m = mbuf;
-  r.x = x;
-  r.gamma = w.out_ln_gamma;
-  r.beta = w.out_ln_beta;
-  r.y = y;
+  r.x = x_f;
+  r.gamma = rm.out_gamma;
+  r.beta = rm.out_beta;
+  r.y = y_f;
   r.batch = batch;
   r.n = d.n;
   r.d = d.d;
@@ -500,6 +520,65 @@ int32_t fusion_forward(const wk_fusion_desc* d, const wk_fusion_weights* w, int6
   st = linear(1, qn, w->w_up, w->b_up, g, d->d_ff, d->d, wk::kActSiluGate, nullptr);
   if (st != WK_OK) return st;
   return linear(2, g, w->w_down, w->b_down, hf, d->d, d->d_ff, wk::kActNone, q);
+}
+
+// ---- mixture of experts: several Wukong modules in one layer, each writing
+// its share of the output rows (FMB rows of every expert first, then LCB rows).
+constexpr int kMaxExperts = 64;
+
+int32_t check_moe(const wk_moe_desc* m, int64_t batch, size_t* bytes) {
+  if (!m || !m->experts || m->num_experts < 1 || m->num_experts > kMaxExperts) return WK_ERR_INVALID_ARG;
+  if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
+  const wk_layer_desc& e0 = m->experts[0];
+  int64_t rows = 0;
+  size_t need = 0;
+  for (int e = 0; e < m->num_experts; ++e) {
+    const wk_layer_desc& d = m->experts[e];
+    const int32_t st = check_desc(&d, true);
+    if (st != WK_OK) return st;
+    if (d.n != e0.n || d.d != e0.d || d.dtype != e0.dtype || d.ln_eps != e0.ln_eps) return WK_ERR_INVALID_ARG;
+    rows += (int64_t)d.n_f + d.n_l;
+    const size_t b = plan_layer(d, batch).bytes;
+    need = b > need ? b : need;
+  }
+  if (rows != e0.n) return WK_ERR_UNSUPPORTED;  // the residual needs n output rows
+  if (bytes) *bytes = need ? need : kAlign;
+  return WK_OK;
+}
+
+int32_t moe_forward(const wk_moe_desc* m, const wk_layer_weights* weights, const void* out_gamma,
+                    const void* out_beta, int64_t batch, const void* x, void* y, void* ws, size_t ws_bytes,
+                    void* stream, wk_trace* trace) {
+  size_t need = 0;
+  int32_t st = check_moe(m, batch, &need);
+  if (st != WK_OK) return st;
+  if (!weights) return WK_ERR_INVALID_ARG;
+  for (int e = 0; e < m->num_experts; ++e) {
+    st = check_weights(m->experts[e], &weights[e]);
+    if (st != WK_OK) return st;
+  }
+  if ((out_gamma && !aligned16(out_gamma)) || (out_beta && !aligned16(out_beta))) return WK_ERR_INVALID_ARG;
+  if (batch == 0) return WK_OK;
+  const wk_layer_desc& e0 = m->experts[0];
+  const size_t act = (size_t)batch * e0.n * e0.d * esize(e0.dtype);
+  if (!x || !y || !aligned16(x) || !aligned16(y)) return WK_ERR_INVALID_ARG;
+  if (overlap(x, act, y, act)) return WK_ERR_INVALID_ARG;
+  if (!ws || !aligned16(ws)) return WK_ERR_INVALID_ARG;
+  if (ws_bytes < need) return WK_ERR_WORKSPACE;
+  if (overlap(ws, need, x, act) || overlap(ws, need, y, act)) return WK_ERR_INVALID_ARG;
+  int n_f_total = 0;
+  for (int e = 0; e < m->num_experts; ++e) n_f_total += m->experts[e].n_f;
+  Launch launch{trace, static_cast<hipStream_t>(stream)};
+  int fmb_row = 0, lcb_row = n_f_total;
+  for (int e = 0; e < m->num_experts; ++e) {
+    const wk_layer_desc& d = m->experts[e];
+    const RowMap rm{fmb_row, lcb_row, out_gamma, out_beta};
+    st = run_layer(d, weights[e], batch, x, y, static_cast<char*>(ws), plan_layer(d, batch), launch, e, &rm);
+    if (st != WK_OK) return st;
+    fmb_row += d.n_f;
+    lcb_row += d.n_l;
+  }
+  return WK_OK;
 }
 
 // ---- backward of one bf16 layer.
@@ -904,6 +983,27 @@ int32_t wukong_fusion_forward_traced(const wk_fusion_desc* desc, const wk_fusion
                                      size_t workspace_bytes, void* stream, wk_trace* trace) {
   if (!trace) return WK_ERR_INVALID_ARG;
   return fusion_forward(desc, weights, batch, hw, hs, hf, workspace, workspace_bytes, stream, trace);
+}
+
+size_t wukong_moe_layer_workspace_size(const wk_moe_desc* desc, int64_t batch) {
+  size_t b = 0;
+  return check_moe(desc, batch, &b) == WK_OK ? b : 0;
+}
+
+int32_t wukong_moe_layer_forward(const wk_moe_desc* desc, const wk_layer_weights* experts, const void* out_ln_gamma,
+                                 const void* out_ln_beta, int64_t batch, const void* x, void* y, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  return moe_forward(desc, experts, out_ln_gamma, out_ln_beta, batch, x, y, workspace, workspace_bytes, stream,
+                     nullptr);
+}
+
+int32_t wukong_moe_layer_forward_traced(const wk_moe_desc* desc, const wk_layer_weights* experts,
+                                        const void* out_ln_gamma, const void* out_ln_beta, int64_t batch,
+                                        const void* x, void* y, void* workspace, size_t workspace_bytes,
+                                        void* stream, wk_trace* trace) {
+  if (!trace) return WK_ERR_INVALID_ARG;
+  return moe_forward(desc, experts, out_ln_gamma, out_ln_beta, batch, x, y, workspace, workspace_bytes, stream,
+                     trace);
 }
 
 size_t wukong_layer_saved_size(const wk_layer_desc* desc, int64_t batch) {

@@ -183,12 +183,24 @@ class HostLayerWeights:
 def make_layer_weights(cfg_name: str, layer: int, shape: LayerShape, dtype: str, seed: int,
                        affine: str = "identity") -> HostLayerWeights:
     """Xavier-uniform weights of one layer.  affine: 'identity' or 'random'."""
-    t = f"{cfg_name}/L{layer}"
-    n, d, k = shape.n, shape.d, shape.k
+    return _module_weights(f"{cfg_name}/L{layer}", shape.n, shape.d, shape.k, shape.n_l, shape.mlp, dtype, seed,
+                           affine)
+
+
+def make_expert_weights(tag: str, expert: int, n: int, d: int, k: int, n_l: int, mlp, dtype: str, seed: int,
+                        affine: str = "identity") -> HostLayerWeights:
+    """Xavier-uniform weights of one expert of a mixture-of-experts layer (a
+    Wukong module with its own k, LCB rows n_l and MLP widths mlp, ending in
+    n_F * d).  Its out_gamma / out_beta are drawn but the layer's own are used."""
+    return _module_weights(f"{tag}/E{expert}", n, d, k, n_l, tuple(mlp), dtype, seed, affine)
+
+
+def _module_weights(t: str, n: int, d: int, k: int, n_l: int, mlp, dtype: str, seed: int,
+                    affine: str) -> HostLayerWeights:
     phi = xavier_uniform(seed, f"{t}/phi", k, n, dtype)
-    w_l = xavier_uniform(seed, f"{t}/w_l", shape.n_l, n, dtype)
+    w_l = xavier_uniform(seed, f"{t}/w_l", n_l, n, dtype)
     mlp_w, mlp_b = [], []
-    for i, (a, b) in enumerate(zip(shape.mlp[:-1], shape.mlp[1:])):
+    for i, (a, b) in enumerate(zip(mlp[:-1], mlp[1:])):
         mlp_w.append(xavier_uniform(seed, f"{t}/mlp_w{i}", b, a, dtype))
         if affine == "random":
             mlp_b.append(_store(_uniform_pm(seed, f"{t}/mlp_b{i}", b, 0.5), dtype))
@@ -328,3 +340,13 @@ def make_upstream_grad(cfg: WukongConfig, seed: int, batch: Optional[int] = None
     s0 = cfg.layers[0]
     b = cfg.batch if batch is None else batch
     return _draw(seed, f"{cfg.name}/dy", b * s0.n * s0.d, "normal", dtype=cfg.dtype).reshape(b, s0.n, s0.d)
+
+
+def make_out_layernorm(tag: str, d: int, dtype: str, seed: int, affine: str = "identity"):
+    """(gamma, beta) [d] of a layer's output LayerNorm: 1 and 0, or 1 + U(-0.5, 0.5) and U(-0.5, 0.5)."""
+    if affine == "identity":
+        return _store(np.ones(d, np.float32), dtype), _store(np.zeros(d, np.float32), dtype)
+    if affine != "random":
+        raise ValueError(affine)
+    return (_store(_uniform_pm(seed, f"{tag}/out_gamma", d, 0.5, 1.0), dtype),
+            _store(_uniform_pm(seed, f"{tag}/out_beta", d, 0.5), dtype))
