@@ -292,3 +292,35 @@ def test_backward_argument_errors_launch_nothing():
                                           None) == _abi.WK_ERR_INVALID_ARG
     assert lib.wukong_layer_forward_train(ctypes.byref(desc), ctypes.byref(weights), 0, None, None, None, 0,
                                           None) == _abi.WK_OK
+
+
+def test_moe_sizes_and_argument_errors():
+    lib = wk.load_library()
+    E = [wk.LayerSpec(128, 160, 32, 16, 16, (4096, 2048, 2560)) for _ in range(4)]
+    B = 64
+    one = wk.layer_workspace_size(wk.LayerSpec(128, 160, 32, 16, 112, (4096, 2048, 2560)), B)
+    assert wk.moe_workspace_size(wk.MoeSpec(E), B) == one            # experts share one layer workspace
+    assert wk.moe_workspace_size(wk.MoeSpec(E[:3]), B) == 0         # rows must add up to n
+    bad_d = E[:3] + [wk.LayerSpec(128, 80, 32, 16, 16, (4096, 2048, 1280))]
+    assert wk.moe_workspace_size(wk.MoeSpec(bad_d), B) == 0         # equal d
+    units = [wk.LayerSpec(64, 8, 4, 16, 16, (256, 128)) for _ in range(2)]
+    assert wk.moe_workspace_size(wk.MoeSpec(units), B) == 0         # bf16 experts need d % 16 == 0
+    spec = wk.MoeSpec(E)
+    desc, _keep = spec.make_desc()
+    wp = [(ctypes.c_void_p * 2)(0x40000 + 0x1000 * e, 0x80000 + 0x1000 * e) for e in range(4)]
+    ws_arr = (_abi.wk_layer_weights * 4)(*[
+        _abi.wk_layer_weights(0x10000, 0x20000, None, None, ctypes.cast(wp[e], ctypes.POINTER(ctypes.c_void_p)),
+                              None, None, None) for e in range(4)])
+    need = wk.moe_workspace_size(spec, B)
+    X, Y, WS = 0x1000000, 0x2000000, 0x10000000
+
+    def call(x=X, y=Y, ws=WS, nbytes=need, gamma=None, beta=None, batch=B):
+        return lib.wukong_moe_layer_forward(ctypes.byref(desc), ws_arr, gamma, beta, batch, x, y, ws, nbytes, None)
+    assert call(nbytes=need - 1) == _abi.WK_ERR_WORKSPACE
+    assert call(x=None) == _abi.WK_ERR_INVALID_ARG
+    assert call(y=X + 512) == _abi.WK_ERR_INVALID_ARG                 # output overlaps input
+    assert call(gamma=0x30008) == _abi.WK_ERR_INVALID_ARG             # misaligned gamma
+    assert call(batch=-1) == _abi.WK_ERR_INVALID_ARG
+    assert call(x=None, y=None, ws=None, nbytes=0, batch=0) == _abi.WK_OK
+    desc.num_experts = 0
+    assert call() == _abi.WK_ERR_INVALID_ARG
