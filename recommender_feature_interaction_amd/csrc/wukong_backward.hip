@@ -23,7 +23,13 @@
 // One workgroup of 8 waves walks examples blockIdx.x, + gridDim.x, ... and
 // keeps the weight-gradient sums of its examples in registers; the host then
 // adds the per-workgroup planes in a fixed order (launch_sum_planes), so every
-// result is independent of timing.  X of one example, the LDS copies of Phi
+// result is independent of timing.  An example's inputs are fetched into
+// registers one example ahead (all of a thread's 16-byte loads together) and
+// written to LDS at the top of the next iteration; barriers are LDS-only, so
+// those loads stay in flight through the compute phases.  Nothing else reads
+// global memory inside the example loop: a load issued behind the prefetch
+// would wait for it (the vector-memory counter retires in order), which is
+// why W_L's operands are held in registers.  X of one example, the LDS copies of Phi
 // and W_L and the per-example operands all live in LDS (up to 160 KB per
 // workgroup on gfx950): the shapes this covers are those whose LDS plan and
 // per-wave tile counts fit (wukong_bwd_supported).
@@ -90,6 +96,27 @@ __device__ __forceinline__ float block_sum(float v, float* red, int slot) {
   return s;
 }
 
+// Two sums at once (red holds 2 slots of 2 BW floats).
+__device__ __forceinline__ void block_sum2(float& a, float& b, float* red, int slot) {
+  a = xor_sum<1>(a);
+  b = xor_sum<1>(b);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* r = red + slot * 2 * BW;
+  if (lane == 0) {
+    r[wave] = a;
+    r[BW + wave] = b;
+  }
+  lds_barrier();
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int w = 0; w < BW; ++w) {
+    sa += r[w];
+    sb += r[BW + w];
+  }
+  a = sa;
+  b = sb;
+}
+
 __device__ __forceinline__ void zero_lds(uint16_t* base, int bytes) {
   for (int i = threadIdx.x * 16; i < bytes; i += BT * 16)
     *reinterpret_cast<u32x4*>(reinterpret_cast<char*>(base) + i) = u32x4{0u, 0u, 0u, 0u};
@@ -134,16 +161,45 @@ __device__ __forceinline__ void stage_rows(uint16_t* smem_base, int off, int pit
   }
 }
 
+// stage_rows in two halves, so the loads can be issued one example ahead:
+// fetch_rows puts a thread's chunks in registers, put_rows writes them to LDS.
+template <int MAXC>
+__device__ __forceinline__ void fetch_rows(u32x4 (&reg)[MAXC], const uint16_t* src, int rows, int c8) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int rpp = BT / c8, r0 = tid / c8, c = (tid - r0 * c8) * 8;
+  const bool act = r0 < rpp;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int r = r0 + i * rpp;
+    if (act && r < rows) reg[i] = *reinterpret_cast<const u32x4*>(src + (int64_t)r * c8 * 8 + c);
+  }
+}
+
+template <int MAXC>
+__device__ __forceinline__ void put_rows(const u32x4 (&reg)[MAXC], uint16_t* smem_base, int off, int pitch, int rows,
+                                         int c8) {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int rpp = BT / c8, r0 = tid / c8, c = (tid - r0 * c8) * 8;
+  const bool act = r0 < rpp;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int r = r0 + i * rpp;
+    if (act && r < rows) *reinterpret_cast<u32x4*>(smem_base + off + r * pitch + c) = reg[i];
+  }
+}
+
 // ---------------------------------------------------------------- LDS plans
 constexpr int kMaxXChunks = 6;  // 16-byte chunks of X per thread and example
 constexpr int kMaxRChunks = 3;  // ... of dLc, and of the FMB rows of dR
 constexpr int kMaxFChunks = 2;  // ... of d_Fn (as rows of 4 chunks)
-constexpr int kMaxRows = 8;     // LayerNorm rows per lane group and example (bwd_out_kernel)
-constexpr int kRowBatch = 4;    // ... whose loads are issued together
+constexpr int kMaxKa = 256;     // the dX product's contraction 2 k + n_l, padded
+constexpr int kLcK = 8;         // K steps of W_L X held as registers (n <= 256)
 
 struct OutPlan {  // bwd_out_kernel
-  int n32, pd, pn, nlp, g;
-  int xs, wl, ls, red, bytes;  // byte offsets
+  int n32, pd, nlp, g;
+  int xs, ys, ms, ls, bytes;  // byte offsets: X, dY, M (bf16, pitch pd), Lc (fp32, pitch d)
 };
 
 __host__ __device__ inline int pow2_at_least(int v) {
@@ -156,14 +212,14 @@ __host__ __device__ inline OutPlan out_plan(int n, int d, int n_l) {
   OutPlan p;
   p.n32 = up32(n);
   p.pd = up32(d) + 8;
-  p.pn = p.n32 + 8;
   p.nlp = up16(n_l);
   p.g = pow2_at_least((d + 7) / 8);
   p.xs = 0;
-  p.wl = p.xs + p.n32 * p.pd * 2;
-  p.ls = p.wl + p.nlp * p.pn * 2;
-  p.red = p.ls + p.nlp * d * 4;
-  p.bytes = p.red + BW * 2 * d * 4;
+  p.ys = p.xs + p.n32 * p.pd * 2;
+  p.ms = p.ys + n * p.pd * 2;
+  p.ls = p.ms + (n - n_l) * p.pd * 2;
+  const int ls_bytes = p.nlp * d * 4, red_bytes = BW * 2 * d * 4;  // the sums reuse Lc's LDS at the end
+  p.bytes = p.ls + (ls_bytes > red_bytes ? ls_bytes : red_bytes);
   return p;
 }
 
@@ -188,7 +244,7 @@ __host__ __device__ inline FmbPlan fmb_plan(int n, int d, int k, int n_l) {
   p.dms = p.bs + p.ka * p.pd * 2;
   p.dfs = p.dms + (n - n_l) * p.pd * 2;
   p.red = p.dfs + (n * k * 2 + 15) / 16 * 16;
-  p.bytes = p.red + 2 * BW * 4;
+  p.bytes = p.red + 6 * BW * 4;  // block_sum's 2 slots, block_sum2's 2 slots of 2
   return p;
 }
 
@@ -210,12 +266,12 @@ struct BwdOutKArgs {
 template <int G>
 __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
   extern __shared__ __align__(16) uint16_t smem[];
-  const int n = p.n, d = p.d, n_f = p.n_f, n_l = p.n_l;
+  const int n = p.n, d = p.d, n_f = p.n_f, n_l = p.n_l, d8 = d / 8;
   const OutPlan pl = out_plan(n, d, n_l);
   uint16_t* Xs = smem + pl.xs / 2;
-  uint16_t* WLs = smem + pl.wl / 2;
+  const uint16_t* Ys = smem + pl.ys / 2;
+  const uint16_t* Ms = smem + pl.ms / 2;
   float* Ls = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + pl.ls);
-  float* red = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + pl.red);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lg = lane >> 4;
   constexpr int RPW = kWave / G;  // rows per wave and pass
@@ -223,9 +279,8 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
   const bool col_ok = c < d;
   const int row0 = wave * RPW + grp, rstep = BW * RPW;
 
-  zero_lds(smem, pl.ls);
+  zero_lds(smem, pl.ys);  // X's padding rows and columns stay zero
   __syncthreads();
-  load_rows(WLs, pl.pn, p.w_l, n_l, n);
 
   float gam[8], pg[8], pb[8];
 #pragma unroll
@@ -236,103 +291,133 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
   }
   const int dt = d / 16, tiles = (pl.nlp / 16) * dt;
   const float inv_d = 1.f / (float)d;
-
-  for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
-    // dY and M rows in batches of kRowBatch per lane group; the first batch is
-    // in flight with X and while Lc is computed
-    u32x4 yv[kRowBatch], mv[kRowBatch];
-    auto load_batch = [&](int q0) {
+  // W_L as MFMA A operands, loaded once: wave w computes Lc row block w % rb_n
+  // for the column blocks w / rb_n, + wpr, ...  (when every row block has a
+  // wave and n <= 32 kLcK; otherwise each tile reads W_L from L2).  Loads of
+  // W_L inside the example loop would queue behind the next example's
+  // prefetch on the in-order vector-memory counter.
+  const int rb_n = pl.nlp / 16;
+  const bool cached = rb_n <= BW && pl.n32 <= 32 * kLcK;
+  const int wpr = cached ? BW / rb_n : 1, my_rb = wave % rb_n, my_slot = wave / rb_n;
+  u32x4 wa[kLcK];
 #pragma unroll
-      for (int j = 0; j < kRowBatch; ++j) {
-        const int r = row0 + (q0 + j) * rstep;
-        if (r < n && col_ok) {
-          yv[j] = *reinterpret_cast<const u32x4*>(p.dy + (b * n + r) * d + c);
-          if (r < n_f) mv[j] = *reinterpret_cast<const u32x4*>(p.m + (b * n_f + r) * d + c);
+  for (int kk = 0; kk < kLcK; ++kk) {
+    const int wr = my_rb * 16 + li, kc = kk * 32 + 8 * lg;
+    wa[kk] = (cached && kk * 32 < pl.n32 && wr < n_l && kc < n) ? *reinterpret_cast<const u32x4*>(p.w_l + wr * n + kc)
+                                                               : u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // X, dY and M of an example in one burst of loads, issued one example ahead
+  u32x4 gx[kMaxXChunks], gy[kMaxXChunks], gm[kMaxRChunks];
+  auto fetch_example = [&](int64_t e) {
+    fetch_rows(gx, p.x + e * n * d, n, d8);
+    fetch_rows(gy, p.dy + e * n * d, n, d8);
+    fetch_rows(gm, p.m + e * n_f * d, n_f, d8);
+  };
+  if ((int64_t)blockIdx.x < p.batch) fetch_example(blockIdx.x);
+  for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
+    put_rows(gx, smem, pl.xs / 2, pl.pd, n, d8);
+    put_rows(gy, smem, pl.ys / 2, pl.pd, n, d8);
+    put_rows(gm, smem, pl.ms / 2, pl.pd, n_f, d8);
+    lds_barrier();
+    {
+      const int64_t nb = b + gridDim.x;
+      if (nb < p.batch) fetch_example(nb);
+    }
+    // Lc = W_L X -> Ls (fp32)
+    if (cached) {
+      if (my_slot < wpr) {
+        for (int cb = my_slot; cb < dt; cb += wpr) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < kLcK; ++kk)
+            if (kk * 32 < pl.n32) acc = mfma16x16x32(wa[kk], tr_op(Xs, pl.pd, kk * 32, cb * 16, li, lg), acc);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = my_rb * 16 + 4 * lg + q;
+            if (r < n_l) Ls[r * d + cb * 16 + li] = acc[q];
+          }
         }
       }
-    };
-    load_batch(0);
-    stage_rows<kMaxXChunks>(smem, pl.xs / 2, pl.pd, p.x + b * n * d, n, d / 8);
-    lds_barrier();
-    // Lc = W_L X -> Ls (fp32)
-    for (int t = wave; t < tiles; t += BW) {
-      const int rb = t / dt, cb = t - rb * dt;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < pl.n32; k0 += 32)
-        acc = mfma16x16x32(row_op(WLs, pl.pn, rb * 16, k0, li, lg), tr_op(Xs, pl.pd, k0, cb * 16, li, lg), acc);
+    } else {
+      for (int t = wave; t < tiles; t += BW) {
+        const int rb = t / dt, cb = t - rb * dt;
+        const int wr = rb * 16 + li;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int k0 = 0; k0 < pl.n32; k0 += 32) {
+          const int kc = k0 + 8 * lg;
+          const u32x4 a = (wr < n_l && kc < n) ? *reinterpret_cast<const u32x4*>(p.w_l + wr * n + kc)
+                                               : u32x4{0u, 0u, 0u, 0u};
+          acc = mfma16x16x32(a, tr_op(Xs, pl.pd, k0, cb * 16, li, lg), acc);
+        }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = rb * 16 + 4 * lg + q;
-        if (r < n_l) Ls[r * d + cb * 16 + li] = acc[q];
+        for (int q = 0; q < 4; ++q) {
+          const int r = rb * 16 + 4 * lg + q;
+          if (r < n_l) Ls[r * d + cb * 16 + li] = acc[q];
+        }
       }
     }
     lds_barrier();
-    // rows: R = [M; Lc] + X, LayerNorm backward
-#pragma unroll 1
-    for (int q0 = 0; q0 < kMaxRows; q0 += kRowBatch) {
-      if (row0 + q0 * rstep >= n) break;  // uniform over the lane group
-      if (q0 > 0) load_batch(q0);
+    // rows: R = [M; Lc] + X, LayerNorm backward (all operands in LDS)
+    for (int r = row0; r < n; r += rstep) {  // uniform over the lane group
+      float R[8], dyv[8];
 #pragma unroll
-      for (int j = 0; j < kRowBatch; ++j) {
-        const int r = row0 + (q0 + j) * rstep;
-        if (r >= n) break;
-        float R[8], dyv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) R[e] = dyv[e] = 0.f;
-        if (col_ok) {
-          const u32x4 xv = *reinterpret_cast<const u32x4*>(Xs + r * pl.pd + c);
-          if (r < n_f) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              R[2 * e] = bf16lo(mv[j][e]) + bf16lo(xv[e]);
-              R[2 * e + 1] = bf16hi(mv[j][e]) + bf16hi(xv[e]);
-            }
-          } else {
-            const float* lr = Ls + (r - n_f) * d + c;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              R[2 * e] = lr[2 * e] + bf16lo(xv[e]);
-              R[2 * e + 1] = lr[2 * e + 1] + bf16hi(xv[e]);
-            }
-          }
+      for (int e = 0; e < 8; ++e) R[e] = dyv[e] = 0.f;
+      if (col_ok) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(Xs + r * pl.pd + c);
+        const u32x4 yv = *reinterpret_cast<const u32x4*>(Ys + r * pl.pd + c);
+        if (r < n_f) {
+          const u32x4 mv = *reinterpret_cast<const u32x4*>(Ms + r * pl.pd + c);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            dyv[2 * e] = bf16lo(yv[j][e]);
-            dyv[2 * e + 1] = bf16hi(yv[j][e]);
+            R[2 * e] = bf16lo(mv[e]) + bf16lo(xv[e]);
+            R[2 * e + 1] = bf16hi(mv[e]) + bf16hi(xv[e]);
+          }
+        } else {
+          const float* lr = Ls + (r - n_f) * d + c;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            R[2 * e] = lr[2 * e] + bf16lo(xv[e]);
+            R[2 * e + 1] = lr[2 * e + 1] + bf16hi(xv[e]);
           }
         }
-        float s = 0.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) s += R[e];
-        const float mean = group_sum<G>(s) * inv_d;
-        float v = 0.f;
+        for (int e = 0; e < 4; ++e) {
+          dyv[2 * e] = bf16lo(yv[e]);
+          dyv[2 * e + 1] = bf16hi(yv[e]);
+        }
+      }
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += R[e];
+      const float mean = group_sum<G>(s) * inv_d;
+      float v = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float t = col_ok ? R[e] - mean : 0.f;
+        v += t * t;
+      }
+      const float rstd = rsqrtf(group_sum<G>(v) * inv_d + p.eps);
+      float s1 = 0.f, s2 = 0.f, rh[8], g[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        rh[e] = (R[e] - mean) * rstd;
+        g[e] = dyv[e] * gam[e];
+        s1 += g[e];
+        s2 += g[e] * rh[e];
+      }
+      const float m1 = group_sum<G>(s1) * inv_d, m2 = group_sum<G>(s2) * inv_d;
+      if (col_ok) {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = pack_bf16x2(rstd * (g[2 * e] - m1 - rh[2 * e] * m2), rstd * (g[2 * e + 1] - m1 - rh[2 * e + 1] * m2));
+        uint16_t* dst = r < n_f ? p.dm + (b * n_f + r) * d + c : p.dlc + (b * n_l + (r - n_f)) * d + c;
+        *reinterpret_cast<u32x4*>(dst) = o;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float t = col_ok ? R[e] - mean : 0.f;
-          v += t * t;
-        }
-        const float rstd = rsqrtf(group_sum<G>(v) * inv_d + p.eps);
-        float s1 = 0.f, s2 = 0.f, rh[8], g[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          rh[e] = (R[e] - mean) * rstd;
-          g[e] = dyv[e] * gam[e];
-          s1 += g[e];
-          s2 += g[e] * rh[e];
-        }
-        const float m1 = group_sum<G>(s1) * inv_d, m2 = group_sum<G>(s2) * inv_d;
-        if (col_ok) {
-          u32x4 o;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = pack_bf16x2(rstd * (g[2 * e] - m1 - rh[2 * e] * m2), rstd * (g[2 * e + 1] - m1 - rh[2 * e + 1] * m2));
-          uint16_t* dst = r < n_f ? p.dm + (b * n_f + r) * d + c : p.dlc + (b * n_l + (r - n_f)) * d + c;
-          *reinterpret_cast<u32x4*>(dst) = o;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pg[e] += dyv[e] * rh[e];
-            pb[e] += dyv[e];
-          }
+          pg[e] += dyv[e] * rh[e];
+          pb[e] += dyv[e];
         }
       }
     }
@@ -347,6 +432,7 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
       pb[j] += __shfl_xor(pb[j], mk, kWave);
     }
   }
+  float* red = Ls;
   if (lane < G && col_ok) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -424,12 +510,23 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
     }
   }
 
-  int slot = 0;
+  int slot = 0, slot2 = 0;
+  float* red2 = red + 2 * BW;
+  // an example's inputs: X, dLc, the FMB rows of dR, d_Fn; fetched one example
+  // ahead (during the previous example's dX phase) and written to LDS here
+  u32x4 gx[kMaxXChunks], gl[kMaxRChunks], gm[kMaxRChunks], gf[kMaxFChunks];
+  auto fetch_example = [&](int64_t e) {
+    fetch_rows(gx, p.x + e * n * d, n, d8);
+    fetch_rows(gl, p.dlc + e * n_l * d, n_l, d8);
+    fetch_rows(gm, p.dm + e * n_f * d, n_f, d8);
+    fetch_rows(gf, p.dfn + e * nk, nk / 32, 4);
+  };
+  if ((int64_t)blockIdx.x < p.batch) fetch_example(blockIdx.x);
   for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
-    stage_rows<kMaxXChunks>(smem, pl.xs / 2, pl.pd, p.x + b * n * d, n, d8);
-    stage_rows<kMaxRChunks>(smem, pl.bs / 2 + 2 * kp * pl.pd, pl.pd, p.dlc + b * n_l * d, n_l, d8);
-    stage_rows<kMaxRChunks>(smem, pl.dms / 2, pl.pd, p.dm + b * n_f * d, n_f, d8);
-    stage_rows<kMaxFChunks>(smem, pl.dfs / 2, 32, p.dfn + b * nk, nk / 32, 4);
+    put_rows(gx, smem, pl.xs / 2, pl.pd, n, d8);
+    put_rows(gl, smem, pl.bs / 2 + 2 * kp * pl.pd, pl.pd, n_l, d8);
+    put_rows(gm, smem, pl.dms / 2, pl.pd, n_f, d8);
+    put_rows(gf, smem, pl.dfs / 2, 32, nk / 32, 4);
     lds_barrier();
     // Z = Phi X -> Bs rows [0, kp)
     for (int t = wave; t < jb_n * cb_n; t += BW) {
@@ -499,10 +596,10 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
         }
       }
     }
-    s1 = block_sum(s1, red, slot) * inv_nk;
-    slot ^= 1;
-    s2 = block_sum(s2, red, slot) * inv_nk;
-    slot ^= 1;
+    block_sum2(s1, s2, red2, slot2);
+    slot2 ^= 1;
+    s1 *= inv_nk;
+    s2 *= inv_nk;
     // dF^T -> As rows [0, kp) (zeros at padding), FM LayerNorm parameter sums
 #pragma unroll
     for (int q = 0; q < QF; ++q) {
@@ -557,19 +654,31 @@ __global__ __launch_bounds__(BT) void bwd_fmb_kernel(BwdFmbKArgs p) {
       }
     }
     lds_barrier();  // X no longer read: its LDS takes the dX tiles
-    // dX = dR + [dF | Phi^T | W_L^T] [Z; dZ; dLc] -> Xs (bf16)
-    for (int t = wave; t < ib_n * cb_n; t += BW) {
-      const int ib = t / cb_n, cb = t - ib * cb_n;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < pl.ka; k0 += 32)
-        acc = mfma16x16x32(tr_op(As, pl.pn, k0, ib * 16, li, lg), tr_op(Bs, pl.pd, k0, cb * 16, li, lg), acc);
-      const int e = cb * 16 + li;
+    {
+      const int64_t nb = b + gridDim.x;
+      if (nb < p.batch) fetch_example(nb);
+    }
+    // dX = dR + [dF | Phi^T | W_L^T] [Z; dZ; dLc] -> Xs (bf16); a wave owns
+    // 16-row blocks and keeps their A operands for every column tile
+    for (int ib = wave; ib < ib_n; ib += BW) {
+      u32x4 af[kMaxKa / 32];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = ib * 16 + 4 * lg + q;
-        if (i < n) {
-          const float res = i < n_f ? bf16_to_f32(DMs[i * pl.pd + e]) : bf16_to_f32(Bs[(2 * kp + i - n_f) * pl.pd + e]);
-          Xs[i * pl.pd + e] = to_bf16(acc[q] + res);
+      for (int kk = 0; kk < kMaxKa / 32; ++kk)
+        if (kk * 32 < pl.ka) af[kk] = tr_op(As, pl.pn, kk * 32, ib * 16, li, lg);
+      for (int cb = 0; cb < cb_n; ++cb) {
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < kMaxKa / 32; ++kk)
+          if (kk * 32 < pl.ka) acc = mfma16x16x32(af[kk], tr_op(Bs, pl.pd, kk * 32, cb * 16, li, lg), acc);
+        const int e = cb * 16 + li;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = ib * 16 + 4 * lg + q;
+          if (i < n) {
+            const float res =
+                i < n_f ? bf16_to_f32(DMs[i * pl.pd + e]) : bf16_to_f32(Bs[(2 * kp + i - n_f) * pl.pd + e]);
+            Xs[i * pl.pd + e] = to_bf16(acc[q] + res);
+          }
         }
       }
     }
@@ -718,16 +827,14 @@ namespace {
 bool out_supported(int n, int d, int n_l) {
   if (n <= 0 || d <= 0 || n_l <= 0 || n_l >= n || d % 16 || n % 8 || d > 512) return false;
   const OutPlan a = out_plan(n, d, n_l);
-  if (a.bytes > kLdsMax || !stage_fits(n, d / 8, kMaxXChunks)) return false;
-  const int rows_per_pass = BW * (kWave / a.g);
-  return (n + rows_per_pass - 1) / rows_per_pass <= kMaxRows;
+  return a.bytes <= kLdsMax && stage_fits(n, d / 8, kMaxXChunks) && stage_fits(n - n_l, d / 8, kMaxRChunks);
 }
 
 // The shapes bwd_fmb_kernel takes: its LDS plan, staging and register tiles fit.
 bool fmb_supported(int n, int d, int k, int n_l) {
   if (n <= 0 || d <= 0 || k <= 0 || n_l <= 0 || n_l >= n || d % 16 || n % 8) return false;
   const FmbPlan f = fmb_plan(n, d, k, n_l);
-  if (f.bytes > kLdsMax) return false;
+  if (f.bytes > kLdsMax || f.ka > kMaxKa) return false;
   if (!stage_fits(n, d / 8, kMaxXChunks) || !stage_fits(n - n_l, d / 8, kMaxRChunks) ||
       !stage_fits(n_l, d / 8, kMaxRChunks) || (n * k) % 32 || !stage_fits(n * k / 32, 4, kMaxFChunks))
     return false;
