@@ -304,8 +304,9 @@ def measure_moe(wk, ws, torch, cfg, x, stream, steps, warmup, seed):
     for e, (k, nf, nl, mlp) in enumerate(shapes):
         acct[("fmb_lcb", e, 0)] = {"flops": B * (2 * (k + nl) * s.n * s.d + 2 * s.n * s.d * k),
                                    "bytes": B * (s.n * s.d + s.n * k + nl * s.d) * es + (k + nl) * s.n * es}
-        # whether the last Linear carries the output LayerNorm depends on d and that Linear only
-        fused = wk.workspace_layout(wk.LayerSpec(s.n, s.d, k, nf, s.n - nf, mlp, 1e-5, cfg.dtype), B)["m"] < 0
+        # the last Linear carries the output LayerNorm for bf16, d in {16, 32, 80, 160}
+        # and an input width that is a multiple of 64 (include/wukong.h)
+        fused = cfg.dtype == "bf16" and s.d in (16, 32, 80, 160) and mlp[-2] % 64 == 0
         T = len(mlp) - 1
         for t, (a_, b_) in enumerate(zip(mlp[:-1], mlp[1:])):
             extra = B * b_ if (fused and t == T - 1) else 0
@@ -323,6 +324,16 @@ def measure_moe(wk, ws, torch, cfg, x, stream, steps, warmup, seed):
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
                                                                                 PEAK_BF16_TFLOPS, 4),
             "roofline": roof, "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"], k["index"]))}
+
+
+def optional_section(name, fn, *args):
+    """Run one optional measurement; a failure is reported in its place instead
+    of ending the run (the main result line must still be printed)."""
+    try:
+        return fn(*args)
+    except Exception as e:  # noqa: BLE001
+        print(f"# {name} section failed: {e}", file=sys.stderr, flush=True)
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def measure_head(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
@@ -655,28 +666,32 @@ def main():
 
     head = None
     if not args.no_head:
-        head = measure_head(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
-        print(f"# head {head['dims']}: {head['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
+        head = optional_section("head", measure_head, wk, ws, torch, cfg, y, stream, args.steps, args.warmup,
+                                args.seed)
+        if head and "error" not in head:
+            print(f"# head {head['dims']}: {head['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
 
     fusion = None
     if not args.no_fusion and cfg.dtype == "bf16":
-        fusion = measure_fusion(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
-        if fusion is not None:
+        fusion = optional_section("fusion", measure_fusion, wk, ws, torch, cfg, y, stream, args.steps, args.warmup,
+                                  args.seed)
+        if fusion is not None and "error" not in fusion:
             print(f"# fusion n={fusion['n']} d={fusion['d']} L={fusion['L']}: {fusion['ms_per_call']:.3f} ms/call",
                   file=sys.stderr, flush=True)
 
     training = None
     if not args.no_training:
-        training = measure_training(wk, ws, torch, cfg, layers[0], x, stream, args.steps, args.warmup, args.seed)
-        if training is not None:
+        training = optional_section("training", measure_training, wk, ws, torch, cfg, layers[0], x, stream,
+                                    args.steps, args.warmup, args.seed)
+        if training is not None and "error" not in training:
             print(f"# training step (forward + backward): {training['ms_per_step']:.3f} ms "
                   f"(forward {training['forward_train_ms']:.3f}, backward {training['backward_ms']:.3f})",
                   file=sys.stderr, flush=True)
 
     moe = None
     if not args.no_moe and cfg.dtype == "bf16":
-        moe = measure_moe(wk, ws, torch, cfg, x, stream, args.steps, args.warmup, args.seed)
-        if moe is not None:
+        moe = optional_section("moe", measure_moe, wk, ws, torch, cfg, x, stream, args.steps, args.warmup, args.seed)
+        if moe is not None and "error" not in moe:
             print(f"# mixture of {MOE_EXPERTS} experts: {moe['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
 
     step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
