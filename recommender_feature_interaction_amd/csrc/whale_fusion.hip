@@ -16,7 +16,8 @@
 // reads, for O += P V): the shared K = V is loaded once.  S and O use
 // v_mfma_f32_16x16x32_bf16; the softmax is the online form (running row
 // maximum and sum, O rescaled when the maximum grows), in base 2 with the
-// 1/sqrt(d) scale folded into the exponent.  P goes through a per-wave LDS
+// 1/sqrt(d) scale folded into the exponent; row maxima and sums are DPP
+// row rotations.  P goes through a per-wave LDS
 // tile in bf16 to become the A operand of P V.  Positions past L read as
 // zero through the buffer resource and are masked to -inf.
 #include <math.h>
@@ -48,6 +49,27 @@ __device__ __forceinline__ u32x4 tr_rows8(const uint16_t* p0, const uint16_t* p1
   const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(WF_LDS_I16X4(p1));
   const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
+}
+
+// Max and sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), every
+// lane receiving the result: v op= v rotated by 8, 4, 2, 1 within the row
+// (row_ror), a butterfly in which each lane ends up combining all 16 values.
+// Plain VALU with a DPP operand, instead of LDS-crossbar permutes.
+template <int ROR>
+__device__ __forceinline__ float row_ror(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + ROR, 0xf, 0xf, true));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, row_ror<8>(v));
+  v = fmaxf(v, row_ror<4>(v));
+  v = fmaxf(v, row_ror<2>(v));
+  return fmaxf(v, row_ror<1>(v));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += row_ror<8>(v);
+  v += row_ror<4>(v);
+  v += row_ror<2>(v);
+  return v + row_ror<1>(v);
 }
 
 struct AttnArgs {
@@ -157,21 +179,21 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v0 = s[qt][0][r] * p.scale_log2, v1 = s[qt][1][r] * p.scale_log2;
-        if (t * AKT + li >= L) v0 = -INFINITY;
-        if (t * AKT + 16 + li >= L) v1 = -INFINITY;
-        float mx = fmaxf(v0, v1);
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+        if (t == T - 1) {  // only the last key tile can reach past L
+          if (t * AKT + li >= L) v0 = -INFINITY;
+          if (t * AKT + 16 + li >= L) v1 = -INFINITY;
+        }
+        const float mx = row16_max(fmaxf(v0, v1));
         const float mnew = fmaxf(mrow[qt][r], mx);
         const float alpha = exp2f(mrow[qt][r] - mnew);
         const float e0 = exp2f(v0 - mnew), e1 = exp2f(v1 - mnew);
-        float sum = e0 + e1;
+        lrow[qt][r] = lrow[qt][r] * alpha + row16_sum(e0 + e1);
+        // rescale O only when some row's running maximum grew (alpha is exactly 1 otherwise)
+        if (__builtin_amdgcn_ballot_w64(mnew != mrow[qt][r]) != 0) {
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) sum += __shfl_xor(sum, off, 64);
-        lrow[qt][r] = lrow[qt][r] * alpha + sum;
+          for (int dt = 0; dt < DT; ++dt) o[qt][dt][r] *= alpha;
+        }
         mrow[qt][r] = mnew;
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[qt][dt][r] *= alpha;
         const int row = qt * 16 + 4 * lg + r;
         pw[row * AKT + li] = (uint16_t)f32_to_bf16(e0);
         pw[row * AKT + 16 + li] = (uint16_t)f32_to_bf16(e1);
