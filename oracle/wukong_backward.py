@@ -153,3 +153,30 @@ def layer_backward(X, w, dY, eps: float = LN_EPS, storage: Iterable[str] = (),
 def layer_loss(X, w, dY, eps: float = LN_EPS) -> float:
     """The scalar sum(dY * layer(X)) whose gradient `layer_backward` returns (fp64, no rounding)."""
     return float((to_f64(dY) * wukong_layer(X, w, eps)).sum())
+
+
+def stack_backward(X, weights, dY, eps: float = LN_EPS, storage: Iterable[str] = ()):
+    """Gradients of l stacked layers (the forward of `wukong_oracle.wukong_stack`):
+    the forward keeps every layer's input X_i (rounded to bf16 when "Y" is in
+    storage, as the layer output it is), then `layer_backward` runs from the
+    last layer to the first, each layer's dX being the upstream gradient of the
+    layer before it.  Returns (dX, [per-layer gradient dicts, layer order])."""
+    storage = frozenset(storage)
+    xs = [to_f64(X)]
+    for w in weights[:-1]:
+        xs.append(wukong_layer(xs[-1], w, eps, storage & STORAGE_NAMES))
+    g = to_f64(dY)
+    grads = [None] * len(weights)
+    for i in range(len(weights) - 1, -1, -1):
+        out = layer_backward(xs[i], weights[i], g, eps, storage)
+        grads[i] = out
+        g = out["dX"]
+    return g, grads
+
+
+def stack_loss(X, weights, dY, eps: float = LN_EPS) -> float:
+    """sum(dY * stack(X)) in fp64 without rounding: the scalar `stack_backward` differentiates."""
+    Y = to_f64(X)
+    for w in weights:
+        Y = wukong_layer(Y, w, eps)
+    return float((to_f64(dY) * Y).sum())

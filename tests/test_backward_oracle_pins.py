@@ -7,7 +7,9 @@
     and to the normalised row (eps = 0, unit gamma);
   * the output scale's gradient equals sum dY * (Y - beta) / gamma read off
     the forward's own output;
-  * a zero upstream gradient gives zero gradients everywhere.
+  * a zero upstream gradient gives zero gradients everywhere;
+  * two stacked layers: the chained backward against central differences of
+    the stack's loss.
 Each planted mistake in MUTANTS must fail at least one pin.
 """
 import math
@@ -119,9 +121,32 @@ def pin_zero_upstream(mod):
         assert not np.any(out["mlp_w"][t]) and not np.any(out["mlp_b"][t])
 
 
+def pin_stack_finite_differences(mod):
+    """Two stacked layers: the chained backward against central differences of the stack's loss."""
+    w1, X, dY = _case(hidden=(8,), seed=8)
+    w2, _, _ = _case(hidden=(5,), seed=9)
+    ws_ = [w1, w2]
+    dX, grads = mod.stack_backward(X, ws_, dY)
+    h, rng = 1e-6, np.random.default_rng(12)
+    V = rng.normal(size=X.shape)
+    fd = (WB.stack_loss(X + h * V, ws_, dY) - WB.stack_loss(X - h * V, ws_, dY)) / (2 * h)
+    assert abs(fd - float((dX * V).sum())) <= 2e-6 * max(1.0, abs(fd))
+    for li, name in ((0, "phi"), (0, "w_l"), (1, "phi"), (1, "out_gamma")):
+        P = getattr(ws_[li], name)
+        V = rng.normal(size=P.shape)
+        P0 = P.copy()
+        P[...] = P0 + h * V
+        lp = WB.stack_loss(X, ws_, dY)
+        P[...] = P0 - h * V
+        lm = WB.stack_loss(X, ws_, dY)
+        P[...] = P0
+        fd = (lp - lm) / (2 * h)
+        assert abs(fd - float((grads[li][name] * V).sum())) <= 2e-6 * max(1.0, abs(fd)), (li, name)
+
+
 PINS = {f.__name__: f for f in (pin_finite_differences_one_hidden, pin_finite_differences_two_hidden,
                                  pin_finite_differences_no_affine_no_bias, pin_layernorm_projection,
-                                 pin_out_gamma_from_forward, pin_zero_upstream)}
+                                 pin_out_gamma_from_forward, pin_zero_upstream, pin_stack_finite_differences)}
 
 
 @pytest.mark.parametrize("name", sorted(PINS))
@@ -157,6 +182,9 @@ MUTANTS = {
     "dW_transposed_input": ("d_mlp_w[t] = g.T @ acts[t]", "d_mlp_w[t] = g.T @ (acts[t] * (acts[t] > 0))"),
     "dz_transposed": ("np.matmul(np.swapaxes(dF, 1, 2), X)", "np.matmul(np.swapaxes(dF, 1, 2), X) * 0.5"),
     "out_gamma_not_applied": ("layer_norm_backward(dY * g_out,", "layer_norm_backward(dY,"),
+    "stack_first_input_everywhere": ("out = layer_backward(xs[i], weights[i], g, eps, storage)",
+                                     "out = layer_backward(xs[0], weights[i], g, eps, storage)"),
+    "stack_upstream_not_chained": ("        g = out[\"dX\"]\n", "        g = g\n"),
 }
 
 
