@@ -336,6 +336,28 @@ int32_t wukong_layer_backward_traced(const wk_layer_desc* desc, const wk_layer_w
                                      const wk_layer_grads* grads, void* workspace, size_t workspace_bytes,
                                      void* stream, wk_trace* trace);
 
+/* Training a stack of num_layers layers (equal n, d; bf16; each layer as
+ * wukong_layer_backward supports).  The saved buffer holds, per layer, its
+ * input (for every layer after the first; the first one's is x) and its
+ * wukong_layer_forward_train activations.  The backward runs the layers last
+ * to first, each layer's dX being the previous layer's upstream gradient;
+ * grads is a HOST array of num_layers gradient sets (layer order).  The
+ * workspace holds two [batch, n, d] gradient buffers and one layer's backward
+ * workspace.  Conventions as wukong_layer_backward; records of the traced
+ * form carry the layer index. */
+size_t wukong_stack_saved_size(int32_t num_layers, const wk_layer_desc* descs, int64_t batch);
+int32_t wukong_stack_forward_train(int32_t num_layers, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                                   int64_t batch, const void* x, void* y, void* saved, size_t saved_bytes,
+                                   void* stream);
+size_t wukong_stack_backward_workspace_size(int32_t num_layers, const wk_layer_desc* descs, int64_t batch);
+int32_t wukong_stack_backward(int32_t num_layers, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                              int64_t batch, const void* x, const void* saved, const void* dy, void* dx,
+                              const wk_layer_grads* grads, void* workspace, size_t workspace_bytes, void* stream);
+int32_t wukong_stack_backward_traced(int32_t num_layers, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                                     int64_t batch, const void* x, const void* saved, const void* dy, void* dx,
+                                     const wk_layer_grads* grads, void* workspace, size_t workspace_bytes,
+                                     void* stream, wk_trace* trace);
+
 /* ---- WHALE fusion step ----------------------------------------------------
  * WHALE technical summaries, section 2.1 (attention-based fusion module) and
  * section 2.2 (shared key-value, shared-gate SwiGLU): the Wukong output H_w

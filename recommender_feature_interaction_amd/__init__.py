@@ -15,7 +15,8 @@ include/wukong.h; this package is the Python binding.
 from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceFusion, DeviceHead, DeviceLayer,  # noqa: F401
                    FusionSpec, HeadSpec, LayerGrads, LayerSpec, Trace, WukongError, alloc_workspace,
                    fusion_forward, layer_backward, layer_backward_workspace_size, layer_forward_train,
-                   layer_saved_size, saved_layout, MoeSpec, DeviceMoe, moe_forward, moe_workspace_size,
+                   layer_saved_size, saved_layout, stack_saved_size, stack_forward_train,
+                   stack_backward_workspace_size, stack_backward, MoeSpec, DeviceMoe, moe_forward, moe_workspace_size,
                    fusion_workspace_size, head_forward, head_workspace_size,
                    layer_forward, layer_workspace_size, library_path, load_library, stack_forward,
                    stack_workspace_size, status_string, to_device, workspace_layout, EXPORTED_SYMBOLS)

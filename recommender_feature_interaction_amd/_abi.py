@@ -133,6 +133,20 @@ _SIGNATURES = [
      [ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64, ctypes.c_void_p,
       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(wk_layer_grads), ctypes.c_void_p,
       ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_stack_saved_size", ctypes.c_size_t, [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.c_int64]),
+    ("wukong_stack_forward_train", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_stack_backward_workspace_size", ctypes.c_size_t,
+     [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.c_int64]),
+    ("wukong_stack_backward", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(wk_layer_grads),
+      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    ("wukong_stack_backward_traced", ctypes.c_int32,
+     [ctypes.c_int32, ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64,
+      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(wk_layer_grads),
+      ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
     ("wukong_head_workspace_size", ctypes.c_size_t, [ctypes.POINTER(wk_head_desc), ctypes.c_int64]),
     ("wukong_head_forward", ctypes.c_int32,
      [ctypes.POINTER(wk_head_desc), ctypes.POINTER(wk_head_weights), ctypes.c_int64, ctypes.c_void_p,
@@ -487,6 +501,62 @@ def layer_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layer
         _check(lib.wukong_layer_backward(*args), "wukong_layer_backward")
     else:
         _check(lib.wukong_layer_backward_traced(*args, trace.handle), "wukong_layer_backward_traced")
+    return dx, grads
+
+
+def stack_saved_size(specs: Sequence[LayerSpec], batch: int) -> int:
+    pairs = [sp.make_desc() for sp in specs]
+    descs = (wk_layer_desc * len(specs))(*[p[0] for p in pairs])
+    return int(load_library().wukong_stack_saved_size(len(specs), descs, batch))
+
+
+def stack_backward_workspace_size(specs: Sequence[LayerSpec], batch: int) -> int:
+    pairs = [sp.make_desc() for sp in specs]
+    descs = (wk_layer_desc * len(specs))(*[p[0] for p in pairs])
+    return int(load_library().wukong_stack_backward_workspace_size(len(specs), descs, batch))
+
+
+def stack_forward_train(x: torch.Tensor, layers: Sequence[DeviceLayer], y: Optional[torch.Tensor] = None,
+                        saved: Optional[torch.Tensor] = None, stream=None):
+    """Training forward of a bf16 stack: returns (y, saved), saved holding every layer's input and activations."""
+    lib = load_library()
+    B = _check_x(x, layers[0].spec)
+    y = torch.empty_like(x) if y is None else y
+    need = stack_saved_size([l.spec for l in layers], B)
+    if need == 0:
+        raise WukongError(WK_ERR_UNSUPPORTED, "wukong_stack_saved_size")
+    if saved is None:
+        saved = alloc_workspace(need, x.device)
+    descs, ws = _descs(layers)
+    _check(lib.wukong_stack_forward_train(len(layers), descs, ws, B, x.data_ptr(), y.data_ptr(), saved.data_ptr(),
+                                          saved.numel() * saved.element_size(), _stream_handle(stream)),
+           "wukong_stack_forward_train")
+    return y, saved
+
+
+def stack_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layers: Sequence[DeviceLayer],
+                   grads: Optional[Sequence[LayerGrads]] = None, dx: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None, stream=None, trace: "Trace" = None):
+    """Backward of a bf16 stack: returns (dx, [LayerGrads per layer])."""
+    lib = load_library()
+    B = _check_x(x, layers[0].spec)
+    if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
+        raise ValueError("dy must be contiguous and shaped like x")
+    grads = [LayerGrads(l) for l in layers] if grads is None else list(grads)
+    dx = torch.empty_like(x) if dx is None else dx
+    need = stack_backward_workspace_size([l.spec for l in layers], B)
+    if need == 0:
+        raise WukongError(WK_ERR_UNSUPPORTED, "wukong_stack_backward_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    descs, ws = _descs(layers)
+    garr = (wk_layer_grads * len(grads))(*[g.c for g in grads])
+    args = [len(layers), descs, ws, B, x.data_ptr(), saved.data_ptr(), dy.data_ptr(), dx.data_ptr(), garr,
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream)]
+    if trace is None:
+        _check(lib.wukong_stack_backward(*args), "wukong_stack_backward")
+    else:
+        _check(lib.wukong_stack_backward_traced(*args, trace.handle), "wukong_stack_backward_traced")
     return dx, grads
 
 

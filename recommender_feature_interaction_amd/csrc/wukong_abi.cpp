@@ -671,7 +671,7 @@ int32_t layer_forward_train(const wk_layer_desc* d, const wk_layer_weights* w, i
 
 int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_t batch, const void* x,
                        const void* saved, const void* dy, void* dx, const wk_layer_grads* gr, void* ws,
-                       size_t ws_bytes, void* stream, wk_trace* trace) {
+                       size_t ws_bytes, void* stream, wk_trace* trace, int layer_idx = 0) {
   int32_t st = check_backward_desc(d);
   if (st != WK_OK) return st;
   if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
@@ -720,18 +720,18 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   oa.d = d->d;
   oa.n_l = d->n_l;
   oa.eps = d->ln_eps;
-  st = launch(WK_KERNEL_BWD_OUT, 0, 0, [&](int64_t* g) { return wk::launch_bwd_out(oa, s, g); });
+  st = launch(WK_KERNEL_BWD_OUT, layer_idx, 0, [&](int64_t* g) { return wk::launch_bwd_out(oa, s, g); });
   if (st != WK_OK) return st;
   const int64_t po = (int64_t)wk::wukong_bwd_out_part_floats(d->d);
   if (gr->out_ln_gamma) {
-    st = launch(WK_KERNEL_BWD_REDUCE, 0, 0, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 0, [&](int64_t* g) {
       *g = 1;
       return wk::launch_sum_planes_strided(part_out, wg, po, d->d, gr->out_ln_gamma, s);
     });
     if (st != WK_OK) return st;
   }
   if (gr->out_ln_beta) {
-    st = launch(WK_KERNEL_BWD_REDUCE, 0, 1, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 1, [&](int64_t* g) {
       *g = 1;
       return wk::launch_sum_planes_strided(part_out + d->d, wg, po, d->d, gr->out_ln_beta, s);
     });
@@ -749,18 +749,18 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
     const int mi = d->mlp_dims[t], mo = d->mlp_dims[t + 1];
     const void* a_t = t == 0 ? static_cast<const void*>(sbase + sv.fn) : static_cast<const void*>(sbase + sv.hid[t - 1]);
     float* db = gr->mlp_b ? gr->mlp_b[t] : nullptr;
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, 3 * t, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t, [&](int64_t* g) {
       return wk::launch_transpose_bf16(g_next, batch, mo, Bp, gt, db ? colpart : nullptr, s, g);
     });
     if (st != WK_OK) return st;
     if (db) {
-      st = launch(WK_KERNEL_BWD_REDUCE, 0, 2 + t, [&](int64_t* g) {
+      st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 2 + t, [&](int64_t* g) {
         *g = 1;
         return wk::launch_sum_planes(colpart, (int)(Bp / 64), mo, db, s);
       });
       if (st != WK_OK) return st;
     }
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, 3 * t + 1, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t + 1, [&](int64_t* g) {
       return wk::launch_transpose_bf16(a_t, batch, mi, Bp, at, nullptr, s, g);
     });
     if (st != WK_OK) return st;
@@ -773,11 +773,11 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
     wa.N = mi;
     wa.K = (int)Bp;
     wa.act = wk::kActNone;
-    st = launch(WK_KERNEL_BWD_WGRAD, 0, t, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_WGRAD, layer_idx, t, [&](int64_t* g) {
       return wk::launch_linear_bf16_f32out_split(wa, gr->mlp_w[t], split, s, g);
     });
     if (st != WK_OK) return st;
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, 0, 3 * t + 2, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t + 2, [&](int64_t* g) {
       return wk::launch_transpose_bf16(w->mlp_w[t], mo, mi, mo, wt, nullptr, s, g);
     });
     if (st != WK_OK) return st;
@@ -792,7 +792,7 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
     da.K = mo;
     da.act = t == 0 ? wk::kActNone : wk::kActReluMask;
     da.res = t == 0 ? nullptr : a_t;
-    st = launch(WK_KERNEL_BWD_DGRAD, 0, t, [&](int64_t* g) { return wk::launch_linear_bf16(da, s, g); });
+    st = launch(WK_KERNEL_BWD_DGRAD, layer_idx, t, [&](int64_t* g) { return wk::launch_linear_bf16(da, s, g); });
     if (st != WK_OK) return st;
     g_next = g_out;
   }
@@ -814,7 +814,7 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   fa.k = d->k;
   fa.n_l = d->n_l;
   fa.eps = d->ln_eps;
-  st = launch(WK_KERNEL_BWD_FMB, 0, 0, [&](int64_t* g) { return wk::launch_bwd_fmb(fa, s, g); });
+  st = launch(WK_KERNEL_BWD_FMB, layer_idx, 0, [&](int64_t* g) { return wk::launch_bwd_fmb(fa, s, g); });
   if (st != WK_OK) return st;
   const int64_t pf = (int64_t)wk::wukong_bwd_fmb_part_floats(d->n, d->k, d->n_l);
   const int64_t kn = (int64_t)d->k * d->n, ln = (int64_t)d->n_l * d->n, nk = (int64_t)d->n * d->k;
@@ -824,10 +824,113 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   } outs[4] = {{gr->phi, 0, kn}, {gr->w_l, kn, ln}, {gr->fm_ln_gamma, kn + ln, nk}, {gr->fm_ln_beta, kn + ln + nk, nk}};
   for (int i = 0; i < 4; ++i) {
     if (!outs[i].dst) continue;
-    st = launch(WK_KERNEL_BWD_REDUCE, 0, 2 + T + i, [&](int64_t* g) {
+    st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 2 + T + i, [&](int64_t* g) {
       *g = 1;
       return wk::launch_sum_planes_strided(part_fmb + outs[i].off, wg, pf, outs[i].len, outs[i].dst, s);
     });
+    if (st != WK_OK) return st;
+  }
+  return WK_OK;
+}
+
+// ---- training a stack: per layer, its input (layers after the first) and its
+// saved activations; the backward runs the layers last to first.
+struct StackTrainPlan {
+  std::vector<size_t> in, sv;
+  size_t bytes = 0;
+};
+
+int32_t check_stack_train(int32_t l, const wk_layer_desc* descs, int64_t batch, StackTrainPlan* out,
+                          size_t* bwd_bytes) {
+  int32_t st = check_stack(l, descs, batch, nullptr);
+  if (st != WK_OK) return st;
+  for (int i = 0; i < l; ++i) {
+    st = check_backward_desc(&descs[i]);
+    if (st != WK_OK) return st;
+  }
+  const size_t act = align_up((size_t)batch * descs[0].n * descs[0].d * 2);
+  StackTrainPlan p;
+  size_t off = 0, bw = 0;
+  for (int i = 0; i < l; ++i) {
+    p.in.push_back(off);
+    if (i > 0) off += act;
+    p.sv.push_back(off);
+    off += plan_saved(descs[i], batch).bytes;
+    const size_t b = plan_backward(descs[i], batch).bytes;
+    bw = b > bw ? b : bw;
+  }
+  p.bytes = off ? off : kAlign;
+  if (out) *out = p;
+  if (bwd_bytes) *bwd_bytes = 2 * act + bw;  // two gradient ping-pong buffers, then one layer's workspace
+  return WK_OK;
+}
+
+int32_t stack_forward_train(int32_t l, const wk_layer_desc* descs, const wk_layer_weights* weights, int64_t batch,
+                            const void* x, void* y, void* saved, size_t saved_bytes, void* stream) {
+  StackTrainPlan sp;
+  int32_t st = check_stack_train(l, descs, batch, &sp, nullptr);
+  if (st != WK_OK) return st;
+  if (!weights) return WK_ERR_INVALID_ARG;
+  for (int i = 0; i < l; ++i) {
+    st = check_weights(descs[i], &weights[i]);
+    if (st != WK_OK) return st;
+  }
+  if (batch == 0) return WK_OK;
+  const size_t act = (size_t)batch * descs[0].n * descs[0].d * 2;
+  if (!x || !y || !saved || !aligned16(x) || !aligned16(y) || !aligned16(saved)) return WK_ERR_INVALID_ARG;
+  if (saved_bytes < sp.bytes) return WK_ERR_WORKSPACE;
+  if (overlap(x, act, y, act) || overlap(saved, sp.bytes, x, act) || overlap(saved, sp.bytes, y, act))
+    return WK_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(saved);
+  Launch launch{nullptr, static_cast<hipStream_t>(stream)};
+  for (int i = 0; i < l; ++i) {
+    const void* in = i == 0 ? x : static_cast<const void*>(base + sp.in[i]);
+    void* out = i == l - 1 ? y : static_cast<void*>(base + sp.in[i + 1]);
+    st = run_layer(descs[i], weights[i], batch, in, out, base + sp.sv[i], plan_saved(descs[i], batch), launch, i);
+    if (st != WK_OK) return st;
+  }
+  return WK_OK;
+}
+
+int32_t stack_backward(int32_t l, const wk_layer_desc* descs, const wk_layer_weights* weights, int64_t batch,
+                       const void* x, const void* saved, const void* dy, void* dx, const wk_layer_grads* grads,
+                       void* ws, size_t ws_bytes, void* stream, wk_trace* trace) {
+  StackTrainPlan sp;
+  size_t need = 0;
+  int32_t st = check_stack_train(l, descs, batch, &sp, &need);
+  if (st != WK_OK) return st;
+  if (!weights || !grads) return WK_ERR_INVALID_ARG;
+  // everything the per-layer calls would check, up front: nothing is launched on an error
+  for (int i = 0; i < l; ++i) {
+    st = check_weights(descs[i], &weights[i]);
+    if (st != WK_OK) return st;
+    const wk_layer_grads& gr = grads[i];
+    if (!gr.phi || !gr.w_l || !gr.mlp_w) return WK_ERR_INVALID_ARG;
+    for (int t = 0; t < descs[i].num_linear; ++t)
+      if (!gr.mlp_w[t]) return WK_ERR_INVALID_ARG;
+  }
+  if (batch == 0) return WK_OK;
+  const size_t act = (size_t)batch * descs[0].n * descs[0].d * 2;
+  if (!x || !saved || !dy || !dx || !ws) return WK_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(saved) || !aligned16(dy) || !aligned16(dx) || !aligned16(ws))
+    return WK_ERR_INVALID_ARG;
+  if (ws_bytes < need) return WK_ERR_WORKSPACE;
+  if (overlap(ws, need, x, act) || overlap(ws, need, dy, act) || overlap(ws, need, dx, act) ||
+      overlap(ws, need, saved, sp.bytes) || overlap(dx, act, x, act) || overlap(dx, act, dy, act) ||
+      overlap(dx, act, saved, sp.bytes))
+    return WK_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(ws);
+  const size_t act_al = align_up(act);
+  void* g[2] = {base, base + act_al};
+  char* lws = base + 2 * act_al;
+  const size_t lws_bytes = ws_bytes - 2 * act_al;
+  const char* sb = static_cast<const char*>(saved);
+  for (int i = l - 1; i >= 0; --i) {
+    const void* xi = i == 0 ? x : static_cast<const void*>(sb + sp.in[i]);
+    const void* dyi = i == l - 1 ? dy : static_cast<const void*>(g[(i + 1) % 2]);
+    void* dxi = i == 0 ? dx : g[i % 2];
+    st = layer_backward(&descs[i], &weights[i], batch, xi, sb + sp.sv[i], dyi, dxi, &grads[i], lws, lws_bytes,
+                        stream, trace, i);
     if (st != WK_OK) return st;
   }
   return WK_OK;
@@ -1015,6 +1118,38 @@ size_t wukong_layer_saved_size(const wk_layer_desc* desc, int64_t batch) {
 int32_t wukong_layer_forward_train(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
                                    const void* x, void* y, void* saved, size_t saved_bytes, void* stream) {
   return layer_forward_train(desc, weights, batch, x, y, saved, saved_bytes, stream);
+}
+
+size_t wukong_stack_saved_size(int32_t num_layers, const wk_layer_desc* descs, int64_t batch) {
+  StackTrainPlan sp;
+  return check_stack_train(num_layers, descs, batch, &sp, nullptr) == WK_OK ? sp.bytes : 0;
+}
+
+int32_t wukong_stack_forward_train(int32_t num_layers, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                                   int64_t batch, const void* x, void* y, void* saved, size_t saved_bytes,
+                                   void* stream) {
+  return stack_forward_train(num_layers, descs, weights, batch, x, y, saved, saved_bytes, stream);
+}
+
+size_t wukong_stack_backward_workspace_size(int32_t num_layers, const wk_layer_desc* descs, int64_t batch) {
+  size_t b = 0;
+  return check_stack_train(num_layers, descs, batch, nullptr, &b) == WK_OK ? b : 0;
+}
+
+int32_t wukong_stack_backward(int32_t num_layers, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                              int64_t batch, const void* x, const void* saved, const void* dy, void* dx,
+                              const wk_layer_grads* grads, void* workspace, size_t workspace_bytes, void* stream) {
+  return stack_backward(num_layers, descs, weights, batch, x, saved, dy, dx, grads, workspace, workspace_bytes,
+                        stream, nullptr);
+}
+
+int32_t wukong_stack_backward_traced(int32_t num_layers, const wk_layer_desc* descs, const wk_layer_weights* weights,
+                                     int64_t batch, const void* x, const void* saved, const void* dy, void* dx,
+                                     const wk_layer_grads* grads, void* workspace, size_t workspace_bytes,
+                                     void* stream, wk_trace* trace) {
+  if (!trace) return WK_ERR_INVALID_ARG;
+  return stack_backward(num_layers, descs, weights, batch, x, saved, dy, dx, grads, workspace, workspace_bytes,
+                        stream, trace);
 }
 
 size_t wukong_layer_backward_workspace_size(const wk_layer_desc* desc, int64_t batch) {

@@ -324,3 +324,40 @@ def test_moe_sizes_and_argument_errors():
     assert call(x=None, y=None, ws=None, nbytes=0, batch=0) == _abi.WK_OK
     desc.num_experts = 0
     assert call() == _abi.WK_ERR_INVALID_ARG
+
+
+def test_stack_training_sizes_and_argument_errors():
+    lib = wk.load_library()
+    sp = wk.LayerSpec(40, 32, 20, 16, 24, (800, 96, 512))
+    B = 37
+    act = al(B * 40 * 32 * 2)
+    one = wk.layer_saved_size(sp, B)
+    assert wk.stack_saved_size([sp, sp], B) == one + act + one       # layer 1's input between the two
+    assert wk.stack_backward_workspace_size([sp, sp], B) == 2 * act + wk.layer_backward_workspace_size(sp, B)
+    assert wk.stack_saved_size([C2, C2], B) == 0                      # n = 256: no backward
+    pairs = [sp.make_desc() for _ in range(2)]
+    descs = (_abi.wk_layer_desc * 2)(*[p[0] for p in pairs])
+    wp = (ctypes.c_void_p * 2)(0x40000, 0x50000)
+    w1 = _abi.wk_layer_weights(0x10000, 0x20000, None, None, ctypes.cast(wp, ctypes.POINTER(ctypes.c_void_p)),
+                               None, None, None)
+    warr = (_abi.wk_layer_weights * 2)(w1, w1)
+    gw = (ctypes.c_void_p * 2)(0x60000, 0x70000)
+    g1 = _abi.wk_layer_grads(0x80000, 0x90000, None, None, ctypes.cast(gw, ctypes.POINTER(ctypes.c_void_p)),
+                             None, None, None)
+    gmiss = (ctypes.c_void_p * 2)(0x60000, None)
+    g_bad = _abi.wk_layer_grads(0x80000, 0x90000, None, None, ctypes.cast(gmiss, ctypes.POINTER(ctypes.c_void_p)),
+                                None, None, None)
+    need = wk.stack_backward_workspace_size([sp, sp], B)
+    X, SV, DY, DX, WS = 0x1000000, 0x2000000, 0x3000000, 0x4000000, 0x10000000
+
+    def call(grads=(g1, g1), dx=DX, nbytes=need, batch=B):
+        garr = (_abi.wk_layer_grads * 2)(*grads)
+        return lib.wukong_stack_backward(2, descs, warr, batch, X, SV, DY, dx, garr, WS, nbytes, None)
+    assert call(nbytes=need - 1) == _abi.WK_ERR_WORKSPACE
+    assert call(grads=(g1, g_bad)) == _abi.WK_ERR_INVALID_ARG        # checked before layer 1 launches anything
+    assert call(dx=DX + 8) == _abi.WK_ERR_INVALID_ARG                 # misaligned dx, used by the last call only
+    assert call(dx=X + 256) == _abi.WK_ERR_INVALID_ARG                # dx overlaps x
+    assert call(batch=0) == _abi.WK_OK
+    saved = wk.stack_saved_size([sp, sp], B)
+    assert lib.wukong_stack_forward_train(2, descs, warr, B, X, 0x5000000, SV, saved - 1, None) == \
+        _abi.WK_ERR_WORKSPACE

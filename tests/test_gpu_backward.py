@@ -18,6 +18,7 @@ import oracle
 import recommender_feature_interaction_amd as wk
 import wukong_synth as ws
 from _gpu_helpers import check, host_f64, log, spec_of, to_host
+from _metrics import TOL_BF16, TOL_BF16_RMS, normwise_err, rms_err
 
 pytestmark = pytest.mark.gpu
 
@@ -74,14 +75,14 @@ def _grad_host(t):
     return t.detach().cpu().double().numpy()
 
 
-def check_grads(got: wk.LayerGrads, ref: dict, T: int):
-    check("d_phi", _grad_host(got.phi), ref["phi"], "bf16")
-    check("d_w_l", _grad_host(got.w_l), ref["w_l"], "bf16")
+def check_grads(got: wk.LayerGrads, ref: dict, T: int, elementwise: bool = True):
+    check("d_phi", _grad_host(got.phi), ref["phi"], "bf16", elementwise)
+    check("d_w_l", _grad_host(got.w_l), ref["w_l"], "bf16", elementwise)
     for name in ("fm_gamma", "fm_beta", "out_gamma", "out_beta"):
-        check(f"d_{name}", _grad_host(getattr(got, name)), ref[name], "bf16")
+        check(f"d_{name}", _grad_host(getattr(got, name)), ref[name], "bf16", elementwise)
     for t in range(T):
-        check(f"d_W{t}", _grad_host(got.mlp_w[t]), ref["mlp_w"][t], "bf16")
-        check(f"d_b{t}", _grad_host(got.mlp_b[t]), ref["mlp_b"][t], "bf16")
+        check(f"d_W{t}", _grad_host(got.mlp_w[t]), ref["mlp_w"][t], "bf16", elementwise)
+        check(f"d_b{t}", _grad_host(got.mlp_b[t]), ref["mlp_b"][t], "bf16", elementwise)
 
 
 @pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
@@ -220,3 +221,112 @@ def test_backward_full_batch_layer_d160():
             cols[units[t - 1]] = False
         check(f"d_W{t} (away from flipped units)", gw[rows][:, cols], rw[rows][:, cols], "bf16")
         check(f"d_b{t} (away from flipped units)", gb[rows], rb[rows], "bf16")
+
+
+# Oracle parity of stacks runs on shapes with narrow hidden layers.  With the
+# d = 160 layer's 2048-unit hidden layer, the upper layer's input (the lower
+# layer's bf16 output, whose rounding differs from the oracle's by flips) also
+# moves a few of its ReLU decisions, each of which changes one example's
+# gradient as a whole, a random event no tolerance derived from the arithmetic
+# bounds; that stack is checked bit for bit against the layer backward chained
+# by hand (test_stack_backward_chains_the_layer_backward), the layer backward
+# itself against the oracle above.
+STACK_CASES = [
+    # (name, n, d, k, n_f, mlp, layers, batch)
+    ("bwd_stack2_padded", 40, 32, 20, 16, (800, 96, 512), 2, 37),
+    ("bwd_stack3_tiny", 16, 16, 4, 8, (64, 64, 128), 3, 300),   # several examples per workgroup
+]
+STACK_D160 = ("bwd_stack2_d160", 128, 160, 32, 64, (4096, 2048, 10240), 2, 24)
+
+
+def _stack_run(case):
+    name, n, d, k, n_f, mlp, layers, B = case
+    shape = ws.LayerShape(n, d, k, n_f, n - n_f, tuple(mlp))
+    cfg = ws.WukongConfig(name, "bf16", B, tuple([shape] * layers))
+    host = ws.make_stack_weights(cfg, 5, "random")
+    x = ws.make_input(cfg, 5)
+    dy = ws.make_upstream_grad(cfg, 5)
+    spec = spec_of(shape, "bf16")
+    dev_layers = [wk.DeviceLayer.from_host(spec, h) for h in host]
+    return cfg, host, x, dy, spec, dev_layers
+
+
+@pytest.mark.parametrize("case", STACK_CASES, ids=lambda c: c[0])
+def test_stack_backward_parity(case):
+    """Stacks are gated normwise and by rms, like the forward stacks.  A layer's
+    input is the previous layer's bf16 output, whose rounding flips against the
+    oracle's carry into every later gradient, and some gradients are
+    ill-conditioned in that input (a layer's d_Phi and FM LayerNorm gradients
+    pass through the LayerNorm backward of its n k interaction values).  The
+    floor of each quantity is measured on the oracle alone: the same stack with
+    the inter-layer activations kept in fp64 instead of rounded to bf16.  Each
+    quantity must be within max(gate, 2 x floor) normwise and by rms."""
+    name, n, d, k, n_f, mlp, layers, B = case
+    cfg, host, x, dy, spec, dev_layers = _stack_run(case)
+    xd = wk.to_device(x, "bf16", "cuda")
+    y, saved = wk.stack_forward_train(xd, dev_layers)
+    tr = wk.Trace(capacity=256)
+    dx, grads = wk.stack_backward(xd, saved, wk.to_device(dy, "bf16", "cuda"), dev_layers, trace=tr)
+    torch.cuda.synchronize()
+    assert sorted({r["layer"] for r in tr.records()}) == list(range(layers))
+    tr.close()
+    log(f"stack backward {name}: {layers} layers, B={B}")
+    st = FWD_STORAGE + ("Y",)
+    check("Y (stack training forward)", host_f64(to_host(y)), oracle.wukong_stack(x, host, storage=st), "bf16",
+          elementwise=False)
+    ref_dx, ref = oracle.stack_backward(x, host, dy, storage=st + BWD_STORAGE)
+    alt_dx, alt = oracle.stack_backward(x, host, dy, storage=FWD_STORAGE + BWD_STORAGE)  # fp64 between layers
+
+    def items(dx_, g_):
+        out = [("dX", dx_)]
+        for i in range(layers):
+            gi = g_[i] if isinstance(g_[i], dict) else {k_: (v.cpu().double().numpy() if isinstance(v, torch.Tensor)
+                                                             else [t.cpu().double().numpy() for t in v])
+                                                        for k_, v in g_[i].as_dict().items() if v is not None}
+            for key in ("phi", "w_l", "fm_gamma", "fm_beta", "out_gamma", "out_beta"):
+                out.append((f"layer {i} d_{key}", gi[key]))
+            for t in range(len(mlp) - 1):
+                out.append((f"layer {i} d_W{t}", gi["mlp_w"][t]))
+                out.append((f"layer {i} d_b{t}", gi["mlp_b"][t]))
+        return out
+
+    for (label, g_), (_, r_), (_, a_) in zip(items(host_f64(to_host(dx)), grads), items(ref_dx, ref),
+                                             items(alt_dx, alt)):
+        nw_floor, rms_floor = normwise_err(a_, r_), rms_err(a_, r_)
+        tol_nw, tol_rms = max(TOL_BF16, 2 * nw_floor), max(TOL_BF16_RMS, 2 * rms_floor)
+        e_nw, e_rms = normwise_err(g_, r_), rms_err(g_, r_)
+        log(f"  {label}: normwise={e_nw:.3e} (tol {tol_nw:.2e}) rms={e_rms:.3e} (tol {tol_rms:.2e})")
+        assert np.all(np.isfinite(g_)), label
+        assert e_nw <= tol_nw and e_rms <= tol_rms, f"{label}: normwise {e_nw:.3e}, rms {e_rms:.3e}"
+
+
+def test_stack_backward_chains_the_layer_backward():
+    """The stack backward equals the layer backward called layer by layer, last
+    to first, on the inputs and activations the stack's training forward kept
+    (bit for bit: the same kernels on the same data)."""
+    cfg, host, x, dy, spec, dev_layers = _stack_run(STACK_D160)
+    layers = len(dev_layers)
+    xd = wk.to_device(x, "bf16", "cuda")
+    dyd = wk.to_device(dy, "bf16", "cuda")
+    y, saved = wk.stack_forward_train(xd, dev_layers)
+    dx, grads = wk.stack_backward(xd, saved, dyd, dev_layers)
+    # by hand: the training forward layer by layer, then the backward in reverse
+    xs, sv = [xd], []
+    for i, l in enumerate(dev_layers):
+        yi, si = wk.layer_forward_train(xs[-1], l)
+        sv.append(si)
+        xs.append(yi)
+    g = dyd
+    hand = [None] * layers
+    for i in range(layers - 1, -1, -1):
+        g, hand[i] = wk.layer_backward(xs[i], sv[i], g.contiguous(), dev_layers[i])
+    torch.cuda.synchronize()
+    assert torch.equal(xs[-1], y)
+    assert torch.equal(g, dx)
+    for i in range(layers):
+        for key, v in grads[i].as_dict().items():
+            w = hand[i].as_dict()[key]
+            if isinstance(v, list):
+                assert all(torch.equal(a, b) for a, b in zip(v, w)), (i, key)
+            elif v is not None:
+                assert torch.equal(v, w), (i, key)
