@@ -74,6 +74,7 @@ struct LinearLnKArgs {
   const uint16_t* gamma;  // [D] or null
   const uint16_t* beta;   // [D] or null
   uint16_t* y;            // row m at y + m * ld
+  uint16_t* m_out;        // the bf16 GEMM output M, row m at m_out + m * N (MOUT kernels only)
   int64_t M;
   int N, K;
   int64_t ld;
@@ -384,7 +385,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int D>
+// MOUT: the epilogue also stores M = bf16(A W^T + bias) (the training forward
+// keeps it for the backward): block j's values go out right after block j's
+// wait, so every later wait counts those NB stores as well.
+template <int BM, int BN, int WGM, int WGN, int D, bool MOUT>
 __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs p) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MB = WTM / 16, NB = WTN / 16;
@@ -456,7 +460,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
   }
   if (cw >= N) return;  // wave-uniform: this wave's columns are all past N
   const float inv_d = 1.0f / static_cast<float>(D);
-  constexpr int ST = NG * GI;  // Y stores per row block
+  constexpr int ST = NG * GI;         // Y stores per row block
+  constexpr int SM = MOUT ? NB : 0;   // M stores per row block
+  const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(MOUT ? p.m_out + m0 * N : p.y), (short)0, MOUT ? (int)(rows * (int64_t)N * 2) : 0, 0x00020000);
 #pragma unroll
   for (int j = 0; j < MB; ++j) {
     // block j must have landed; younger: block j+1's DMA (if issued before it) and the
@@ -464,9 +471,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
     if (j == 0) {
       if (MB > 1) __builtin_amdgcn_s_waitcnt(vm_wait(RES_INS)); else __builtin_amdgcn_s_waitcnt(vm_wait(0));
     } else if (j + 1 < MB) {
-      __builtin_amdgcn_s_waitcnt(vm_wait(ST + RES_INS));
+      __builtin_amdgcn_s_waitcnt(vm_wait(SM + ST + RES_INS));
     } else {
-      __builtin_amdgcn_s_waitcnt(vm_wait(ST));
+      __builtin_amdgcn_s_waitcnt(vm_wait(SM + ST));
+    }
+    if (MOUT) {  // M of this row block, before the residual is added in place
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const int n = cw + i * 16 + lg * 4;
+        const f32x4 r = acc[i][j];
+        const u32x2 o{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
+        const uint32_t off = n < N ? (uint32_t)(((int64_t)(wm * WTM + j * 16 + l16) * N + n) * 2) : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b64(o, rm, off, 0, 0);
+      }
     }
     const uint16_t* res = slot[j & 1] + l16 * WTN + lg * 4;
 #pragma unroll
@@ -719,8 +736,10 @@ const LinearVariant* pick_linear(int64_t M, int N, int K) {
 struct LinearLnVariant {
   int d;
   void (*kernel)(LinearLnKArgs);
+  void (*kernel_m)(LinearLnKArgs);  // also stores M
 };
-#define WK_LN_VARIANT(D) LinearLnVariant { D, linear_ln_kernel<256, 320, 4, 2, D> }
+#define WK_LN_VARIANT(D) \
+  LinearLnVariant { D, linear_ln_kernel<256, 320, 4, 2, D, false>, linear_ln_kernel<256, 320, 4, 2, D, true> }
 const LinearLnVariant kLnVariants[] = {WK_LN_VARIANT(16), WK_LN_VARIANT(32), WK_LN_VARIANT(80),
                                        WK_LN_VARIANT(160)};
 constexpr int kLnBM = 256, kLnBN = 320, kLnThreads = 512;
@@ -748,6 +767,7 @@ hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int6
   k.gamma = static_cast<const uint16_t*>(a.gamma);
   k.beta = static_cast<const uint16_t*>(a.beta);
   k.y = static_cast<uint16_t*>(a.y);
+  k.m_out = static_cast<uint16_t*>(a.m_out);
   k.M = a.M;
   k.N = a.N;
   k.K = a.K;
@@ -758,7 +778,7 @@ hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int6
   const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;
   if (workgroups) *workgroups = blocks;
   if (blocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(v->kernel, dim3((unsigned)blocks), dim3(kLnThreads), 0, stream, k);
+  hipLaunchKernelGGL(a.m_out ? v->kernel_m : v->kernel, dim3((unsigned)blocks), dim3(kLnThreads), 0, stream, k);
   return hipGetLastError();
 }
 

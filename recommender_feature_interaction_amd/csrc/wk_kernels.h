@@ -120,6 +120,7 @@ struct LinearLnArgs {
   int N, K, d;
   int64_t ld;
   float eps;
+  void* m_out = nullptr;  // or [M, N]: also store M = bf16(A W^T + bias) (kept for the backward)
 };
 bool linear_ln_bf16_supported(int64_t M, int N, int K, int d);
 hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int64_t* workgroups);

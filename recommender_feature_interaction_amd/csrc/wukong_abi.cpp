@@ -262,6 +262,7 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.d = d.d;
     a.ld = (int64_t)d.n * d.d;
     a.eps = d.ln_eps;
+    a.m_out = plan.keep_hidden ? static_cast<void*>(mbuf) : nullptr;  // the training forward keeps M
     return launch(WK_KERNEL_MLP_LINEAR, layer_idx, t,
                   [&](int64_t* g) { return wk::launch_linear_ln_bf16(a, launch.stream, g); });
   }
@@ -604,6 +605,7 @@ LayerPlan plan_saved(const wk_layer_desc& d, int64_t batch) {
   p.m = off;
   off += align_up(B * (size_t)d.n_f * d.d * 2);
   p.bytes = off;
+  p.fused_out = fuse_output_ln(d);  // the fused last Linear stores M for the backward as well
   return p;
 }
 
