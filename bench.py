@@ -57,6 +57,7 @@ KERNEL_SOURCES = {
     "fusion_attention": ("whale_fusion.hip",),
     "fusion_linear": ("linear_bf16.hip",),
     "fusion_ln": ("whale_fusion.hip",),
+    "fusion_ffn": ("whale_fusion.hip",),
     "bwd_out": ("wukong_backward.hip",),
     "bwd_fmb": ("wukong_backward.hip",),
     "bwd_transpose": ("wukong_backward.hip",),
@@ -386,6 +387,9 @@ def fusion_accounting(B, n, d, L, dff):
         ("fusion_linear", 0, 1): {"flops": 2 * rows * d * dff, "bytes": (rows * d + dff * d + dff + rows * dff) * 2},
         ("fusion_linear", 0, 2): {"flops": 2 * rows * dff * d,
                                   "bytes": (rows * dff + d * dff + d + 2 * rows * d) * 2},
+        # LN + both FFN products + residual in one kernel: Q read once, H_f written, silu(U) * U on chip
+        ("fusion_ffn", 0, 0): {"flops": 4 * rows * d * dff,
+                               "bytes": (2 * rows * d + 2 * dff * d + dff + 3 * d) * 2},
     }
 
 

@@ -171,9 +171,10 @@ enum {
   WK_KERNEL_BWD_WGRAD = 11,   /* backward: dW_t (index t)                     */
   WK_KERNEL_BWD_DGRAD = 12,   /* backward: gradient of the Linear's input (t) */
   WK_KERNEL_BWD_FMB = 13,     /* backward: FM LayerNorm, interaction, dX      */
-  WK_KERNEL_BWD_REDUCE = 14   /* backward: per-workgroup / per-split sums: index 0, 1
+  WK_KERNEL_BWD_REDUCE = 14,  /* backward: per-workgroup / per-split sums: index 0, 1
                                  gamma_out, beta_out; 2 + t the bias of Linear t;
                                  2 + T + 0..3 Phi, W_L, gamma_fm, beta_fm */
+  WK_KERNEL_FUSION_FFN = 15   /* fusion: pre-norm LayerNorm + SwiGLU FFN + residual in one kernel */
 };
 typedef struct wk_trace wk_trace;
 /* Creates a trace able to hold `capacity` launch records (creates HIP events
@@ -393,8 +394,12 @@ typedef struct {        /* device pointers, row-major, [out, in] weights        
   const void* b_down;   /* [d] or NULL                                          */
 } wk_fusion_weights;
 
-/* Workspace bytes for wukong_fusion_forward ([H_w, A], Q, LN(Q), silu(U) * U),
- * 0 for an invalid or unsupported desc. */
+/* Workspace bytes for wukong_fusion_forward, 0 for an invalid or unsupported
+ * desc.  The workspace holds [H_w, A] ([batch, n, 2d], at offset 0) and Q
+ * ([batch, n, d], at the next multiple of 256 bytes); when d_ff % 32 != 0 or
+ * d_ff > 4096 the FFN runs as separate kernels and LN(Q) and silu(U) * U
+ * follow.  Otherwise the LayerNorm, both FFN products and the residual are one
+ * kernel that keeps silu(U) * U on chip. */
 size_t wukong_fusion_workspace_size(const wk_fusion_desc* desc, int64_t batch);
 
 /* hf [batch, n, d] (device) from hw [batch, n, d] and hs [batch, L, d]

@@ -23,12 +23,13 @@ KERNEL_FMB_LCB, KERNEL_MLP_LINEAR, KERNEL_RESIDUAL_LN, KERNEL_HEAD_LINEAR, KERNE
 KERNEL_FUSION_ATTN, KERNEL_FUSION_LINEAR, KERNEL_FUSION_LN = 6, 7, 8
 KERNEL_BWD_OUT, KERNEL_BWD_TRANSPOSE, KERNEL_BWD_WGRAD, KERNEL_BWD_DGRAD, KERNEL_BWD_FMB, KERNEL_BWD_REDUCE = \
     9, 10, 11, 12, 13, 14
+KERNEL_FUSION_FFN = 15
 KERNEL_NAMES = {KERNEL_FMB_LCB: "fmb_lcb", KERNEL_MLP_LINEAR: "mlp_linear", KERNEL_RESIDUAL_LN: "residual_ln",
                 KERNEL_HEAD_LINEAR: "head_linear", KERNEL_HEAD_OUT: "head_out",
                 KERNEL_FUSION_ATTN: "fusion_attention", KERNEL_FUSION_LINEAR: "fusion_linear",
                 KERNEL_FUSION_LN: "fusion_ln", KERNEL_BWD_OUT: "bwd_out", KERNEL_BWD_TRANSPOSE: "bwd_transpose",
                 KERNEL_BWD_WGRAD: "bwd_wgrad", KERNEL_BWD_DGRAD: "bwd_dgrad", KERNEL_BWD_FMB: "bwd_fmb",
-                KERNEL_BWD_REDUCE: "bwd_reduce"}
+                KERNEL_BWD_REDUCE: "bwd_reduce", KERNEL_FUSION_FFN: "fusion_ffn"}
 ABI_VERSION = 1
 
 

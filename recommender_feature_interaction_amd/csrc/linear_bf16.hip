@@ -58,11 +58,7 @@ __device__ __forceinline__ float apply_res(float v, float r, int act) {
 
 __device__ __forceinline__ float apply_act(float v, int act) {
   if (act == kActRelu) return fmaxf(v, 0.f);
-  if (act == kActSiluGate) {  // v * silu(v) = v^2 * logistic(v), overflow-free
-    const float e = expf(-fabsf(v));
-    const float sig = v >= 0.f ? 1.f / (1.f + e) : e / (1.f + e);
-    return v * v * sig;
-  }
+  if (act == kActSiluGate) return silu_gate(v);
   return v;
 }
 
@@ -267,6 +263,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
   f32x4 acc[NB][MB];
   dma_mainloop<BM, BN, WGM, WGN, SPREAD>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
   const uint16_t* bias = p.bias;
+  const uint16_t* res = p.res;
+  // The residual (or mask) values are all requested before the first store:
+  // as far as the compiler knows a store to C may alias them, so a load
+  // placed after a store would wait out its whole latency on its own.
+  u32x2 rv[NB][MB];
+  if (res != nullptr) {
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int n = n0 + wn * WTN + i * 16 + lg * 4;
+#pragma unroll
+      for (int j = 0; j < MB; ++j) {
+        const int64_t m = m0 + wm * WTM + j * 16 + l16;
+        rv[i][j] = (m < M && n < N) ? *reinterpret_cast<const u32x2*>(res + m * N + n) : u32x2{0u, 0u};
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int n = n0 + wn * WTN + i * 16 + lg * 4;
@@ -282,8 +294,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
         float v[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = apply_act(acc[i][j][t] + bb[t], p.act);
-        if (p.res != nullptr) {
-          const u32x2 r2 = *reinterpret_cast<const u32x2*>(p.res + m * N + n);
+        if (res != nullptr) {
+          const u32x2 r2 = rv[i][j];
           v[0] = apply_res(v[0], bf16lo(r2[0]), p.act);
           v[1] = apply_res(v[1], bf16hi(r2[0]), p.act);
           v[2] = apply_res(v[2], bf16lo(r2[1]), p.act);

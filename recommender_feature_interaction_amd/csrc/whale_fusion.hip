@@ -1,6 +1,7 @@
-// WHALE's attention-based fusion step: the cross-branch attention and a row
-// LayerNorm (bf16, fp32 accumulation).  The Linear layers of the step run on
-// the MLP GEMM kernels.
+// WHALE's attention-based fusion step: the cross-branch attention, the FFN
+// as one kernel, and a row LayerNorm for the unfused FFN (bf16, fp32
+// accumulation).  The Fusion MLP's Linear (and the unfused FFN's Linears)
+// run on the MLP GEMM kernels.
 //
 // WHALE technical summaries, section 2.1: the Wukong module's interaction
 // representation H_w is the query and the HSTU module's behaviour
@@ -279,7 +280,256 @@ __global__ __launch_bounds__(256) void row_ln_bf16_kernel(const uint16_t* x, uin
   *reinterpret_cast<u32x4*>(y + r * d + sub * 8) = o;
 }
 
+// ---- The fusion step's FFN in one kernel (WHALE section 2.2, pre-norm
+// shared-gate SwiGLU with its residual):
+//   H_f = Q + (silu(U) * U) W_down^T + b_down,   U = LN_d(Q) W_up^T + b_up.
+// A workgroup of W waves takes W x 32 rows (32 per wave) and walks d_ff in
+// chunks of 32: the chunk's 32 rows of W_up and 32 columns of W_down are
+// DMA'd (buffer_load ... lds) into one of two LDS stages while the other
+// stage is consumed, so silu(U) * U never leaves registers and the hidden
+// width costs no HBM traffic.  Register layouts, lane = (l16, lg), lg = lane / 16:
+//  * LN(Q) is the B operand of U^T = W_up LN(Q)^T: the lane holds row l16,
+//    columns 32 ks + 8 lg .. + 7 (one 16-byte load of Q per K step).
+//  * A-operand row i of U block fb is the chunk's W_up row 8 (i / 4) + 4 fb +
+//    i % 4, so output lane (l16, lg) receives row l16's U at chunk columns
+//    8 lg + 4 fb + t: over its two blocks, 8 consecutive columns, which is
+//    the B operand of H^T = W_down G^T for the chunk's K step as it stands.
+//  * H^T: the lane holds row l16, columns 16 jb + 4 lg + t; the bias, the
+//    residual Q (reloaded in this layout) and the stores are 8 bytes a lane.
+// The LDS copies are XOR-swizzled in 16-byte units so the 16-row fragment
+// reads spread over the banks.  Rows past the end read as zero and their
+// stores are dropped (buffer resources end at the last row).
+struct FfnKArgs {
+  const uint16_t* q;
+  const uint16_t* gamma;
+  const uint16_t* beta;
+  const uint16_t* w_up;
+  const uint16_t* b_up;
+  const uint16_t* w_down;
+  const uint16_t* b_down;
+  uint16_t* out;
+  int64_t rows;
+  int F;
+  float eps;
+};
+
+constexpr int FRB = 2;          // 16-row blocks per wave
+constexpr int FC = 32;          // d_ff columns per chunk
+constexpr int kFfnMaxF = 4096;  // b_up is staged in LDS whole
+
+// 16-byte unit swizzle of a W_up chunk row (C units a row): within groups of 8
+// units when C % 8 == 0, else of 4
+template <int C>
+__device__ __forceinline__ int up_swz(int row) {
+  return C % 8 == 0 ? ((row & 3) | ((row >> 1) & 4)) : (((row >> 1) & 1) | ((row >> 2) & 2));
+}
+__device__ __forceinline__ int down_swz(int j) { return (j >> 1) & 3; }
+
+template <int D, int W>
+__global__ __launch_bounds__(W * 64) void fusion_ffn_kernel(FfnKArgs p) {
+  constexpr int KS = D / 32, JB = D / 16, C16 = D / 8;
+  constexpr int SU = FC * D, SD = D * FC;      // u16 of a stage's W_up and W_down parts
+  constexpr int NIU = SU / 512, NI = (SU + SD) / 512;  // 1 KB DMA instructions per chunk
+  constexpr int ROWS = W * FRB * 16;
+  static_assert(D % 32 == 0 && SU % 512 == 0, "whole K steps and DMA instructions");
+  __shared__ __align__(16) uint16_t wu0[SU], wd0[SD], wu1[SU], wd1[SD];
+  __shared__ __align__(16) uint16_t sbu[kFfnMaxF];
+  __shared__ __align__(16) uint16_t sg[D], sbt[D], sbd[D];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int F = p.F, NC = F / FC;
+
+  const __amdgpu_buffer_rsrc_t rwu = __builtin_amdgcn_make_buffer_rsrc((void*)p.w_up, (short)0, F * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rwd =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.w_down, (short)0, D * F * 2, 0x00020000);
+  auto dma = [&](uint16_t* su, uint16_t* sd, int c) {
+    for (int i = wave; i < NI; i += W) {  // wave-uniform
+      const int u = (i < NIU ? i : i - NIU) * 64 + lane;  // 16-byte unit of the part
+      if (i < NIU) {
+        const int row = u / C16, pu = u - row * C16;
+        const uint32_t vo = (uint32_t)(((c * FC + row) * D + (pu ^ up_swz<C16>(row)) * 8) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rwu, WF_LDSV(su + i * 512), 16, vo, 0, 0, 0);
+      } else {
+        const int j = u >> 2, pu = u & 3;
+        const uint32_t vo = (uint32_t)((j * F + c * FC + (pu ^ down_swz(j)) * 8) * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rwd, WF_LDSV(sd + (i - NIU) * 512), 16, vo, 0, 0, 0);
+      }
+    }
+  };
+  dma(wu0, wd0, 0);
+  for (int i = tid; i < F; i += W * 64) sbu[i] = p.b_up ? p.b_up[i] : (uint16_t)0;
+  for (int i = tid; i < D; i += W * 64) {
+    sg[i] = p.gamma ? p.gamma[i] : (uint16_t)0x3f80u;
+    sbt[i] = p.beta ? p.beta[i] : (uint16_t)0;
+    sbd[i] = p.b_down ? p.b_down[i] : (uint16_t)0;
+  }
+
+  // this workgroup's rows: Q in the B-operand layout
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  const int nrows = (int)min<int64_t>(ROWS, p.rows - r0);
+  const __amdgpu_buffer_rsrc_t rq =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.q + r0 * D), (short)0, nrows * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.out + r0 * D), (short)0, nrows * D * 2, 0x00020000);
+  const int wrow = wave * FRB * 16;
+  u32x4 qn[FRB][KS];
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb)
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qn[rb][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+          rq, (uint32_t)(((wrow + rb * 16 + l16) * D + ks * 32 + lg * 8) * 2), 0, 0);
+  __syncthreads();  // the staged constants (and chunk 0, which the wait inside covers)
+
+  // LN(Q) per row: the row's D values sit in the 4 lanes l16 + 16 lg
+  const float inv_d = 1.0f / static_cast<float>(D);
+#pragma unroll
+  for (int rb = 0; rb < FRB; ++rb) {
+    float v[KS][8];
+    float sm = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[ks][2 * e] = bf16lo(qn[rb][ks][e]);
+        v[ks][2 * e + 1] = bf16hi(qn[rb][ks][e]);
+        sm += v[ks][2 * e] + v[ks][2 * e + 1];
+      }
+    sm += __shfl_xor(sm, 16, kWave);
+    sm += __shfl_xor(sm, 32, kWave);
+    const float mean = sm * inv_d;
+    float q = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q += (v[ks][e] - mean) * (v[ks][e] - mean);
+    q += __shfl_xor(q, 16, kWave);
+    q += __shfl_xor(q, 32, kWave);
+    const float rstd = rsqrtf(q * inv_d + p.eps);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const u32x4 g = *reinterpret_cast<const u32x4*>(sg + ks * 32 + lg * 8);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(sbt + ks * 32 + lg * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        qn[rb][ks][e] = pack_bf16x2((v[ks][2 * e] - mean) * rstd * bf16lo(g[e]) + bf16lo(b[e]),
+                                    (v[ks][2 * e + 1] - mean) * rstd * bf16hi(g[e]) + bf16hi(b[e]));
+    }
+  }
+
+  f32x4 oacc[JB][FRB];
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb) oacc[jb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // the W_up rows this lane supplies as A-operand row l16 of blocks 0 and 1
+  const int urow0 = 8 * (l16 >> 2) + (l16 & 3), urow1 = urow0 + 4;
+  auto chunk = [&](const uint16_t* su, const uint16_t* sd, uint16_t* nu, uint16_t* nd, int c) {
+    if (c + 1 < NC) dma(nu, nd, c + 1);
+    f32x4 uacc[2][FRB];
+#pragma unroll
+    for (int fb = 0; fb < 2; ++fb)
+#pragma unroll
+      for (int rb = 0; rb < FRB; ++rb) uacc[fb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cu = ks * 4 + lg;
+      const u32x4 a0 = *reinterpret_cast<const u32x4*>(su + (urow0 * C16 + (cu ^ up_swz<C16>(urow0))) * 8);
+      const u32x4 a1 = *reinterpret_cast<const u32x4*>(su + (urow1 * C16 + (cu ^ up_swz<C16>(urow1))) * 8);
+#pragma unroll
+      for (int rb = 0; rb < FRB; ++rb) {
+        uacc[0][rb] = mfma16x16x32(a0, qn[rb][ks], uacc[0][rb]);
+        uacc[1][rb] = mfma16x16x32(a1, qn[rb][ks], uacc[1][rb]);
+      }
+    }
+    // G = silu(U) * U in bf16: the B operand of the W_down product
+    const u32x4 bu = *reinterpret_cast<const u32x4*>(sbu + c * FC + lg * 8);
+    u32x4 gop[FRB];
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb)
+#pragma unroll
+      for (int fb = 0; fb < 2; ++fb) {
+        const f32x4 u = uacc[fb][rb];
+        const uint32_t b01 = bu[2 * fb], b23 = bu[2 * fb + 1];
+        gop[rb][2 * fb] = pack_bf16x2(silu_gate(u[0] + bf16lo(b01)), silu_gate(u[1] + bf16hi(b01)));
+        gop[rb][2 * fb + 1] = pack_bf16x2(silu_gate(u[2] + bf16lo(b23)), silu_gate(u[3] + bf16hi(b23)));
+      }
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int j = jb * 16 + l16;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(sd + (j * 4 + (lg ^ down_swz(j))) * 8);
+#pragma unroll
+      for (int rb = 0; rb < FRB; ++rb) oacc[jb][rb] = mfma16x16x32(a, gop[rb], oacc[jb][rb]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0070);  // this wave's part of the next chunk landed (vmcnt(0), lgkmcnt(0))
+    lds_barrier();                       // ... every wave's, and every wave is done with this stage
+  };
+  for (int c = 0; c < NC; c += 2) {
+    chunk(wu0, wd0, wu1, wd1, c);
+    if (c + 1 < NC) chunk(wu1, wd1, wu0, wd0, c + 1);
+  }
+
+  // H_f = Q + H + b_down, Q reloaded in the H^T layout
+  u32x2 qr[JB][FRB];
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb)
+      qr[jb][rb] = __builtin_amdgcn_raw_buffer_load_b64(
+          rq, (uint32_t)(((wrow + rb * 16 + l16) * D + jb * 16 + lg * 4) * 2), 0, 0);
+#pragma unroll
+  for (int jb = 0; jb < JB; ++jb) {
+    const u32x2 bd = *reinterpret_cast<const u32x2*>(sbd + jb * 16 + lg * 4);
+#pragma unroll
+    for (int rb = 0; rb < FRB; ++rb) {
+      const f32x4 h = oacc[jb][rb];
+      const u32x2 r = qr[jb][rb];
+      u32x2 o;
+      o[0] = pack_bf16x2(h[0] + bf16lo(bd[0]) + bf16lo(r[0]), h[1] + bf16hi(bd[0]) + bf16hi(r[0]));
+      o[1] = pack_bf16x2(h[2] + bf16lo(bd[1]) + bf16lo(r[1]), h[3] + bf16hi(bd[1]) + bf16hi(r[1]));
+      __builtin_amdgcn_raw_buffer_store_b64(o, ro, (uint32_t)(((wrow + rb * 16 + l16) * D + jb * 16 + lg * 4) * 2),
+                                            0, 0);
+    }
+  }
+}
+
 }  // namespace
+
+bool fusion_ffn_supported(int d, int d_ff) {
+  return (d == 32 || d == 64 || d == 96 || d == 128 || d == 160) && d_ff >= FC && d_ff % FC == 0 &&
+         d_ff <= kFfnMaxF;
+}
+
+hipError_t launch_fusion_ffn(const FusionFfnArgs& a, hipStream_t stream, int64_t* workgroups) {
+  if (!fusion_ffn_supported(a.d, a.d_ff) || a.rows < 0) return hipErrorInvalidValue;
+  constexpr int W = 8;
+  FfnKArgs k;
+  k.q = static_cast<const uint16_t*>(a.q);
+  k.gamma = static_cast<const uint16_t*>(a.gamma);
+  k.beta = static_cast<const uint16_t*>(a.beta);
+  k.w_up = static_cast<const uint16_t*>(a.w_up);
+  k.b_up = static_cast<const uint16_t*>(a.b_up);
+  k.w_down = static_cast<const uint16_t*>(a.w_down);
+  k.b_down = static_cast<const uint16_t*>(a.b_down);
+  k.out = static_cast<uint16_t*>(a.out);
+  k.rows = a.rows;
+  k.F = a.d_ff;
+  k.eps = a.eps;
+  const int64_t blocks = (a.rows + W * FRB * 16 - 1) / (W * FRB * 16);
+  if (workgroups) *workgroups = blocks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks), block(W * 64);
+  switch (a.d) {
+    case 32: hipLaunchKernelGGL((fusion_ffn_kernel<32, W>), grid, block, 0, stream, k); break;
+    case 64: hipLaunchKernelGGL((fusion_ffn_kernel<64, W>), grid, block, 0, stream, k); break;
+    case 96: hipLaunchKernelGGL((fusion_ffn_kernel<96, W>), grid, block, 0, stream, k); break;
+    case 128: hipLaunchKernelGGL((fusion_ffn_kernel<128, W>), grid, block, 0, stream, k); break;
+    default: hipLaunchKernelGGL((fusion_ffn_kernel<160, W>), grid, block, 0, stream, k); break;
+  }
+  return hipGetLastError();
+}
 
 bool whale_attention_supported(int n, int d, int L) {
   return n > 0 && n % 16 == 0 && L > 0 && (d == 32 || d == 64 || d == 96 || d == 128 || d == 160) &&

@@ -65,6 +65,15 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
+// The shared-gate SwiGLU activation silu(v) * v = v^2 * logistic(v), in an
+// overflow-free form, with the hardware exp2 and reciprocal (about 1 ulp
+// each; the callers round the result to bf16).
+__device__ __forceinline__ float silu_gate(float v) {
+  const float e = __expf(-fabsf(v));
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
+  return v * v * (v >= 0.f ? r : e * r);
+}
+
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
 // workgroup release/acquire fence plus s_barrier, and on gfx9 the release
 // half waits for every outstanding vector memory operation (global loads and

@@ -37,6 +37,24 @@ hipError_t launch_whale_attention(const void* hw, const void* hs, void* c, int64
                                   hipStream_t stream, int64_t* workgroups);
 hipError_t launch_row_ln_bf16(const void* x, void* y, int64_t rows, int d, const void* gamma, const void* beta,
                               float eps, hipStream_t stream, int64_t* workgroups);
+// The fusion step's FFN as one kernel: out = q + (silu(U) * U) w_down^T + b_down,
+// U = LN_d(q; gamma, beta) w_up^T + b_up, rows of d (bf16; gamma, beta and the
+// biases may be null).  d in {32, 64, 96, 128, 160}, d_ff % 32 == 0, d_ff <= 4096.
+struct FusionFfnArgs {
+  const void* q;       // [rows, d]: the FFN input and its residual
+  const void* gamma;   // [d]
+  const void* beta;    // [d]
+  const void* w_up;    // [d_ff, d]
+  const void* b_up;    // [d_ff]
+  const void* w_down;  // [d, d_ff]
+  const void* b_down;  // [d]
+  void* out;           // [rows, d]
+  int64_t rows;
+  int d, d_ff;
+  float eps;
+};
+bool fusion_ffn_supported(int d, int d_ff);
+hipError_t launch_fusion_ffn(const FusionFfnArgs& a, hipStream_t stream, int64_t* workgroups);
 // Units of width d = 8 (fmb_lcb_units.hip): transpose, one batched GEMM with
 // fp32 output, and an epilogue kernel; needs fmb_lcb_units_workspace() bytes
 // of scratch (16-byte aligned), n % 64 == 0, k % 4 == 0, k <= 32,

@@ -453,16 +453,21 @@ int32_t check_fusion_desc(const wk_fusion_desc* d) {
 
 struct FusionPlan {
   size_t c = 0, q = 0, qn = 0, g = 0, bytes = 0;
+  bool fused_ffn = false;  // LayerNorm + FFN + residual as one kernel: no LN(Q) or G buffers
 };
 
 FusionPlan plan_fusion(const wk_fusion_desc& d, int64_t batch) {
   FusionPlan p;
   const size_t rows = (size_t)batch * d.n;
+  p.fused_ffn = wk::fusion_ffn_supported(d.d, d.d_ff);
   p.c = 0;
   p.q = p.c + align_up(rows * 2 * d.d * 2);
-  p.qn = p.q + align_up(rows * d.d * 2);
-  p.g = p.qn + align_up(rows * d.d * 2);
-  p.bytes = p.g + align_up(rows * d.d_ff * 2);
+  p.bytes = p.q + align_up(rows * d.d * 2);
+  if (!p.fused_ffn) {
+    p.qn = p.bytes;
+    p.g = p.qn + align_up(rows * d.d * 2);
+    p.bytes = p.g + align_up(rows * d.d_ff * 2);
+  }
   if (p.bytes == 0) p.bytes = kAlign;
   return p;
 }
@@ -514,6 +519,23 @@ int32_t fusion_forward(const wk_fusion_desc* d, const wk_fusion_weights* w, int6
   };
   st = linear(0, c, w->w_f, w->b_f, q, d->d, 2 * d->d, wk::kActNone, nullptr);
   if (st != WK_OK) return st;
+  if (fp.fused_ffn) {
+    wk::FusionFfnArgs fa;
+    fa.q = q;
+    fa.gamma = w->ln_gamma;
+    fa.beta = w->ln_beta;
+    fa.w_up = w->w_up;
+    fa.b_up = w->b_up;
+    fa.w_down = w->w_down;
+    fa.b_down = w->b_down;
+    fa.out = hf;
+    fa.rows = rows;
+    fa.d = d->d;
+    fa.d_ff = d->d_ff;
+    fa.eps = d->ln_eps;
+    return launch(WK_KERNEL_FUSION_FFN, 0, 0,
+                  [&](int64_t* wg) { return wk::launch_fusion_ffn(fa, launch.stream, wg); });
+  }
   st = launch(WK_KERNEL_FUSION_LN, 0, 0, [&](int64_t* wg) {
     return wk::launch_row_ln_bf16(q, qn, rows, d->d, w->ln_gamma, w->ln_beta, d->ln_eps, launch.stream, wg);
   });

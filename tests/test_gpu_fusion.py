@@ -63,6 +63,8 @@ CASES = [
     (3, 16, 32, 1, 128),       # one position: A equals it for every query
     (2, 48, 96, 33, 384),      # a partly filled query chunk
     (2, 144, 128, 100, 512),   # two query chunks
+    (3, 48, 160, 70, 200),     # d_ff % 32 != 0: the FFN as separate kernels
+    (7, 80, 160, 20, 32),      # one d_ff chunk; 560 rows, a ragged last FFN tile
 ]
 
 
@@ -92,14 +94,19 @@ def test_fusion_sharp_softmax_and_identity_affine():
     check("H_f (sharp attention)", host_f64(to_host(r.forward())), r.oracle(), "bf16")
 
 
-def test_fusion_trace_determinism_and_batch_invariance():
-    r = FusionRun(6, 128, 160, 257, 640, seed=5)
+FUSED_KINDS = [("fusion_attention", 0), ("fusion_linear", 0), ("fusion_ffn", 0)]
+UNFUSED_KINDS = [("fusion_attention", 0), ("fusion_linear", 0), ("fusion_ln", 0), ("fusion_linear", 1),
+                 ("fusion_linear", 2)]
+
+
+@pytest.mark.parametrize("dff,kinds", [(640, FUSED_KINDS), (200, UNFUSED_KINDS)], ids=["fused_ffn", "unfused_ffn"])
+def test_fusion_trace_determinism_and_batch_invariance(dff, kinds):
+    r = FusionRun(6, 128, 160, 257, dff, seed=5)
     tr = wk.Trace(capacity=16)
     y1 = to_host(r.forward(trace=tr))
-    kinds = [(x["kernel"], x["index"]) for x in tr.records()]
+    got = [(x["kernel"], x["index"]) for x in tr.records()]
     tr.close()
-    assert kinds == [("fusion_attention", 0), ("fusion_linear", 0), ("fusion_ln", 0), ("fusion_linear", 1),
-                     ("fusion_linear", 2)], kinds
+    assert got == kinds, got
     assert np.array_equal(y1, to_host(r.forward())), "two runs differ"
     sub = wk.fusion_forward(r.hwd[2:5].contiguous(), r.hsd[2:5].contiguous(), r.dev)
     torch.cuda.synchronize()
