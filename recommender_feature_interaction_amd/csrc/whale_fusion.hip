@@ -332,7 +332,8 @@ __global__ __launch_bounds__(W * 64) void fusion_ffn_kernel(FfnKArgs p) {
   constexpr int NIU = SU / 512, NI = (SU + SD) / 512;  // 1 KB DMA instructions per chunk
   constexpr int ROWS = W * FRB * 16;
   static_assert(D % 32 == 0 && SU % 512 == 0, "whole K steps and DMA instructions");
-  __shared__ __align__(16) uint16_t wu0[SU], wd0[SD], wu1[SU], wd1[SD];
+  constexpr int HI = (NI + W - 1) / W, LO = NI / W, R = NI % W;  // a wave's DMA instructions per chunk
+  __shared__ __align__(16) uint16_t wu0[SU], wd0[SD], wu1[SU], wd1[SD], wu2[SU], wd2[SD];
   __shared__ __align__(16) uint16_t sbu[kFfnMaxF];
   __shared__ __align__(16) uint16_t sg[D], sbt[D], sbd[D];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -358,6 +359,7 @@ __global__ __launch_bounds__(W * 64) void fusion_ffn_kernel(FfnKArgs p) {
     }
   };
   dma(wu0, wd0, 0);
+  if (NC > 1) dma(wu1, wd1, 1);
   for (int i = tid; i < F; i += W * 64) sbu[i] = p.b_up ? p.b_up[i] : (uint16_t)0;
   for (int i = tid; i < D; i += W * 64) {
     sg[i] = p.gamma ? p.gamma[i] : (uint16_t)0x3f80u;
@@ -425,13 +427,17 @@ __global__ __launch_bounds__(W * 64) void fusion_ffn_kernel(FfnKArgs p) {
     for (int rb = 0; rb < FRB; ++rb) oacc[jb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
   // the W_up rows this lane supplies as A-operand row l16 of blocks 0 and 1
   const int urow0 = 8 * (l16 >> 2) + (l16 & 3), urow1 = urow0 + 4;
+  // chunk c reads stage c % 3 and sends chunk c + 2 to stage (c + 2) % 3, last read by chunk c - 1
   auto chunk = [&](const uint16_t* su, const uint16_t* sd, uint16_t* nu, uint16_t* nd, int c) {
-    if (c + 1 < NC) dma(nu, nd, c + 1);
+    if (c + 2 < NC) dma(nu, nd, c + 2);
+    // U starts from its bias: chunk columns 8 lg + 4 fb + t
+    const u32x4 bu = *reinterpret_cast<const u32x4*>(sbu + c * FC + lg * 8);
     f32x4 uacc[2][FRB];
 #pragma unroll
     for (int fb = 0; fb < 2; ++fb)
 #pragma unroll
-      for (int rb = 0; rb < FRB; ++rb) uacc[fb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < FRB; ++rb)
+        uacc[fb][rb] = f32x4{bf16lo(bu[2 * fb]), bf16hi(bu[2 * fb]), bf16lo(bu[2 * fb + 1]), bf16hi(bu[2 * fb + 1])};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int cu = ks * 4 + lg;
@@ -443,31 +449,42 @@ __global__ __launch_bounds__(W * 64) void fusion_ffn_kernel(FfnKArgs p) {
         uacc[1][rb] = mfma16x16x32(a1, qn[rb][ks], uacc[1][rb]);
       }
     }
+    // the W_down fragments, requested before the gate so their latency hides under it
+    u32x4 wdf[JB];
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) {
+      const int j = jb * 16 + l16;
+      wdf[jb] = *reinterpret_cast<const u32x4*>(sd + (j * 4 + (lg ^ down_swz(j))) * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keeps the scheduler from sinking them to their use
     // G = silu(U) * U in bf16: the B operand of the W_down product
-    const u32x4 bu = *reinterpret_cast<const u32x4*>(sbu + c * FC + lg * 8);
     u32x4 gop[FRB];
 #pragma unroll
     for (int rb = 0; rb < FRB; ++rb)
 #pragma unroll
       for (int fb = 0; fb < 2; ++fb) {
         const f32x4 u = uacc[fb][rb];
-        const uint32_t b01 = bu[2 * fb], b23 = bu[2 * fb + 1];
-        gop[rb][2 * fb] = pack_bf16x2(silu_gate(u[0] + bf16lo(b01)), silu_gate(u[1] + bf16hi(b01)));
-        gop[rb][2 * fb + 1] = pack_bf16x2(silu_gate(u[2] + bf16lo(b23)), silu_gate(u[3] + bf16hi(b23)));
+        gop[rb][2 * fb] = pack_bf16x2(silu_gate(u[0]), silu_gate(u[1]));
+        gop[rb][2 * fb + 1] = pack_bf16x2(silu_gate(u[2]), silu_gate(u[3]));
       }
 #pragma unroll
-    for (int jb = 0; jb < JB; ++jb) {
-      const int j = jb * 16 + l16;
-      const u32x4 a = *reinterpret_cast<const u32x4*>(sd + (j * 4 + (lg ^ down_swz(j))) * 8);
+    for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
-      for (int rb = 0; rb < FRB; ++rb) oacc[jb][rb] = mfma16x16x32(a, gop[rb], oacc[jb][rb]);
+      for (int rb = 0; rb < FRB; ++rb) oacc[jb][rb] = mfma16x16x32(wdf[jb], gop[rb], oacc[jb][rb]);
+    // this wave's copies of chunk c + 1 have landed (those of chunk c + 2 may be in flight),
+    // then every wave's, and every wave is done with this stage
+    if (c + 2 < NC) {
+      if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(HI));
+      else __builtin_amdgcn_s_waitcnt(vm_enc(LO));
+    } else {
+      __builtin_amdgcn_s_waitcnt(vm_enc(0));
     }
-    __builtin_amdgcn_s_waitcnt(0x0070);  // this wave's part of the next chunk landed (vmcnt(0), lgkmcnt(0))
-    lds_barrier();                       // ... every wave's, and every wave is done with this stage
+    lds_barrier();
   };
-  for (int c = 0; c < NC; c += 2) {
-    chunk(wu0, wd0, wu1, wd1, c);
+  for (int c = 0; c < NC; c += 3) {
+    chunk(wu0, wd0, wu2, wd2, c);
     if (c + 1 < NC) chunk(wu1, wd1, wu0, wd0, c + 1);
+    if (c + 2 < NC) chunk(wu2, wd2, wu1, wd1, c + 2);
   }
 
   // H_f = Q + H + b_down, Q reloaded in the H^T layout

@@ -65,13 +65,12 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
-// The shared-gate SwiGLU activation silu(v) * v = v^2 * logistic(v), in an
-// overflow-free form, with the hardware exp2 and reciprocal (about 1 ulp
-// each; the callers round the result to bf16).
+// The shared-gate SwiGLU activation silu(v) * v = v^2 * logistic(v) with the
+// hardware exp2 and reciprocal (about 1 ulp each; the callers round the
+// result to bf16).  For v < -88, exp(-v) overflows to +inf and the reciprocal
+// gives 0, the value to bf16 precision.
 __device__ __forceinline__ float silu_gate(float v) {
-  const float e = __expf(-fabsf(v));
-  const float r = __builtin_amdgcn_rcpf(1.f + e);
-  return v * v * (v >= 0.f ? r : e * r);
+  return v * v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
