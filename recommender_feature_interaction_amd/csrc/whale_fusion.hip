@@ -13,14 +13,18 @@
 // whale_attention_kernel: one workgroup of 4 waves per (example, 128
 // queries), 32 queries per wave.  Key tiles of 32 positions x d are DMA'd
 // (buffer_load ... lds) into a ring of 4 LDS slots, 3 tiles ahead; each tile
-// is read twice from LDS, as K (rows, for S = Q K^T) and as V (transposed
-// reads, for O += P V): the shared K = V is loaded once.  S and O use
-// v_mfma_f32_16x16x32_bf16; the softmax is the online form (running row
-// maximum and sum, O rescaled when the maximum grows), in base 2 with the
-// 1/sqrt(d) scale folded into the exponent; row maxima and sums are DPP
-// row rotations.  P goes through a per-wave LDS
-// tile in bf16 to become the A operand of P V.  Positions past L read as
-// zero through the buffer resource and are masked to -inf.
+// is read twice from LDS, as K (rows, for S^T = K Q^T) and as V (transposed
+// reads, for O^T += V^T P^T): the shared K = V is loaded once.  Both products
+// are computed transposed on v_mfma_f32_16x16x32_bf16, so a lane (li, lg)
+// holds scores of one query (li) at keys 16 kk + 4 lg + t: over the tile's two
+// key blocks, 8 keys, which in bf16 are exactly its B operand of the P V
+// product when V^T's rows are read in the same key order -- P stays in
+// registers.  The softmax is the online form (running maximum per query, O
+// rescaled when it grows), in base 2 with the 1/sqrt(d) scale folded into the
+// exponent; the 4 lanes of a query combine maxima with two xor-shuffles per
+// key tile and keep partial sums that are combined once at the end.
+// Positions past L read as zero through the buffer resource and are masked
+// to -inf.
 #include <math.h>
 
 #include "wk_device.h"
@@ -52,27 +56,6 @@ __device__ __forceinline__ u32x4 tr_rows8(const uint16_t* p0, const uint16_t* p1
   return u32x4{ua[0], ua[1], ub[0], ub[1]};
 }
 
-// Max and sum over the 16 lanes of a DPP row (lanes 16 r .. 16 r + 15), every
-// lane receiving the result: v op= v rotated by 8, 4, 2, 1 within the row
-// (row_ror), a butterfly in which each lane ends up combining all 16 values.
-// Plain VALU with a DPP operand, instead of LDS-crossbar permutes.
-template <int ROR>
-__device__ __forceinline__ float row_ror(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x120 + ROR, 0xf, 0xf, true));
-}
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, row_ror<8>(v));
-  v = fmaxf(v, row_ror<4>(v));
-  v = fmaxf(v, row_ror<2>(v));
-  return fmaxf(v, row_ror<1>(v));
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += row_ror<8>(v);
-  v += row_ror<4>(v);
-  v += row_ror<2>(v);
-  return v + row_ror<1>(v);
-}
-
 struct AttnArgs {
   const uint16_t* hw;  // [B, n, D]
   const uint16_t* hs;  // [B, L, D]
@@ -91,7 +74,6 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
   constexpr int INS_HI = (INS + AW - 1) / AW, INS_LO = INS / AW, R = INS % AW;
   static_assert(D % 32 == 0 && INS * 1024 == TILE * 2, "D must be a multiple of 32");
   __shared__ __align__(16) uint16_t s0[TILE], s1[TILE], s2[TILE], s3[TILE];
-  __shared__ __align__(16) uint16_t ps[AW][AQ * AKT];
   uint16_t* const slot[4] = {s0, s1, s2, s3};  // indexed with compile-time numbers only
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -102,6 +84,7 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
   const int64_t b = blockIdx.x / qchunks;
   const int q0 = (int)(blockIdx.x - b * qchunks) * (AW * AQ) + wave * AQ;
   const int T = (L + AKT - 1) / AKT;
+  const float scale = p.scale_log2;
 
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.hs + b * (int64_t)L * D), (short)0, L * D * 2, 0x00020000);
@@ -116,7 +99,7 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
     }
   };
 
-  // queries of this wave as MFMA A operands: rows q0 + 16 qt + li, columns 32 c + 8 lg ..
+  // queries of this wave as MFMA B operands: query q0 + 16 qt + li, columns 32 c + 8 lg ..
   u32x4 qf[2][DC];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
@@ -131,20 +114,19 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
   for (int u = 0; u < 3; ++u)
     if (u < T) dma(slot[u], u);
 
+  // O^T: o[qt][dt][t] = O[query q0 + 16 qt + li][column 16 dt + 4 lg + t]; per query
+  // (qt) the running maximum (scaled, base 2) and this lane's part of the sum
   f32x4 o[2][DT];
-  float mrow[2][4], lrow[2][4];
+  float mrow[2], lrow[2];
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      mrow[qt][t] = -INFINITY;
-      lrow[qt][t] = 0.f;
-    }
+    mrow[qt] = -INFINITY;
+    lrow[qt] = 0.f;
   }
-  const int xa = (8 * lg + (li >> 2)) * D + 4 * (li & 3);  // transposed-read lane offset
-  uint16_t* pw = ps[wave];
+  // V^T operand lanes: key rows 4 lg + li / 4 (and 16 further), column 4 (li % 4)
+  const int xa = (4 * lg + (li >> 2)) * D + 4 * (li & 3);
 
   auto step = [&](const uint16_t* kt, uint16_t* next, int t) {
     const int newer = (T - 1 - t < 2) ? T - 1 - t : 2;  // DMA steps issued after step t
@@ -159,56 +141,64 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
     }
     lds_barrier();
     if (t + 3 < T) dma(next, t + 3);
-    // S = Q K^T: rows 4 lg + r of query tile qt, key 16 kk + li
-    f32x4 s[2][2];
+    // S^T = K Q^T: s[qt][kk][t] = S[query 16 qt + li][key 16 kk + 4 lg + t]
+    f32x4 sc[2][2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) s[qt][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < 2; ++kk) sc[qt][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + (kk * 16 + li) * D + c * 32 + lg * 8);
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) s[qt][kk] = mfma16x16x32(qf[qt][c], kf, s[qt][kk]);
+        for (int qt = 0; qt < 2; ++qt) sc[qt][kk] = mfma16x16x32(kf, qf[qt][c], sc[qt][kk]);
       }
     }
-    // online softmax (base 2), P to this wave's LDS tile as bf16 [32 queries][32 keys]
+    // online softmax per query; P^T in bf16 as the B operand of V^T P^T, key slots
+    // 0..3 = keys 4 lg + t, 4..7 = keys 16 + 4 lg + t
+    u32x4 pf[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
+      if (t == T - 1) {  // only the last key tile can reach past L
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float v0 = s[qt][0][r] * p.scale_log2, v1 = s[qt][1][r] * p.scale_log2;
-        if (t == T - 1) {  // only the last key tile can reach past L
-          if (t * AKT + li >= L) v0 = -INFINITY;
-          if (t * AKT + 16 + li >= L) v1 = -INFINITY;
-        }
-        const float mx = row16_max(fmaxf(v0, v1));
-        const float mnew = fmaxf(mrow[qt][r], mx);
-        const float alpha = exp2f(mrow[qt][r] - mnew);
-        const float e0 = exp2f(v0 - mnew), e1 = exp2f(v1 - mnew);
-        lrow[qt][r] = lrow[qt][r] * alpha + row16_sum(e0 + e1);
-        // rescale O only when some row's running maximum grew (alpha is exactly 1 otherwise)
-        if (__builtin_amdgcn_ballot_w64(mnew != mrow[qt][r]) != 0) {
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-          for (int dt = 0; dt < DT; ++dt) o[qt][dt][r] *= alpha;
-        }
-        mrow[qt][r] = mnew;
-        const int row = qt * 16 + 4 * lg + r;
-        pw[row * AKT + li] = (uint16_t)f32_to_bf16(e0);
-        pw[row * AKT + 16 + li] = (uint16_t)f32_to_bf16(e1);
+          for (int r = 0; r < 4; ++r)
+            if (t * AKT + kk * 16 + 4 * lg + r >= L) sc[qt][kk][r] = -INFINITY;
       }
+      float mx = fmaxf(fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3])),
+                       fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float mnew = fmaxf(mrow[qt], mx * scale);
+      const float alpha = exp2f(mrow[qt] - mnew);
+      float e[2][4];
+      float sm = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          e[kk][r] = exp2f(fmaf(sc[qt][kk][r], scale, -mnew));
+          sm += e[kk][r];
+        }
+      lrow[qt] = fmaf(lrow[qt], alpha, sm);
+      // rescale O only when some query's running maximum grew (alpha is exactly 1 otherwise)
+      if (__builtin_amdgcn_ballot_w64(mnew != mrow[qt]) != 0) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
+      }
+      mrow[qt] = mnew;
+      pf[qt] = u32x4{pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]), pack_bf16x2(e[1][0], e[1][1]),
+                     pack_bf16x2(e[1][2], e[1][3])};
     }
-    // O += P V, V = the same key tile read transposed
+    // O^T += V^T P^T, V = the same key tile read transposed in the slot order
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      const u32x4 pf = *reinterpret_cast<const u32x4*>(pw + (qt * 16 + li) * AKT + lg * 8);
+    for (int dt = 0; dt < DT; ++dt) {
+      const u32x4 vf = tr_rows8(kt + xa + dt * 16, kt + xa + 16 * D + dt * 16);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const u32x4 vf = tr_rows8(kt + xa + dt * 16, kt + xa + 4 * D + dt * 16);
-        o[qt][dt] = mfma16x16x32(pf, vf, o[qt][dt]);
-      }
+      for (int qt = 0; qt < 2; ++qt) o[qt][dt] = mfma16x16x32(vf, pf[qt], o[qt][dt]);
     }
   };
   for (int t0 = 0; t0 < T; t0 += 4) {
@@ -219,17 +209,21 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
     }
   }
 
-  // A = O / l into columns D .. 2D-1 of C; H_w rows into columns 0 .. D-1
+  // A = O / l into columns D .. 2D-1 of C (8-byte stores); H_w rows into columns 0 .. D-1
   uint16_t* cb = p.c + b * (int64_t)n * (2 * D);
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
+    float l = lrow[qt];
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    const float inv = 1.0f / l;
+    const int q = q0 + qt * 16 + li;
+    if (q < n) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int q = q0 + qt * 16 + 4 * lg + r;
-      if (q < n) {
-        const float inv = 1.0f / lrow[qt][r];
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) cb[(int64_t)q * (2 * D) + D + dt * 16 + li] = (uint16_t)f32_to_bf16(o[qt][dt][r] * inv);
+      for (int dt = 0; dt < DT; ++dt) {
+        const f32x4 v = o[qt][dt];
+        *reinterpret_cast<u32x2*>(cb + (int64_t)q * (2 * D) + D + dt * 16 + 4 * lg) =
+            u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
       }
     }
   }
