@@ -11,7 +11,8 @@
 //   A = softmax(H_w H_s^T / sqrt(d)) H_s,   C = [H_w, A]   (n x 2d)
 //
 // whale_attention_kernel: one workgroup of 4 waves per (example, 128
-// queries), 32 queries per wave.  Key tiles of 32 positions x d are DMA'd
+// queries), 32 queries per wave.  Key tiles of 32 positions x d (64 at d = 64,
+// 128 at d = 32) are DMA'd
 // (buffer_load ... lds) into a ring of 4 LDS slots, 3 tiles ahead; each tile
 // is read twice from LDS, as K (rows, for S^T = K Q^T) and as V (transposed
 // reads, for O^T += V^T P^T): the shared K = V is loaded once.  Both products
@@ -40,7 +41,9 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int AW = 4;    // waves per workgroup
 constexpr int AQ = 32;   // queries per wave (two 16-row tiles)
-constexpr int AKT = 32;  // sequence positions per step
+// 16-position key blocks per step: more at small d, where a step's products are short
+// and the per-step maxima, barrier and waits would otherwise dominate
+__host__ __device__ constexpr int attn_kb(int d) { return d <= 32 ? 8 : (d <= 64 ? 4 : 2); }
 
 constexpr int vm_enc(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14); }
 
@@ -67,12 +70,14 @@ struct AttnArgs {
 
 template <int D>
 __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p) {
+  constexpr int KB = attn_kb(D);            // 16-position key blocks per step
+  constexpr int AKT = 16 * KB;              // sequence positions per step
   constexpr int DC = D / 32;                // 32-wide chunks of the Q K^T contraction
   constexpr int DT = D / 16;                // 16-wide output column tiles
   constexpr int TILE = AKT * D;             // u16 per key tile
   constexpr int INS = TILE * 2 / 1024;      // 1 KB DMA instructions per tile
   constexpr int INS_HI = (INS + AW - 1) / AW, INS_LO = INS / AW, R = INS % AW;
-  static_assert(D % 32 == 0 && INS * 1024 == TILE * 2, "D must be a multiple of 32");
+  static_assert(D % 32 == 0 && INS * 1024 == TILE * 2 && KB % 2 == 0, "D must be a multiple of 32");
   __shared__ __align__(16) uint16_t s0[TILE], s1[TILE], s2[TILE], s3[TILE];
   uint16_t* const slot[4] = {s0, s1, s2, s3};  // indexed with compile-time numbers only
 
@@ -141,46 +146,50 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
     }
     lds_barrier();
     if (t + 3 < T) dma(next, t + 3);
-    // S^T = K Q^T: s[qt][kk][t] = S[query 16 qt + li][key 16 kk + 4 lg + t]
-    f32x4 sc[2][2];
+    // S^T = K Q^T: sc[qt][kk][t] = S[query 16 qt + li][key 16 kk + 4 lg + t]
+    f32x4 sc[2][KB];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) sc[qt][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kk = 0; kk < KB; ++kk) sc[qt][kk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
+      for (int kk = 0; kk < KB; ++kk) {
         const u32x4 kf = *reinterpret_cast<const u32x4*>(kt + (kk * 16 + li) * D + c * 32 + lg * 8);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) sc[qt][kk] = mfma16x16x32(kf, qf[qt][c], sc[qt][kk]);
       }
     }
-    // online softmax per query; P^T in bf16 as the B operand of V^T P^T, key slots
-    // 0..3 = keys 4 lg + t, 4..7 = keys 16 + 4 lg + t
-    u32x4 pf[2];
+    // online softmax per query; P^T in bf16 as the B operand of V^T P^T: in K step ks,
+    // key slots 0..3 = keys 32 ks + 4 lg + t, 4..7 = keys 32 ks + 16 + 4 lg + t
+    u32x4 pf[2][KB / 2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       if (t == T - 1) {  // only the last key tile can reach past L
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             if (t * AKT + kk * 16 + 4 * lg + r >= L) sc[qt][kk][r] = -INFINITY;
       }
-      float mx = fmaxf(fmaxf(fmaxf(sc[qt][0][0], sc[qt][0][1]), fmaxf(sc[qt][0][2], sc[qt][0][3])),
-                       fmaxf(fmaxf(sc[qt][1][0], sc[qt][1][1]), fmaxf(sc[qt][1][2], sc[qt][1][3])));
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk)
+        mx = fmaxf(mx, fmaxf(fmaxf(sc[qt][kk][0], sc[qt][kk][1]), fmaxf(sc[qt][kk][2], sc[qt][kk][3])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
       const float mnew = fmaxf(mrow[qt], mx * scale);
-      const float alpha = exp2f(mrow[qt] - mnew);
-      float e[2][4];
+      // v_exp_f32 directly: no denormal range handling (results below 2^-126 flush to 0,
+      // against a maximum term of 1); exp2(-inf) = 0 for the first step's alpha
+      const float alpha = __builtin_amdgcn_exp2f(mrow[qt] - mnew);
+      float e[KB][4];
       float sm = 0.f;
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < KB; ++kk)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          e[kk][r] = exp2f(fmaf(sc[qt][kk][r], scale, -mnew));
+          e[kk][r] = __builtin_amdgcn_exp2f(fmaf(sc[qt][kk][r], scale, -mnew));
           sm += e[kk][r];
         }
       lrow[qt] = fmaf(lrow[qt], alpha, sm);
@@ -190,16 +199,22 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
         for (int dt = 0; dt < DT; ++dt) o[qt][dt] *= alpha;
       }
       mrow[qt] = mnew;
-      pf[qt] = u32x4{pack_bf16x2(e[0][0], e[0][1]), pack_bf16x2(e[0][2], e[0][3]), pack_bf16x2(e[1][0], e[1][1]),
-                     pack_bf16x2(e[1][2], e[1][3])};
+#pragma unroll
+      for (int ks = 0; ks < KB / 2; ++ks)
+        pf[qt][ks] = u32x4{pack_bf16x2(e[2 * ks][0], e[2 * ks][1]), pack_bf16x2(e[2 * ks][2], e[2 * ks][3]),
+                           pack_bf16x2(e[2 * ks + 1][0], e[2 * ks + 1][1]),
+                           pack_bf16x2(e[2 * ks + 1][2], e[2 * ks + 1][3])};
     }
     // O^T += V^T P^T, V = the same key tile read transposed in the slot order
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const u32x4 vf = tr_rows8(kt + xa + dt * 16, kt + xa + 16 * D + dt * 16);
+    for (int ks = 0; ks < KB / 2; ++ks)
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) o[qt][dt] = mfma16x16x32(vf, pf[qt], o[qt][dt]);
-    }
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t* vk = kt + ks * 32 * D + xa + dt * 16;
+        const u32x4 vf = tr_rows8(vk, vk + 16 * D);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) o[qt][dt] = mfma16x16x32(vf, pf[qt][ks], o[qt][dt]);
+      }
   };
   for (int t0 = 0; t0 < T; t0 += 4) {
 #pragma unroll

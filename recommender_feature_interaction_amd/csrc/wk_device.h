@@ -66,11 +66,12 @@ __device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
 }
 
 // The shared-gate SwiGLU activation silu(v) * v = v^2 * logistic(v) with the
-// hardware exp2 and reciprocal (about 1 ulp each; the callers round the
-// result to bf16).  For v < -88, exp(-v) overflows to +inf and the reciprocal
-// gives 0, the value to bf16 precision.
+// hardware exp2 and reciprocal (v_exp_f32, v_rcp_f32: about 1 ulp each, no
+// denormal range handling; the callers round the result to bf16).  For
+// v < -88, exp(-v) overflows to +inf and the reciprocal gives 0, the value to
+// bf16 precision.
 __device__ __forceinline__ float silu_gate(float v) {
-  return v * v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+  return v * v * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(v * -1.44269504088896341f));
 }
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() is a
