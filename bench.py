@@ -380,9 +380,10 @@ def fusion_accounting(B, n, d, L, dff):
     """Algorithmic FLOPs and HBM bytes per launch of the fusion step's kernels (bf16)."""
     rows = B * n
     return {
-        # S = Q K^T and O = P V; H_s (K = V) read once, H_w read, C = [H_w, A] written
-        ("fusion_attention", 0, 0): {"flops": 4 * B * n * L * d, "bytes": (B * L * d + B * n * d + rows * 2 * d) * 2},
-        ("fusion_linear", 0, 0): {"flops": 2 * rows * 2 * d * d, "bytes": (rows * 2 * d + d * 2 * d + d + rows * d) * 2},
+        # S = Q K^T, O = P V and the Fusion Linear Q = [H_w, A] W_f^T + b_f in one kernel:
+        # H_s (K = V) read once, H_w read, W_f and b_f read, Q written
+        ("fusion_attention", 0, 0): {"flops": 4 * B * n * L * d + 2 * rows * 2 * d * d,
+                                     "bytes": (B * L * d + B * n * d + 2 * d * d + d + rows * d) * 2},
         ("fusion_ln", 0, 0): {"flops": 0, "bytes": 2 * rows * d * 2},
         ("fusion_linear", 0, 1): {"flops": 2 * rows * d * dff, "bytes": (rows * d + dff * d + dff + rows * dff) * 2},
         ("fusion_linear", 0, 2): {"flops": 2 * rows * dff * d,

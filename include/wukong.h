@@ -162,8 +162,8 @@ enum {
   WK_KERNEL_RESIDUAL_LN = 3, /* FMB rows of Y: LN(M + X)                     */
   WK_KERNEL_HEAD_LINEAR = 4,  /* one hidden Linear of the prediction head     */
   WK_KERNEL_HEAD_OUT = 5,     /* the head's last Linear + logistic function   */
-  WK_KERNEL_FUSION_ATTN = 6,  /* WHALE fusion: shared K = V cross-attention    */
-  WK_KERNEL_FUSION_LINEAR = 7, /* fusion Linear (index 0), SwiGLU up (1), down (2) */
+  WK_KERNEL_FUSION_ATTN = 6,  /* WHALE fusion: shared K = V cross-attention and the Fusion Linear */
+  WK_KERNEL_FUSION_LINEAR = 7, /* fusion, unfused FFN: SwiGLU up (index 1), down (2) */
   WK_KERNEL_FUSION_LN = 8,    /* fusion: the pre-norm LayerNorm               */
   WK_KERNEL_BWD_OUT = 9,      /* backward: output LayerNorm + LCB rows (dR)   */
   WK_KERNEL_BWD_TRANSPOSE = 10, /* backward: bf16 transpose of Linear t's output gradient
@@ -395,11 +395,12 @@ typedef struct {        /* device pointers, row-major, [out, in] weights        
 } wk_fusion_weights;
 
 /* Workspace bytes for wukong_fusion_forward, 0 for an invalid or unsupported
- * desc.  The workspace holds [H_w, A] ([batch, n, 2d], at offset 0) and Q
- * ([batch, n, d], at the next multiple of 256 bytes); when d_ff % 32 != 0 or
- * d_ff > 4096 the FFN runs as separate kernels and LN(Q) and silu(U) * U
- * follow.  Otherwise the LayerNorm, both FFN products and the residual are one
- * kernel that keeps silu(U) * U on chip. */
+ * desc.  The workspace holds Q ([batch, n, d], at offset 0), which the
+ * attention kernel writes (it applies the Fusion Linear to [H_w, A] on chip);
+ * when d_ff % 32 != 0 or d_ff > 4096 the FFN runs as separate kernels and
+ * LN(Q) and silu(U) * U follow at multiples of 256 bytes.  Otherwise the
+ * LayerNorm, both FFN products and the residual are one kernel that keeps
+ * silu(U) * U on chip. */
 size_t wukong_fusion_workspace_size(const wk_fusion_desc* desc, int64_t batch);
 
 /* hf [batch, n, d] (device) from hw [batch, n, d] and hs [batch, L, d]

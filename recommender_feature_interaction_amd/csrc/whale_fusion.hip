@@ -28,6 +28,8 @@
 // to -inf.
 #include <math.h>
 
+#include <type_traits>
+
 #include "wk_device.h"
 #include "wk_kernels.h"
 
@@ -60,12 +62,14 @@ __device__ __forceinline__ u32x4 tr_rows8(const uint16_t* p0, const uint16_t* p1
 }
 
 struct AttnArgs {
-  const uint16_t* hw;  // [B, n, D]
-  const uint16_t* hs;  // [B, L, D]
-  uint16_t* c;         // [B, n, 2D]: H_w copied to columns 0..D-1, A to D..2D-1
+  const uint16_t* hw;   // [B, n, D]
+  const uint16_t* hs;   // [B, L, D]
+  const uint16_t* w_f;  // [D, 2D]: the Fusion MLP's Linear
+  const uint16_t* b_f;  // [D] or null
+  uint16_t* q;          // [B, n, D]: Q = [H_w, A] W_f^T + b_f
   int64_t batch;
   int n, L;
-  float scale_log2;    // log2(e) / sqrt(D)
+  float scale_log2;     // log2(e) / sqrt(D)
 };
 
 template <int D>
@@ -78,7 +82,12 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
   constexpr int INS = TILE * 2 / 1024;      // 1 KB DMA instructions per tile
   constexpr int INS_HI = (INS + AW - 1) / AW, INS_LO = INS / AW, R = INS % AW;
   static_assert(D % 32 == 0 && INS * 1024 == TILE * 2 && KB % 2 == 0, "D must be a multiple of 32");
+  // the ring continues past the key tiles with W_f: a W_f step holds AKT / 2 of its rows
+  // (all 2D columns, TILE u16 like a key tile), i.e. JPS 16-row output blocks of Q
+  constexpr int NJ = D / 16, JPS = AKT / 32, NWS = (NJ + JPS - 1) / JPS;
+  constexpr int WU = D / 4;                 // 16-byte units of a W_f row
   __shared__ __align__(16) uint16_t s0[TILE], s1[TILE], s2[TILE], s3[TILE];
+  __shared__ __align__(16) uint16_t sbf[D];
   uint16_t* const slot[4] = {s0, s1, s2, s3};  // indexed with compile-time numbers only
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -89,17 +98,33 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
   const int64_t b = blockIdx.x / qchunks;
   const int q0 = (int)(blockIdx.x - b * qchunks) * (AW * AQ) + wave * AQ;
   const int T = (L + AKT - 1) / AKT;
+  const int TT = T + NWS;  // steps: key tiles, then W_f
   const float scale = p.scale_log2;
+  for (int i = tid; i < D; i += AW * 64) sbf[i] = p.b_f ? p.b_f[i] : (uint16_t)0;
 
   const __amdgpu_buffer_rsrc_t rk =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.hs + b * (int64_t)L * D), (short)0, L * D * 2, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rwf =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.w_f, (short)0, 4 * D * D, 0x00020000);
   auto dma = [&](uint16_t* dst, int step) {
+    if (step < T) {  // key tile: contiguous
 #pragma unroll
-    for (int q = 0; q < INS_HI; ++q) {
-      const int i = wave + q * AW;  // wave-uniform
-      if (i < INS) {
-        const uint32_t vo = (uint32_t)step * (TILE * 2) + (uint32_t)(i * 1024 + lane * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, WF_LDSV(dst + i * 512), 16, vo, 0, 0, 0);
+      for (int q = 0; q < INS_HI; ++q) {
+        const int i = wave + q * AW;  // wave-uniform
+        if (i < INS) {
+          const uint32_t vo = (uint32_t)step * (TILE * 2) + (uint32_t)(i * 1024 + lane * 16);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, WF_LDSV(dst + i * 512), 16, vo, 0, 0, 0);
+        }
+      }
+    } else {  // W_f rows, 16-byte unit u of row r at LDS unit u ^ (r % 8); rows past D read zero
+#pragma unroll
+      for (int q = 0; q < INS_HI; ++q) {
+        const int i = wave + q * AW;
+        if (i < INS) {
+          const int pos = i * 64 + lane, r = pos / WU, pu = pos - r * WU;
+          const uint32_t vo = (uint32_t)(((step - T) * (AKT / 2) + r) * (4 * D) + (pu ^ (r & 7)) * 16);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rwf, WF_LDSV(dst + i * 512), 16, vo, 0, 0, 0);
+        }
       }
     }
   };
@@ -117,7 +142,7 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
 
 #pragma unroll
   for (int u = 0; u < 3; ++u)
-    if (u < T) dma(slot[u], u);
+    if (u < TT) dma(slot[u], u);
 
   // O^T: o[qt][dt][t] = O[query q0 + 16 qt + li][column 16 dt + 4 lg + t]; per query
   // (qt) the running maximum (scaled, base 2) and this lane's part of the sum
@@ -133,8 +158,9 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
   // V^T operand lanes: key rows 4 lg + li / 4 (and 16 further), column 4 (li % 4)
   const int xa = (4 * lg + (li >> 2)) * D + 4 * (li & 3);
 
-  auto step = [&](const uint16_t* kt, uint16_t* next, int t) {
-    const int newer = (T - 1 - t < 2) ? T - 1 - t : 2;  // DMA steps issued after step t
+  // step t's copies landed (up to two newer steps may be in flight), for every wave
+  auto step_begin = [&](uint16_t* next, int t) {
+    const int newer = (TT - 1 - t < 2) ? TT - 1 - t : 2;  // DMA steps issued after step t
     if (newer <= 0) {
       __builtin_amdgcn_s_waitcnt(vm_enc(0));
     } else if (newer == 1) {
@@ -145,7 +171,10 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
       else __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_LO));
     }
     lds_barrier();
-    if (t + 3 < T) dma(next, t + 3);
+    if (t + 3 < TT) dma(next, t + 3);
+  };
+  auto step = [&](const uint16_t* kt, uint16_t* next, int t) {
+    step_begin(next, t);
     // S^T = K Q^T: sc[qt][kk][t] = S[query 16 qt + li][key 16 kk + 4 lg + t]
     f32x4 sc[2][KB];
 #pragma unroll
@@ -216,6 +245,51 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
         for (int qt = 0; qt < 2; ++qt) o[qt][dt] = mfma16x16x32(vf, pf[qt][ks], o[qt][dt]);
       }
   };
+  // The Fusion MLP's Linear on [H_w, A]: Q^T = W_f [H_w, A]^T + b_f, with the C^T
+  // operand in registers: H_w as loaded (qf), A = O / l rounded to bf16 in the
+  // slot order of O^T (K step ks: columns 32 ks + 4 lg + t, then 32 ks + 16 + 4 lg + t),
+  // which the W_f reads of A's half follow (two 8-byte pieces).
+  u32x4 aop[2][DC];
+  auto wf_step = [&](const uint16_t* wt, uint16_t* next, int t) {
+    step_begin(next, t);
+    const int w = t - T;
+#pragma unroll
+    for (int jj = 0; jj < JPS; ++jj) {
+      const int jb = w * JPS + jj;
+      if (jb < NJ) {  // uniform
+        const int r = jj * 16 + li;  // W_f row 16 jb + li within the step
+        const uint16_t* wr = wt + r * (2 * D);
+        const int sw = r & 7;
+        const u32x2 bb = *reinterpret_cast<const u32x2*>(sbf + jb * 16 + lg * 4);
+        f32x4 qa[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) qa[qt] = f32x4{bf16lo(bb[0]), bf16hi(bb[0]), bf16lo(bb[1]), bf16hi(bb[1])};
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks) {  // H_w half: columns 32 ks + 8 lg ..
+          const u32x4 a = *reinterpret_cast<const u32x4*>(wr + (((ks * 4 + lg) ^ sw) * 8));
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) qa[qt] = mfma16x16x32(a, qf[qt][ks], qa[qt]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < DC; ++ks) {  // A half: columns D + 32 ks + 4 lg .. and D + 32 ks + 16 + 4 lg ..
+          const int u0 = D / 8 + ks * 4 + (lg >> 1), h = (lg & 1) * 4;
+          const u32x2 a0 = *reinterpret_cast<const u32x2*>(wr + ((u0 ^ sw) * 8) + h);
+          const u32x2 a1 = *reinterpret_cast<const u32x2*>(wr + (((u0 + 2) ^ sw) * 8) + h);
+          const u32x4 a = u32x4{a0[0], a0[1], a1[0], a1[1]};
+#pragma unroll
+          for (int qt = 0; qt < 2; ++qt) qa[qt] = mfma16x16x32(a, aop[qt][ks], qa[qt]);
+        }
+        // Q[query 16 qt + li][16 jb + 4 lg + t]
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const int q = q0 + qt * 16 + li;
+          if (q < n)
+            *reinterpret_cast<u32x2*>(p.q + (b * n + q) * D + jb * 16 + lg * 4) =
+                u32x2{pack_bf16x2(qa[qt][0], qa[qt][1]), pack_bf16x2(qa[qt][2], qa[qt][3])};
+        }
+      }
+    }
+  };
   for (int t0 = 0; t0 < T; t0 += 4) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {  // unrolled: every slot is a known object at each step
@@ -223,31 +297,37 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
       step(slot[u], slot[(u + 3) & 3], t0 + u);
     }
   }
-
-  // A = O / l into columns D .. 2D-1 of C (8-byte stores); H_w rows into columns 0 .. D-1
-  uint16_t* cb = p.c + b * (int64_t)n * (2 * D);
+  // A from O^T and the row sums (O is dead after this)
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt) {
     float l = lrow[qt];
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     const float inv = 1.0f / l;
-    const int q = q0 + qt * 16 + li;
-    if (q < n) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const f32x4 v = o[qt][dt];
-        *reinterpret_cast<u32x2*>(cb + (int64_t)q * (2 * D) + D + dt * 16 + 4 * lg) =
-            u32x2{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv)};
-      }
+    for (int ks = 0; ks < DC; ++ks) {
+      const f32x4 v0 = o[qt][2 * ks], v1 = o[qt][2 * ks + 1];
+      aop[qt][ks] = u32x4{pack_bf16x2(v0[0] * inv, v0[1] * inv), pack_bf16x2(v0[2] * inv, v0[3] * inv),
+                          pack_bf16x2(v1[0] * inv, v1[1] * inv), pack_bf16x2(v1[2] * inv, v1[3] * inv)};
     }
   }
-  for (int i = lane; i < AQ * (D / 8); i += 64) {
-    const int r = i / (D / 8), cc = i - r * (D / 8);
-    const int q = q0 + r;
-    if (q < n)
-      *reinterpret_cast<u32x4*>(cb + (int64_t)q * (2 * D) + cc * 8) =
-          *reinterpret_cast<const u32x4*>(p.hw + (b * n + q) * D + cc * 8);
+  // the W_f steps T .. TT - 1 continue the ring: step t in slot t % 4, the phase T % 4 a
+  // compile-time constant in each branch
+  auto wf_loop = [&](auto phase) {
+    constexpr int P = decltype(phase)::value;
+    for (int t0 = T; t0 < TT; t0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t0 + u >= TT) break;
+        wf_step(slot[(P + u) & 3], slot[(P + u + 3) & 3], t0 + u);
+      }
+    }
+  };
+  switch (T & 3) {
+    case 0: wf_loop(std::integral_constant<int, 0>{}); break;
+    case 1: wf_loop(std::integral_constant<int, 1>{}); break;
+    case 2: wf_loop(std::integral_constant<int, 2>{}); break;
+    default: wf_loop(std::integral_constant<int, 3>{}); break;
   }
 }
 
@@ -562,13 +642,15 @@ bool whale_attention_supported(int n, int d, int L) {
          (int64_t)L * d * 2 < ((int64_t)1 << 31);
 }
 
-hipError_t launch_whale_attention(const void* hw, const void* hs, void* c, int64_t batch, int n, int d, int L,
-                                  hipStream_t stream, int64_t* workgroups) {
-  if (!whale_attention_supported(n, d, L)) return hipErrorInvalidValue;
+hipError_t launch_whale_attention(const void* hw, const void* hs, const void* w_f, const void* b_f, void* q,
+                                  int64_t batch, int n, int d, int L, hipStream_t stream, int64_t* workgroups) {
+  if (!whale_attention_supported(n, d, L) || w_f == nullptr) return hipErrorInvalidValue;
   AttnArgs a;
   a.hw = static_cast<const uint16_t*>(hw);
   a.hs = static_cast<const uint16_t*>(hs);
-  a.c = static_cast<uint16_t*>(c);
+  a.w_f = static_cast<const uint16_t*>(w_f);
+  a.b_f = static_cast<const uint16_t*>(b_f);
+  a.q = static_cast<uint16_t*>(q);
   a.batch = batch;
   a.n = n;
   a.L = L;

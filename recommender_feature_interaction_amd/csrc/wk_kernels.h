@@ -29,12 +29,13 @@ bool fmb_lcb_stream_supported(int n, int d, int k, int n_l);
 hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups);
-// WHALE fusion step (whale_fusion.hip): shared K = V cross-attention writing
-// C = [H_w, A] ([B, n, 2d] bf16), n % 16 == 0, d in {32, 64, 96, 128, 160};
-// and a row LayerNorm (d % 8 == 0, d <= 512).
+// WHALE fusion step (whale_fusion.hip): shared K = V cross-attention followed
+// by the Fusion MLP's Linear, writing Q = [H_w, A] W_f^T + b_f ([B, n, d] bf16),
+// n % 16 == 0, d in {32, 64, 96, 128, 160}; and a row LayerNorm (d % 8 == 0,
+// d <= 512).
 bool whale_attention_supported(int n, int d, int L);
-hipError_t launch_whale_attention(const void* hw, const void* hs, void* c, int64_t batch, int n, int d, int L,
-                                  hipStream_t stream, int64_t* workgroups);
+hipError_t launch_whale_attention(const void* hw, const void* hs, const void* w_f, const void* b_f, void* q,
+                                  int64_t batch, int n, int d, int L, hipStream_t stream, int64_t* workgroups);
 hipError_t launch_row_ln_bf16(const void* x, void* y, int64_t rows, int d, const void* gamma, const void* beta,
                               float eps, hipStream_t stream, int64_t* workgroups);
 // The fusion step's FFN as one kernel: out = q + (silu(U) * U) w_down^T + b_down,

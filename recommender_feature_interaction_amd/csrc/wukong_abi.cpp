@@ -441,7 +441,8 @@ int32_t head_forward(const wk_head_desc* d, const wk_head_weights* w, int64_t ba
   return launch(WK_KERNEL_HEAD_OUT, 0, 0, [&](int64_t* g) { return wk::launch_head_out(o, bf, launch.stream, g); });
 }
 
-// ---- WHALE fusion step: attention, three Linears on the MLP GEMMs, one row LayerNorm.
+// ---- WHALE fusion step: attention with the Fusion Linear in the same kernel, then the
+// FFN as one kernel (or, for d_ff % 32 != 0, a row LayerNorm and two Linears on the MLP GEMMs).
 int32_t check_fusion_desc(const wk_fusion_desc* d) {
   if (!d || d->n <= 0 || d->d <= 0 || d->L <= 0 || d->d_ff <= 0) return WK_ERR_INVALID_ARG;
   if (!(d->ln_eps >= 0.0f) || !std::isfinite(d->ln_eps)) return WK_ERR_INVALID_ARG;
@@ -452,7 +453,7 @@ int32_t check_fusion_desc(const wk_fusion_desc* d) {
 }
 
 struct FusionPlan {
-  size_t c = 0, q = 0, qn = 0, g = 0, bytes = 0;
+  size_t q = 0, qn = 0, g = 0, bytes = 0;
   bool fused_ffn = false;  // LayerNorm + FFN + residual as one kernel: no LN(Q) or G buffers
 };
 
@@ -460,8 +461,7 @@ FusionPlan plan_fusion(const wk_fusion_desc& d, int64_t batch) {
   FusionPlan p;
   const size_t rows = (size_t)batch * d.n;
   p.fused_ffn = wk::fusion_ffn_supported(d.d, d.d_ff);
-  p.c = 0;
-  p.q = p.c + align_up(rows * 2 * d.d * 2);
+  p.q = 0;
   p.bytes = p.q + align_up(rows * d.d * 2);
   if (!p.fused_ffn) {
     p.qn = p.bytes;
@@ -492,14 +492,13 @@ int32_t fusion_forward(const wk_fusion_desc* d, const wk_fusion_weights* w, int6
     return WK_ERR_INVALID_ARG;
 
   char* base = static_cast<char*>(ws);
-  void* c = base + fp.c;
   void* q = base + fp.q;
   void* qn = base + fp.qn;
   void* g = base + fp.g;
   const int64_t rows = batch * d->n;
   Launch launch{trace, static_cast<hipStream_t>(stream)};
   st = launch(WK_KERNEL_FUSION_ATTN, 0, 0, [&](int64_t* wg) {
-    return wk::launch_whale_attention(hw, hs, c, batch, d->n, d->d, d->L, launch.stream, wg);
+    return wk::launch_whale_attention(hw, hs, w->w_f, w->b_f, q, batch, d->n, d->d, d->L, launch.stream, wg);
   });
   if (st != WK_OK) return st;
   auto linear = [&](int index, const void* a, const void* wt, const void* bias, void* out, int N, int K, int act_kind,
@@ -517,8 +516,6 @@ int32_t fusion_forward(const wk_fusion_desc* d, const wk_fusion_weights* w, int6
     return launch(WK_KERNEL_FUSION_LINEAR, 0, index,
                   [&](int64_t* wg) { return wk::launch_linear_bf16(la, launch.stream, wg); });
   };
-  st = linear(0, c, w->w_f, w->b_f, q, d->d, 2 * d->d, wk::kActNone, nullptr);
-  if (st != WK_OK) return st;
   if (fp.fused_ffn) {
     wk::FusionFfnArgs fa;
     fa.q = q;

@@ -210,13 +210,13 @@ def test_fusion_workspace_and_argument_errors():
     spec = wk.FusionSpec(128, 160, 1024, 640)
     B = 7
     rows = B * 128
-    # d_ff % 32 == 0: LN, FFN and residual are one kernel, so only [H_w, A] and Q live in the workspace
-    assert wk.fusion_workspace_size(spec, B) == al(rows * 320 * 2) + al(rows * 160 * 2)
+    # d_ff % 32 == 0: LN, FFN and residual are one kernel, so only Q lives in the workspace
+    assert wk.fusion_workspace_size(spec, B) == al(rows * 160 * 2)
     # otherwise LN(Q) and silu(U) * U follow
     assert wk.fusion_workspace_size(wk.FusionSpec(128, 160, 1024, 200), B) == \
-        al(rows * 320 * 2) + 2 * al(rows * 160 * 2) + al(rows * 200 * 2)
+        2 * al(rows * 160 * 2) + al(rows * 200 * 2)
     assert wk.fusion_workspace_size(wk.FusionSpec(128, 160, 1024, 4128), B) == \
-        al(rows * 320 * 2) + 2 * al(rows * 160 * 2) + al(rows * 4128 * 2)
+        2 * al(rows * 160 * 2) + al(rows * 4128 * 2)
     assert wk.fusion_workspace_size(wk.FusionSpec(120, 160, 1024, 640), B) == 0   # n % 16
     assert wk.fusion_workspace_size(wk.FusionSpec(128, 48, 1024, 640), B) == 0    # d not a compiled width
     assert wk.fusion_workspace_size(wk.FusionSpec(128, 160, 0, 640), B) == 0      # L >= 1

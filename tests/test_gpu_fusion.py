@@ -29,10 +29,6 @@ def _gpu():
     wk.load_library()
 
 
-def _al(v):
-    return (v + 255) // 256 * 256
-
-
 class FusionRun:
     def __init__(self, B, n, d, L, dff, seed, affine="random", hw_scale=1.0):
         self.spec = wk.FusionSpec(n, d, L, dff)
@@ -77,15 +73,9 @@ def test_fusion_parity_and_intermediates(B, n, d, L, dff):
     log(f"fusion B={B} n={n} d={d} L={L} d_ff={dff}")
     check("H_f", hf, ref, "bf16")
     rows = B * n
-    c = host_f64(to_host(wst[:rows * 2 * d * 2].view(torch.bfloat16))).reshape(B, n, 2 * d)
-    assert np.array_equal(c[..., :d], host_f64(r.hw)), "C's left half is H_w"
-    check("A", c[..., d:], it["A"], "bf16")
-    q_off = _al(rows * 2 * d * 2)
-    q = host_f64(to_host(wst[q_off:q_off + rows * d * 2].view(torch.bfloat16))).reshape(B, n, d)
+    # Q = [H_w, A] W_f^T + b_f, written by the attention kernel at the start of the workspace
+    q = host_f64(to_host(wst[:rows * d * 2].view(torch.bfloat16))).reshape(B, n, d)
     check("Q", q, it["Q"], "bf16")
-    if L == 1:
-        assert np.array_equal(c[..., d:], np.broadcast_to(host_f64(r.hs)[:, :1, :], (B, n, d))), \
-            "one position: A is that position's row"
 
 
 def test_fusion_sharp_softmax_and_identity_affine():
@@ -94,9 +84,8 @@ def test_fusion_sharp_softmax_and_identity_affine():
     check("H_f (sharp attention)", host_f64(to_host(r.forward())), r.oracle(), "bf16")
 
 
-FUSED_KINDS = [("fusion_attention", 0), ("fusion_linear", 0), ("fusion_ffn", 0)]
-UNFUSED_KINDS = [("fusion_attention", 0), ("fusion_linear", 0), ("fusion_ln", 0), ("fusion_linear", 1),
-                 ("fusion_linear", 2)]
+FUSED_KINDS = [("fusion_attention", 0), ("fusion_ffn", 0)]
+UNFUSED_KINDS = [("fusion_attention", 0), ("fusion_ln", 0), ("fusion_linear", 1), ("fusion_linear", 2)]
 
 
 @pytest.mark.parametrize("dff,kinds", [(640, FUSED_KINDS), (200, UNFUSED_KINDS)], ids=["fused_ffn", "unfused_ffn"])
