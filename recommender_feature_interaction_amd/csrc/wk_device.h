@@ -57,6 +57,26 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Sum over aligned groups of G consecutive lanes (G a power of two <= 64):
+// within a 16-lane row on the VALU with DPP (quad_perm for lanes l ^ 1 and
+// l ^ 2, row_half_mirror and row_mirror to join the quads and then the two
+// halves of the row), across rows with shuffles.  Every lane of a group ends
+// with the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
+}
+template <int G>
+__device__ __forceinline__ float group_sum_v(float v) {
+  if constexpr (G >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  if constexpr (G >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  if constexpr (G >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (G >= 16) v += dpp_f<0x140>(v); // row_mirror
+  if constexpr (G >= 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (G >= 64) v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
 // Select 16-bit halves of two dwords (v_perm_b32): lo16(a) | lo16(b) << 16 ...
 __device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_perm(b, a, 0x05040100u);

@@ -390,14 +390,14 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
       float s = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s += R[e];
-      const float mean = group_sum<G>(s) * inv_d;
+      const float mean = group_sum_v<G>(s) * inv_d;
       float v = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float t = col_ok ? R[e] - mean : 0.f;
         v += t * t;
       }
-      const float rstd = rsqrtf(group_sum<G>(v) * inv_d + p.eps);
+      const float rstd = rsqrtf(group_sum_v<G>(v) * inv_d + p.eps);
       float s1 = 0.f, s2 = 0.f, rh[8], g[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(BT) void bwd_out_kernel(BwdOutKArgs p) {
         s1 += g[e];
         s2 += g[e] * rh[e];
       }
-      const float m1 = group_sum<G>(s1) * inv_d, m2 = group_sum<G>(s2) * inv_d;
+      const float m1 = group_sum_v<G>(s1) * inv_d, m2 = group_sum_v<G>(s2) * inv_d;
       if (col_ok) {
         u32x4 o;
 #pragma unroll
