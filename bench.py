@@ -165,14 +165,13 @@ def backward_accounting(B, s):
     kernels (recomputed products included: they are work the kernels do)."""
     n, d, k, n_f, n_l = s.n, s.d, s.k, s.n_f, s.n_l
     Bp = (B + 63) // 64 * 64
-    T = len(s.mlp) - 1
     out = {
         # X, M, dY in; dR (dM and dLc) out; W_L once.  Lc = W_L X recomputed.
         ("bwd_out", 0, 0): {"flops": B * 2 * n_l * n * d, "bytes": B * (3 * n * d + n_f * d) * 2 + n_l * n * 2},
         # X, d_Fn, dR in; dX out; [Phi; W_L] once.  Z, F recomputed; dZ, dX, d_Phi, d_W_L.
         ("bwd_fmb", 0, 0): {"flops": B * (2 * k * n * d * 4 + 2 * n * d * (2 * k + n_l) + 2 * n_l * n * d),
                             "bytes": B * (3 * n * d + n * k) * 2 + (k + n_l) * n * 2},
-        ("bwd_reduce", 0, 0): {"flops": 0, "bytes": 0}, ("bwd_reduce", 0, 1): {"flops": 0, "bytes": 0},
+        ("bwd_reduce", 0, 0): {"flops": 0, "bytes": 0},  # the output LN's and the FMB / LCB weight sums
     }
     for t, (a, b) in enumerate(zip(s.mlp[:-1], s.mlp[1:])):
         out[("bwd_transpose", 0, 3 * t)] = {"flops": 0, "bytes": (B * b + Bp * b) * 2}
@@ -182,8 +181,6 @@ def backward_accounting(B, s):
         out[("bwd_dgrad", 0, t)] = {"flops": 2 * B * b * a,
                                     "bytes": (B * b + a * b + B * a + (B * a if t > 0 else 0)) * 2}
         out[("bwd_reduce", 0, 2 + t)] = {"flops": 0, "bytes": 0}
-    for i in range(4):
-        out[("bwd_reduce", 0, 2 + T + i)] = {"flops": 0, "bytes": 0}
     return out
 
 

@@ -171,9 +171,9 @@ enum {
   WK_KERNEL_BWD_WGRAD = 11,   /* backward: dW_t (index t)                     */
   WK_KERNEL_BWD_DGRAD = 12,   /* backward: gradient of the Linear's input (t) */
   WK_KERNEL_BWD_FMB = 13,     /* backward: FM LayerNorm, interaction, dX      */
-  WK_KERNEL_BWD_REDUCE = 14,  /* backward: per-workgroup / per-split sums: index 0, 1
-                                 gamma_out, beta_out; 2 + t the bias of Linear t;
-                                 2 + T + 0..3 Phi, W_L, gamma_fm, beta_fm */
+  WK_KERNEL_BWD_REDUCE = 14,  /* backward: per-workgroup / per-split sums: index 0
+                                 gamma_out, beta_out, Phi, W_L, gamma_fm, beta_fm (one
+                                 launch); 2 + t the bias of Linear t */
   WK_KERNEL_FUSION_FFN = 15   /* fusion: pre-norm LayerNorm + SwiGLU FFN + residual in one kernel */
 };
 typedef struct wk_trace wk_trace;

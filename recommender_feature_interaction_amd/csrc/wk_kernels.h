@@ -123,6 +123,18 @@ hipError_t launch_sum_planes(const float* part, int planes, int64_t len, float* 
 // out[j] = sum over p of part[p * stride + j], j < len <= stride.
 hipError_t launch_sum_planes_strided(const float* part, int planes, int64_t stride, int64_t len, float* out,
                                      hipStream_t stream);
+// Up to kMaxPlaneSegs such sums over the same number of planes in one launch;
+// segments with a null out are skipped.  Each column adds planes q = s, s + 8, ..
+// for slices s = 0 .. 7, then the slices in order (with at most 8 planes this is
+// plane order).
+struct PlaneSeg {
+  const float* part;
+  float* out;
+  int64_t stride, len;
+};
+constexpr int kMaxPlaneSegs = 8;
+hipError_t launch_sum_planes_multi(const PlaneSeg* segs, int nseg, int planes, hipStream_t stream,
+                                   int64_t* workgroups);
 
 // The last Linear with the FMB rows' output stage fused in (bf16):
 // Y[b, r] = LN_d(bf16(A[b] W^T + bias)[r d .. r d + d) + X[b, r]) for r < n_f,

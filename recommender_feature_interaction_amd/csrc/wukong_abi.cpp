@@ -743,21 +743,7 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   oa.eps = d->ln_eps;
   st = launch(WK_KERNEL_BWD_OUT, layer_idx, 0, [&](int64_t* g) { return wk::launch_bwd_out(oa, s, g); });
   if (st != WK_OK) return st;
-  const int64_t po = (int64_t)wk::wukong_bwd_out_part_floats(d->d);
-  if (gr->out_ln_gamma) {
-    st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 0, [&](int64_t* g) {
-      *g = 1;
-      return wk::launch_sum_planes_strided(part_out, wg, po, d->d, gr->out_ln_gamma, s);
-    });
-    if (st != WK_OK) return st;
-  }
-  if (gr->out_ln_beta) {
-    st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 1, [&](int64_t* g) {
-      *g = 1;
-      return wk::launch_sum_planes_strided(part_out + d->d, wg, po, d->d, gr->out_ln_beta, s);
-    });
-    if (st != WK_OK) return st;
-  }
+  const int64_t po = (int64_t)wk::wukong_bwd_out_part_floats(d->d);  // summed with the FMB planes at the end
 
   // MLP, last Linear first: g_{t+1} -> dW_t, db_t, g_t
   const void* g_next = dm;
@@ -837,21 +823,17 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   fa.eps = d->ln_eps;
   st = launch(WK_KERNEL_BWD_FMB, layer_idx, 0, [&](int64_t* g) { return wk::launch_bwd_fmb(fa, s, g); });
   if (st != WK_OK) return st;
+  // the output LayerNorm's gamma / beta and the FMB / LCB weight gradients: one launch of plane sums
   const int64_t pf = (int64_t)wk::wukong_bwd_fmb_part_floats(d->n, d->k, d->n_l);
   const int64_t kn = (int64_t)d->k * d->n, ln = (int64_t)d->n_l * d->n, nk = (int64_t)d->n * d->k;
-  struct Out {
-    float* dst;
-    int64_t off, len;
-  } outs[4] = {{gr->phi, 0, kn}, {gr->w_l, kn, ln}, {gr->fm_ln_gamma, kn + ln, nk}, {gr->fm_ln_beta, kn + ln + nk, nk}};
-  for (int i = 0; i < 4; ++i) {
-    if (!outs[i].dst) continue;
-    st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 2 + T + i, [&](int64_t* g) {
-      *g = 1;
-      return wk::launch_sum_planes_strided(part_fmb + outs[i].off, wg, pf, outs[i].len, outs[i].dst, s);
-    });
-    if (st != WK_OK) return st;
-  }
-  return WK_OK;
+  const wk::PlaneSeg segs[6] = {{part_out, gr->out_ln_gamma, po, d->d},
+                                {part_out + d->d, gr->out_ln_beta, po, d->d},
+                                {part_fmb, gr->phi, pf, kn},
+                                {part_fmb + kn, gr->w_l, pf, ln},
+                                {part_fmb + kn + ln, gr->fm_ln_gamma, pf, nk},
+                                {part_fmb + kn + ln + nk, gr->fm_ln_beta, pf, nk}};
+  return launch(WK_KERNEL_BWD_REDUCE, layer_idx, 0,
+                [&](int64_t* g) { return wk::launch_sum_planes_multi(segs, 6, wg, s, g); });
 }
 
 // ---- training a stack: per layer, its input (layers after the first) and its

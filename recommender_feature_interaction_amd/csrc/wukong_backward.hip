@@ -804,6 +804,35 @@ __global__ __launch_bounds__(256) void sum_many_planes_kernel(const float* part,
   }
 }
 
+// Several plane sums in one launch: segment i covers workgroups first[i] ..
+// first[i + 1] - 1, 32 columns each, summed exactly as sum_many_planes_kernel.
+struct PlaneSegsK {
+  PlaneSeg seg[kMaxPlaneSegs];
+  int64_t first[kMaxPlaneSegs + 1];
+  int nseg, planes;
+};
+__global__ __launch_bounds__(256) void sum_planes_multi_kernel(PlaneSegsK a) {
+  __shared__ float red[8][33];
+  int i = 0;
+  while (i + 1 < a.nseg && (int64_t)blockIdx.x >= a.first[i + 1]) ++i;  // uniform
+  const PlaneSeg sg = a.seg[i];
+  const int c = threadIdx.x & 31, sl = threadIdx.x >> 5;
+  const int64_t col = ((int64_t)blockIdx.x - a.first[i]) * 32 + c;
+  float v = 0.f;
+  if (col < sg.len) {
+#pragma unroll 4
+    for (int q = sl; q < a.planes; q += 8) v += sg.part[(int64_t)q * sg.stride + col];
+  }
+  red[sl][c] = v;
+  __syncthreads();
+  if (sl == 0 && col < sg.len) {
+    float t = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) t += red[k][c];
+    sg.out[col] = t;
+  }
+}
+
 int workgroups_for(int64_t batch) { return (int)(batch < 256 ? batch : 256); }
 
 // Lets a kernel take the whole 160 KB of LDS as dynamic shared memory (a host-side attribute, set per launch).
@@ -943,6 +972,29 @@ hipError_t launch_sum_planes_strided(const float* part, int planes, int64_t stri
   int64_t grid = (len + 255) / 256;
   if (grid > 2048) grid = 2048;
   hipLaunchKernelGGL(sum_planes_kernel, dim3((unsigned)grid), dim3(256), 0, stream, part, planes, stride, len, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_planes_multi(const PlaneSeg* segs, int nseg, int planes, hipStream_t stream,
+                                   int64_t* workgroups) {
+  if (nseg < 0 || nseg > kMaxPlaneSegs || planes < 1) return hipErrorInvalidValue;
+  PlaneSegsK a;
+  a.nseg = 0;
+  a.planes = planes;
+  int64_t blocks = 0;
+  for (int i = 0; i < nseg; ++i) {
+    if (segs[i].len < 0 || segs[i].stride < segs[i].len) return hipErrorInvalidValue;
+    if (segs[i].len == 0 || segs[i].out == nullptr) continue;
+    a.seg[a.nseg] = segs[i];
+    a.first[a.nseg] = blocks;
+    blocks += (segs[i].len + 31) / 32;
+    ++a.nseg;
+  }
+  a.first[a.nseg] = blocks;
+  if (workgroups) *workgroups = blocks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sum_planes_multi_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
