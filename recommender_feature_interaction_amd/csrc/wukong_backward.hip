@@ -85,7 +85,7 @@ __device__ __forceinline__ uint16_t to_bf16(float v) { return (uint16_t)f32_to_b
 // LDS-only barrier per call is enough: a slot is rewritten two calls later,
 // after every thread has passed the barrier of the call in between.
 __device__ __forceinline__ float block_sum(float v, float* red, int slot) {
-  v = xor_sum<1>(v);
+  v = group_sum_v<64>(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* r = red + slot * BW;
   if (lane == 0) r[wave] = v;
@@ -98,8 +98,8 @@ __device__ __forceinline__ float block_sum(float v, float* red, int slot) {
 
 // Two sums at once (red holds 2 slots of 2 BW floats).
 __device__ __forceinline__ void block_sum2(float& a, float& b, float* red, int slot) {
-  a = xor_sum<1>(a);
-  b = xor_sum<1>(b);
+  a = group_sum_v<64>(a);
+  b = group_sum_v<64>(b);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* r = red + slot * 2 * BW;
   if (lane == 0) {
