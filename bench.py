@@ -425,7 +425,8 @@ def measure_fusion(wk, ws, torch, cfg, y, stream, steps, warmup, seed):
     roof = None
     if dom is not None:
         roof = roofline_of(dom, acct[(dom["kernel"], dom["layer"], dom["index"])], dom["avg_ms"], cfg.dtype, cfg.name)
-    flops = sum(a["flops"] for a in acct.values())
+    # the kernels that ran (the accounting also lists the unfused FFN's)
+    flops = sum(acct[(k["kernel"], k["layer"], k["index"])]["flops"] for k in kernels)
     return {"n": n, "d": d, "L": L, "d_ff": dff, "ms_per_call": round(ms, 4),
             "examples_per_s": round(cfg.batch / ms * 1e3, 1), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
             "roofline": roof, "kernels": sorted(kernels, key=lambda k: (k["kernel"], k["index"]))}
