@@ -316,7 +316,9 @@ def measure_moe(wk, ws, torch, cfg, x, stream, steps, warmup, seed):
     trace.close()
     roof = None
     if dom is not None:
-        roof = roofline_of(dom, acct[(dom["kernel"], dom["layer"], dom["index"])], dom["avg_ms"], cfg.dtype, cfg.name)
+        # the experts' kernels share names with the layer's but not its shapes: no layer traffic file applies
+        roof = roofline_of(dom, acct[(dom["kernel"], dom["layer"], dom["index"])], dom["avg_ms"], cfg.dtype,
+                           f"{cfg.name}_moe")
     return {"experts": [{"k": k, "n_f": nf, "n_l": nl, "mlp": list(mlp)} for k, nf, nl, mlp in shapes],
             "ms_per_call": round(ms, 4), "examples_per_s": round(cfg.batch / ms * 1e3, 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "mfma_frac": round(flops / (ms * 1e-3) / 1e12 /
