@@ -269,7 +269,7 @@ __global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
         const int j = jt * 16 + lg * 4 + t;
         if (m < n && j < k) s += facc[mi][jt][t];
       }
-  s = xor_sum<1>(s);
+  s = group_sum_v<64>(s);
   if (lane == 0) red[wave] = s;
   lds_barrier();
   float tot = 0.f;
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(NW * 64) void fmb_lcb_bf16_kernel(FmbLcbArgs p) {
           q += dv * dv;
         }
       }
-  q = xor_sum<1>(q);
+  q = group_sum_v<64>(q);
   if (lane == 0) red[NW + wave] = q;
   lds_barrier();
   float qt = 0.f;
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
           const int j = jt * 16 + lg * 4 + t;
           if (m < n && j < k) sm += facc[mi][jt][t];
         }
-    sm = xor_sum<1>(sm);
+    sm = group_sum_v<64>(sm);
     if (lane == 0) red[wave] = sm;
     lds_barrier();
     float tot = 0.f;
@@ -640,7 +640,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fmb_lcb_resident_kernel(FmbLcbArgs
             q += dv * dv;
           }
         }
-    q = xor_sum<1>(q);
+    q = group_sum_v<64>(q);
     if (lane == 0) red[NW + wave] = q;
     lds_barrier();  // also: every wave is done reading Xs and Zs of this example
     float qt = 0.f;

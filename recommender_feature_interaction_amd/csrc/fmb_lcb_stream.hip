@@ -438,7 +438,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
             const int j = jt * 16 + lg * 4 + t;
             if (m < n && j < k) sm += facc[mi][jt][t];
           }
-      sm = xor_sum<1>(sm);
+      sm = group_sum_v<64>(sm);
       if (lane == 0) red[wave] = sm;
       lds_barrier();
       float tot = 0.f;
@@ -459,7 +459,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
               q += dv * dv;
             }
           }
-      q = xor_sum<1>(q);
+      q = group_sum_v<64>(q);
       if (lane == 0) red[NWAVE + wave] = q;
       lds_barrier();
       float qt = 0.f;

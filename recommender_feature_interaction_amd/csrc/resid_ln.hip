@@ -144,14 +144,14 @@ __global__ __launch_bounds__(256) void resid_ln_f32_kernel(const float* m, const
   float* yr = y + (b * n + r) * (int64_t)d;
   float s = 0.f;
   for (int e = lane; e < d; e += 64) s += mr[e] + xr[e];
-  s = xor_sum<1>(s);
+  s = group_sum_v<64>(s);
   const float mean = s / (float)d;
   float q = 0.f;
   for (int e = lane; e < d; e += 64) {
     const float dv = mr[e] + xr[e] - mean;
     q += dv * dv;
   }
-  q = xor_sum<1>(q);
+  q = group_sum_v<64>(q);
   const float rstd = rsqrtf(q / (float)d + eps);
   for (int e = lane; e < d; e += 64) {
     const float gm = gamma ? gamma[e] : 1.f, bt = beta ? beta[e] : 0.f;
