@@ -254,8 +254,12 @@ typedef struct {
                                     bf16 experts need d % 16 == 0                      */
 } wk_moe_desc;
 
-/* Workspace bytes for wukong_moe_layer_forward (the largest expert's layer
- * workspace), 0 if desc is invalid or unsupported. */
+/* Workspace bytes for wukong_moe_layer_forward, 0 if desc is invalid or
+ * unsupported: the largest expert's layer workspace, or, when every expert's
+ * last Linear carries the output LayerNorm (bf16, d in {16, 32, 80, 160}, its
+ * input width a multiple of 64), the sum of the experts' (their last Linears
+ * then run as grouped launches, recorded in a trace as layer = num_experts,
+ * index = group; four experts per launch). */
 size_t wukong_moe_layer_workspace_size(const wk_moe_desc* desc, int64_t batch);
 
 /* y [batch, n, d] from x [batch, n, d].  experts: host array of num_experts

@@ -400,8 +400,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
 // MOUT: the epilogue also stores M = bf16(A W^T + bias) (the training forward
 // keeps it for the backward): block j's values go out right after block j's
 // wait, so every later wait counts those NB stores as well.
+// One 256 x 320 tile (workgroup bid of nblk working on p) of the fused last Linear.
 template <int BM, int BN, int WGM, int WGN, int D, bool MOUT>
-__global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs p) {
+__device__ __forceinline__ void linear_ln_tile(const LinearLnKArgs& p, int bid, int nblk) {
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MB = WTM / 16, NB = WTN / 16;
   constexpr int GI = D / 16;    // 16-column blocks per embedding row
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
   const int l16 = lane & 15, lg = lane >> 4;
   int64_t m0;
   int n0;
-  tile_origin(p.tiles_m, p.tiles_n, BM, BN, m0, n0);
+  tile_origin_at(bid, nblk, p.tiles_m, p.tiles_n, BM, BN, m0, n0);
   const int64_t M = p.M;
   const int N = p.N;
   // epilogue constants staged before the main loop (whose first wait covers these loads), so the
@@ -548,6 +549,25 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs
       dma_res(j + 2, slot[j & 1]);
     }
   }
+}
+
+template <int BM, int BN, int WGM, int WGN, int D, bool MOUT>
+__global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_kernel(LinearLnKArgs p) {
+  linear_ln_tile<BM, BN, WGM, WGN, D, MOUT>(p, blockIdx.x, gridDim.x);
+}
+
+// Several fused last Linears of the same D in one launch (the experts of a
+// mixture): group i takes workgroups first[i] .. first[i + 1] - 1.
+struct LinearLnGroupKArgs {
+  LinearLnKArgs a[kMaxLnGroup];
+  int first[kMaxLnGroup + 1];
+  int n;
+};
+template <int BM, int BN, int WGM, int WGN, int D>
+__global__ __launch_bounds__(WGM * WGN * 64) void linear_ln_group_kernel(LinearLnGroupKArgs g) {
+  int i = 0;
+  while (i + 1 < g.n && (int)blockIdx.x >= g.first[i + 1]) ++i;  // uniform
+  linear_ln_tile<BM, BN, WGM, WGN, D, false>(g.a[i], (int)blockIdx.x - g.first[i], g.first[i + 1] - g.first[i]);
 }
 
 template <int BM, int BN, int WGM, int WGN>
@@ -749,9 +769,13 @@ struct LinearLnVariant {
   int d;
   void (*kernel)(LinearLnKArgs);
   void (*kernel_m)(LinearLnKArgs);  // also stores M
+  void (*group)(LinearLnGroupKArgs);
 };
-#define WK_LN_VARIANT(D) \
-  LinearLnVariant { D, linear_ln_kernel<256, 320, 4, 2, D, false>, linear_ln_kernel<256, 320, 4, 2, D, true> }
+#define WK_LN_VARIANT(D)                                                                                       \
+  LinearLnVariant {                                                                                            \
+    D, linear_ln_kernel<256, 320, 4, 2, D, false>, linear_ln_kernel<256, 320, 4, 2, D, true>,                  \
+        linear_ln_group_kernel<256, 320, 4, 2, D>                                                              \
+  }
 const LinearLnVariant kLnVariants[] = {WK_LN_VARIANT(16), WK_LN_VARIANT(32), WK_LN_VARIANT(80),
                                        WK_LN_VARIANT(160)};
 constexpr int kLnBM = 256, kLnBN = 320, kLnThreads = 512;
@@ -766,6 +790,50 @@ const LinearLnVariant* pick_linear_ln(int d) {
 
 bool linear_ln_bf16_supported(int64_t M, int N, int K, int d) {
   return M > 0 && K > 0 && K % kBK == 0 && d > 0 && N % d == 0 && N > 0 && pick_linear_ln(d) != nullptr;
+}
+
+namespace {
+LinearLnKArgs ln_kargs(const LinearLnArgs& a) {
+  LinearLnKArgs k;
+  k.a = static_cast<const uint16_t*>(a.a);
+  k.w = static_cast<const uint16_t*>(a.w);
+  k.bias = static_cast<const uint16_t*>(a.bias);
+  k.x = static_cast<const uint16_t*>(a.x);
+  k.gamma = static_cast<const uint16_t*>(a.gamma);
+  k.beta = static_cast<const uint16_t*>(a.beta);
+  k.y = static_cast<uint16_t*>(a.y);
+  k.m_out = static_cast<uint16_t*>(a.m_out);
+  k.M = a.M;
+  k.N = a.N;
+  k.K = a.K;
+  k.ld = a.ld;
+  k.eps = a.eps;
+  k.tiles_m = (int)((a.M + kLnBM - 1) / kLnBM);
+  k.tiles_n = (a.N + kLnBN - 1) / kLnBN;
+  return k;
+}
+}  // namespace
+
+hipError_t launch_linear_ln_bf16_group(const LinearLnArgs* a, int n, hipStream_t stream, int64_t* workgroups) {
+  if (n < 1 || n > kMaxLnGroup) return hipErrorInvalidValue;
+  const LinearLnVariant* v = pick_linear_ln(a[0].d);
+  if (!v) return hipErrorInvalidValue;
+  LinearLnGroupKArgs g;
+  g.n = n;
+  int64_t blocks = 0;
+  for (int i = 0; i < n; ++i) {
+    if (a[i].d != a[0].d || a[i].m_out != nullptr || !linear_ln_bf16_supported(a[i].M, a[i].N, a[i].K, a[i].d))
+      return hipErrorInvalidValue;
+    g.a[i] = ln_kargs(a[i]);
+    g.first[i] = (int)blocks;
+    blocks += (int64_t)g.a[i].tiles_m * g.a[i].tiles_n;
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  }
+  g.first[n] = (int)blocks;
+  if (workgroups) *workgroups = blocks;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(v->group, dim3((unsigned)blocks), dim3(kLnThreads), 0, stream, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int64_t* workgroups) {

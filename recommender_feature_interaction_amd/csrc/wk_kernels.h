@@ -155,6 +155,10 @@ struct LinearLnArgs {
 };
 bool linear_ln_bf16_supported(int64_t M, int N, int K, int d);
 hipError_t launch_linear_ln_bf16(const LinearLnArgs& a, hipStream_t stream, int64_t* workgroups);
+// Up to kMaxLnGroup of them (same d, no m_out) as one launch: the tiles of all
+// groups fill the GPU together (the experts of a mixture, each with few tiles).
+constexpr int kMaxLnGroup = 4;
+hipError_t launch_linear_ln_bf16_group(const LinearLnArgs* a, int n, hipStream_t stream, int64_t* workgroups);
 
 // FMB rows of the layer output: Y[b, r] = LN_d(M[b, r] + X[b, r]) for r < n_f.
 struct ResidLnArgs {

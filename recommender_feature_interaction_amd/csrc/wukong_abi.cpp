@@ -17,6 +17,7 @@
 #include <cstring>
 #include <mutex>
 #include <new>
+#include <algorithm>
 #include <vector>
 
 #include "wk_kernels.h"
@@ -176,9 +177,11 @@ struct RowMap {
 };
 
 // Launches one layer; all arguments already checked.
+// With defer_last (fused last Linear only), the last Linear's arguments are
+// returned there instead of launched (the mixture launches its experts' together).
 int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t batch, const void* x,
                   void* y, char* scratch, const LayerPlan& plan, Launch& launch, int layer_idx,
-                  const RowMap* rows = nullptr) {
+                  const RowMap* rows = nullptr, wk::LinearLnArgs* defer_last = nullptr) {
   const bool bf = d.dtype == WK_BF16;
   char* fn = scratch + plan.fn;
   char* mbuf = scratch + plan.m;
@@ -263,6 +266,10 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.ld = (int64_t)d.n * d.d;
     a.eps = d.ln_eps;
     a.m_out = plan.keep_hidden ? static_cast<void*>(mbuf) : nullptr;  // the training forward keeps M
+    if (defer_last) {
+      *defer_last = a;
+      return WK_OK;
+    }
     return launch(WK_KERNEL_MLP_LINEAR, layer_idx, t,
                   [&](int64_t* g) { return wk::launch_linear_ln_bf16(a, launch.stream, g); });
   }
@@ -546,12 +553,22 @@ int32_t fusion_forward(const wk_fusion_desc* d, const wk_fusion_weights* w, int6
 // its share of the output rows (FMB rows of every expert first, then LCB rows).
 constexpr int kMaxExperts = 64;
 
+// Whether the experts' last Linears run as grouped launches: all of them
+// carry the output LayerNorm.  Each expert then keeps a workspace of its own
+// (its last hidden activation lives until the grouped launch).
+bool moe_grouped(const wk_moe_desc* m) {
+  if (m->num_experts < 2) return false;
+  for (int e = 0; e < m->num_experts; ++e)
+    if (!fuse_output_ln(m->experts[e])) return false;
+  return true;
+}
+
 int32_t check_moe(const wk_moe_desc* m, int64_t batch, size_t* bytes) {
   if (!m || !m->experts || m->num_experts < 1 || m->num_experts > kMaxExperts) return WK_ERR_INVALID_ARG;
   if (batch < 0 || batch > kMaxBatch) return WK_ERR_INVALID_ARG;
   const wk_layer_desc& e0 = m->experts[0];
   int64_t rows = 0;
-  size_t need = 0;
+  size_t need = 0, sum = 0;
   for (int e = 0; e < m->num_experts; ++e) {
     const wk_layer_desc& d = m->experts[e];
     const int32_t st = check_desc(&d, true);
@@ -560,8 +577,10 @@ int32_t check_moe(const wk_moe_desc* m, int64_t batch, size_t* bytes) {
     rows += (int64_t)d.n_f + d.n_l;
     const size_t b = plan_layer(d, batch).bytes;
     need = b > need ? b : need;
+    sum += align_up(b);
   }
   if (rows != e0.n) return WK_ERR_UNSUPPORTED;  // the residual needs n output rows
+  if (moe_grouped(m)) need = sum;
   if (bytes) *bytes = need ? need : kAlign;
   return WK_OK;
 }
@@ -589,14 +608,29 @@ int32_t moe_forward(const wk_moe_desc* m, const wk_layer_weights* weights, const
   int n_f_total = 0;
   for (int e = 0; e < m->num_experts; ++e) n_f_total += m->experts[e].n_f;
   Launch launch{trace, static_cast<hipStream_t>(stream)};
+  const bool grouped = moe_grouped(m);
+  std::vector<wk::LinearLnArgs> last(grouped ? m->num_experts : 0);
   int fmb_row = 0, lcb_row = n_f_total;
+  size_t off = 0;
   for (int e = 0; e < m->num_experts; ++e) {
     const wk_layer_desc& d = m->experts[e];
     const RowMap rm{fmb_row, lcb_row, out_gamma, out_beta};
-    st = run_layer(d, weights[e], batch, x, y, static_cast<char*>(ws), plan_layer(d, batch), launch, e, &rm);
+    const LayerPlan pl = plan_layer(d, batch);
+    st = run_layer(d, weights[e], batch, x, y, static_cast<char*>(ws) + off, pl, launch, e, &rm,
+                   grouped ? &last[e] : nullptr);
     if (st != WK_OK) return st;
+    if (grouped) off += align_up(pl.bytes);
     fmb_row += d.n_f;
     lcb_row += d.n_l;
+  }
+  // the experts' last Linears (with the output LayerNorm of their FMB rows), kMaxLnGroup per
+  // launch, recorded as layer num_experts
+  for (int c0 = 0; c0 < (int)last.size(); c0 += wk::kMaxLnGroup) {
+    const int cnt = std::min<int>(wk::kMaxLnGroup, (int)last.size() - c0);
+    st = launch(WK_KERNEL_MLP_LINEAR, m->num_experts, c0 / wk::kMaxLnGroup, [&](int64_t* g) {
+      return wk::launch_linear_ln_bf16_group(last.data() + c0, cnt, launch.stream, g);
+    });
+    if (st != WK_OK) return st;
   }
   return WK_OK;
 }

@@ -304,8 +304,14 @@ def test_moe_sizes_and_argument_errors():
     lib = wk.load_library()
     E = [wk.LayerSpec(128, 160, 32, 16, 16, (4096, 2048, 2560)) for _ in range(4)]
     B = 64
-    one = wk.layer_workspace_size(wk.LayerSpec(128, 160, 32, 16, 112, (4096, 2048, 2560)), B)
-    assert wk.moe_workspace_size(wk.MoeSpec(E), B) == one            # experts share one layer workspace
+    # every expert carries the output LayerNorm in its last Linear, so those run as one grouped launch
+    # and each expert keeps its own workspace (Fn [B, n k] and h_1 [B, 2048]) until then
+    al = lambda v: (v + 255) // 256 * 256
+    assert wk.moe_workspace_size(wk.MoeSpec(E), B) == 4 * (al(B * 4096 * 2) + al(B * 2048 * 2))
+    # otherwise (K % 64 != 0: residual LayerNorm kernel) the experts share the largest one
+    E2 = [wk.LayerSpec(128, 160, 32, 16, 16, (4096, 2016, 2560)) for _ in range(4)]
+    one = wk.layer_workspace_size(wk.LayerSpec(128, 160, 32, 16, 112, (4096, 2016, 2560)), B)
+    assert wk.moe_workspace_size(wk.MoeSpec(E2), B) == one
     assert wk.moe_workspace_size(wk.MoeSpec(E[:3]), B) == 0         # rows must add up to n
     bad_d = E[:3] + [wk.LayerSpec(128, 80, 32, 16, 16, (4096, 2048, 1280))]
     assert wk.moe_workspace_size(wk.MoeSpec(bad_d), B) == 0         # equal d

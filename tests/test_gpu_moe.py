@@ -101,6 +101,22 @@ def test_moe_trace_and_determinism():
     assert np.array_equal(y1, to_host(r.forward())), "two runs differ"
 
 
+def test_moe_grouped_last_linears():
+    """Experts whose last Linears carry the output LayerNorm run those as one grouped launch
+    (recorded as layer = number of experts); each expert launches its FMB+LCB and first Linear."""
+    tag, n, d, experts, B = CASES[1]
+    r = MoeRun(tag, n, d, experts, B)
+    tr = wk.Trace(capacity=64)
+    y = r.forward(trace=tr)
+    recs = [(x["kernel"], x["layer"], x["index"]) for x in tr.records()]
+    tr.close()
+    assert recs.count(("mlp_linear", len(experts), 0)) == 1, recs
+    for e in range(len(experts)):
+        assert [k for k in recs if k[1] == e] == [("fmb_lcb", e, 0), ("mlp_linear", e, 0)], recs
+    check("Y (grouped last Linears)", host_f64(to_host(y)), r.oracle(), "bf16")
+    assert np.array_equal(to_host(y), to_host(r.forward())), "two runs differ"
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_moe_full_batch_sampled():
