@@ -534,7 +534,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the Wukong forward needs no "
+        print(json.dumps({"error": "the benchmark measures one GPU only: the Wukong forward needs no "
                                    "collectives and every example is independent, so N GPUs would each run "
                                    "this same one-GPU workload on their share of the batch; run with --gpus 1"}))
         sys.exit(2)
