@@ -117,6 +117,18 @@ def test_moe_grouped_last_linears():
     assert np.array_equal(to_host(y), to_host(r.forward())), "two runs differ"
 
 
+def test_moe_grouped_launches_of_four():
+    """Six experts with fused last Linears: those run as two grouped launches (four, then two)."""
+    experts = [(16, 8, 8, (128,))] * 2 + [(24, 12, 12, (192,))] * 4  # rows 2 * 16 + 4 * 24 = 128
+    r = MoeRun("moe6_d160", 128, 160, experts, 20)
+    tr = wk.Trace(capacity=64)
+    y = r.forward(trace=tr)
+    recs = [(x["kernel"], x["layer"], x["index"]) for x in tr.records()]
+    tr.close()
+    assert [k for k in recs if k[1] == len(experts)] == [("mlp_linear", 6, 0), ("mlp_linear", 6, 1)], recs
+    check("Y (six experts)", host_f64(to_host(y)), r.oracle(), "bf16")
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_moe_full_batch_sampled():
