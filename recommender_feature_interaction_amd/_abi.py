@@ -452,12 +452,16 @@ def layer_forward_train(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.T
 
 
 class LayerGrads:
-    """fp32 device gradients of one layer's weights (the C ABI overwrites them)."""
+    """fp32 device gradients of one layer's weights (the C ABI overwrites them).
 
-    def __init__(self, layer: DeviceLayer, affine: bool = True, bias: bool = True):
+    zero=True fills them with zeros: the gradients of an empty batch, for which
+    the C ABI launches nothing."""
+
+    def __init__(self, layer: DeviceLayer, affine: bool = True, bias: bool = True, zero: bool = False):
         spec = layer.spec
         dev = layer.phi.device
-        z = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)  # noqa: E731
+        alloc = torch.zeros if zero else torch.empty
+        z = lambda *shape: alloc(*shape, dtype=torch.float32, device=dev)  # noqa: E731
         n, d, k = spec.n, spec.d, spec.k
         T = len(spec.mlp) - 1
         self.phi, self.w_l = z(k, n), z(spec.n_l, n)
@@ -483,12 +487,14 @@ class LayerGrads:
 def layer_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layer: DeviceLayer,
                    grads: Optional[LayerGrads] = None, dx: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None, trace: "Trace" = None):
-    """Backward of one bf16 layer: returns (dx, grads) from x, the training forward's saved buffer and dy."""
+    """Backward of one bf16 layer: returns (dx, grads) from x, the training forward's saved buffer and dy.
+
+    With an empty batch, gradients allocated here are zero; grads passed in are left untouched."""
     lib = load_library()
     B = _check_x(x, layer.spec)
     if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
         raise ValueError("dy must be contiguous and shaped like x")
-    grads = LayerGrads(layer) if grads is None else grads
+    grads = LayerGrads(layer, zero=B == 0) if grads is None else grads
     dx = torch.empty_like(x) if dx is None else dx
     need = layer_backward_workspace_size(layer.spec, B)
     if need == 0:
@@ -538,12 +544,14 @@ def stack_forward_train(x: torch.Tensor, layers: Sequence[DeviceLayer], y: Optio
 def stack_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layers: Sequence[DeviceLayer],
                    grads: Optional[Sequence[LayerGrads]] = None, dx: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None, stream=None, trace: "Trace" = None):
-    """Backward of a bf16 stack: returns (dx, [LayerGrads per layer])."""
+    """Backward of a bf16 stack: returns (dx, [LayerGrads per layer]).
+
+    With an empty batch, gradients allocated here are zero; grads passed in are left untouched."""
     lib = load_library()
     B = _check_x(x, layers[0].spec)
     if dy.shape != x.shape or dy.dtype != x.dtype or not dy.is_contiguous():
         raise ValueError("dy must be contiguous and shaped like x")
-    grads = [LayerGrads(l) for l in layers] if grads is None else list(grads)
+    grads = [LayerGrads(l, zero=B == 0) for l in layers] if grads is None else list(grads)
     dx = torch.empty_like(x) if dx is None else dx
     need = stack_backward_workspace_size([l.spec for l in layers], B)
     if need == 0:

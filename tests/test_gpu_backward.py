@@ -115,6 +115,28 @@ def test_saved_activations_match_the_forward():
     check("M (saved)", view(lay["m"], r.spec.n_f * d), it["M"].reshape(B, -1), "bf16")
 
 
+def test_backward_empty_and_single_example():
+    """An empty batch: empty dX, zero gradients, and gradients passed in are left as they were.
+    One example: every batch sum has a single term (the weight gradients are outer products)."""
+    r = BackwardRun(CASES[2], seed=10, batch=1)
+    _, _, dx, grads = r.run()
+    ref = r.oracle()
+    check("dX (one example)", host_f64(to_host(dx)), ref["dX"], "bf16")
+    check_grads(grads, ref, len(CASES[2].layers[0].mlp) - 1)
+    x0, dy0 = r.xd[:0], r.dyd[:0]
+    y0, saved0 = wk.layer_forward_train(x0, r.layer)
+    dx0, g0 = wk.layer_backward(x0, saved0, dy0, r.layer)
+    torch.cuda.synchronize()
+    assert y0.shape == dx0.shape == (0, r.spec.n, r.spec.d)
+    for name, t in g0.as_dict().items():
+        for u in t if isinstance(t, list) else [t]:
+            assert u is not None and torch.count_nonzero(u).item() == 0, name
+    before = [t.clone() for t in grads.mlp_w]
+    wk.layer_backward(x0, saved0, dy0, r.layer, grads=grads)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(before, grads.mlp_w))
+
+
 def test_backward_identity_affine_no_bias_effects():
     """Identity LayerNorm affines and zero biases (their gradients are still computed)."""
     r = BackwardRun(CASES[0], seed=7, affine="identity")

@@ -129,6 +129,14 @@ def test_moe_grouped_launches_of_four():
     check("Y (six experts)", host_f64(to_host(y)), r.oracle(), "bf16")
 
 
+def test_moe_empty_and_single_example():
+    r = MoeRun("moe_mixed", 40, 32, CASES[0][3], 1)
+    check("Y (one example)", host_f64(to_host(r.forward())), r.oracle(), "bf16")
+    empty = wk.moe_forward(r.xd[:0], r.moe)
+    torch.cuda.synchronize()
+    assert empty.shape == (0, 40, 32)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(600)
 def test_moe_full_batch_sampled():
