@@ -61,6 +61,7 @@ CASES = [
     (2, 144, 128, 100, 512),   # two query chunks
     (3, 48, 160, 70, 200),     # d_ff % 32 != 0: the FFN as separate kernels
     (7, 80, 160, 20, 32),      # one d_ff chunk; 560 rows, a ragged last FFN tile
+    (1, 128, 160, 1024, 640),  # one example of the measured shape: 128 rows, half an FFN tile
 ]
 
 
