@@ -352,3 +352,18 @@ def test_stack_backward_chains_the_layer_backward():
                 assert all(torch.equal(a, b) for a, b in zip(v, w)), (i, key)
             elif v is not None:
                 assert torch.equal(v, w), (i, key)
+
+
+def test_stack_backward_empty_batch():
+    """An empty batch through a stack: empty outputs and zero gradients for every layer."""
+    _, _, x, dy, spec, dev_layers = _stack_run(STACK_CASES[0])
+    xd = wk.to_device(x, "bf16", "cuda")[:0]
+    dyd = wk.to_device(dy, "bf16", "cuda")[:0]
+    y, saved = wk.stack_forward_train(xd, dev_layers)
+    dx, grads = wk.stack_backward(xd, saved, dyd, dev_layers)
+    torch.cuda.synchronize()
+    assert y.shape == dx.shape == (0, spec.n, spec.d) and len(grads) == len(dev_layers)
+    for g in grads:
+        for name, t in g.as_dict().items():
+            for u in t if isinstance(t, list) else [t]:
+                assert u is not None and torch.count_nonzero(u).item() == 0, name
