@@ -77,6 +77,14 @@ def to_f64(a: np.ndarray) -> np.ndarray:
     return a.astype(np.float64)
 
 
+def to_dtype(a: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """Host array (float32/float64, or uint16 bf16 bits) -> `dtype` (float64 by default)."""
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return decode_bf16(a).astype(dtype, copy=False)
+    return a.astype(dtype, copy=False)
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """Round float64 values to the nearest bf16 value, ties to even.
 
@@ -103,9 +111,9 @@ def layer_norm(v: np.ndarray, gamma, beta, eps: float = LN_EPS) -> np.ndarray:
     var = ((v - mu) ** 2).mean(axis=-1, keepdims=True)
     out = (v - mu) / np.sqrt(var + eps)
     if gamma is not None:
-        out = out * to_f64(gamma)
+        out = out * to_dtype(gamma, out.dtype)
     if beta is not None:
-        out = out + to_f64(beta)
+        out = out + to_dtype(beta, out.dtype)
     return out
 
 
@@ -128,10 +136,10 @@ def fmb_mlp(f_hat: np.ndarray, mlp_w: Sequence[np.ndarray], mlp_b: Sequence,
     h = f_hat
     T = len(mlp_w)
     for t in range(T):
-        W = to_f64(mlp_w[t])
+        W = to_dtype(mlp_w[t], h.dtype)
         h = h @ W.T
         if mlp_b is not None and mlp_b[t] is not None:
-            h = h + to_f64(mlp_b[t])
+            h = h + to_dtype(mlp_b[t], h.dtype)
         if t < T - 1:
             h = np.maximum(h, 0.0)
             h = _maybe_round(h, "h", storage)
@@ -150,24 +158,29 @@ def lcb(X: np.ndarray, w_l: np.ndarray) -> np.ndarray:
 
 # ---------------------------------------------------------------- layer and stack
 def wukong_layer(X, w, eps: float = LN_EPS, storage: Iterable[str] = (),
-                 intermediates: bool = False):
+                 intermediates: bool = False, dtype=np.float64):
     """One Wukong layer on a batch X [S, n, d] (float32 / bf16 bits / float64).
 
     `w` carries phi [k,n], w_l [n_L,n], fm_gamma/fm_beta [n*k], mlp_w (list of
     [m_t, m_{t-1}]), mlp_b (list of [m_t]), out_gamma/out_beta [d]; any of the
     gamma/beta/bias entries may be None.  Returns Y [S, n, d] in float64, or
     (Y, dict of intermediates) when intermediates=True.
+
+    dtype=np.float32 runs the same steps in float32 (a timing variant only: the
+    parity reference is float64); storage rounding needs float64.
     """
     storage = frozenset(storage)
     unknown = storage - STORAGE_NAMES
     if unknown:
         raise ValueError(f"unknown storage names {sorted(unknown)}")
-    X = to_f64(X)
+    if storage and dtype != np.float64:
+        raise ValueError("storage rounding is defined on the float64 oracle")
+    X = to_dtype(X, dtype)
     if X.ndim != 3:
         raise ValueError("X must be [batch, n, d]")
     S, n, d = X.shape
-    phi = to_f64(w.phi)
-    w_l = to_f64(w.w_l)
+    phi = to_dtype(w.phi, dtype)
+    w_l = to_dtype(w.w_l, dtype)
     k, n_l = phi.shape[0], w_l.shape[0]
     if phi.shape[1] != n or w_l.shape[1] != n:
         raise ValueError("Phi and W_L must have n columns")
@@ -196,11 +209,11 @@ def wukong_layer(X, w, eps: float = LN_EPS, storage: Iterable[str] = (),
     return Y, {"Z": Z, "F": F, "Fn": f_hat, "h": hs, "M": M, "L": Lc, "R": R, "Y": Y}
 
 
-def wukong_stack(X, weights: Sequence, eps: float = LN_EPS, storage: Iterable[str] = ()):
+def wukong_stack(X, weights: Sequence, eps: float = LN_EPS, storage: Iterable[str] = (), dtype=np.float64):
     """l stacked layers: X^(i+1) = wukong_layer(X^(i), weights[i]) (step 10)."""
-    Y = to_f64(X)
+    Y = to_dtype(X, dtype)
     for w in weights:
-        Y = wukong_layer(Y, w, eps, storage)
+        Y = wukong_layer(Y, w, eps, storage, dtype=dtype)
     return Y
 
 

@@ -155,6 +155,8 @@ _SIGNATURES = [
     ("wukong_head_forward_traced", ctypes.c_int32,
      [ctypes.POINTER(wk_head_desc), ctypes.POINTER(wk_head_weights), ctypes.c_int64, ctypes.c_void_p,
       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_probe_mfma_bf16", ctypes.c_int32,
+     [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
 ]
 EXPORTED_SYMBOLS = tuple(s[0] for s in _SIGNATURES)
 
@@ -293,9 +295,20 @@ class DeviceLayer:
         return int(sum(t.numel() * t.element_size() for t in ts if t is not None))
 
 
-def _stream_handle(stream) -> Optional[int]:
-    s = torch.cuda.current_stream() if stream is None else stream
-    return s.cuda_stream
+def _stream_handle(stream, *tensors) -> Optional[int]:
+    """The HIP stream to launch on.  When it is not the current stream, it first
+    waits for the current stream's work (which includes making the tensors this
+    call allocated), and every tensor the launches touch is marked as used on it,
+    so the caching allocator does not hand their memory to other work before the
+    launches have finished with it."""
+    cur = torch.cuda.current_stream()
+    if stream is None or stream == cur:
+        return cur.cuda_stream
+    stream.wait_stream(cur)
+    for t in tensors:
+        if isinstance(t, torch.Tensor) and t.is_cuda:
+            t.record_stream(stream)
+    return stream.cuda_stream
 
 
 def _descs(layers: Sequence[DeviceLayer]):
@@ -347,7 +360,7 @@ def layer_forward(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.Tensor]
         workspace = alloc_workspace(need, x.device)
     st = lib.wukong_layer_forward(ctypes.byref(layer.desc), ctypes.byref(layer.weights), B, x.data_ptr(),
                                   y.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                  _stream_handle(stream))
+                                  _stream_handle(stream, x, y, workspace))
     _check(st, "wukong_layer_forward")
     return y
 
@@ -400,7 +413,8 @@ def moe_forward(x: torch.Tensor, moe: DeviceMoe, y: Optional[torch.Tensor] = Non
     if workspace is None:
         workspace = alloc_workspace(need, x.device)
     args = [ctypes.byref(moe.desc), moe.weights, _ptr(moe.out_gamma), _ptr(moe.out_beta), B, x.data_ptr(),
-            y.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream)]
+            y.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(stream, x, y, workspace)]
     if trace is None:
         _check(lib.wukong_moe_layer_forward(*args), "wukong_moe_layer_forward")
     else:
@@ -446,7 +460,7 @@ def layer_forward_train(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.T
         saved = alloc_workspace(need, x.device)
     st = lib.wukong_layer_forward_train(ctypes.byref(layer.desc), ctypes.byref(layer.weights), B, x.data_ptr(),
                                         y.data_ptr(), saved.data_ptr(), saved.numel() * saved.element_size(),
-                                        _stream_handle(stream))
+                                        _stream_handle(stream, x, y, saved))
     _check(st, "wukong_layer_forward_train")
     return y, saved
 
@@ -483,6 +497,11 @@ class LayerGrads:
         return {"phi": self.phi, "w_l": self.w_l, "fm_gamma": self.fm_gamma, "fm_beta": self.fm_beta,
                 "mlp_w": self.mlp_w, "mlp_b": self.mlp_b, "out_gamma": self.out_gamma, "out_beta": self.out_beta}
 
+    def tensors(self) -> list:
+        """Every gradient tensor (the backward writes all of them)."""
+        ts = [self.phi, self.w_l, self.fm_gamma, self.fm_beta, self.out_gamma, self.out_beta, *self.mlp_w]
+        return [t for t in ts + list(self.mlp_b or []) if t is not None]
+
 
 def layer_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layer: DeviceLayer,
                    grads: Optional[LayerGrads] = None, dx: Optional[torch.Tensor] = None,
@@ -503,7 +522,8 @@ def layer_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layer
         workspace = alloc_workspace(need, x.device)
     args = [ctypes.byref(layer.desc), ctypes.byref(layer.weights), B, x.data_ptr(), saved.data_ptr(),
             dy.data_ptr(), dx.data_ptr(), ctypes.byref(grads.c), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream_handle(stream)]
+            workspace.numel() * workspace.element_size(),
+            _stream_handle(stream, x, saved, dy, dx, workspace, *grads.tensors())]
     if trace is None:
         _check(lib.wukong_layer_backward(*args), "wukong_layer_backward")
     else:
@@ -536,7 +556,7 @@ def stack_forward_train(x: torch.Tensor, layers: Sequence[DeviceLayer], y: Optio
         saved = alloc_workspace(need, x.device)
     descs, ws = _descs(layers)
     _check(lib.wukong_stack_forward_train(len(layers), descs, ws, B, x.data_ptr(), y.data_ptr(), saved.data_ptr(),
-                                          saved.numel() * saved.element_size(), _stream_handle(stream)),
+                                          saved.numel() * saved.element_size(), _stream_handle(stream, x, y, saved)),
            "wukong_stack_forward_train")
     return y, saved
 
@@ -561,7 +581,8 @@ def stack_backward(x: torch.Tensor, saved: torch.Tensor, dy: torch.Tensor, layer
     descs, ws = _descs(layers)
     garr = (wk_layer_grads * len(grads))(*[g.c for g in grads])
     args = [len(layers), descs, ws, B, x.data_ptr(), saved.data_ptr(), dy.data_ptr(), dx.data_ptr(), garr,
-            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream)]
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(stream, x, saved, dy, dx, workspace, *[t for g in grads for t in g.tensors()])]
     if trace is None:
         _check(lib.wukong_stack_backward(*args), "wukong_stack_backward")
     else:
@@ -621,7 +642,7 @@ def stack_forward(x: torch.Tensor, layers: Sequence[DeviceLayer], y: Optional[to
     if workspace is None:
         workspace = alloc_workspace(need, x.device)
     args = (len(layers), descs, ws, B, x.data_ptr(), y.data_ptr(), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size(), _stream_handle(stream))
+            workspace.numel() * workspace.element_size(), _stream_handle(stream, x, y, workspace))
     if trace is None:
         st = lib.wukong_stack_forward(*args)
     else:
@@ -694,7 +715,8 @@ def head_forward(y: torch.Tensor, head: DeviceHead, prob: Optional[torch.Tensor]
     if workspace is None:
         workspace = alloc_workspace(need, y.device)
     args = (ctypes.byref(head.desc), ctypes.byref(head.weights), B, y.data_ptr(), prob.data_ptr(),
-            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(stream))
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(stream, y, prob, workspace))
     if trace is None:
         st = lib.wukong_head_forward(*args)
     else:
@@ -764,10 +786,30 @@ def fusion_forward(hw: torch.Tensor, hs: torch.Tensor, fusion: DeviceFusion, hf:
         workspace = alloc_workspace(fusion_workspace_size(spec, B), hw.device)
     args = (ctypes.byref(fusion.desc), ctypes.byref(fusion.weights), B, hw.data_ptr(), hs.data_ptr(),
             hf.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-            _stream_handle(stream))
+            _stream_handle(stream, hw, hs, hf, workspace))
     if trace is None:
         st = lib.wukong_fusion_forward(*args)
     else:
         st = lib.wukong_fusion_forward_traced(*args, trace.handle)
     _check(st, "wukong_fusion_forward")
     return hf
+
+
+# ------------------------------------------------------------------ measurement aid
+def probe_mfma_bf16(blocks: int = 1024, iters: int = 4000, reps: int = 3, device="cuda") -> float:
+    """On-chip bf16 MFMA rate in TFLOP/s (wukong_probe_mfma_bf16): 8 waves per
+    workgroup, operands that change between consecutive instructions."""
+    lib = load_library()
+    g = torch.Generator(device="cpu").manual_seed(7)
+    ops = (torch.rand(16 * 64 * 8, generator=g) * 2 - 1).to(torch.bfloat16).to(device)
+    sink = torch.empty(blocks * 512, dtype=torch.float32, device=device)
+    st = torch.cuda.current_stream()
+    _check(lib.wukong_probe_mfma_bf16(ops.data_ptr(), sink.data_ptr(), blocks, 8, st.cuda_stream), "probe")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        _check(lib.wukong_probe_mfma_bf16(ops.data_ptr(), sink.data_ptr(), blocks, iters, st.cuda_stream), "probe")
+    e1.record(st)
+    torch.cuda.synchronize()
+    flops = reps * blocks * 8.0 * iters * 16 * 16384
+    return flops / (e0.elapsed_time(e1) * 1e-3) / 1e12

@@ -275,14 +275,13 @@ def _stack_run(case):
 
 @pytest.mark.parametrize("case", STACK_CASES, ids=lambda c: c[0])
 def test_stack_backward_parity(case):
-    """Stacks are gated normwise and by rms, like the forward stacks.  A layer's
-    input is the previous layer's bf16 output, whose rounding flips against the
-    oracle's carry into every later gradient, and some gradients are
-    ill-conditioned in that input (a layer's d_Phi and FM LayerNorm gradients
-    pass through the LayerNorm backward of its n k interaction values).  The
-    floor of each quantity is measured on the oracle alone: the same stack with
-    the inter-layer activations kept in fp64 instead of rounded to bf16.  Each
-    quantity must be within max(gate, 2 x floor) normwise and by rms."""
+    """Stacks against the bf16-storage oracle, normwise and by rms at the fixed
+    bf16 gate (2e-2 normwise, 1e-2 rms) for dX and every layer's weight
+    gradients.  A layer's input is the previous layer's bf16 output, whose
+    rounding flips against the oracle's carry into every later gradient, so the
+    elementwise view is left to the per-layer test below.  The oracle's own
+    floor (the same stack with the inter-layer activations kept in fp64
+    instead of bf16) is logged beside each error as a diagnostic only."""
     name, n, d, k, n_f, mlp, layers, B = case
     cfg, host, x, dy, spec, dev_layers = _stack_run(case)
     xd = wk.to_device(x, "bf16", "cuda")
@@ -315,11 +314,11 @@ def test_stack_backward_parity(case):
     for (label, g_), (_, r_), (_, a_) in zip(items(host_f64(to_host(dx)), grads), items(ref_dx, ref),
                                              items(alt_dx, alt)):
         nw_floor, rms_floor = normwise_err(a_, r_), rms_err(a_, r_)
-        tol_nw, tol_rms = max(TOL_BF16, 2 * nw_floor), max(TOL_BF16_RMS, 2 * rms_floor)
         e_nw, e_rms = normwise_err(g_, r_), rms_err(g_, r_)
-        log(f"  {label}: normwise={e_nw:.3e} (tol {tol_nw:.2e}) rms={e_rms:.3e} (tol {tol_rms:.2e})")
+        log(f"  {label}: normwise={e_nw:.3e} rms={e_rms:.3e} (oracle floor: normwise {nw_floor:.2e}, "
+            f"rms {rms_floor:.2e})")
         assert np.all(np.isfinite(g_)), label
-        assert e_nw <= tol_nw and e_rms <= tol_rms, f"{label}: normwise {e_nw:.3e}, rms {e_rms:.3e}"
+        assert e_nw <= TOL_BF16 and e_rms <= TOL_BF16_RMS, f"{label}: normwise {e_nw:.3e}, rms {e_rms:.3e}"
 
 
 def test_stack_backward_chains_the_layer_backward():
@@ -367,3 +366,30 @@ def test_stack_backward_empty_batch():
         for name, t in g.as_dict().items():
             for u in t if isinstance(t, list) else [t]:
                 assert u is not None and torch.count_nonzero(u).item() == 0, name
+
+
+@pytest.mark.parametrize("case", STACK_CASES, ids=lambda c: c[0])
+def test_stack_backward_teacher_forced_per_layer(case):
+    """Each layer of a stack's backward, elementwise at the bf16 gate: layer i on
+    the GPU takes the oracle's bf16 input of that layer (the oracle's forward
+    output of the layer below) and the oracle's bf16 gradient arriving from the
+    layer above, so no rounding flip of another layer reaches the comparison."""
+    name, n, d, k, n_f, mlp, layers, B = case
+    cfg, host, x, dy, spec, dev_layers = _stack_run(case)
+    st_f = FWD_STORAGE + ("Y",)
+    xs = [x]
+    for i in range(layers - 1):  # the oracle's bf16 input of every layer
+        yi = oracle.wukong_layer(xs[-1], host[i], storage=st_f)
+        xs.append(ws.to_bf16_bits(yi.astype(np.float32)))
+    g = dy
+    log(f"stack backward per layer {name}: {layers} layers, B={B}")
+    for i in range(layers - 1, -1, -1):
+        r = BackwardRun.__new__(BackwardRun)
+        r.cfg, r.host_w, r.x, r.dy, r.spec, r.layer = cfg.with_layers(1), host[i], xs[i], g, spec, dev_layers[i]
+        r.xd, r.dyd = wk.to_device(xs[i], "bf16", "cuda"), wk.to_device(g, "bf16", "cuda")
+        _, _, dx, grads = r.run()
+        ref = r.oracle()
+        log(f" layer {i}")
+        check("  dX", host_f64(to_host(dx)), ref["dX"], "bf16")
+        check_grads(grads, ref, len(mlp) - 1)
+        g = ws.to_bf16_bits(ref["dX"].astype(np.float32))  # dX is stored in bf16: exact

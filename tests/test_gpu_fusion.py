@@ -53,8 +53,16 @@ class FusionRun:
         return oracle.whale_fusion(hw, hs, self.w, storage=STORAGE, intermediates=intermediates)
 
 
+# Key tiles hold 32 positions at d >= 96, 64 at d = 64 and 128 at d = 32; the ring has 4
+# slots, so the number of tiles T modulo 4 selects the slot the Fusion Linear's W_f
+# stream starts from.
 CASES = [
-    (5, 32, 64, 50, 256),      # two key tiles, the second ragged
+    (5, 32, 64, 50, 256),      # d = 64: one ragged key tile
+    (3, 48, 64, 130, 256),     # d = 64: three key tiles, the last ragged (T % 4 = 3)
+    (2, 48, 64, 300, 256),     # d = 64: five key tiles, the last ragged (T % 4 = 1)
+    (3, 48, 32, 300, 128),     # d = 32: three 128-position tiles, the last ragged (T % 4 = 3)
+    (2, 32, 32, 600, 128),     # d = 32: five tiles, the last ragged (T % 4 = 1)
+    (2, 16, 32, 520, 128),     # d = 32: five tiles, a last tile of 8 positions
     (4, 128, 160, 1024, 640),  # the measured shape
     (3, 16, 32, 1, 128),       # one position: A equals it for every query
     (2, 48, 96, 33, 384),      # a partly filled query chunk

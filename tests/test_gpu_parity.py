@@ -40,9 +40,15 @@ def test_tiny_f32_full_batch():
         check("Y", y, r.oracle(), "f32")
 
 
-@pytest.mark.parametrize("cfg", [ws.TINY_F32, ws.LAYER_D160, ws.SMALLD_N720, ws.UNITS_N2880], ids=lambda c: c.name)
-def test_single_layer_intermediates(cfg):
-    B = 64 if cfg.dtype == "f32" else 48
+# One layer of each workload (the 8-layer stacks' layer shapes included: n = 256
+# with three Linears, and n = 512, whose FMB+LCB runs the streamed kernel with
+# one example per group), at a batch the oracle finishes in seconds.
+SINGLE = [(ws.TINY_F32, 64), (ws.LAYER_D160, 48), (ws.SMALLD_N720, 48), (ws.UNITS_N2880, 48),
+          (ws.STACK8_N256.with_layers(1), 8), (ws.STACK8_N512.with_layers(1), 6)]
+
+
+@pytest.mark.parametrize("cfg,B", SINGLE, ids=[c.name for c, _ in SINGLE])
+def test_single_layer_intermediates(cfg, B):
     r = Run(cfg, seed=11, affine="random", batch=B)
     spec = spec_of(cfg.layers[0], cfg.dtype)
     wst = wk.alloc_workspace(wk.layer_workspace_size(spec, B))
@@ -75,6 +81,31 @@ def test_stack_two_layers(cfg, batch):
     y = host_f64(to_host(r.forward()))
     check("Y (bf16-storage oracle)", y, r.oracle(), "bf16", elementwise=False)
     log(f"  vs pure fp64 oracle: elementwise {rel_err(y, r.oracle(storage=())):.3e} (reported)")
+
+
+def _oracle_layer_bits(x_bits, host_w):
+    """The oracle's bf16-storage output of one layer, as the bf16 bit patterns the GPU takes
+    as the next layer's input (the stored Y is a bf16 value, so the conversion is exact)."""
+    ref = oracle.wukong_layer(x_bits, host_w, storage=BF16_STORAGE)
+    bits = ws.to_bf16_bits(ref.astype(np.float32))
+    assert np.array_equal(ws.bf16_bits_to_f32(bits).astype(np.float64), ref), "oracle Y is not bf16-valued"
+    return ref, bits
+
+
+@pytest.mark.parametrize("cfg,batch", [(ws.STACK8_N256, 4), (ws.STACK8_N512, 3)], ids=["stack8_n256", "stack8_n512"])
+def test_stack_teacher_forced_per_layer(cfg, batch):
+    """Every layer of the 8-layer stacks, elementwise: layer i on the GPU takes the
+    oracle's (bf16) output of layer i - 1 as its input, so each layer is gated at
+    2e-2 elementwise on its own instead of inheriting the rounding flips of the
+    layers below it (which only the normwise and rms views tolerate)."""
+    r = Run(cfg, seed=7, affine="random", batch=batch)
+    x_bits = r.x
+    for i, layer in enumerate(r.layers):
+        ref, nxt = _oracle_layer_bits(x_bits, r.host_w[i])
+        y = wk.layer_forward(wk.to_device(x_bits, "bf16", "cuda"), layer)
+        torch.cuda.synchronize()
+        check(f"layer {i} Y (input: oracle layer {i - 1})", host_f64(to_host(y)), ref, "bf16")
+        x_bits = nxt
 
 
 def _custom(name, dtype, n, d, k, n_f, mlp, batch, layers=1):
@@ -202,7 +233,7 @@ def test_large_magnitudes():
     check("Y (x100)", y, r.oracle(), "bf16")
 
 
-FULL = [(ws.LAYER_D160, 8), (ws.SMALLD_N720, 8), (ws.STACK8_N256, 4), (ws.STACK8_N512, 4), (ws.UNITS_N2880, 8)]
+FULL = [(ws.STACK8_N256, 4), (ws.STACK8_N512, 4), (ws.UNITS_N2880, 8)]
 
 
 @pytest.mark.slow
@@ -220,3 +251,60 @@ def test_full_size_sampled(cfg, count):
     ref = r.oracle(idx)
     check(f"Y at examples {idx.tolist()}", got, ref, "bf16", elementwise=cfg.num_layers == 1)
     log(f"  vs pure fp64 oracle: elementwise {rel_err(got, r.oracle(idx, storage=())):.3e} (reported)")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg", [ws.LAYER_D160, ws.SMALLD_N720], ids=lambda c: c.name)
+def test_full_batch_every_example(cfg):
+    """The single-layer workloads at their full batch (4096 and 8192 examples), in the
+    benchmark's launch configuration, compared with the bf16-storage oracle on every
+    example, elementwise: cross-example and tail-tile mistakes cannot hide in a sample."""
+    r = Run(cfg, seed=cfg.batch % 89, affine="identity")
+    got = host_f64(to_host(r.forward()))
+    worst = {"elementwise": 0.0, "normwise": 0.0, "rms": 0.0}
+    chunk = 1024
+    for b0 in range(0, cfg.batch, chunk):
+        ref = oracle.wukong_stack(r.x[b0:b0 + chunk], r.host_w, storage=BF16_STORAGE)
+        e = check(f"Y examples {b0}..{b0 + len(ref) - 1}", got[b0:b0 + chunk], ref, "bf16")
+        worst = {k: max(worst[k], e[k]) for k in worst}
+    log(f"  all {cfg.batch} examples: worst {worst}")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("cfg,count", [(ws.STACK8_N256, 3), (ws.STACK8_N512, 3)], ids=["stack8_n256", "stack8_n512"])
+def test_full_size_teacher_forced(cfg, count):
+    """The 8-layer stacks at full batch, one layer call per layer (the launch
+    configuration of the stack's own layers): before each layer, the rows of the
+    sampled examples in its input are replaced by the oracle's output of the layer
+    below, and those examples' outputs are gated elementwise against the oracle's
+    layer on that same input."""
+    r = Run(cfg, seed=cfg.batch % 97, affine="identity")
+    idx = sample_indices(cfg.batch, count, seed=3)
+    idx_d = torch.as_tensor(idx, device="cuda")
+    spec = r.layers[0].spec
+    wst = wk.alloc_workspace(wk.layer_workspace_size(spec, cfg.batch))
+    cur, nxt = r.xd, torch.empty_like(r.xd)
+    x_bits = r.x[idx]
+    for i, layer in enumerate(r.layers):
+        cur[idx_d] = wk.to_device(x_bits, "bf16", "cuda")
+        wk.layer_forward(cur, layer, y=nxt, workspace=wst)
+        torch.cuda.synchronize()
+        assert torch.isfinite(nxt.float()).all().item(), f"layer {i}: non-finite values in the full output"
+        ref, x_bits = _oracle_layer_bits(x_bits, r.host_w[i])
+        check(f"layer {i} Y at examples {idx.tolist()}", host_f64(to_host(nxt[idx_d])), ref, "bf16")
+        cur, nxt = nxt, cur
+
+
+def test_side_stream_launch():
+    """A call on a stream other than the current one: the binding orders it after the
+    current stream's work and keeps the memory it allocated alive for that stream;
+    the result equals the call on the current stream."""
+    r = Run(ws.LAYER_D160, seed=13, affine="random", batch=16)
+    y_ref = to_host(wk.stack_forward(r.xd, r.layers))
+    side = torch.cuda.Stream()
+    y = wk.stack_forward(r.xd, r.layers, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(y), y_ref)

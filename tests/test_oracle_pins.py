@@ -387,11 +387,11 @@ MUTANTS = {
     "residual_dropped": ("R = np.concatenate([M, Lc], axis=1) + X", "R = np.concatenate([M, Lc], axis=1)"),
     "relu_on_last": ("if t < T - 1:", "if True:"),
     "relu_missing": ("h = np.maximum(h, 0.0)", "h = h"),
-    "bias_dropped": ("h = h + to_f64(mlp_b[t])", "h = h"),
+    "bias_dropped": ("h = h + to_dtype(mlp_b[t], h.dtype)", "h = h"),
     "ln_unbiased": ("var = ((v - mu) ** 2).mean(axis=-1, keepdims=True)",
                     "var = ((v - mu) ** 2).sum(axis=-1, keepdims=True) / (v.shape[-1] - 1)"),
     "ln_eps_outside": ("out = (v - mu) / np.sqrt(var + eps)", "out = (v - mu) / (np.sqrt(var) + eps)"),
-    "ln_beta_dropped": ("out = out + to_f64(beta)", "out = out"),
+    "ln_beta_dropped": ("out = out + to_dtype(beta, out.dtype)", "out = out"),
     "lcb_row_shift": ("return np.matmul(w_l, X)", "return np.matmul(w_l, np.roll(X, 1, axis=1))"),
     "fm_ln_skipped": ("f_hat = layer_norm(f, w.fm_gamma, w.fm_beta, eps)", "f_hat = f"),
     "out_ln_over_rows": ("Y = layer_norm(R, w.out_gamma, w.out_beta, eps)",
@@ -427,3 +427,20 @@ def test_mutant_is_caught(mutant):
         except Exception:  # an assertion or a shape error both expose the mistake
             caught.append(name)
     assert caught, f"no pin catches the planted mistake {mutant!r}"
+
+
+def test_float32_timing_variant_follows_the_float64_oracle():
+    """The float32 variant (used only to time the oracle in fp32) runs the same
+    steps: on a d = 160 layer it agrees with the float64 oracle to float32
+    rounding, and it refuses bf16 storage rounding, which is defined in float64."""
+    import wukong_synth as ws
+
+    cfg = ws.LAYER_D160.with_batch(3)
+    w = ws.make_stack_weights(cfg, 2, "random")
+    x = ws.make_input(cfg, 2)
+    y64 = WO.wukong_stack(x, w)
+    y32 = WO.wukong_stack(x, w, dtype=np.float32)
+    assert y32.dtype == np.float32
+    assert np.max(np.abs(y32 - y64)) / np.max(np.abs(y64)) < 1e-5
+    with pytest.raises(ValueError):
+        WO.wukong_stack(x, w, storage=("Y",), dtype=np.float32)
