@@ -1,27 +1,36 @@
 """Throughput of the Wukong layer-stack forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config layer_d160]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config stack8_n256]
+                    [--sections stack8_n512,smalld_n720,layer_d160]
 
 A step is one forward pass of the whole stack (FMB+LCB kernel, every MLP
-Linear, the residual LayerNorm of the FMB rows, for every layer) over one batch of seeded
-synthetic input that is already resident in HBM.  W untimed warm-up steps,
-then K timed steps bracketed by device synchronisation give `value`.  A
-second pass of K steps runs with HIP events recorded by the library around
-each kernel launch (on the launch stream): the per-kernel durations, and the
-kernel with the largest share of the step reported against its roofline.
-The CPU oracle is timed on a bounded sample of the same workload on this host
-as a reference baseline.
+Linear, the residual LayerNorm of the FMB rows, for every layer) over one
+batch of seeded synthetic input that is already resident in HBM.  The
+headline workload is the 8-layer n = 256 stack (B = 16384, d = 160).  W
+untimed warm-up steps, then K timed steps bracketed by device
+synchronisation give `value`.  Each step is also timed between HIP events on
+the launch stream ("step_ms_events": median, min, p90, mean), replayed from a
+HIP graph, and timed with 512 MB written between steps (no input or weight
+left in L2 or the last-level cache: "cold_cache_ms_per_step").  A pass with
+HIP events recorded by the library around each kernel launch gives the
+per-kernel durations and the kernel with the largest share of the step,
+reported against its roofline.  "step_roofline_frac" is the sum over kernels
+of max(FLOPs / peak, bytes / HBM bandwidth) divided by the measured step.
 
-The same steps are timed once more with 512 MB written between them (no
-input or weight left in L2 or the last-level cache: "cold_cache_ms_per_step"),
-a 256 MiB device copy gives the on-box HBM bandwidth ("copy_gbps_measured"),
-and "step_roofline_frac" is the sum over kernels of max(FLOPs / peak, bytes /
-HBM bandwidth) divided by the measured step.
+Two on-box ceilings are measured first: a 256 MiB device copy
+("copy_gbps_measured") and the bf16 MFMA rate on changing operands
+("mfma_tflops_measured", the library's probe kernel).
 
-The prediction head (top MLP + logistic function) and WHALE's fusion step
-(the stack's output as the query H_w, a seeded sequence H_s of 1024
-positions) are then timed on their own and reported under "head" and
-"fusion"; neither is part of `value`.
+The other workloads (the n = 512 stack, the n = 720 small-d layer, the
+d = 160 layer) are measured the same way in the same run and reported under
+"workloads"; the n = 720 layer's "memory_bound_kernels" gives the
+algorithmic bytes of FMB+LCB (and the residual LayerNorm where it runs) over
+their time.  The prediction head and WHALE's fusion step are timed on the
+headline's output; the fusion step, the training step (forward + backward)
+and the mixture-of-experts layer on the single-layer workloads.  None of
+these is part of `value`.  The CPU oracle is timed on a bounded sample of the
+headline workload on this host as a reference baseline (fp64, and the same
+steps in fp32).
 
 Prints one JSON line.
 
@@ -480,30 +489,233 @@ def blas_threads():
 
 
 def cpu_baseline(cfg, host_w, x, budget_s):
-    """The oracle (pure fp64, as it stands) on the first examples of the batch,
-    in chunks, until about budget_s seconds of host time are spent."""
+    """The oracle (as it stands) on the first examples of the batch, in chunks,
+    until about budget_s seconds of host time are spent: pure fp64 (the parity
+    reference), then the same steps in fp32 for about half that time."""
+    import numpy as np
+
     import oracle
 
-    chunk = 64 if cfg.num_layers == 1 else 4
-    done, t0 = 0, time.perf_counter()
-    while done < cfg.batch:
-        m = min(chunk, cfg.batch - done)
-        oracle.wukong_stack(x[done:done + m], host_w, storage=())
-        done += m
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
+    def run(dtype, budget):
+        chunk = 64 if cfg.num_layers == 1 else 4
+        done, t0 = 0, time.perf_counter()
+        while done < cfg.batch:
+            m = min(chunk, cfg.batch - done)
+            oracle.wukong_stack(x[done:done + m], host_w, storage=(), dtype=dtype)
+            done += m
+            if time.perf_counter() - t0 >= budget:
+                break
+        return done, time.perf_counter() - t0
+
+    done, el = run(np.float64, budget_s)
+    done32, el32 = run(np.float32, budget_s / 2)
     return {"value": round(done / el, 3), "unit": "examples/s", "cores": blas_threads(), "kind": "oracle",
             "sample": f"first {done} of {cfg.batch} examples of {cfg.name}, fp64 numpy oracle, "
-                      f"{el:.1f} s on {os.cpu_count()} host CPUs"}
+                      f"{el:.1f} s on {os.cpu_count()} host CPUs",
+            "value_f32": round(done32 / el32, 3),
+            "sample_f32": f"first {done32} examples, the same oracle steps in fp32, {el32:.1f} s"}
+
+
+# workloads measured in the same run as the headline, each reported as a section of its own
+SECTIONS = ("stack8_n512", "smalld_n720", "layer_d160")
+
+
+def stats_ms(v):
+    import numpy as np
+
+    a = np.sort(np.asarray(v, dtype=np.float64))
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a[0]), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "mean": round(float(a.mean()), 4)}
+
+
+def memory_bound_share(cfg, kernels, acct, copy_gbps):
+    """Algorithmic bytes of the memory-bound kernels (FMB+LCB and the residual
+    LayerNorm, or the fused last Linear's extra X / Y traffic is not counted
+    here) over their measured time, as a fraction of HBM bandwidth."""
+    names = ("fmb_lcb", "residual_ln")
+    by = [k for k in kernels if k["kernel"] in names]
+    if not by:
+        return None
+    nbytes = sum(acct[(k["kernel"], k["layer"], k["index"])]["bytes"] for k in by)
+    ms = sum(k["avg_ms"] for k in by)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"kernels": sorted({k["kernel"] for k in by}), "algorithmic_bytes": nbytes, "ms": round(ms, 5),
+            "gbps": round(gbps, 1), "hbm_frac": round(gbps / PEAK_HBM_GBPS, 4),
+            "frac_of_measured_copy": round(gbps / copy_gbps, 4)}
+
+
+def measure_workload(wk, ws, torch, name, args, dev, stream, copy_gbps, mfma_probe, extras=()):
+    """One workload: the stack forward over its batch, timed as the headline is
+    (wall clock over K steps, per-step events, HIP-graph replay, 512 MB flush
+    between steps, per-kernel events), plus the optional sections in `extras`.
+    Returns (result, host weights, host input)."""
+    cfg = ws.get(name)
+    t_gen = time.time()
+    host_w = ws.make_stack_weights(cfg, args.seed, "identity")
+    x_host = ws.make_input(cfg, args.seed)
+    layers = [wk.DeviceLayer.from_host(wk.LayerSpec(s.n, s.d, s.k, s.n_f, s.n_l, tuple(s.mlp), 1e-5, cfg.dtype),
+                                       h, device=dev) for s, h in zip(cfg.layers, host_w)]
+    x = wk.to_device(x_host, cfg.dtype, dev)
+    y = torch.empty_like(x)
+    specs = [l.spec for l in layers]
+    ws_t = wk.alloc_workspace(wk.stack_workspace_size(specs, cfg.batch), dev)
+    torch.cuda.synchronize()
+    print(f"# {cfg.name}: inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    def fwd(trace=None):
+        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream, trace=trace)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        fwd()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    print(f"# {cfg.name}: timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # each step between HIP events on the launch stream (no synchronisation between steps)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        fwd()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = stats_ms([e0.elapsed_time(e1) for e0, e1 in ev])
+
+    # the same step captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed
+    graph_ms = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                wk.stack_forward(x, layers, y=y, workspace=ws_t)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            wk.stack_forward(x, layers, y=y, workspace=ws_t)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
+        del graph
+
+    # per-kernel pass: the library records HIP events around every launch on the launch stream
+    kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step (at most)
+    kernels, dominant, traced_ms = [], None, None
+    fused_layers = [li for li, sp in enumerate(specs) if wk.workspace_layout(sp, cfg.batch)["m"] < 0]
+    acct = kernel_accounting(cfg, fused_layers)
+    if not args.no_trace:
+        trace = wk.Trace(capacity=kpl * args.steps + 16)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            fwd(trace)
+        torch.cuda.synchronize()
+        traced_ms = (time.perf_counter() - t1) * 1e3 / args.steps
+        kernels, dominant = summarize_trace(trace.records(), acct, traced_ms, args.steps)
+        trace.close()
+    roofline = None
+    if dominant is not None:
+        roofline = roofline_of(dominant, acct[(dominant["kernel"], dominant["layer"], dominant["index"])],
+                               dominant["avg_ms"], cfg.dtype, cfg.name)
+        if roofline["unit"] == "GB/s":
+            roofline["frac_of_measured_copy"] = round(roofline["achieved"] / copy_gbps, 4)
+        elif cfg.dtype == "bf16" and mfma_probe:
+            roofline["frac_of_measured_mfma"] = round(roofline["achieved"] / mfma_probe, 4)
+
+    # the same steps with 512 MB written between them (untimed), so no input or weight is
+    # still in L2 or the 256 MB last-level cache when a step starts
+    cold_ms = None
+    if not args.no_cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        evc = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for e0, e1 in evc:
+            flush.fill_(1)
+            e0.record(stream)
+            fwd()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        cold_ms = sum(e0.elapsed_time(e1) for e0, e1 in evc) / args.steps
+        del flush
+
+    # layer roofline fraction: sum over kernels of max(F/P, B/BW) against the measured step
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    ideal_ms = sum(1e3 * max(ac["flops"] / (peak * 1e12), ac["bytes"] / (PEAK_HBM_GBPS * 1e9))
+                   for ac in acct.values())
+    step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
+    s0 = cfg.layers[0]
+    res = {
+        "workload": cfg.name, "global_batch": cfg.batch, "layers": cfg.num_layers, "n": s0.n, "d": s0.d,
+        "k": s0.k, "n_f": s0.n_f, "n_l": s0.n_l, "mlp": list(s0.mlp), "dtype": cfg.dtype,
+        "ms_per_step": round(ms_per_step, 4),
+        "examples_per_s": round(cfg.batch / ms_per_step * 1e3, 1),
+        "step_ms_events": step_ms,
+        "traced_ms_per_step": None if traced_ms is None else round(traced_ms, 4),
+        "step_tflops": round(step_tflops, 2),
+        "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4) if cfg.dtype == "bf16" else None,
+        "step_mfma_frac_of_measured": (round(step_tflops / mfma_probe, 4)
+                                       if cfg.dtype == "bf16" and mfma_probe else None),
+        "step_roofline_frac": round(ideal_ms / ms_per_step, 4),
+        "roofline": roofline,
+        "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 4),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "memory_bound_kernels": memory_bound_share(cfg, kernels, acct, copy_gbps),
+        "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
+    }
+    if "head" in extras:
+        res["head"] = optional_section("head", measure_head, wk, ws, torch, cfg, y, stream, args.steps,
+                                       args.warmup, args.seed)
+    if "fusion" in extras and cfg.dtype == "bf16":
+        res["fusion"] = optional_section("fusion", measure_fusion, wk, ws, torch, cfg, y, stream, args.steps,
+                                         args.warmup, args.seed)
+    if "training" in extras:
+        res["training"] = optional_section("training", measure_training, wk, ws, torch, cfg, layers[0], x, stream,
+                                           args.steps, args.warmup, args.seed)
+    if "moe" in extras and cfg.dtype == "bf16":
+        res["moe"] = optional_section("moe", measure_moe, wk, ws, torch, cfg, x, stream, args.steps, args.warmup,
+                                      args.seed)
+    for key in ("head", "fusion", "training", "moe"):
+        v = res.get(key)
+        if v and "error" not in v:
+            ms = v.get("ms_per_call", v.get("ms_per_step"))
+            print(f"# {cfg.name} {key}: {ms:.3f} ms", file=sys.stderr, flush=True)
+    del x, y, ws_t, layers
+    torch.cuda.empty_cache()
+    return res, host_w, x_host
+
+
+def measure_copy(torch, dev, stream):
+    """On-box copy bandwidth: a 256 MiB device-to-device copy (reads + writes)."""
+    csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(10):
+        cdst.copy_(csrc)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    return 2 * (256 << 20) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="layer_d160")
+    ap.add_argument("--config", default="stack8_n256", help="the headline workload")
+    ap.add_argument("--sections", default=",".join(SECTIONS),
+                    help="comma-separated further workloads measured in the same run ('' for none)")
     ap.add_argument("--seed", type=int, default=1)
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -539,30 +751,22 @@ def main():
                                    "this same one-GPU workload on their share of the batch; run with --gpus 1"}))
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
     import torch
 
     import recommender_feature_interaction_amd as wk
     import wukong_synth as ws
 
-    cfg = ws.get(args.config)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    t_gen = time.time()
-    host_w = ws.make_stack_weights(cfg, args.seed, "identity")
-    x_host = ws.make_input(cfg, args.seed)
-    layers = [wk.DeviceLayer.from_host(wk.LayerSpec(s.n, s.d, s.k, s.n_f, s.n_l, tuple(s.mlp), 1e-5, cfg.dtype),
-                                       h, device=dev) for s, h in zip(cfg.layers, host_w)]
-    x = wk.to_device(x_host, cfg.dtype, dev)
-    y = torch.empty_like(x)
-    specs = [l.spec for l in layers]
-    ws_t = wk.alloc_workspace(wk.stack_workspace_size(specs, cfg.batch), dev)
-    torch.cuda.synchronize()
-    print(f"# {cfg.name}: inputs ready in {time.time() - t_gen:.1f}s", file=sys.stderr, flush=True)
-
     stream = torch.cuda.current_stream()
+
     if args.only:
-        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
+        cfg = ws.get(args.config)
+        host_w = ws.make_stack_weights(cfg, args.seed, "identity")
+        layers = [wk.DeviceLayer.from_host(wk.LayerSpec(s.n, s.d, s.k, s.n_f, s.n_l, tuple(s.mlp), 1e-5, cfg.dtype),
+                                           h, device=dev) for s, h in zip(cfg.layers, host_w)]
+        x = wk.to_device(ws.make_input(cfg, args.seed), cfg.dtype, dev)
+        y = wk.stack_forward(x, layers, stream=stream)
         torch.cuda.synchronize()
         if args.only == "fusion":
             res = measure_fusion(wk, ws, torch, cfg, y, stream, args.steps, args.warmup, args.seed)
@@ -573,174 +777,59 @@ def main():
         print(json.dumps({"only": args.only, "config": {"workload": cfg.name, "global_batch": cfg.batch},
                           args.only: res}), flush=True)
         return
-    for _ in range(args.warmup):
-        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
-    torch.cuda.synchronize()
 
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    value = cfg.batch * args.steps / elapsed
-    print(f"# timed {args.steps} steps: {ms_per_step:.3f} ms/step", file=sys.stderr, flush=True)
+    copy_gbps = measure_copy(torch, dev, stream)
+    mfma_probe = wk.probe_mfma_bf16()
+    print(f"# copy {copy_gbps:.1f} GB/s, MFMA probe {mfma_probe:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    # the same step captured once into a HIP graph (torch.cuda.CUDAGraph) and replayed:
-    # identical kernels and buffers, without per-call host work and launch gaps
-    graph_ms = None
-    if not args.no_graph:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for _ in range(2):
-                wk.stack_forward(x, layers, y=y, workspace=ws_t)
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            wk.stack_forward(x, layers, y=y, workspace=ws_t)
-        for _ in range(args.warmup):
-            graph.replay()
-        torch.cuda.synchronize()
-        tg = time.perf_counter()
-        for _ in range(args.steps):
-            graph.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - tg) * 1e3 / args.steps
-        del graph
-        print(f"# graph replay: {graph_ms:.3f} ms/step", file=sys.stderr, flush=True)
+    extras = [e for e, off in (("head", args.no_head), ("fusion", args.no_fusion)) if not off]
+    head_res, host_w, x_host = measure_workload(wk, ws, torch, args.config, args, dev, stream, copy_gbps, mfma_probe,
+                                                extras)
+    cfg = ws.get(args.config)
+    sections = {}
+    for name in [s for s in args.sections.split(",") if s and s != args.config]:
+        ex = ["fusion"] if not args.no_fusion else []
+        if ws.get(name).num_layers == 1:
+            ex += [e for e, off in (("training", args.no_training), ("moe", args.no_moe)) if not off]
+        sections[name] = optional_section(name, lambda n=name, e=ex: measure_workload(
+            wk, ws, torch, n, args, dev, stream, copy_gbps, mfma_probe, e)[0])
 
-    # per-kernel pass: the library records HIP events around every launch on the launch stream
-    kpl = sum(2 + len(s.mlp) - 1 for s in cfg.layers)  # launches per step (at most)
-    trace = None
-    traced_ms = None
-    if not args.no_trace:
-        trace = wk.Trace(capacity=kpl * args.steps + 16)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream, trace=trace)
-        torch.cuda.synchronize()
-        traced_ms = (time.perf_counter() - t1) * 1e3 / args.steps
-
-    fused_layers = [li for li, sp in enumerate(specs) if wk.workspace_layout(sp, cfg.batch)["m"] < 0]
-    acct = kernel_accounting(cfg, fused_layers)
-    kernels = []
-    dominant = None
-    if trace is not None:
-        kernels, dominant = summarize_trace(trace.records(), acct, traced_ms, args.steps)
-        trace.close()
-
-    roofline = None
-    if dominant is not None:
-        roofline = roofline_of(dominant, acct[(dominant["kernel"], dominant["layer"], dominant["index"])],
-                               dominant["avg_ms"], cfg.dtype, cfg.name)
-
-    # the same steps with 512 MB written between them (untimed), so no input or
-    # weight is still in L2 or the 256 MB last-level cache when a step starts;
-    # each step timed with HIP events on the launch stream
-    cold_ms = None
-    if not args.no_cold:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-        for e0, e1 in ev:
-            flush.fill_(1)
-            e0.record(stream)
-            wk.stack_forward(x, layers, y=y, workspace=ws_t, stream=stream)
-            e1.record(stream)
-        torch.cuda.synchronize()
-        cold_ms = sum(e0.elapsed_time(e1) for e0, e1 in ev) / args.steps
-        del flush
-
-    # on-box copy bandwidth: a 256 MiB device-to-device copy (reads + writes)
-    csrc = torch.empty(256 << 20, dtype=torch.uint8, device=dev).fill_(1)
-    cdst = torch.empty_like(csrc)
-    for _ in range(3):
-        cdst.copy_(csrc)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(10):
-        cdst.copy_(csrc)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * (256 << 20) * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
-    del csrc, cdst
-    if roofline is not None and roofline["unit"] == "GB/s":
-        roofline["frac_of_measured_copy"] = round(roofline["achieved"] / copy_gbps, 4)
-
-    # layer roofline fraction: sum over kernels of max(F/P, B/BW) against the measured step
-    ideal_ms = 0.0
-    for key, ac in acct.items():
-        ideal_ms += 1e3 * max(ac["flops"] / (PEAK_BF16_TFLOPS * 1e12 if cfg.dtype == "bf16" else PEAK_F32_TFLOPS * 1e12),
-                              ac["bytes"] / (PEAK_HBM_GBPS * 1e9))
-
-    head = None
-    if not args.no_head:
-        head = optional_section("head", measure_head, wk, ws, torch, cfg, y, stream, args.steps, args.warmup,
-                                args.seed)
-        if head and "error" not in head:
-            print(f"# head {head['dims']}: {head['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
-
-    fusion = None
-    if not args.no_fusion and cfg.dtype == "bf16":
-        fusion = optional_section("fusion", measure_fusion, wk, ws, torch, cfg, y, stream, args.steps, args.warmup,
-                                  args.seed)
-        if fusion is not None and "error" not in fusion:
-            print(f"# fusion n={fusion['n']} d={fusion['d']} L={fusion['L']}: {fusion['ms_per_call']:.3f} ms/call",
-                  file=sys.stderr, flush=True)
-
-    training = None
-    if not args.no_training:
-        training = optional_section("training", measure_training, wk, ws, torch, cfg, layers[0], x, stream,
-                                    args.steps, args.warmup, args.seed)
-        if training is not None and "error" not in training:
-            print(f"# training step (forward + backward): {training['ms_per_step']:.3f} ms "
-                  f"(forward {training['forward_train_ms']:.3f}, backward {training['backward_ms']:.3f})",
-                  file=sys.stderr, flush=True)
-
-    moe = None
-    if not args.no_moe and cfg.dtype == "bf16":
-        moe = optional_section("moe", measure_moe, wk, ws, torch, cfg, x, stream, args.steps, args.warmup, args.seed)
-        if moe is not None and "error" not in moe:
-            print(f"# mixture of {MOE_EXPERTS} experts: {moe['ms_per_call']:.3f} ms/call", file=sys.stderr, flush=True)
-
-    step_tflops = cfg.flops_per_example() * cfg.batch / (ms_per_step * 1e-3) / 1e12
-    s0 = cfg.layers[0]
+    h = head_res
     out = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(cfg.batch * 1e3 / h["ms_per_step"], 1),
         "unit": "examples/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) inputs, Xavier-uniform weights)",
-        "config": {"workload": cfg.name, "global_batch": cfg.batch, "layers": cfg.num_layers, "n": s0.n,
-                   "d": s0.d, "k": s0.k, "n_f": s0.n_f, "n_l": s0.n_l, "mlp": list(s0.mlp),
+        "config": {"workload": cfg.name, "global_batch": cfg.batch, "layers": cfg.num_layers, "n": h["n"],
+                   "d": h["d"], "k": h["k"], "n_f": h["n_f"], "n_l": h["n_l"], "mlp": h["mlp"],
                    "parallelism": "single GPU"},
-        "traced_ms_per_step": None if traced_ms is None else round(traced_ms, 4),
-        "step_tflops": round(step_tflops, 2),
-        "step_mfma_frac": round(step_tflops / PEAK_BF16_TFLOPS, 4),
-        "roofline": roofline,
-        "step_roofline_frac": round(ideal_ms / ms_per_step, 4),
-        "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 4),
-        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 4),
+        "roofline": h["roofline"],
+        "step_ms_events": h["step_ms_events"],
+        "traced_ms_per_step": h["traced_ms_per_step"],
+        "step_tflops": h["step_tflops"],
+        "step_mfma_frac": h["step_mfma_frac"],
+        "step_mfma_frac_of_measured": h["step_mfma_frac_of_measured"],
+        "step_roofline_frac": h["step_roofline_frac"],
+        "cold_cache_ms_per_step": h["cold_cache_ms_per_step"],
+        "graph_ms_per_step": h["graph_ms_per_step"],
         "copy_gbps_measured": round(copy_gbps, 1),
-        "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"] != "fmb_lcb", k["kernel"], k["index"])),
-        "head": head,
-        "fusion": fusion,
-        "training": training,
-        "moe": moe,
+        "mfma_tflops_measured": round(mfma_probe, 1),
+        "mfma_frac_measured_of_peak": round(mfma_probe / PEAK_BF16_TFLOPS, 4),
+        "memory_bound_kernels": h["memory_bound_kernels"],
+        "kernels": h["kernels"],
+        "head": h.get("head"),
+        "fusion": h.get("fusion"),
+        "workloads": sections,
     }
     if not args.no_cpu_baseline:
-        del x, y, ws_t, layers
-        torch.cuda.empty_cache()
         out["cpu_baseline"] = cpu_baseline(cfg, host_w, x_host, args.cpu_budget)
     else:
         out["cpu_baseline"] = None

@@ -419,6 +419,17 @@ int32_t wukong_fusion_forward_traced(const wk_fusion_desc* desc, const wk_fusion
                                      const void* hw, const void* hs, void* hf, void* workspace,
                                      size_t workspace_bytes, void* stream, wk_trace* trace);
 
+/* ---- Measurement aid ---------------------------------------------------------
+ * The on-chip bf16 MFMA ceiling, reported by the benchmark beside the published
+ * peak: `blocks` workgroups of 8 waves each run `iters` rounds of 16
+ * v_mfma_f32_16x16x32_bf16 (16 x 16 x 32 multiply-adds each) on operands that
+ * change from one instruction to the next.  operands: device buffer of 16 KB
+ * (16 x 64 lanes x 8 bf16, any values; the caller fills it), read-only;
+ * sink: device buffer of blocks x 512 floats, written.  FLOPs of one call:
+ * blocks x 8 x iters x 16 x 16384.  Asynchronous on `stream`.
+ * Returns WK_ERR_INVALID_ARG for null buffers or non-positive sizes. */
+int32_t wukong_probe_mfma_bf16(const void* operands, void* sink, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,4 +19,5 @@ from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceFusion, DeviceHea
                    stack_backward_workspace_size, stack_backward, MoeSpec, DeviceMoe, moe_forward, moe_workspace_size,
                    fusion_workspace_size, head_forward, head_workspace_size,
                    layer_forward, layer_workspace_size, library_path, load_library, stack_forward,
-                   stack_workspace_size, status_string, to_device, workspace_layout, EXPORTED_SYMBOLS)
+                   stack_workspace_size, status_string, to_device, workspace_layout, EXPORTED_SYMBOLS,
+                   probe_mfma_bf16)
