@@ -117,6 +117,23 @@ int32_t wukong_layer_forward(const wk_layer_desc* desc, const wk_layer_weights* 
                              int64_t batch, const void* x, void* y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): wukong_layer_forward
+ * with its workspace taken from a static device array of the library
+ * (wukong_layer_forward_noalloc_max_workspace() bytes, 64 MiB, one copy per GPU,
+ * held until the process ends).  The caller passes x and y as for
+ * wukong_layer_forward; the call allocates and frees nothing.  Returns
+ * WK_ERR_WORKSPACE, launching nothing, when wukong_layer_workspace_size(desc,
+ * batch) exceeds that size (the d = 160, n = 128 layer fits up to a batch of
+ * about 5400 examples), WK_ERR_HIP if the array's device address cannot be
+ * obtained, else as wukong_layer_forward.  Every call on one GPU uses the same
+ * array: calls that overlap on one GPU (on different streams, or from several
+ * threads without ordering) race on it and must not be made.  The array keeps
+ * the last call's intermediates; nothing in it needs clearing between calls. */
+int32_t wukong_layer_forward_noalloc(const wk_layer_desc* desc, const wk_layer_weights* weights,
+                                     int64_t batch, const void* x, void* y, void* stream);
+size_t wukong_layer_forward_noalloc_max_workspace(void);
+
 /* Byte offsets, within a layer's workspace, of the intermediates a
  * wukong_layer_forward call leaves there (for per-kernel checks):
  *   fn      [batch, n*k]       the normalised interaction Fn

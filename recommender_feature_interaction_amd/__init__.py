@@ -20,4 +20,4 @@ from ._abi import (ABI_VERSION, BF16, F32, KERNEL_NAMES, DeviceFusion, DeviceHea
                    fusion_workspace_size, head_forward, head_workspace_size,
                    layer_forward, layer_workspace_size, library_path, load_library, stack_forward,
                    stack_workspace_size, status_string, to_device, workspace_layout, EXPORTED_SYMBOLS,
-                   probe_mfma_bf16)
+                   probe_mfma_bf16, layer_forward_noalloc, noalloc_max_workspace)

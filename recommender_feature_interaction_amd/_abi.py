@@ -155,6 +155,10 @@ _SIGNATURES = [
     ("wukong_head_forward_traced", ctypes.c_int32,
      [ctypes.POINTER(wk_head_desc), ctypes.POINTER(wk_head_weights), ctypes.c_int64, ctypes.c_void_p,
       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_layer_forward_noalloc", ctypes.c_int32,
+     [ctypes.POINTER(wk_layer_desc), ctypes.POINTER(wk_layer_weights), ctypes.c_int64, ctypes.c_void_p,
+      ctypes.c_void_p, ctypes.c_void_p]),
+    ("wukong_layer_forward_noalloc_max_workspace", ctypes.c_size_t, []),
     ("wukong_probe_mfma_bf16", ctypes.c_int32,
      [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]),
 ]
@@ -363,6 +367,23 @@ def layer_forward(x: torch.Tensor, layer: DeviceLayer, y: Optional[torch.Tensor]
                                   _stream_handle(stream, x, y, workspace))
     _check(st, "wukong_layer_forward")
     return y
+
+
+def layer_forward_noalloc(x: torch.Tensor, layer: DeviceLayer, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """One Wukong layer on x [batch, n, d] into the caller's y, with the library's static
+    workspace (wukong_layer_forward_noalloc: nothing is allocated by the call or here)."""
+    lib = load_library()
+    B = _check_x(x, layer.spec)
+    if y.shape != x.shape or y.dtype != x.dtype or not y.is_contiguous() or not y.is_cuda:
+        raise ValueError("y must be a contiguous CUDA tensor shaped like x")
+    st = lib.wukong_layer_forward_noalloc(ctypes.byref(layer.desc), ctypes.byref(layer.weights), B, x.data_ptr(),
+                                          y.data_ptr(), _stream_handle(stream, x, y))
+    _check(st, "wukong_layer_forward_noalloc")
+    return y
+
+
+def noalloc_max_workspace() -> int:
+    return int(load_library().wukong_layer_forward_noalloc_max_workspace())
 
 
 # ------------------------------------------------------------------ mixture of experts

@@ -975,6 +975,33 @@ int32_t stack_backward(int32_t l, const wk_layer_desc* descs, const wk_layer_wei
 
 }  // namespace
 
+// ---- The layer forward without any allocation: its workspace is a file-scope
+// device array (one copy per GPU, held until the process ends).  In host code
+// `scratch` names a host-side stand-in, so its device address is looked up
+// once per device with hipGetSymbolAddress and only that address is used.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)64 << 20;  // the maximum workspace of wukong_layer_forward_noalloc
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int32_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WK_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return WK_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return WK_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int32_t wukong_abi_version(void) { return WUKONG_ABI_VERSION; }
@@ -1015,6 +1042,20 @@ int32_t wukong_layer_workspace_layout(const wk_layer_desc* desc, int64_t batch, 
 int32_t wukong_layer_forward(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
                              const void* x, void* y, void* workspace, size_t workspace_bytes, void* stream) {
   return stack_forward(1, desc, weights, batch, x, y, workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t wukong_layer_forward_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int32_t wukong_layer_forward_noalloc(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
+                                     const void* x, void* y, void* stream) {
+  StackPlan sp;
+  const int32_t st = check_stack(1, desc, batch, &sp);
+  if (st != WK_OK) return st;
+  if (sp.bytes > kScratchBytes) return WK_ERR_WORKSPACE;  // the layer needs more than the static workspace
+  void* ws = nullptr;
+  const int32_t sst = scratch_of_current_device(&ws);
+  if (sst != WK_OK) return sst;
+  return stack_forward(1, desc, weights, batch, x, y, ws, kScratchBytes, stream, nullptr);
 }
 
 size_t wukong_stack_workspace_size(int32_t num_layers, const wk_layer_desc* descs, int64_t batch) {
