@@ -169,19 +169,41 @@ def summarize_trace(recs, acct, per_step_ms, steps):
     return kernels, best[1][0]
 
 
-def backward_accounting(B, s):
+def backward_accounting(B, s, wide=False):
     """Algorithmic FLOPs and HBM bytes per launch of one bf16 layer's backward
-    kernels (recomputed products included: they are work the kernels do)."""
+    kernels (recomputed products included: they are work the kernels do).  wide:
+    the wide layers' backward (output rows, FM part per example, [Phi; W_L]
+    products as GEMMs over the batch-major gradient matrix G = [dZ; dLc])."""
     n, d, k, n_f, n_l = s.n, s.d, s.k, s.n_f, s.n_l
     Bp = (B + 63) // 64 * 64
-    out = {
-        # X, M, dY in; dR (dM and dLc) out; W_L once.  Lc = W_L X recomputed.
-        ("bwd_out", 0, 0): {"flops": B * 2 * n_l * n * d, "bytes": B * (3 * n * d + n_f * d) * 2 + n_l * n * 2},
-        # X, d_Fn, dR in; dX out; [Phi; W_L] once.  Z, F recomputed; dZ, dX, d_Phi, d_W_L.
-        ("bwd_fmb", 0, 0): {"flops": B * (2 * k * n * d * 4 + 2 * n * d * (2 * k + n_l) + 2 * n_l * n * d),
-                            "bytes": B * (3 * n * d + n * k) * 2 + (k + n_l) * n * 2},
-        ("bwd_reduce", 0, 0): {"flops": 0, "bytes": 0},  # the output LN's and the FMB / LCB weight sums
-    }
+    if not wide:
+        out = {
+            # X, M, dY in; dR (dM and dLc) out; W_L once.  Lc = W_L X recomputed.
+            ("bwd_out", 0, 0): {"flops": B * 2 * n_l * n * d, "bytes": B * (3 * n * d + n_f * d) * 2 + n_l * n * 2},
+            # X, d_Fn, dR in; dX out; [Phi; W_L] once.  Z, F recomputed; dZ, dX, d_Phi, d_W_L.
+            ("bwd_fmb", 0, 0): {"flops": B * (2 * k * n * d * 4 + 2 * n * d * (2 * k + n_l) + 2 * n_l * n * d),
+                                "bytes": B * (3 * n * d + n * k) * 2 + (k + n_l) * n * 2},
+        }
+    else:
+        T = len(s.mlp) - 1
+        kc, bd = k + n_l, B * d
+        ldg = (bd + 63) // 64 * 64
+        kcp = (kc + 63) // 64 * 64
+        out = {
+            # X, dY, M (bf16) and Lc (fp32) in; dR out (dM and the dLc rows of G)
+            ("bwd_out", 0, 0): {"flops": 0, "bytes": B * ((3 * n * d + n_f * d) * 2 + n_l * d * 4)},
+            # X, Z, d_Fn, dR in; dZ (bf16) and dR + dF Z (fp32) out; F recomputed, dZ = dF^T X, dF Z
+            ("bwd_fmb", 0, 0): {"flops": B * 6 * n * k * d,
+                                "bytes": B * ((2 * n * d + k * d + n * k + k * d) * 2 + n * d * 4)},
+            ("bwd_transpose", 0, 3 * T): {"flops": 0, "bytes": 2 * B * n * d * 2},  # X batch-major
+            ("bwd_transpose", 0, 3 * T + 1): {"flops": 0, "bytes": (kc * n + n * kcp) * 2},  # [Phi; W_L]^T
+            ("bwd_transpose", 0, 3 * T + 2): {"flops": 0, "bytes": (kc * ldg + ldg * kcp) * 2},  # G^T
+            ("bwd_wgrad", 0, T): {"flops": 2 * k * n * bd, "bytes": (k + n) * ldg * 2 + k * n * 4},  # d_Phi
+            ("bwd_wgrad", 0, T + 1): {"flops": 2 * n_l * n * bd, "bytes": (n_l + n) * ldg * 2 + n_l * n * 4},
+            ("bwd_dgrad", 0, T): {"flops": 2 * n * kc * bd, "bytes": (ldg * kcp + n * kcp) * 2 + n * ldg * 4},
+            ("bwd_reduce", 0, 1): {"flops": 0, "bytes": B * n * d * (4 + 4 + 2)},  # dX = bf16(dXa + C)
+        }
+    out[("bwd_reduce", 0, 0)] = {"flops": 0, "bytes": 0}  # the LayerNorm and FMB / LCB weight sums
     for t, (a, b) in enumerate(zip(s.mlp[:-1], s.mlp[1:])):
         out[("bwd_transpose", 0, 3 * t)] = {"flops": 0, "bytes": (B * b + Bp * b) * 2}
         out[("bwd_transpose", 0, 3 * t + 1)] = {"flops": 0, "bytes": (B * a + Bp * a) * 2}
@@ -229,7 +251,7 @@ def measure_training(wk, ws, torch, cfg, layer, x, stream, steps, warmup, seed):
     torch.cuda.synchronize()
     fwd_ms = (time.perf_counter() - t0) * 1e3 / steps
     T = len(s.mlp) - 1
-    per = 3 + 5 * T + 4 + 4
+    per = 5 * T + 16
     trace = wk.Trace(capacity=per * steps + 8)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -237,8 +259,10 @@ def measure_training(wk, ws, torch, cfg, layer, x, stream, steps, warmup, seed):
         wk.layer_backward(x, saved, dy, layer, grads=grads, dx=dx, workspace=bws, stream=stream, trace=trace)
     torch.cuda.synchronize()
     bwd_ms = (time.perf_counter() - t1) * 1e3 / steps
-    acct = backward_accounting(B, s)
-    kernels, dom = summarize_trace(trace.records(), acct, bwd_ms, steps)
+    recs = trace.records()
+    wide = any(r["kernel"] == "bwd_wgrad" and r["index"] == T for r in recs)
+    acct = backward_accounting(B, s, wide)
+    kernels, dom = summarize_trace(recs, acct, bwd_ms, steps)
     trace.close()
     roof = None
     if dom is not None:
@@ -783,6 +807,8 @@ def main():
     print(f"# copy {copy_gbps:.1f} GB/s, MFMA probe {mfma_probe:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
     extras = [e for e, off in (("head", args.no_head), ("fusion", args.no_fusion)) if not off]
+    if ws.get(args.config).num_layers == 1:
+        extras += [e for e, off in (("training", args.no_training), ("moe", args.no_moe)) if not off]
     head_res, host_w, x_host = measure_workload(wk, ws, torch, args.config, args, dev, stream, copy_gbps, mfma_probe,
                                                 extras)
     cfg = ws.get(args.config)
@@ -827,6 +853,8 @@ def main():
         "kernels": h["kernels"],
         "head": h.get("head"),
         "fusion": h.get("fusion"),
+        "training": h.get("training"),
+        "moe": h.get("moe"),
         "workloads": sections,
     }
     if not args.no_cpu_baseline:

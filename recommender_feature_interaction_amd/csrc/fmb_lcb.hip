@@ -789,6 +789,10 @@ hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t s
   // weights are then read once per workgroup), else the streamed kernel (X
   // and the weights through an LDS ring, several examples per workgroup),
   // else the resident or chunked kernels.
+  if (a.z_out != nullptr || a.lc_out != nullptr) {  // the training outputs: streamed kernel only
+    if (!fmb_lcb_stream_supported(a.n, a.d, a.k, a.n_l)) return hipErrorInvalidValue;
+    return launch_fmb_lcb_stream(a, batch, stream, workgroups);
+  }
   const ResidentVariant* res = pick_resident(a.n, a.d, a.k, a.n_l);
   if (!(res && res->wl) && fmb_lcb_stream_supported(a.n, a.d, a.k, a.n_l))
     return launch_fmb_lcb_stream(a, batch, stream, workgroups);

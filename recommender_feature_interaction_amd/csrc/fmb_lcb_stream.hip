@@ -67,7 +67,9 @@ __host__ __device__ constexpr int zs_pitch(int d) { return (d + 31) / 32 * 32 + 
 // GUARD: a wave skips its weight tiles past the shape's ZT (operands read first, one test per
 // tile); without it every wave computes all WZ * ZPW tiles, the ones past ZT reading zero tiles
 // of the slot (needs ZTMAX >= WZ * ZPW), branch-free with each operand consumed as it is read.
-template <int ET, int ZPW, int WZ, int WE, int EPW, int MPW, int KJ, int ZTMAX, int S, bool GUARD>
+// TRAIN: the training forward also stores Z (bf16, as the interaction uses it) and Lc (fp32, as
+// the LCB rows' LayerNorm uses it) for the backward.
+template <int ET, int ZPW, int WZ, int WE, int EPW, int MPW, int KJ, int ZTMAX, int S, bool GUARD, bool TRAIN>
 __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p, int64_t batch, StreamShape sh) {
   constexpr int D = 16 * ET;
   constexpr int E = WE * EPW;
@@ -299,6 +301,14 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
     // ---- Z -> LDS, LCB rows of Y.  The residual rows are all requested first so
     // their latencies overlap.
     const __amdgpu_buffer_rsrc_t ry = grp_rsrc(p.y, g, n * D);
+    __amdgpu_buffer_rsrc_t rz = ry, rlc = ry;
+    if constexpr (TRAIN) {
+      rz = grp_rsrc(p.z_out, g, k * D);
+      const int64_t b0 = g * E;
+      const int cnt = batch - b0 < E ? (int)(batch - b0) : E;
+      rlc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lc_out + b0 * (int64_t)n_l * D), (short)0,
+                                              cnt * n_l * D * 4, 0x00020000);
+    }
     u32x2 xres[ZPW][EPW][ET];
 #pragma unroll
     for (int zi = 0; zi < ZPW; ++zi) {
@@ -327,6 +337,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
             v[0] = pack_bf16x2(acc[zi][ex][et][0], acc[zi][ex][et][1]);
             v[1] = pack_bf16x2(acc[zi][ex][et][2], acc[zi][ex][et][3]);
             *reinterpret_cast<u32x2*>(zrow + et * 16 + lg * 4) = v;
+            if constexpr (TRAIN) {
+              const uint32_t zoff = z < k ? (uint32_t)(((we * EPW + ex) * k + z) * D + et * 16 + lg * 4) * 2u : kOOB;
+              __builtin_amdgcn_raw_buffer_store_b64(v, rz, zoff, 0, 0);
+            }
           }
         }
       } else {
@@ -334,6 +348,13 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
 #pragma unroll
         for (int ex = 0; ex < EPW; ++ex) {
           const bool valid = zl < n_l;  // examples past the batch: dropped by the resource bound
+          if constexpr (TRAIN) {
+            const uint32_t loff = valid ? (uint32_t)(((we * EPW + ex) * n_l + zl) * D + lg * 4) * 4u : kOOB;
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[zi][ex][et]), rlc,
+                                                     loff + et * 64, 0, 0);
+          }
           float v[ET][4];
           float sm = 0.f;
 #pragma unroll
@@ -503,12 +524,14 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
 struct StreamVariant {
   int et, zpw, wz, we, epw, mpw, kj, ztmax, s;
   void (*kernel)(FmbLcbArgs, int64_t, StreamShape);
+  void (*kernel_train)(FmbLcbArgs, int64_t, StreamShape);  // also stores Z and Lc
 };
 
-#define WK_STREAM(ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD)                 \
-  StreamVariant {                                                                 \
-    ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S,                                      \
-        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD>     \
+#define WK_STREAM(ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD)                       \
+  StreamVariant {                                                                       \
+    ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S,                                            \
+        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD, false>,   \
+        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD, true>     \
   }
 
 // LDS per variant (static): S x (ZTMAX 16 KC + E KC D) + E KJ 16 ZP + 2 D u16.
@@ -555,8 +578,10 @@ hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t
   const int64_t groups = (batch + sh.e - 1) / sh.e;
   const int64_t grid = groups < 256 ? groups : 256;
   if (workgroups) *workgroups = grid;
+  if ((a.z_out == nullptr) != (a.lc_out == nullptr)) return hipErrorInvalidValue;
   if (batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(v->kernel, dim3((unsigned)grid), dim3(NTHREAD), 0, stream, a, batch, sh);
+  hipLaunchKernelGGL(a.z_out ? v->kernel_train : v->kernel, dim3((unsigned)grid), dim3(NTHREAD), 0, stream, a, batch,
+                     sh);
   return hipGetLastError();
 }
 

@@ -949,22 +949,31 @@ hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t 
 // Split-K form of the fp32-output product for shapes whose 256 x 256 tiles
 // leave CUs idle: splits double while tiles x splits < CUs, each split keeps
 // a multiple of 64 of K and at least 1024 of it.
-int linear_bf16_f32out_splits(int64_t M, int N, int K) {
+int linear_bf16_f32out_splits_max(int64_t M, int N, int K, int max_splits) {
   if (!linear_bf16_f32out_supported(M, N, K)) return 1;
   const double tiles = (double)((M + 255) / 256) * (double)((N + 255) / 256);
   int sp = 1;
-  while (sp < kMaxSplits && tiles * sp < (double)kNumCU && K % (2 * sp * kBK) == 0 && K / (2 * sp) >= 1024) sp *= 2;
+  while (sp < max_splits && tiles * sp < (double)kNumCU && K % (2 * sp * kBK) == 0 && K / (2 * sp) >= 1024) sp *= 2;
   return sp;
 }
+int linear_bf16_f32out_splits(int64_t M, int N, int K) { return linear_bf16_f32out_splits_max(M, N, K, kMaxSplits); }
 
-size_t linear_bf16_f32out_split_bytes(int64_t M, int N, int K) {
-  const int sp = linear_bf16_f32out_splits(M, N, K);
+size_t linear_bf16_f32out_split_bytes_max(int64_t M, int N, int K, int max_splits) {
+  const int sp = linear_bf16_f32out_splits_max(M, N, K, max_splits);
   return sp > 1 ? (size_t)sp * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+size_t linear_bf16_f32out_split_bytes(int64_t M, int N, int K) {
+  return linear_bf16_f32out_split_bytes_max(M, N, K, kMaxSplits);
 }
 
 hipError_t launch_linear_bf16_f32out_split(const LinearArgs& a, float* c, float* partial, hipStream_t stream,
                                            int64_t* workgroups) {
-  const int sp = linear_bf16_f32out_splits(a.M, a.N, a.K);
+  return launch_linear_bf16_f32out_split_max(a, c, partial, kMaxSplits, stream, workgroups);
+}
+
+hipError_t launch_linear_bf16_f32out_split_max(const LinearArgs& a, float* c, float* partial, int max_splits,
+                                               hipStream_t stream, int64_t* workgroups) {
+  const int sp = linear_bf16_f32out_splits_max(a.M, a.N, a.K, max_splits);
   if (sp <= 1) return launch_linear_bf16_f32out(a, c, stream, workgroups);
   if (c == nullptr || partial == nullptr) return hipErrorInvalidValue;
   LinearKArgs k;

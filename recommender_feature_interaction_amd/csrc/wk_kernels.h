@@ -20,6 +20,9 @@ struct FmbLcbArgs {
   uint16_t* y;               // [B, n, d]: rows n_f..n-1 are written
   int n, d, k, n_f, n_l;
   float eps;
+  // training forward of the wide layers (streamed kernel only; both or neither):
+  uint16_t* z_out = nullptr;  // [B, k, d] Z = bf16(Phi X), as the interaction uses it
+  float* lc_out = nullptr;    // [B, n_l, d] Lc = W_L X in fp32, as the LCB rows' LayerNorm uses it
 };
 bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l);
 // Streamed variant (fmb_lcb_stream.hip): several examples per workgroup, the
@@ -212,6 +215,53 @@ struct BwdFmbArgs {
   float eps;
 };
 hipError_t launch_bwd_fmb(const BwdFmbArgs& a, hipStream_t stream, int64_t* workgroups);
+// Backward of the wide layers (wukong_backward_wide.hip): n of 256 .. 720 at
+// d = 160 (k <= 64), 32 (k <= 32) or 64, with the per-example gradient
+// matrix G = [dZ; dLc] kept batch-major ([k + n_l, ldg], example b's
+// columns b d .. b d + d - 1) so the weight products run as GEMMs.
+bool wukong_bwd_wide_supported(int n, int d, int k, int n_l);
+struct BwdRowsArgs {
+  const void* x;      // [B, n, d]
+  const void* m;      // [B, n_f, d] the forward's M (bf16)
+  const float* lc;    // [B, n_l, d] the forward's Lc (fp32)
+  const void* dy;     // [B, n, d]
+  const void* gamma;  // [d] or null
+  void* dm;           // [B, n_f, d] out: dR rows < n_f
+  void* g;            // out: dR rows >= n_f at rows k .. of G
+  int64_t ldg;
+  float* part;        // [workgroups, 2 d]: sum dY R_hat, sum dY
+  int64_t batch;
+  int n, d, k, n_f, n_l;
+  float eps;
+};
+hipError_t launch_bwd_rows(const BwdRowsArgs& a, int grid, hipStream_t stream, int64_t* workgroups);
+struct BwdFmWideArgs {
+  const void* x;         // [B, n, d]
+  const void* z;         // [B, k, d] the forward's Z (bf16)
+  const void* dfn;       // [B, n k]
+  const void* fm_gamma;  // [n k] or null
+  const void* dm;        // [B, n_f, d] dR rows < n_f
+  void* g;               // in: dR rows >= n_f at rows k .. of G; out: dZ at rows 0 .. k-1
+  int64_t ldg;
+  float* dxa;            // [B, n, d] out: dR + dF Z
+  float* part;           // [workgroups, 2 n k]: sum d_Fn F_hat, sum d_Fn
+  int64_t batch;
+  int n, d, k, n_f;
+  float eps;
+};
+hipError_t launch_bwd_fm_wide(const BwdFmWideArgs& a, int grid, hipStream_t stream, int64_t* workgroups);
+// dst[r][b D + e] = src[b][r][e] for b < batch, zero for columns batch D .. ld - 1
+hipError_t launch_to_batch_major(const void* src, int64_t batch, int R, int D, int64_t ld, void* dst,
+                                 hipStream_t stream);
+hipError_t launch_zero_cols(void* p, int R, int64_t ld, int64_t c0, hipStream_t stream);
+// dX[b][j][e] = bf16(dXa[b][j][e] + C[j][b D + e])
+hipError_t launch_dx_final(const float* dxa, const float* c, int64_t ldc, int64_t batch, int n, int D, void* dx,
+                           hipStream_t stream, int64_t* workgroups);
+// The fp32-output product split along K into as many as max_splits parts (summed in split order).
+int linear_bf16_f32out_splits_max(int64_t M, int N, int K, int max_splits);
+size_t linear_bf16_f32out_split_bytes_max(int64_t M, int N, int K, int max_splits);
+hipError_t launch_linear_bf16_f32out_split_max(const LinearArgs& a, float* c, float* partial, int max_splits,
+                                               hipStream_t stream, int64_t* workgroups);
 // at[c][r] = a[r][c] (a: [R, C] bf16, C % 8 == 0), zero for R <= r < Rp
 // (Rp % 8 == 0); colpart (or null) gets ceil(Rp / 64) planes of per-64-row
 // column sums, [plane][C] fp32.

@@ -82,6 +82,8 @@ struct LayerPlan {
   size_t hid[kMaxLinear] = {};
   bool fused_out = false;  // last Linear writes the FMB rows of Y itself; no M buffer
   bool use_units = false;  // d = 8: the FMB+LCB step runs as transpose + batched GEMM + epilogue
+  bool save_zl = false;    // training forward of a wide layer: the FMB+LCB step also keeps Z and Lc
+  size_t z = 0, lc = 0;
 };
 
 // Units of width 8 (bf16) take the batched-GEMM form of the FMB+LCB step.
@@ -201,6 +203,10 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.out_beta = static_cast<const uint16_t*>(rm.out_beta);
     a.fn = reinterpret_cast<uint16_t*>(fn);
     a.y = static_cast<uint16_t*>(y);
+    if (plan.save_zl) {
+      a.z_out = reinterpret_cast<uint16_t*>(scratch + plan.z);
+      a.lc_out = reinterpret_cast<float*>(scratch + plan.lc);
+    }
     a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = rm.lcb_row0; a.n_l = d.n_l; a.eps = d.ln_eps;
     if (plan.use_units) {
       void* us = scratch + plan.units;
@@ -636,14 +642,23 @@ int32_t moe_forward(const wk_moe_desc* m, const wk_layer_weights* weights, const
 }
 
 // ---- backward of one bf16 layer.
+// Wide layers (n of 256 .. 720) take the backward of wukong_backward_wide.hip,
+// whose training forward also keeps Z and Lc (streamed FMB+LCB kernel).
+bool wide_backward(const wk_layer_desc& d) {
+  return !wk::wukong_bwd_supported(d.n, d.d, d.k, d.n_l) && wk::wukong_bwd_wide_supported(d.n, d.d, d.k, d.n_l) &&
+         wk::fmb_lcb_stream_supported(d.n, d.d, d.k, d.n_l);
+}
+
 int32_t check_backward_desc(const wk_layer_desc* d) {
   const int32_t st = check_desc(d);
   if (st != WK_OK) return st;
-  if (d->dtype != WK_BF16 || !wk::wukong_bwd_supported(d->n, d->d, d->k, d->n_l)) return WK_ERR_UNSUPPORTED;
+  if (d->dtype != WK_BF16) return WK_ERR_UNSUPPORTED;
+  if (!wk::wukong_bwd_supported(d->n, d->d, d->k, d->n_l) && !wide_backward(*d)) return WK_ERR_UNSUPPORTED;
   return WK_OK;
 }
 
-// Saved activations of the training forward: Fn, h_1 .. h_{T-1}, M.
+// Saved activations of the training forward: Fn, h_1 .. h_{T-1}, M (and for a
+// wide layer Z in bf16 and Lc in fp32).
 LayerPlan plan_saved(const wk_layer_desc& d, int64_t batch) {
   LayerPlan p;
   const size_t B = (size_t)batch;
@@ -657,6 +672,13 @@ LayerPlan plan_saved(const wk_layer_desc& d, int64_t batch) {
   }
   p.m = off;
   off += align_up(B * (size_t)d.n_f * d.d * 2);
+  if (wide_backward(d)) {
+    p.save_zl = true;
+    p.z = off;
+    off += align_up(B * (size_t)d.k * d.d * 2);
+    p.lc = off;
+    off += align_up(B * (size_t)d.n_l * d.d * 4);
+  }
   p.bytes = off;
   p.fused_out = fuse_output_ln(d);  // the fused last Linear stores M for the backward as well
   return p;
@@ -667,7 +689,14 @@ int64_t pad64(int64_t v) { return (v + 63) / 64 * 64; }
 struct BackwardPlan {
   size_t dm = 0, dlc = 0, g[2] = {0, 0}, dfn = 0, gt = 0, at = 0, wt = 0, colpart = 0, split = 0, part_out = 0,
          part_fmb = 0, bytes = 0;
+  // wide layers: G = [dZ; dLc] batch-major [kc, ldg], its transpose [ldg, kcp], X batch-major
+  // [n, ldg], [Phi; W_L] and its transpose, dR + dF Z (fp32), C = [Phi; W_L]^T G (fp32), split partials
+  bool wide = false;
+  int64_t ldg = 0;
+  int kc = 0, kcp = 0;
+  size_t gm = 0, gmt = 0, xb = 0, wcat = 0, wcatt = 0, dxa = 0, cm = 0, wsplit = 0;
 };
+constexpr int kWideWgradSplits = 256;
 
 BackwardPlan plan_backward(const wk_layer_desc& d, int64_t batch) {
   BackwardPlan p;
@@ -691,7 +720,7 @@ BackwardPlan plan_backward(const wk_layer_desc& d, int64_t batch) {
     return o;
   };
   p.dm = take(B * d.n_f * d.d * 2);
-  p.dlc = take(B * d.n_l * d.d * 2);
+  if (!wide_backward(d)) p.dlc = take(B * d.n_l * d.d * 2);  // a wide layer keeps dLc in G
   p.g[0] = take(B * maxhid * 2);
   p.g[1] = take(B * maxhid * 2);
   p.dfn = take(B * d.n * d.k * 2);
@@ -701,7 +730,26 @@ BackwardPlan plan_backward(const wk_layer_desc& d, int64_t batch) {
   p.colpart = take((Bp / 64) * maxdim * 4);
   p.split = take(maxsplit);
   p.part_out = take(wg * wk::wukong_bwd_out_part_floats(d.d) * 4);
-  p.part_fmb = take(wg * wk::wukong_bwd_fmb_part_floats(d.n, d.k, d.n_l) * 4);
+  if (wide_backward(d)) {
+    p.wide = true;
+    p.ldg = (int64_t)(B * d.d + 63) / 64 * 64;
+    p.kc = d.k + d.n_l;
+    p.kcp = (p.kc + 63) / 64 * 64;
+    const size_t L = (size_t)p.ldg;
+    p.part_fmb = take(wg * 2 * (size_t)d.n * d.k * 4);
+    p.gm = take((size_t)p.kc * L * 2);
+    p.gmt = take(L * p.kcp * 2);
+    p.xb = take((size_t)d.n * L * 2);
+    p.wcat = take((size_t)p.kc * d.n * 2);
+    p.wcatt = take((size_t)d.n * p.kcp * 2);
+    p.dxa = take(B * d.n * d.d * 4);
+    p.cm = take((size_t)d.n * L * 4);
+    const size_t s1 = wk::linear_bf16_f32out_split_bytes_max(d.k, d.n, (int)p.ldg, kWideWgradSplits);
+    const size_t s2 = wk::linear_bf16_f32out_split_bytes_max(d.n_l, d.n, (int)p.ldg, kWideWgradSplits);
+    p.wsplit = take(s1 > s2 ? s1 : s2);
+  } else {
+    p.part_fmb = take(wg * wk::wukong_bwd_fmb_part_floats(d.n, d.k, d.n_l) * 4);
+  }
   p.bytes = off;
   return p;
 }
@@ -724,6 +772,130 @@ int32_t layer_forward_train(const wk_layer_desc* d, const wk_layer_weights* w, i
   return run_layer(*d, *w, batch, x, y, static_cast<char*>(saved), sp, launch, 0);
 }
 
+// Backward of a wide layer (wukong_backward_wide.hip): output rows, the MLP,
+// the FM part per example, then the products with [Phi; W_L] as GEMMs over the
+// batch-major gradient matrix G = [dZ; dLc].
+template <class MlpBackward>
+int32_t layer_backward_wide(const wk_layer_desc* d, const wk_layer_weights* w, int64_t batch, const void* x,
+                            const char* sbase, const LayerPlan& sv, const void* dy, void* dx, const wk_layer_grads* gr,
+                            char* base, const BackwardPlan& bp, Launch& launch, int layer_idx, MlpBackward& mlp_backward) {
+  hipStream_t s = launch.stream;
+  const int T = d->num_linear;
+  const int wg = wk::wukong_bwd_workgroups(batch);
+  const int64_t L = bp.ldg;
+  const int n = d->n, D = d->d, k = d->k;
+  void* G = base + bp.gm;
+  float* part_out = reinterpret_cast<float*>(base + bp.part_out);
+  float* part_fm = reinterpret_cast<float*>(base + bp.part_fmb);
+  int32_t st;
+  if (L > batch * D) {  // the padding columns of G take part in the weight products: zero
+    st = hip_status(wk::launch_zero_cols(G, bp.kc, L, batch * D, s));
+    if (st != WK_OK) return st;
+  }
+  wk::BwdRowsArgs ra;
+  ra.x = x;
+  ra.m = sbase + sv.m;
+  ra.lc = reinterpret_cast<const float*>(sbase + sv.lc);
+  ra.dy = dy;
+  ra.gamma = w->out_ln_gamma;
+  ra.dm = base + bp.dm;
+  ra.g = G;
+  ra.ldg = L;
+  ra.part = part_out;
+  ra.batch = batch;
+  ra.n = n;
+  ra.d = D;
+  ra.k = k;
+  ra.n_f = d->n_f;
+  ra.n_l = d->n_l;
+  ra.eps = d->ln_eps;
+  st = launch(WK_KERNEL_BWD_OUT, layer_idx, 0, [&](int64_t* g) { return wk::launch_bwd_rows(ra, wg, s, g); });
+  if (st != WK_OK) return st;
+  st = mlp_backward();
+  if (st != WK_OK) return st;
+  wk::BwdFmWideArgs fa;
+  fa.x = x;
+  fa.z = sbase + sv.z;
+  fa.dfn = base + bp.dfn;
+  fa.fm_gamma = w->fm_ln_gamma;
+  fa.dm = base + bp.dm;
+  fa.g = G;
+  fa.ldg = L;
+  fa.dxa = reinterpret_cast<float*>(base + bp.dxa);
+  fa.part = part_fm;
+  fa.batch = batch;
+  fa.n = n;
+  fa.d = D;
+  fa.k = k;
+  fa.n_f = d->n_f;
+  fa.eps = d->ln_eps;
+  st = launch(WK_KERNEL_BWD_FMB, layer_idx, 0, [&](int64_t* g) { return wk::launch_bwd_fm_wide(fa, wg, s, g); });
+  if (st != WK_OK) return st;
+  // X batch-major, then d[Phi; W_L] = G X'^T split along the batch
+  void* xb = base + bp.xb;
+  st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * T, [&](int64_t* g) {
+    *g = 1;
+    return wk::launch_to_batch_major(x, batch, n, D, L, xb, s);
+  });
+  if (st != WK_OK) return st;
+  float* wsplit = reinterpret_cast<float*>(base + bp.wsplit);
+  for (int part = 0; part < 2; ++part) {
+    wk::LinearArgs wa;
+    wa.a = static_cast<char*>(G) + (part ? (size_t)k * L * 2 : 0);
+    wa.w = xb;
+    wa.bias = nullptr;
+    wa.c = nullptr;
+    wa.M = part ? d->n_l : k;
+    wa.N = n;
+    wa.K = (int)L;
+    wa.act = wk::kActNone;
+    float* out = part ? gr->w_l : gr->phi;
+    st = launch(WK_KERNEL_BWD_WGRAD, layer_idx, T + part, [&](int64_t* g) {
+      return wk::launch_linear_bf16_f32out_split_max(wa, out, wsplit, kWideWgradSplits, s, g);
+    });
+    if (st != WK_OK) return st;
+  }
+  // C = [Phi; W_L]^T G (batch-major, fp32), then dX = bf16(dR + dF Z + C)
+  void* wcat = base + bp.wcat;
+  void* wcatt = base + bp.wcatt;
+  void* gmt = base + bp.gmt;
+  if (hipMemcpyAsync(wcat, w->phi, (size_t)k * n * 2, hipMemcpyDeviceToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(static_cast<char*>(wcat) + (size_t)k * n * 2, w->w_l, (size_t)d->n_l * n * 2,
+                     hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return WK_ERR_HIP;
+  st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * T + 1, [&](int64_t* g) {
+    return wk::launch_transpose_bf16(wcat, bp.kc, n, bp.kcp, wcatt, nullptr, s, g);
+  });
+  if (st != WK_OK) return st;
+  st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * T + 2, [&](int64_t* g) {
+    return wk::launch_transpose_bf16(G, bp.kc, (int)L, bp.kcp, gmt, nullptr, s, g);
+  });
+  if (st != WK_OK) return st;
+  wk::LinearArgs ca;
+  ca.a = wcatt;
+  ca.w = gmt;
+  ca.bias = nullptr;
+  ca.c = nullptr;
+  ca.M = n;
+  ca.N = (int)L;
+  ca.K = bp.kcp;
+  ca.act = wk::kActNone;
+  float* cm = reinterpret_cast<float*>(base + bp.cm);
+  st = launch(WK_KERNEL_BWD_DGRAD, layer_idx, T, [&](int64_t* g) { return wk::launch_linear_bf16_f32out(ca, cm, s, g); });
+  if (st != WK_OK) return st;
+  st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 1, [&](int64_t* g) {
+    return wk::launch_dx_final(reinterpret_cast<const float*>(base + bp.dxa), cm, L, batch, n, D, dx, s, g);
+  });
+  if (st != WK_OK) return st;
+  const int64_t nk = (int64_t)n * k;
+  const wk::PlaneSeg segs[4] = {{part_out, gr->out_ln_gamma, 2 * D, D},
+                                {part_out + D, gr->out_ln_beta, 2 * D, D},
+                                {part_fm, gr->fm_ln_gamma, 2 * nk, nk},
+                                {part_fm + nk, gr->fm_ln_beta, 2 * nk, nk}};
+  return launch(WK_KERNEL_BWD_REDUCE, layer_idx, 0,
+                [&](int64_t* g) { return wk::launch_sum_planes_multi(segs, 4, wg, s, g); });
+}
+
 int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_t batch, const void* x,
                        const void* saved, const void* dy, void* dx, const wk_layer_grads* gr, void* ws,
                        size_t ws_bytes, void* stream, wk_trace* trace, int layer_idx = 0) {
@@ -740,6 +912,7 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   const size_t act = (size_t)batch * d->n * d->d * 2;
   const LayerPlan sv = plan_saved(*d, batch);
   const BackwardPlan bp = plan_backward(*d, batch);
+  if (bp.wide && bp.ldg > INT32_MAX) return WK_ERR_UNSUPPORTED;  // GEMM K and N are 32-bit
   if (!x || !saved || !dy || !dx) return WK_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(saved) || !aligned16(dy) || !aligned16(dx)) return WK_ERR_INVALID_ARG;
   if (!ws || !aligned16(ws)) return WK_ERR_INVALID_ARG;
@@ -759,6 +932,73 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   void* dlc = base + bp.dlc;
   float* part_out = reinterpret_cast<float*>(base + bp.part_out);
   float* part_fmb = reinterpret_cast<float*>(base + bp.part_fmb);
+  const int64_t po = (int64_t)wk::wukong_bwd_out_part_floats(d->d);  // summed with the FMB planes at the end
+
+  // MLP, last Linear first: g_{t+1} -> dW_t, db_t, g_t; the first g is dM, the last d_Fn
+  auto mlp_backward = [&]() -> int32_t {
+    const void* g_next = dm;
+    void* gt = base + bp.gt;
+    void* at = base + bp.at;
+    void* wt = base + bp.wt;
+    float* colpart = reinterpret_cast<float*>(base + bp.colpart);
+    float* split = reinterpret_cast<float*>(base + bp.split);
+    for (int t = T - 1; t >= 0; --t) {
+      const int mi = d->mlp_dims[t], mo = d->mlp_dims[t + 1];
+      const void* a_t =
+          t == 0 ? static_cast<const void*>(sbase + sv.fn) : static_cast<const void*>(sbase + sv.hid[t - 1]);
+      float* db = gr->mlp_b ? gr->mlp_b[t] : nullptr;
+      int32_t r = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t, [&](int64_t* g) {
+        return wk::launch_transpose_bf16(g_next, batch, mo, Bp, gt, db ? colpart : nullptr, s, g);
+      });
+      if (r != WK_OK) return r;
+      if (db) {
+        r = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 2 + t, [&](int64_t* g) {
+          *g = 1;
+          return wk::launch_sum_planes(colpart, (int)(Bp / 64), mo, db, s);
+        });
+        if (r != WK_OK) return r;
+      }
+      r = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t + 1, [&](int64_t* g) {
+        return wk::launch_transpose_bf16(a_t, batch, mi, Bp, at, nullptr, s, g);
+      });
+      if (r != WK_OK) return r;
+      wk::LinearArgs wa;
+      wa.a = gt;
+      wa.w = at;
+      wa.bias = nullptr;
+      wa.c = nullptr;
+      wa.M = mo;
+      wa.N = mi;
+      wa.K = (int)Bp;
+      wa.act = wk::kActNone;
+      r = launch(WK_KERNEL_BWD_WGRAD, layer_idx, t, [&](int64_t* g) {
+        return wk::launch_linear_bf16_f32out_split(wa, gr->mlp_w[t], split, s, g);
+      });
+      if (r != WK_OK) return r;
+      r = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t + 2, [&](int64_t* g) {
+        return wk::launch_transpose_bf16(w->mlp_w[t], mo, mi, mo, wt, nullptr, s, g);
+      });
+      if (r != WK_OK) return r;
+      void* g_out = t == 0 ? static_cast<void*>(base + bp.dfn) : static_cast<void*>(base + bp.g[t % 2]);
+      wk::LinearArgs da;
+      da.a = g_next;
+      da.w = wt;
+      da.bias = nullptr;
+      da.c = g_out;
+      da.M = batch;
+      da.N = mi;
+      da.K = mo;
+      da.act = t == 0 ? wk::kActNone : wk::kActReluMask;
+      da.res = t == 0 ? nullptr : a_t;
+      r = launch(WK_KERNEL_BWD_DGRAD, layer_idx, t, [&](int64_t* g) { return wk::launch_linear_bf16(da, s, g); });
+      if (r != WK_OK) return r;
+      g_next = g_out;
+    }
+    return WK_OK;
+  };
+
+  if (bp.wide) return layer_backward_wide(d, w, batch, x, sbase, sv, dy, dx, gr, base, bp, launch, layer_idx,
+                                          mlp_backward);
 
   // output LayerNorm + LCB rows: dR -> dM, dLc
   wk::BwdOutArgs oa;
@@ -777,66 +1017,8 @@ int32_t layer_backward(const wk_layer_desc* d, const wk_layer_weights* w, int64_
   oa.eps = d->ln_eps;
   st = launch(WK_KERNEL_BWD_OUT, layer_idx, 0, [&](int64_t* g) { return wk::launch_bwd_out(oa, s, g); });
   if (st != WK_OK) return st;
-  const int64_t po = (int64_t)wk::wukong_bwd_out_part_floats(d->d);  // summed with the FMB planes at the end
-
-  // MLP, last Linear first: g_{t+1} -> dW_t, db_t, g_t
-  const void* g_next = dm;
-  void* gt = base + bp.gt;
-  void* at = base + bp.at;
-  void* wt = base + bp.wt;
-  float* colpart = reinterpret_cast<float*>(base + bp.colpart);
-  float* split = reinterpret_cast<float*>(base + bp.split);
-  for (int t = T - 1; t >= 0; --t) {
-    const int mi = d->mlp_dims[t], mo = d->mlp_dims[t + 1];
-    const void* a_t = t == 0 ? static_cast<const void*>(sbase + sv.fn) : static_cast<const void*>(sbase + sv.hid[t - 1]);
-    float* db = gr->mlp_b ? gr->mlp_b[t] : nullptr;
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t, [&](int64_t* g) {
-      return wk::launch_transpose_bf16(g_next, batch, mo, Bp, gt, db ? colpart : nullptr, s, g);
-    });
-    if (st != WK_OK) return st;
-    if (db) {
-      st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 2 + t, [&](int64_t* g) {
-        *g = 1;
-        return wk::launch_sum_planes(colpart, (int)(Bp / 64), mo, db, s);
-      });
-      if (st != WK_OK) return st;
-    }
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t + 1, [&](int64_t* g) {
-      return wk::launch_transpose_bf16(a_t, batch, mi, Bp, at, nullptr, s, g);
-    });
-    if (st != WK_OK) return st;
-    wk::LinearArgs wa;
-    wa.a = gt;
-    wa.w = at;
-    wa.bias = nullptr;
-    wa.c = nullptr;
-    wa.M = mo;
-    wa.N = mi;
-    wa.K = (int)Bp;
-    wa.act = wk::kActNone;
-    st = launch(WK_KERNEL_BWD_WGRAD, layer_idx, t, [&](int64_t* g) {
-      return wk::launch_linear_bf16_f32out_split(wa, gr->mlp_w[t], split, s, g);
-    });
-    if (st != WK_OK) return st;
-    st = launch(WK_KERNEL_BWD_TRANSPOSE, layer_idx, 3 * t + 2, [&](int64_t* g) {
-      return wk::launch_transpose_bf16(w->mlp_w[t], mo, mi, mo, wt, nullptr, s, g);
-    });
-    if (st != WK_OK) return st;
-    void* g_out = t == 0 ? static_cast<void*>(base + bp.dfn) : static_cast<void*>(base + bp.g[t % 2]);
-    wk::LinearArgs da;
-    da.a = g_next;
-    da.w = wt;
-    da.bias = nullptr;
-    da.c = g_out;
-    da.M = batch;
-    da.N = mi;
-    da.K = mo;
-    da.act = t == 0 ? wk::kActNone : wk::kActReluMask;
-    da.res = t == 0 ? nullptr : a_t;
-    st = launch(WK_KERNEL_BWD_DGRAD, layer_idx, t, [&](int64_t* g) { return wk::launch_linear_bf16(da, s, g); });
-    if (st != WK_OK) return st;
-    g_next = g_out;
-  }
+  st = mlp_backward();
+  if (st != WK_OK) return st;
 
   // FM LayerNorm, interaction, compression: dX and the FMB / LCB weight sums
   wk::BwdFmbArgs fa;
@@ -1232,8 +1414,9 @@ int32_t wukong_stack_backward_traced(int32_t num_layers, const wk_layer_desc* de
 
 size_t wukong_layer_backward_workspace_size(const wk_layer_desc* desc, int64_t batch) {
   if (check_backward_desc(desc) != WK_OK || batch < 0 || batch > kMaxBatch) return 0;
-  const size_t b = plan_backward(*desc, batch).bytes;
-  return b ? b : kAlign;
+  const BackwardPlan bp = plan_backward(*desc, batch);
+  if (bp.wide && bp.ldg > INT32_MAX) return 0;
+  return bp.bytes ? bp.bytes : kAlign;
 }
 
 int32_t wukong_layer_backward(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,

@@ -250,8 +250,13 @@ def test_backward_sizes_and_support():
     lay = wk.saved_layout(C1, B)
     assert lay == {"fn": 0, "hidden": [al(B * 4096 * 2)], "m": al(B * 4096 * 2) + al(B * 2048 * 2)}
     assert wk.layer_backward_workspace_size(C1, B) > wk.layer_saved_size(C1, B)
-    # outside the per-example LDS plan (n = 256, d = 160), fp32, d % 16 != 0: unsupported
-    assert wk.layer_saved_size(C2, B) == 0 and wk.layer_backward_workspace_size(C2, B) == 0
+    # the n = 256 layer takes the wide-layer backward: the saved buffer also holds Z (bf16) and Lc (fp32)
+    fn, h1, h2, m = al(B * 12288 * 2), al(B * 4096 * 2), al(B * 4096 * 2), al(B * 128 * 160 * 2)
+    assert wk.layer_saved_size(C2, B) == fn + h1 + h2 + m + al(B * 48 * 160 * 2) + al(B * 128 * 160 * 4)
+    assert wk.layer_backward_workspace_size(C2, B) > 0
+    # the n = 512 layer (X alone is 160 KB per example) and fp32 layers: unsupported
+    C3 = wk.LayerSpec(512, 160, 96, 256, 256, (49152, 8192, 8192, 40960))
+    assert wk.layer_saved_size(C3, B) == 0 and wk.layer_backward_workspace_size(C3, B) == 0
     f32 = wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128), dtype="f32")
     assert wk.layer_backward_workspace_size(f32, B) == 0
     assert wk.layer_backward_workspace_size(wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128)), 37) > 0
@@ -346,7 +351,9 @@ def test_stack_training_sizes_and_argument_errors():
     one = wk.layer_saved_size(sp, B)
     assert wk.stack_saved_size([sp, sp], B) == one + act + one       # layer 1's input between the two
     assert wk.stack_backward_workspace_size([sp, sp], B) == 2 * act + wk.layer_backward_workspace_size(sp, B)
-    assert wk.stack_saved_size([C2, C2], B) == 0                      # n = 256: no backward
+    assert wk.stack_saved_size([C2, C2], B) > 0                       # n = 256: the wide-layer backward
+    C3 = wk.LayerSpec(512, 160, 96, 256, 256, (49152, 8192, 8192, 40960))
+    assert wk.stack_saved_size([C3, C3], B) == 0                      # n = 512: no backward
     pairs = [sp.make_desc() for _ in range(2)]
     descs = (_abi.wk_layer_desc * 2)(*[p[0] for p in pairs])
     wp = (ctypes.c_void_p * 2)(0x40000, 0x50000)
