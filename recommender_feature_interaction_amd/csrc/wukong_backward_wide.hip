@@ -13,10 +13,11 @@
 //    [dZ; dLc] (element (row r, example b, column e) at G[r][b d + e]);
 //    per-workgroup sums of dY R_hat and dY (gamma_out / beta_out gradients).
 //  (the MLP's backward, on the GEMM kernels, gives d_Fn.)
-//  bwd_fm_wide_kernel, per example with X, the saved Z and dF in LDS: F = X
-//    Z^T with MFMA, the FM LayerNorm's statistics and input gradient dF
-//    (bf16), dZ = dF^T X (bf16, to rows 0 .. k - 1 of G) and dXa = dR + dF Z
-//    (fp32); per-workgroup sums of d_Fn F_hat and d_Fn (gamma_fm / beta_fm).
+//  bwd_fm_wide_kernel, per example, X streamed through LDS in row chunks (twice)
+//    with the saved Z in LDS: F = X Z^T with MFMA, the FM LayerNorm's statistics
+//    and input gradient dF (bf16), dZ = dF^T X (bf16, to rows 0 .. k - 1 of G)
+//    and dXa = dR + dF Z (fp32); per-workgroup sums of d_Fn F_hat and d_Fn
+//    (gamma_fm / beta_fm).
 //  Then, on the GEMM kernels: d[Phi; W_L] = G X'^T with X' the batch-major
 //  copy of X (split along the batch), and C = [Phi; W_L]^T G, from which
 //  dx_final_kernel forms dX = bf16(dXa + C) (C is batch-major as well).
@@ -188,40 +189,49 @@ __global__ __launch_bounds__(kRowThreads) void bwd_rows_kernel(BwdRowsArgs p) {
 constexpr int kFmWaves = 8;
 constexpr int kFmThreads = kFmWaves * 64;
 
+// Rows of X walk through LDS in chunks of kChunk (one 16-row tile per wave), twice per
+// example: pass 1 forms F chunk by chunk and gathers the FM LayerNorm's sums (Chan's
+// parallel combination for the variance), pass 2 forms F again, dF, dZ += dF^T X and
+// dR + dF Z for the chunk.  So any n fits; LDS holds Z, one chunk of X and of dF.
+constexpr int kChunk = 16 * kFmWaves;
+
 struct FmLds {
-  int np, kp, xp, fp;  // rows of X and dF (n rounded up to 32), k rounded up to 32, pitches (u16)
-  size_t xs, zs, fs, red, bytes;
+  int kp, xp, fp;  // k rounded up to 32, pitches (u16) of the X / Z rows and of the dF rows
+  size_t zs, xs, fs, red, bytes;
 };
 __host__ __device__ inline FmLds fm_lds(int n, int d, int k) {
+  (void)n;
   FmLds L;
-  L.np = (n + 31) / 32 * 32;
   L.kp = (k + 31) / 32 * 32;
   L.xp = d + 8;
   L.fp = L.kp + 8;
-  L.xs = 0;
-  L.zs = L.xs + (size_t)L.np * L.xp * 2;
-  L.fs = L.zs + (size_t)L.kp * L.xp * 2;
-  L.red = L.fs + (size_t)L.np * L.fp * 2;
-  L.bytes = L.red + 4 * kFmWaves * sizeof(float);
+  L.zs = 0;
+  L.xs = L.zs + (size_t)L.kp * L.xp * 2;
+  L.fs = L.xs + (size_t)kChunk * L.xp * 2;
+  L.red = L.fs + (size_t)kChunk * L.fp * 2;
+  L.bytes = L.red + 8 * kFmWaves * sizeof(float);
   return L;
 }
 
-// D: embedding width; MPW: 16-row tiles of F per wave (ceil(n / 128)); KJ: 16-column tiles of k.
-template <int D, int MPW, int KJ>
+// D: embedding width; KJ: 16-column tiles of k; DZW: dZ tiles (of KJ x D/16) per wave.
+template <int D, int KJ>
 __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p) {
+  constexpr int ET = D / 16;
+  constexpr int DZW = (KJ * ET + kFmWaves - 1) / kFmWaves;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n = p.n, k = p.k, n_f = p.n_f;
   const FmLds L = fm_lds(n, D, k);
-  uint16_t* Xs = reinterpret_cast<uint16_t*>(smem + L.xs);
   uint16_t* Zs = reinterpret_cast<uint16_t*>(smem + L.zs);
+  uint16_t* Xs = reinterpret_cast<uint16_t*>(smem + L.xs);
   uint16_t* Fs = reinterpret_cast<uint16_t*>(smem + L.fs);
   float* red = reinterpret_cast<float*>(smem + L.red);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
-  const int XP = L.xp, FP = L.fp, NP = L.np, KP = L.kp;
+  const int XP = L.xp, FP = L.fp, KP = L.kp;
   const int nk = n * k;
-  // zero once: the padding rows of X, Z and dF and the padding columns of dF
+  const int chunks = (n + kChunk - 1) / kChunk;
+  // zero once: the padding rows of Z and the padding columns of dF stay zero
   for (int i = tid; i < (int)(L.red / 2); i += kFmThreads) reinterpret_cast<uint16_t*>(smem)[i] = 0;
   __syncthreads();
   const uint16_t* X = static_cast<const uint16_t*>(p.x);
@@ -231,133 +241,134 @@ __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p
   const uint16_t* DM = static_cast<const uint16_t*>(p.dm);
   uint16_t* G = static_cast<uint16_t*>(p.g);
   float* part = p.part + (int64_t)blockIdx.x * 2 * nk;
-  const float inv_nk = 1.0f / (float)nk;
+  const float fnk = (float)nk;
   bool first = true;
-  for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
-    // X and Z of the example into LDS (rows < n and < k; the padding stays zero)
-    for (int c = tid; c < n * (D / 8); c += kFmThreads) {
+  // X rows c0 .. c0 + kChunk - 1 of example b into Xs (rows past n as zero)
+  auto load_chunk = [&](int64_t b, int c0) {
+    for (int c = tid; c < kChunk * (D / 8); c += kFmThreads) {
       const int r = c / (D / 8), e = (c - r * (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Xs + r * XP + e) = *reinterpret_cast<const u32x4*>(X + (b * n + r) * D + e);
+      u32x4 v = u32x4{0u, 0u, 0u, 0u};
+      if (c0 + r < n) v = *reinterpret_cast<const u32x4*>(X + (b * n + c0 + r) * D + e);
+      *reinterpret_cast<u32x4*>(Xs + r * XP + e) = v;
     }
+  };
+  // this wave's F tile row of the chunk: lane holds F[m = c0 + 16 wave + li][j = 16 jt + 4 lg + t]
+  auto f_tiles = [&](f32x4 (&f)[KJ]) {
+#pragma unroll
+    for (int jt = 0; jt < KJ; ++jt) {
+      f[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (16 * jt >= k) continue;  // uniform: columns past k
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks)
+        f[jt] = mfma16x16x32(row_frag(Zs, XP, 16 * jt, 32 * ks, li, lg), row_frag(Xs, XP, 16 * wave, 32 * ks, li, lg),
+                             f[jt]);
+    }
+  };
+  for (int64_t b = blockIdx.x; b < p.batch; b += gridDim.x) {
+    __syncthreads();  // the previous example's reads of Z are done
     for (int c = tid; c < k * (D / 8); c += kFmThreads) {
       const int r = c / (D / 8), e = (c - r * (D / 8)) * 8;
       *reinterpret_cast<u32x4*>(Zs + r * XP + e) = *reinterpret_cast<const u32x4*>(Z + (b * k + r) * D + e);
     }
-    __syncthreads();
-    // F^T tiles: lane holds F[m = 16 mt + li][j = 16 jt + 4 lg + t]
-    f32x4 facc[MPW][KJ];
-#pragma unroll
-    for (int i = 0; i < MPW; ++i) {
-      const int mt = wave + kFmWaves * i;
-#pragma unroll
-      for (int jt = 0; jt < KJ; ++jt) {
-        facc[i][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (16 * mt < n && 16 * jt < k) {  // wave-uniform
-#pragma unroll
-          for (int ks = 0; ks < D / 32; ++ks)
-            facc[i][jt] = mfma16x16x32(row_frag(Zs, XP, 16 * jt, 32 * ks, li, lg),
-                                       row_frag(Xs, XP, 16 * mt, 32 * ks, li, lg), facc[i][jt]);
-        }
-      }
-    }
-    auto valid = [&](int i, int jt) {
-      const int m = 16 * (wave + kFmWaves * i) + li, j = 16 * jt + 4 * lg;
-      return m < n && j < k;  // k % 4 == 0: the lane's 4 values are all valid or all not
-    };
-    // the FM LayerNorm's statistics over the n k values of the example
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < MPW; ++i)
-#pragma unroll
-      for (int jt = 0; jt < KJ; ++jt)
-        if (valid(i, jt)) s += (facc[i][jt][0] + facc[i][jt][1]) + (facc[i][jt][2] + facc[i][jt][3]);
-    s = group_sum_v<64>(s);
-    if (lane == 0) red[wave] = s;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kFmWaves; ++w) tot += red[w];
-    const float mean = tot * inv_nk;
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < MPW; ++i)
-#pragma unroll
-      for (int jt = 0; jt < KJ; ++jt)
-        if (valid(i, jt))
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const float dv = facc[i][jt][t] - mean;
-            q += dv * dv;
-          }
-    q = group_sum_v<64>(q);
-    if (lane == 0) red[kFmWaves + wave] = q;
-    __syncthreads();
-    float qt = 0.f;
-#pragma unroll
-    for (int w = 0; w < kFmWaves; ++w) qt += red[kFmWaves + w];
-    const float rstd = rsqrtf(qt * inv_nk + p.eps);
-    // d_Fn gamma_fm, and its two means
-    u32x2 dfv[MPW][KJ];
-    float sq = 0.f, sqf = 0.f;
-#pragma unroll
-    for (int i = 0; i < MPW; ++i)
+    // ---- pass 1: per-lane count, mean and M2 of F (Chan), and the sums of q = d_Fn gamma_fm and q F
+    float cnt = 0.f, mu = 0.f, m2 = 0.f, sq = 0.f, sqf = 0.f;
+    for (int ch = 0; ch < chunks; ++ch) {
+      const int c0 = ch * kChunk;
+      __syncthreads();  // the previous chunk's (and example's) reads are done
+      load_chunk(b, c0);
+      __syncthreads();
+      f32x4 f[KJ];
+      f_tiles(f);
+      const int m = c0 + 16 * wave + li;
 #pragma unroll
       for (int jt = 0; jt < KJ; ++jt) {
-        dfv[i][jt] = u32x2{0u, 0u};
-        if (valid(i, jt)) {
-          const int m = 16 * (wave + kFmWaves * i) + li, j = 16 * jt + 4 * lg;
+        const int j = 16 * jt + 4 * lg;
+        if (m < n && j < k) {  // k % 4 == 0: the lane's 4 values are all valid or all not
           const u32x2 dv = *reinterpret_cast<const u32x2*>(DFN + b * nk + m * k + j);
           const u32x2 gv = GAM ? *reinterpret_cast<const u32x2*>(GAM + m * k + j) : u32x2{0x3f803f80u, 0x3f803f80u};
-          dfv[i][jt] = dv;
           const float d4[4] = {bf16lo(dv[0]), bf16hi(dv[0]), bf16lo(dv[1]), bf16hi(dv[1])};
           const float g4[4] = {bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float fh = (facc[i][jt][t] - mean) * rstd;
-            const float qq = d4[t] * g4[t];
-            facc[i][jt][t] = fh;  // from here on F_hat
-            sq += qq;
-            sqf += qq * fh;
+            const float v = f[jt][t];
+            cnt += 1.f;
+            const float dl = v - mu;
+            mu += dl / cnt;
+            m2 += dl * (v - mu);
+            const float q = d4[t] * g4[t];
+            sq += q;
+            sqf += q * v;
           }
         }
       }
+    }
+    // combine (count, mean, M2) over the lanes of the wave, then over the waves
+    auto chan = [&](float& c1, float& m1, float& s1, float c2, float mean2, float s2) {
+      const float c = c1 + c2;
+      if (c > 0.f) {
+        const float dl = mean2 - m1;
+        m1 += dl * (c2 / c);
+        s1 += s2 + dl * dl * (c1 * c2 / c);
+      }
+      c1 = c;
+    };
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float c2 = __shfl_xor(cnt, off, kWave), mean2 = __shfl_xor(mu, off, kWave), s2 = __shfl_xor(m2, off, kWave);
+      chan(cnt, mu, m2, c2, mean2, s2);
+    }
     sq = group_sum_v<64>(sq);
     sqf = group_sum_v<64>(sqf);
     if (lane == 0) {
-      red[2 * kFmWaves + wave] = sq;
-      red[3 * kFmWaves + wave] = sqf;
+      red[wave] = cnt;
+      red[kFmWaves + wave] = mu;
+      red[2 * kFmWaves + wave] = m2;
+      red[3 * kFmWaves + wave] = sq;
+      red[4 * kFmWaves + wave] = sqf;
     }
     __syncthreads();
-    float mq = 0.f, mqf = 0.f;
+    float tc = 0.f, tmu = 0.f, tm2 = 0.f, tq = 0.f, tqf = 0.f;
 #pragma unroll
     for (int w = 0; w < kFmWaves; ++w) {
-      mq += red[2 * kFmWaves + w];
-      mqf += red[3 * kFmWaves + w];
+      chan(tc, tmu, tm2, red[w], red[kFmWaves + w], red[2 * kFmWaves + w]);
+      tq += red[3 * kFmWaves + w];
+      tqf += red[4 * kFmWaves + w];
     }
-    mq *= inv_nk;
-    mqf *= inv_nk;
-    // dF = rstd (q - mean(q) - F_hat mean(q F_hat)) in bf16 to LDS; the gamma_fm / beta_fm
-    // sums of this workgroup's examples (each (m, j) belongs to one lane of the workgroup)
+    const float rstd = rsqrtf(tm2 / fnk + p.eps);
+    const float mq = tq / fnk;                         // mean of q
+    const float mqf = rstd * (tqf - tmu * tq) / fnk;   // mean of q F_hat
+    // ---- pass 2: F again, dF (bf16) to LDS, dZ += dF^T X, dR + dF Z
+    f32x4 dz[DZW];
 #pragma unroll
-    for (int i = 0; i < MPW; ++i)
+    for (int i = 0; i < DZW; ++i) dz[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ch = 0; ch < chunks; ++ch) {
+      const int c0 = ch * kChunk;
+      __syncthreads();
+      load_chunk(b, c0);
+      __syncthreads();
+      f32x4 f[KJ];
+      f_tiles(f);
+      const int m = c0 + 16 * wave + li;
 #pragma unroll
-      for (int jt = 0; jt < KJ; ++jt)
-        if (valid(i, jt)) {
-          const int m = 16 * (wave + kFmWaves * i) + li, j = 16 * jt + 4 * lg;
-          const u32x2 dv = dfv[i][jt];
+      for (int jt = 0; jt < KJ; ++jt) {
+        const int j = 16 * jt + 4 * lg;
+        u32x2 o = u32x2{0u, 0u};
+        if (m < n && j < k) {
+          const u32x2 dv = *reinterpret_cast<const u32x2*>(DFN + b * nk + m * k + j);
           const u32x2 gv = GAM ? *reinterpret_cast<const u32x2*>(GAM + m * k + j) : u32x2{0x3f803f80u, 0x3f803f80u};
           const float d4[4] = {bf16lo(dv[0]), bf16hi(dv[0]), bf16lo(dv[1]), bf16hi(dv[1])};
           const float g4[4] = {bf16lo(gv[0]), bf16hi(gv[0]), bf16lo(gv[1]), bf16hi(gv[1])};
-          float o[4];
+          float df[4];
           f32x4 pg, pb;
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float fh = facc[i][jt][t];
-            o[t] = rstd * (d4[t] * g4[t] - mq - fh * mqf);
+            const float fh = (f[jt][t] - tmu) * rstd;
+            df[t] = rstd * (d4[t] * g4[t] - mq - fh * mqf);
             pg[t] = d4[t] * fh;
             pb[t] = d4[t];
           }
-          *reinterpret_cast<u32x2*>(Fs + m * FP + j) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          o = u32x2{pack_bf16x2(df[0], df[1]), pack_bf16x2(df[2], df[3])};
+          // this workgroup's gamma_fm / beta_fm sums: each (m, j) belongs to one lane
           f32x4* pgp = reinterpret_cast<f32x4*>(part + m * k + j);
           f32x4* pbp = reinterpret_cast<f32x4*>(part + nk + m * k + j);
           if (!first) {
@@ -367,37 +378,52 @@ __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p
           *pgp = pg;
           *pbp = pb;
         }
-    __syncthreads();
-    // dZ = dF^T X: tiles (jt, et), lane holds dZ[16 jt + 4 lg + t][16 et + li]
-    for (int tq = wave; tq < KJ * (D / 16); tq += kFmWaves) {
-      const int jt = tq / (D / 16), et = tq - jt * (D / 16);
-      if (16 * jt >= k) continue;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int m0 = 0; m0 < NP; m0 += 32)
-        acc = mfma16x16x32(col_frag(Fs, FP, m0, 16 * jt, li, lg), col_frag(Xs, XP, m0, 16 * et, li, lg), acc);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int j = 16 * jt + 4 * lg + t;
-        if (j < k) G[(int64_t)j * p.ldg + b * D + 16 * et + li] = (uint16_t)f32_to_bf16(acc[t]);
+        if (j < KP) *reinterpret_cast<u32x2*>(Fs + (16 * wave + li) * FP + j) = o;  // rows past n: zero
       }
-    }
-    // dXa = dR + dF Z: tiles (mt, et), lane holds [16 mt + 4 lg + t][16 et + li]
-    for (int tq = wave; tq < (NP / 16) * (D / 16); tq += kFmWaves) {
-      const int mt = tq / (D / 16), et = tq - mt * (D / 16);
-      if (16 * mt >= n) continue;
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int j0 = 0; j0 < KP; j0 += 32)
-        acc = mfma16x16x32(row_frag(Fs, FP, 16 * mt, j0, li, lg), col_frag(Zs, XP, j0, 16 * et, li, lg), acc);
+      __syncthreads();
+      // dZ tiles (jt, et) owned by this wave: + dF_chunk^T X_chunk over the chunk's rows
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int m = 16 * mt + 4 * lg + t, e = 16 * et + li;
-        if (m < n) {
-          const uint16_t dr = m < n_f ? DM[(b * n_f + m) * D + e] : G[(int64_t)(k + m - n_f) * p.ldg + b * D + e];
-          p.dxa[(b * n + m) * D + e] = acc[t] + bf(dr);
+      for (int i = 0; i < DZW; ++i) {
+        const int tq2 = wave + kFmWaves * i;
+        if (tq2 < KJ * ET && 16 * (tq2 / ET) < k) {  // wave-uniform
+          const int jt = tq2 / ET, et = tq2 - jt * ET;
+#pragma unroll
+          for (int m0 = 0; m0 < kChunk; m0 += 32)
+            dz[i] = mfma16x16x32(col_frag(Fs, FP, m0, 16 * jt, li, lg), col_frag(Xs, XP, m0, 16 * et, li, lg), dz[i]);
+        }
+      }
+      // dR + dF Z for the chunk's rows: tiles (this wave's row tile, et)
+      if (c0 + 16 * wave < n) {  // wave-uniform
+#pragma unroll
+        for (int et = 0; et < ET; ++et) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int j0 = 0; j0 < KP; j0 += 32)
+            acc = mfma16x16x32(row_frag(Fs, FP, 16 * wave, j0, li, lg), col_frag(Zs, XP, j0, 16 * et, li, lg), acc);
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int mm = c0 + 16 * wave + 4 * lg + t, e = 16 * et + li;
+            if (mm < n) {
+              const uint16_t dr =
+                  mm < n_f ? DM[(b * n_f + mm) * D + e] : G[(int64_t)(k + mm - n_f) * p.ldg + b * D + e];
+              p.dxa[(b * n + mm) * D + e] = acc[t] + bf(dr);
+            }
+          }
         }
       }
     }
-    __syncthreads();  // LDS reused by the next example
+    // dZ (bf16) to its rows of G: lane holds dZ[16 jt + 4 lg + t][16 et + li]
+#pragma unroll
+    for (int i = 0; i < DZW; ++i) {
+      const int tq2 = wave + kFmWaves * i;
+      if (tq2 < KJ * ET) {
+        const int jt = tq2 / ET, et = tq2 - jt * ET;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int j = 16 * jt + 4 * lg + t;
+          if (j < k) G[(int64_t)j * p.ldg + b * D + 16 * et + li] = (uint16_t)f32_to_bf16(dz[i][t]);
+        }
+      }
+    }
     first = false;
   }
   if (first) {  // no example: the sums are zero
@@ -456,18 +482,20 @@ hipError_t allow_lds_w(K* kern) {
 }
 
 struct FmVariant {
-  int d, mpw, kj;
+  int d, kj;
   void (*kernel)(BwdFmWideArgs);
 };
 const FmVariant kFmVariants[] = {
-    {160, 2, 4, bwd_fm_wide_kernel<160, 2, 4>},  // n <= 256, k <= 64 at d = 160
-    {32, 6, 2, bwd_fm_wide_kernel<32, 6, 2>},    // n <= 768, k <= 32 at d = 32
-    {64, 3, 2, bwd_fm_wide_kernel<64, 3, 2>},    // n <= 384, k <= 32 at d = 64
+    {160, 3, bwd_fm_wide_kernel<160, 3>},  // d = 160, k <= 48
+    {160, 6, bwd_fm_wide_kernel<160, 6>},  // d = 160, k <= 96
+    {32, 2, bwd_fm_wide_kernel<32, 2>},    // d = 32, k <= 32
+    {64, 2, bwd_fm_wide_kernel<64, 2>},    // d = 64, k <= 32
 };
 
 const FmVariant* pick_fm(int n, int d, int k) {
+  (void)n;
   for (const auto& v : kFmVariants) {
-    if (v.d != d || (n + 15) / 16 > kFmWaves * v.mpw || (k + 15) / 16 > v.kj) continue;
+    if (v.d != d || (k + 15) / 16 > v.kj) continue;
     if (fm_lds(n, d, k).bytes > (size_t)kLdsMaxW) continue;
     return &v;
   }

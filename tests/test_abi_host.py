@@ -254,9 +254,9 @@ def test_backward_sizes_and_support():
     fn, h1, h2, m = al(B * 12288 * 2), al(B * 4096 * 2), al(B * 4096 * 2), al(B * 128 * 160 * 2)
     assert wk.layer_saved_size(C2, B) == fn + h1 + h2 + m + al(B * 48 * 160 * 2) + al(B * 128 * 160 * 4)
     assert wk.layer_backward_workspace_size(C2, B) > 0
-    # the n = 512 layer (X alone is 160 KB per example) and fp32 layers: unsupported
     C3 = wk.LayerSpec(512, 160, 96, 256, 256, (49152, 8192, 8192, 40960))
-    assert wk.layer_saved_size(C3, B) == 0 and wk.layer_backward_workspace_size(C3, B) == 0
+    assert wk.layer_saved_size(C3, 2048) > 0 and wk.layer_backward_workspace_size(C3, 2048) > 0
+    # fp32 layers: unsupported
     f32 = wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128), dtype="f32")
     assert wk.layer_backward_workspace_size(f32, B) == 0
     assert wk.layer_backward_workspace_size(wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128)), 37) > 0
@@ -353,7 +353,7 @@ def test_stack_training_sizes_and_argument_errors():
     assert wk.stack_backward_workspace_size([sp, sp], B) == 2 * act + wk.layer_backward_workspace_size(sp, B)
     assert wk.stack_saved_size([C2, C2], B) > 0                       # n = 256: the wide-layer backward
     C3 = wk.LayerSpec(512, 160, 96, 256, 256, (49152, 8192, 8192, 40960))
-    assert wk.stack_saved_size([C3, C3], B) == 0                      # n = 512: no backward
+    assert wk.stack_saved_size([C3, C3], B) > 0                       # n = 512: the wide-layer backward
     pairs = [sp.make_desc() for _ in range(2)]
     descs = (_abi.wk_layer_desc * 2)(*[p[0] for p in pairs])
     wp = (ctypes.c_void_p * 2)(0x40000, 0x50000)
