@@ -197,10 +197,9 @@ constexpr int kChunk = 16 * kFmWaves;
 
 struct FmLds {
   int kp, xp, fp;  // k rounded up to 32, pitches (u16) of the X / Z rows and of the dF rows
-  size_t zs, xs, fs, red, bytes;
+  size_t zs, xs, fs, red, sums, bytes;
 };
-__host__ __device__ inline FmLds fm_lds(int n, int d, int k) {
-  (void)n;
+__host__ __device__ inline FmLds fm_lds(int n, int d, int k, bool sums_in_lds = false) {
   FmLds L;
   L.kp = (k + 31) / 32 * 32;
   L.xp = d + 8;
@@ -209,30 +208,36 @@ __host__ __device__ inline FmLds fm_lds(int n, int d, int k) {
   L.xs = L.zs + (size_t)L.kp * L.xp * 2;
   L.fs = L.xs + (size_t)kChunk * L.xp * 2;
   L.red = L.fs + (size_t)kChunk * L.fp * 2;
-  L.bytes = L.red + 8 * kFmWaves * sizeof(float);
+  L.sums = L.red + 8 * kFmWaves * sizeof(float);
+  L.bytes = L.sums + (sums_in_lds ? (size_t)2 * n * k * sizeof(float) : 0);
   return L;
 }
 
 // D: embedding width; KJ: 16-column tiles of k; DZW: dZ tiles (of KJ x D/16) per wave.
-template <int D, int KJ>
+// The workgroup's gamma_fm / beta_fm sums over its examples (each lane owns the same
+// (m, j) in every example): NCH > 0: at most NCH row chunks, the sums in registers;
+// NCH = -1: in LDS after the other arrays (fm_lds(.., true)); NCH = 0: read-modify-
+// written in the workgroup's plane in global memory.
+template <int D, int KJ, int NCH>
 __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p) {
   constexpr int ET = D / 16;
   constexpr int DZW = (KJ * ET + kFmWaves - 1) / kFmWaves;
   extern __shared__ __align__(16) unsigned char smem[];
   const int n = p.n, k = p.k, n_f = p.n_f;
-  const FmLds L = fm_lds(n, D, k);
+  const FmLds L = fm_lds(n, D, k, NCH < 0);
   uint16_t* Zs = reinterpret_cast<uint16_t*>(smem + L.zs);
   uint16_t* Xs = reinterpret_cast<uint16_t*>(smem + L.xs);
   uint16_t* Fs = reinterpret_cast<uint16_t*>(smem + L.fs);
   float* red = reinterpret_cast<float*>(smem + L.red);
+  float* Ss = reinterpret_cast<float*>(smem + L.sums);  // NCH < 0: the gamma_fm / beta_fm sums
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, lg = lane >> 4;
   const int XP = L.xp, FP = L.fp, KP = L.kp;
   const int nk = n * k;
   const int chunks = (n + kChunk - 1) / kChunk;
-  // zero once: the padding rows of Z and the padding columns of dF stay zero
-  for (int i = tid; i < (int)(L.red / 2); i += kFmThreads) reinterpret_cast<uint16_t*>(smem)[i] = 0;
+  // zero once: the padding rows of Z and the padding columns of dF stay zero (and the sums start at 0)
+  for (int i = tid; i < (int)(L.bytes / 2); i += kFmThreads) reinterpret_cast<uint16_t*>(smem)[i] = 0;
   __syncthreads();
   const uint16_t* X = static_cast<const uint16_t*>(p.x);
   const uint16_t* Z = static_cast<const uint16_t*>(p.z);
@@ -243,6 +248,14 @@ __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p
   float* part = p.part + (int64_t)blockIdx.x * 2 * nk;
   const float fnk = (float)nk;
   bool first = true;
+  constexpr int NC = NCH > 0 ? NCH : 1;
+  f32x4 psg[NC][KJ], psb[NC][KJ];  // used when NCH > 0
+  if constexpr (NCH > 0) {
+#pragma unroll
+    for (int ch = 0; ch < NC; ++ch)
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt) psg[ch][jt] = psb[ch][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   // X rows c0 .. c0 + kChunk - 1 of example b into Xs (rows past n as zero)
   auto load_chunk = [&](int64_t b, int c0) {
     for (int c = tid; c < kChunk * (D / 8); c += kFmThreads) {
@@ -341,7 +354,7 @@ __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p
     f32x4 dz[DZW];
 #pragma unroll
     for (int i = 0; i < DZW; ++i) dz[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int ch = 0; ch < chunks; ++ch) {
+    auto pass2 = [&](int ch, f32x4 (&pgs)[KJ], f32x4 (&pbs)[KJ]) {
       const int c0 = ch * kChunk;
       __syncthreads();
       load_chunk(b, c0);
@@ -369,14 +382,24 @@ __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p
           }
           o = u32x2{pack_bf16x2(df[0], df[1]), pack_bf16x2(df[2], df[3])};
           // this workgroup's gamma_fm / beta_fm sums: each (m, j) belongs to one lane
-          f32x4* pgp = reinterpret_cast<f32x4*>(part + m * k + j);
-          f32x4* pbp = reinterpret_cast<f32x4*>(part + nk + m * k + j);
-          if (!first) {
-            pg += *pgp;
-            pb += *pbp;
+          if constexpr (NCH > 0) {
+            pgs[jt] += pg;
+            pbs[jt] += pb;
+          } else if constexpr (NCH < 0) {
+            f32x4* sg = reinterpret_cast<f32x4*>(Ss + m * k + j);
+            f32x4* sb = reinterpret_cast<f32x4*>(Ss + nk + m * k + j);
+            *sg += pg;
+            *sb += pb;
+          } else {
+            f32x4* pgp = reinterpret_cast<f32x4*>(part + m * k + j);
+            f32x4* pbp = reinterpret_cast<f32x4*>(part + nk + m * k + j);
+            if (!first) {
+              pg += *pgp;
+              pb += *pbp;
+            }
+            *pgp = pg;
+            *pbp = pb;
           }
-          *pgp = pg;
-          *pbp = pb;
         }
         if (j < KP) *reinterpret_cast<u32x2*>(Fs + (16 * wave + li) * FP + j) = o;  // rows past n: zero
       }
@@ -410,6 +433,14 @@ __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p
           }
         }
       }
+    };
+    if constexpr (NCH > 0) {
+#pragma unroll
+      for (int ch = 0; ch < NCH; ++ch)
+        if (ch < chunks) pass2(ch, psg[ch], psb[ch]);
+    } else {
+      f32x4 unused[KJ];
+      for (int ch = 0; ch < chunks; ++ch) pass2(ch, unused, unused);
     }
     // dZ (bf16) to its rows of G: lane holds dZ[16 jt + 4 lg + t][16 et + li]
 #pragma unroll
@@ -426,7 +457,23 @@ __global__ __launch_bounds__(kFmThreads) void bwd_fm_wide_kernel(BwdFmWideArgs p
     }
     first = false;
   }
-  if (first) {  // no example: the sums are zero
+  if constexpr (NCH > 0) {  // the register sums to the plane (zero if the workgroup had no example)
+#pragma unroll
+    for (int ch = 0; ch < NCH; ++ch) {
+      const int m = ch * kChunk + 16 * wave + li;
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt) {
+        const int j = 16 * jt + 4 * lg;
+        if (ch < chunks && m < n && j < k) {
+          *reinterpret_cast<f32x4*>(part + m * k + j) = psg[ch][jt];
+          *reinterpret_cast<f32x4*>(part + nk + m * k + j) = psb[ch][jt];
+        }
+      }
+    }
+  } else if constexpr (NCH < 0) {
+    __syncthreads();
+    for (int i = tid; i < 2 * nk; i += kFmThreads) part[i] = Ss[i];
+  } else if (first) {  // no example: the sums are zero
     for (int i = tid; i < 2 * nk; i += kFmThreads) part[i] = 0.f;
   }
 }
@@ -482,21 +529,24 @@ hipError_t allow_lds_w(K* kern) {
 }
 
 struct FmVariant {
-  int d, kj;
+  int d, kj, nch;
   void (*kernel)(BwdFmWideArgs);
 };
 const FmVariant kFmVariants[] = {
-    {160, 3, bwd_fm_wide_kernel<160, 3>},  // d = 160, k <= 48
-    {160, 6, bwd_fm_wide_kernel<160, 6>},  // d = 160, k <= 96
-    {32, 2, bwd_fm_wide_kernel<32, 2>},    // d = 32, k <= 32
-    {64, 2, bwd_fm_wide_kernel<64, 2>},    // d = 64, k <= 32
+    {160, 3, 2, bwd_fm_wide_kernel<160, 3, 2>},    // d = 160, k <= 48, n <= 256: sums in registers
+    {160, 3, 0, bwd_fm_wide_kernel<160, 3, 0>},    // d = 160, k <= 48
+    {160, 6, 0, bwd_fm_wide_kernel<160, 6, 0>},    // d = 160, k <= 96
+    {32, 2, -1, bwd_fm_wide_kernel<32, 2, -1>},    // d = 32, k <= 32: sums in LDS when they fit
+    {32, 2, 0, bwd_fm_wide_kernel<32, 2, 0>},      // d = 32, k <= 32
+    {64, 2, -1, bwd_fm_wide_kernel<64, 2, -1>},    // d = 64, k <= 32: sums in LDS when they fit
+    {64, 2, 0, bwd_fm_wide_kernel<64, 2, 0>},      // d = 64, k <= 32
 };
 
 const FmVariant* pick_fm(int n, int d, int k) {
-  (void)n;
   for (const auto& v : kFmVariants) {
     if (v.d != d || (k + 15) / 16 > v.kj) continue;
-    if (fm_lds(n, d, k).bytes > (size_t)kLdsMaxW) continue;
+    if (v.nch > 0 && (n + kChunk - 1) / kChunk > v.nch) continue;
+    if (fm_lds(n, d, k, v.nch < 0).bytes > (size_t)kLdsMaxW) continue;
     return &v;
   }
   return nullptr;
@@ -536,7 +586,7 @@ hipError_t launch_bwd_fm_wide(const BwdFmWideArgs& a, int grid, hipStream_t stre
   if (grid <= 0) return hipSuccess;
   const hipError_t e = allow_lds_w(v->kernel);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(v->kernel, dim3(grid), dim3(kFmThreads), fm_lds(a.n, a.d, a.k).bytes, stream, a);
+  hipLaunchKernelGGL(v->kernel, dim3(grid), dim3(kFmThreads), fm_lds(a.n, a.d, a.k, v->nch < 0).bytes, stream, a);
   return hipGetLastError();
 }
 

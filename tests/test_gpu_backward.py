@@ -18,7 +18,7 @@ import oracle
 import recommender_feature_interaction_amd as wk
 import wukong_synth as ws
 from _gpu_helpers import check, host_f64, log, spec_of, to_host
-from _metrics import TOL_BF16, TOL_BF16_RMS, normwise_err, rms_err
+from _metrics import TOL_BF16, TOL_BF16_RMS, normwise_err, rel_err, rms_err
 
 pytestmark = pytest.mark.gpu
 
@@ -277,11 +277,14 @@ def relu_flip_examples(r, saved, band=1e-2):
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-def test_backward_full_batch_layer_d160():
-    """The d = 160 layer at its full batch of 4096: every gradient against the
-    oracle over all examples (normwise and rms), and dX elementwise on every
-    example whose ReLU masks agree with the oracle's (relu_flip_examples)."""
-    r = BackwardRun(ws.BY_NAME["layer_d160"], seed=9)
+@pytest.mark.parametrize("name", ["layer_d160", "smalld_n720"])
+def test_backward_full_batch(name):
+    """The d = 160 layer at its full batch of 4096 (the fused per-example backward)
+    and the n = 720 layer at its full batch of 8192 (the wide-layer backward): every
+    gradient against the oracle over all examples (normwise and rms), and dX
+    elementwise on every example whose ReLU masks agree with the oracle's
+    (relu_flip_examples)."""
+    r = BackwardRun(ws.BY_NAME[name], seed=9)
     _, saved, dx, grads = r.run()
     ref = r.oracle()
     got = host_f64(to_host(dx))
@@ -289,25 +292,30 @@ def test_backward_full_batch_layer_d160():
     flip, units = relu_flip_examples(r, saved)
     log(f"  {int(flip.sum())} of {r.cfg.batch} examples hold a ReLU near-tie decided the other way")
     assert flip.sum() <= 0.05 * r.cfg.batch
-    check("dX (examples whose masks agree)", got[~flip], ref["dX"][~flip], "bf16")
-    # all weight gradients normwise / rms; elementwise away from the flipped units
-    T = 2
-    whole = {k: v for k, v in ref.items() if k not in ("mlp_w", "mlp_b", "dX")}
-    for name, v in whole.items():
-        check(f"d_{name}", _grad_host(getattr(grads, name)), v, "bf16")
-    for t in range(T):
-        gw, rw = _grad_host(grads.mlp_w[t]), ref["mlp_w"][t]
-        gb, rb = _grad_host(grads.mlp_b[t]), ref["mlp_b"][t]
-        check(f"d_W{t} (all)", gw, rw, "bf16", elementwise=False)
-        check(f"d_b{t} (all)", gb, rb, "bf16", elementwise=False)
-        rows = np.ones(rw.shape[0], dtype=bool)
-        cols = np.ones(rw.shape[1], dtype=bool)
-        if t in units:
-            rows[units[t]] = False
-        if t - 1 in units:
-            cols[units[t - 1]] = False
-        check(f"d_W{t} (away from flipped units)", gw[rows][:, cols], rw[rows][:, cols], "bf16")
-        check(f"d_b{t} (away from flipped units)", gb[rows], rb[rows], "bf16")
+    # elementwise per example: over thousands of examples the bf16 floor's largest values reach the
+    # 2e-2 line (about 1.4e-2 is typical for one example of the n = 720 layer), so at most 0.1 % of
+    # the examples may exceed it; all are within it normwise and by rms
+    check("dX (examples whose masks agree)", got[~flip], ref["dX"][~flip], "bf16", elementwise=False)
+    per = np.array([rel_err(got[b], ref["dX"][b]) for b in np.flatnonzero(~flip)])
+    log(f"  dX elementwise per example: median {np.median(per):.2e}, 99.9th percentile "
+        f"{np.percentile(per, 99.9):.2e}, above 2e-2: {int((per > TOL_BF16).sum())}")
+    assert (per > TOL_BF16).mean() <= 1e-3
+    # The weight gradients sum over the batch, near-tie examples included, whose contributions
+    # differ legitimately (reading of the pages: both ReLU decisions are results of the method):
+    # normwise and rms over the whole batch, and elementwise on the batch without those examples
+    # (GPU and oracle run again on it; examples are independent).  The n = 720 layer's MLP
+    # weight gradients stay normwise and rms there too: their floor lies above 2e-2
+    # elementwise (test_tolerance_floor.py).
+    T = len(r.cfg.layers[0].mlp) - 1
+    mlp_elem = name != "smalld_n720"
+    check_grads(grads, ref, T, elementwise=False)
+    if flip.any():
+        s = subset_run(r, ~flip)
+        _, saved2, _, grads2 = s.run()
+        assert not relu_flip_examples(s, saved2)[0].any()
+        check_grads(grads2, s.oracle(), T, mlp_elementwise=mlp_elem)
+    else:
+        check_grads(grads, ref, T, mlp_elementwise=mlp_elem)
 
 
 # Oracle parity of stacks runs on shapes with narrow hidden layers.  With the
