@@ -307,13 +307,16 @@ int32_t wukong_moe_layer_forward_traced(const wk_moe_desc* desc, const wk_layer_
  *   dF     = LN backward of d_Fn over the n*k values of F
  *   dZ = dF^T X;  dX += dF Z + Phi^T dZ;  d_Phi = sum_b dZ X^T
  *   d_gamma / d_beta of both LayerNorms: sums of d(out) * normalised(in) / d(out)
- * bf16 only.  The forward's Fn, h_t and M come from wukong_layer_forward_train;
- * Lc, Z and F are recomputed from x.  Stored in bf16: dR (as dM and dLc),
- * every g_t, d_Fn, dF and dZ (as product operands) and dX; fp32 accumulation
- * and LayerNorm statistics; weight gradients are fp32.  Shapes: those of the
- * bf16 forward with d % 16 == 0, whose per-example working set fits one
- * workgroup's LDS (X, [Phi; W_L] and the operand panels; a c1-sized layer,
- * n = 128, d = 160, k = 32, n_l = 64, does), else WK_ERR_UNSUPPORTED. */
+ * bf16 only.  The forward's Fn, h_t and M come from wukong_layer_forward_train.
+ * Layers whose per-example working set fits one workgroup's LDS (X, [Phi; W_L]
+ * and the operand panels; the n = 128, d = 160, k = 32, n_l = 64 layer does)
+ * recompute Lc, Z and F from x.  Wider layers (n = 256 .. 768 where the
+ * streamed forward kernel takes the shape: the layers of the n = 256 and
+ * n = 512 stacks and the n = 720, d = 32 layer) also keep Z (bf16) and Lc
+ * (fp32) from the training forward and recompute only F.  Stored in bf16: dR
+ * (as dM and dLc), every g_t, d_Fn, dF and dZ (as product operands) and dX;
+ * fp32 accumulation and LayerNorm statistics; weight gradients are fp32.
+ * Other shapes, and d % 16 != 0: WK_ERR_UNSUPPORTED. */
 typedef struct {       /* device pointers, fp32, overwritten (not accumulated)  */
   float* phi;          /* [k, n]                                               */
   float* w_l;          /* [n_l, n]                                             */
@@ -327,14 +330,17 @@ typedef struct {       /* device pointers, fp32, overwritten (not accumulated)  
 
 /* Bytes of the activations wukong_layer_forward_train saves for the backward:
  * Fn [batch, n*k], h_t [batch, m_t] for t = 1..num_linear-1 and M
- * [batch, n_f*d], in that order, each at a 256-byte-aligned offset.  0 if desc
- * is invalid or the backward does not support it. */
+ * [batch, n_f*d], in that order, each at a 256-byte-aligned offset; for the
+ * wider layers (see wukong_layer_backward) also Z [batch, k, d] bf16 and Lc
+ * [batch, n_l, d] fp32 after them.  0 if desc is invalid or the backward does
+ * not support it. */
 size_t wukong_layer_saved_size(const wk_layer_desc* desc, int64_t batch);
 
-/* The forward of wukong_layer_forward that also keeps Fn, every h_t and M in
- * `saved` (device, saved_bytes >= wukong_layer_saved_size).  y equals the
- * plain forward's within bf16 rounding (M is rounded to bf16 before the
- * residual LayerNorm here).  x, y and saved must not overlap. */
+/* The forward of wukong_layer_forward that also keeps Fn, every h_t and M (and
+ * for the wider layers Z and Lc) in `saved` (device, saved_bytes >=
+ * wukong_layer_saved_size).  y equals the plain forward's within bf16
+ * rounding (M is rounded to bf16 before the residual LayerNorm here).  x, y
+ * and saved must not overlap. */
 int32_t wukong_layer_forward_train(const wk_layer_desc* desc, const wk_layer_weights* weights, int64_t batch,
                                    const void* x, void* y, void* saved, size_t saved_bytes, void* stream);
 
