@@ -26,8 +26,9 @@ d = 160 layer) are measured the same way in the same run and reported under
 "workloads"; the n = 720 layer's "memory_bound_kernels" gives the
 algorithmic bytes of FMB+LCB (and the residual LayerNorm where it runs) over
 their time.  The prediction head and WHALE's fusion step are timed on the
-headline's output; the fusion step, the training step (forward + backward)
-and the mixture-of-experts layer on the single-layer workloads.  None of
+headline's output; the training step (forward + backward of the layer or
+the whole stack) on every workload; the fusion step and the
+mixture-of-experts layer on the single-layer workloads.  None of
 these is part of `value`.  The CPU oracle is timed on a bounded sample of the
 headline workload on this host as a reference baseline (fp64, and the same
 steps in fp32).
@@ -215,53 +216,72 @@ def backward_accounting(B, s, wide=False):
     return out
 
 
-def measure_training(wk, ws, torch, cfg, layer, x, stream, steps, warmup, seed):
-    """One training step of a single bf16 layer: the forward that keeps Fn, h_t
-    and M, then the backward (dX and every weight gradient) for a seeded dY."""
-    if cfg.num_layers != 1 or cfg.dtype != "bf16":
+def measure_training(wk, ws, torch, cfg, layers, x, stream, steps, warmup, seed):
+    """One training step of a bf16 layer or stack: the forward that keeps what
+    the backward needs (every layer's input, Fn, h_t and M; Z and Lc for the
+    wider layers), then the backward (dX and every weight gradient) for a
+    seeded dY."""
+    if cfg.dtype != "bf16":
         return None
-    s = cfg.layers[0]
     B = cfg.batch
-    spec = layer.spec
-    need = wk.layer_backward_workspace_size(spec, B)
-    if need == 0:
+    specs = [l.spec for l in layers]
+    single = len(layers) == 1
+    if single:
+        need, saved_b = wk.layer_backward_workspace_size(specs[0], B), wk.layer_saved_size(specs[0], B)
+    else:
+        need, saved_b = wk.stack_backward_workspace_size(specs, B), wk.stack_saved_size(specs, B)
+    if need == 0 or saved_b == 0:
         return None
     dy = wk.to_device(ws.make_upstream_grad(cfg, seed), "bf16", x.device)
     y = torch.empty_like(x)
     dx = torch.empty_like(x)
-    saved = wk.alloc_workspace(wk.layer_saved_size(spec, B), x.device)
+    saved = wk.alloc_workspace(saved_b, x.device)
     bws = wk.alloc_workspace(need, x.device)
-    grads = wk.LayerGrads(layer)
+    grads = [wk.LayerGrads(l) for l in layers]
 
-    def step(trace=None):
-        wk.layer_forward_train(x, layer, y=y, saved=saved, stream=stream)
-        wk.layer_backward(x, saved, dy, layer, grads=grads, dx=dx, workspace=bws, stream=stream, trace=trace)
+    def forward():
+        if single:
+            wk.layer_forward_train(x, layers[0], y=y, saved=saved, stream=stream)
+        else:
+            wk.stack_forward_train(x, layers, y=y, saved=saved, stream=stream)
+
+    def backward(trace=None):
+        if single:
+            wk.layer_backward(x, saved, dy, layers[0], grads=grads[0], dx=dx, workspace=bws, stream=stream,
+                              trace=trace)
+        else:
+            wk.stack_backward(x, saved, dy, layers, grads=grads, dx=dx, workspace=bws, stream=stream, trace=trace)
 
     for _ in range(warmup):
-        step()
+        forward()
+        backward()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(steps):
-        step()
+        forward()
+        backward()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
     t0 = time.perf_counter()
     for _ in range(steps):
-        wk.layer_forward_train(x, layer, y=y, saved=saved, stream=stream)
+        forward()
     torch.cuda.synchronize()
     fwd_ms = (time.perf_counter() - t0) * 1e3 / steps
-    T = len(s.mlp) - 1
-    per = 5 * T + 16
+    per = sum(5 * (len(s.mlp) - 1) + 16 for s in cfg.layers)
     trace = wk.Trace(capacity=per * steps + 8)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     for _ in range(steps):
-        wk.layer_backward(x, saved, dy, layer, grads=grads, dx=dx, workspace=bws, stream=stream, trace=trace)
+        backward(trace)
     torch.cuda.synchronize()
     bwd_ms = (time.perf_counter() - t1) * 1e3 / steps
     recs = trace.records()
-    wide = any(r["kernel"] == "bwd_wgrad" and r["index"] == T for r in recs)
-    acct = backward_accounting(B, s, wide)
+    acct = {}
+    for i, s in enumerate(cfg.layers):
+        T = len(s.mlp) - 1
+        wide = any(r["kernel"] == "bwd_wgrad" and r["layer"] == i and r["index"] == T for r in recs)
+        for (kname, _, idx), v in backward_accounting(B, s, wide).items():
+            acct[(kname, i, idx)] = v
     kernels, dom = summarize_trace(recs, acct, bwd_ms, steps)
     trace.close()
     roof = None
@@ -275,7 +295,7 @@ def measure_training(wk, ws, torch, cfg, layer, x, stream, steps, warmup, seed):
             "model_tflops": round(3 * fwd_flops / (ms * 1e-3) / 1e12, 2),
             "kernel_tflops": round((fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12, 2),
             "roofline": roof,
-            "kernels": sorted(kernels, key=lambda k: (k["kernel"], k["index"]))}
+            "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"], k["index"]))}
 
 
 MOE_EXPERTS = 4  # experts of the measured mixture-of-experts layer
@@ -702,7 +722,7 @@ def measure_workload(wk, ws, torch, name, args, dev, stream, copy_gbps, mfma_pro
         res["fusion"] = optional_section("fusion", measure_fusion, wk, ws, torch, cfg, y, stream, args.steps,
                                          args.warmup, args.seed)
     if "training" in extras:
-        res["training"] = optional_section("training", measure_training, wk, ws, torch, cfg, layers[0], x, stream,
+        res["training"] = optional_section("training", measure_training, wk, ws, torch, cfg, layers, x, stream,
                                            args.steps, args.warmup, args.seed)
     if "moe" in extras and cfg.dtype == "bf16":
         res["moe"] = optional_section("moe", measure_moe, wk, ws, torch, cfg, x, stream, args.steps, args.warmup,
@@ -749,7 +769,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing")
     ap.add_argument("--no-fusion", action="store_true", help="skip the WHALE fusion-step measurement")
     ap.add_argument("--no-training", action="store_true",
-                    help="skip the single-layer training step (forward + backward) measurement")
+                    help="skip the training step (forward + backward of the layer or stack) measurement")
     ap.add_argument("--no-moe", action="store_true", help="skip the mixture-of-experts layer measurement")
     ap.add_argument("--only", choices=("fusion", "training", "moe"), default=None,
                     help="profiling aid: run the stack forward once, then time only this section and print it")
@@ -797,7 +817,7 @@ def main():
         elif args.only == "moe":
             res = measure_moe(wk, ws, torch, cfg, x, stream, args.steps, args.warmup, args.seed)
         else:
-            res = measure_training(wk, ws, torch, cfg, layers[0], x, stream, args.steps, args.warmup, args.seed)
+            res = measure_training(wk, ws, torch, cfg, layers, x, stream, args.steps, args.warmup, args.seed)
         print(json.dumps({"only": args.only, "config": {"workload": cfg.name, "global_batch": cfg.batch},
                           args.only: res}), flush=True)
         return
@@ -806,17 +826,18 @@ def main():
     mfma_probe = wk.probe_mfma_bf16()
     print(f"# copy {copy_gbps:.1f} GB/s, MFMA probe {mfma_probe:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
-    extras = [e for e, off in (("head", args.no_head), ("fusion", args.no_fusion)) if not off]
-    if ws.get(args.config).num_layers == 1:
-        extras += [e for e, off in (("training", args.no_training), ("moe", args.no_moe)) if not off]
+    extras = [e for e, off in (("head", args.no_head), ("fusion", args.no_fusion), ("training", args.no_training))
+              if not off]
+    if ws.get(args.config).num_layers == 1 and not args.no_moe:
+        extras.append("moe")
     head_res, host_w, x_host = measure_workload(wk, ws, torch, args.config, args, dev, stream, copy_gbps, mfma_probe,
                                                 extras)
     cfg = ws.get(args.config)
     sections = {}
     for name in [s for s in args.sections.split(",") if s and s != args.config]:
-        ex = ["fusion"] if not args.no_fusion else []
-        if ws.get(name).num_layers == 1:
-            ex += [e for e, off in (("training", args.no_training), ("moe", args.no_moe)) if not off]
+        ex = [e for e, off in (("fusion", args.no_fusion), ("training", args.no_training)) if not off]
+        if ws.get(name).num_layers == 1 and not args.no_moe:
+            ex.append("moe")
         sections[name] = optional_section(name, lambda n=name, e=ex: measure_workload(
             wk, ws, torch, n, args, dev, stream, copy_gbps, mfma_probe, e)[0])
 
