@@ -201,8 +201,9 @@ def backward_accounting(B, s, wide=False):
             ("bwd_transpose", 0, 3 * T + 2): {"flops": 0, "bytes": (kc * ldg + ldg * kcp) * 2},  # G^T
             ("bwd_wgrad", 0, T): {"flops": 2 * k * n * bd, "bytes": (k + n) * ldg * 2 + k * n * 4},  # d_Phi
             ("bwd_wgrad", 0, T + 1): {"flops": 2 * n_l * n * bd, "bytes": (n_l + n) * ldg * 2 + n_l * n * 4},
-            ("bwd_dgrad", 0, T): {"flops": 2 * n * kc * bd, "bytes": (ldg * kcp + n * kcp) * 2 + n * ldg * 4},
-            ("bwd_reduce", 0, 1): {"flops": 0, "bytes": B * n * d * (4 + 4 + 2)},  # dX = bf16(dXa + C)
+            # dX = bf16(dXa + [Phi; W_L]^T G): G^T and [Phi; W_L]^T in, dXa (fp32) in, dX out
+            ("bwd_dgrad", 0, T): {"flops": 2 * n * kc * bd,
+                                  "bytes": (ldg * kcp + n * kcp) * 2 + B * n * d * (4 + 2)},
         }
     out[("bwd_reduce", 0, 0)] = {"flops": 0, "bytes": 0}  # the LayerNorm and FMB / LCB weight sums
     for t, (a, b) in enumerate(zip(s.mlp[:-1], s.mlp[1:])):

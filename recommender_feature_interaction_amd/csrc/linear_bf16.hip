@@ -356,6 +356,45 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_splitk_kernel(LinearKAr
   }
 }
 
+// dX[b][m][e] = bf16(dXa[b][m][e] + C[m][b D + e]) with C = A W^T (M rows, N = B D
+// columns, batch-major): a product whose columns are (example, embedding) pairs,
+// added to an fp32 tensor of the example-major layout and stored in bf16.  The
+// wide-layer backward forms dX this way, without writing C.  A lane's 4
+// consecutive columns lie in one example (D % 4 == 0).
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void linear_dx_kernel(LinearKArgs p, const float* dxa, uint16_t* dx,
+                                                                 int D) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l16 = lane & 15, lg = lane >> 4;
+  int64_t m0;
+  int n0;
+  tile_origin(p.tiles_m, p.tiles_n, BM, BN, m0, n0);
+  const int64_t M = p.M;
+  const int N = p.N;
+  f32x4 acc[NB][MB];
+  dma_mainloop<BM, BN, WGM, WGN, false>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int n = n0 + wn * WTN + i * 16 + lg * 4;
+    const int b = n / D, e = n - b * D;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int64_t m = m0 + wm * WTM + j * 16 + l16;
+      if (m < M && n < N) {
+        const int64_t o = ((int64_t)b * M + m) * D + e;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(dxa + o);
+        const f32x4 v = acc[i][j];
+        *reinterpret_cast<u32x2*>(dx + o) =
+            u32x2{pack_bf16x2(v[0] + a[0], v[1] + a[1]), pack_bf16x2(v[2] + a[2], v[3] + a[3])};
+      }
+    }
+  }
+}
+
 // C = bf16(act(sum_s part[s] + bias) + res), 8 consecutive columns per thread (N % 8 == 0).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int splits, int64_t M, int N,
                                                             const uint16_t* bias, int act, const uint16_t* res,
@@ -943,6 +982,33 @@ hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t 
   if (workgroups) *workgroups = blocks;
   hipLaunchKernelGGL((linear_splitk_kernel<256, 256, 2, 4, false>), dim3((unsigned)blocks), dim3(512), 0, stream, k, c,
                      1);
+  return hipGetLastError();
+}
+
+bool linear_bf16_dx_supported(int64_t M, int N, int K, int D) {
+  return M > 0 && N > 0 && K > 0 && K % kBK == 0 && D > 0 && D % 4 == 0 && N % D == 0;
+}
+
+hipError_t launch_linear_bf16_dx(const LinearArgs& a, const float* dxa, void* dx, int D, hipStream_t stream,
+                                 int64_t* workgroups) {
+  if (!linear_bf16_dx_supported(a.M, a.N, a.K, D) || dxa == nullptr || dx == nullptr) return hipErrorInvalidValue;
+  LinearKArgs k;
+  k.a = static_cast<const uint16_t*>(a.a);
+  k.w = static_cast<const uint16_t*>(a.w);
+  k.bias = nullptr;
+  k.c = nullptr;
+  k.M = a.M;
+  k.N = a.N;
+  k.K = a.K;
+  k.act = kActNone;
+  k.res = nullptr;
+  k.tiles_m = (int)((a.M + 255) / 256);
+  k.tiles_n = (a.N + 255) / 256;
+  const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (workgroups) *workgroups = blocks;
+  hipLaunchKernelGGL((linear_dx_kernel<256, 256, 2, 4>), dim3((unsigned)blocks), dim3(512), 0, stream, k, dxa,
+                     static_cast<uint16_t*>(dx), D);
   return hipGetLastError();
 }
 

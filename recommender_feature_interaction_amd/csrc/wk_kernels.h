@@ -115,6 +115,11 @@ hipError_t launch_linear_bf16_splitk(const LinearArgs& a, float* partial, hipStr
 // C = A W^T in fp32 (no bias, no activation), K % 64 == 0, N % 8 == 0.
 bool linear_bf16_f32out_supported(int64_t M, int N, int K);
 hipError_t launch_linear_bf16_f32out(const LinearArgs& a, float* c, hipStream_t stream, int64_t* workgroups);
+// dX[b][m][e] = bf16(dXa[b][m][e] + C[m][b D + e]) for C = A W^T on 256 x 256 tiles
+// (C's columns are (example, embedding) pairs; K % 64 == 0, D % 4 == 0, N % D == 0).
+bool linear_bf16_dx_supported(int64_t M, int N, int K, int D);
+hipError_t launch_linear_bf16_dx(const LinearArgs& a, const float* dxa, void* dx, int D, hipStream_t stream,
+                                 int64_t* workgroups);
 // The same with K split when the tiles leave CUs idle: the fp32 partials
 // (linear_bf16_f32out_split_bytes(), 0 when unsplit) are summed in split order.
 int linear_bf16_f32out_splits(int64_t M, int N, int K);
@@ -254,9 +259,6 @@ hipError_t launch_bwd_fm_wide(const BwdFmWideArgs& a, int grid, hipStream_t stre
 hipError_t launch_to_batch_major(const void* src, int64_t batch, int R, int D, int64_t ld, void* dst,
                                  hipStream_t stream);
 hipError_t launch_zero_cols(void* p, int R, int64_t ld, int64_t c0, hipStream_t stream);
-// dX[b][j][e] = bf16(dXa[b][j][e] + C[j][b D + e])
-hipError_t launch_dx_final(const float* dxa, const float* c, int64_t ldc, int64_t batch, int n, int D, void* dx,
-                           hipStream_t stream, int64_t* workgroups);
 // The fp32-output product split along K into as many as max_splits parts (summed in split order).
 int linear_bf16_f32out_splits_max(int64_t M, int N, int K, int max_splits);
 size_t linear_bf16_f32out_split_bytes_max(int64_t M, int N, int K, int max_splits);

@@ -690,11 +690,11 @@ struct BackwardPlan {
   size_t dm = 0, dlc = 0, g[2] = {0, 0}, dfn = 0, gt = 0, at = 0, wt = 0, colpart = 0, split = 0, part_out = 0,
          part_fmb = 0, bytes = 0;
   // wide layers: G = [dZ; dLc] batch-major [kc, ldg], its transpose [ldg, kcp], X batch-major
-  // [n, ldg], [Phi; W_L] and its transpose, dR + dF Z (fp32), C = [Phi; W_L]^T G (fp32), split partials
+  // [n, ldg], [Phi; W_L] and its transpose, dR + dF Z (fp32), split partials
   bool wide = false;
   int64_t ldg = 0;
   int kc = 0, kcp = 0;
-  size_t gm = 0, gmt = 0, xb = 0, wcat = 0, wcatt = 0, dxa = 0, cm = 0, wsplit = 0;
+  size_t gm = 0, gmt = 0, xb = 0, wcat = 0, wcatt = 0, dxa = 0, wsplit = 0;
 };
 constexpr int kWideWgradSplits = 256;
 
@@ -743,7 +743,6 @@ BackwardPlan plan_backward(const wk_layer_desc& d, int64_t batch) {
     p.wcat = take((size_t)p.kc * d.n * 2);
     p.wcatt = take((size_t)d.n * p.kcp * 2);
     p.dxa = take(B * d.n * d.d * 4);
-    p.cm = take((size_t)d.n * L * 4);
     const size_t s1 = wk::linear_bf16_f32out_split_bytes_max(d.k, d.n, (int)p.ldg, kWideWgradSplits);
     const size_t s2 = wk::linear_bf16_f32out_split_bytes_max(d.n_l, d.n, (int)p.ldg, kWideWgradSplits);
     p.wsplit = take(s1 > s2 ? s1 : s2);
@@ -880,11 +879,11 @@ int32_t layer_backward_wide(const wk_layer_desc* d, const wk_layer_weights* w, i
   ca.N = (int)L;
   ca.K = bp.kcp;
   ca.act = wk::kActNone;
-  float* cm = reinterpret_cast<float*>(base + bp.cm);
-  st = launch(WK_KERNEL_BWD_DGRAD, layer_idx, T, [&](int64_t* g) { return wk::launch_linear_bf16_f32out(ca, cm, s, g); });
-  if (st != WK_OK) return st;
-  st = launch(WK_KERNEL_BWD_REDUCE, layer_idx, 1, [&](int64_t* g) {
-    return wk::launch_dx_final(reinterpret_cast<const float*>(base + bp.dxa), cm, L, batch, n, D, dx, s, g);
+  // dX = bf16(dR + dF Z + [Phi; W_L]^T G): the product's epilogue adds the fp32 sum
+  // of the other terms and stores dX (its columns past B d, the padding of G, are dropped)
+  ca.N = (int)(batch * D);
+  st = launch(WK_KERNEL_BWD_DGRAD, layer_idx, T, [&](int64_t* g) {
+    return wk::launch_linear_bf16_dx(ca, reinterpret_cast<const float*>(base + bp.dxa), dx, D, s, g);
   });
   if (st != WK_OK) return st;
   const int64_t nk = (int64_t)n * k;

@@ -19,8 +19,8 @@
 //    and dXa = dR + dF Z (fp32); per-workgroup sums of d_Fn F_hat and d_Fn
 //    (gamma_fm / beta_fm).
 //  Then, on the GEMM kernels: d[Phi; W_L] = G X'^T with X' the batch-major
-//  copy of X (split along the batch), and C = [Phi; W_L]^T G, from which
-//  dx_final_kernel forms dX = bf16(dXa + C) (C is batch-major as well).
+//  copy of X (split along the batch), and C = [Phi; W_L]^T G, whose epilogue
+//  forms dX = bf16(dXa + C) (C's columns are (example, embedding) pairs).
 #include "wk_device.h"
 #include "wk_kernels.h"
 
@@ -507,22 +507,6 @@ __global__ __launch_bounds__(256) void zero_cols_kernel(uint16_t* p, int R, int6
   }
 }
 
-// dX[b][j][e] = bf16(dXa[b][j][e] + C[j][b D + e]), 4 elements per thread
-__global__ __launch_bounds__(256) void dx_final_kernel(const float* dxa, const float* c, int64_t ldc, int64_t batch,
-                                                      int n, int D, uint16_t* dx) {
-  const int64_t total = batch * n * D / 4;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
-    const int64_t i = q * 4;
-    const int64_t row = i / D;
-    const int e = (int)(i - row * D);
-    const int64_t b = row / n;
-    const int j = (int)(row - b * n);
-    const f32x4 a = *reinterpret_cast<const f32x4*>(dxa + i);
-    const f32x4 g = *reinterpret_cast<const f32x4*>(c + (int64_t)j * ldc + b * D + e);
-    *reinterpret_cast<u32x2*>(dx + i) = u32x2{pack_bf16x2(a[0] + g[0], a[1] + g[1]), pack_bf16x2(a[2] + g[2], a[3] + g[3])};
-  }
-}
-
 template <class K>
 hipError_t allow_lds_w(K* kern) {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMaxW);
@@ -610,16 +594,5 @@ hipError_t launch_zero_cols(void* p, int R, int64_t ld, int64_t c0, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_dx_final(const float* dxa, const float* c, int64_t ldc, int64_t batch, int n, int D, void* dx,
-                           hipStream_t stream, int64_t* workgroups) {
-  if (D % 4) return hipErrorInvalidValue;
-  int64_t grid = (batch * n * D / 4 + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  if (workgroups) *workgroups = grid;
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL(dx_final_kernel, dim3((unsigned)grid), dim3(256), 0, stream, dxa, c, ldc, batch, n, D,
-                     static_cast<uint16_t*>(dx));
-  return hipGetLastError();
-}
 
 }  // namespace wk
