@@ -68,10 +68,10 @@ KERNEL_SOURCES = {
     "fusion_linear": ("linear_bf16.hip",),
     "fusion_ln": ("whale_fusion.hip",),
     "fusion_ffn": ("whale_fusion.hip",),
-    "bwd_out": ("wukong_backward.hip",),
-    "bwd_fmb": ("wukong_backward.hip",),
-    "bwd_transpose": ("wukong_backward.hip",),
-    "bwd_reduce": ("wukong_backward.hip",),
+    "bwd_out": ("wukong_backward.hip", "wukong_backward_wide.hip"),
+    "bwd_fmb": ("wukong_backward.hip", "wukong_backward_wide.hip"),
+    "bwd_transpose": ("wukong_backward.hip", "wukong_backward_wide.hip"),
+    "bwd_reduce": ("wukong_backward.hip", "wukong_backward_wide.hip"),
     "bwd_wgrad": ("linear_bf16.hip",),
     "bwd_dgrad": ("linear_bf16.hip",),
 }
@@ -277,6 +277,8 @@ def measure_training(wk, ws, torch, cfg, layers, x, stream, steps, warmup, seed)
     torch.cuda.synchronize()
     bwd_ms = (time.perf_counter() - t1) * 1e3 / steps
     recs = trace.records()
+    per_step = len(recs) // steps if steps else 0
+    launch_order = [[r["kernel"], r["layer"], r["index"]] for r in recs[:per_step]]
     acct = {}
     for i, s in enumerate(cfg.layers):
         T = len(s.mlp) - 1
@@ -296,7 +298,8 @@ def measure_training(wk, ws, torch, cfg, layers, x, stream, steps, warmup, seed)
             "model_tflops": round(3 * fwd_flops / (ms * 1e-3) / 1e12, 2),
             "kernel_tflops": round((fwd_flops + bwd_flops) / (ms * 1e-3) / 1e12, 2),
             "roofline": roof,
-            "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"], k["index"]))}
+            "kernels": sorted(kernels, key=lambda k: (k["layer"], k["kernel"], k["index"])),
+            "backward_launch_order": launch_order}
 
 
 MOE_EXPERTS = 4  # experts of the measured mixture-of-experts layer
@@ -725,6 +728,8 @@ def measure_workload(wk, ws, torch, name, args, dev, stream, copy_gbps, mfma_pro
     if "training" in extras:
         res["training"] = optional_section("training", measure_training, wk, ws, torch, cfg, layers, x, stream,
                                            args.steps, args.warmup, args.seed)
+        if isinstance(res["training"], dict):
+            res["training"].pop("backward_launch_order", None)  # for profiling runs (--only training) only
     if "moe" in extras and cfg.dtype == "bf16":
         res["moe"] = optional_section("moe", measure_moe, wk, ws, torch, cfg, x, stream, args.steps, args.warmup,
                                       args.seed)
