@@ -105,7 +105,10 @@ int32_t wukong_abi_version(void);
 const char* wukong_status_string(int32_t status);
 
 /* Bytes of device workspace wukong_layer_forward needs for `batch`
- * examples, or 0 if desc is invalid or unsupported. */
+ * examples, or 0 if desc is invalid or unsupported.  Besides the
+ * intermediates it holds, for the wider bf16 layers (n of 256 and more), a
+ * copy of [Phi; W_L] rearranged into the tile order the FMB+LCB kernel
+ * streams, rewritten at every call. */
 size_t wukong_layer_workspace_size(const wk_layer_desc* desc, int64_t batch);
 
 /* One Wukong layer: y[b] = layer(x[b]) for b < batch.
@@ -332,8 +335,9 @@ typedef struct {       /* device pointers, fp32, overwritten (not accumulated)  
  * Fn [batch, n*k], h_t [batch, m_t] for t = 1..num_linear-1 and M
  * [batch, n_f*d], in that order, each at a 256-byte-aligned offset; for the
  * wider layers (see wukong_layer_backward) also Z [batch, k, d] bf16 and Lc
- * [batch, n_l, d] fp32 after them.  0 if desc is invalid or the backward does
- * not support it. */
+ * [batch, n_l, d] fp32 after them, and last the scratch copy of [Phi; W_L]
+ * the FMB+LCB kernel streams (not an activation; rewritten by each training
+ * forward).  0 if desc is invalid or the backward does not support it. */
 size_t wukong_layer_saved_size(const wk_layer_desc* desc, int64_t batch);
 
 /* The forward of wukong_layer_forward that also keeps Fn, every h_t and M (and

@@ -783,6 +783,13 @@ bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l) {
          pick(n, d, k, n_l) != nullptr;
 }
 
+size_t fmb_lcb_bf16_pack_bytes(int n, int d, int k, int n_l, bool train) {
+  // the same choice as launch_fmb_lcb_bf16: only the streamed kernel reads packed weights
+  const ResidentVariant* res = pick_resident(n, d, k, n_l);
+  if (train || !(res && res->wl)) return fmb_lcb_stream_pack_bytes(n, d, k, n_l);
+  return 0;
+}
+
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups) {
   // Order: the resident kernel when [Phi; W_L] fits in its LDS next to X (the

@@ -12,8 +12,10 @@
 // copied global -> LDS by buffer_load ... lds into a ring of S slots (3 or
 // 4), S - 1 steps ahead, so the weights are read once per E examples and the
 // HBM stream of X runs ahead of the MFMAs.  Phi occupies the first ceil(k/16)
-// 16-row tiles and W_L the following ones (a tile never mixes the two, so a
-// DMA instruction has one source; the padding rows read as zero).  The
+// 16-row tiles and W_L the following ones.  A pack kernel first rearranges
+// [Phi; W_L] into the ring's own order (step, tile, 16 rows x 32 columns,
+// zero padded), so each weight DMA instruction copies 1 KB of consecutive
+// bytes instead of 16 row pieces of 64 bytes (half an L2 line each).  The
 // MFMA computes the transposed tile [Z; Lc]^T = X^T [Phi; W_L]^T: the X^T
 // operand comes from the row-major X rows with ds_read_b64_tr_b16 (in each
 // 16-lane group, lane i receives value i%4 of the 8-byte rows addressed by
@@ -55,6 +57,7 @@ constexpr int vm_enc(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4)
 
 struct StreamShape {
   int zt;    // 16-row tiles of [Phi; W_L]: kz + ceil(n_l / 16)
+  int ztp;   // weight tiles per step in the packed weights and in a ring slot (the variant's ZTMAX >= zt)
   int kz;    // tiles holding Phi: ceil(k / 16)
   int steps; // ceil(n / KC)
   int e;     // examples per group
@@ -77,20 +80,23 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
   constexpr int DZ = (D + 31) / 32 * 32;
   constexpr int NKS = DZ / 32;                 // 32-wide K steps of phase 2
   constexpr bool GB_REG = MPW * KJ <= 12;      // FMB LayerNorm gamma / beta held in registers
-  // DMA instructions per step: ZTP = ZTMAX 16-row weight tiles (tiles past the
-  // shape's ZT read as zero) and X_INS for the X rows (1 KB each), dealt round
-  // robin: waves below R issue INS_HI per step, the others INS_LO, so every
-  // counter wait is a compile-time constant.
+  // DMA instructions per step: ZTP = ZTMAX 16-row weight tiles of 1 KB (the
+  // packed weights hold ZTP tiles per step; those past the shape's ZT are
+  // zero) and X_INS for the X rows (1 KB each).  Weight tile i = 8 q + wave
+  // goes out in round q, then X instruction j = 8 q + wave: every wave issues
+  // the same code, and only the last round of each kind is partial (waves
+  // below RW, RX).  A wave's copies per step are C0 + (wave < RW) + (wave < RX).
   constexpr int X_INS = E * D / 16;
   constexpr int ZTP = ZTMAX;  // >= the shape's ZT (host check); may exceed WZ * ZPW (padding tiles)
-  constexpr int NINS = ZTP + X_INS;
-  constexpr int INS_HI = (NINS + NWAVE - 1) / NWAVE, INS_LO = NINS / NWAVE, R = NINS % NWAVE;
+  constexpr int WQ = (ZTP + NWAVE - 1) / NWAVE, XQ = (X_INS + NWAVE - 1) / NWAVE;
+  constexpr int RW = ZTP % NWAVE, RX = X_INS % NWAVE;
+  constexpr int C0 = ZTP / NWAVE + X_INS / NWAVE;
   constexpr int SW = ZTP * 16 * KC;       // weight part of a ring slot (u16)
   constexpr int SX = E * KC * D;          // X part of a ring slot
   static_assert(WZ * WE == NWAVE, "8 waves");
   static_assert(S == 3 || S == 4, "ring of 3 or 4 slots");
   static_assert(GUARD || ZTMAX >= WZ * ZPW, "unguarded tiles must lie in the slot");
-  static_assert(2 * ((ZTMAX + WE * EPW * ET + NWAVE - 1) / NWAVE) <= 63, "vmcnt range");
+  static_assert(2 * (WQ + XQ) <= 63, "vmcnt range");
   // The ring slots are separate objects: the compiler then knows a DMA into
   // one slot does not alias reads of another and inserts no wait for it.
   __shared__ __align__(16) uint16_t w0[SW], w1[SW], w2[SW], w3[S > 3 ? SW : 8];
@@ -119,12 +125,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
     Zs[(size_t)row * ZP + D + c] = 0;
   }
 
-  // ---- DMA issue: instruction i of a step goes to wave i % 8; 0 .. ZTP-1 are
-  // weight tiles, the rest X rows.
-  const __amdgpu_buffer_rsrc_t rphi =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.phi, (short)0, k * n * 2, 0x00020000);
-  const __amdgpu_buffer_rsrc_t rwl =
-      __builtin_amdgcn_make_buffer_rsrc((void*)p.w_l, (short)0, n_l * n * 2, 0x00020000);
+  // ---- DMA issue.  The packed weights: step t, tile i at byte (t ZTP + i) 1024.
+  const __amdgpu_buffer_rsrc_t rpk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.wpack, (short)0, STEPS * ZTP * 1024, 0x00020000);
+  const bool ragged = n % KC != 0;  // the last step has rows past n, which read as zero
   auto dma_step = [&](const __amdgpu_buffer_rsrc_t& rx, uint16_t* sw, uint16_t* sx, int step) {
     const int k0 = step * KC;
     // The lane's offsets are recomputed at every step (a few VALU operations)
@@ -133,32 +137,39 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
     // vector-memory counter would also wait for the DMA in flight.
     int lane = lane_id;
     asm volatile("" : "+v"(lane));
+    const uint32_t l16 = (uint32_t)lane * 16u;
 #pragma unroll
-    for (int q = 0; q < INS_HI; ++q) {
-      const int i = wave + q * NWAVE;  // wave-uniform
-      if (i >= NINS) break;
-      if (i < ZTP) {
-        // weight tile i: row z = 16 i + lane / 4, columns k0 + 8 (lane % 4) .. + 7
-        const int col = k0 + 8 * (lane & 3);
-        const int r = 16 * i + (lane >> 2);
-        uint16_t* dst = sw + i * 16 * KC;
-        if (i < KZ) {
-          const uint32_t vo = (r < k && col < n) ? (uint32_t)(r * n + col) * 2u : kOOB;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rphi, WK_LDSV(dst), 16, vo, 0, 0, 0);
-        } else {
-          const int rl = r - 16 * KZ;
-          const uint32_t vo = (rl < n_l && col < n) ? (uint32_t)(rl * n + col) * 2u : kOOB;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rwl, WK_LDSV(dst), 16, vo, 0, 0, 0);
-        }
-      } else {
-        const int j = i - ZTP;
-        const int ex = j / (D / 16), bb = j - ex * (D / 16);
-        const int o = bb * 512 + lane * 8;  // element offset within the example's KC x D rows
-        const int row = o / D, col = o - row * D;
-        uint16_t* dst = sx + ex * KC * D + bb * 512;
-        const uint32_t vo = (k0 + row < n) ? (uint32_t)(((ex * n) + k0 + row) * D + col) * 2u : kOOB;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, WK_LDSV(dst), 16, vo, 0, 0, 0);
-      }
+    for (int q = 0; q < WQ; ++q) {
+      const int i = q * NWAVE + wave;  // wave-uniform
+      if (RW != 0 && q == WQ - 1 && i >= ZTP) break;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rpk, WK_LDSV(sw + i * 16 * KC), 16,
+                                               l16 + (uint32_t)((step * ZTP + i) * 1024), 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < XQ; ++q) {
+      const int j = q * NWAVE + wave;  // wave-uniform
+      if (RX != 0 && q == XQ - 1 && j >= X_INS) break;
+      const int ex = j / (D / 16), bb = j - ex * (D / 16);
+      // elements bb 512 + 8 lane .. + 7 of the example's KC x D block of rows k0 ..
+      uint32_t vo = l16 + (uint32_t)(((ex * n + k0) * D + bb * 512) * 2);
+      if (ragged && k0 + KC > n && k0 + (bb * 512 + lane * 8) / D >= n) vo = kOOB;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, WK_LDSV(sx + ex * KC * D + bb * 512), 16, vo, 0, 0, 0);
+    }
+  };
+  // wait until this wave's copies of a step have landed while the `newer` (0 .. 2)
+  // steps issued after it may still be in flight
+  const int extra = (wave < RW ? 1 : 0) + (wave < RX ? 1 : 0);  // wave-uniform
+  auto wait_copies = [&](int newer) {
+    if (newer <= 0) {
+      __builtin_amdgcn_s_waitcnt(vm_enc(0));
+    } else if (newer == 1) {
+      if (extra == 0) __builtin_amdgcn_s_waitcnt(vm_enc(C0));
+      else if (extra == 1) __builtin_amdgcn_s_waitcnt(vm_enc(C0 + 1));
+      else __builtin_amdgcn_s_waitcnt(vm_enc(C0 + 2));
+    } else {
+      if (extra == 0) __builtin_amdgcn_s_waitcnt(vm_enc(2 * C0));
+      else if (extra == 1) __builtin_amdgcn_s_waitcnt(vm_enc(2 * C0 + 2));
+      else __builtin_amdgcn_s_waitcnt(vm_enc(2 * C0 + 4));
     }
   };
   // per-group buffer resources: byte offsets stay 32-bit (one VGPR each) and
@@ -238,17 +249,8 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
     // step t reads slot t % S and sends step t + S - 1 to slot (t + S - 1) % S
     auto step = [&](const uint16_t* sw, const uint16_t* sx, uint16_t* nw, uint16_t* nx, int t) {
       // step t must have landed; the (up to S - 2) steps issued after it may still be in flight
-      const int newer = (STEPS - 1 - t < S - 2) ? STEPS - 1 - t : S - 2;
-      if (newer <= 0) {
-        __builtin_amdgcn_s_waitcnt(vm_enc(0));
-      } else if (S > 3 && newer >= 2) {
-        if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_HI));
-        else __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_LO));
-      } else {
-        if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(INS_HI));
-        else __builtin_amdgcn_s_waitcnt(vm_enc(INS_LO));
-      }
-      lds_barrier();
+      wait_copies((STEPS - 1 - t < S - 2) ? STEPS - 1 - t : S - 2);
+      ring_barrier();
       if (t + S - 1 < STEPS) dma_step(rx, nw, nx, t + S - 1);
       if constexpr (GUARD) {
         // the step's X^T operands first, then one uniform test per weight tile
@@ -521,6 +523,34 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
 }
 
 
+// [Phi; W_L] in the ring's order: 16-byte chunk c = (t ZTP + i) 64 + l holds
+// row 16 i + l / 4 of [Phi (padded to KZ tiles); W_L], columns 32 t + 8 (l % 4)
+// .. + 7, zero outside the matrices and in the tiles past ZT.
+__global__ __launch_bounds__(256) void pack_stream_weights_kernel(const uint16_t* __restrict__ phi,
+                                                                  const uint16_t* __restrict__ w_l,
+                                                                  uint16_t* __restrict__ out, int n, int k, int n_l,
+                                                                  int kz, int zt, int ztp, int steps) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= steps * ztp * 64) return;
+  const int l = c & 63, ti = c >> 6;
+  const int i = ti % ztp, t = ti / ztp;
+  const int r = 16 * i + (l >> 2), col = KC * t + 8 * (l & 3);
+  const uint16_t* src = phi;
+  int row = r, rows = k;
+  if (i >= kz) {
+    src = w_l;
+    row = r - 16 * kz;
+    rows = i < zt ? n_l : 0;  // tiles past zt: zero padding
+  }
+  uint16_t v[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (row < rows && col + e < n) ? src[(int64_t)row * n + col + e] : (uint16_t)0;
+  u32x4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (uint32_t)v[2 * e] | ((uint32_t)v[2 * e + 1] << 16);
+  *reinterpret_cast<u32x4*>(out + (int64_t)c * 8) = o;
+}
+
 struct StreamVariant {
   int et, zpw, wz, we, epw, mpw, kj, ztmax, s;
   void (*kernel)(FmbLcbArgs, int64_t, StreamShape);
@@ -547,6 +577,7 @@ StreamShape stream_shape(const StreamVariant& v, int n, int k, int n_l) {
   sh.zt = sh.kz + (n_l + 15) / 16;
   sh.steps = (n + KC - 1) / KC;
   sh.e = v.we * v.epw;
+  sh.ztp = v.ztmax;
   return sh;
 }
 
@@ -571,6 +602,12 @@ const StreamVariant* pick_stream(int n, int d, int k, int n_l, StreamShape* out)
 
 bool fmb_lcb_stream_supported(int n, int d, int k, int n_l) { return pick_stream(n, d, k, n_l, nullptr) != nullptr; }
 
+size_t fmb_lcb_stream_pack_bytes(int n, int d, int k, int n_l) {
+  StreamShape sh;
+  if (!pick_stream(n, d, k, n_l, &sh)) return 0;
+  return (size_t)sh.steps * sh.ztp * 1024;
+}
+
 hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t stream, int64_t* workgroups) {
   StreamShape sh;
   const StreamVariant* v = pick_stream(a.n, a.d, a.k, a.n_l, &sh);
@@ -579,7 +616,11 @@ hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t
   const int64_t grid = groups < 256 ? groups : 256;
   if (workgroups) *workgroups = grid;
   if ((a.z_out == nullptr) != (a.lc_out == nullptr)) return hipErrorInvalidValue;
+  if (a.wpack == nullptr || (reinterpret_cast<uintptr_t>(a.wpack) & 15) != 0) return hipErrorInvalidValue;
   if (batch == 0) return hipSuccess;
+  const int chunks = sh.steps * sh.ztp * 64;
+  hipLaunchKernelGGL(pack_stream_weights_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a.phi,
+                     a.w_l, a.wpack, a.n, a.k, a.n_l, sh.kz, sh.zt, sh.ztp, sh.steps);
   hipLaunchKernelGGL(a.z_out ? v->kernel_train : v->kernel, dim3((unsigned)grid), dim3(NTHREAD), 0, stream, a, batch,
                      sh);
   return hipGetLastError();

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(AW * 64, 2) void whale_attention_kernel(AttnArgs p)
       if (wave < R) __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_HI));
       else __builtin_amdgcn_s_waitcnt(vm_enc(2 * INS_LO));
     }
-    lds_barrier();
+    ring_barrier();  // not lds_barrier: its fence would also wait for the two newer steps' DMA
     if (t + 3 < TT) dma(next, t + 3);
   };
   auto step = [&](const uint16_t* kt, uint16_t* next, int t) {
@@ -568,7 +568,7 @@ __global__ __launch_bounds__(W * 64) void fusion_ffn_kernel(FfnKArgs p) {
     } else {
       __builtin_amdgcn_s_waitcnt(vm_enc(0));
     }
-    lds_barrier();
+    ring_barrier();  // not lds_barrier: its fence would also wait for chunk c + 2's DMA
   };
   for (int c = 0; c < NC; c += 3) {
     chunk(wu0, wd0, wu2, wd2, c);

@@ -106,4 +106,14 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Workgroup barrier of an LDS ring filled by LDS DMA (buffer_load ... lds).
+// The DMA writes count as outstanding LDS writes, so a release fence on LDS
+// (lds_barrier) makes the compiler wait for every DMA in flight (vmcnt(0)),
+// prefetches of later slots included, and the ring drains at every step.  The
+// callers wait for their own DMAs of the slot about to be read with an explicit
+// vmcnt count first; this barrier waits only for the wave's LDS operations
+// (lgkmcnt(0)).  The asm's memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void ring_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 }  // namespace wk

@@ -23,6 +23,9 @@ struct FmbLcbArgs {
   // training forward of the wide layers (streamed kernel only; both or neither):
   uint16_t* z_out = nullptr;  // [B, k, d] Z = bf16(Phi X), as the interaction uses it
   float* lc_out = nullptr;    // [B, n_l, d] Lc = W_L X in fp32, as the LCB rows' LayerNorm uses it
+  // scratch for [Phi; W_L] rearranged into the streamed kernel's 1 KB step tiles
+  // (fmb_lcb_bf16_pack_bytes(); needed when that is non-zero)
+  uint16_t* wpack = nullptr;
 };
 bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l);
 // Streamed variant (fmb_lcb_stream.hip): several examples per workgroup, the
@@ -30,6 +33,10 @@ bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l);
 // the shape.
 bool fmb_lcb_stream_supported(int n, int d, int k, int n_l);
 hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t stream, int64_t* workgroups);
+// Bytes of the rearranged weights the streamed kernel reads (0 when the shape takes another kernel).
+size_t fmb_lcb_stream_pack_bytes(int n, int d, int k, int n_l);
+// Scratch (FmbLcbArgs::wpack) launch_fmb_lcb_bf16 needs for this shape; train: the Z / Lc outputs are set.
+size_t fmb_lcb_bf16_pack_bytes(int n, int d, int k, int n_l, bool train);
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups);
 // WHALE fusion step (whale_fusion.hip): shared K = V cross-attention followed

@@ -76,7 +76,7 @@ int32_t check_desc(const wk_layer_desc* d, bool expert = false) {
 }
 
 struct LayerPlan {
-  size_t fn = 0, h[2] = {0, 0}, m = 0, units = 0, bytes = 0;
+  size_t fn = 0, h[2] = {0, 0}, m = 0, units = 0, wpack = 0, bytes = 0;
   int num_hidden_bufs = 0;
   bool keep_hidden = false;  // h_{t+1} goes to hid[t] (the training forward keeps them all)
   size_t hid[kMaxLinear] = {};
@@ -124,6 +124,13 @@ LayerPlan plan_layer(const wk_layer_desc& d, int64_t batch) {
   if (p.use_units) {  // transposed X, [Phi; W_L], fp32 [Z; Lc] (dead once Fn and the LCB rows are written)
     p.units = off;
     off += align_up(wk::fmb_lcb_units_workspace(batch, d.n, d.k, d.n_l));
+  }
+  if (d.dtype == WK_BF16 && !p.use_units) {  // [Phi; W_L] in the streamed kernel's tile order
+    const size_t pk = wk::fmb_lcb_bf16_pack_bytes(d.n, d.d, d.k, d.n_l, false);
+    if (pk) {
+      p.wpack = off;
+      off += align_up(pk);
+    }
   }
   p.bytes = off;
   return p;
@@ -207,6 +214,7 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
       a.z_out = reinterpret_cast<uint16_t*>(scratch + plan.z);
       a.lc_out = reinterpret_cast<float*>(scratch + plan.lc);
     }
+    if (plan.wpack) a.wpack = reinterpret_cast<uint16_t*>(scratch + plan.wpack);
     a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = rm.lcb_row0; a.n_l = d.n_l; a.eps = d.ln_eps;
     if (plan.use_units) {
       void* us = scratch + plan.units;
@@ -678,6 +686,10 @@ LayerPlan plan_saved(const wk_layer_desc& d, int64_t batch) {
     off += align_up(B * (size_t)d.k * d.d * 2);
     p.lc = off;
     off += align_up(B * (size_t)d.n_l * d.d * 4);
+  }
+  if (const size_t pk = wk::fmb_lcb_bf16_pack_bytes(d.n, d.d, d.k, d.n_l, p.save_zl)) {
+    p.wpack = off;  // scratch of the FMB+LCB step (rearranged [Phi; W_L]), not a saved activation
+    off += align_up(pk);
   }
   p.bytes = off;
   p.fused_out = fuse_output_ln(d);  // the fused last Linear stores M for the backward as well

@@ -62,9 +62,10 @@ def test_workspace_sizes_follow_layout():
     # K of the last Linear not a multiple of 64: M is stored
     k72 = wk.LayerSpec(40, 32, 12, 16, 24, (480, 72, 512))
     assert wk.workspace_layout(k72, B)["m"] == al(B * 480 * 2) + al(B * 72 * 2)
-    # two hidden ping-pong buffers
+    # two hidden ping-pong buffers, then [Phi; W_L] rearranged for the streamed FMB+LCB kernel
+    # (n = 256: 8 steps of 32 columns x 12 tiles of 16 x 32 bf16)
     B = 100
-    assert wk.layer_workspace_size(C2, B) == al(B * 12288 * 2) + 2 * al(B * 4096 * 2)
+    assert wk.layer_workspace_size(C2, B) == al(B * 12288 * 2) + 2 * al(B * 4096 * 2) + al(8 * 12 * 1024)
     # stacks add ping-pong activation buffers
     scratch = wk.layer_workspace_size(C2, B)
     act = al(B * 256 * 160 * 2)
@@ -252,7 +253,8 @@ def test_backward_sizes_and_support():
     assert wk.layer_backward_workspace_size(C1, B) > wk.layer_saved_size(C1, B)
     # the n = 256 layer takes the wide-layer backward: the saved buffer also holds Z (bf16) and Lc (fp32)
     fn, h1, h2, m = al(B * 12288 * 2), al(B * 4096 * 2), al(B * 4096 * 2), al(B * 128 * 160 * 2)
-    assert wk.layer_saved_size(C2, B) == fn + h1 + h2 + m + al(B * 48 * 160 * 2) + al(B * 128 * 160 * 4)
+    assert wk.layer_saved_size(C2, B) == (fn + h1 + h2 + m + al(B * 48 * 160 * 2) + al(B * 128 * 160 * 4)
+                                          + al(8 * 12 * 1024))  # + the rearranged [Phi; W_L]
     assert wk.layer_backward_workspace_size(C2, B) > 0
     C3 = wk.LayerSpec(512, 160, 96, 256, 256, (49152, 8192, 8192, 40960))
     assert wk.layer_saved_size(C3, 2048) > 0 and wk.layer_backward_workspace_size(C3, 2048) > 0
@@ -316,7 +318,9 @@ def test_moe_sizes_and_argument_errors():
     # otherwise (K % 64 != 0: residual LayerNorm kernel) the experts share the largest one
     E2 = [wk.LayerSpec(128, 160, 32, 16, 16, (4096, 2016, 2560)) for _ in range(4)]
     one = wk.layer_workspace_size(wk.LayerSpec(128, 160, 32, 16, 112, (4096, 2016, 2560)), B)
-    assert wk.moe_workspace_size(wk.MoeSpec(E2), B) == one
+    # that stand-in layer (n_l = 112) takes the streamed FMB+LCB kernel and so also holds its
+    # rearranged [Phi; W_L] (4 steps x 12 tiles of 1 KB); the experts (n_l = 16) take the resident one
+    assert wk.moe_workspace_size(wk.MoeSpec(E2), B) == one - al(4 * 12 * 1024)
     assert wk.moe_workspace_size(wk.MoeSpec(E[:3]), B) == 0         # rows must add up to n
     bad_d = E[:3] + [wk.LayerSpec(128, 80, 32, 16, 16, (4096, 2048, 1280))]
     assert wk.moe_workspace_size(wk.MoeSpec(bad_d), B) == 0         # equal d
