@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define WUKONG_ABI_VERSION 1
+#define WUKONG_ABI_VERSION 2
 
 typedef enum {
   WK_OK = 0,
@@ -147,12 +147,19 @@ size_t wukong_layer_forward_noalloc_max_workspace(void);
  *           Linear applies the residual LayerNorm in its own epilogue (bf16
  *           layers with d in {16, 32, 80, 160} and a last-Linear input width
  *           that is a multiple of 64): then M is never stored
+ *   fn_kblock_rows  0 when Fn is row-major as above; R > 0 when it is stored
+ *           K-blocked for the first Linear: element (b, c) at
+ *           ((c / 64) R + b) 64 + c % 64, R = batch rounded up to a multiple
+ *           of 256 (bf16 layers of n >= 256 whose first Linear has
+ *           n*k >= 8192 inputs: the Linear's 64-column steps of Fn are then
+ *           contiguous; rows b >= batch hold no data)
  * Returns WK_OK, or an error as wukong_layer_forward would for desc/batch. */
 typedef struct {
   int64_t fn;
   int64_t m;
   int32_t num_hidden;
   int64_t hidden[8]; /* first min(num_hidden, 8) entries are meaningful */
+  int64_t fn_kblock_rows;
 } wk_workspace_layout;
 int32_t wukong_layer_workspace_layout(const wk_layer_desc* desc, int64_t batch,
                                       wk_workspace_layout* out);

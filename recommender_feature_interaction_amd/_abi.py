@@ -30,7 +30,7 @@ KERNEL_NAMES = {KERNEL_FMB_LCB: "fmb_lcb", KERNEL_MLP_LINEAR: "mlp_linear", KERN
                 KERNEL_FUSION_LN: "fusion_ln", KERNEL_BWD_OUT: "bwd_out", KERNEL_BWD_TRANSPOSE: "bwd_transpose",
                 KERNEL_BWD_WGRAD: "bwd_wgrad", KERNEL_BWD_DGRAD: "bwd_dgrad", KERNEL_BWD_FMB: "bwd_fmb",
                 KERNEL_BWD_REDUCE: "bwd_reduce", KERNEL_FUSION_FFN: "fusion_ffn"}
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 
 class wk_layer_desc(ctypes.Structure):
@@ -78,7 +78,7 @@ class wk_moe_desc(ctypes.Structure):
 
 class wk_workspace_layout(ctypes.Structure):
     _fields_ = [("fn", ctypes.c_int64), ("m", ctypes.c_int64), ("num_hidden", ctypes.c_int32),
-                ("hidden", ctypes.c_int64 * 8)]
+                ("hidden", ctypes.c_int64 * 8), ("fn_kblock_rows", ctypes.c_int64)]
 
 
 # (name, restype, argtypes) of every exported symbol
@@ -338,7 +338,8 @@ def workspace_layout(spec: LayerSpec, batch: int) -> dict:
     _check(load_library().wukong_layer_workspace_layout(ctypes.byref(desc), batch, ctypes.byref(out)),
            "wukong_layer_workspace_layout")
     return {"fn": out.fn, "m": out.m,
-            "hidden": [out.hidden[i] for i in range(min(out.num_hidden, 8))]}
+            "hidden": [out.hidden[i] for i in range(min(out.num_hidden, 8))],
+            "fn_kblock_rows": out.fn_kblock_rows}
 
 
 def alloc_workspace(nbytes: int, device="cuda") -> torch.Tensor:

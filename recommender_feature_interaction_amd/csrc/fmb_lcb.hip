@@ -790,8 +790,20 @@ size_t fmb_lcb_bf16_pack_bytes(int n, int d, int k, int n_l, bool train) {
   return 0;
 }
 
+bool fmb_lcb_kblocked_fn_supported(int n, int d, int k, int n_l) {
+  const ResidentVariant* res = pick_resident(n, d, k, n_l);
+  return !(res && res->wl) && fmb_lcb_stream_supported(n, d, k, n_l) && (n * k) % 64 == 0;
+}
+
 hipError_t launch_fmb_lcb_bf16(const FmbLcbArgs& a, int64_t batch, hipStream_t stream,
                                int64_t* workgroups) {
+  if (a.fn_kblock_rows > 0) {  // K-blocked Fn: the plain forward's streamed kernel only
+    if (a.z_out != nullptr || !fmb_lcb_kblocked_fn_supported(a.n, a.d, a.k, a.n_l) ||
+        a.fn_kblock_rows % 256 != 0 || a.fn_kblock_rows < batch ||
+        a.fn_kblock_rows * (int64_t)a.n * a.k * 2 >= ((int64_t)1 << 31))
+      return hipErrorInvalidValue;
+    return launch_fmb_lcb_stream(a, batch, stream, workgroups);
+  }
   // Order: the resident kernel when [Phi; W_L] fits in its LDS next to X (the
   // weights are then read once per workgroup), else the streamed kernel (X
   // and the weights through an LDS ring, several examples per workgroup),

@@ -420,7 +420,12 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
         }
       }
     };
-    const __amdgpu_buffer_rsrc_t rfn = grp_rsrc(p.fn, g, n * k);
+    // Fn row-major per group, or K-blocked over the whole batch (64-column blocks of
+    // fn_kblock_rows rows: the first Linear's A operand; the host keeps it below 2 GB)
+    const uint32_t fkb = (uint32_t)p.fn_kblock_rows;
+    const __amdgpu_buffer_rsrc_t rfn =
+        fkb ? __builtin_amdgcn_make_buffer_rsrc((void*)p.fn, (short)0, (int)(fkb * (uint32_t)(n * k) * 2u), 0x00020000)
+            : grp_rsrc(p.fn, g, n * k);
     load_x(0);
     if constexpr (GB_REG) load_gb();
     for (int ex = 0; ex < E; ++ex) {
@@ -502,7 +507,10 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
                                (f[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(b2[0]));
             o[1] = pack_bf16x2((f[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(b2[1]),
                                (f[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(b2[1]));
-            __builtin_amdgcn_raw_buffer_store_b64(o, rfn, (uint32_t)((ex * n + m) * k + j0) * 2u, 0, 0);
+            const uint32_t c = (uint32_t)(m * k + j0);  // 4-aligned: the 4 values share a 64-column block
+            const uint32_t off = fkb ? (((c >> 6) * fkb + (uint32_t)b) * 64u + (c & 63u)) * 2u
+                                     : (uint32_t)((ex * n + m) * k + j0) * 2u;
+            __builtin_amdgcn_raw_buffer_store_b64(o, rfn, off, 0, 0);
           }
         }
       };

@@ -47,6 +47,7 @@ struct LinearKArgs {
   int act;                // LinearAct
   const uint16_t* res;    // [M, N] added after the activation (kActReluMask: the mask), or null
   int tiles_m, tiles_n;
+  int64_t a_kb_rows = 0;  // > 0: A is K-blocked (see LinearArgs::a_kblock_rows)
 };
 
 // The residual input: added after the activation, or, for kActReluMask, the
@@ -123,12 +124,15 @@ __device__ __forceinline__ void interleave_mfma_vmem() {
 // instead of in one burst, and the stage loop has no branch (K % 128 == 0;
 // the DMA issued after the last stage reads the rows' next 64 columns or
 // zeros past the resource and lands in a stage nobody reads).
+// a_kb_rows > 0: A is K-blocked, element (m, c) at ((c / 64) a_kb_rows + m) 64 + c % 64
+// (a_kb_rows >= every row a tile reads, K % 64 == 0): a tile's 64-column step of A is
+// then one contiguous run of BM x 128 bytes instead of BM rows K x 2 bytes apart.
 template <int BM, int BN, int WGM, int WGN, bool SPREAD = false>
 __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint16_t* w_base, int64_t M, int N,
                                              int K, int64_t m0, int n0, uint16_t* sA0, uint16_t* sW0,
                                              uint16_t* sA1, uint16_t* sW1,
                                              f32x4 (&acc)[BN / WGN / 16][BM / WGM / 16], int kbeg = 0,
-                                             int klen = -1) {
+                                             int klen = -1, int64_t a_kb_rows = 0) {
   constexpr int NW = WGM * WGN;
   constexpr int WTM = BM / WGM, WTN = BN / WGN;
   constexpr int MB = WTM / 16, NB = WTN / 16;
@@ -137,8 +141,13 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WGM, wn = wave / WGM;
   const int rows_a = (int)min<int64_t>(BM, M - m0), rows_w = min(BN, N - n0);
+  const bool akb = a_kb_rows > 0;  // uniform
+  // K-blocked A: the resource runs from the tile's first row of block 0 to the end of the
+  // array; rows past M hold whatever the producer left there and only feed output rows
+  // that are never stored
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a_base + m0 * K), (short)0, rows_a * K * 2, 0x00020000);
+      (void*)(a_base + m0 * (akb ? kBK : K)), (short)0,
+      akb ? (int)min<int64_t>((a_kb_rows * K - m0 * kBK) * 2, 0x7fffffff) : rows_a * K * 2, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(w_base + (int64_t)n0 * K), (short)0, rows_w * K * 2, 0x00020000);
   // A DMA instruction writes 64 lanes x 16 B = 8 LDS rows; lane -> row lane/8,
@@ -148,6 +157,10 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   const uint32_t voff0 = (uint32_t)(lrow * K + ((lpos ^ (lrow >> 1)) << 3)) * 2u;
   const uint32_t voff1 = (uint32_t)(lrow * K + ((lpos ^ (4 + (lrow >> 1))) << 3)) * 2u;
   const uint32_t blk_bytes = (uint32_t)(16 * K);
+  // K-blocked A: rows 128 bytes apart, a 64-column step a_kb_rows x 128 bytes further
+  const uint32_t avoff0 = akb ? (uint32_t)(lrow * kBK + ((lpos ^ (lrow >> 1)) << 3)) * 2u : voff0;
+  const uint32_t avoff1 = akb ? (uint32_t)(lrow * kBK + ((lpos ^ (4 + (lrow >> 1))) << 3)) * 2u : voff1;
+  const uint32_t ablk_bytes = akb ? 8u * kBK * 2u : blk_bytes;
   // A K range that ends in half a step (K % 64 == 32): in the last step the
   // lanes of columns 32..63 read zero (an offset past every record count)
   // instead of the next row's first columns.
@@ -157,11 +170,13 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   auto dma = [&](uint16_t* sa, uint16_t* sw, int k0) {
     const bool half = k0 + kBK > kspan;  // uniform
     const uint32_t v0 = half ? voff0t : voff0, v1 = half ? voff1t : voff1;
+    // A's step offset (uniform): columns kbeg + k0 of a row, or block (kbeg + k0) / 64
+    const int a_soff = akb ? (int)(((kbeg + k0) / kBK) * a_kb_rows * (kBK * 2)) : (kbeg + k0) * 2;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int blk = wave * A_INS + i;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, WK_LDS(sa + blk * 512), 16,
-                                               ((blk & 1) ? v1 : v0) + blk * blk_bytes, (kbeg + k0) * 2, 0, 0);
+      const uint32_t av = akb ? ((blk & 1) ? avoff1 : avoff0) + blk * ablk_bytes : ((blk & 1) ? v1 : v0) + blk * blk_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, WK_LDS(sa + blk * 512), 16, av, a_soff, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < W_INS; ++i) {
@@ -261,7 +276,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void linear_dma_kernel(LinearKArgs 
   const int64_t M = p.M;
   const int N = p.N;
   f32x4 acc[NB][MB];
-  dma_mainloop<BM, BN, WGM, WGN, SPREAD>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
+  dma_mainloop<BM, BN, WGM, WGN, SPREAD>(p.a, p.w, M, N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc, 0, -1, p.a_kb_rows);
   const uint16_t* bias = p.bias;
   const uint16_t* res = p.res;
   // The residual (or mask) values are all requested before the first store:
@@ -1070,7 +1085,13 @@ bool linear_bf16_supported(int64_t M, int N, int K) {
 
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups) {
   const LinearVariant* v = pick_linear(a.M, a.N, a.K);
+  if (a.a_kblock_rows > 0) {  // K-blocked A: the DMA kernels only, every row of every tile inside the array
+    if (a.K % kBK != 0 || v->kmod < 32 || a.a_kblock_rows % 256 != 0 || a.a_kblock_rows < a.M ||
+        a.a_kblock_rows * (int64_t)a.K * 2 >= ((int64_t)1 << 31))
+      return hipErrorInvalidValue;
+  }
   LinearKArgs k;
+  k.a_kb_rows = a.a_kblock_rows;
   k.a = static_cast<const uint16_t*>(a.a);
   k.w = static_cast<const uint16_t*>(a.w);
   k.bias = static_cast<const uint16_t*>(a.bias);

@@ -26,7 +26,13 @@ struct FmbLcbArgs {
   // scratch for [Phi; W_L] rearranged into the streamed kernel's 1 KB step tiles
   // (fmb_lcb_bf16_pack_bytes(); needed when that is non-zero)
   uint16_t* wpack = nullptr;
+  // > 0 (streamed kernel only): Fn is written K-blocked, element (b, c) at
+  // ((c / 64) fn_kblock_rows + b) 64 + c % 64, the first Linear's A operand in
+  // the layout LinearArgs::a_kblock_rows describes
+  int64_t fn_kblock_rows = 0;
 };
+// Whether launch_fmb_lcb_bf16 can write Fn K-blocked for this shape (the plain forward).
+bool fmb_lcb_kblocked_fn_supported(int n, int d, int k, int n_l);
 bool fmb_lcb_bf16_supported(int n, int d, int k, int n_l);
 // Streamed variant (fmb_lcb_stream.hip): several examples per workgroup, the
 // weights and X rows DMA'd through an LDS ring.  Used first when it supports
@@ -108,6 +114,9 @@ struct LinearArgs {
   int N, K;
   int act;
   const void* res = nullptr;  // bf16 only: [M, N] added after the activation (the mask for kActReluMask), or null
+  // bf16 launch_linear_bf16 only, K % 64 == 0: > 0 when A is K-blocked, element (m, c) at
+  // ((c / 64) a_kblock_rows + m) 64 + c % 64 (a_kblock_rows: a multiple of 256, >= M)
+  int64_t a_kblock_rows = 0;
 };
 bool linear_bf16_supported(int64_t M, int N, int K);
 hipError_t launch_linear_bf16(const LinearArgs& a, hipStream_t stream, int64_t* workgroups);

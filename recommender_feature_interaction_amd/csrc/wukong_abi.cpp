@@ -77,6 +77,7 @@ int32_t check_desc(const wk_layer_desc* d, bool expert = false) {
 
 struct LayerPlan {
   size_t fn = 0, h[2] = {0, 0}, m = 0, units = 0, wpack = 0, bytes = 0;
+  int64_t fn_kb = 0;  // > 0: Fn K-blocked with this many rows per 64-column block (first Linear's A)
   int num_hidden_bufs = 0;
   bool keep_hidden = false;  // h_{t+1} goes to hid[t] (the training forward keeps them all)
   size_t hid[kMaxLinear] = {};
@@ -101,13 +102,27 @@ bool fuse_output_ln(const wk_layer_desc& d) {
 // FMB+LCB kernel; grid dimensions are 32-bit).
 constexpr int64_t kMaxBatch = (int64_t)1 << 30;
 
+// The plain bf16 forward writes Fn K-blocked when the streamed FMB+LCB kernel
+// produces it and the first Linear (a plain GEMM) reads it with a long K: each
+// of the GEMM's 64-column steps of A is then one contiguous run instead of rows
+// n k x 2 bytes apart.
+int64_t fn_kblock_rows(const wk_layer_desc& d, int64_t batch) {
+  const int64_t nk = (int64_t)d.n * d.k;
+  const int unfused = fuse_output_ln(d) ? d.num_linear - 1 : d.num_linear;
+  if (d.dtype != WK_BF16 || units_path(d) || unfused < 1 || nk < 8192) return 0;
+  if (!wk::fmb_lcb_kblocked_fn_supported(d.n, d.d, d.k, d.n_l)) return 0;
+  const int64_t rows = (batch + 255) / 256 * 256;
+  return rows * nk * 2 < ((int64_t)1 << 31) ? rows : 0;
+}
+
 LayerPlan plan_layer(const wk_layer_desc& d, int64_t batch) {
   LayerPlan p;
   const size_t es = esize(d.dtype);
   const size_t B = (size_t)batch;
   size_t off = 0;
   p.fn = off;
-  off += align_up(B * d.n * d.k * es);
+  p.fn_kb = fn_kblock_rows(d, batch);
+  off += align_up((p.fn_kb ? (size_t)p.fn_kb : B) * d.n * d.k * es);
   int64_t maxhid = 0;
   for (int t = 1; t < d.num_linear; ++t) maxhid = d.mlp_dims[t] > maxhid ? d.mlp_dims[t] : maxhid;
   p.num_hidden_bufs = d.num_linear >= 3 ? 2 : (d.num_linear == 2 ? 1 : 0);
@@ -215,6 +230,7 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
       a.lc_out = reinterpret_cast<float*>(scratch + plan.lc);
     }
     if (plan.wpack) a.wpack = reinterpret_cast<uint16_t*>(scratch + plan.wpack);
+    a.fn_kblock_rows = plan.fn_kb;
     a.n = d.n; a.d = d.d; a.k = d.k; a.n_f = rm.lcb_row0; a.n_l = d.n_l; a.eps = d.ln_eps;
     if (plan.use_units) {
       void* us = scratch + plan.units;
@@ -256,6 +272,7 @@ int32_t run_layer(const wk_layer_desc& d, const wk_layer_weights& w, int64_t bat
     a.N = d.mlp_dims[t + 1];
     a.K = d.mlp_dims[t];
     a.act = last ? wk::kActNone : wk::kActRelu;
+    if (t == 0) a.a_kblock_rows = plan.fn_kb;
     st = launch(WK_KERNEL_MLP_LINEAR, layer_idx, t, [&](int64_t* g) {
       return bf ? wk::launch_linear_bf16(a, launch.stream, g) : wk::launch_linear_f32(a, launch.stream, g);
     });
@@ -1222,6 +1239,7 @@ int32_t wukong_layer_workspace_layout(const wk_layer_desc* desc, int64_t batch, 
   if (st != WK_OK) return st;
   const LayerPlan p = plan_layer(*desc, batch);
   out->fn = (int64_t)p.fn;
+  out->fn_kblock_rows = p.fn_kb;
   out->m = p.fused_out ? -1 : (int64_t)p.m;
   out->num_hidden = desc->num_linear - 1;
   for (int i = 0; i < 8; ++i) out->hidden[i] = -1;

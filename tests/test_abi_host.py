@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_status_strings():
     lib = wk.load_library()
-    assert lib.wukong_abi_version() == 1
+    assert lib.wukong_abi_version() == 2
     for s in range(5):
         assert wk.status_string(s).startswith(["WK_OK", "WK_ERR_INVALID_ARG", "WK_ERR_UNSUPPORTED",
                                                "WK_ERR_WORKSPACE", "WK_ERR_HIP"][s])
@@ -62,10 +62,13 @@ def test_workspace_sizes_follow_layout():
     # K of the last Linear not a multiple of 64: M is stored
     k72 = wk.LayerSpec(40, 32, 12, 16, 24, (480, 72, 512))
     assert wk.workspace_layout(k72, B)["m"] == al(B * 480 * 2) + al(B * 72 * 2)
-    # two hidden ping-pong buffers, then [Phi; W_L] rearranged for the streamed FMB+LCB kernel
+    # Fn K-blocked for the first Linear (the batch rounded up to 256 rows per 64-column block), two
+    # hidden ping-pong buffers, then [Phi; W_L] rearranged for the streamed FMB+LCB kernel
     # (n = 256: 8 steps of 32 columns x 12 tiles of 16 x 32 bf16)
     B = 100
-    assert wk.layer_workspace_size(C2, B) == al(B * 12288 * 2) + 2 * al(B * 4096 * 2) + al(8 * 12 * 1024)
+    assert wk.layer_workspace_size(C2, B) == al(256 * 12288 * 2) + 2 * al(B * 4096 * 2) + al(8 * 12 * 1024)
+    assert wk.workspace_layout(C2, B)["fn_kblock_rows"] == 256
+    assert wk.workspace_layout(C1, B)["fn_kblock_rows"] == 0  # n = 128: the resident kernel, row-major Fn
     # stacks add ping-pong activation buffers
     scratch = wk.layer_workspace_size(C2, B)
     act = al(B * 256 * 160 * 2)

@@ -32,6 +32,17 @@ def _ws_tensor(ws_t, off, count, dtype):
     return to_host(ws_t[off:off + count * es].view(tdt))
 
 
+def _ws_fn(ws_t, lay, batch, nk, dtype):
+    """Fn [batch, nk] from a layer workspace: row-major, or K-blocked (64-column blocks of
+    fn_kblock_rows rows, as wk_workspace_layout documents) for the first Linear."""
+    rows = lay["fn_kblock_rows"]
+    if rows == 0:
+        return _ws_tensor(ws_t, lay["fn"], batch * nk, dtype).reshape(batch, nk)
+    assert nk % 64 == 0 and rows >= batch and rows % 256 == 0
+    blocked = _ws_tensor(ws_t, lay["fn"], rows * nk, dtype).reshape(nk // 64, rows, 64)
+    return np.ascontiguousarray(blocked.transpose(1, 0, 2)).reshape(rows, nk)[:batch]
+
+
 def test_tiny_f32_full_batch():
     for affine in ("identity", "random"):
         r = Run(ws.TINY_F32, seed=0, affine=affine)
@@ -59,7 +70,9 @@ def test_single_layer_intermediates(cfg, B):
     Y, it = oracle.wukong_layer(r.x, r.host_w[0], storage=st, intermediates=True)
     tol = cfg.dtype
     s = cfg.layers[0]
-    fn = host_f64(_ws_tensor(wst, lay["fn"], B * s.n * s.k, cfg.dtype)).reshape(B, -1)
+    fn = host_f64(_ws_fn(wst, lay, B, s.n * s.k, cfg.dtype))
+    if lay["fn_kblock_rows"]:
+        log(f"  Fn K-blocked ({lay['fn_kblock_rows']} rows per 64-column block)")
     check("Fn", fn, it["Fn"], tol)
     for t, off in enumerate(lay["hidden"]):
         if off >= 0:
