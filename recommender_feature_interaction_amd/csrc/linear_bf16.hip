@@ -145,9 +145,13 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   // K-blocked A: the resource runs from the tile's first row of block 0 to the end of the
   // array; rows past M hold whatever the producer left there and only feed output rows
   // that are never stored
-  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a_base + m0 * (akb ? kBK : K)), (short)0,
-      akb ? (int)min<int64_t>((a_kb_rows * K - m0 * kBK) * 2, 0x7fffffff) : rows_a * K * 2, 0x00020000);
+  // (readfirstlane: the compiler cannot tell the select is uniform, and a resource it takes
+  // for divergent turns every DMA into a loop over lanes)
+  const int a_bytes = __builtin_amdgcn_readfirstlane(
+      akb ? (int)min<int64_t>((a_kb_rows * K - m0 * kBK) * 2, 0x7fffffff) : rows_a * K * 2);
+  const int a_row = __builtin_amdgcn_readfirstlane(akb ? kBK : K);
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a_base + m0 * a_row), (short)0, a_bytes, 0x00020000);
   const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(w_base + (int64_t)n0 * K), (short)0, rows_w * K * 2, 0x00020000);
   // A DMA instruction writes 64 lanes x 16 B = 8 LDS rows; lane -> row lane/8,
@@ -157,26 +161,28 @@ __device__ __forceinline__ void dma_mainloop(const uint16_t* a_base, const uint1
   const uint32_t voff0 = (uint32_t)(lrow * K + ((lpos ^ (lrow >> 1)) << 3)) * 2u;
   const uint32_t voff1 = (uint32_t)(lrow * K + ((lpos ^ (4 + (lrow >> 1))) << 3)) * 2u;
   const uint32_t blk_bytes = (uint32_t)(16 * K);
-  // K-blocked A: rows 128 bytes apart, a 64-column step a_kb_rows x 128 bytes further
-  const uint32_t avoff0 = akb ? (uint32_t)(lrow * kBK + ((lpos ^ (lrow >> 1)) << 3)) * 2u : voff0;
-  const uint32_t avoff1 = akb ? (uint32_t)(lrow * kBK + ((lpos ^ (4 + (lrow >> 1))) << 3)) * 2u : voff1;
-  const uint32_t ablk_bytes = akb ? 8u * kBK * 2u : blk_bytes;
-  // A K range that ends in half a step (K % 64 == 32): in the last step the
+  // A's rows are a_row elements apart: K, or 64 when K-blocked
+  const uint32_t avoff0 = (uint32_t)(lrow * a_row + ((lpos ^ (lrow >> 1)) << 3)) * 2u;
+  const uint32_t avoff1 = (uint32_t)(lrow * a_row + ((lpos ^ (4 + (lrow >> 1))) << 3)) * 2u;
+  const uint32_t ablk_bytes = (uint32_t)(16 * a_row);
+  // A K range that ends in half a step (K % 64 == 32, never K-blocked): in the last step the
   // lanes of columns 32..63 read zero (an offset past every record count)
   // instead of the next row's first columns.
   const int kspan = klen < 0 ? K : klen;
-  const uint32_t voff0t = ((lpos ^ (lrow >> 1)) >= 4) ? 0x80000000u : voff0;
-  const uint32_t voff1t = ((lpos ^ (4 + (lrow >> 1))) >= 4) ? 0x80000000u : voff1;
+  const bool hi0 = (lpos ^ (lrow >> 1)) >= 4, hi1 = (lpos ^ (4 + (lrow >> 1))) >= 4;
+  const uint32_t voff0t = hi0 ? 0x80000000u : voff0, voff1t = hi1 ? 0x80000000u : voff1;
+  const uint32_t avoff0t = hi0 ? 0x80000000u : avoff0, avoff1t = hi1 ? 0x80000000u : avoff1;
   auto dma = [&](uint16_t* sa, uint16_t* sw, int k0) {
     const bool half = k0 + kBK > kspan;  // uniform
     const uint32_t v0 = half ? voff0t : voff0, v1 = half ? voff1t : voff1;
+    const uint32_t a0 = half ? avoff0t : avoff0, a1 = half ? avoff1t : avoff1;
     // A's step offset (uniform): columns kbeg + k0 of a row, or block (kbeg + k0) / 64
     const int a_soff = akb ? (int)(((kbeg + k0) / kBK) * a_kb_rows * (kBK * 2)) : (kbeg + k0) * 2;
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int blk = wave * A_INS + i;
-      const uint32_t av = akb ? ((blk & 1) ? avoff1 : avoff0) + blk * ablk_bytes : ((blk & 1) ? v1 : v0) + blk * blk_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, WK_LDS(sa + blk * 512), 16, av, a_soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, WK_LDS(sa + blk * 512), 16, ((blk & 1) ? a1 : a0) + blk * ablk_bytes,
+                                               a_soff, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < W_INS; ++i) {
