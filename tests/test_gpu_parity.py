@@ -88,6 +88,29 @@ def test_single_layer_intermediates(cfg, B):
     check("Y rows of LCB", yh[:, s.n_f:], Y[:, s.n_f:], tol)
 
 
+# Ragged batches of the streamed FMB+LCB layers, whose Fn is K-blocked for the first Linear:
+# B = 257 leaves 255 padding rows per 64-column block and a last group of one example (two per
+# group at n = 256, four at n = 720); B = 259 a last group of three at n = 720.
+RAGGED = [(ws.STACK8_N256.with_layers(1), 257), (ws.SMALLD_N720, 257), (ws.SMALLD_N720, 259)]
+
+
+@pytest.mark.parametrize("cfg,B", RAGGED, ids=[f"{c.name}_B{b}" for c, b in RAGGED])
+def test_ragged_batch_kblocked_fn(cfg, B):
+    r = Run(cfg, seed=B, affine="random", batch=B)
+    spec = spec_of(cfg.layers[0], cfg.dtype)
+    lay = wk.workspace_layout(spec, B)
+    assert lay["fn_kblock_rows"] == 512, lay
+    wst = wk.alloc_workspace(wk.layer_workspace_size(spec, B))
+    y = wk.layer_forward(r.xd, r.layers[0], workspace=wst)
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, 127, 255, 256] + list(range(257, B)))
+    s = cfg.layers[0]
+    Y, it = oracle.wukong_layer(r.x[idx], r.host_w[0], storage=BF16_STORAGE, intermediates=True)
+    fn = host_f64(_ws_fn(wst, lay, B, s.n * s.k, cfg.dtype))[idx]
+    check(f"Fn at examples {idx.tolist()}", fn, it["Fn"], "bf16")
+    check(f"Y at examples {idx.tolist()}", host_f64(to_host(y))[idx], Y, "bf16")
+
+
 @pytest.mark.parametrize("cfg,batch", [(ws.STACK8_N256, 6), (ws.STACK8_N512, 4)], ids=["stack8_n256", "stack8_n512"])
 def test_stack_two_layers(cfg, batch):
     r = Run(cfg, seed=5, affine="random", num_layers=2, batch=batch)
