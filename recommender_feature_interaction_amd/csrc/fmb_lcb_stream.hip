@@ -72,7 +72,10 @@ __host__ __device__ constexpr int zs_pitch(int d) { return (d + 31) / 32 * 32 + 
 // of the slot (needs ZTMAX >= WZ * ZPW), branch-free with each operand consumed as it is read.
 // TRAIN: the training forward also stores Z (bf16, as the interaction uses it) and Lc (fp32, as
 // the LCB rows' LayerNorm uses it) for the backward.
-template <int ET, int ZPW, int WZ, int WE, int EPW, int MPW, int KJ, int ZTMAX, int S, bool GUARD, bool TRAIN>
+// CONTIG: [Phi; W_L] rows are packed without padding between Phi and W_L (row z < k is Phi's,
+// z - k W_L's), so a tile may hold both kinds; a lane's row kind is decided per lane.
+template <int ET, int ZPW, int WZ, int WE, int EPW, int MPW, int KJ, int ZTMAX, int S, bool GUARD, bool CONTIG,
+          bool TRAIN>
 __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p, int64_t batch, StreamShape sh) {
   constexpr int D = 16 * ET;
   constexpr int E = WE * EPW;
@@ -123,6 +126,12 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
   for (int i = tid; i < E * KJ * 16 * (ZP - D); i += NTHREAD) {
     const int row = i / (ZP - D), c = i - row * (ZP - D);
     Zs[(size_t)row * ZP + D + c] = 0;
+  }
+  if constexpr (CONTIG) {  // Z rows k .. 16 KJ - 1 stay zero (their tile rows are W_L's)
+    for (int i = tid; i < E * KJ * 16 * D; i += NTHREAD) {
+      const int row = i / D, c = i - row * D;
+      if (row % (KJ * 16) >= p.k) Zs[(size_t)row * ZP + c] = 0;
+    }
   }
 
   // ---- DMA issue.  The packed weights: step t, tile i at byte (t ZTP + i) 1024.
@@ -311,27 +320,32 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
       rlc = __builtin_amdgcn_make_buffer_rsrc((void*)(p.lc_out + b0 * (int64_t)n_l * D), (short)0,
                                               cnt * n_l * D * 4, 0x00020000);
     }
-    u32x2 xres[ZPW][EPW][ET];
+    // lane row kinds: Z row z < k (CONTIG) or tile < KZ; else LCB output row zl
+    auto is_z = [&](int zt, int z) { return CONTIG ? z < k : zt < KZ; };
+    auto lcb_row = [&](int z) { return CONTIG ? z - k : z - 16 * KZ; };
+    // the residual rows X[n_f + zl] of one example, requested one example ahead
+    auto load_res = [&](int ex, u32x2 (&xr)[ZPW][ET]) {
 #pragma unroll
-    for (int zi = 0; zi < ZPW; ++zi) {
-      const int zt = wz * ZPW + zi;
-      const int zl = zt * 16 + li - 16 * KZ;  // LCB output row (tiles >= KZ only)
-#pragma unroll
-      for (int ex = 0; ex < EPW; ++ex) {
-        const bool valid = zt < ZT && zt >= KZ && zl < n_l;
+      for (int zi = 0; zi < ZPW; ++zi) {
+        const int zt = wz * ZPW + zi;
+        const int z = zt * 16 + li, zl = lcb_row(z);
+        const bool valid = zt < ZT && !is_z(zt, z) && zl < n_l;
         const uint32_t off = valid ? (uint32_t)(((we * EPW + ex) * n + n_f + zl) * D + lg * 4) * 2u : kOOB;
 #pragma unroll
-        for (int et = 0; et < ET; ++et) xres[zi][ex][et] = __builtin_amdgcn_raw_buffer_load_b64(rx, off + et * 32, 0, 0);
+        for (int et = 0; et < ET; ++et) xr[zi][et] = __builtin_amdgcn_raw_buffer_load_b64(rx, off + et * 32, 0, 0);
       }
-    }
+    };
+    u32x2 xres[2][ZPW][ET];
+    load_res(0, xres[0]);
 #pragma unroll
-    for (int zi = 0; zi < ZPW; ++zi) {
-      const int zt = wz * ZPW + zi;
-      if (zt >= ZT) continue;  // wave-uniform
-      const int z = zt * 16 + li;
-      if (zt < KZ) {
+    for (int ex = 0; ex < EPW; ++ex) {
+      if (ex + 1 < EPW) load_res(ex + 1, xres[(ex + 1) & 1]);
 #pragma unroll
-        for (int ex = 0; ex < EPW; ++ex) {
+      for (int zi = 0; zi < ZPW; ++zi) {
+        const int zt = wz * ZPW + zi;
+        if (zt >= ZT) continue;  // wave-uniform
+        const int z = zt * 16 + li;
+        if (is_z(zt, z)) {  // uniform unless CONTIG (then the 4 lanes of a row agree)
           uint16_t* zrow = Zs + ((we * EPW + ex) * KJ * 16 + z) * ZP;
 #pragma unroll
           for (int et = 0; et < ET; ++et) {
@@ -344,11 +358,8 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
               __builtin_amdgcn_raw_buffer_store_b64(v, rz, zoff, 0, 0);
             }
           }
-        }
-      } else {
-        const int zl = z - 16 * KZ;  // LCB output row
-#pragma unroll
-        for (int ex = 0; ex < EPW; ++ex) {
+        } else {
+          const int zl = lcb_row(z);  // LCB output row
           const bool valid = zl < n_l;  // examples past the batch: dropped by the resource bound
           if constexpr (TRAIN) {
             const uint32_t loff = valid ? (uint32_t)(((we * EPW + ex) * n_l + zl) * D + lg * 4) * 4u : kOOB;
@@ -361,7 +372,7 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
           float sm = 0.f;
 #pragma unroll
           for (int et = 0; et < ET; ++et) {
-            const u32x2 xv = xres[zi][ex][et];
+            const u32x2 xv = xres[ex & 1][zi][et];
             v[et][0] = acc[zi][ex][et][0] + bf16lo(xv[0]);
             v[et][1] = acc[zi][ex][et][1] + bf16hi(xv[0]);
             v[et][2] = acc[zi][ex][et][2] + bf16lo(xv[1]);
@@ -532,12 +543,12 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
 
 
 // [Phi; W_L] in the ring's order: 16-byte chunk c = (t ZTP + i) 64 + l holds
-// row 16 i + l / 4 of [Phi (padded to KZ tiles); W_L], columns 32 t + 8 (l % 4)
-// .. + 7, zero outside the matrices and in the tiles past ZT.
+// row 16 i + l / 4 of [Phi (padded to KZ tiles, or not at all when contig); W_L],
+// columns 32 t + 8 (l % 4) .. + 7, zero outside the matrices and in the tiles past ZT.
 __global__ __launch_bounds__(256) void pack_stream_weights_kernel(const uint16_t* __restrict__ phi,
                                                                   const uint16_t* __restrict__ w_l,
                                                                   uint16_t* __restrict__ out, int n, int k, int n_l,
-                                                                  int kz, int zt, int ztp, int steps) {
+                                                                  int kz, int zt, int ztp, int steps, int contig) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (c >= steps * ztp * 64) return;
   const int l = c & 63, ti = c >> 6;
@@ -545,9 +556,9 @@ __global__ __launch_bounds__(256) void pack_stream_weights_kernel(const uint16_t
   const int r = 16 * i + (l >> 2), col = KC * t + 8 * (l & 3);
   const uint16_t* src = phi;
   int row = r, rows = k;
-  if (i >= kz) {
+  if (contig ? r >= k : i >= kz) {
     src = w_l;
-    row = r - 16 * kz;
+    row = contig ? r - k : r - 16 * kz;
     rows = i < zt ? n_l : 0;  // tiles past zt: zero padding
   }
   uint16_t v[8];
@@ -561,28 +572,31 @@ __global__ __launch_bounds__(256) void pack_stream_weights_kernel(const uint16_t
 
 struct StreamVariant {
   int et, zpw, wz, we, epw, mpw, kj, ztmax, s;
+  bool contig;
   void (*kernel)(FmbLcbArgs, int64_t, StreamShape);
   void (*kernel_train)(FmbLcbArgs, int64_t, StreamShape);  // also stores Z and Lc
 };
 
-#define WK_STREAM(ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD)                       \
-  StreamVariant {                                                                       \
-    ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S,                                            \
-        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD, false>,   \
-        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD, true>     \
+#define WK_STREAM(ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD, CONTIG)                       \
+  StreamVariant {                                                                               \
+    ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, CONTIG,                                            \
+        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD, CONTIG, false>,   \
+        fmb_lcb_stream_kernel<ET, ZPW, WZ, WE, EPW, MPW, KJ, ZTMAX, S, GUARD, CONTIG, true>     \
   }
 
 // LDS per variant (static): S x (ZTMAX 16 KC + E KC D) + E KJ 16 ZP + 2 D u16.
 const StreamVariant kStream[] = {
-    WK_STREAM(10, 3, 4, 2, 1, 2, 3, 12, 3, false),  // n<=256, d=160, k<=48, ZT<=12: 2 examples per group
-    WK_STREAM(10, 3, 8, 1, 1, 4, 6, 24, 3, false),  // n<=512, d=160, k<=96, ZT<=24
-    WK_STREAM(2, 4, 8, 1, 4, 6, 2, 25, 4, true),    // n<=768, d=32,  k<=32, ZT<=25: 4 examples per group
+    WK_STREAM(10, 3, 4, 2, 1, 2, 3, 12, 3, false, false),  // n<=256, d=160, k<=48, ZT<=12: 2 examples per group
+    WK_STREAM(10, 3, 8, 1, 1, 4, 6, 24, 3, false, false),  // n<=512, d=160, k<=96, ZT<=24
+    // n<=768, d=32, k<=32, k+n_l<=384 (24 contiguous tiles, 3 per wave): 8 examples per group
+    WK_STREAM(2, 3, 8, 1, 8, 6, 2, 24, 3, false, true),
+    WK_STREAM(2, 4, 8, 1, 4, 6, 2, 25, 4, true, false),    // n<=768, d=32,  k<=32, ZT<=25: 4 examples per group
 };
 
 StreamShape stream_shape(const StreamVariant& v, int n, int k, int n_l) {
   StreamShape sh;
-  sh.kz = (k + 15) / 16;
-  sh.zt = sh.kz + (n_l + 15) / 16;
+  sh.kz = v.contig ? 0 : (k + 15) / 16;
+  sh.zt = v.contig ? (k + n_l + 15) / 16 : sh.kz + (n_l + 15) / 16;
   sh.steps = (n + KC - 1) / KC;
   sh.e = v.we * v.epw;
   sh.ztp = v.ztmax;
@@ -595,7 +609,7 @@ const StreamVariant* pick_stream(int n, int d, int k, int n_l, StreamShape* out)
     if (16 * v.et != d) continue;
     const StreamShape sh = stream_shape(v, n, k, n_l);
     if (sh.zt > v.ztmax || sh.zt > v.wz * v.zpw) continue;  // DMA'd tiles and tiles with an owner wave
-    if (sh.kz > v.kj) continue;
+    if ((k + 15) / 16 > v.kj) continue;
     if ((n + 15) / 16 > NWAVE * v.mpw) continue;
 
     // 32-bit byte offsets within one group's X and within the weights
@@ -628,7 +642,7 @@ hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t
   if (batch == 0) return hipSuccess;
   const int chunks = sh.steps * sh.ztp * 64;
   hipLaunchKernelGGL(pack_stream_weights_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a.phi,
-                     a.w_l, a.wpack, a.n, a.k, a.n_l, sh.kz, sh.zt, sh.ztp, sh.steps);
+                     a.w_l, a.wpack, a.n, a.k, a.n_l, sh.kz, sh.zt, sh.ztp, sh.steps, v->contig ? 1 : 0);
   hipLaunchKernelGGL(a.z_out ? v->kernel_train : v->kernel, dim3((unsigned)grid), dim3(NTHREAD), 0, stream, a, batch,
                      sh);
   return hipGetLastError();
