@@ -10,18 +10,18 @@
 // MFMA tiles of the other FMB+LCB kernels, and [Phi; W_L] (k + n_L rows of n)
 // is far too large to stream per example.  So the left multiply becomes one
 // GEMM over the whole batch:
-//   1. units_transpose_kernel: Xt[b][e][j] = X[b][j][e] (the GEMM's A operand,
+//   1. units_transpose_kernel: Xt[b][e][j] = X[b][j][e] (the GEMM's operand,
 //      K = n contiguous);
-//   2. the bf16 DMA GEMM with fp32 output: C[(b, e)][r] = sum_j Xt[(b, e)][j]
-//      [Phi; W_L][r][j], i.e. C[b][e][r] = [Z_b; Lc_b][r][e];
+//   2. the bf16 DMA GEMM C'[r][(b, e)] = sum_j [Phi; W_L][r][j] Xt[(b, e)][j]
+//      (units_gemm_kernel): its epilogue writes Z_b in fp32 and finishes the
+//      LCB rows of Y (Lc in fp32 + residual, LayerNorm over the 8 values);
 //   3. units_epilogue_kernel, a group of examples per workgroup: Z_b rounded
 //      to bf16 (the MFMA operand precision of the other kernels) as a register
 //      operand; F_b^T = Z_b X_b^T on the MFMA 32 rows at a time, the
 //      statistics merged by Chan's parallel-variance formula (count, mean, sum
-//      of squared deviations) and reduced over the workgroup, with the LCB
-//      rows of Y finished from the same X rows (Lc in fp32 + residual,
-//      LayerNorm over the 8 values); then a second pass that recomputes each
-//      block and writes Fn with the FMB LayerNorm's gamma / beta.
+//      of squared deviations) and reduced over the workgroup; then a second
+//      pass that recomputes each block and writes Fn with the FMB LayerNorm's
+//      gamma / beta.
 #include "wk_device.h"
 #include "wk_kernels.h"
 
@@ -54,14 +54,11 @@ __global__ __launch_bounds__(256) void units_transpose_kernel(const uint16_t* x,
 
 struct UnitsArgs {
   const uint16_t* x;
-  const float* c;            // [B][8][k + n_l]
+  const float* z;            // [B][k][8]
   const uint16_t* fm_gamma;  // [n k] or null
   const uint16_t* fm_beta;
-  const uint16_t* out_gamma; // [8] or null
-  const uint16_t* out_beta;
   uint16_t* fn;              // [B][n k]
-  uint16_t* y;               // [B][n][8]: rows n_f .. n-1 written here
-  int n, k, n_f, n_l;
+  int n, k;
   float eps;
 };
 
@@ -91,15 +88,8 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
   __shared__ float stat[UE][2];  // mean, rstd of F per example
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
-  const int n = p.n, k = p.k, n_f = p.n_f, n_l = p.n_l;
-  const int N = k + n_l;
+  const int n = p.n, k = p.k;
   const float inv_nk = 1.0f / (float)(n * k);
-  float og[UD], ob[UD];
-#pragma unroll
-  for (int e = 0; e < UD; ++e) {
-    og[e] = p.out_gamma ? bf16_to_f32(p.out_gamma[e]) : 1.f;
-    ob[e] = p.out_beta ? bf16_to_f32(p.out_beta[e]) : 0.f;
-  }
   const int64_t groups = (batch + UE - 1) / UE;
   for (int64_t g = blockIdx.x; g < groups; g += gridDim.x) {
     const int64_t b0 = g * UE;
@@ -110,9 +100,10 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
     for (int ex = 0; ex < UE; ++ex) {
       zop[ex] = u32x4{0u, 0u, 0u, 0u};
       if (ex < ne && h == 0 && l32 < k) {
-        const float* cz = p.c + (b0 + ex) * UD * (int64_t)N + l32;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) zop[ex][t] = pack_bf16x2(cz[(2 * t) * N], cz[(2 * t + 1) * N]);
+        const f32x4* cz = reinterpret_cast<const f32x4*>(p.z + ((b0 + ex) * (int64_t)k + l32) * UD);
+        const f32x4 z0 = cz[0], z1 = cz[1];
+        zop[ex] = u32x4{pack_bf16x2(z0[0], z0[1]), pack_bf16x2(z0[2], z0[3]), pack_bf16x2(z1[0], z1[1]),
+                        pack_bf16x2(z1[2], z1[3])};
       }
     }
     auto x_row = [&](int ex, int m) {  // lanes 0..31: X row m; lanes 32..63: zero (the padding)
@@ -125,35 +116,6 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
 #pragma unroll
       for (int r = 0; r < 16; ++r) zero[r] = 0.f;
       return mfma32x32x16(zop[ex], xop, zero);
-    };
-    // an LCB row of Y from the X row already in registers: Lc (fp32) + residual,
-    // LayerNorm over the 8 values
-    auto lcb_row = [&](int ex, int m, const u32x4& xr) {
-      const int64_t b = b0 + ex;
-      const int i = m - n_f;
-      float v[UD];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        v[2 * t] = bf16lo(xr[t]);
-        v[2 * t + 1] = bf16hi(xr[t]);
-      }
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < UD; ++e) {
-        v[e] += p.c[(b * UD + e) * (int64_t)N + k + i];
-        s += v[e];
-      }
-      const float mean = s * (1.0f / UD);
-      float m2 = 0.f;
-#pragma unroll
-      for (int e = 0; e < UD; ++e) m2 += (v[e] - mean) * (v[e] - mean);
-      const float rstd = rsqrtf(m2 * (1.0f / UD) + p.eps);
-      u32x4 o;
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-        o[t] = pack_bf16x2((v[2 * t] - mean) * rstd * og[2 * t] + ob[2 * t],
-                           (v[2 * t + 1] - mean) * rstd * og[2 * t + 1] + ob[2 * t + 1]);
-      *reinterpret_cast<u32x4*>(p.y + (b * n + m) * UD) = o;
     };
     // pass 1: statistics (count, mean, M2) per example
     float cnt[UE], mu[UE], m2[UE];
@@ -176,7 +138,6 @@ __global__ __launch_bounds__(UT) void units_epilogue_kernel(UnitsArgs p, int64_t
         if (ex >= ne) break;
         const u32x4 xop = xc[ex];
         const f32x16 d = f_block(ex, xop);
-        if (h == 0 && m >= n_f && m < n) lcb_row(ex, m, xop);
         float s = 0.f, c = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -279,7 +240,7 @@ bool fmb_lcb_units_supported(int n, int d, int k, int n_l) {
 
 size_t fmb_lcb_units_workspace(int64_t batch, int n, int k, int n_l) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  return al((size_t)batch * n * UD * 2) + al((size_t)(k + n_l) * n * 2) + al((size_t)batch * UD * (k + n_l) * 4);
+  return al((size_t)batch * n * UD * 2) + al((size_t)(k + n_l) * n * 2) + al((size_t)batch * k * UD * 4);
 }
 
 hipError_t launch_fmb_lcb_units(const FmbLcbArgs& a, int64_t batch, void* scratch, hipStream_t stream,
@@ -291,8 +252,7 @@ hipError_t launch_fmb_lcb_units(const FmbLcbArgs& a, int64_t batch, void* scratc
   char* base = static_cast<char*>(scratch);
   uint16_t* xt = reinterpret_cast<uint16_t*>(base);
   uint16_t* wcat = reinterpret_cast<uint16_t*>(base + al((size_t)batch * a.n * UD * 2));
-  float* c = reinterpret_cast<float*>(base + al((size_t)batch * a.n * UD * 2) + al((size_t)(a.k + a.n_l) * a.n * 2));
-  const int N = a.k + a.n_l;
+  float* z = reinterpret_cast<float*>(base + al((size_t)batch * a.n * UD * 2) + al((size_t)(a.k + a.n_l) * a.n * 2));
   // [Phi; W_L] as one [k + n_l, n] operand
   hipError_t e = hipMemcpyAsync(wcat, a.phi, (size_t)a.k * a.n * 2, hipMemcpyDeviceToDevice, stream);
   if (e != hipSuccess) return e;
@@ -303,31 +263,30 @@ hipError_t launch_fmb_lcb_units(const FmbLcbArgs& a, int64_t batch, void* scratc
   hipLaunchKernelGGL(units_transpose_kernel, dim3((unsigned)tgrid), dim3(256), 0, stream, a.x, xt, batch, a.n);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  LinearArgs g;
-  g.a = xt;
-  g.w = wcat;
-  g.bias = nullptr;
-  g.c = c;
-  g.M = batch * UD;
-  g.N = N;
-  g.K = a.n;
-  g.act = kActNone;
+  UnitsGemmArgs g;
+  g.wcat = wcat;
+  g.xt = xt;
+  g.x = a.x;
+  g.out_gamma = a.out_gamma;
+  g.out_beta = a.out_beta;
+  g.z = z;
+  g.y = a.y;
+  g.batch = batch;
+  g.n = a.n;
+  g.k = a.k;
+  g.n_l = a.n_l;
+  g.eps = a.eps;
   int64_t gw = 0;
-  e = launch_linear_bf16_f32out(g, c, stream, &gw);
+  e = launch_units_gemm(g, stream, &gw);
   if (e != hipSuccess) return e;
   UnitsArgs u;
   u.x = a.x;
-  u.c = c;
+  u.z = z;
   u.fm_gamma = a.fm_gamma;
   u.fm_beta = a.fm_beta;
-  u.out_gamma = a.out_gamma;
-  u.out_beta = a.out_beta;
   u.fn = a.fn;
-  u.y = a.y;
   u.n = a.n;
   u.k = a.k;
-  u.n_f = a.n_f;
-  u.n_l = a.n_l;
   u.eps = a.eps;
   const int64_t groups = (batch + UE - 1) / UE;
   const int64_t egrid = groups < 2048 ? groups : 2048;

@@ -846,7 +846,129 @@ const LinearLnVariant* pick_linear_ln(int d) {
   return nullptr;
 }
 
+// Embedding units of width 8 (Wukong paper, section 2.1: each 8-wide unit
+// takes part in the interaction as a feature of its own), the left multiply of
+// the layer (section 2.2) over the whole batch: C'[r][(b, e)] =
+// sum_j [Phi; W_L][r][j] X_b[j][e], rows r of [Phi; W_L] against the columns
+// (example, element) of the transposed X.  A lane holds 4 consecutive
+// elements e0 .. e0 + 3 (e0 = 0 or 4) of one example and row, and lane ^ 16
+// the other 4, so the epilogue finishes everything that needs only this
+// product: Z_b rows (r < k) go out in fp32, [b][r][e], for the interaction;
+// the LCB rows (r = k + i) get the residual X_b[n_F + i], the LayerNorm over
+// their 8 values (one xor-shuffle per statistic) and go out as Y_b[n_F + i].
+struct UnitsGemmKArgs {
+  const uint16_t* wcat;      // [k + n_l][n] (the A operand)
+  const uint16_t* xt;        // [B 8][n]: xt[(b, e)][j] = X[b][j][e] (the W operand)
+  const uint16_t* x;         // [B][n][8]
+  const uint16_t* out_gamma; // [8] or null
+  const uint16_t* out_beta;
+  float* z;                  // [B][k][8]
+  uint16_t* y;               // [B][n][8]: rows n_f .. n - 1 written
+  int64_t M;                 // k + n_l
+  int N, K;                  // B 8, n
+  int k, n_f, n_l;
+  float eps;
+  int tiles_m, tiles_n;
+};
+
+template <int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(WGM * WGN * 64) void units_gemm_kernel(UnitsGemmKArgs p) {
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int MB = WTM / 16, NB = WTN / 16;
+  constexpr int UD = 8;
+  __shared__ __align__(16) uint16_t sA0[BM * kBK], sW0[BN * kBK], sA1[BM * kBK], sW1[BN * kBK];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int l16 = lane & 15, lg = lane >> 4;
+  int64_t m0;
+  int n0;
+  tile_origin(p.tiles_m, p.tiles_n, BM, BN, m0, n0);
+  f32x4 acc[NB][MB];
+  dma_mainloop<BM, BN, WGM, WGN, false>(p.wcat, p.xt, p.M, p.N, p.K, m0, n0, sA0, sW0, sA1, sW1, acc);
+  const int k = p.k, n = p.K, n_f = p.n_f, n_l = p.n_l;
+  const int e0 = (4 * lg) & (UD - 1);  // every column block starts at a multiple of 16
+  float og[4], ob[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    og[t] = p.out_gamma ? bf16_to_f32(p.out_gamma[e0 + t]) : 1.f;
+    ob[t] = p.out_beta ? bf16_to_f32(p.out_beta[e0 + t]) : 0.f;
+  }
+  // the residual elements of the LCB rows, all requested before the first store
+  u32x2 rv[NB][MB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int q = n0 + wn * WTN + i * 16 + lg * 4;
+    const int64_t b = q >> 3;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int r = (int)(m0 + wm * WTM + j * 16 + l16);
+      const bool lcb = r >= k && r < k + n_l && q < p.N;
+      rv[i][j] = lcb ? *reinterpret_cast<const u32x2*>(p.x + ((b * n + n_f + r - k) * UD + e0)) : u32x2{0u, 0u};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int q = n0 + wn * WTN + i * 16 + lg * 4;
+    const int64_t b = q >> 3;
+    const bool qv = q < p.N;
+#pragma unroll
+    for (int j = 0; j < MB; ++j) {
+      const int r = (int)(m0 + wm * WTM + j * 16 + l16);
+      const f32x4 a = acc[i][j];
+      if (r < k && qv) *reinterpret_cast<f32x4*>(p.z + (b * k + r) * UD + e0) = a;
+      const u32x2 x2 = rv[i][j];
+      float v[4] = {a[0] + bf16lo(x2[0]), a[1] + bf16hi(x2[0]), a[2] + bf16lo(x2[1]), a[3] + bf16hi(x2[1])};
+      // every lane takes part in the shuffles; only the LCB rows are stored
+      float sm = (v[0] + v[1]) + (v[2] + v[3]);
+      sm += __shfl_xor(sm, 16, kWave);
+      const float mean = sm * (1.0f / UD);
+      float sq = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) sq += (v[t] - mean) * (v[t] - mean);
+      sq += __shfl_xor(sq, 16, kWave);
+      const float rstd = rsqrtf(sq * (1.0f / UD) + p.eps);
+      if (r >= k && r < k + n_l && qv) {
+        u32x2 o;
+        o[0] = pack_bf16x2((v[0] - mean) * rstd * og[0] + ob[0], (v[1] - mean) * rstd * og[1] + ob[1]);
+        o[1] = pack_bf16x2((v[2] - mean) * rstd * og[2] + ob[2], (v[3] - mean) * rstd * og[3] + ob[3]);
+        *reinterpret_cast<u32x2*>(p.y + (b * n + n_f + r - k) * UD + e0) = o;
+      }
+    }
+  }
+}
+
 }  // namespace
+
+bool units_gemm_supported(int64_t batch, int n, int k, int n_l) {
+  return batch > 0 && batch * 8 <= 0x7fffffff && n > 0 && n % kBK == 0 && k > 0 && k % 4 == 0 && n_l > 0 &&
+         n_l % 4 == 0 && n_l <= n;
+}
+
+hipError_t launch_units_gemm(const UnitsGemmArgs& a, hipStream_t stream, int64_t* workgroups) {
+  if (!units_gemm_supported(a.batch, a.n, a.k, a.n_l) || !a.wcat || !a.xt || !a.x || !a.z || !a.y)
+    return hipErrorInvalidValue;
+  UnitsGemmKArgs k;
+  k.wcat = static_cast<const uint16_t*>(a.wcat);
+  k.xt = static_cast<const uint16_t*>(a.xt);
+  k.x = static_cast<const uint16_t*>(a.x);
+  k.out_gamma = static_cast<const uint16_t*>(a.out_gamma);
+  k.out_beta = static_cast<const uint16_t*>(a.out_beta);
+  k.z = a.z;
+  k.y = static_cast<uint16_t*>(a.y);
+  k.M = a.k + a.n_l;
+  k.N = (int)(a.batch * 8);
+  k.K = a.n;
+  k.k = a.k;
+  k.n_f = a.n - a.n_l;
+  k.n_l = a.n_l;
+  k.eps = a.eps;
+  k.tiles_m = (int)((k.M + 255) / 256);
+  k.tiles_n = (k.N + 255) / 256;
+  const int64_t blocks = (int64_t)k.tiles_m * k.tiles_n;
+  if (workgroups) *workgroups = blocks;
+  hipLaunchKernelGGL((units_gemm_kernel<256, 256, 2, 4>), dim3((unsigned)blocks), dim3(512), 0, stream, k);
+  return hipGetLastError();
+}
 
 bool linear_ln_bf16_supported(int64_t M, int N, int K, int d) {
   return M > 0 && K > 0 && K % kBK == 0 && d > 0 && N % d == 0 && N > 0 && pick_linear_ln(d) != nullptr;

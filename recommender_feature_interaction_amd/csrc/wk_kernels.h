@@ -72,10 +72,28 @@ struct FusionFfnArgs {
 };
 bool fusion_ffn_supported(int d, int d_ff);
 hipError_t launch_fusion_ffn(const FusionFfnArgs& a, hipStream_t stream, int64_t* workgroups);
-// Units of width d = 8 (fmb_lcb_units.hip): transpose, one batched GEMM with
-// fp32 output, and an epilogue kernel; needs fmb_lcb_units_workspace() bytes
+// Units of width d = 8 (fmb_lcb_units.hip): transpose, one batched GEMM whose
+// epilogue finishes the LCB rows, and an epilogue kernel for the FMB rows; needs
+// fmb_lcb_units_workspace() bytes
 // of scratch (16-byte aligned), n % 64 == 0, k % 4 == 0, k <= 32,
 // (k + n_l) % 8 == 0.
+// The units' batched product with the LCB rows finished in its epilogue
+// (linear_bf16.hip): Z (fp32, [B][k][8]) and Y's LCB rows (rows n - n_l ..)
+// from the transposed X; n % 64 == 0, k % 4 == 0, n_l % 4 == 0.
+struct UnitsGemmArgs {
+  const void* wcat;  // [k + n_l][n] bf16
+  const void* xt;    // [B 8][n] bf16, xt[(b, e)][j] = X[b][j][e]
+  const void* x;     // [B][n][8] bf16
+  const void* out_gamma;
+  const void* out_beta;
+  float* z;
+  void* y;
+  int64_t batch;
+  int n, k, n_l;
+  float eps;
+};
+bool units_gemm_supported(int64_t batch, int n, int k, int n_l);
+hipError_t launch_units_gemm(const UnitsGemmArgs& a, hipStream_t stream, int64_t* workgroups);
 bool fmb_lcb_units_supported(int n, int d, int k, int n_l);
 size_t fmb_lcb_units_workspace(int64_t batch, int n, int k, int n_l);
 hipError_t launch_fmb_lcb_units(const FmbLcbArgs& a, int64_t batch, void* scratch, hipStream_t stream,

@@ -136,7 +136,7 @@ LayerPlan plan_layer(const wk_layer_desc& d, int64_t batch) {
     off += align_up(B * (size_t)d.n_f * d.d * es);
   }
   p.use_units = units_path(d);
-  if (p.use_units) {  // transposed X, [Phi; W_L], fp32 [Z; Lc] (dead once Fn and the LCB rows are written)
+  if (p.use_units) {  // transposed X, [Phi; W_L], fp32 Z (dead once Fn and the LCB rows are written)
     p.units = off;
     off += align_up(wk::fmb_lcb_units_workspace(batch, d.n, d.k, d.n_l));
   }

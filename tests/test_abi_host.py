@@ -75,11 +75,11 @@ def test_workspace_sizes_follow_layout():
     assert wk.stack_workspace_size([C2], B) == scratch
     assert wk.stack_workspace_size([C2] * 2, B) == scratch + act
     assert wk.stack_workspace_size([C2] * 8, B) == scratch + 2 * act
-    # units of width 8: + transposed X, [Phi; W_L] and the fp32 [Z; Lc] after the M buffer
+    # units of width 8: + transposed X, [Phi; W_L] and the fp32 Z after the M buffer
     u = wk.LayerSpec(64, 8, 8, 32, 32, (512, 64, 256))
     B = 9
     assert wk.layer_workspace_size(u, B) == (al(B * 512 * 2) + al(B * 64 * 2) + al(B * 256 * 2)
-                                             + al(al(B * 64 * 8 * 2) + al(40 * 64 * 2) + al(B * 8 * 40 * 4)))
+                                             + al(al(B * 64 * 8 * 2) + al(40 * 64 * 2) + al(B * 8 * 8 * 4)))
     f32 = wk.LayerSpec(16, 16, 4, 8, 8, (64, 64, 128), dtype="f32")
     assert wk.layer_workspace_size(f32, 64) == al(64 * 64 * 4) + al(64 * 64 * 4) + al(64 * 128 * 4)
 
