@@ -37,6 +37,7 @@ namespace wk {
 namespace {
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 #define WK_LDS_I16X4(p) ((__attribute__((address_space(3))) i16x4*)(p))
 #define WK_LDSV(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -542,6 +543,344 @@ __global__ __launch_bounds__(NTHREAD, 2) void fmb_lcb_stream_kernel(FmbLcbArgs p
 }
 
 
+// FMB + LCB with [Phi; W_L] held in registers and X streamed in 32-column
+// chunks (bf16, fp32 accumulation; the plain forward).
+//
+// The interaction is a sum over embedding columns: with Z_b = Phi X_b,
+// F_b = X_b Z_b^T = sum_c X_b[:, c] Z_b[:, c]^T over column blocks c, and
+// Z_b[:, c] = Phi X_b[:, c] needs only the same columns of X_b (Wukong paper,
+// section 2.2: compress, then interact).  The LCB rows Lc_b = W_L X_b split by
+// columns the same way.  So one pass over X, chunk by chunk, finishes
+// everything an example needs while the chunk is in LDS: [Z; Lc][:, c], the
+// residual X_b[n_F + i][c] added to the LCB columns, Z[:, c] rounded to bf16
+// into LDS, and F_b += X_b[:, c] Z_b[:, c]^T.  X is read from HBM exactly once
+// per layer (the two-phase kernel reads it twice when a group's X does not
+// stay in L2 between its phases).
+//
+// Work split: a persistent workgroup of 4 waves (one per SIMD) takes one
+// example at a time.  The weights are the same for every example, so each
+// wave keeps its MFMA operand fragments of [Phi; W_L] in registers for the
+// whole kernel: its Phi tile (wave < ceil(k / 16)) and W_L tiles wave and
+// wave + 4, all n columns (the n = 256 layer: 96 registers).  LDS then holds
+// only the X ring: NCH = d / 32 chunks of n rows x 32 columns (16 KB) per
+// example in NCH slots, each chunk requested NCH - 1 chunks ahead (the next
+// example's first chunks are in flight during this one's epilogue).  Phase A
+// of a chunk multiplies its two 16-column tiles (the X^T operand, read with
+// ds_read_b64_tr_b16) by the wave's weight tiles over K = n; phase B adds
+// Z_c X_c^T to the wave's F^T blocks (rows wave + 4 mi of X).  A wave keeps
+// its two LCB row tiles of every chunk in registers until the example's
+// LayerNorm over d.
+template <int N, int D, int MPW, int KJ>
+__global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, int64_t batch, StreamShape sh) {
+  constexpr int NW = 4;                 // waves
+  constexpr int CW = 32;                // chunk width (embedding columns)
+  constexpr int NCH = D / CW;           // chunks per example = ring slots
+  constexpr int S = NCH;
+  constexpr int STEPS = N / KC;         // K steps of phase A
+  constexpr int MT = N / 16;            // 16-row blocks of X
+  constexpr int CX = N / 16 / NW;       // chunk DMA instructions per wave (1 KB = 16 rows x 32 columns)
+  constexpr int ZP = CW + 8;            // Zs row pitch (u16)
+  constexpr int SX = N * CW;            // ring slot (u16)
+  // vector-memory operations a wave issues per example after the last chunk copy
+  // of the next example it sent: the LCB rows (2 tiles x NCH x 2) and Fn (MPW x KJ)
+  constexpr int STORES = 2 * NCH * 2 + MPW * KJ;
+  static_assert(D % CW == 0 && N % (16 * NW) == 0 && MT == NW * MPW, "shape");
+  static_assert(S >= 3 && S <= 5, "ring slots");
+  static_assert((S - 2) * CX + STORES <= 63, "vmcnt range");
+  __shared__ __align__(16) uint16_t x0[SX], x1[SX], x2[SX], x3[S > 3 ? SX : 8], x4[S > 4 ? SX : 8];
+  // a select rather than a table of pointers: a table with a constant initialiser may be
+  // placed in constant memory, and a pointer loaded from there is taken to be global
+  auto xslot = [&](int i) -> uint16_t* { return i == 0 ? x0 : i == 1 ? x1 : i == 2 ? x2 : i == 3 ? x3 : x4; };
+  __shared__ __align__(16) uint16_t Zs[KJ * 16 * ZP];
+  __shared__ __align__(16) uint16_t Gs[2 * D];
+  __shared__ __align__(16) uint16_t Gfm[2 * N * 16 * KJ];  // the FMB LayerNorm's gamma, then beta ([n k] each)
+  __shared__ float red[2 * NW];
+
+  const int k = p.k, n_f = p.n_f;
+  const int KZ = sh.kz, ZTP = sh.ztp;
+  const int KT = (k + 15) >> 4;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int li = lane & 15, lg = lane >> 4;
+  const int64_t first = blockIdx.x;
+  if (first >= batch) return;
+  const int64_t stride = gridDim.x;
+
+  for (int i = tid; i < 2 * D; i += 256) {
+    const uint16_t* src = i < D ? p.out_gamma : p.out_beta;
+    Gs[i] = src ? src[i < D ? i : i - D] : (uint16_t)(i < D ? 0x3f80u : 0u);
+  }
+  for (int i = tid; i < KJ * 16 * ZP; i += 256) Zs[i] = 0;  // rows past 16 KZ stay zero
+  {  // the FMB LayerNorm's gamma / beta into LDS, 16 bytes per lane, all loads issued together
+    const int nkg = N * k / 8;  // k % 16 == 0
+    const __amdgpu_buffer_rsrc_t rgam =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.fm_gamma, (short)0, p.fm_gamma ? N * k * 2 : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rbet =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.fm_beta, (short)0, p.fm_beta ? N * k * 2 : 0, 0x00020000);
+    constexpr int GR = (N * KJ * 16 / 8 + 255) / 256;
+    u32x4 gv[GR], bv[GR];
+#pragma unroll
+    for (int r = 0; r < GR; ++r) {
+      const uint32_t off = (uint32_t)(tid + r * 256) * 16u;
+      gv[r] = p.fm_gamma ? __builtin_amdgcn_raw_buffer_load_b128(rgam, off, 0, 0)
+                         : u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};
+      bv[r] = __builtin_amdgcn_raw_buffer_load_b128(rbet, off, 0, 0);  // zero when absent
+    }
+#pragma unroll
+    for (int r = 0; r < GR; ++r) {
+      const int i = tid + r * 256;
+      if (i < nkg) {
+        *reinterpret_cast<u32x4*>(Gfm + i * 8) = gv[r];
+        *reinterpret_cast<u32x4*>(Gfm + N * k + i * 8) = bv[r];
+      }
+    }
+  }
+
+  // ---- chunk c of example b into a slot: row r of the chunk at r CW, lane l of
+  // instruction j holding row 16 j + l / 4, columns 8 (l % 4) .. + 7.  An example
+  // past the batch gets a resource of no records: its lanes read nothing and the
+  // slot it lands in is never consumed; issuing it anyway keeps the count of copies
+  // in flight the same at every chunk.
+  // The copies are written as inline asm: the compiler then does not track them, and
+  // inserts no wait for them before LDS reads it cannot prove disjoint from the slot
+  // being filled (it loses track of which slot a read addresses).  Every wait for them
+  // is explicit (vmcnt before the chunk's barrier), and the asm's memory clobber keeps
+  // LDS accesses from moving across an issue.
+  const uint32_t xlane = (uint32_t)(((lane >> 2) * D + (lane & 3) * 8) * 2);
+  auto dma_chunk = [&](uint16_t* sx, int64_t b, int c) {
+    const bool in = b < batch;  // uniform
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(in ? p.x + b * (int64_t)N * D : p.x), (short)0, in ? N * D * 2 : 0, 0x00020000);
+#pragma unroll
+    for (int q = 0; q < CX; ++q) {
+      const int j = q * NW + wave;
+      const uint32_t lds = (uint32_t)reinterpret_cast<uintptr_t>(WK_LDSV(sx + j * 512));
+      // s_nop 4: the hazard recogniser does not look inside asm, and the offset, resource or
+      // M0 may have just been written by a vector instruction (v_readlane), which a vector
+      // memory instruction may only read five wait states later
+      asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                   :
+                   : "v"(xlane), "s"(rx), "s"(__builtin_amdgcn_readfirstlane((16 * j * D + CW * c) * 2)),
+                     "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                   : "memory");
+    }
+  };
+  // ---- the weight fragments, from the packed [Phi; W_L] (step t, tile i: 1 KB at
+  // (t ZTP + i) 1024; lane 4 r + g of it holds row 16 i + r, columns 32 t + 8 g ..):
+  // lane (li, lg) takes row li, columns 8 lg .. of each step
+  u32x4 wz[STEPS], wlc[2][STEPS];
+  {
+    const __amdgpu_buffer_rsrc_t rpk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)p.wpack, (short)0, STEPS * ZTP * 1024, 0x00020000);
+    const uint32_t lo = (uint32_t)(4 * li + lg) * 16u;
+#pragma unroll
+    for (int t = 0; t < STEPS; ++t) {
+      const uint32_t zo = wave < KZ ? (uint32_t)((t * ZTP + wave) * 1024) + lo : kOOB;
+      wz[t] = __builtin_amdgcn_raw_buffer_load_b128(rpk, zo, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        wlc[i][t] = __builtin_amdgcn_raw_buffer_load_b128(rpk, (uint32_t)((t * ZTP + KZ + wave + NW * i) * 1024) + lo,
+                                                           0, 0);
+    }
+  }
+  // the first example's chunks 0 .. S - 2 (after the register loads, which the first wait covers)
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) dma_chunk(xslot(s), first, s);
+
+  const float inv_d = 1.0f / static_cast<float>(D);
+  const float inv_nk = 1.0f / static_cast<float>(N * k);
+  const int xa = (8 * lg + (li >> 2)) * CW + 4 * (li & 3);  // X^T operand lanes (ds_read_b64_tr_b16)
+  const uint32_t fkb = (uint32_t)p.fn_kblock_rows;
+  const bool has_z = wave < KZ;  // wave-uniform
+
+  for (int64_t b = first; b < batch; b += stride) {
+    f32x4 lc[2][NCH][2];  // LCB row tiles: lane holds e = 32 c + 16 et + 4 lg + t, row 16 (wave + 4 i) + li
+    f32x4 facc[MPW][KJ];  // F^T blocks: lane holds j = 16 jt + 4 lg + t, m = 16 (wave + 4 mi) + li
+#pragma unroll
+    for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt) facc[mi][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint16_t* sx = xslot(c);
+      // chunk c landed: newer copies are the S - 2 chunks after it, plus, at an
+      // example's first chunk, the previous example's stores (issued after them)
+      if (c == 0 && b != first) __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX + STORES));
+      else __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX));
+      ring_barrier();  // the chunk landed for every wave; slot c - 1 and Zs are free
+      // phase A: [Z; Lc]^T[:, chunk] = X_c^T [Phi; W_L]^T, the LCB accumulators starting
+      // from the residual rows X[n_F + i][chunk] (so no vector ALU touches them before the
+      // LayerNorm)
+      f32x4 za[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int zl = (wave + NW * i) * 16 + li;  // < n_l (every W_L tile is full)
+        const uint16_t* xr = sx + (n_f + zl) * CW + lg * 4;
+#pragma unroll
+        for (int et = 0; et < 2; ++et) {
+          const u32x2 xv = *reinterpret_cast<const u32x2*>(xr + et * 16);
+          lc[i][c][et] = f32x4{bf16lo(xv[0]), bf16hi(xv[0]), bf16lo(xv[1]), bf16hi(xv[1])};
+        }
+      }
+      // the next step's X^T operands are requested before this step's MFMAs
+      u32x4 xn0 = tr_pair(sx + xa, sx + xa + 4 * CW), xn1 = tr_pair(sx + xa + 16, sx + xa + 4 * CW + 16);
+#pragma unroll
+      for (int t = 0; t < STEPS; ++t) {
+        const u32x4 xo0 = xn0, xo1 = xn1;
+        if (t + 1 < STEPS) {
+          const uint16_t* xs = sx + (t + 1) * KC * CW + xa;
+          xn0 = tr_pair(xs, xs + 4 * CW);
+          xn1 = tr_pair(xs + 16, xs + 4 * CW + 16);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          lc[i][c][0] = mfma16x16x32(xo0, wlc[i][t], lc[i][c][0]);
+          lc[i][c][1] = mfma16x16x32(xo1, wlc[i][t], lc[i][c][1]);
+        }
+        // (waves past the Phi tiles hold zero fragments: no branch in the MFMA stream)
+        za[0] = mfma16x16x32(xo0, wz[t], za[0]);
+        za[1] = mfma16x16x32(xo1, wz[t], za[1]);
+      }
+      // Z columns to LDS (bf16, the interaction's operand)
+      if (has_z) {
+        uint16_t* zrow = Zs + (wave * 16 + li) * ZP + lg * 4;
+#pragma unroll
+        for (int et = 0; et < 2; ++et) {
+          u32x2 v;
+          v[0] = pack_bf16x2(za[et][0], za[et][1]);
+          v[1] = pack_bf16x2(za[et][2], za[et][3]);
+          *reinterpret_cast<u32x2*>(zrow + et * 16) = v;
+        }
+      }
+      ring_barrier();  // Z columns of the chunk complete
+      // phase B: F^T += Z_c X_c^T
+      u32x4 zf[KJ];
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt) zf[jt] = *reinterpret_cast<const u32x4*>(Zs + (jt * 16 + li) * ZP + lg * 8);
+#pragma unroll
+      for (int mi = 0; mi < MPW; ++mi) {
+        const u32x4 xf = *reinterpret_cast<const u32x4*>(sx + ((wave + mi * NW) * 16 + li) * CW + lg * 8);
+#pragma unroll
+        for (int jt = 0; jt < KJ; ++jt)
+          if (jt < KT) facc[mi][jt] = mfma16x16x32(zf[jt], xf, facc[mi][jt]);
+      }
+      // chunk c + S - 1 of the sequence into the slot chunk c - 1 left (every wave passed
+      // this chunk's barrier, so none still reads it): this example's last chunk when
+      // c == 0, else the next example's chunk c - 1.  Issued after this chunk's LDS
+      // reads, which then need no wait for it.
+      if (c == 0) dma_chunk(xslot(S - 1), b, S - 1);
+      else dma_chunk(xslot(c - 1), b + stride, c - 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- LCB rows: LayerNorm over d of Lc + residual, Y[n_F + i]
+    const __amdgpu_buffer_rsrc_t ry =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.y + b * (int64_t)N * D), (short)0, N * D * 2, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int zl = (wave + NW * i) * 16 + li;
+      float sm = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int et = 0; et < 2; ++et)
+          sm += (lc[i][c][et][0] + lc[i][c][et][1]) + (lc[i][c][et][2] + lc[i][c][et][3]);
+      sm += __shfl_xor(sm, 16, kWave);
+      sm += __shfl_xor(sm, 32, kWave);
+      const float mean = sm * inv_d;
+      float q = 0.f;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int et = 0; et < 2; ++et)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const float dv = lc[i][c][et][t] - mean;
+            q += dv * dv;
+          }
+      q += __shfl_xor(q, 16, kWave);
+      q += __shfl_xor(q, 32, kWave);
+      const float rstd = rsqrtf(q * inv_d + p.eps);
+      const uint32_t yoff = (uint32_t)((n_f + zl) * D) * 2u;
+#pragma unroll
+      for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int et = 0; et < 2; ++et) {
+          const int e = c * CW + et * 16 + lg * 4;
+          const u32x2 g2 = *reinterpret_cast<const u32x2*>(Gs + e);
+          const u32x2 b2 = *reinterpret_cast<const u32x2*>(Gs + D + e);
+          const f32x4 v = lc[i][c][et];
+          u32x2 o;
+          o[0] = pack_bf16x2((v[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(b2[0]),
+                             (v[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(b2[0]));
+          o[1] = pack_bf16x2((v[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(b2[1]),
+                             (v[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(b2[1]));
+          __builtin_amdgcn_raw_buffer_store_b64(o, ry, yoff + e * 2, 0, 0);
+        }
+    }
+
+    // ---- the FMB LayerNorm over vec(F) (n k values) and Fn
+    float sm = 0.f;
+#pragma unroll
+    for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (jt * 16 + lg * 4 + t < k) sm += facc[mi][jt][t];
+    sm = group_sum_v<64>(sm);
+    if (lane == 0) red[wave] = sm;
+    ring_barrier();
+    const float mean = ((red[0] + red[1]) + (red[2] + red[3])) * inv_nk;
+    float q = 0.f;
+#pragma unroll
+    for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (jt * 16 + lg * 4 + t < k) {
+            const float dv = facc[mi][jt][t] - mean;
+            q += dv * dv;
+          }
+    q = group_sum_v<64>(q);
+    if (lane == 0) red[NW + wave] = q;
+    ring_barrier();
+    const float rstd = rsqrtf(((red[NW] + red[NW + 1]) + (red[NW + 2] + red[NW + 3])) * inv_nk + p.eps);
+    // Fn row-major, or K-blocked over the whole batch (64-column blocks of fn_kblock_rows rows);
+    // every lane stores (those past k to an offset past the record count), so each wave
+    // issues exactly MPW x KJ stores per example
+    // (the resource is assembled from uniform values: the compiler cannot tell the select is
+    // uniform, and a resource it takes for divergent turns every store into a loop over lanes)
+    const uint64_t fbase = reinterpret_cast<uint64_t>(fkb ? p.fn : p.fn + b * (int64_t)N * k);
+    const uint64_t fb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(fbase >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)fbase);
+    const __amdgpu_buffer_rsrc_t rfn = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>(fb), (short)0,
+        __builtin_amdgcn_readfirstlane(fkb ? (int)(fkb * (uint32_t)(N * k) * 2u) : N * k * 2), 0x00020000);
+#pragma unroll
+    for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+      for (int jt = 0; jt < KJ; ++jt) {
+        const int m = (wave + mi * NW) * 16 + li;
+        const int j0 = jt * 16 + lg * 4;  // k % 4 == 0: the 4 values j0 .. j0+3 are all valid or all not
+        const int gi = j0 < k ? m * k + j0 : 0;
+        const u32x2 g2 = *reinterpret_cast<const u32x2*>(Gfm + gi);
+        const u32x2 b2 = *reinterpret_cast<const u32x2*>(Gfm + N * k + gi);
+        const f32x4 f = facc[mi][jt];
+        u32x2 o;
+        o[0] = pack_bf16x2((f[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(b2[0]),
+                           (f[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(b2[0]));
+        o[1] = pack_bf16x2((f[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(b2[1]),
+                           (f[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(b2[1]));
+        const uint32_t cc = (uint32_t)(m * k + j0);  // 4-aligned: the 4 values share a 64-column block
+        const uint32_t off = j0 >= k ? kOOB : fkb ? (((cc >> 6) * fkb + (uint32_t)b) * 64u + (cc & 63u)) * 2u : cc * 2u;
+        __builtin_amdgcn_raw_buffer_store_b64(o, rfn, off, 0, 0);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(vm_enc(0));  // the copies issued past the last example
+}
+
 // [Phi; W_L] in the ring's order: 16-byte chunk c = (t ZTP + i) 64 + l holds
 // row 16 i + l / 4 of [Phi (padded to KZ tiles, or not at all when contig); W_L],
 // columns 32 t + 8 (l % 4) .. + 7, zero outside the matrices and in the tiles past ZT.
@@ -620,6 +959,15 @@ const StreamVariant* pick_stream(int n, int d, int k, int n_l, StreamShape* out)
   return nullptr;
 }
 
+// The d-chunked kernel (weights in registers) serves the plain forward of the
+// n = 256, d = 160 layer with n_l = 128 (8 full W_L tiles, two per wave) and
+// k <= 48, k % 16 == 0 (at most 3 Phi tiles, whole ones), packed by the
+// n <= 256 streamed variant (Phi padded to whole tiles).
+bool dchunk_fits(const StreamVariant& v, const StreamShape& sh, int n, int d, int k, int n_l) {
+  return n == 256 && d == 160 && n_l == 128 && k <= 48 && k % 16 == 0 && !v.contig && sh.kz == k / 16 &&
+         sh.zt == sh.kz + 8 && sh.steps == 8 && sh.ztp >= sh.zt;
+}
+
 }  // namespace
 
 bool fmb_lcb_stream_supported(int n, int d, int k, int n_l) { return pick_stream(n, d, k, n_l, nullptr) != nullptr; }
@@ -643,6 +991,13 @@ hipError_t launch_fmb_lcb_stream(const FmbLcbArgs& a, int64_t batch, hipStream_t
   const int chunks = sh.steps * sh.ztp * 64;
   hipLaunchKernelGGL(pack_stream_weights_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, stream, a.phi,
                      a.w_l, a.wpack, a.n, a.k, a.n_l, sh.kz, sh.zt, sh.ztp, sh.steps, v->contig ? 1 : 0);
+  if (a.z_out == nullptr && dchunk_fits(*v, sh, a.n, a.d, a.k, a.n_l)) {
+    const int64_t g = batch < 256 ? batch : 256;
+    if (workgroups) *workgroups = g;
+    hipLaunchKernelGGL((fmb_lcb_dchunk_kernel<256, 160, 4, 3>), dim3((unsigned)g), dim3(256), 0, stream, a, batch,
+                       sh);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(a.z_out ? v->kernel_train : v->kernel, dim3((unsigned)grid), dim3(NTHREAD), 0, stream, a, batch,
                      sh);
   return hipGetLastError();
