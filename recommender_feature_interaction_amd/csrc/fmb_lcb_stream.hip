@@ -581,8 +581,7 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
   constexpr int CX = N / 16 / NW;       // chunk DMA instructions per wave (1 KB = 16 rows x 32 columns)
   constexpr int ZP = CW + 8;            // Zs row pitch (u16)
   constexpr int SX = N * CW;            // ring slot (u16)
-  // vector-memory operations a wave issues per example after the last chunk copy
-  // of the next example it sent: the LCB rows (2 tiles x NCH x 2) and Fn (MPW x KJ)
+  // stores a wave issues per example: the LCB rows (2 tiles x NCH x 2) and Fn (MPW x KJ)
   constexpr int STORES = 2 * NCH * 2 + MPW * KJ;
   static_assert(D % CW == 0 && N % (16 * NW) == 0 && MT == NW * MPW, "shape");
   static_assert(S >= 3 && S <= 5, "ring slots");
@@ -592,7 +591,7 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
   // placed in constant memory, and a pointer loaded from there is taken to be global
   auto xslot = [&](int i) -> uint16_t* { return i == 0 ? x0 : i == 1 ? x1 : i == 2 ? x2 : i == 3 ? x3 : x4; };
   __shared__ __align__(16) uint16_t Zs[KJ * 16 * ZP];
-  __shared__ __align__(16) uint16_t Gs[2 * D];
+  __shared__ __align__(16) float GsF[2 * D];  // the output LayerNorm's gamma, then beta (fp32)
   __shared__ __align__(16) uint16_t Gfm[2 * N * 16 * KJ];  // the FMB LayerNorm's gamma, then beta ([n k] each)
   __shared__ float red[2 * NW];
 
@@ -608,7 +607,7 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
 
   for (int i = tid; i < 2 * D; i += 256) {
     const uint16_t* src = i < D ? p.out_gamma : p.out_beta;
-    Gs[i] = src ? src[i < D ? i : i - D] : (uint16_t)(i < D ? 0x3f80u : 0u);
+    GsF[i] = src ? bf16_to_f32(src[i < D ? i : i - D]) : (i < D ? 1.f : 0.f);
   }
   for (int i = tid; i < KJ * 16 * ZP; i += 256) Zs[i] = 0;  // rows past 16 KZ stay zero
   {  // the FMB LayerNorm's gamma / beta into LDS, 16 bytes per lane, all loads issued together
@@ -693,6 +692,86 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
   const uint32_t fkb = (uint32_t)p.fn_kblock_rows;
   const bool has_z = wave < KZ;  // wave-uniform
 
+  // The output stage of an example (the LCB rows' LayerNorm and Y stores, the FMB
+  // LayerNorm and Fn stores) is software-pipelined into the next example's first
+  // chunk: its statistics are reduced at the end of the example (the FMB sums go
+  // to `red`, published by the next chunk's barrier), and its 32 normalise-and-store
+  // units are spread over that chunk's K steps, where the vector ALU work and the
+  // stores fill issue slots between MFMAs.  Before the first example the units run
+  // on zeros with resources of no records (the stores are dropped), so every
+  // example's first chunk issues the same 32 stores.
+  f32x4 plc[2][NCH][2];  // the previous example's LCB rows (Lc + residual)
+  f32x4 pfacc[MPW][KJ];  // and its F^T blocks
+  float pmean[2] = {0.f, 0.f}, prstd[2] = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) plc[i][c][0] = plc[i][c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+    for (int jt = 0; jt < KJ; ++jt) pfacc[mi][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (lane == 0) red[wave] = red[NW + wave] = 0.f;
+  int64_t pb = first;  // the previous example
+  bool live = false;   // uniform: there is a previous example
+  constexpr int UNITS = 2 * NCH * 2 + MPW * KJ;  // = STORES
+  static_assert(UNITS == STORES, "one store per unit");
+
+  // resources of the previous example's outputs (no records before the first example)
+  auto out_rsrc = [&](__amdgpu_buffer_rsrc_t& ry, __amdgpu_buffer_rsrc_t& rfn) {
+    ry = __builtin_amdgcn_make_buffer_rsrc((void*)(p.y + pb * (int64_t)N * D), (short)0, live ? N * D * 2 : 0,
+                                           0x00020000);
+    // (assembled from uniform values: the compiler cannot tell the select is uniform, and a
+    // resource it takes for divergent turns every store into a loop over lanes)
+    const uint64_t fbase = reinterpret_cast<uint64_t>(fkb ? p.fn : p.fn + pb * (int64_t)N * k);
+    const uint64_t fb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(fbase >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)fbase);
+    const int frec = !live ? 0 : fkb ? (int)(fkb * (uint32_t)(N * k) * 2u) : N * k * 2;
+    rfn = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(fb), (short)0,
+                                            __builtin_amdgcn_readfirstlane(frec), 0x00020000);
+  };
+  // unit u < 2 NCH 2: LCB tile i, chunk c, half et of the previous example; else its Fn block
+  auto out_unit = [&](int u, const __amdgpu_buffer_rsrc_t& ry, const __amdgpu_buffer_rsrc_t& rfn, float fm_mean,
+                      float fm_rstd) {
+    if (u < 2 * NCH * 2) {
+      const int i = u / (2 * NCH), c = (u / 2) % NCH, et = u % 2;
+      const int zl = (wave + NW * i) * 16 + li;
+      const int e = c * CW + et * 16 + lg * 4;
+      const f32x4 g4 = *reinterpret_cast<const f32x4*>(GsF + e);
+      const f32x4 b4 = *reinterpret_cast<const f32x4*>(GsF + D + e);
+      const f32x4 v = plc[i][c][et];
+      const float mean = pmean[i], rstd = prstd[i];
+      u32x2 o;
+      o[0] = pack_bf16x2((v[0] - mean) * rstd * g4[0] + b4[0], (v[1] - mean) * rstd * g4[1] + b4[1]);
+      o[1] = pack_bf16x2((v[2] - mean) * rstd * g4[2] + b4[2], (v[3] - mean) * rstd * g4[3] + b4[3]);
+      __builtin_amdgcn_raw_buffer_store_b64(o, ry, (uint32_t)(((n_f + zl) * D + e) * 2), 0, 0);
+    } else {
+      const int q = u - 2 * NCH * 2, mi = q / KJ, jt = q % KJ;
+      const int m = (wave + mi * NW) * 16 + li;
+      const int j0 = jt * 16 + lg * 4;  // k % 4 == 0: the 4 values j0 .. j0+3 are all valid or all not
+      const int gi = j0 < k ? m * k + j0 : 0;
+      const u32x2 g2 = *reinterpret_cast<const u32x2*>(Gfm + gi);
+      const u32x2 b2 = *reinterpret_cast<const u32x2*>(Gfm + N * k + gi);
+      const f32x4 f = pfacc[mi][jt];
+      u32x2 o;
+      o[0] = pack_bf16x2((f[0] - fm_mean) * fm_rstd * bf16lo(g2[0]) + bf16lo(b2[0]),
+                         (f[1] - fm_mean) * fm_rstd * bf16hi(g2[0]) + bf16hi(b2[0]));
+      o[1] = pack_bf16x2((f[2] - fm_mean) * fm_rstd * bf16lo(g2[1]) + bf16lo(b2[1]),
+                         (f[3] - fm_mean) * fm_rstd * bf16hi(g2[1]) + bf16hi(b2[1]));
+      // every lane stores (those past k to an offset past the record count), so each
+      // unit is exactly one store
+      const uint32_t cc = (uint32_t)(m * k + j0);  // 4-aligned: the 4 values share a 64-column block
+      const uint32_t off = j0 >= k ? kOOB : fkb ? (((cc >> 6) * fkb + (uint32_t)pb) * 64u + (cc & 63u)) * 2u : cc * 2u;
+      __builtin_amdgcn_raw_buffer_store_b64(o, rfn, off, 0, 0);
+    }
+  };
+  // the FMB LayerNorm statistics of the previous example, from every wave's sums
+  auto fm_stats = [&](float& mean, float& rstd) {
+    mean = ((red[0] + red[1]) + (red[2] + red[3])) * inv_nk;
+    const float ex2 = ((red[NW] + red[NW + 1]) + (red[NW + 2] + red[NW + 3])) * inv_nk;
+    rstd = rsqrtf(fmaxf(ex2 - mean * mean, 0.f) + p.eps);
+  };
+
   for (int64_t b = first; b < batch; b += stride) {
     f32x4 lc[2][NCH][2];  // LCB row tiles: lane holds e = 32 c + 16 et + 4 lg + t, row 16 (wave + 4 i) + li
     f32x4 facc[MPW][KJ];  // F^T blocks: lane holds j = 16 jt + 4 lg + t, m = 16 (wave + 4 mi) + li
@@ -703,11 +782,18 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const uint16_t* sx = xslot(c);
-      // chunk c landed: newer copies are the S - 2 chunks after it, plus, at an
-      // example's first chunk, the previous example's stores (issued after them)
-      if (c == 0 && b != first) __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX + STORES));
+      // chunk c landed.  Newer operations: the copies of the S - 2 chunks after it, and,
+      // for chunks 1 .. S - 2, the previous example's stores, issued in chunk 0 after
+      // those chunks' copies (chunk 0's own copy came before them, chunk S - 1's after)
+      if (c >= 1 && c <= S - 2) __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX + STORES));
       else __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX));
       ring_barrier();  // the chunk landed for every wave; slot c - 1 and Zs are free
+      __amdgpu_buffer_rsrc_t ry, rfn;
+      float fm_mean = 0.f, fm_rstd = 0.f;
+      if (c == 0) {
+        out_rsrc(ry, rfn);
+        fm_stats(fm_mean, fm_rstd);
+      }
       // phase A: [Z; Lc]^T[:, chunk] = X_c^T [Phi; W_L]^T, the LCB accumulators starting
       // from the residual rows X[n_F + i][chunk] (so no vector ALU touches them before the
       // LayerNorm)
@@ -740,6 +826,10 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
         // (waves past the Phi tiles hold zero fragments: no branch in the MFMA stream)
         za[0] = mfma16x16x32(xo0, wz[t], za[0]);
         za[1] = mfma16x16x32(xo1, wz[t], za[1]);
+        if (c == 0) {  // the previous example's output units, UNITS / STEPS per step
+#pragma unroll
+          for (int u = t * UNITS / STEPS; u < (t + 1) * UNITS / STEPS; ++u) out_unit(u, ry, rfn, fm_mean, fm_rstd);
+        }
       }
       // Z columns to LDS (bf16, the interaction's operand)
       if (has_z) {
@@ -773,110 +863,67 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
     }
     __builtin_amdgcn_sched_barrier(0);
 
-    // ---- LCB rows: LayerNorm over d of Lc + residual, Y[n_F + i]
-    const __amdgpu_buffer_rsrc_t ry =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(p.y + b * (int64_t)N * D), (short)0, N * D * 2, 0x00020000);
+    // ---- end of the example: its LayerNorm statistics; the normalisation and the stores
+    // run in the next example's first chunk (or after the loop)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int zl = (wave + NW * i) * 16 + li;
-      float sm = 0.f;
-#pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int et = 0; et < 2; ++et)
-          sm += (lc[i][c][et][0] + lc[i][c][et][1]) + (lc[i][c][et][2] + lc[i][c][et][3]);
-      sm += __shfl_xor(sm, 16, kWave);
-      sm += __shfl_xor(sm, 32, kWave);
-      const float mean = sm * inv_d;
-      float q = 0.f;
+      // one pass: the sum and the sum of squares (fp32; the rows are O(1) LayerNorm inputs)
+      float sm = 0.f, sq = 0.f;
 #pragma unroll
       for (int c = 0; c < NCH; ++c)
 #pragma unroll
         for (int et = 0; et < 2; ++et)
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
-            const float dv = lc[i][c][et][t] - mean;
-            q += dv * dv;
+            sm += lc[i][c][et][t];
+            sq += lc[i][c][et][t] * lc[i][c][et][t];
           }
-      q += __shfl_xor(q, 16, kWave);
-      q += __shfl_xor(q, 32, kWave);
-      const float rstd = rsqrtf(q * inv_d + p.eps);
-      const uint32_t yoff = (uint32_t)((n_f + zl) * D) * 2u;
+      sm += __shfl_xor(sm, 16, kWave);
+      sq += __shfl_xor(sq, 16, kWave);
+      sm += __shfl_xor(sm, 32, kWave);
+      sq += __shfl_xor(sq, 32, kWave);
+      pmean[i] = sm * inv_d;
+      prstd[i] = rsqrtf(fmaxf(sq * inv_d - pmean[i] * pmean[i], 0.f) + p.eps);
 #pragma unroll
-      for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int et = 0; et < 2; ++et) {
-          const int e = c * CW + et * 16 + lg * 4;
-          const u32x2 g2 = *reinterpret_cast<const u32x2*>(Gs + e);
-          const u32x2 b2 = *reinterpret_cast<const u32x2*>(Gs + D + e);
-          const f32x4 v = lc[i][c][et];
-          u32x2 o;
-          o[0] = pack_bf16x2((v[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(b2[0]),
-                             (v[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(b2[0]));
-          o[1] = pack_bf16x2((v[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(b2[1]),
-                             (v[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(b2[1]));
-          __builtin_amdgcn_raw_buffer_store_b64(o, ry, yoff + e * 2, 0, 0);
-        }
+      for (int c = 0; c < NCH; ++c) plc[i][c][0] = lc[i][c][0], plc[i][c][1] = lc[i][c][1];
     }
-
-    // ---- the FMB LayerNorm over vec(F) (n k values) and Fn
-    float sm = 0.f;
+    {  // the FMB LayerNorm over vec(F): each wave's sum and sum of squares (fp32)
+      float sm = 0.f, sq = 0.f;
 #pragma unroll
-    for (int mi = 0; mi < MPW; ++mi)
+      for (int mi = 0; mi < MPW; ++mi)
 #pragma unroll
-      for (int jt = 0; jt < KJ; ++jt)
+        for (int jt = 0; jt < KJ; ++jt)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (jt * 16 + lg * 4 + t < k) sm += facc[mi][jt][t];
-    sm = group_sum_v<64>(sm);
-    if (lane == 0) red[wave] = sm;
-    ring_barrier();
-    const float mean = ((red[0] + red[1]) + (red[2] + red[3])) * inv_nk;
-    float q = 0.f;
-#pragma unroll
-    for (int mi = 0; mi < MPW; ++mi)
-#pragma unroll
-      for (int jt = 0; jt < KJ; ++jt)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (jt * 16 + lg * 4 + t < k) {
-            const float dv = facc[mi][jt][t] - mean;
-            q += dv * dv;
-          }
-    q = group_sum_v<64>(q);
-    if (lane == 0) red[NW + wave] = q;
-    ring_barrier();
-    const float rstd = rsqrtf(((red[NW] + red[NW + 1]) + (red[NW + 2] + red[NW + 3])) * inv_nk + p.eps);
-    // Fn row-major, or K-blocked over the whole batch (64-column blocks of fn_kblock_rows rows);
-    // every lane stores (those past k to an offset past the record count), so each wave
-    // issues exactly MPW x KJ stores per example
-    // (the resource is assembled from uniform values: the compiler cannot tell the select is
-    // uniform, and a resource it takes for divergent turns every store into a loop over lanes)
-    const uint64_t fbase = reinterpret_cast<uint64_t>(fkb ? p.fn : p.fn + b * (int64_t)N * k);
-    const uint64_t fb = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(fbase >> 32)) << 32) |
-                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)fbase);
-    const __amdgpu_buffer_rsrc_t rfn = __builtin_amdgcn_make_buffer_rsrc(
-        reinterpret_cast<void*>(fb), (short)0,
-        __builtin_amdgcn_readfirstlane(fkb ? (int)(fkb * (uint32_t)(N * k) * 2u) : N * k * 2), 0x00020000);
-#pragma unroll
-    for (int mi = 0; mi < MPW; ++mi)
-#pragma unroll
-      for (int jt = 0; jt < KJ; ++jt) {
-        const int m = (wave + mi * NW) * 16 + li;
-        const int j0 = jt * 16 + lg * 4;  // k % 4 == 0: the 4 values j0 .. j0+3 are all valid or all not
-        const int gi = j0 < k ? m * k + j0 : 0;
-        const u32x2 g2 = *reinterpret_cast<const u32x2*>(Gfm + gi);
-        const u32x2 b2 = *reinterpret_cast<const u32x2*>(Gfm + N * k + gi);
-        const f32x4 f = facc[mi][jt];
-        u32x2 o;
-        o[0] = pack_bf16x2((f[0] - mean) * rstd * bf16lo(g2[0]) + bf16lo(b2[0]),
-                           (f[1] - mean) * rstd * bf16hi(g2[0]) + bf16hi(b2[0]));
-        o[1] = pack_bf16x2((f[2] - mean) * rstd * bf16lo(g2[1]) + bf16lo(b2[1]),
-                           (f[3] - mean) * rstd * bf16hi(g2[1]) + bf16hi(b2[1]));
-        const uint32_t cc = (uint32_t)(m * k + j0);  // 4-aligned: the 4 values share a 64-column block
-        const uint32_t off = j0 >= k ? kOOB : fkb ? (((cc >> 6) * fkb + (uint32_t)b) * 64u + (cc & 63u)) * 2u : cc * 2u;
-        __builtin_amdgcn_raw_buffer_store_b64(o, rfn, off, 0, 0);
+          for (int t = 0; t < 4; ++t)
+            if (jt * 16 + lg * 4 + t < k) {
+              sm += facc[mi][jt][t];
+              sq += facc[mi][jt][t] * facc[mi][jt][t];
+            }
+      sm = group_sum_v<64>(sm);
+      sq = group_sum_v<64>(sq);
+      // (every wave read the previous example's sums in this example's first chunk,
+      // before that chunk's second barrier)
+      if (lane == 0) {
+        red[wave] = sm;
+        red[NW + wave] = sq;
       }
+#pragma unroll
+      for (int mi = 0; mi < MPW; ++mi)
+#pragma unroll
+        for (int jt = 0; jt < KJ; ++jt) pfacc[mi][jt] = facc[mi][jt];
+    }
+    pb = b;
+    live = true;
+  }
+  // the last example's output stage
+  ring_barrier();  // its FMB sums
+  {
+    __amdgpu_buffer_rsrc_t ry, rfn;
+    float fm_mean, fm_rstd;
+    out_rsrc(ry, rfn);
+    fm_stats(fm_mean, fm_rstd);
+#pragma unroll
+    for (int u = 0; u < UNITS; ++u) out_unit(u, ry, rfn, fm_mean, fm_rstd);
   }
   __builtin_amdgcn_s_waitcnt(vm_enc(0));  // the copies issued past the last example
 }
