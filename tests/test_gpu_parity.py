@@ -111,6 +111,28 @@ def test_ragged_batch_kblocked_fn(cfg, B):
     check(f"Y at examples {idx.tolist()}", host_f64(to_host(y))[idx], Y, "bf16")
 
 
+def test_n256_layer_three_examples_per_workgroup():
+    """The n = 256 layer's FMB+LCB kernel takes one example at a time per persistent
+    workgroup and finishes each example's output stage during the next one's first
+    chunk (the last example's after the loop).  At B = 515 workgroups 0..2 take three
+    examples and the others two: the examples checked are first, middle and last ones
+    of those sequences (Fn K-blocked over 768 rows, and Y)."""
+    cfg, B = ws.STACK8_N256.with_layers(1), 515
+    r = Run(cfg, seed=B, affine="random", batch=B)
+    spec = spec_of(cfg.layers[0], cfg.dtype)
+    lay = wk.workspace_layout(spec, B)
+    assert lay["fn_kblock_rows"] == 768, lay
+    wst = wk.alloc_workspace(wk.layer_workspace_size(spec, B))
+    y = wk.layer_forward(r.xd, r.layers[0], workspace=wst)
+    torch.cuda.synchronize()
+    idx = np.array([0, 1, 2, 3, 255, 256, 257, 258, 259, 511, 512, 513, 514])
+    s = cfg.layers[0]
+    Y, it = oracle.wukong_layer(r.x[idx], r.host_w[0], storage=BF16_STORAGE, intermediates=True)
+    fn = host_f64(_ws_fn(wst, lay, B, s.n * s.k, cfg.dtype))[idx]
+    check(f"Fn at examples {idx.tolist()}", fn, it["Fn"], "bf16")
+    check(f"Y at examples {idx.tolist()}", host_f64(to_host(y))[idx], Y, "bf16")
+
+
 @pytest.mark.parametrize("cfg,batch", [(ws.STACK8_N256, 6), (ws.STACK8_N512, 4)], ids=["stack8_n256", "stack8_n512"])
 def test_stack_two_layers(cfg, batch):
     r = Run(cfg, seed=5, affine="random", num_layers=2, batch=batch)
