@@ -842,6 +842,11 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
           *reinterpret_cast<u32x2*>(zrow + et * 16) = v;
         }
       }
+      // phase B's X rows are requested before the barrier (the chunk itself is complete)
+      u32x4 xf4[MPW];
+#pragma unroll
+      for (int mi = 0; mi < MPW; ++mi)
+        xf4[mi] = *reinterpret_cast<const u32x4*>(sx + ((wave + mi * NW) * 16 + li) * CW + lg * 8);
       ring_barrier();  // Z columns of the chunk complete
       // phase B: F^T += Z_c X_c^T
       u32x4 zf[KJ];
@@ -849,7 +854,7 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
       for (int jt = 0; jt < KJ; ++jt) zf[jt] = *reinterpret_cast<const u32x4*>(Zs + (jt * 16 + li) * ZP + lg * 8);
 #pragma unroll
       for (int mi = 0; mi < MPW; ++mi) {
-        const u32x4 xf = *reinterpret_cast<const u32x4*>(sx + ((wave + mi * NW) * 16 + li) * CW + lg * 8);
+        const u32x4 xf = xf4[mi];
 #pragma unroll
         for (int jt = 0; jt < KJ; ++jt)
           if (jt < KT) facc[mi][jt] = mfma16x16x32(zf[jt], xf, facc[mi][jt]);
