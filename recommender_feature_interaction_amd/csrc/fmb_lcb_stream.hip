@@ -693,13 +693,14 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
   const bool has_z = wave < KZ;  // wave-uniform
 
   // The output stage of an example (the LCB rows' LayerNorm and Y stores, the FMB
-  // LayerNorm and Fn stores) is software-pipelined into the next example's first
-  // chunk: its statistics are reduced at the end of the example (the FMB sums go
-  // to `red`, published by the next chunk's barrier), and its 32 normalise-and-store
-  // units are spread over that chunk's K steps, where the vector ALU work and the
-  // stores fill issue slots between MFMAs.  Before the first example the units run
-  // on zeros with resources of no records (the stores are dropped), so every
-  // example's first chunk issues the same 32 stores.
+  // LayerNorm and Fn stores) is software-pipelined into the next example's first two
+  // chunks: its statistics are reduced at the end of the example (the FMB sums go to
+  // `red`, published by the next chunk's barrier), and its 32 normalise-and-store
+  // units are spread over those chunks' K steps (the Fn blocks and the first LCB tile
+  // in chunk 0, the second LCB tile in chunk 1), where the vector ALU work and the
+  // stores fill issue slots between MFMAs.  Before the first example the units run on
+  // zeros with resources of no records (the stores are dropped), so every example's
+  // first two chunks issue the same stores.
   f32x4 plc[2][NCH][2];  // the previous example's LCB rows (Lc + residual)
   f32x4 pfacc[MPW][KJ];  // and its F^T blocks
   float pmean[2] = {0.f, 0.f}, prstd[2] = {0.f, 0.f};
@@ -716,6 +717,8 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
   bool live = false;   // uniform: there is a previous example
   constexpr int UNITS = 2 * NCH * 2 + MPW * KJ;  // = STORES
   static_assert(UNITS == STORES, "one store per unit");
+  constexpr int U0 = MPW * KJ + 2 * NCH, U1 = 2 * NCH;  // units (stores) in chunks 0 and 1
+  static_assert(U0 + U1 == UNITS, "every unit scheduled");
 
   // resources of the previous example's outputs (no records before the first example)
   auto out_rsrc = [&](__amdgpu_buffer_rsrc_t& ry, __amdgpu_buffer_rsrc_t& rfn) {
@@ -782,18 +785,18 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const uint16_t* sx = xslot(c);
-      // chunk c landed.  Newer operations: the copies of the S - 2 chunks after it, and,
-      // for chunks 1 .. S - 2, the previous example's stores, issued in chunk 0 after
-      // those chunks' copies (chunk 0's own copy came before them, chunk S - 1's after)
-      if (c >= 1 && c <= S - 2) __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX + STORES));
+      // chunk c landed.  Newer operations: the copies of the S - 2 chunks after it, and the
+      // previous example's stores issued after its copy: U0 in chunk 0 (after the copies of
+      // chunks 1 .. 3, before chunk 4's) and U1 in chunk 1 (after chunk 4's copy)
+      if (c == 1) __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX + U0));
+      else if (c == 2 || c == 3) __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX + U0 + U1));
+      else if (c == 4) __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX + U1));
       else __builtin_amdgcn_s_waitcnt(vm_enc((S - 2) * CX));
       ring_barrier();  // the chunk landed for every wave; slot c - 1 and Zs are free
       __amdgpu_buffer_rsrc_t ry, rfn;
       float fm_mean = 0.f, fm_rstd = 0.f;
-      if (c == 0) {
-        out_rsrc(ry, rfn);
-        fm_stats(fm_mean, fm_rstd);
-      }
+      if (c <= 1) out_rsrc(ry, rfn);
+      if (c == 0) fm_stats(fm_mean, fm_rstd);
       // phase A: [Z; Lc]^T[:, chunk] = X_c^T [Phi; W_L]^T, the LCB accumulators starting
       // from the residual rows X[n_F + i][chunk] (so no vector ALU touches them before the
       // LayerNorm)
@@ -826,9 +829,15 @@ __global__ __launch_bounds__(256, 1) void fmb_lcb_dchunk_kernel(FmbLcbArgs p, in
         // (waves past the Phi tiles hold zero fragments: no branch in the MFMA stream)
         za[0] = mfma16x16x32(xo0, wz[t], za[0]);
         za[1] = mfma16x16x32(xo1, wz[t], za[1]);
-        if (c == 0) {  // the previous example's output units, UNITS / STEPS per step
+        // the previous example's output units: in chunk 0 its Fn blocks and first LCB tile
+        // (U0), in chunk 1 its second LCB tile (U1), spread over the K steps
+        if (c == 0) {
 #pragma unroll
-          for (int u = t * UNITS / STEPS; u < (t + 1) * UNITS / STEPS; ++u) out_unit(u, ry, rfn, fm_mean, fm_rstd);
+          for (int v = t * U0 / STEPS; v < (t + 1) * U0 / STEPS; ++v)
+            out_unit(v < MPW * KJ ? 2 * NCH * 2 + v : v - MPW * KJ, ry, rfn, fm_mean, fm_rstd);
+        } else if (c == 1) {
+#pragma unroll
+          for (int v = t * U1 / STEPS; v < (t + 1) * U1 / STEPS; ++v) out_unit(2 * NCH + v, ry, rfn, fm_mean, fm_rstd);
         }
       }
       // Z columns to LDS (bf16, the interaction's operand)
